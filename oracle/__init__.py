@@ -1,0 +1,309 @@
+"""CPU oracle for the IntLoRA integer merge and integer linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this package.  It shares no code with the
+GPU library (``integer_rank_adaptation_amd``) and never imports it.
+
+The scalar arithmetic lives in ``intlora_oracle.c`` (plain C, compiled with
+``-ffp-contract=off``, OpenMP over independent rows/tokens only); this module marshals
+numpy arrays into it and adds the binary64 algebra of the pages (``algebra``).
+
+Pins (see ``tests/test_oracle_*.py``): Philox against rocRAND's reference engine,
+the binary32 log against 40-digit decimal logarithms on its whole input domain, the
+merges against exact rationals, brute force and the closed forms of the pages.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+from . import algebra  # noqa: F401  (re-exported)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "intlora_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+CFLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra"]
+
+
+def build(force: bool = True) -> str:
+    """Compile the C oracle with gcc into ``oracle/liboracle.so``."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *CFLAGS, "-o", tmp, _SRC, "-lm"], check=True)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    """Load the compiled oracle (building it only when nothing is built yet)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            build(force=True)
+        _lib = ctypes.CDLL(_LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int
+_U32 = ctypes.c_uint32
+_U64 = ctypes.c_uint64
+_F32 = ctypes.c_float
+_F64 = ctypes.c_double
+
+
+def _declare(L):
+    sig = {
+        "ora_philox4x32_10": (None, [_P, _P, _P]),
+        "ora_philox_batch": (None, [_I64, _P, _P, _P]),
+        "ora_ln_rn32": (_F32, [_F32]),
+        "ora_laplace": (_F32, [_U32]),
+        "ora_gen_r": (None, [_I64, _I64, _U64, _U32, _P, _P]),
+        "ora_gen_r_rows": (None, [_I64, _I64, _I64, _U64, _U32, _P, _P]),
+        "ora_sigma_w": (None, [_I64, _I64, _P, _P]),
+        "ora_vmc_scale": (None, [_I64, _P, _F64, _P]),
+        "ora_base_quant": (None, [_I64, _I64, _I32, _P, _P, _P, _P, _P]),
+        "ora_adaptation": (None, [_I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_mul_params": (None, [_I64, _I32, _P, _P, _P, _P]),
+        "ora_merge_mul": (_I64, [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_log2_round": (_I32, [_F32]),
+        "ora_shift_scale": (_F32, [_F32, _F32]),
+        "ora_merge_shift": (_I64, [_I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_quant_act": (None, [_I64, _I64, _P, _P, _P, _P]),
+        "ora_bf16_rne": (ctypes.c_uint16, [_F32]),
+        "ora_linear": (None, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_linear_sampled": (None, [_I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
+        "ora_num_threads": (_I32, []),
+        "ora_laplace_batch": (None, [_I64, _P, _P]),
+        "ora_ln_batch": (None, [_I64, _P, _P]),
+        "ora_log2_round_batch": (None, [_I64, _P, _P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a
+
+
+def _p(a):
+    return a.ctypes.data_as(ctypes.c_void_p) if a is not None else None
+
+
+def num_threads() -> int:
+    return int(lib().ora_num_threads())
+
+
+# --------------------------------------------------------------------------- RNG
+def philox(ctr, key):
+    """Philox4x32-10 of each (counter[4], key[2]) row -> uint32[N, 4]."""
+    ctr = _c(ctr, np.uint32).reshape(-1, 4)
+    key = _c(key, np.uint32).reshape(-1, 2)
+    assert ctr.shape[0] == key.shape[0]
+    out = np.empty_like(ctr)
+    lib().ora_philox_batch(ctr.shape[0], _p(ctr), _p(key), _p(out))
+    return out
+
+
+def ln_rn32(g):
+    g = _c(g, np.float32)
+    out = np.empty_like(g)
+    lib().ora_ln_batch(g.size, _p(g), _p(out))
+    return out
+
+
+def laplace(words):
+    words = _c(words, np.uint32)
+    out = np.empty(words.shape, np.float32)
+    lib().ora_laplace_batch(words.size, _p(words), _p(out))
+    return out
+
+
+def gen_r(d, n, seed, layer_id, c):
+    c = _c(c, np.float32)
+    assert c.shape == (d,)
+    out = np.empty((d, n), np.float32)
+    lib().ora_gen_r(d, n, seed, layer_id, _p(c), _p(out))
+    return out
+
+
+def gen_r_rows(row0, rows, n, seed, layer_id, c_rows):
+    c_rows = _c(c_rows, np.float32)
+    assert c_rows.shape == (rows,)
+    out = np.empty((rows, n), np.float32)
+    lib().ora_gen_r_rows(row0, rows, n, seed, layer_id, _p(c_rows), _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------- setup
+def sigma_w(W):
+    W = _c(W, np.float32)
+    d, n = W.shape
+    out = np.empty(d, np.float32)
+    lib().ora_sigma_w(d, n, _p(W), _p(out))
+    return out
+
+
+def vmc_scale(sigma, alpha):
+    sigma = _c(sigma, np.float32)
+    out = np.empty_like(sigma)
+    lib().ora_vmc_scale(sigma.size, _p(sigma), float(alpha), _p(out))
+    return out
+
+
+def base_quant(W, rstar, bits):
+    W = _c(W, np.float32)
+    rstar = _c(rstar, np.float32)
+    d, n = W.shape
+    wr = np.empty((d, n), np.uint8)
+    z = np.empty(d, np.int32)
+    s = np.empty(d, np.float32)
+    lib().ora_base_quant(d, n, bits, _p(W), _p(rstar), _p(wr), _p(z), _p(s))
+    return wr, z, s
+
+
+def setup_layer(W, seed, layer_id, bits, alpha=1.5):
+    """AQS + VMC set-up of one pretrained layer: sigma_W -> c -> R* -> Q[W - R*]."""
+    d, n = W.shape
+    sig = sigma_w(W)
+    c = vmc_scale(sig, alpha)
+    rstar = gen_r(d, n, seed, layer_id, c)
+    wr, z, s = base_quant(W, rstar, bits)
+    return dict(sigma=sig, c=c, rstar=rstar, wround=wr, z=z, s=s)
+
+
+# --------------------------------------------------------------------------- merge
+def adaptation(wround, z, s, rstar, A, B, want_u=True):
+    wround = _c(wround, np.uint8)
+    rows, n = wround.shape
+    A = _c(A, np.float32)
+    B = _c(B, np.float32)
+    r = A.shape[1]
+    assert A.shape == (rows, r) and B.shape == (r, n)
+    z = _c(z, np.int32)
+    s = _c(s, np.float32)
+    rstar = _c(rstar, np.float32)
+    u = np.empty((rows, n), np.float32) if want_u else None
+    umin = np.empty(rows, np.float32)
+    umax = np.empty(rows, np.float32)
+    lib().ora_adaptation(rows, n, r, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(u), _p(umin), _p(umax))
+    return u, umin, umax
+
+
+def mul_params(umin, umax, u_bits):
+    umin = _c(umin, np.float32)
+    umax = _c(umax, np.float32)
+    sbar = np.empty_like(umin)
+    zbar = np.empty(umin.shape, np.int32)
+    lib().ora_mul_params(umin.size, u_bits, _p(umin), _p(umax), _p(sbar), _p(zbar))
+    return sbar, zbar
+
+
+def merge_mul(wround, z, s, rstar, A, B, u_bits):
+    wround = _c(wround, np.uint8)
+    rows, n = wround.shape
+    A = _c(A, np.float32)
+    B = _c(B, np.float32)
+    r = A.shape[1]
+    assert A.shape == (rows, r) and B.shape == (r, n)
+    z, s, rstar = _c(z, np.int32), _c(s, np.float32), _c(rstar, np.float32)
+    m = np.empty((rows, n), np.int16)
+    ur = np.empty((rows, n), np.uint8)
+    sbar = np.empty(rows, np.float32)
+    zbar = np.empty(rows, np.int32)
+    umin = np.empty(rows, np.float32)
+    umax = np.empty(rows, np.float32)
+    sat = lib().ora_merge_mul(rows, n, r, u_bits, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(m), _p(ur),
+                              _p(sbar), _p(zbar), _p(umin), _p(umax))
+    return dict(m=m, uround=ur, sbar=sbar, zbar=zbar, umin=umin, umax=umax, sat=int(sat))
+
+
+def log2_round(a: float) -> int:
+    return int(lib().ora_log2_round(float(a)))
+
+
+def log2_round_batch(a):
+    a = _c(a, np.float32)
+    out = np.empty(a.shape, np.int32)
+    lib().ora_log2_round_batch(a.size, _p(a), _p(out))
+    return out
+
+
+def merge_shift(wround, z, s, rstar, A, B, w_bits, v_bits):
+    wround = _c(wround, np.uint8)
+    rows, n = wround.shape
+    A = _c(A, np.float32)
+    B = _c(B, np.float32)
+    r = A.shape[1]
+    assert A.shape == (rows, r) and B.shape == (r, n)
+    z, s, rstar = _c(z, np.int32), _c(s, np.float32), _c(rstar, np.float32)
+    m = np.empty((rows, n), np.int8)
+    sh = np.empty((rows, n), np.uint8)
+    sbar = np.empty(rows, np.float32)
+    umin = np.empty(rows, np.float32)
+    umax = np.empty(rows, np.float32)
+    sat = lib().ora_merge_shift(rows, n, r, w_bits, v_bits, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(m),
+                                _p(sh), _p(sbar), _p(umin), _p(umax))
+    return dict(m=m, shift=sh, sbar=sbar, umin=umin, umax=umax, sat=int(sat))
+
+
+# --------------------------------------------------------------------------- linear
+def quant_act(X):
+    X = _c(X, np.float32)
+    M, n = X.shape
+    xq = np.empty((M, n), np.int8)
+    sx = np.empty(M, np.float32)
+    rs = np.empty(M, np.int32)
+    lib().ora_quant_act(M, n, _p(X), _p(xq), _p(sx), _p(rs))
+    return xq, sx, rs
+
+
+def bf16_rne(y: float) -> int:
+    return int(lib().ora_bf16_rne(float(y)))
+
+
+def linear(xq, sx, m, sbar, want_exact=True):
+    xq = _c(xq, np.int8)
+    M, n = xq.shape
+    m = _c(m, np.int32)
+    d = m.shape[0]
+    assert m.shape == (d, n)
+    sx, sbar = _c(sx, np.float32), _c(sbar, np.float32)
+    exact = np.empty((M, d), np.int64) if want_exact else None
+    y32 = np.empty((M, d), np.float32)
+    y = np.empty((M, d), np.uint16)
+    lib().ora_linear(M, d, n, _p(xq), _p(sx), _p(m), _p(sbar), _p(exact), _p(y32), _p(y))
+    return exact, y32, y
+
+
+def linear_sampled(ts, is_, xq, sx, m, sbar):
+    ts = _c(ts, np.int64)
+    is_ = _c(is_, np.int64)
+    xq = _c(xq, np.int8)
+    m = _c(m, np.int32)
+    n = xq.shape[1]
+    assert m.shape[1] == n
+    sx, sbar = _c(sx, np.float32), _c(sbar, np.float32)
+    exact = np.empty(ts.size, np.int64)
+    y = np.empty(ts.size, np.uint16)
+    lib().ora_linear_sampled(ts.size, _p(ts), _p(is_), n, _p(xq), _p(sx), _p(m), _p(sbar), _p(exact), _p(y))
+    return exact, y
+
+
+def byte_planes(m):
+    """Bias byte split of int16 merged integers: hi = m >> 8, lo = (m & 0xFF) - 128,
+    so that m = 256*hi + lo + 128 for every int16 (the two int8 GEMM planes)."""
+    m = np.asarray(m).astype(np.int32)
+    hi = m >> 8
+    lo = (m & 0xFF) - 128
+    return hi.astype(np.int8), lo.astype(np.int8)
