@@ -1,0 +1,212 @@
+/*
+ * intlora.h -- C ABI of libintlora.so: the IntLoRA integer merge and the W8A8 / W4A8
+ * integer linear layer that consumes the merged integers, on AMD Instinct MI355X
+ * (gfx950).
+ *
+ * Method: "IntLoRA: Integral Low-rank Adaptation of Quantized Diffusion Models"
+ * (Paper-Notes, ICML 2025):
+ *   section "1. AQS"  W' = Q[W - sg(R)] + sg(R) + AB; R regenerated from statistics
+ *                     and a fixed seed, so it is never stored;
+ *   section "2. MLA"  W' = [s I + (R + AB) / (W_round - z)] (.) (W_round - z);
+ *   section "3. VMC"  R* = r^alpha R with r = sigma_W / sigma_R;
+ *   section "two implementation variants":
+ *                     MUL   W' = s_bar (U_round - z_bar) (.) (W_round - z),
+ *                     SHIFT W' = sign(V) (.) [(W_round - z) >> shift];
+ *   section "training and inference efficiency": the merged integers are the
+ *                     deployed W8A8 / W4A8 weights, with no post-training quantization.
+ * The Laplace law of R follows the auxiliary-matrix ablation of the atlas.scime.ai
+ * summary of the same paper; per-token activation scales with per-channel weight
+ * scales follow "implementation details" of the SVDQuant article (8-bit setting).
+ *
+ * Conventions shared by every entry point
+ *  - W is d x n (out_features x in_features), row-major.  "Row" = output channel.
+ *  - All array pointers are DEVICE pointers owned by the caller, except `desc`
+ *    and the `intlora_base` / `intlora_lora` structs themselves (host structs holding
+ *    device pointers).  The library allocates no memory and keeps no state between
+ *    calls; scratch memory is the caller's workspace (`ws`, `ws_bytes`, sized by
+ *    intlora_workspace_bytes()).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).  Every
+ *    call only enqueues work; outputs are valid after the caller synchronizes the
+ *    stream.  The status reports host-side validation and launch errors.
+ *  - Sizes are int64; 0 rows / 0 tokens are valid no-ops (n must be >= 1).
+ *  - Codes: 8-bit codes are one uint8 per element; 4-bit codes are packed two per
+ *    byte, low nibble = even column, row stride n/2 bytes (n must be even).
+ *  - Pointers must be 16-byte aligned (INTLORA_EALIGN otherwise).
+ *  - Results are deterministic and independent of launch geometry: R depends only
+ *    on (seed, layer_id, i, j), so any row block regenerates the same values.
+ *  - Readings of points the pages leave open (the quantizer form, the w == 0
+ *    convention, the SHIFT scale, the counter layout of R, ...) are stated at each
+ *    entry point below.
+ *  - On error the call enqueues nothing and intlora_last_error() returns a
+ *    thread-local description.
+ */
+#ifndef INTLORA_H
+#define INTLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum intlora_status {
+  INTLORA_OK = 0,
+  INTLORA_EINVAL = 1,     /* null pointer or argument out of range (bit width, rank, alpha, mode) */
+  INTLORA_ESHAPE = 2,     /* unsupported or inconsistent sizes                                   */
+  INTLORA_EALIGN = 3,     /* a pointer is not 16-byte aligned                                    */
+  INTLORA_EWORKSPACE = 4, /* workspace missing or smaller than intlora_workspace_bytes()         */
+  INTLORA_EDEVICE = 5,    /* no usable gfx950 device                                             */
+  INTLORA_ELAUNCH = 6     /* a kernel launch failed (hipGetLastError)                            */
+};
+
+/* intlora_stats modes */
+enum { INTLORA_SIGMA_W = 0, INTLORA_U_MINMAX = 1 };
+
+/* merged-weight formats for intlora_linear_fwd */
+enum {
+  INTLORA_W_INT4 = 4,  /* SHIFT, b_W = 4: packed signed nibbles (two's complement)            */
+  INTLORA_W_INT8 = 8,  /* SHIFT, b_W = 8: int8                                                */
+  INTLORA_W_INT16 = 16 /* MUL: int16 merged integers (U_round - z_bar) * (W_round - z)        */
+};
+
+/* operations for intlora_workspace_bytes */
+enum {
+  INTLORA_OP_STATS_UMINMAX = 1,
+  INTLORA_OP_MERGE_MUL = 2,
+  INTLORA_OP_MERGE_SHIFT = 3,
+  INTLORA_OP_LINEAR = 4,
+  INTLORA_OP_BASE_QUANT = 5
+};
+
+/* One pretrained layer.  r is the LoRA rank (1..128); w_bits the base code width
+ * (4 or 8); (seed, layer_id) select the auxiliary-matrix stream. */
+typedef struct intlora_desc {
+  int64_t d;         /* out_features (rows)          */
+  int64_t n;         /* in_features (columns)        */
+  int32_t r;         /* LoRA rank                    */
+  int32_t w_bits;    /* 4 or 8                       */
+  uint64_t seed;     /* Philox key                   */
+  uint32_t layer_id; /* Philox counter word 2        */
+  uint32_t reserved; /* must be 0                    */
+} intlora_desc;
+
+/* Stored state of a quantized base layer (AQS: Q[W - R*] with R* regenerated). */
+typedef struct intlora_base {
+  const void* w_round;  /* codes of W - R*: uint8 d x n (w_bits 8) or packed d x n/2 (w_bits 4) */
+  const int32_t* z;     /* [d] zero points                                                       */
+  const float* s;       /* [d] scales                                                            */
+  const float* vmc_c;   /* [d] VMC scale c_i = (sigma_W,i / sigma_R)^alpha, from intlora_vmc_scale */
+} intlora_base;
+
+/* LoRA factors in fp32 (floating point during tuning). */
+typedef struct intlora_lora {
+  const float* A; /* d x r row-major */
+  const float* B; /* r x n row-major */
+} intlora_lora;
+
+/* ---------------------------------------------------------------------------- */
+const char* intlora_status_string(int status);
+/* Thread-local text of the last error returned on this thread ("" if none). */
+const char* intlora_last_error(void);
+/* Library ABI version (major * 100 + minor). */
+int intlora_version(void);
+
+/* Workspace bytes needed by `op` for a layer (M tokens for INTLORA_OP_LINEAR).
+ * Returns 0 for ops that need none.  MUL/SHIFT merge and U statistics: the fp32
+ * adaptation term U (4 d n bytes) plus per-tile row partials. */
+size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M);
+
+/* ---------------------------------------------------------------------------- */
+/* Auxiliary matrix (section "1. AQS" with section "3. VMC"):
+ *   R*_ij = c_i * L_ij,  L_ij ~ Laplace(0, 1) by the inverse CDF
+ *   L = -sign(v) ln(1 - 2|v|), v = u - 1/2, u = (2 floor(x / 2^9) + 1) 2^-24,
+ *   x = word (q & 3) of Philox4x32-10 with counter (q >> 2 [64 bits], layer_id, 0)
+ *   and key (seed low, seed high), q = i*n + j.  ln is correctly rounded to binary32,
+ *   R* = RN32(c_i * L).  r_out: d x n fp32.  Uses desc->d, n, seed, layer_id. */
+int intlora_gen_r(const intlora_desc* desc, const float* vmc_c, float* r_out, void* stream);
+
+/* Per-row statistics.
+ *  INTLORA_SIGMA_W:  out0[d] = population std of each row of the fp32 weight W
+ *                    (binary64 accumulation, rounded to binary32; base/lora unused).
+ *                    The VMC statistic of section "3. VMC", per output channel.
+ *  INTLORA_U_MINMAX: out0[d] = U_min, out1[d] = U_max of the adaptation term
+ *                    U = s + (R* + AB) / w over the row's valid elements
+ *                    (w = W_round - z != 0); +inf / -inf for a row with none.
+ *                    Needs base, lora and the workspace. */
+int intlora_stats(const intlora_desc* desc, int mode, const float* W, const intlora_base* base,
+                  const intlora_lora* lora, float* out0, float* out1, void* ws, size_t ws_bytes, void* stream);
+
+/* VMC scale (section "3. VMC"): c_out[i] = RN32((sigma_w[i] / sqrt(2))^alpha); sigma_R =
+ * sqrt(2) is the standard deviation of the unit Laplace law.  alpha in [0, 8]. */
+int intlora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_out, void* stream);
+
+/* Base quantization Q[W - R*] (section "1. AQS"), per row, asymmetric with a range
+ * that always contains 0:  x = W - R*, lo = min(0, min x), hi = max(0, max x),
+ * s = (hi - lo) / (2^b - 1) (1 if that is 0), z = clamp(rint(-lo / s), 0, 2^b - 1),
+ * W_round = clamp(rint(x / s) + z, 0, 2^b - 1); rint = half to even; every step IEEE
+ * binary32.  Outputs w_round (uint8 d x n, or packed d x n/2), z_out[d], s_out[d].
+ * n <= 32768 (the row is staged in LDS).  No workspace. */
+int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vmc_c, void* w_round_out,
+                       int32_t* z_out, float* s_out, void* stream);
+
+/* IntLoRA_MUL merge (section "two implementation variants", MUL).  Per element with
+ * w = W_round - z != 0: acc = fma chain of A[i,k] B[k,j] for k = 0..r-1 from +0,
+ * U = s_i + (R*_ij + acc) / w (binary32, IEEE division).  Per row: lo = min(U_min, 0),
+ * hi = max(U_max, 0), s_bar = (hi - lo) / (2^u_bits - 1) (1 unless positive),
+ * z_bar = clamp(rint(-lo / s_bar), 0, 2^u_bits - 1); U_round = clamp(rint(U / s_bar) +
+ * z_bar, 0, 2^u_bits - 1); m = (U_round - z_bar) * w stored as int16, saturating
+ * (counted).  Reading for w == 0 (zero MLA denominator): excluded from the range,
+ * U_round = z_bar, m = 0.  The merged weight is s_bar_i * m_ij.
+ * Outputs: m (int16 d x n), s_bar[d], z_bar[d]; optional (NULL to skip):
+ * u_round_dbg (uint8 d x n), sat_count (one uint64, overwritten with the number of
+ * saturated elements).  u_bits in [2, 8].  Workspace: INTLORA_OP_MERGE_MUL. */
+int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* u_round_dbg,
+                      unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
+
+/* IntLoRA_SHIFT merge (section "two implementation variants", SHIFT).  U as for MUL.
+ * Reading: s_bar = max |U| over the row's valid elements (1 for an empty or all-zero
+ * row) and V = U / s_bar, so |V| <= 1 and only right shifts occur;
+ * shift = clamp(-round(log2 |V|), 0, 2^v_bits - 1), exact from the bits (no ties);
+ * m = sign(V) * (w >> shift), ">>" arithmetic (floor); V == 0 gives m = 0 and the
+ * largest shift code; m saturates to the signed w_bits range (counted); w == 0 gives
+ * m = 0 and shift code 255.  The merged weight is s_bar_i * m_ij.
+ * Outputs: m (int8 d x n for w_bits 8; packed signed nibbles d x n/2 for w_bits 4),
+ * s_bar[d]; optional shift_dbg (uint8 d x n), sat_count.  v_bits in [1, 8].
+ * Workspace: INTLORA_OP_MERGE_SHIFT. */
+int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int v_bits,
+                        void* m, float* s_bar, uint8_t* shift_dbg, unsigned long long* sat_count, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* Per-token symmetric int8 activation quantization: s_x[t] = max_j |X[t,j]| / 127
+ * (1 for an all-zero token), xq = clamp(rint(X / s_x), -127, 127), x_rowsum[t] =
+ * sum_j xq[t,j] (x_rowsum may be NULL).  X: M x n fp32. */
+int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s_x, int32_t* x_rowsum,
+                      void* stream);
+
+/* Integer linear layer on merged integers: Y[t, i] for t < M tokens, i < d outputs.
+ *   exact = sum_j xq[t,j] * m[i,j] (integer);
+ *   y = RN32(RN32(float(exact) * s_x[t]) * s_bar[i]),  Y = bf16 round-to-nearest-even.
+ * wfmt INTLORA_W_INT8 / INTLORA_W_INT4 (SHIFT merged integers): one int8 MFMA pass.
+ * wfmt INTLORA_W_INT16 (MUL merged integers): bias byte split hi = m >> 8,
+ * lo = (m & 0xFF) - 128, two int8 MFMA passes, exact = 256 acc_hi + acc_lo +
+ * 128 x_rowsum[t] in int64 (x_rowsum required).
+ * xq: M x n int8; m: d x n (layout per wfmt); Y_bf16: M x d (bf16 bits, row-major);
+ * acc_dbg (optional): planes x M x d int32 raw accumulators (planes = 2 for INT16:
+ * hi then lo; 1 otherwise).  n must be a multiple of 32 and <= 131071 (no int32
+ * overflow).  No workspace. */
+int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x, const int32_t* x_rowsum,
+                       int wfmt, const void* m, const float* s_bar, uint16_t* Y_bf16, int32_t* acc_dbg, void* ws,
+                       size_t ws_bytes, void* stream);
+
+/* Diagnostic: the binary32 natural log used by intlora_gen_r, on g = G * 2^-23 for
+ * odd G in [1, 2^23) (the only values it is ever given): out[t] = RN32(ln(G[t] 2^-23)).
+ * Inputs outside that set give unspecified values. */
+int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* INTLORA_H */

@@ -1,0 +1,325 @@
+// C ABI of libintlora.so (declared in include/intlora.h): host-side validation,
+// workspace layout and kernel dispatch.  No allocation, no state across calls.
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/intlora.h"
+#include "intlora_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return INTLORA_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int launch_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(INTLORA_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+// Largest dynamic LDS any kernel asks for; set once per device before first use.
+int ensure_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(INTLORA_EDEVICE, "no HIP device");
+  static thread_local int configured_dev = -1;
+  if (configured_dev == dev) return INTLORA_OK;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(INTLORA_EDEVICE, "hipGetDeviceProperties failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(INTLORA_EDEVICE, "device %d is %s; this library is built for gfx950", dev, prop.gcnArchName);
+  configured_dev = dev;
+  return INTLORA_OK;
+}
+
+constexpr int64_t kMaxDim = int64_t(1) << 31;
+
+int check_desc(const intlora_desc* d, bool need_rank) {
+  if (!d) return fail(INTLORA_EINVAL, "desc is NULL");
+  if (d->w_bits != 4 && d->w_bits != 8) return fail(INTLORA_EINVAL, "w_bits must be 4 or 8 (got %d)", d->w_bits);
+  if (need_rank && (d->r < 1 || d->r > 128)) return fail(INTLORA_EINVAL, "rank r must be in [1, 128] (got %d)", d->r);
+  if (d->reserved != 0) return fail(INTLORA_EINVAL, "desc.reserved must be 0");
+  if (d->d < 0 || d->n < 1 || d->d >= kMaxDim || d->n >= kMaxDim)
+    return fail(INTLORA_ESHAPE, "bad shape d=%lld n=%lld", (long long)d->d, (long long)d->n);
+  if (d->w_bits == 4 && (d->n & 1)) return fail(INTLORA_ESHAPE, "4-bit codes need an even n (got %lld)", (long long)d->n);
+  if ((unsigned long long)d->d * (unsigned long long)d->n >= (1ull << 40))
+    return fail(INTLORA_ESHAPE, "d*n too large");
+  return INTLORA_OK;
+}
+
+int check_ptrs(std::initializer_list<const void*> ps, const char* what) {
+  for (const void* p : ps) {
+    if (!p) return fail(INTLORA_EINVAL, "%s: NULL pointer", what);
+    if (!aligned16(p)) return fail(INTLORA_EALIGN, "%s: pointer %p not 16-byte aligned", what, p);
+  }
+  return INTLORA_OK;
+}
+
+int check_opt(const void* p, const char* what) {
+  if (p && !aligned16(p)) return fail(INTLORA_EALIGN, "%s: pointer %p not 16-byte aligned", what, p);
+  return INTLORA_OK;
+}
+
+// Workspace layout of the merge / U statistics: U (d*n fp32) | pmin | pmax (d*ntiles fp32 each)
+struct MergeWs {
+  float* U;
+  float* pmin;
+  float* pmax;
+  int ntiles;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t merge_ws_bytes(int64_t d, int64_t n) {
+  const size_t nt = (size_t)intlora::adapt_max_ntiles(n);
+  return align256((size_t)d * (size_t)n * 4) + 2 * align256((size_t)d * nt * 4);
+}
+
+MergeWs carve(void* ws, int64_t d, int64_t n) {
+  MergeWs w;
+  w.ntiles = intlora::adapt_max_ntiles(n);
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  w.U = reinterpret_cast<float*>(p);
+  p += align256((size_t)d * (size_t)n * 4);
+  w.pmin = reinterpret_cast<float*>(p);
+  p += align256((size_t)d * (size_t)w.ntiles * 4);  // capacity; the kernels use <= ntiles per row
+  w.pmax = reinterpret_cast<float*>(p);
+  return w;
+}
+
+int check_ws(void* ws, size_t ws_bytes, size_t need) {
+  if (need == 0) return INTLORA_OK;
+  if (!ws) return fail(INTLORA_EWORKSPACE, "workspace is NULL (need %zu bytes)", need);
+  if (!aligned16(ws)) return fail(INTLORA_EALIGN, "workspace not 16-byte aligned");
+  if (ws_bytes < need) return fail(INTLORA_EWORKSPACE, "workspace too small: %zu < %zu bytes", ws_bytes, need);
+  return INTLORA_OK;
+}
+
+int run_adapt(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, MergeWs& w,
+              unsigned long long* sat_zero, hipStream_t st) {
+  intlora::AdaptArgs a;
+  a.d = desc->d;
+  a.n = desc->n;
+  a.r = desc->r;
+  a.w_bits = desc->w_bits;
+  a.seed = desc->seed;
+  a.layer_id = desc->layer_id;
+  a.wround = static_cast<const uint8_t*>(base->w_round);
+  a.z = base->z;
+  a.s = base->s;
+  a.c = base->vmc_c;
+  a.A = lora->A;
+  a.B = lora->B;
+  a.U = w.U;
+  a.pmin = w.pmin;
+  a.pmax = w.pmax;
+  a.sat_zero = sat_zero;
+  a.force_generic = false;
+  return launch_status(intlora::launch_adapt(a, &w.ntiles, st), "adaptation kernel");
+}
+
+int check_base_lora(const intlora_base* base, const intlora_lora* lora) {
+  if (!base || !lora) return fail(INTLORA_EINVAL, "base / lora struct is NULL");
+  int s = check_ptrs({base->w_round, base->z, base->s, base->vmc_c}, "base");
+  if (s) return s;
+  return check_ptrs({lora->A, lora->B}, "lora");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* intlora_status_string(int status) {
+  switch (status) {
+    case INTLORA_OK: return "ok";
+    case INTLORA_EINVAL: return "invalid argument";
+    case INTLORA_ESHAPE: return "unsupported shape";
+    case INTLORA_EALIGN: return "misaligned pointer";
+    case INTLORA_EWORKSPACE: return "workspace too small";
+    case INTLORA_EDEVICE: return "no usable device";
+    case INTLORA_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* intlora_last_error(void) { return g_err; }
+
+int intlora_version(void) { return 100; }
+
+size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
+  (void)M;
+  if (!desc || desc->d < 0 || desc->n < 1) return 0;
+  switch (op) {
+    case INTLORA_OP_STATS_UMINMAX:
+    case INTLORA_OP_MERGE_MUL:
+    case INTLORA_OP_MERGE_SHIFT:
+      return merge_ws_bytes(desc->d, desc->n);
+    default:
+      return 0;
+  }
+}
+
+int intlora_gen_r(const intlora_desc* desc, const float* vmc_c, float* r_out, void* stream) {
+  int s = check_desc(desc, false);
+  if (s) return s;
+  if (desc->d == 0) return ok();
+  if ((s = check_ptrs({vmc_c, r_out}, "gen_r"))) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_gen_r(desc->d, desc->n, desc->seed, desc->layer_id, vmc_c, r_out,
+                                             static_cast<hipStream_t>(stream)),
+                       "gen_r");
+}
+
+int intlora_stats(const intlora_desc* desc, int mode, const float* W, const intlora_base* base,
+                  const intlora_lora* lora, float* out0, float* out1, void* ws, size_t ws_bytes, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (mode == INTLORA_SIGMA_W) {
+    if (!desc) return fail(INTLORA_EINVAL, "desc is NULL");
+    if (desc->d < 0 || desc->n < 1 || desc->d >= kMaxDim || desc->n >= kMaxDim)
+      return fail(INTLORA_ESHAPE, "bad shape");
+    if (desc->d == 0) return ok();
+    int s = check_ptrs({W, out0}, "stats(sigma_w)");
+    if (s) return s;
+    if ((s = ensure_device())) return s;
+    return launch_status(intlora::launch_sigma_w(desc->d, desc->n, W, out0, st), "sigma_w");
+  }
+  if (mode != INTLORA_U_MINMAX) return fail(INTLORA_EINVAL, "unknown stats mode %d", mode);
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (desc->d == 0) return ok();
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_ptrs({out0, out1}, "stats(u_minmax)"))) return s;
+  if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
+  if ((s = ensure_device())) return s;
+  MergeWs w = carve(ws, desc->d, desc->n);
+  if ((s = run_adapt(desc, base, lora, w, nullptr, st))) return s;
+  return launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, out0, out1, st), "row range");
+}
+
+int intlora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_out, void* stream) {
+  if (d < 0) return fail(INTLORA_ESHAPE, "d < 0");
+  if (!(alpha >= 0.0 && alpha <= 8.0)) return fail(INTLORA_EINVAL, "alpha must be in [0, 8]");
+  if (d == 0) return ok();
+  int s = check_ptrs({sigma_w, c_out}, "vmc_scale");
+  if (s) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_vmc_scale(d, sigma_w, alpha, c_out, static_cast<hipStream_t>(stream)),
+                       "vmc_scale");
+}
+
+int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vmc_c, void* w_round_out,
+                       int32_t* z_out, float* s_out, void* stream) {
+  int s = check_desc(desc, false);
+  if (s) return s;
+  if (desc->n > 32768) return fail(INTLORA_ESHAPE, "base_quant supports n <= 32768 (got %lld)", (long long)desc->n);
+  if (desc->d == 0) return ok();
+  if ((s = check_ptrs({W, vmc_c, w_round_out, z_out, s_out}, "base_quant"))) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_base_quant(desc->d, desc->n, desc->w_bits, desc->seed, desc->layer_id, W, vmc_c,
+                                                  static_cast<uint8_t*>(w_round_out), z_out, s_out,
+                                                  static_cast<hipStream_t>(stream)),
+                       "base_quant");
+}
+
+int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* u_round_dbg, unsigned long long* sat_count,
+                      void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (u_bits < 2 || u_bits > 8) return fail(INTLORA_EINVAL, "u_bits must be in [2, 8] (got %d)", u_bits);
+  if (desc->d == 0) return ok();
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_ptrs({m, s_bar, z_bar}, "merge_mul"))) return s;
+  if ((s = check_opt(u_round_dbg, "u_round_dbg")) || (s = check_opt(sat_count, "sat_count"))) return s;
+  if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
+  if ((s = ensure_device())) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MergeWs w = carve(ws, desc->d, desc->n);
+  if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
+  return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
+                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.pmin,
+                                                 w.pmax, w.ntiles, m, s_bar, z_bar, u_round_dbg, sat_count, st),
+                       "quant_mul");
+}
+
+int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int v_bits,
+                        void* m, float* s_bar, uint8_t* shift_dbg, unsigned long long* sat_count, void* ws,
+                        size_t ws_bytes, void* stream) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (v_bits < 1 || v_bits > 8) return fail(INTLORA_EINVAL, "v_bits must be in [1, 8] (got %d)", v_bits);
+  if (desc->d == 0) return ok();
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_ptrs({m, s_bar}, "merge_shift"))) return s;
+  if ((s = check_opt(shift_dbg, "shift_dbg")) || (s = check_opt(sat_count, "sat_count"))) return s;
+  if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
+  if ((s = ensure_device())) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MergeWs w = carve(ws, desc->d, desc->n);
+  if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
+  return launch_status(intlora::launch_quant_shift(desc->d, desc->n, desc->w_bits, v_bits,
+                                                   static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.pmin,
+                                                   w.pmax, w.ntiles, static_cast<uint8_t*>(m), s_bar, shift_dbg,
+                                                   sat_count, st),
+                       "quant_shift");
+}
+
+int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s_x, int32_t* x_rowsum,
+                      void* stream) {
+  if (M < 0 || n < 1 || M >= kMaxDim || n >= kMaxDim) return fail(INTLORA_ESHAPE, "bad shape M=%lld n=%lld",
+                                                                 (long long)M, (long long)n);
+  if (M == 0) return ok();
+  int s = check_ptrs({X, xq, s_x}, "quant_act");
+  if (s) return s;
+  if ((s = check_opt(x_rowsum, "x_rowsum"))) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_quant_act(M, n, X, xq, s_x, x_rowsum, static_cast<hipStream_t>(stream)),
+                       "quant_act");
+}
+
+int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x, const int32_t* x_rowsum,
+                       int wfmt, const void* m, const float* s_bar, uint16_t* Y_bf16, int32_t* acc_dbg, void* ws,
+                       size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (wfmt != INTLORA_W_INT4 && wfmt != INTLORA_W_INT8 && wfmt != INTLORA_W_INT16)
+    return fail(INTLORA_EINVAL, "wfmt must be INTLORA_W_INT4, _INT8 or _INT16 (got %d)", wfmt);
+  if (M < 0 || d < 0 || n < 1 || M >= kMaxDim || d >= kMaxDim) return fail(INTLORA_ESHAPE, "bad shape");
+  if (n % 32 != 0 || n > 131071)
+    return fail(INTLORA_ESHAPE, "linear needs n a multiple of 32 and <= 131071 (got %lld)", (long long)n);
+  if ((int64_t)((M + 255) / 256) * (int64_t)((d + 127) / 128) >= (int64_t(1) << 31))
+    return fail(INTLORA_ESHAPE, "too many tiles");
+  if (M == 0 || d == 0) return ok();
+  int s = check_ptrs({xq, s_x, m, s_bar, Y_bf16}, "linear_fwd");
+  if (s) return s;
+  if (wfmt == INTLORA_W_INT16 && (s = check_ptrs({x_rowsum}, "linear_fwd x_rowsum (INT16)"))) return s;
+  if ((s = check_opt(acc_dbg, "acc_dbg"))) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_linear(M, d, n, xq, s_x, x_rowsum, wfmt, m, s_bar, Y_bf16, acc_dbg,
+                                              static_cast<hipStream_t>(stream)),
+                       "linear");
+}
+
+int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream) {
+  if (count < 0) return fail(INTLORA_ESHAPE, "count < 0");
+  if (count == 0) return ok();
+  int s = check_ptrs({G, out}, "debug_ln");
+  if (s) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_ln_odd(count, G, out, static_cast<hipStream_t>(stream)), "debug_ln");
+}
+
+}  // extern "C"

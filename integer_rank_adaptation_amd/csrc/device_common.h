@@ -1,0 +1,170 @@
+// Device helpers shared by the IntLoRA kernels (gfx950, wave64).
+//
+// Every floating-point step that decides an integer code is a single IEEE binary32
+// operation with round-to-nearest-even; the library is compiled with
+// -ffp-contract=off so that no multiply-add is fused behind our back, and fused
+// multiply-adds appear only where written as fmaf().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace intlora {
+
+constexpr int kWave = 64;
+
+// --------------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of two 32x32->64
+// multiplies; the high halves are XORed with the other two counter words and the
+// round key; the key advances by the two Weyl constants between rounds.
+// --------------------------------------------------------------------------------
+struct U4 {
+  uint32_t x, y, z, w;
+};
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    U4 n;
+    n.x = (uint32_t)(p1 >> 32) ^ c.y ^ k0;
+    n.y = (uint32_t)p1;
+    n.z = (uint32_t)(p0 >> 32) ^ c.w ^ k1;
+    n.w = (uint32_t)p0;
+    c = n;
+  }
+  return c;
+}
+
+// Counter block of linear element index q (q >> 2), layer id in word 2; the element
+// uses output word q & 3.  Key = (seed low, seed high).
+__device__ __forceinline__ U4 philox_block(uint64_t q4, uint32_t layer_id, uint64_t seed) {
+  U4 c{(uint32_t)q4, (uint32_t)(q4 >> 32), layer_id, 0u};
+  return philox4x32_10(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+}
+
+__device__ __forceinline__ uint32_t pick_word(const U4& v, unsigned idx) {
+  return idx == 0 ? v.x : idx == 1 ? v.y : idx == 2 ? v.z : v.w;
+}
+
+// --------------------------------------------------------------------------------
+// Natural logarithm of g = G * 2^-23 (G odd, 1 <= G < 2^23) rounded to binary32.
+// Evaluated in binary64: g = m * 2^e with m in [0.75, 1.5); ln m = -ln(r_k) +
+// log1p(m r_k - 1) with a 96-entry table (r_k short enough that m r_k is exact) and
+// a degree-9 series for log1p on |f| <= 2^-7.  The binary64 result is within a few
+// units of 2^-53 relative of ln g, far inside the distance of every ln g on this
+// domain from a binary32 rounding midpoint, so the final conversion gives RN32(ln g).
+// --------------------------------------------------------------------------------
+struct LnEntry {
+  double neg_ln_r_hi;
+  float neg_ln_r_lo;
+  float r;
+};
+
+__device__ __forceinline__ float ln_odd_g(uint32_t G, const LnEntry* __restrict__ tab) {
+  // leading-bit position p (0..22); m24 = G << (23 - p) in [2^23, 2^24)
+  const int p = 31 - __clz(G);
+  uint32_t m24 = G << (23 - p);
+  int e = p - 23;                  // g = (m24 * 2^-23) * 2^e
+  uint32_t F;                      // m * 2^24 as an integer, m in [0.75, 1.5)
+  if (m24 >= 0xC00000u) {          // m >= 1.5: halve
+    F = m24;                       // (m/2) * 2^24 = m24
+    e += 1;
+  } else {
+    F = m24 << 1;
+  }
+  const int k = (int)((F - 0xC00000u) >> 17);
+  const LnEntry t = tab[k];
+  const double m = (double)F * 0x1p-24;
+  const double f = fma(m, (double)t.r, -1.0);  // exact
+  // log1p(f) = f - f^2/2 + f^3/3 - ... + f^9/9
+  double p9 = 1.0 / 9.0;
+  p9 = fma(p9, f, -1.0 / 8.0);
+  p9 = fma(p9, f, 1.0 / 7.0);
+  p9 = fma(p9, f, -1.0 / 6.0);
+  p9 = fma(p9, f, 1.0 / 5.0);
+  p9 = fma(p9, f, -0.25);
+  p9 = fma(p9, f, 1.0 / 3.0);
+  p9 = fma(p9, f, -0.5);
+  const double f2 = f * f;
+  const double lp = fma(f2, p9, f);
+  // e*ln2 as a head with trailing zeros (exact product) plus a tail
+  const double LN2_HI = 0x1.62e42fefa3800p-1;
+  const double LN2_LO = 0x1.ef35793c76730p-45;
+  const double ed = (double)e;
+  const double a = ed * LN2_HI;                 // exact
+  const double s1 = a + t.neg_ln_r_hi;          // |a| >= |head| whenever e != 0
+  const double err = (ed != 0.0) ? (t.neg_ln_r_hi - (s1 - a)) : 0.0;  // Fast2Sum tail
+  const double tail = fma(ed, LN2_LO, (double)t.neg_ln_r_lo) + err;
+  const double res = s1 + (lp + tail);
+  return (float)res;
+}
+
+// Laplace(0, 1) sample from one word: u = (2 floor(x / 2^9) + 1) 2^-24, v = u - 1/2,
+// g = 1 - 2|v|, L = -sign(v) ln g.  Computed on integers: N = 2a + 1 - 2^23 is the odd
+// numerator of v (in units of 2^-24), G = 2^23 - |N| the odd numerator of g.
+__device__ __forceinline__ float laplace_from_word(uint32_t x, const LnEntry* __restrict__ tab) {
+  const int32_t a = (int32_t)(x >> 9);
+  const int32_t N = 2 * a + 1 - (1 << 23);
+  const uint32_t G = (uint32_t)((1 << 23) - (N < 0 ? -N : N));
+  const float lg = ln_odd_g(G, tab);
+  return (N < 0) ? lg : -lg;
+}
+
+// --------------------------------------------------------------------------------
+// Wave reductions (64 lanes) with shuffles; exact for min / max / integer sums.
+// --------------------------------------------------------------------------------
+__device__ __forceinline__ float wave_min(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fminf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_sum_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+// binary32 -> bfloat16, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t bf16_rne(float y) {
+  uint32_t b = __float_as_uint(y);
+  b += 0x7FFFu + ((b >> 16) & 1u);
+  return (uint16_t)(b >> 16);
+}
+
+// round(log2 |v|) for a nonzero binary32, exactly, from the bits: the unbiased
+// exponent plus one when the significand is at or above sqrt(2) (field >= 0x3504F4;
+// sqrt(2) is irrational, so there are no ties).  Subnormals are normalized first.
+__device__ __forceinline__ int log2_round_bits(float v) {
+  uint32_t b = __float_as_uint(v) & 0x7FFFFFFFu;
+  int ex = (int)(b >> 23);
+  uint32_t frac = b & 0x7FFFFFu;
+  if (ex == 0) {  // subnormal: shift the leading one up to bit 23
+    const int lz = __clz(frac) - 8;  // frac != 0 here
+    frac = (frac << lz) & 0x7FFFFFu;
+    ex = 1 - lz;
+  }
+  return ex - 127 + (frac >= 0x3504F4u ? 1 : 0);
+}
+
+}  // namespace intlora

@@ -1,0 +1,53 @@
+// Internal launcher interface between the C ABI layer and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace intlora {
+
+struct AdaptArgs {
+  int64_t d, n;
+  int r, w_bits;
+  uint64_t seed;
+  uint32_t layer_id;
+  const uint8_t* wround;
+  const int32_t* z;
+  const float* s;
+  const float* c;
+  const float* A;
+  const float* B;
+  float* U;
+  float* pmin;
+  float* pmax;
+  unsigned long long* sat_zero;  // zeroed by the adaptation kernel (nullable)
+  bool force_generic;
+};
+
+// Upper bound of the number of column tiles of the adaptation kernel (sizes the
+// workspace of row partials).
+int adapt_max_ntiles(int64_t n);
+
+hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out,
+                        hipStream_t st);
+hipError_t launch_ln_odd(int64_t count, const uint32_t* G, float* out, hipStream_t st);
+hipError_t launch_sigma_w(int64_t d, int64_t n, const float* W, float* sigma, hipStream_t st);
+hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, hipStream_t st);
+hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint32_t layer_id, const float* W,
+                             const float* c, uint8_t* wround, int32_t* z, float* s, hipStream_t st);
+hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* sx, int32_t* rowsum,
+                            hipStream_t st);
+hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st);
+hipError_t launch_row_range(int64_t d, int ntiles, const float* pmin, const float* pmax, float* umin, float* umax,
+                            hipStream_t st);
+hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
+                            const float* U, const float* pmin, const float* pmax, int ntiles, int16_t* m,
+                            float* sbar, int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat,
+                            hipStream_t st);
+hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
+                              const float* U, const float* pmin, const float* pmax, int ntiles, uint8_t* m,
+                              float* sbar, uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st);
+hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
+                         int wfmt, const void* m, const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st);
+
+}  // namespace intlora

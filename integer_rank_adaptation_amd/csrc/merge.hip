@@ -1,0 +1,769 @@
+// IntLoRA merge kernels for gfx950: R* generation, per-channel statistics, the MLA
+// adaptation term, and the MUL / SHIFT integer merges.
+//
+// Method ("IntLoRA: Integral Low-rank Adaptation of Quantized Diffusion Models",
+// Paper-Notes ICML 2025):
+//   AQS   W' = Q[W - sg(R)] + sg(R) + AB, R regenerated from a seed (no storage)
+//   MLA   W' = [s I + (R + AB) / (W_round - z)] (.) (W_round - z)
+//   VMC   R* = r^alpha R, r = sigma_W / sigma_R
+//   MUL   W' = s_bar (U_round - z_bar) (.) (W_round - z)
+//   SHIFT W' = sign(V) (.) [(W_round - z) >> shift]
+// The merge runs as two kernels per layer:
+//   adapt:     R* in registers (Philox -> Laplace -> x c_i), U = s + (R* + AB) / w
+//              written to the workspace, per-tile row min / max over valid elements;
+//   quantize:  row statistics from the tile partials, then the MUL or SHIFT code
+//              and merged integer per element (HBM-bound: U + W_round in, m out).
+#include "device_common.h"
+#include "intlora_internal.h"
+
+namespace intlora {
+
+__device__ const LnEntry kLnTable[96] = {
+#include "ln_table.inc"
+};
+
+__device__ __forceinline__ void load_ln_table(LnEntry* dst) {
+  for (int t = threadIdx.x; t < 96; t += blockDim.x) dst[t] = kLnTable[t];
+}
+
+// R*_ij for one element (general path).
+__device__ __forceinline__ float rstar_element(uint64_t q, float ci, uint32_t layer_id, uint64_t seed,
+                                               const LnEntry* tab) {
+  const U4 blk = philox_block(q >> 2, layer_id, seed);
+  return ci * laplace_from_word(pick_word(blk, (unsigned)(q & 3)), tab);
+}
+
+// ---------------------------------------------------------------------------------
+// K1: R*_ij = c_i * Laplace(Philox(seed, layer, i*n + j)); one thread per counter
+// block of four consecutive linear elements.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
+                                              const float* __restrict__ c, float* __restrict__ out) {
+  __shared__ LnEntry tab[96];
+  load_ln_table(tab);
+  __syncthreads();
+  const uint64_t total = (uint64_t)d * (uint64_t)n;
+  const uint64_t nblk = (total + 3) >> 2;
+  for (uint64_t b = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk;
+       b += (uint64_t)gridDim.x * blockDim.x) {
+    const U4 v = philox_block(b, layer_id, seed);
+    const uint64_t q0 = b << 2;
+    uint64_t i = q0 / (uint64_t)n;
+    uint64_t j = q0 - i * (uint64_t)n;
+    float r[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (q0 + e < total) {
+        r[e] = c[i] * laplace_from_word(pick_word(v, e), tab);
+      }
+      if (++j == (uint64_t)n) {
+        j = 0;
+        ++i;
+      }
+    }
+    if (q0 + 3 < total && ((reinterpret_cast<uintptr_t>(out) & 15) == 0)) {
+      *reinterpret_cast<float4*>(out + q0) = make_float4(r[0], r[1], r[2], r[3]);
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (q0 + e < total) out[q0 + e] = r[e];
+    }
+  }
+}
+
+// Debug: binary32 natural log on odd multiples of 2^-23 (input G, output ln(G 2^-23)).
+__global__ __launch_bounds__(256) void k_ln_odd(int64_t count, const uint32_t* __restrict__ G,
+                                               float* __restrict__ out) {
+  __shared__ LnEntry tab[96];
+  load_ln_table(tab);
+  __syncthreads();
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < count; t += (int64_t)gridDim.x * blockDim.x)
+    out[t] = ln_odd_g(G[t], tab);
+}
+
+// ---------------------------------------------------------------------------------
+// Block reductions for 256-thread blocks.
+// ---------------------------------------------------------------------------------
+template <typename T, typename Op>
+__device__ __forceinline__ T block_reduce_256(T v, T* scratch /*[4]*/, Op op) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = op(v, __shfl_xor(v, o, kWave));
+  __syncthreads();
+  if (lane == 0) scratch[wid] = v;
+  __syncthreads();
+  T r = scratch[0];
+  r = op(r, scratch[1]);
+  r = op(r, scratch[2]);
+  r = op(r, scratch[3]);
+  return r;
+}
+
+// ---------------------------------------------------------------------------------
+// sigma_W: population standard deviation of each row of W (binary64 accumulation,
+// two passes: mean, then mean squared deviation), rounded to binary32.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sigma_w(int64_t n, const float* __restrict__ W,
+                                                float* __restrict__ sigma) {
+  __shared__ double red[4];
+  const float* row = W + (int64_t)blockIdx.x * n;
+  double acc = 0.0;
+  for (int64_t j = threadIdx.x; j < n; j += 256) acc += (double)row[j];
+  const double mean = block_reduce_256(acc, red, [](double a, double b) { return a + b; }) / (double)n;
+  double ss = 0.0;
+  for (int64_t j = threadIdx.x; j < n; j += 256) {
+    const double e = (double)row[j] - mean;
+    ss += e * e;
+  }
+  const double tot = block_reduce_256(ss, red, [](double a, double b) { return a + b; });
+  if (threadIdx.x == 0) sigma[blockIdx.x] = (float)sqrt(tot / (double)n);
+}
+
+// VMC scale c_i = RN32((sigma_W,i / sqrt 2)^alpha) (sigma_R = sqrt 2 for unit Laplace).
+__global__ __launch_bounds__(256) void k_vmc_scale(int64_t d, const float* __restrict__ sigma, double alpha,
+                                                  float* __restrict__ c) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < d) c[i] = (float)pow((double)sigma[i] / sqrt(2.0), alpha);
+}
+
+// ---------------------------------------------------------------------------------
+// Base quantizer Q[W - R*] per output row (AQS set-up). One block per row; the row
+// of x = W - R* is kept in LDS between the range pass and the code pass.
+//   lo = min(0, min x), hi = max(0, max x), s = (hi - lo)/(2^b - 1) (1 if 0),
+//   z = clamp(rint(-lo/s), 0, 2^b-1), W_round = clamp(rint(x/s) + z, 0, 2^b-1).
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_base_quant(int64_t n, int bits, uint64_t seed, uint32_t layer_id,
+                                                   const float* __restrict__ W, const float* __restrict__ c,
+                                                   uint8_t* __restrict__ wround, int32_t* __restrict__ z_out,
+                                                   float* __restrict__ s_out) {
+  extern __shared__ float xs[];  // n floats
+  __shared__ LnEntry tab[96];
+  __shared__ float red[4];
+  load_ln_table(tab);
+  __syncthreads();
+  const int64_t i = blockIdx.x;
+  const float ci = c[i];
+  float lo = 0.0f, hi = 0.0f;
+  for (int64_t j = threadIdx.x; j < n; j += 256) {
+    const float r = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab);
+    const float x = W[i * n + j] - r;
+    xs[j] = x;
+    lo = fminf(lo, x);
+    hi = fmaxf(hi, x);
+  }
+  lo = block_reduce_256(lo, red, [](float a, float b) { return fminf(a, b); });
+  hi = block_reduce_256(hi, red, [](float a, float b) { return fmaxf(a, b); });
+  const int qmax = (1 << bits) - 1;
+  float s = (hi - lo) / (float)qmax;
+  if (!(s > 0.0f)) s = 1.0f;
+  const float zf = rintf(-lo / s);
+  const int z = zf < 0.0f ? 0 : (zf > (float)qmax ? qmax : (int)zf);
+  if (threadIdx.x == 0) {
+    s_out[i] = s;
+    z_out[i] = z;
+  }
+  __syncthreads();
+  auto code_of = [&](float x) -> int {
+    float q = rintf(x / s);
+    q = fminf(fmaxf(q, -1.0e6f), 1.0e6f);
+    int v = (int)q + z;
+    return v < 0 ? 0 : (v > qmax ? qmax : v);
+  };
+  if (bits == 8) {
+    for (int64_t j = threadIdx.x; j < n; j += 256) wround[i * n + j] = (uint8_t)code_of(xs[j]);
+  } else {  // 4-bit, two codes per byte, low nibble = even column
+    const int64_t nb = n >> 1;
+    for (int64_t jb = threadIdx.x; jb < nb; jb += 256) {
+      const int a = code_of(xs[2 * jb]), b = code_of(xs[2 * jb + 1]);
+      wround[i * nb + jb] = (uint8_t)(a | (b << 4));
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Per-token symmetric int8 activation quantization: s_x = max|x| / 127 (1 if 0),
+// X_q = clamp(rint(x / s_x), -127, 127), rowsum = sum X_q.  One block per token.
+// ---------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_quant_act(int64_t n, const float* __restrict__ X, int8_t* __restrict__ xq,
+                                                  float* __restrict__ sx_out, int32_t* __restrict__ rowsum) {
+  __shared__ float redf[4];
+  __shared__ int redi[4];
+  const int64_t t = blockIdx.x;
+  const float* row = X + t * n;
+  float amax = 0.0f;
+  for (int64_t j = threadIdx.x; j < n; j += 256) amax = fmaxf(amax, fabsf(row[j]));
+  amax = block_reduce_256(amax, redf, [](float a, float b) { return fmaxf(a, b); });
+  float sx = amax / 127.0f;
+  if (!(sx > 0.0f)) sx = 1.0f;
+  int sum = 0;
+  for (int64_t j = threadIdx.x; j < n; j += 256) {
+    float q = rintf(row[j] / sx);
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    xq[t * n + j] = (int8_t)q;
+    sum += (int)q;
+  }
+  sum = block_reduce_256(sum, redi, [](int a, int b) { return a + b; });
+  if (threadIdx.x == 0) {
+    sx_out[t] = sx;
+    if (rowsum) rowsum[t] = sum;
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// K2 (fast path): adaptation term U and per-tile row range.
+// Block = 256 threads x 4 consecutive columns (1024-column tile) x kRows rows.
+// B[:, j..j+3] stays in registers for all kRows rows; A[i, :] is uniform per row
+// (scalar loads).  One Philox block serves the 4 elements of a thread's row segment
+// (needs n % 4 == 0).  U is written for every element (0 where w == 0).
+// ---------------------------------------------------------------------------------
+constexpr int kAdaptCols = 1024;  // tile width of the generic path and of CPT = 4
+constexpr int kAdaptMinCols = 512;
+constexpr int kAdaptRows = 8;
+
+template <int R, int CPT, bool W4>
+__global__ __launch_bounds__(256) void k_adapt_fast(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
+                                                   const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
+                                                   const float* __restrict__ s, const float* __restrict__ c,
+                                                   const float* __restrict__ A, const float* __restrict__ B,
+                                                   float* __restrict__ U, float* __restrict__ pmin,
+                                                   float* __restrict__ pmax, int ntiles,
+                                                   unsigned long long* __restrict__ sat_zero) {
+  __shared__ LnEntry tab[96];
+  __shared__ float smin[4][kAdaptRows], smax[4][kAdaptRows];
+  load_ln_table(tab);
+  if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int64_t j0 = (int64_t)blockIdx.x * (256 * CPT) + (int64_t)threadIdx.x * CPT;
+  const bool active = j0 < n;
+  float b[R][CPT];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (CPT == 4) {
+      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (active) v = *reinterpret_cast<const float4*>(B + (int64_t)k * n + j0);
+      b[k][0] = v.x; b[k][1] = v.y; b[k][2 % CPT] = v.z; b[k][3 % CPT] = v.w;
+    } else {
+      float2 v = make_float2(0.f, 0.f);
+      if (active) v = *reinterpret_cast<const float2*>(B + (int64_t)k * n + j0);
+      b[k][0] = v.x; b[k][1] = v.y;
+    }
+  }
+  const int64_t i_begin = (int64_t)blockIdx.y * kAdaptRows;
+  for (int ii = 0; ii < kAdaptRows; ++ii) {
+    const int64_t i = i_begin + ii;
+    if (i >= d) break;
+    float lmin = __builtin_inff(), lmax = -__builtin_inff();
+    if (active) {
+      int w[CPT];
+      const int zi = z[i];
+      if (W4) {
+        const uint32_t v = CPT == 4 ? *reinterpret_cast<const uint16_t*>(wround + i * (n >> 1) + (j0 >> 1))
+                                    : wround[i * (n >> 1) + (j0 >> 1)];
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) w[e] = (int)((v >> (4 * e)) & 15u) - zi;
+      } else {
+        const uint32_t v = CPT == 4 ? *reinterpret_cast<const uint32_t*>(wround + i * n + j0)
+                                    : *reinterpret_cast<const uint16_t*>(wround + i * n + j0);
+#pragma unroll
+        for (int e = 0; e < CPT; ++e) w[e] = (int)((v >> (8 * e)) & 255u) - zi;
+      }
+      const uint64_t q0 = (uint64_t)i * (uint64_t)n + (uint64_t)j0;
+      const U4 rnd = philox_block(q0 >> 2, layer_id, seed);
+      const unsigned wsel = (unsigned)(q0 & 3);  // 0 for CPT = 4; 0 or 2 for CPT = 2
+      const float ci = c[i], si = s[i];
+      const float* Ai = A + i * R;
+      float u[CPT];
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < R; ++k) acc = fmaf(Ai[k], b[k][e], acc);
+        const float rs = ci * laplace_from_word(pick_word(rnd, wsel + e), tab);
+        const float t = rs + acc;
+        const bool valid = w[e] != 0;
+        const float q = t / (float)(valid ? w[e] : 1);
+        const float uu = si + q;
+        u[e] = valid ? uu : 0.0f;
+        if (valid) {
+          lmin = fminf(lmin, uu);
+          lmax = fmaxf(lmax, uu);
+        }
+      }
+      if (CPT == 4)
+        *reinterpret_cast<float4*>(U + i * n + j0) = make_float4(u[0], u[1], u[2 % CPT], u[3 % CPT]);
+      else
+        *reinterpret_cast<float2*>(U + i * n + j0) = make_float2(u[0], u[1]);
+    }
+    lmin = wave_min(lmin);
+    lmax = wave_max(lmax);
+    if (lane == 0) {
+      smin[wid][ii] = lmin;
+      smax[wid][ii] = lmax;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < kAdaptRows) {
+    const int64_t i = i_begin + threadIdx.x;
+    if (i < d) {
+      const int t = threadIdx.x;
+      pmin[i * ntiles + blockIdx.x] = fminf(fminf(smin[0][t], smin[1][t]), fminf(smin[2][t], smin[3][t]));
+      pmax[i * ntiles + blockIdx.x] = fmaxf(fmaxf(smax[0][t], smax[1][t]), fmaxf(smax[2][t], smax[3][t]));
+    }
+  }
+}
+
+// K2 (general path): any n, any r <= kMaxRank.  One thread per element; the same
+// arithmetic as the fast path.  Tile partials over kAdaptCols columns.
+__global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int r, int w_bits, uint64_t seed,
+                                                      uint32_t layer_id, const uint8_t* __restrict__ wround,
+                                                      const int32_t* __restrict__ z, const float* __restrict__ s,
+                                                      const float* __restrict__ c, const float* __restrict__ A,
+                                                      const float* __restrict__ B, float* __restrict__ U,
+                                                      float* __restrict__ pmin, float* __restrict__ pmax, int ntiles,
+                                                      unsigned long long* __restrict__ sat_zero) {
+  __shared__ LnEntry tab[96];
+  __shared__ float smin[4], smax[4];
+  load_ln_table(tab);
+  if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
+  __syncthreads();
+  const int64_t i = blockIdx.y;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  float lmin = __builtin_inff(), lmax = -__builtin_inff();
+  const int64_t jt = (int64_t)blockIdx.x * kAdaptCols;
+  for (int64_t j = jt + threadIdx.x; j < jt + kAdaptCols && j < n; j += 256) {
+    int code;
+    if (w_bits == 4) {
+      const uint8_t byte = wround[i * ((n + 1) >> 1) + (j >> 1)];
+      code = (j & 1) ? (byte >> 4) : (byte & 15);
+    } else {
+      code = wround[i * n + j];
+    }
+    const int w = code - z[i];
+    float acc = 0.0f;
+    for (int k = 0; k < r; ++k) acc = fmaf(A[i * r + k], B[(int64_t)k * n + j], acc);
+    const float rs = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, c[i], layer_id, seed, tab);
+    const float t = rs + acc;
+    const bool valid = w != 0;
+    const float q = t / (float)(valid ? w : 1);
+    const float uu = s[i] + q;
+    U[i * n + j] = valid ? uu : 0.0f;
+    if (valid) {
+      lmin = fminf(lmin, uu);
+      lmax = fmaxf(lmax, uu);
+    }
+  }
+  lmin = wave_min(lmin);
+  lmax = wave_max(lmax);
+  if (lane == 0) {
+    smin[wid] = lmin;
+    smax[wid] = lmax;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    pmin[i * ntiles + blockIdx.x] = fminf(fminf(smin[0], smin[1]), fminf(smin[2], smin[3]));
+    pmax[i * ntiles + blockIdx.x] = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+  }
+}
+
+// Row range from the tile partials (uniform per block).
+__device__ __forceinline__ void row_range(const float* __restrict__ pmin, const float* __restrict__ pmax, int64_t i,
+                                          int ntiles, float& umin, float& umax) {
+  umin = __builtin_inff();
+  umax = -__builtin_inff();
+  for (int t = 0; t < ntiles; ++t) {
+    umin = fminf(umin, pmin[i * ntiles + t]);
+    umax = fmaxf(umax, pmax[i * ntiles + t]);
+  }
+}
+
+// Exposes U_min / U_max (the statistics entry point).
+__global__ __launch_bounds__(256) void k_row_range(int64_t d, int ntiles, const float* __restrict__ pmin,
+                                                  const float* __restrict__ pmax, float* __restrict__ umin,
+                                                  float* __restrict__ umax) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < d) {
+    float a, b;
+    row_range(pmin, pmax, i, ntiles, a, b);
+    umin[i] = a;
+    umax[i] = b;
+  }
+}
+
+__device__ __forceinline__ void add_saturations(unsigned long long* sat, int local) {
+  const unsigned long long tot = wave_sum_u64((unsigned long long)local);
+  if (sat && (threadIdx.x & 63) == 0 && tot) atomicAdd(sat, tot);
+}
+
+// ---------------------------------------------------------------------------------
+// K3: MUL quantize + integer Hadamard.  Block = 256 threads x 8 elements of one row.
+//   lo = min(U_min, 0), hi = max(U_max, 0), s_bar = (hi - lo)/(2^bU - 1) (1 unless > 0)
+//   z_bar = clamp(rint(-lo / s_bar)), U_round = clamp(rint(U / s_bar) + z_bar),
+//   m = (U_round - z_bar) w as int16 (saturating, counted); w == 0 -> m = 0, U_round = z_bar.
+// ---------------------------------------------------------------------------------
+constexpr int kQuantElems = 8;
+constexpr int kQuantCols = 256 * kQuantElems;
+
+struct MulParams {
+  float sbar;
+  int zbar;
+};
+
+__device__ __forceinline__ MulParams mul_params(float umin, float umax, int qmax) {
+  const float lo = fminf(umin, 0.0f), hi = fmaxf(umax, 0.0f);
+  float sbar = (hi - lo) / (float)qmax;
+  if (!(sbar > 0.0f)) sbar = 1.0f;
+  const float zf = rintf(-lo / sbar);
+  const int zbar = zf < 0.0f ? 0 : (zf > (float)qmax ? qmax : (int)zf);
+  return MulParams{sbar, zbar};
+}
+
+__device__ __forceinline__ int mul_code(float u, float sbar, int zbar, int qmax) {
+  float q = rintf(u / sbar);
+  q = fminf(fmaxf(q, -65536.0f), 65536.0f);
+  const int v = (int)q + zbar;
+  return v < 0 ? 0 : (v > qmax ? qmax : v);
+}
+
+template <bool W4>
+__global__ __launch_bounds__(256) void k_quant_mul(int64_t d, int64_t n, int u_bits, const uint8_t* __restrict__ wround,
+                                                  const int32_t* __restrict__ z, const float* __restrict__ U,
+                                                  const float* __restrict__ pmin, const float* __restrict__ pmax,
+                                                  int ntiles, int16_t* __restrict__ m, float* __restrict__ sbar_out,
+                                                  int32_t* __restrict__ zbar_out, uint8_t* __restrict__ uround_dbg,
+                                                  unsigned long long* __restrict__ sat) {
+  const int64_t i = blockIdx.y;
+  const int qmax = (1 << u_bits) - 1;
+  float umin, umax;
+  row_range(pmin, pmax, i, ntiles, umin, umax);
+  const MulParams P = mul_params(umin, umax, qmax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    sbar_out[i] = P.sbar;
+    zbar_out[i] = P.zbar;
+  }
+  const int zi = z[i];
+  int nsat = 0;
+  const int64_t j0 = (int64_t)blockIdx.x * kQuantCols + (int64_t)threadIdx.x * kQuantElems;
+  if ((n & 7) == 0) {
+    if (j0 < n) {
+      int code[8];
+      if (W4) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(wround + i * (n >> 1) + (j0 >> 1));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e] = (int)((v >> (4 * e)) & 15u);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(wround + i * n + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          code[e] = (int)((v.x >> (8 * e)) & 255u);
+          code[4 + e] = (int)((v.y >> (8 * e)) & 255u);
+        }
+      }
+      const float4 ua = *reinterpret_cast<const float4*>(U + i * n + j0);
+      const float4 ub = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
+      const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+      int mm[8], ur[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = code[e] - zi;
+        int mv = 0, uv = P.zbar;
+        if (w != 0) {
+          uv = mul_code(uu[e], P.sbar, P.zbar, qmax);
+          mv = (uv - P.zbar) * w;
+        }
+        if (mv > 32767) { mv = 32767; ++nsat; }
+        if (mv < -32768) { mv = -32768; ++nsat; }
+        mm[e] = mv;
+        ur[e] = uv;
+      }
+      int4 pk;
+      pk.x = (mm[0] & 0xFFFF) | (mm[1] << 16);
+      pk.y = (mm[2] & 0xFFFF) | (mm[3] << 16);
+      pk.z = (mm[4] & 0xFFFF) | (mm[5] << 16);
+      pk.w = (mm[6] & 0xFFFF) | (mm[7] << 16);
+      *reinterpret_cast<int4*>(m + i * n + j0) = pk;
+      if (uround_dbg) {
+        uint2 pu;
+        pu.x = (uint32_t)ur[0] | ((uint32_t)ur[1] << 8) | ((uint32_t)ur[2] << 16) | ((uint32_t)ur[3] << 24);
+        pu.y = (uint32_t)ur[4] | ((uint32_t)ur[5] << 8) | ((uint32_t)ur[6] << 16) | ((uint32_t)ur[7] << 24);
+        *reinterpret_cast<uint2*>(uround_dbg + i * n + j0) = pu;
+      }
+    }
+  } else {
+    for (int e = 0; e < kQuantElems; ++e) {
+      const int64_t j = j0 + e;
+      if (j >= n) break;
+      int code;
+      if (W4) {
+        const uint8_t byte = wround[i * ((n + 1) >> 1) + (j >> 1)];
+        code = (j & 1) ? (byte >> 4) : (byte & 15);
+      } else {
+        code = wround[i * n + j];
+      }
+      const int w = code - zi;
+      int mv = 0, uv = P.zbar;
+      if (w != 0) {
+        uv = mul_code(U[i * n + j], P.sbar, P.zbar, qmax);
+        mv = (uv - P.zbar) * w;
+      }
+      if (mv > 32767) { mv = 32767; ++nsat; }
+      if (mv < -32768) { mv = -32768; ++nsat; }
+      m[i * n + j] = (int16_t)mv;
+      if (uround_dbg) uround_dbg[i * n + j] = (uint8_t)uv;
+    }
+  }
+  add_saturations(sat, nsat);
+}
+
+// ---------------------------------------------------------------------------------
+// K4: SHIFT quantize.  s_bar = max(|U_min|, |U_max|) (1 for an empty / zero row),
+// V = U / s_bar, shift = clamp(-round(log2|V|), 0, 2^bV - 1) (V == 0: largest code,
+// m = 0), m = sign(V) (w >> shift) (arithmetic), saturated to bW signed bits.
+// Output int8 (bW = 8) or packed int4 nibbles (bW = 4, low nibble = even column).
+// ---------------------------------------------------------------------------------
+__device__ __forceinline__ float shift_scale(float umin, float umax) {
+  float sb = fmaxf(fabsf(umin), fabsf(umax));
+  if (!(sb > 0.0f) || isinf(sb)) sb = 1.0f;
+  return sb;
+}
+
+__device__ __forceinline__ int shift_merge(int w, float u, float sbar, int smax, int mlo, int mhi, int& sh,
+                                           int& nsat) {
+  if (w == 0) {
+    sh = 255;
+    return 0;
+  }
+  const float v = u / sbar;
+  int mv;
+  if (v == 0.0f) {
+    sh = smax;
+    mv = 0;
+  } else {
+    int k = -log2_round_bits(v);
+    sh = k < 0 ? 0 : (k > smax ? smax : k);
+    const int fl = w >> (sh > 31 ? 31 : sh);
+    mv = v > 0.0f ? fl : -fl;
+  }
+  if (mv > mhi) { mv = mhi; ++nsat; }
+  if (mv < mlo) { mv = mlo; ++nsat; }
+  return mv;
+}
+
+template <bool W4>
+__global__ __launch_bounds__(256) void k_quant_shift(int64_t d, int64_t n, int v_bits,
+                                                    const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
+                                                    const float* __restrict__ U, const float* __restrict__ pmin,
+                                                    const float* __restrict__ pmax, int ntiles,
+                                                    uint8_t* __restrict__ m, float* __restrict__ sbar_out,
+                                                    uint8_t* __restrict__ shift_dbg,
+                                                    unsigned long long* __restrict__ sat) {
+  const int64_t i = blockIdx.y;
+  const int smax = (1 << v_bits) - 1;
+  const int mhi = W4 ? 7 : 127, mlo = W4 ? -8 : -128;
+  float umin, umax;
+  row_range(pmin, pmax, i, ntiles, umin, umax);
+  const float sbar = shift_scale(umin, umax);
+  if (blockIdx.x == 0 && threadIdx.x == 0) sbar_out[i] = sbar;
+  const int zi = z[i];
+  int nsat = 0;
+  const int64_t j0 = (int64_t)blockIdx.x * kQuantCols + (int64_t)threadIdx.x * kQuantElems;
+  if ((n & 7) == 0) {
+    if (j0 < n) {
+      int code[8];
+      if (W4) {
+        const uint32_t v = *reinterpret_cast<const uint32_t*>(wround + i * (n >> 1) + (j0 >> 1));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) code[e] = (int)((v >> (4 * e)) & 15u);
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(wround + i * n + j0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          code[e] = (int)((v.x >> (8 * e)) & 255u);
+          code[4 + e] = (int)((v.y >> (8 * e)) & 255u);
+        }
+      }
+      const float4 ua = *reinterpret_cast<const float4*>(U + i * n + j0);
+      const float4 ub = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
+      const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
+      int mm[8], sh[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mm[e] = shift_merge(code[e] - zi, uu[e], sbar, smax, mlo, mhi, sh[e], nsat);
+      if (W4) {
+        uint32_t pk = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pk |= ((uint32_t)mm[e] & 15u) << (4 * e);
+        *reinterpret_cast<uint32_t*>(m + i * (n >> 1) + (j0 >> 1)) = pk;
+      } else {
+        uint2 pk;
+        pk.x = ((uint32_t)mm[0] & 255u) | (((uint32_t)mm[1] & 255u) << 8) | (((uint32_t)mm[2] & 255u) << 16) |
+               ((uint32_t)mm[3] << 24);
+        pk.y = ((uint32_t)mm[4] & 255u) | (((uint32_t)mm[5] & 255u) << 8) | (((uint32_t)mm[6] & 255u) << 16) |
+               ((uint32_t)mm[7] << 24);
+        *reinterpret_cast<uint2*>(m + i * n + j0) = pk;
+      }
+      if (shift_dbg) {
+        uint2 ps;
+        ps.x = (uint32_t)sh[0] | ((uint32_t)sh[1] << 8) | ((uint32_t)sh[2] << 16) | ((uint32_t)sh[3] << 24);
+        ps.y = (uint32_t)sh[4] | ((uint32_t)sh[5] << 8) | ((uint32_t)sh[6] << 16) | ((uint32_t)sh[7] << 24);
+        *reinterpret_cast<uint2*>(shift_dbg + i * n + j0) = ps;
+      }
+    }
+  } else {
+    // general n: W4 needs even n (validated); handle pairs so a byte is written whole
+    for (int e = 0; e < kQuantElems; e += 2) {
+      const int64_t j = j0 + e;
+      if (j >= n) break;
+      int mm2[2], sh2[2];
+      for (int h = 0; h < 2; ++h) {
+        const int64_t jj = j + h;
+        if (jj >= n) {
+          mm2[h] = 0;
+          sh2[h] = 255;
+          continue;
+        }
+        int code;
+        if (W4) {
+          const uint8_t byte = wround[i * (n >> 1) + (jj >> 1)];
+          code = (jj & 1) ? (byte >> 4) : (byte & 15);
+        } else {
+          code = wround[i * n + jj];
+        }
+        mm2[h] = shift_merge(code - zi, U[i * n + jj], sbar, smax, mlo, mhi, sh2[h], nsat);
+      }
+      if (W4) {
+        m[i * (n >> 1) + (j >> 1)] = (uint8_t)(((uint32_t)mm2[0] & 15u) | (((uint32_t)mm2[1] & 15u) << 4));
+      } else {
+        m[i * n + j] = (uint8_t)mm2[0];
+        if (j + 1 < n) m[i * n + j + 1] = (uint8_t)mm2[1];
+      }
+      if (shift_dbg) {
+        shift_dbg[i * n + j] = (uint8_t)sh2[0];
+        if (j + 1 < n) shift_dbg[i * n + j + 1] = (uint8_t)sh2[1];
+      }
+    }
+  }
+  add_saturations(sat, nsat);
+}
+
+// =================================================================================
+// Host launchers (called by the C ABI layer after validation).
+// =================================================================================
+static inline unsigned grid1(uint64_t work, unsigned block) {
+  uint64_t g = (work + block - 1) / block;
+  if (g > (1u << 20)) g = 1u << 20;
+  return (unsigned)(g ? g : 1);
+}
+
+hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out,
+                        hipStream_t st) {
+  const uint64_t blocks4 = ((uint64_t)d * (uint64_t)n + 3) / 4;
+  hipLaunchKernelGGL(k_gen_r, dim3(grid1(blocks4, 256)), dim3(256), 0, st, d, n, seed, layer_id, c, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ln_odd(int64_t count, const uint32_t* G, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_ln_odd, dim3(grid1((uint64_t)count, 256)), dim3(256), 0, st, count, G, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_sigma_w(int64_t d, int64_t n, const float* W, float* sigma, hipStream_t st) {
+  hipLaunchKernelGGL(k_sigma_w, dim3((unsigned)d), dim3(256), 0, st, n, W, sigma);
+  return hipGetLastError();
+}
+
+hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, hipStream_t st) {
+  hipLaunchKernelGGL(k_vmc_scale, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, sigma, alpha, c);
+  return hipGetLastError();
+}
+
+hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint32_t layer_id, const float* W,
+                             const float* c, uint8_t* wround, int32_t* z, float* s, hipStream_t st) {
+  const size_t lds = (size_t)n * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_base_quant),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 32768 * (int)sizeof(float));
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL(k_base_quant, dim3((unsigned)d), dim3(256), lds, st, n, bits, seed, layer_id, W, c, wround, z, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* sx, int32_t* rowsum,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_quant_act, dim3((unsigned)M), dim3(256), 0, st, n, X, xq, sx, rowsum);
+  return hipGetLastError();
+}
+
+int adapt_max_ntiles(int64_t n) { return (int)((n + kAdaptMinCols - 1) / kAdaptMinCols); }
+
+template <int R, int CPT>
+static hipError_t launch_adapt_r(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+  const int cols = 256 * CPT;
+  const int ntiles = (int)((a.n + cols - 1) / cols);
+  *ntiles_out = ntiles;
+  dim3 grid((unsigned)ntiles, (unsigned)((a.d + kAdaptRows - 1) / kAdaptRows));
+  if (a.w_bits == 4)
+    hipLaunchKernelGGL((k_adapt_fast<R, CPT, true>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
+                       a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
+  else
+    hipLaunchKernelGGL((k_adapt_fast<R, CPT, false>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
+                       a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+  const bool fast_ok = (a.n % 4) == 0 && ((reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.U)) & 15) == 0 &&
+                       (reinterpret_cast<uintptr_t>(a.wround) & 3) == 0;
+  if (fast_ok && !a.force_generic) {
+    switch (a.r) {
+      case 4: return launch_adapt_r<4, 4>(a, ntiles_out, st);
+      case 8: return launch_adapt_r<8, 4>(a, ntiles_out, st);
+      case 16: return launch_adapt_r<16, 4>(a, ntiles_out, st);
+      case 32: return launch_adapt_r<32, 4>(a, ntiles_out, st);
+      case 64: return launch_adapt_r<64, 2>(a, ntiles_out, st);
+      default: break;
+    }
+  }
+  const int ntiles = (int)((a.n + kAdaptCols - 1) / kAdaptCols);
+  *ntiles_out = ntiles;
+  dim3 grid((unsigned)ntiles, (unsigned)a.d);
+  hipLaunchKernelGGL(k_adapt_generic, grid, dim3(256), 0, st, a.d, a.n, a.r, a.w_bits, a.seed, a.layer_id, a.wround,
+                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
+  return hipGetLastError();
+}
+
+hipError_t launch_row_range(int64_t d, int ntiles, const float* pmin, const float* pmax, float* umin, float* umax,
+                            hipStream_t st) {
+  hipLaunchKernelGGL(k_row_range, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin, umax);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
+                            const float* U, const float* pmin, const float* pmax, int ntiles, int16_t* m,
+                            float* sbar, int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat,
+                            hipStream_t st) {
+  dim3 grid((unsigned)((n + kQuantCols - 1) / kQuantCols), (unsigned)d);
+  if (w_bits == 4)
+    hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(256), 0, st, d, n, u_bits, wround, z, U, pmin, pmax, ntiles, m,
+                       sbar, zbar, uround_dbg, sat);
+  else
+    hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(256), 0, st, d, n, u_bits, wround, z, U, pmin, pmax, ntiles, m,
+                       sbar, zbar, uround_dbg, sat);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
+                              const float* U, const float* pmin, const float* pmax, int ntiles, uint8_t* m,
+                              float* sbar, uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st) {
+  dim3 grid((unsigned)((n + kQuantCols - 1) / kQuantCols), (unsigned)d);
+  if (w_bits == 4)
+    hipLaunchKernelGGL(k_quant_shift<true>, grid, dim3(256), 0, st, d, n, v_bits, wround, z, U, pmin, pmax, ntiles, m,
+                       sbar, shift_dbg, sat);
+  else
+    hipLaunchKernelGGL(k_quant_shift<false>, grid, dim3(256), 0, st, d, n, v_bits, wround, z, U, pmin, pmax, ntiles,
+                       m, sbar, shift_dbg, sat);
+  return hipGetLastError();
+}
+
+}  // namespace intlora

@@ -1,0 +1,120 @@
+"""Convenience calls over the C ABI: allocate outputs / workspaces with torch (device
+memory only) and run one IntLoRA step through libintlora.so.  No arithmetic of the
+method happens here."""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+def _dev(t):
+    return t.device
+
+
+def gen_r(d, n, seed, layer_id, c):
+    out = torch.empty((d, n), dtype=torch.float32, device=_dev(c))
+    B.intlora_gen_r(B.desc(d, n, 1, 8, seed, layer_id), c, out)
+    return out
+
+
+def sigma_w(W):
+    d, n = W.shape
+    out = torch.empty(d, dtype=torch.float32, device=_dev(W))
+    B.intlora_stats(B.desc(d, n, 1, 8), B.INTLORA_SIGMA_W, W=W, out0=out)
+    return out
+
+
+def vmc_scale(sigma, alpha):
+    c = torch.empty_like(sigma)
+    B.intlora_vmc_scale(sigma.numel(), sigma, alpha, c)
+    return c
+
+
+def code_bytes(d, n, w_bits):
+    return (d, n) if w_bits == 8 else (d, n // 2)
+
+
+def base_quant(W, c, w_bits, seed, layer_id):
+    d, n = W.shape
+    wr = torch.empty(code_bytes(d, n, w_bits), dtype=torch.uint8, device=_dev(W))
+    z = torch.empty(d, dtype=torch.int32, device=_dev(W))
+    s = torch.empty(d, dtype=torch.float32, device=_dev(W))
+    B.intlora_base_quant(B.desc(d, n, 1, w_bits, seed, layer_id), W, c, wr, z, s)
+    return wr, z, s
+
+
+def setup_layer(W, w_bits, seed, layer_id, alpha=1.5):
+    """AQS + VMC set-up of a pretrained layer on the GPU: sigma_W, c, Q[W - R*]."""
+    sig = sigma_w(W)
+    c = vmc_scale(sig, alpha)
+    wr, z, s = base_quant(W, c, w_bits, seed, layer_id)
+    return dict(sigma=sig, c=c, wround=wr, z=z, s=s)
+
+
+def workspace(op, d, n, r, w_bits, device):
+    nbytes = B.intlora_workspace_bytes(op, B.desc(d, n, r, w_bits))
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def u_minmax(st, A, Bm, w_bits, seed, layer_id, ws=None):
+    d, r = A.shape
+    n = Bm.shape[1]
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    ws = workspace(B.INTLORA_OP_STATS_UMINMAX, d, n, r, w_bits, A.device) if ws is None else ws
+    umin = torch.empty(d, dtype=torch.float32, device=A.device)
+    umax = torch.empty_like(umin)
+    B.intlora_stats(dsc, B.INTLORA_U_MINMAX, None, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm),
+                    umin, umax, ws)
+    return umin, umax
+
+
+def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out=None):
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    ws = workspace(B.INTLORA_OP_MERGE_MUL, d, n, r, w_bits, dev) if ws is None else ws
+    o = out or dict(m=torch.empty((d, n), dtype=torch.int16, device=dev),
+                    sbar=torch.empty(d, dtype=torch.float32, device=dev),
+                    zbar=torch.empty(d, dtype=torch.int32, device=dev),
+                    sat=torch.zeros(2, dtype=torch.int64, device=dev))
+    if dbg and "uround" not in o:
+        o["uround"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
+    B.intlora_merge_mul(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), u_bits, o["m"],
+                        o["sbar"], o["zbar"], o.get("uround") if dbg else None, o["sat"], ws)
+    return o
+
+
+def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, out=None):
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    ws = workspace(B.INTLORA_OP_MERGE_SHIFT, d, n, r, w_bits, dev) if ws is None else ws
+    o = out or dict(m=torch.empty(code_bytes(d, n, w_bits), dtype=torch.uint8, device=dev),
+                    sbar=torch.empty(d, dtype=torch.float32, device=dev),
+                    sat=torch.zeros(2, dtype=torch.int64, device=dev))
+    if dbg and "shift" not in o:
+        o["shift"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
+    B.intlora_merge_shift(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), v_bits, o["m"],
+                          o["sbar"], o.get("shift") if dbg else None, o["sat"], ws)
+    return o
+
+
+def quant_act(X):
+    M, n = X.shape
+    xq = torch.empty((M, n), dtype=torch.int8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    rs = torch.empty(M, dtype=torch.int32, device=X.device)
+    B.intlora_quant_act(M, n, X, xq, sx, rs)
+    return xq, sx, rs
+
+
+def linear(xq, sx, rowsum, wfmt, m, sbar, d, acc_dbg=False, out=None):
+    M, n = xq.shape
+    Y = torch.empty((M, d), dtype=torch.int16, device=xq.device) if out is None else out
+    planes = 2 if wfmt == B.INTLORA_W_INT16 else 1
+    acc = torch.empty((planes, M, d), dtype=torch.int32, device=xq.device) if acc_dbg else None
+    B.intlora_linear_fwd(M, d, n, xq, sx, rowsum, wfmt, m, sbar, Y, acc)
+    return Y, acc

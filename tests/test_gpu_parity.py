@@ -1,0 +1,315 @@
+"""GPU parity: every entry point of the C ABI against the CPU oracle (marker `gpu`).
+
+Integers (codes, merged integers, accumulators, saturation counts) and the binary32
+quantities that decide them (R*, U range, s_bar, z, s, c) must be bit-identical; the
+bf16 output is compared bit for bit too (both sides follow the same epilogue), with
+the 1e-3 relative rule checked as well.  Inputs come from the seeded generators only.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from integer_rank_adaptation_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from integer_rank_adaptation_amd import ops as _ops
+
+    _ops.B.lib()
+    return _ops
+
+
+def cuda(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def pack4(codes):
+    codes = np.asarray(codes, np.uint8)
+    return (codes[:, 0::2] & 15) | ((codes[:, 1::2] & 15) << 4)
+
+
+def unpack4(b):
+    b = np.asarray(b, np.uint8)
+    out = np.empty((b.shape[0], b.shape[1] * 2), np.uint8)
+    out[:, 0::2] = b & 15
+    out[:, 1::2] = b >> 4
+    return out
+
+
+def unpack4s(b):
+    u = unpack4(b).astype(np.int16)
+    return np.where(u >= 8, u - 16, u).astype(np.int8)
+
+
+def bits(a):
+    a = np.asarray(a)
+    return a.view(np.uint32) if a.dtype == np.float32 else a
+
+
+def random_state(seed, d, n, r, w_bits):
+    """Synthetic stored state of a quantized layer plus LoRA factors."""
+    wr = synth.random_codes(seed, (d, n), w_bits)
+    z = synth.random_ints(seed + 1, d, 0, (1 << w_bits) - 1)
+    s = synth.random_positive(seed + 2, d, 1e-3, 5e-2)
+    c = synth.random_positive(seed + 3, d, 1e-4, 1e-2)
+    A = synth.random_matrix(seed + 4, (d, r), 0.5)
+    Bm = synth.random_matrix(seed + 5, (r, n), 0.0316)
+    return wr, z, s, c, A, Bm
+
+
+def gpu_state(wr, z, s, c, w_bits):
+    return dict(wround=cuda(pack4(wr) if w_bits == 4 else wr), z=cuda(z), s=cuda(s), c=cuda(c))
+
+
+# ----------------------------------------------------------------------------- primitives
+def test_ln_exhaustive(ops):
+    G = np.arange(1, 2**23, 2, dtype=np.uint32)
+    out = torch.empty(G.size, dtype=torch.float32, device="cuda")
+    ops.B.intlora_debug_ln(G.size, cuda(G), out)
+    got = host(out)
+    ref = oracle.ln_rn32((G.astype(np.float64) * 2.0**-23).astype(np.float32))
+    bad = np.nonzero(bits(got) != bits(ref))[0]
+    assert bad.size == 0, (bad.size, G[bad[:5]], got[bad[:5]], ref[bad[:5]])
+
+
+@pytest.mark.parametrize("d,n,seed,layer", [(1, 1, 0, 0), (3, 5, 7, 1), (7, 13, 2**40 + 3, 9), (64, 256, 0, 0),
+                                            (5, 1023, 11, 4), (33, 4096, 0, 2), (2, 3, 0xFFFFFFFFFFFFFFFF, 0xFFFFFFFF)])
+def test_gen_r_bitexact(ops, d, n, seed, layer):
+    c = synth.random_positive(d + n, d, 1e-4, 2.0)
+    got = host(ops.gen_r(d, n, seed, layer, cuda(c)))
+    ref = oracle.gen_r(d, n, seed, layer, c)
+    assert np.array_equal(bits(got), bits(ref))
+
+
+def test_sigma_and_vmc(ops):
+    W = synth.weight(synth.WORKLOADS[3], 0, d=67, n=777)
+    got = host(ops.sigma_w(cuda(W)))
+    ref = oracle.sigma_w(W)
+    ulps = np.abs(bits(got).astype(np.int64) - bits(ref).astype(np.int64))
+    assert ulps.max() <= 1 and (ulps == 0).mean() >= 0.95
+    sig = synth.random_positive(5, 1000, 1e-4, 1.0)
+    for alpha in (0.0, 0.5, 1.0, 1.5, 2.0):
+        c = host(ops.vmc_scale(cuda(sig), alpha))
+        assert np.array_equal(bits(c), bits(oracle.vmc_scale(sig, alpha))), alpha
+
+
+@pytest.mark.parametrize("w_bits", [4, 8])
+@pytest.mark.parametrize("d,n", [(1, 2), (5, 64), (37, 1000), (8, 4096), (3, 12288)])
+def test_base_quant(ops, w_bits, d, n):
+    W = synth.weight(synth.WORKLOADS[0], 0, d=d, n=n)
+    c = synth.random_positive(d * 7 + n, d, 1e-4, 3e-3)
+    wr, z, s = ops.base_quant(cuda(W), cuda(c), w_bits, 5, 3)
+    wr = host(wr)
+    if w_bits == 4:
+        wr = unpack4(wr)
+    R = oracle.gen_r(d, n, 5, 3, c)
+    ref_wr, ref_z, ref_s = oracle.base_quant(W, R, w_bits)
+    assert np.array_equal(wr, ref_wr)
+    assert np.array_equal(host(z), ref_z)
+    assert np.array_equal(bits(host(s)), bits(ref_s))
+
+
+# ----------------------------------------------------------------------------- merges
+MERGE_CASES = [
+    # d, n, r, w_bits  (n % 8 != 0 -> general quantize path; n % 4 != 0 or r not in
+    # {4, 8, 16, 32, 64} -> general adaptation path)
+    (1, 8, 1, 8),
+    (17, 100, 4, 8),
+    (9, 102, 4, 4),
+    (33, 1024, 32, 4),
+    (16, 2048, 64, 8),
+    (5, 96, 5, 8),
+    (3, 4096, 16, 4),
+    (40, 520, 8, 4),
+    (0, 64, 4, 8),
+    (11, 3072, 32, 4),
+    (6, 1536, 64, 4),
+]
+
+
+@pytest.mark.parametrize("d,n,r,w_bits", MERGE_CASES)
+def test_merge_mul_bitexact(ops, d, n, r, w_bits):
+    seed = 100 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    st = gpu_state(wr, z, s, c, w_bits)
+    for u_bits in sorted({2, w_bits, 8}):
+        g = ops.merge_mul(st, cuda(A), cuda(Bm), w_bits, u_bits, 77, 5, dbg=True)
+        umin, umax = ops.u_minmax(st, cuda(A), cuda(Bm), w_bits, 77, 5)
+        R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+        ref = oracle.merge_mul(wr, z, s, R, A, Bm, u_bits)
+        assert np.array_equal(host(g["m"]), ref["m"]), u_bits
+        assert np.array_equal(host(g["uround"]), ref["uround"])
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert np.array_equal(host(g["zbar"]), ref["zbar"])
+        assert np.array_equal(bits(host(umin)), bits(ref["umin"]))
+        assert np.array_equal(bits(host(umax)), bits(ref["umax"]))
+        assert int(host(g["sat"])[0]) == ref["sat"]
+
+
+@pytest.mark.parametrize("d,n,r,w_bits", MERGE_CASES)
+def test_merge_shift_bitexact(ops, d, n, r, w_bits):
+    seed = 200 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    st = gpu_state(wr, z, s, c, w_bits)
+    for v_bits in (1, 4, 8):
+        g = ops.merge_shift(st, cuda(A), cuda(Bm), w_bits, v_bits, 3, 11, dbg=True)
+        R = oracle.gen_r_rows(0, d, n, 3, 11, c)
+        ref = oracle.merge_shift(wr, z, s, R, A, Bm, w_bits, v_bits)
+        m = host(g["m"])
+        m = unpack4s(m) if w_bits == 4 else m.view(np.int8)
+        assert np.array_equal(m, ref["m"]), v_bits
+        assert np.array_equal(host(g["shift"]), ref["shift"])
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert int(host(g["sat"])[0]) == ref["sat"]
+
+
+def test_merge_degenerate_rows(ops):
+    """Rows with no valid element (w == 0 everywhere) and rows with U == s everywhere."""
+    d, n, r = 4, 64, 4
+    wr = np.full((d, n), 7, np.uint8)
+    z = np.array([7, 7, 0, 3], np.int32)  # rows 0, 1: all w == 0
+    s = np.full(d, 0.01, np.float32)
+    c = np.array([0.0, 1e-3, 0.0, 1e-3], np.float32)
+    A = synth.random_matrix(1, (d, r), 0.5)
+    Bm = np.zeros((r, n), np.float32)
+    Bm[:, : n // 2] = synth.random_matrix(2, (r, n // 2), 0.03)
+    A[2] = 0.0  # row 2: c = 0 and A = 0 -> U == s
+    st = gpu_state(wr, z, s, c, 8)
+    R = oracle.gen_r(d, n, 0, 0, c)
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), 8, 8, 0, 0, dbg=True)
+    ref = oracle.merge_mul(wr, z, s, R, A, Bm, 8)
+    for k in ("m", "uround", "zbar"):
+        assert np.array_equal(host(g[k]), ref[k]), k
+    assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+    umin, umax = ops.u_minmax(st, cuda(A), cuda(Bm), 8, 0, 0)
+    assert np.all(np.isposinf(host(umin)[:2])) and np.all(np.isneginf(host(umax)[:2]))
+    g2 = ops.merge_shift(st, cuda(A), cuda(Bm), 8, 4, 0, 0, dbg=True)
+    ref2 = oracle.merge_shift(wr, z, s, R, A, Bm, 8, 4)
+    assert np.array_equal(host(g2["m"]).view(np.int8), ref2["m"])
+    assert np.array_equal(host(g2["shift"]), ref2["shift"])
+    assert np.array_equal(bits(host(g2["sbar"])), bits(ref2["sbar"]))
+
+
+def test_merge_is_deterministic(ops):
+    wr, z, s, c, A, Bm = random_state(9, 64, 3072, 32, 4)
+    st = gpu_state(wr, z, s, c, 4)
+    a = ops.merge_mul(st, cuda(A), cuda(Bm), 4, 4, 0, 1)
+    b = ops.merge_mul(st, cuda(A), cuda(Bm), 4, 4, 0, 1)
+    assert torch.equal(a["m"], b["m"]) and torch.equal(a["sbar"], b["sbar"])
+
+
+# ----------------------------------------------------------------------------- linear
+@pytest.mark.parametrize("M,n", [(1, 32), (17, 1000), (5, 4097), (64, 320)])
+def test_quant_act(ops, M, n):
+    X = synth.activations(synth.WORKLOADS[0], n, M)
+    if M > 3:
+        X[3] = 0.0
+    xq, sx, rs = ops.quant_act(cuda(X))
+    rxq, rsx, rrs = oracle.quant_act(X)
+    assert np.array_equal(host(xq), rxq)
+    assert np.array_equal(bits(host(sx)), bits(rsx))
+    assert np.array_equal(host(rs), rrs)
+
+
+def _linear_case(ops, M, d, n, wfmt, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(seed + 1, M, 1e-3, 0.1)
+    sbar = synth.random_positive(seed + 2, d, 1e-5, 1e-2)
+    rs = xq.astype(np.int32).sum(axis=1).astype(np.int32)
+    if wfmt == 16:
+        m = rng.integers(-32768, 32768, size=(d, n)).astype(np.int16)
+        mg = cuda(m)
+    elif wfmt == 8:
+        m = rng.integers(-128, 128, size=(d, n)).astype(np.int8)
+        mg = cuda(m)
+    else:
+        m = rng.integers(-8, 8, size=(d, n)).astype(np.int8)
+        mg = cuda(pack4(m.astype(np.uint8) & 15))
+    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, acc_dbg=True)
+    exact, y32, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
+    Yh = host(Y).view(np.uint16)
+    acc = host(acc)
+    if wfmt == 16:
+        hi, lo = oracle.byte_planes(m)
+        assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
+        assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
+    else:
+        assert np.array_equal(acc[0].astype(np.int64), exact)
+    # bf16: bit-identical expected; the 1e-3 relative rule as a backstop
+    ybf = torch.from_numpy(Yh.view(np.int16)).view(torch.bfloat16).float().numpy()
+    rbf = torch.from_numpy(yref.view(np.int16)).view(torch.bfloat16).float().numpy()
+    assert np.all(np.abs(ybf - rbf) <= 1e-3 * np.abs(rbf) + 1e-30)
+    assert np.array_equal(Yh, yref)
+
+
+@pytest.mark.parametrize("wfmt", [8, 4, 16])
+@pytest.mark.parametrize("M,d,n", [(1, 1, 32), (37, 100, 96), (300, 260, 512), (257, 129, 320), (64, 520, 1280)])
+def test_linear_bitexact(ops, wfmt, M, d, n):
+    _linear_case(ops, M, d, n, wfmt, seed=M * 7 + d * 3 + n + wfmt)
+
+
+# ----------------------------------------------------------------------------- workloads
+def _gpu_pipeline(ops, wl, li, d, n, M, mode, bits_):
+    W = synth.weight(wl, li, d=d, n=n)
+    A, Bm = synth.lora(wl, li, d=d, n=n)
+    X = synth.activations(wl, n, M, li)
+    seed, lid = synth.PHILOX_SEED, synth.layer_id(wl.index, li)
+    st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+    if mode == "mul":
+        g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, bits_, seed, lid, dbg=True)
+        wfmt = 16
+    else:
+        g = ops.merge_shift(st, cuda(A), cuda(Bm), wl.w_bits, bits_, seed, lid, dbg=True)
+        wfmt = wl.w_bits
+    xq, sx, rs = ops.quant_act(cuda(X))
+    Y, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], d)
+    return dict(W=W, A=A, B=Bm, X=X, st=st, g=g, Y=Y, xq=xq, sx=sx)
+
+
+@pytest.mark.parametrize("wl_index", [0, 1, 2, 3, 4])
+def test_workload_end_to_end_reduced(ops, wl_index):
+    """Whole path from the raw fp32 weight, LoRA factors and activations, on the first
+    rows of every layer shape of the workload (full in_features, 96 tokens)."""
+    wl = synth.WORKLOADS[wl_index]
+    for li, L in enumerate(wl.layers):
+        d = min(L.d, 96)
+        M = min(wl.tokens[0], 96)
+        for mode, bits_ in wl.modes:
+            P = _gpu_pipeline(ops, wl, li, d, L.n, M, mode, bits_)
+            st = oracle.setup_layer(P["W"], synth.PHILOX_SEED, synth.layer_id(wl.index, li), wl.w_bits, synth.ALPHA)
+            sig_ulps = np.abs(bits(host(P["st"]["sigma"])).astype(np.int64) - bits(st["sigma"]).astype(np.int64))
+            assert sig_ulps.max() <= 1
+            assert np.array_equal(bits(host(P["st"]["c"])), bits(st["c"])), "VMC scale"
+            wr = host(P["st"]["wround"])
+            assert np.array_equal(unpack4(wr) if wl.w_bits == 4 else wr, st["wround"])
+            assert np.array_equal(host(P["st"]["z"]), st["z"])
+            if mode == "mul":
+                ref = oracle.merge_mul(st["wround"], st["z"], st["s"], st["rstar"], P["A"], P["B"], bits_)
+                m = host(P["g"]["m"])
+                assert np.array_equal(host(P["g"]["uround"]), ref["uround"])
+                assert np.array_equal(host(P["g"]["zbar"]), ref["zbar"])
+            else:
+                ref = oracle.merge_shift(st["wround"], st["z"], st["s"], st["rstar"], P["A"], P["B"], wl.w_bits,
+                                         bits_)
+                m = host(P["g"]["m"])
+                m = unpack4s(m) if wl.w_bits == 4 else m.view(np.int8)
+                assert np.array_equal(host(P["g"]["shift"]), ref["shift"])
+            assert np.array_equal(m, ref["m"]), (wl.name, L.name, mode)
+            assert np.array_equal(bits(host(P["g"]["sbar"])), bits(ref["sbar"]))
+            assert int(host(P["g"]["sat"])[0]) == ref["sat"]
+            xq, sx, rs = oracle.quant_act(P["X"])
+            assert np.array_equal(host(P["xq"]), xq)
+            _, _, y = oracle.linear(xq, sx, ref["m"].astype(np.int32), ref["sbar"])
+            assert np.array_equal(host(P["Y"]).view(np.uint16), y), (wl.name, L.name, mode)
