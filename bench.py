@@ -1,0 +1,292 @@
+"""Benchmark of the IntLoRA hot path on one MI355X.
+
+One step = the whole path over one batch of the workload: for every layer, the
+MUL (or SHIFT) merge of the trained LoRA factors into the quantized base (R*
+regeneration, adaptation term, row statistics, quantize + integer Hadamard / shift)
+followed by the integer linear layer that consumes the merged integers (int8 MFMA,
+dequantized bf16 output).  Inputs (quantized base, LoRA factors, quantized
+activations) are resident in HBM before the timed region.
+
+Default workload: the FLUX-like DiT block linears (hidden 3072; qkv 9216x3072,
+out 3072x3072, mlp 12288x3072 and 3072x12288), W4A8, MUL with a 4-bit adaptation
+term, rank 32, 4608 tokens.
+
+Printed (rank 0, one JSON line): value = 100 * T_roof / T_step, where T_roof is the
+step's time at MI355X peak (merge algorithmic bytes at 8 TB/s HBM plus the GEMM's
+executed int8 MFMA operations at 5.0 POP/s) and T_step the measured time of one step.
+Per-layer merge GB/s and GEMM TOP/s are listed alongside.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "merge GB/s + W8A8/W4A8 GEMM int8 TOPS (% of MI355X peak) per layer shape"
+HBM_PEAK_GBPS = 8000.0
+INT8_PEAK_TOPS = 5000.0
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", type=int, default=3)
+    p.add_argument("--tokens", type=int, default=0, help="override M (0: the workload's first)")
+    p.add_argument("--cpu-sample", type=float, default=0.0,
+                   help="fraction of rows/tokens the oracle processes (0: auto, about 15 s)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--json-out", default="")
+    return p.parse_args()
+
+
+def merge_alg_bytes(d, n, r, w_bits, mode):
+    """Bytes the merge itself must move: W_round in, merged integers out, A and B,
+    and the per-row vectors (z, s, c in; s_bar, z_bar out).  R is regenerated."""
+    code_in = d * n * (0.5 if w_bits == 4 else 1.0)
+    if mode == "mul":
+        out = d * n * 2.0
+    else:
+        out = d * n * (0.5 if w_bits == 4 else 1.0)
+    return code_in + out + 4.0 * d * r + 4.0 * r * n + 20.0 * d
+
+
+def gemm_exec_ops(M, d, n, mode):
+    passes = 2 if mode == "mul" else 1
+    return 2.0 * M * d * n * passes
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for f in ("linear.hip", "device_common.h"):
+        with open(os.path.join(ROOT, "integer_rank_adaptation_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(workload_name):
+    """HBM bytes per GEMM launch from the committed counter summary, if it was taken
+    on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", "linear_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha() or rec.get("workload") != workload_name:
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
+                                   "(the merge shards by rows and the GEMM by columns with no exchange; "
+                                   "see DESIGN.md)" % args.gpus}))
+        sys.exit(2)
+
+    import torch
+
+    from integer_rank_adaptation_amd import binding as B
+    from integer_rank_adaptation_amd import ops, synth
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    B.lib()  # fail loudly when the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = synth.WORKLOADS[args.workload]
+    M = args.tokens or wl.tokens[0]
+    mode, mbits = wl.modes[0]
+
+    # ---------------------------------------------------------------- inputs (untimed)
+    t_setup = time.time()
+    layers = []
+    ws_bytes = 0
+    for li, L in enumerate(wl.layers):
+        W = synth.weight(wl, li)
+        A, Bm = synth.lora(wl, li)
+        X = synth.activations(wl, L.n, M, li)
+        lid = synth.layer_id(wl.index, li)
+        Wg = torch.from_numpy(W).to(dev)
+        st = ops.setup_layer(Wg, wl.w_bits, synth.PHILOX_SEED, lid, synth.ALPHA)
+        del Wg
+        xq, sx, rs = ops.quant_act(torch.from_numpy(X).to(dev))
+        op = B.INTLORA_OP_MERGE_MUL if mode == "mul" else B.INTLORA_OP_MERGE_SHIFT
+        ws_bytes = max(ws_bytes, B.intlora_workspace_bytes(op, B.desc(L.d, L.n, wl.r, wl.w_bits)))
+        layers.append(dict(L=L, li=li, lid=lid, W=W, A=A, B=Bm, X=X, st=st, Ag=torch.from_numpy(A).to(dev),
+                           Bg=torch.from_numpy(Bm).to(dev), xq=xq, sx=sx, rs=rs))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    for lay in layers:
+        L = lay["L"]
+        if mode == "mul":
+            lay["out"] = dict(m=torch.empty((L.d, L.n), dtype=torch.int16, device=dev),
+                              sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
+                              zbar=torch.empty(L.d, dtype=torch.int32, device=dev),
+                              sat=torch.zeros(2, dtype=torch.int64, device=dev))
+            lay["wfmt"] = B.INTLORA_W_INT16
+        else:
+            lay["out"] = dict(m=torch.empty(ops.code_bytes(L.d, L.n, wl.w_bits), dtype=torch.uint8, device=dev),
+                              sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
+                              sat=torch.zeros(2, dtype=torch.int64, device=dev))
+            lay["wfmt"] = wl.w_bits
+        lay["Y"] = torch.empty((M, L.d), dtype=torch.int16, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t_setup
+
+    stream = torch.cuda.current_stream()
+
+    def step(events=None):
+        for k, lay in enumerate(layers):
+            if events is not None:
+                events[k][0].record(stream)
+            if mode == "mul":
+                ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
+                              ws=ws, out=lay["out"])
+            else:
+                ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
+                                ws=ws, out=lay["out"])
+            if events is not None:
+                events[k][1].record(stream)
+            ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"], lay["L"].d,
+                       out=lay["Y"])
+            if events is not None:
+                events[k][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for s in range(args.steps):
+        step(ev[s])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+
+    # ---------------------------------------------------------------- per-layer figures
+    per_layer = []
+    roof_ms = 0.0
+    merge_bytes_tot = merge_ms_tot = gemm_ops_tot = gemm_ms_tot = 0.0
+    for k, lay in enumerate(layers):
+        L = lay["L"]
+        mms = float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)]))
+        gms = float(np.mean([ev[s][k][1].elapsed_time(ev[s][k][2]) for s in range(args.steps)]))
+        mb = merge_alg_bytes(L.d, L.n, wl.r, wl.w_bits, mode)
+        gops = gemm_exec_ops(M, L.d, L.n, mode)
+        roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + gops / (INT8_PEAK_TOPS * 1e12) * 1e3
+        merge_bytes_tot += mb
+        merge_ms_tot += mms
+        gemm_ops_tot += gops
+        gemm_ms_tot += gms
+        per_layer.append(dict(layer=L.name, d=L.d, n=L.n, merge_us=round(mms * 1e3, 2),
+                              merge_alg_GBps=round(mb / (mms * 1e-3) / 1e9, 1),
+                              merge_pct_hbm=round(100 * mb / (mms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                              gemm_us=round(gms * 1e3, 2), gemm_TOPS=round(gops / (gms * 1e-3) / 1e12, 1),
+                              gemm_pct_int8_peak=round(100 * gops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+                              sat=int(lay["out"]["sat"][0].item())))
+    value = 100.0 * roof_ms / ms_per_step
+    gemm_avg_ms = gemm_ms_tot / len(layers)
+    achieved = gemm_ops_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e12
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "% of MI355X peak (step time at 8 TB/s HBM for merge bytes + 5.0 POP/s int8 for GEMM ops, "
+                "over measured step time)",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": [f"{L.name} {L.d}x{L.n}" for L in wl.layers], "tokens": M,
+                   "rank": wl.r, "w_bits": wl.w_bits, "mode": mode, "adapt_bits": mbits},
+        "roofline": {"bound": "mfma", "kernel": "k_linear (int8 MFMA, %s)" % ("int16 two-plane" if mode == "mul"
+                                                                            else "int%d" % wl.w_bits),
+                     "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profile(wl.name)},
+        "merge": {"alg_GBps": round(merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9, 1),
+                  "pct_hbm_peak": round(100 * merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                  "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (see DESIGN.md)"},
+        "gemm": {"exec_TOPS": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
+                 "effective_TOPS": round(gemm_ops_tot / (2 if mode == "mul" else 1) / (gemm_ms_tot * 1e-3) / 1e12, 1),
+                 "us_per_step": round(gemm_ms_tot * 1e3, 1)},
+        "per_layer": per_layer,
+        "setup_s": round(setup_s, 1),
+    }
+
+    # ---------------------------------------------------------------- CPU baseline (oracle)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, layers, M, mode, mbits, roof_ms, args.cpu_sample)
+    line = json.dumps(result)
+    print(line)
+    if args.json_out:
+        with open(args.json_out, "w") as fh:
+            fh.write(line + "\n")
+
+
+def cpu_baseline(wl, layers, M, mode, mbits, roof_ms, frac):
+    """The oracle, untuned, on a bounded sample of the same step: every layer's merge on
+    the first `frac` of its rows and the linear layer on the first `frac` of the tokens
+    (all outputs).  The sample's wall time is scaled by 1/frac to a full step."""
+    import oracle
+    from integer_rank_adaptation_amd import synth
+
+    threads = oracle.num_threads()
+    if frac <= 0.0:
+        frac = 1.0 / 3.0
+    t_total = 0.0
+    for lay in layers:
+        L = lay["L"]
+        # stored state of the oracle's own set-up (untimed)
+        ost = oracle.setup_layer(lay["W"], synth.PHILOX_SEED, lay["lid"], wl.w_bits, synth.ALPHA)
+        rows = max(1, int(round(L.d * frac)))
+        toks = max(1, int(round(M * frac)))
+        xq, sx, _ = oracle.quant_act(lay["X"][:toks])
+        t0 = time.perf_counter()
+        R = oracle.gen_r_rows(0, rows, L.n, synth.PHILOX_SEED, lay["lid"], ost["c"][:rows])
+        if mode == "mul":
+            ref = oracle.merge_mul(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows], lay["B"],
+                                   mbits)
+        else:
+            ref = oracle.merge_shift(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows],
+                                     lay["B"], wl.w_bits, mbits)
+        t1 = time.perf_counter()
+        # the linear layer over all outputs needs every merged row: use the sampled rows'
+        # merged integers tiled to d rows (same cost as the true d x n product)
+        m_full = np.resize(ref["m"].astype(np.int32), (L.d, L.n))
+        sbar_full = np.resize(ref["sbar"], L.d)
+        t2 = time.perf_counter()
+        oracle.linear(xq, sx, m_full, sbar_full, want_exact=False)
+        t3 = time.perf_counter()
+        t_total += (t1 - t0) * (L.d / rows) + (t3 - t2) * (M / toks)
+    value = 100.0 * roof_ms / (t_total * 1e3)
+    return {"value": round(value, 6), "unit": "% of MI355X peak (same definition; oracle step time)",
+            "cores": threads, "kind": "oracle",
+            "sample": "every layer: merge of the first %.4g of rows, linear on the first %.4g of tokens; "
+                      "scaled to a full step (%.1f s per full step)" % (frac, frac, t_total),
+            "step_s": round(t_total, 2)}
+
+
+if __name__ == "__main__":
+    main()
