@@ -16,17 +16,19 @@
 //                            exact = 256 acc_hi + acc_lo + 128 rowsum(X_q) (int64).
 //
 // Data path: every operand goes from HBM straight into LDS with buffer_load ... lds
-// (16 bytes per lane, no VGPR staging) through a 3-stage ring, so the loads of stage
-// k+2 are in flight while stage k computes.  Out-of-range rows and K chunks read as
+// (16 bytes per lane, no VGPR staging) through a 4-stage ring, so the loads of stages
+// k+2 and k+3 are in flight while stage k computes.  Out-of-range rows and K chunks read as
 // zero through the buffer descriptor.  LDS rows are XOR-swizzled in 16-byte chunks
 // (conflict-free fragment reads); the swizzle is realized by the global address each
 // lane fetches, since a direct load writes lane l's 16 bytes at base + 16 l.
 //
-// Tiling: a 256-thread block (4 waves, 2 x 2) computes 256 tokens x 128 MFMA columns
-// (128 outputs, or 64 outputs x 2 planes); each wave owns 128 x 64 = 4 x 2 tiles of
-// v_mfma_i32_32x32x32_i8 with the weight fragment as the A operand, so a lane's four
-// consecutive accumulators are four consecutive outputs of one token.  Two blocks
-// share a CU; one block's barrier overlaps the other's MFMAs.
+// Tiling: a 256-thread block (4 waves, 2 x 2) computes 256 tokens x 256 MFMA columns
+// (256 outputs, or 128 outputs x 2 planes); each wave owns 128 x 128 = 4 x 4 tiles of
+// v_mfma_i32_32x32x32_i8 (256 accumulators, one wave per SIMD) with the weight
+// fragment as the A operand, so a lane's four consecutive accumulators are four
+// consecutive outputs of one token.  A 4-stage ring keeps two stages of loads in
+// flight; the barrier of iteration k publishes stage k+1, so the first fragments of
+// the next stage are read while the current stage's MFMAs run.
 #include "device_common.h"
 #include "intlora_internal.h"
 
@@ -39,31 +41,31 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16 };
 
 namespace lin {
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;  // 4 waves: 2 (tokens) x 2 (MFMA columns), 128 x 128 per wave
 constexpr int BM = 256;        // tokens per block
 constexpr int BK = 64;         // K elements per stage
-constexpr int kStages = 3;
+constexpr int kStages = 4;
 constexpr int kGroupM = 8;     // token tiles per group of the tile order (L2 reuse)
 constexpr int A_BYTES = BM * BK;                // 16 KB
-constexpr int B_BYTES_8 = 128 * BK;             // 8 KB: 128 output rows x 64 int8
-constexpr int B_BYTES_16 = 64 * BK * 2;         // 8 KB: 64 output rows x 64 int16
-constexpr int B_BYTES_4 = 128 * BK / 2;         // 4 KB: 128 output rows x 64 nibbles
+constexpr int B_BYTES_8 = 256 * BK;             // 16 KB: 256 output rows x 64 int8
+constexpr int B_BYTES_16 = 128 * BK * 2;        // 16 KB: 128 output rows x 64 int16
+constexpr int B_BYTES_4 = 256 * BK / 2;         // 8 KB: 256 output rows x 64 nibbles
 template <int F>
 struct Cfg {
   static constexpr int B_BYTES = F == F_INT16 ? B_BYTES_16 : (F == F_INT8 ? B_BYTES_8 : B_BYTES_4);
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS = kStages * STAGE;
-  static constexpr int OUT = F == F_INT16 ? 64 : 128;          // outputs per block
+  static constexpr int OUT = F == F_INT16 ? 128 : 256;         // outputs per block
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;           // direct loads per wave per stage
   static constexpr int B_LOADS = B_BYTES / 1024 / 4;
   static constexpr int LOADS = A_LOADS + B_LOADS;
 };
 }  // namespace lin
 
-// XOR swizzles of the 16-byte chunks of an LDS row (chosen so that the 16 or 8 lanes
-// served together by a ds_read_b128 hit distinct banks, for 64- or 32-bank LDS).
-__device__ __forceinline__ int swz64(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }   // 64-byte rows
-__device__ __forceinline__ int swz128(int row) { return (row ^ (row >> 3)) & 7; }        // 128-byte rows
+// XOR swizzles of the 16-byte chunks of an LDS row, chosen by timing the fragment
+// read pattern on gfx950 (each is conflict-free there for its ds_read width).
+__device__ __forceinline__ int swz64(int row) { return (row ^ (row >> 2)) & 3; }          // 64-byte rows
+__device__ __forceinline__ int swz128(int row) { return (row ^ (row >> 2)) & 7; }         // 128-byte rows
 __device__ __forceinline__ int swz32(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }   // 32-byte rows
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
@@ -74,22 +76,30 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every record: the lane reads zeros
 
-// Issue the direct loads of one K stage into one LDS stage buffer.
+// Offset `off` if the chunk starting at K element `k` lies inside the row, else an
+// out-of-range offset (the lane reads zeros).  Branch-free 32-bit arithmetic.
+__device__ __forceinline__ uint32_t in_row(uint32_t off, int k, int n) {
+  const uint32_t keep = (uint32_t)((k - n) >> 31);  // all ones when k < n
+  return (off & keep) | (kOOB & ~keep);
+}
+
+// Issue the direct loads of one K stage into one LDS stage buffer.  Row and column
+// offsets fit in 32 bits (the descriptors are based at the block's first row).
 template <int F>
-__device__ __forceinline__ void issue_stage(int kt, int64_t n, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+__device__ __forceinline__ void issue_stage(int kt, int n, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
                                             uint8_t* stage) {
   using namespace lin;
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t k0 = (int64_t)kt * BK;
+  const int lane = threadIdx.x & 63;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int k0 = kt * BK;
   // A (tokens): 16 rows of 64 bytes per direct load
 #pragma unroll
   for (int q = 0; q < Cfg<F>::A_LOADS; ++q) {
     const int g = wid * Cfg<F>::A_LOADS + q;
     const int row = 16 * g + (lane >> 2);
-    const int c = (lane & 3) ^ swz64(row);
-    const int64_t kb = k0 + 16 * c;
-    const uint32_t off = kb < n ? (uint32_t)(row * n + kb) : kOOB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + g * 1024), 16, off, 0, 0, 0);
+    const int k = k0 + 16 * ((lane & 3) ^ swz64(row));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + g * 1024), 16,
+                                             in_row((uint32_t)(row * n + k), k, n), 0, 0, 0);
   }
   uint8_t* Bs = stage + A_BYTES;
   if (F == F_INT8) {
@@ -97,30 +107,27 @@ __device__ __forceinline__ void issue_stage(int kt, int64_t n, __amdgpu_buffer_r
     for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
       const int g = wid * Cfg<F>::B_LOADS + q;
       const int row = 16 * g + (lane >> 2);
-      const int c = (lane & 3) ^ swz64(row);
-      const int64_t kb = k0 + 16 * c;
-      const uint32_t off = kb < n ? (uint32_t)(row * n + kb) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16, off, 0, 0, 0);
+      const int k = k0 + 16 * ((lane & 3) ^ swz64(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16,
+                                               in_row((uint32_t)(row * n + k), k, n), 0, 0, 0);
     }
   } else if (F == F_INT16) {
 #pragma unroll
     for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
       const int g = wid * Cfg<F>::B_LOADS + q;
       const int row = 8 * g + (lane >> 3);          // 128-byte rows (64 int16)
-      const int c = (lane & 7) ^ swz128(row);
-      const int64_t ke = k0 + 8 * c;                // first K element of the chunk
-      const uint32_t off = ke < n ? (uint32_t)(2 * (row * n + ke)) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16, off, 0, 0, 0);
+      const int k = k0 + 8 * ((lane & 7) ^ swz128(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16,
+                                               in_row((uint32_t)(2 * (row * n + k)), k, n), 0, 0, 0);
     }
   } else {  // F_INT4: 32-byte rows (64 nibbles)
 #pragma unroll
     for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
       const int g = wid * Cfg<F>::B_LOADS + q;
       const int row = 32 * g + (lane >> 1);
-      const int c = (lane & 1) ^ swz32(row);
-      const int64_t ke = k0 + 32 * c;
-      const uint32_t off = ke < n ? (uint32_t)(row * (n >> 1) + (ke >> 1)) : kOOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16, off, 0, 0, 0);
+      const int k = k0 + 32 * ((lane & 1) ^ swz32(row));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16,
+                                               in_row((uint32_t)(row * (n >> 1) + (k >> 1)), k, n), 0, 0, 0);
     }
   }
 }
@@ -139,8 +146,56 @@ __device__ __forceinline__ void unpack4(uint32_t x, uint32_t& o0, uint32_t& o1) 
   o1 = __builtin_amdgcn_perm(H, L, 0x07030602u);
 }
 
+// Fragments of one K sub-step: A (tokens) for 4 tiles and B (weights) for 4 MFMA
+// column tiles; sub-step ks of lane half h covers K 32 h + 16 ks .. + 16 of the stage.
 template <int F>
-__global__ __launch_bounds__(lin::kThreads, 2) void k_linear(int64_t M, int64_t d, int64_t n,
+__device__ __forceinline__ void read_frags(const uint8_t* __restrict__ As, int wm, int wn, int ks, int fr, int h,
+                                           v4i (&af)[4], v4i (&bf)[4]) {
+  using namespace lin;
+  const uint8_t* Bs = As + A_BYTES;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = wm * 128 + i * 32 + fr;
+    af[i] = *reinterpret_cast<const v4i*>(As + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
+  }
+  if (F == F_INT8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + fr;
+      bf[j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
+    }
+  } else if (F == F_INT16) {
+    // two output tiles of 32; tile q gives MFMA column tiles 2q (hi plane), 2q+1 (lo plane)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int row = wn * 64 + q * 32 + fr;
+      const int c0 = 4 * h + 2 * ks;
+      const v4i r0 = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c0 ^ swz128(row)) << 4));
+      const v4i r1 = *reinterpret_cast<const v4i*>(Bs + row * 128 + (((c0 + 1) ^ swz128(row)) << 4));
+      const uint32_t x[8] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w,
+                             (uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
+      // little-endian int16: the high byte of each value is byte 1 or 3 of its dword
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bf[2 * q][e] = (int)__builtin_amdgcn_perm(x[2 * e + 1], x[2 * e], 0x07050301u);
+        bf[2 * q + 1][e] = (int)(__builtin_amdgcn_perm(x[2 * e + 1], x[2 * e], 0x06040200u) ^ 0x80808080u);
+      }
+    }
+  } else {  // F_INT4: 8 packed bytes per lane and sub-step (half of the lane's 16-byte chunk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + fr;
+      const uint2 r = *reinterpret_cast<const uint2*>(Bs + row * 32 + ((h ^ swz32(row)) << 4) + 8 * ks);
+      uint32_t o0_, o1_, o2_, o3_;
+      unpack4(r.x, o0_, o1_);
+      unpack4(r.y, o2_, o3_);
+      bf[j] = v4i{(int)o0_, (int)o1_, (int)o2_, (int)o3_};
+    }
+  }
+}
+
+template <int F>
+__global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t d, int64_t n,
                                                             const int8_t* __restrict__ xq,
                                                             const float* __restrict__ sx,
                                                             const int32_t* __restrict__ rowsum,
@@ -179,163 +234,165 @@ __global__ __launch_bounds__(lin::kThreads, 2) void k_linear(int64_t M, int64_t 
   const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
   const __amdgpu_buffer_rsrc_t rb = make_rsrc(m + o0 * wrow, (d - o0) * wrow);
 
-  v16i acc[4][2];
+  v16i acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
   const int KT = (int)((n + BK - 1) / BK);
-  issue_stage<F>(0, n, ra, rb, lds);
-  if (KT > 1) issue_stage<F>(1, n, ra, rb, lds + STAGE);
-
   const int fr = lane & 31, h = lane >> 5;
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage kt has landed once at most the next stage's loads are outstanding
-    if (kt + 1 < KT)
-      wait_vmcnt<Cfg<F>::LOADS>();
-    else
-      wait_vmcnt<0>();
-    // Every wave has its own loads of stage kt in LDS (vmcnt above); after the barrier
-    // all waves' are, and no wave still reads the buffer the next issue overwrites.
-    // A bare s_barrier: a fence here would also wait for the loads of stage kt+1.
-    __builtin_amdgcn_s_barrier();
-    if (kt + 2 < KT) issue_stage<F>(kt + 2, n, ra, rb, lds + ((kt + 2) % kStages) * STAGE);
-    const uint8_t* As = lds + (kt % kStages) * STAGE;
-    const uint8_t* Bs = As + A_BYTES;
+  // The loop body is one basic block so that the schedule below holds: stages past
+  // the end are still issued, every lane of them reading zeros (out-of-range offset)
+  // into a ring buffer that is never read again, and the fragment reads of stage k+1
+  // at the last iteration fetch unused data.  vmcnt accounting is then uniform.
+  issue_stage<F>(0, (int)n, ra, rb, lds);
+  issue_stage<F>(1, (int)n, ra, rb, lds + STAGE);
+  issue_stage<F>(2, (int)n, ra, rb, lds + 2 * STAGE);
+  wait_vmcnt<2 * Cfg<F>::LOADS>();
+  __builtin_amdgcn_s_barrier();
+  v4i af0[4], bf0[4], af1[4], bf1[4];
+  read_frags<F>(lds, wm, wn, 0, fr, h, af0, bf0);
 
-    // B fragments for both K sub-steps (sub-step ks of lane half h covers K 32h + 16ks ...)
-    v4i bf[2][2];  // [ks][j]
-    if (F == F_INT8) {
+  // Per iteration: the loads of stage k+3 and the reads of sub-step 1 are issued in
+  // the shadow of the first eight MFMAs of sub-step 0; the reads of stage k+1 sub-step
+  // 0 in the shadow of the first eight MFMAs of sub-step 1; VALU fragment conversion
+  // (INT16 byte split, INT4 unpack) after them.
+  constexpr int kValu = F == F_INT16 ? 3 : (F == F_INT4 ? 5 : 0);
+  for (int kt = 0; kt < KT; ++kt) {
+    // stage kt+1 has landed (loads of kt+2 may still be in flight); after the barrier
+    // it is visible to all waves and nobody reads stage kt-1, whose buffer kt+3 reuses
+    wait_vmcnt<Cfg<F>::LOADS>();
+    __builtin_amdgcn_s_barrier();
+    issue_stage<F>(kt + 3, (int)n, ra, rb, lds + ((kt + 3) % kStages) * STAGE);
+    const uint8_t* As = lds + (kt % kStages) * STAGE;
+    read_frags<F>(As, wm, wn, 1, fr, h, af1, bf1);
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wn * 64 + j * 32 + fr;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-          bf[ks][j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
-      }
-    } else if (F == F_INT16) {
-      const int row = wn * 32 + fr;
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf0[j], af0[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        const int c0 = 4 * h + 2 * ks;
-        const v4i r0 = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c0 ^ swz128(row)) << 4));
-        const v4i r1 = *reinterpret_cast<const v4i*>(Bs + row * 128 + (((c0 + 1) ^ swz128(row)) << 4));
-        const uint32_t x[8] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w,
-                               (uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
-        // little-endian int16: the high byte of each value is byte 1 or 3 of its dword
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          bf[ks][0][q] = (int)__builtin_amdgcn_perm(x[2 * q + 1], x[2 * q], 0x07050301u);
-          bf[ks][1][q] = (int)(__builtin_amdgcn_perm(x[2 * q + 1], x[2 * q], 0x06040200u) ^ 0x80808080u);
-        }
-      }
-    } else {  // F_INT4: one 16-byte chunk per lane holds both sub-steps
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int row = wn * 64 + j * 32 + fr;
-        const v4i r = *reinterpret_cast<const v4i*>(Bs + row * 32 + ((h ^ swz32(row)) << 4));
-        uint32_t o0_, o1_, o2_, o3_;
-        unpack4((uint32_t)r.x, o0_, o1_);
-        unpack4((uint32_t)r.y, o2_, o3_);
-        bf[0][j] = v4i{(int)o0_, (int)o1_, (int)o2_, (int)o3_};
-        unpack4((uint32_t)r.z, o0_, o1_);
-        unpack4((uint32_t)r.w, o2_, o3_);
-        bf[1][j] = v4i{(int)o0_, (int)o1_, (int)o2_, (int)o3_};
-      }
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      v4i af[4];
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+    }
+    read_frags<F>(lds + ((kt + 1) % kStages) * STAGE, wm, wn, 0, fr, h, af0, bf0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 128 + i * 32 + fr;
-        af[i] = *reinterpret_cast<const v4i*>(As + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
-      }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf1[j], af1[i], acc[i][j], 0, 0, 0);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[ks][j], af[i], acc[i][j], 0, 0, 0);
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
+      if (kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 1);
     }
   }
+  wait_vmcnt<0>();  // the trailing zero-reading loads land before LDS is reused
 
-  // Epilogue straight from the accumulators: lane l, register r of tile (i, j) holds
-  // token t0 + wm*128 + 32 i + (l % 32) and MFMA column 8 (r / 4) + 4 (l / 32) + r % 4
-  // of tile j; four consecutive registers are four consecutive outputs of one token.
-  const int tok_in = lane & 31;
-  const int colq = 4 * (lane >> 5);
+  // Epilogue, one 32-token slab (i) at a time through LDS: each wave writes its 32 x 128
+  // int32 accumulators as 16-byte groups (lane l, registers 4a..4a+3 of tile j are
+  // token l % 32, MFMA columns 32 j + 8 a + 4 (l / 32) + 0..3) into a padded region of
+  // its own, then reads them back row-contiguously; each lane finishes four outputs.
+  __syncthreads();
+  constexpr int RS = 132;  // padded row stride (ints): conflict-free 16-byte accesses
+  int32_t* R = reinterpret_cast<int32_t*>(lds) + wid * (32 * RS);
   const bool vec_ok = (d & 3) == 0;
-  float sxt[4];
-  int64_t rs128[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t tok = t0 + wm * 128 + i * 32 + tok_in;
-    sxt[i] = tok < M ? sx[tok] : 0.0f;
-    rs128[i] = (F == F_INT16 && tok < M) ? 128 * (int64_t)rowsum[tok] : 0;
-  }
-  constexpr int NJ = (F == F_INT16) ? 1 : 2;  // column tiles (INT16: one output tile, two planes)
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) {
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-      const int64_t c0 = o0 + wn * ((F == F_INT16) ? 32 : 64) + j * 32 + 8 * a + colq;
+      for (int a = 0; a < 4; ++a)
+        *reinterpret_cast<v4i*>(R + fr * RS + j * 32 + 8 * a + 4 * h) =
+            v4i{acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
+    // (a wave's LDS accesses complete in order: its own reads below see these writes)
+    const int64_t tok_base = t0 + wm * 128 + i * 32;
+    if (F == F_INT16) {
+      // region row: [hi 0..31 | lo 0..31 | hi 32..63 | lo 32..63] of the wave's 64 outputs
+      const int o = 4 * (lane & 15);                 // first of four outputs of this lane
+      const int hcol = (o >> 5) * 64 + (o & 31);
+      const int64_t c0 = o0 + wn * 64 + o;
       const bool full = vec_ok && c0 + 3 < d;
-      float4 sb = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (full) {
-        sb = *reinterpret_cast<const float4*>(sbar + c0);
-      } else {
-        if (c0 < d) sb.x = sbar[c0];
-        if (c0 + 1 < d) sb.y = sbar[c0 + 1];
-        if (c0 + 2 < d) sb.z = sbar[c0 + 2];
-        if (c0 + 3 < d) sb.w = sbar[c0 + 3];
-      }
-      const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t tok = t0 + wm * 128 + i * 32 + tok_in;
-        if (tok >= M) continue;
-        int e0[4], e1[4];
+      for (int rr = 0; rr < 32; rr += 4) {
+        const int row = rr + (lane >> 4);
+        const int64_t tok = tok_base + row;
+        if (tok >= M || c0 >= d) continue;
+        const v4i hi = *reinterpret_cast<const v4i*>(R + row * RS + hcol);
+        const v4i lo = *reinterpret_cast<const v4i*>(R + row * RS + hcol + 32);
+        const int64_t rs128 = 128 * (int64_t)rowsum[tok];
+        const float sxt = sx[tok];
         uint32_t hv[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          float y;
-          if (F == F_INT16) {
-            e0[b] = acc[i][0][4 * a + b];
-            e1[b] = acc[i][1][4 * a + b];
-            const int64_t exact = 256 * (int64_t)e0[b] + (int64_t)e1[b] + rs128[i];
-            y = (float)(double)exact;
-          } else {
-            const int v = acc[i][j][4 * a + b];
-            e0[b] = (F == F_INT4) ? (v >> 4) : v;
-            y = (float)e0[b];
-          }
-          y = y * sxt[i];
-          y = y * sbv[b];
+          const int64_t exact = 256 * (int64_t)hi[b] + (int64_t)lo[b] + rs128;
+          float y = (float)(double)exact;
+          y = y * sxt;
+          y = y * (c0 + b < d ? sbar[c0 + b] : 0.0f);
           hv[b] = bf16_rne(y);
         }
         uint16_t* Yp = Y + tok * d + c0;
-        int32_t* D0 = acc_dbg ? acc_dbg + tok * d + c0 : nullptr;
-        int32_t* D1 = acc_dbg ? acc_dbg + M * d + tok * d + c0 : nullptr;
         if (full) {
           *reinterpret_cast<uint2*>(Yp) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
-          if (D0) {
-            *reinterpret_cast<int4*>(D0) = make_int4(e0[0], e0[1], e0[2], e0[3]);
-            if (F == F_INT16) *reinterpret_cast<int4*>(D1) = make_int4(e1[0], e1[1], e1[2], e1[3]);
+          if (acc_dbg) {
+            *reinterpret_cast<v4i*>(acc_dbg + tok * d + c0) = hi;
+            *reinterpret_cast<v4i*>(acc_dbg + M * d + tok * d + c0) = lo;
           }
         } else {
 #pragma unroll
-          for (int b = 0; b < 4; ++b) {
+          for (int b = 0; b < 4; ++b)
             if (c0 + b < d) {
               Yp[b] = (uint16_t)hv[b];
-              if (D0) {
-                D0[b] = e0[b];
-                if (F == F_INT16) D1[b] = e1[b];
+              if (acc_dbg) {
+                acc_dbg[tok * d + c0 + b] = hi[b];
+                acc_dbg[M * d + tok * d + c0 + b] = lo[b];
               }
             }
-          }
+        }
+      }
+    } else {
+      const int cc = 4 * (lane & 31);                // first of four columns of this lane
+      const int64_t c0 = o0 + wn * 128 + cc;
+      const bool full = vec_ok && c0 + 3 < d;
+      for (int rr = 0; rr < 32; rr += 2) {
+        const int row = rr + (lane >> 5);
+        const int64_t tok = tok_base + row;
+        if (tok >= M || c0 >= d) continue;
+        const v4i v = *reinterpret_cast<const v4i*>(R + row * RS + cc);
+        const float sxt = sx[tok];
+        int ex[4];
+        uint32_t hv[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          ex[b] = (F == F_INT4) ? (v[b] >> 4) : v[b];
+          float y = (float)ex[b];
+          y = y * sxt;
+          y = y * (c0 + b < d ? sbar[c0 + b] : 0.0f);
+          hv[b] = bf16_rne(y);
+        }
+        uint16_t* Yp = Y + tok * d + c0;
+        if (full) {
+          *reinterpret_cast<uint2*>(Yp) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+          if (acc_dbg) *reinterpret_cast<v4i*>(acc_dbg + tok * d + c0) = v4i{ex[0], ex[1], ex[2], ex[3]};
+        } else {
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (c0 + b < d) {
+              Yp[b] = (uint16_t)hv[b];
+              if (acc_dbg) acc_dbg[tok * d + c0 + b] = ex[b];
+            }
         }
       }
     }
