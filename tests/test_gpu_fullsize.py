@@ -1,0 +1,109 @@
+"""GPU parity at the full layer sizes of every workload, on sampled outputs (marker `gpu`).
+
+The GPU runs the whole path exactly as the benchmark launches it (set-up, merge,
+activation quantization, integer linear layer over all rows and tokens).  Every step
+of set-up and merge is row-local (per-row statistics; R depends on (seed, layer, i, j)
+only), so the oracle recomputes a sample of rows from the raw inputs of those rows
+alone, and the linear layer's outputs at (sampled token, sampled row) pairs.  All
+sampled values must be bit-identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from integer_rank_adaptation_amd import synth
+from tests.test_gpu_parity import bits, cuda, host, unpack4, unpack4s
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def ops():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from integer_rank_adaptation_amd import ops as _ops
+
+    _ops.B.lib()
+    return _ops
+
+
+def sample_rows(d, k, seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rows = {0, d - 1} | set(rng.choice(d, size=min(k, d), replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def check_layer(ops, wl, li, L, Ms, mode, mbits, block=0, n_rows=6, n_tok=6):
+    lid = synth.layer_id(wl.index, li, block)
+    W = synth.weight(wl, li, block=block)
+    A, Bm = synth.lora(wl, li, block=block)
+    seed = synth.PHILOX_SEED
+    st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+    if mode == "mul":
+        g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid, dbg=True)
+    else:
+        g = ops.merge_shift(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid, dbg=True)
+    rows = sample_rows(L.d, n_rows, 7 * li + block)
+    # oracle on the sampled rows only (row-local set-up and merge)
+    sig = oracle.sigma_w(W[rows])
+    c = oracle.vmc_scale(sig, synth.ALPHA)
+    R = np.concatenate([oracle.gen_r_rows(int(i), 1, L.n, seed, lid, c[k:k + 1]) for k, i in enumerate(rows)])
+    wr, z, s = oracle.base_quant(W[rows], R, wl.w_bits)
+    gwr = host(st["wround"])
+    gwr = unpack4(gwr) if wl.w_bits == 4 else gwr
+    assert np.array_equal(bits(host(st["c"])[rows]), bits(c))
+    assert np.array_equal(gwr[rows], wr)
+    assert np.array_equal(host(st["z"])[rows], z)
+    assert np.array_equal(bits(host(st["s"])[rows]), bits(s))
+    if mode == "mul":
+        ref = oracle.merge_mul(wr, z, s, R, A[rows], Bm, mbits)
+        m_all = host(g["m"])
+        assert np.array_equal(host(g["uround"])[rows], ref["uround"])
+        assert np.array_equal(host(g["zbar"])[rows], ref["zbar"])
+        m_rows = m_all[rows]
+        wfmt = 16
+    else:
+        ref = oracle.merge_shift(wr, z, s, R, A[rows], Bm, wl.w_bits, mbits)
+        m_all = host(g["m"])
+        m_all = unpack4s(m_all) if wl.w_bits == 4 else m_all.view(np.int8)
+        m_rows = m_all[rows]
+        assert np.array_equal(host(g["shift"])[rows], ref["shift"])
+        wfmt = wl.w_bits
+    assert np.array_equal(m_rows, ref["m"]), (wl.name, L.name, mode)
+    assert np.array_equal(bits(host(g["sbar"])[rows]), bits(ref["sbar"]))
+    # linear layer: every token and output on the GPU; oracle at sampled (t, i)
+    for M in Ms:
+        X = synth.activations(wl, L.n, M, li)
+        xq, sx, rs = ops.quant_act(cuda(X))
+        Y, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], L.d)
+        toks = sample_rows(M, n_tok, 11 * li + M)
+        oxq, osx, _ = oracle.quant_act(X[toks])
+        assert np.array_equal(host(xq)[toks], oxq)
+        assert np.array_equal(bits(host(sx)[toks]), bits(osx))
+        tt, ii = np.meshgrid(np.arange(toks.size), np.arange(rows.size), indexing="ij")
+        exact, y = oracle.linear_sampled(tt.ravel(), ii.ravel(), oxq, osx, ref["m"].astype(np.int32), ref["sbar"])
+        Yh = host(Y).view(np.uint16)
+        got = Yh[np.ix_(toks, rows)].ravel()
+        assert np.array_equal(got, y), (wl.name, L.name, mode, M)
+    return int(host(g["sat"])[0])
+
+
+@pytest.mark.parametrize("wl_index", [0, 1, 2, 3, 4])
+def test_workload_full_size_sampled(ops, wl_index):
+    wl = synth.WORKLOADS[wl_index]
+    for li, L in enumerate(wl.layers):
+        for mode, mbits in wl.modes:
+            check_layer(ops, wl, li, L, wl.tokens, mode, mbits)
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("block", [1, 31])
+def test_llama_sweep_blocks_sampled(ops, block):
+    """The merge-only sweep of the Llama-shaped workload: other transformer blocks use
+    other layer ids (7 * block + matrix); sampled rows of every matrix."""
+    wl = synth.WORKLOADS[4]
+    mode, mbits = wl.modes[0]
+    for li, L in enumerate(wl.layers):
+        check_layer(ops, wl, li, L, (16,), mode, mbits, block=block, n_rows=4, n_tok=2)
+    torch.cuda.empty_cache()
