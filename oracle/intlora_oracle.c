@@ -235,9 +235,16 @@ static int u_element(int64_t i, int64_t j, int64_t n, int r, const uint8_t* wrou
     return 1;
 }
 
+/* a < b in the IEEE total order (-0 below +0); operands are never NaN. */
+static int total_less(float a, float b) {
+    if (a < b) return 1;
+    return a == b && signbit(a) && !signbit(b);
+}
+
 /* U for every element (NaN marks w == 0, when u_out is given) and the row
- * range over valid elements (U_min = +inf, U_max = -inf for a row with no
- * valid element). */
+ * range over valid elements: the least and greatest U in the IEEE total order
+ * (so a zero extreme is -0 if any valid U is -0); U_min = +inf, U_max = -inf for
+ * a row with no valid element. */
 ORA_API void ora_adaptation(int64_t rows, int64_t n, int r, const uint8_t* wround, const int32_t* z, const float* s,
                             const float* rstar, const float* A, const float* B, float* u_out, float* umin_out,
                             float* umax_out) {
@@ -251,8 +258,8 @@ ORA_API void ora_adaptation(int64_t rows, int64_t n, int r, const uint8_t* wroun
                 continue;
             }
             if (u_out) u_out[i * n + j] = u;
-            if (u < umin) umin = u;
-            if (u > umax) umax = u;
+            if (total_less(u, umin)) umin = u;
+            if (total_less(umax, u)) umax = u;
         }
         umin_out[i] = umin;
         umax_out[i] = umax;

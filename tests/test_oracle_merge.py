@@ -272,3 +272,20 @@ def test_workload_merge_has_no_saturation(ora, wl_index):
         else:
             out = ora.merge_shift(st["wround"], st["z"], st["s"], st["rstar"], A, B, wl.w_bits, bits)
         assert out["sat"] <= d  # the only SHIFT saturation is the sign flip of -2^(b-1)
+
+
+def test_u_range_zero_extremes(ora):
+    """The row range is taken in the IEEE total order.  With s > 0 a zero U is always
+    +0 (s + (-s) rounds to +0), so a zero extreme must come out as +0 in any column
+    order; here U_max is zero in both rows, reached at different columns."""
+    rows, n = 2, 4
+    wr = np.array([[3, 4, 5, 6], [6, 5, 4, 3]], np.uint8)
+    z = np.array([4, 4], np.int32)               # w = [-1, 0, 1, 2] and [2, 1, 0, -1]
+    s = np.array([1.0, 1.0], np.float32)
+    A = np.zeros((rows, 1), np.float32)
+    Bm = np.zeros((1, n), np.float32)
+    Rs = np.array([[1.0, 0.0, -1.0, -4.0], [-4.0, -1.0, 0.0, 1.0]], np.float32)
+    u, umin, umax = ora.adaptation(wr, z, s, Rs, A, Bm)
+    # valid U: 1 + 1/-1 = +0, 1 + -1/1 = +0, 1 + -4/2 = -1 (w = 0 excluded)
+    assert umax[0] == 0.0 and not np.signbit(umax[0]) and umin[0] == -1.0
+    assert umax[1] == 0.0 and not np.signbit(umax[1]) and umin[1] == -1.0
