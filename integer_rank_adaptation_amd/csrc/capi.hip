@@ -76,8 +76,8 @@ int check_opt(const void* p, const char* what) {
 // Workspace layout of the merge / U statistics: U (d*n fp32) | pmin | pmax (d*ntiles fp32 each)
 struct MergeWs {
   float* U;
-  float* pmin;
-  float* pmax;
+  int* pmin;
+  int* pmax;
   int ntiles;
 };
 
@@ -94,9 +94,9 @@ MergeWs carve(void* ws, int64_t d, int64_t n) {
   uint8_t* p = static_cast<uint8_t*>(ws);
   w.U = reinterpret_cast<float*>(p);
   p += align256((size_t)d * (size_t)n * 4);
-  w.pmin = reinterpret_cast<float*>(p);
+  w.pmin = reinterpret_cast<int*>(p);
   p += align256((size_t)d * (size_t)w.ntiles * 4);  // capacity; the kernels use <= ntiles per row
-  w.pmax = reinterpret_cast<float*>(p);
+  w.pmax = reinterpret_cast<int*>(p);
   return w;
 }
 

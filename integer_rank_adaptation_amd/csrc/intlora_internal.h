@@ -18,8 +18,8 @@ struct AdaptArgs {
   const float* A;
   const float* B;
   float* U;
-  float* pmin;
-  float* pmax;
+  int* pmin;  // per (row, column tile) order keys of the U range
+  int* pmax;
   unsigned long long* sat_zero;  // zeroed by the adaptation kernel (nullable)
   bool force_generic;
 };
@@ -38,14 +38,14 @@ hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint
 hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* sx, int32_t* rowsum,
                             hipStream_t st);
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st);
-hipError_t launch_row_range(int64_t d, int ntiles, const float* pmin, const float* pmax, float* umin, float* umax,
+hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
                             hipStream_t st);
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
-                            const float* U, const float* pmin, const float* pmax, int ntiles, int16_t* m,
+                            const float* U, const int* pmin, const int* pmax, int ntiles, int16_t* m,
                             float* sbar, int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat,
                             hipStream_t st);
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
-                              const float* U, const float* pmin, const float* pmax, int ntiles, uint8_t* m,
+                              const float* U, const int* pmin, const int* pmax, int ntiles, uint8_t* m,
                               float* sbar, uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st);
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st);

@@ -219,17 +219,45 @@ constexpr int kAdaptCols = 1024;  // tile width of the generic path and of CPT =
 constexpr int kAdaptMinCols = 512;
 constexpr int kAdaptRows = 8;
 
+// Reciprocals RN32(1/w) of the signed pretrained integers w in [-255, 255] (0 for
+// w = 0), for the division t / w below.
+__device__ __forceinline__ void load_rcp_table(float* rcp) {
+  for (int t = threadIdx.x; t < 511; t += blockDim.x) {
+    const int w = t - 255;
+    rcp[t] = w == 0 ? 0.0f : 1.0f / (float)w;
+  }
+}
+
+// t / w, correctly rounded, for an integer 1 <= |w| <= 255 with y = RN32(1/w):
+// q0 = RN(t y), r = t - q0 w (exact with a fused multiply-add), q = RN(q0 + r y).
+// An exhaustive check over every binary32 significand of t and every such w shows
+// q == RN(t / w); every step scales exactly with t's exponent, so this holds for all
+// |t| in [2^-100, 2^100].  Outside that range the IEEE division is used.
+__device__ __forceinline__ float div_small_int(float t, float wf, float y) {
+  const float q0 = t * y;
+  const float r = fmaf(-q0, wf, t);
+  float q = fmaf(r, y, q0);
+  const float at = fabsf(t);
+  if (!(at >= 0x1p-100f && at <= 0x1p100f)) q = t / wf;
+  return q;
+}
+
+constexpr int kKeyPosInf = 0x7F800000;  // order key of +inf (identity of min)
+constexpr int kKeyNegInf = (int)0x807FFFFF;  // order key of -inf (identity of max)
+
 template <int R, int CPT, bool W4>
-__global__ __launch_bounds__(256) void k_adapt_fast(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
+__global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
                                                    const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
                                                    const float* __restrict__ s, const float* __restrict__ c,
                                                    const float* __restrict__ A, const float* __restrict__ B,
-                                                   float* __restrict__ U, float* __restrict__ pmin,
-                                                   float* __restrict__ pmax, int ntiles,
+                                                   float* __restrict__ U, int* __restrict__ pmin,
+                                                   int* __restrict__ pmax, int ntiles,
                                                    unsigned long long* __restrict__ sat_zero) {
   __shared__ LnEntry tab[96];
-  __shared__ float smin[4][kAdaptRows], smax[4][kAdaptRows];
+  __shared__ float rcp[511];
+  __shared__ int smin[4][kAdaptRows], smax[4][kAdaptRows];
   load_ln_table(tab);
+  load_rcp_table(rcp);
   if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
   __syncthreads();
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -252,7 +280,7 @@ __global__ __launch_bounds__(256) void k_adapt_fast(int64_t d, int64_t n, uint64
   for (int ii = 0; ii < kAdaptRows; ++ii) {
     const int64_t i = i_begin + ii;
     if (i >= d) break;
-    float lmin = __builtin_inff(), lmax = -__builtin_inff();
+    int kmin = kKeyPosInf, kmax = kKeyNegInf;
     if (active) {
       int w[CPT];
       const int zi = z[i];
@@ -269,7 +297,7 @@ __global__ __launch_bounds__(256) void k_adapt_fast(int64_t d, int64_t n, uint64
       }
       const uint64_t q0 = (uint64_t)i * (uint64_t)n + (uint64_t)j0;
       const U4 rnd = philox_block(q0 >> 2, layer_id, seed);
-      const unsigned wsel = (unsigned)(q0 & 3);  // 0 for CPT = 4; 0 or 2 for CPT = 2
+      const unsigned wsel = CPT == 4 ? 0u : (unsigned)(q0 & 3);  // first word of this thread (0 or 2 when CPT = 2)
       const float ci = c[i], si = s[i];
       const float* Ai = A + i * R;
       float u[CPT];
@@ -278,27 +306,27 @@ __global__ __launch_bounds__(256) void k_adapt_fast(int64_t d, int64_t n, uint64
         float acc = 0.0f;
 #pragma unroll
         for (int k = 0; k < R; ++k) acc = fmaf(Ai[k], b[k][e], acc);
-        const float rs = ci * laplace_from_word(pick_word(rnd, wsel + e), tab);
+        const uint32_t word = CPT == 4 ? pick_word(rnd, e) : (wsel == 0 ? pick_word(rnd, e) : pick_word(rnd, 2 + e));
+        const float rs = ci * laplace_from_word(word, tab);
         const float t = rs + acc;
         const bool valid = w[e] != 0;
-        const float q = t / (float)(valid ? w[e] : 1);
+        const float q = div_small_int(t, (float)w[e], rcp[w[e] + 255]);
         const float uu = si + q;
         u[e] = valid ? uu : 0.0f;
-        if (valid) {
-          lmin = fminf(lmin, uu);
-          lmax = fmaxf(lmax, uu);
-        }
+        const int key = f32_key(uu);
+        kmin = valid ? min(kmin, key) : kmin;
+        kmax = valid ? max(kmax, key) : kmax;
       }
       if (CPT == 4)
         *reinterpret_cast<float4*>(U + i * n + j0) = make_float4(u[0], u[1], u[2 % CPT], u[3 % CPT]);
       else
         *reinterpret_cast<float2*>(U + i * n + j0) = make_float2(u[0], u[1]);
     }
-    lmin = wave_min(lmin);
-    lmax = wave_max(lmax);
+    kmin = wave_min_i32(kmin);
+    kmax = wave_max_i32(kmax);
     if (lane == 0) {
-      smin[wid][ii] = lmin;
-      smax[wid][ii] = lmax;
+      smin[wid][ii] = kmin;
+      smax[wid][ii] = kmax;
     }
   }
   __syncthreads();
@@ -306,8 +334,8 @@ __global__ __launch_bounds__(256) void k_adapt_fast(int64_t d, int64_t n, uint64
     const int64_t i = i_begin + threadIdx.x;
     if (i < d) {
       const int t = threadIdx.x;
-      pmin[i * ntiles + blockIdx.x] = fminf(fminf(smin[0][t], smin[1][t]), fminf(smin[2][t], smin[3][t]));
-      pmax[i * ntiles + blockIdx.x] = fmaxf(fmaxf(smax[0][t], smax[1][t]), fmaxf(smax[2][t], smax[3][t]));
+      pmin[i * ntiles + blockIdx.x] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
+      pmax[i * ntiles + blockIdx.x] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
     }
   }
 }
@@ -319,16 +347,16 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
                                                       const int32_t* __restrict__ z, const float* __restrict__ s,
                                                       const float* __restrict__ c, const float* __restrict__ A,
                                                       const float* __restrict__ B, float* __restrict__ U,
-                                                      float* __restrict__ pmin, float* __restrict__ pmax, int ntiles,
+                                                      int* __restrict__ pmin, int* __restrict__ pmax, int ntiles,
                                                       unsigned long long* __restrict__ sat_zero) {
   __shared__ LnEntry tab[96];
-  __shared__ float smin[4], smax[4];
+  __shared__ int smin[4], smax[4];
   load_ln_table(tab);
   if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
   __syncthreads();
   const int64_t i = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  float lmin = __builtin_inff(), lmax = -__builtin_inff();
+  int kmin = kKeyPosInf, kmax = kKeyNegInf;
   const int64_t jt = (int64_t)blockIdx.x * kAdaptCols;
   for (int64_t j = jt + threadIdx.x; j < jt + kAdaptCols && j < n; j += 256) {
     int code;
@@ -348,37 +376,40 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
     const float uu = s[i] + q;
     U[i * n + j] = valid ? uu : 0.0f;
     if (valid) {
-      lmin = fminf(lmin, uu);
-      lmax = fmaxf(lmax, uu);
+      kmin = min(kmin, f32_key(uu));
+      kmax = max(kmax, f32_key(uu));
     }
   }
-  lmin = wave_min(lmin);
-  lmax = wave_max(lmax);
+  kmin = wave_min_i32(kmin);
+  kmax = wave_max_i32(kmax);
   if (lane == 0) {
-    smin[wid] = lmin;
-    smax[wid] = lmax;
+    smin[wid] = kmin;
+    smax[wid] = kmax;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    pmin[i * ntiles + blockIdx.x] = fminf(fminf(smin[0], smin[1]), fminf(smin[2], smin[3]));
-    pmax[i * ntiles + blockIdx.x] = fmaxf(fmaxf(smax[0], smax[1]), fmaxf(smax[2], smax[3]));
+    pmin[i * ntiles + blockIdx.x] = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
+    pmax[i * ntiles + blockIdx.x] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
   }
 }
 
-// Row range from the tile partials (uniform per block).
-__device__ __forceinline__ void row_range(const float* __restrict__ pmin, const float* __restrict__ pmax, int64_t i,
+// Row range from the tile partials (order keys; uniform per block).  U_min / U_max
+// are the least / greatest valid U of the row in the IEEE total order (+inf / -inf
+// for a row without valid elements).
+__device__ __forceinline__ void row_range(const int* __restrict__ pmin, const int* __restrict__ pmax, int64_t i,
                                           int ntiles, float& umin, float& umax) {
-  umin = __builtin_inff();
-  umax = -__builtin_inff();
+  int kmin = kKeyPosInf, kmax = kKeyNegInf;
   for (int t = 0; t < ntiles; ++t) {
-    umin = fminf(umin, pmin[i * ntiles + t]);
-    umax = fmaxf(umax, pmax[i * ntiles + t]);
+    kmin = min(kmin, pmin[i * ntiles + t]);
+    kmax = max(kmax, pmax[i * ntiles + t]);
   }
+  umin = key_f32(kmin);
+  umax = key_f32(kmax);
 }
 
 // Exposes U_min / U_max (the statistics entry point).
-__global__ __launch_bounds__(256) void k_row_range(int64_t d, int ntiles, const float* __restrict__ pmin,
-                                                  const float* __restrict__ pmax, float* __restrict__ umin,
+__global__ __launch_bounds__(256) void k_row_range(int64_t d, int ntiles, const int* __restrict__ pmin,
+                                                  const int* __restrict__ pmax, float* __restrict__ umin,
                                                   float* __restrict__ umax) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < d) {
@@ -427,7 +458,7 @@ __device__ __forceinline__ int mul_code(float u, float sbar, int zbar, int qmax)
 template <bool W4>
 __global__ __launch_bounds__(256) void k_quant_mul(int64_t d, int64_t n, int u_bits, const uint8_t* __restrict__ wround,
                                                   const int32_t* __restrict__ z, const float* __restrict__ U,
-                                                  const float* __restrict__ pmin, const float* __restrict__ pmax,
+                                                  const int* __restrict__ pmin, const int* __restrict__ pmax,
                                                   int ntiles, int16_t* __restrict__ m, float* __restrict__ sbar_out,
                                                   int32_t* __restrict__ zbar_out, uint8_t* __restrict__ uround_dbg,
                                                   unsigned long long* __restrict__ sat) {
@@ -551,8 +582,8 @@ __device__ __forceinline__ int shift_merge(int w, float u, float sbar, int smax,
 template <bool W4>
 __global__ __launch_bounds__(256) void k_quant_shift(int64_t d, int64_t n, int v_bits,
                                                     const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
-                                                    const float* __restrict__ U, const float* __restrict__ pmin,
-                                                    const float* __restrict__ pmax, int ntiles,
+                                                    const float* __restrict__ U, const int* __restrict__ pmin,
+                                                    const int* __restrict__ pmax, int ntiles,
                                                     uint8_t* __restrict__ m, float* __restrict__ sbar_out,
                                                     uint8_t* __restrict__ shift_dbg,
                                                     unsigned long long* __restrict__ sat) {
@@ -733,14 +764,14 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_row_range(int64_t d, int ntiles, const float* pmin, const float* pmax, float* umin, float* umax,
+hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
                             hipStream_t st) {
   hipLaunchKernelGGL(k_row_range, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin, umax);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
-                            const float* U, const float* pmin, const float* pmax, int ntiles, int16_t* m,
+                            const float* U, const int* pmin, const int* pmax, int ntiles, int16_t* m,
                             float* sbar, int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat,
                             hipStream_t st) {
   dim3 grid((unsigned)((n + kQuantCols - 1) / kQuantCols), (unsigned)d);
@@ -754,7 +785,7 @@ hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const 
 }
 
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
-                              const float* U, const float* pmin, const float* pmax, int ntiles, uint8_t* m,
+                              const float* U, const int* pmin, const int* pmax, int ntiles, uint8_t* m,
                               float* sbar, uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st) {
   dim3 grid((unsigned)((n + kQuantCols - 1) / kQuantCols), (unsigned)d);
   if (w_bits == 4)
