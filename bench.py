@@ -19,7 +19,6 @@ Per-layer merge GB/s and GEMM TOP/s are listed alongside.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -46,7 +45,23 @@ def parse():
                    help="fraction of rows/tokens the oracle processes (0: auto, about 15 s)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--json-out", default="")
+    p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
+
+
+def copy_probe(mib):
+    """A plain copy kernel of known size: the HBM counters of this run calibrate the
+    FETCH_SIZE / WRITE_SIZE readings of the library's kernels."""
+    import torch
+
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": n}))
 
 
 def merge_alg_bytes(d, n, r, w_bits, mode):
@@ -65,24 +80,18 @@ def gemm_exec_ops(M, d, n, mode):
     return 2.0 * M * d * n * passes
 
 
-def kernel_source_sha():
-    h = hashlib.sha256()
-    for f in ("linear.hip", "device_common.h"):
-        with open(os.path.join(ROOT, "integer_rank_adaptation_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
-
-
 def traffic_from_profile(workload_name):
     """HBM bytes per GEMM launch from the committed counter summary, if it was taken
     on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "linear_traffic.json")
+    path = os.path.join(ROOT, "profiles", workload_name + "_traffic.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
     except Exception:
         return None
+    from integer_rank_adaptation_amd.profiling import kernel_source_sha
+
     if rec.get("kernel_source_sha") != kernel_source_sha() or rec.get("workload") != workload_name:
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -90,6 +99,9 @@ def traffic_from_profile(workload_name):
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
                                    "(the merge shards by rows and the GEMM by columns with no exchange; "

@@ -251,7 +251,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
                                                    const float* __restrict__ s, const float* __restrict__ c,
                                                    const float* __restrict__ A, const float* __restrict__ B,
                                                    float* __restrict__ U, int* __restrict__ pmin,
-                                                   int* __restrict__ pmax, int ntiles,
+                                                   int* __restrict__ pmax, int ntiles, int64_t rb0,
                                                    unsigned long long* __restrict__ sat_zero) {
   __shared__ LnEntry tab[96];
   __shared__ float rcp[511];
@@ -276,7 +276,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
       b[k][0] = v.x; b[k][1] = v.y;
     }
   }
-  const int64_t i_begin = (int64_t)blockIdx.y * kAdaptRows;
+  const int64_t i_begin = (rb0 + (int64_t)blockIdx.y) * kAdaptRows;
   for (int ii = 0; ii < kAdaptRows; ++ii) {
     const int64_t i = i_begin + ii;
     if (i >= d) break;
@@ -354,8 +354,8 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
   load_ln_table(tab);
   if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
   __syncthreads();
-  const int64_t i = blockIdx.y;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  for (int64_t i = blockIdx.y; i < d; i += gridDim.y) {
   int kmin = kKeyPosInf, kmax = kKeyNegInf;
   const int64_t jt = (int64_t)blockIdx.x * kAdaptCols;
   for (int64_t j = jt + threadIdx.x; j < jt + kAdaptCols && j < n; j += 256) {
@@ -390,6 +390,8 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
   if (threadIdx.x == 0) {
     pmin[i * ntiles + blockIdx.x] = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
     pmax[i * ntiles + blockIdx.x] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
+  }
+  __syncthreads();  // smin / smax are reused by the next row
   }
 }
 
@@ -426,19 +428,23 @@ __device__ __forceinline__ void add_saturations(unsigned long long* sat, int loc
 }
 
 // ---------------------------------------------------------------------------------
-// K3: MUL quantize + integer Hadamard.  Block = 256 threads x 8 elements of one row.
-//   lo = min(U_min, 0), hi = max(U_max, 0), s_bar = (hi - lo)/(2^bU - 1) (1 unless > 0)
-//   z_bar = clamp(rint(-lo / s_bar)), U_round = clamp(rint(U / s_bar) + z_bar),
-//   m = (U_round - z_bar) w as int16 (saturating, counted); w == 0 -> m = 0, U_round = z_bar.
+// Quantize kernels (MUL and SHIFT).  A block of 128 threads covers 1024 columns of
+// kQRows rows; each thread owns 8 consecutive columns of every one of those rows, and
+// all of its loads (U, W_round codes) are issued before any element is computed.
+// Row groups are walked grid-stride, so any d fits the grid.
 // ---------------------------------------------------------------------------------
-constexpr int kQuantElems = 8;
-constexpr int kQuantCols = 256 * kQuantElems;
+constexpr int kQThreads = 128;
+constexpr int kQElems = 8;
+constexpr int kQCols = kQThreads * kQElems;
+constexpr int kQRows = 2;
 
 struct MulParams {
   float sbar;
   int zbar;
 };
 
+// MUL: lo = min(U_min, 0), hi = max(U_max, 0), s_bar = (hi - lo)/(2^bU - 1) (1 unless
+// > 0), z_bar = clamp(rint(-lo / s_bar)).
 __device__ __forceinline__ MulParams mul_params(float umin, float umax, int qmax) {
   const float lo = fminf(umin, 0.0f), hi = fmaxf(umax, 0.0f);
   float sbar = (hi - lo) / (float)qmax;
@@ -448,6 +454,7 @@ __device__ __forceinline__ MulParams mul_params(float umin, float umax, int qmax
   return MulParams{sbar, zbar};
 }
 
+// U_round = clamp(rint(U / s_bar) + z_bar, 0, 2^bU - 1)
 __device__ __forceinline__ int mul_code(float u, float sbar, int zbar, int qmax) {
   float q = rintf(u / sbar);
   q = fminf(fmaxf(q, -65536.0f), 65536.0f);
@@ -455,102 +462,126 @@ __device__ __forceinline__ int mul_code(float u, float sbar, int zbar, int qmax)
   return v < 0 ? 0 : (v > qmax ? qmax : v);
 }
 
-template <bool W4>
-__global__ __launch_bounds__(256) void k_quant_mul(int64_t d, int64_t n, int u_bits, const uint8_t* __restrict__ wround,
-                                                  const int32_t* __restrict__ z, const float* __restrict__ U,
-                                                  const int* __restrict__ pmin, const int* __restrict__ pmax,
-                                                  int ntiles, int16_t* __restrict__ m, float* __restrict__ sbar_out,
-                                                  int32_t* __restrict__ zbar_out, uint8_t* __restrict__ uround_dbg,
-                                                  unsigned long long* __restrict__ sat) {
-  const int64_t i = blockIdx.y;
-  const int qmax = (1 << u_bits) - 1;
-  float umin, umax;
-  row_range(pmin, pmax, i, ntiles, umin, umax);
-  const MulParams P = mul_params(umin, umax, qmax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) {
-    sbar_out[i] = P.sbar;
-    zbar_out[i] = P.zbar;
+// m = (U_round - z_bar) w as int16, saturating (counted); w == 0 -> U_round = z_bar, m = 0.
+__device__ __forceinline__ int mul_merge(int w, float u, const MulParams& P, int qmax, int& ur, int& nsat) {
+  int mv = 0;
+  ur = P.zbar;
+  if (w != 0) {
+    ur = mul_code(u, P.sbar, P.zbar, qmax);
+    mv = (ur - P.zbar) * w;
   }
-  const int zi = z[i];
+  if (mv > 32767) { mv = 32767; ++nsat; }
+  if (mv < -32768) { mv = -32768; ++nsat; }
+  return mv;
+}
+
+// Eight W_round codes of row i starting at column j0 (j0 % 8 == 0, n % 8 == 0).
+template <bool W4>
+__device__ __forceinline__ uint2 load_codes8(const uint8_t* __restrict__ wround, int64_t i, int64_t n, int64_t j0) {
+  if (W4) return make_uint2(*reinterpret_cast<const uint32_t*>(wround + i * (n >> 1) + (j0 >> 1)), 0u);
+  return *reinterpret_cast<const uint2*>(wround + i * n + j0);
+}
+template <bool W4>
+__device__ __forceinline__ int code_of(uint2 v, int e) {
+  if (W4) return (int)((v.x >> (4 * e)) & 15u);
+  return (int)(((e < 4 ? v.x : v.y) >> (8 * (e & 3))) & 255u);
+}
+template <bool W4>
+__device__ __forceinline__ int code_at(const uint8_t* __restrict__ wround, int64_t i, int64_t n, int64_t j) {
+  if (W4) {
+    const uint8_t byte = wround[i * (n >> 1) + (j >> 1)];
+    return (j & 1) ? (byte >> 4) : (byte & 15);
+  }
+  return wround[i * n + j];
+}
+
+template <bool W4>
+__global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, int u_bits,
+                                                        const uint8_t* __restrict__ wround,
+                                                        const int32_t* __restrict__ z, const float* __restrict__ U,
+                                                        const int* __restrict__ pmin, const int* __restrict__ pmax,
+                                                        int ntiles, int16_t* __restrict__ m,
+                                                        float* __restrict__ sbar_out, int32_t* __restrict__ zbar_out,
+                                                        uint8_t* __restrict__ uround_dbg,
+                                                        unsigned long long* __restrict__ sat) {
+  const int qmax = (1 << u_bits) - 1;
+  const int64_t j0 = (int64_t)blockIdx.x * kQCols + (int64_t)threadIdx.x * kQElems;
+  const int64_t ngroups = (d + kQRows - 1) / kQRows;
   int nsat = 0;
-  const int64_t j0 = (int64_t)blockIdx.x * kQuantCols + (int64_t)threadIdx.x * kQuantElems;
-  if ((n & 7) == 0) {
-    if (j0 < n) {
-      int code[8];
-      if (W4) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(wround + i * (n >> 1) + (j0 >> 1));
+  for (int64_t g = blockIdx.y; g < ngroups; g += gridDim.y) {
+    const int64_t i0 = g * kQRows;
+    if ((n & 7) == 0) {
+      float4 ua[kQRows], ub[kQRows];
+      uint2 cw[kQRows];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) code[e] = (int)((v >> (4 * e)) & 15u);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(wround + i * n + j0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          code[e] = (int)((v.x >> (8 * e)) & 255u);
-          code[4 + e] = (int)((v.y >> (8 * e)) & 255u);
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i < d && j0 < n) {
+          cw[rr] = load_codes8<W4>(wround, i, n, j0);
+          ua[rr] = *reinterpret_cast<const float4*>(U + i * n + j0);
+          ub[rr] = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
         }
       }
-      const float4 ua = *reinterpret_cast<const float4*>(U + i * n + j0);
-      const float4 ub = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
-      const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-      int mm[8], ur[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = code[e] - zi;
-        int mv = 0, uv = P.zbar;
-        if (w != 0) {
-          uv = mul_code(uu[e], P.sbar, P.zbar, qmax);
-          mv = (uv - P.zbar) * w;
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i >= d) break;
+        float umin, umax;
+        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const MulParams P = mul_params(umin, umax, qmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+          sbar_out[i] = P.sbar;
+          zbar_out[i] = P.zbar;
         }
-        if (mv > 32767) { mv = 32767; ++nsat; }
-        if (mv < -32768) { mv = -32768; ++nsat; }
-        mm[e] = mv;
-        ur[e] = uv;
+        if (j0 >= n) continue;
+        const int zi = z[i];
+        const float uu[8] = {ua[rr].x, ua[rr].y, ua[rr].z, ua[rr].w, ub[rr].x, ub[rr].y, ub[rr].z, ub[rr].w};
+        int mm[8], ur[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) mm[e] = mul_merge(code_of<W4>(cw[rr], e) - zi, uu[e], P, qmax, ur[e], nsat);
+        int4 pk;
+        pk.x = (mm[0] & 0xFFFF) | (mm[1] << 16);
+        pk.y = (mm[2] & 0xFFFF) | (mm[3] << 16);
+        pk.z = (mm[4] & 0xFFFF) | (mm[5] << 16);
+        pk.w = (mm[6] & 0xFFFF) | (mm[7] << 16);
+        *reinterpret_cast<int4*>(m + i * n + j0) = pk;
+        if (uround_dbg) {
+          uint2 pu;
+          pu.x = (uint32_t)ur[0] | ((uint32_t)ur[1] << 8) | ((uint32_t)ur[2] << 16) | ((uint32_t)ur[3] << 24);
+          pu.y = (uint32_t)ur[4] | ((uint32_t)ur[5] << 8) | ((uint32_t)ur[6] << 16) | ((uint32_t)ur[7] << 24);
+          *reinterpret_cast<uint2*>(uround_dbg + i * n + j0) = pu;
+        }
       }
-      int4 pk;
-      pk.x = (mm[0] & 0xFFFF) | (mm[1] << 16);
-      pk.y = (mm[2] & 0xFFFF) | (mm[3] << 16);
-      pk.z = (mm[4] & 0xFFFF) | (mm[5] << 16);
-      pk.w = (mm[6] & 0xFFFF) | (mm[7] << 16);
-      *reinterpret_cast<int4*>(m + i * n + j0) = pk;
-      if (uround_dbg) {
-        uint2 pu;
-        pu.x = (uint32_t)ur[0] | ((uint32_t)ur[1] << 8) | ((uint32_t)ur[2] << 16) | ((uint32_t)ur[3] << 24);
-        pu.y = (uint32_t)ur[4] | ((uint32_t)ur[5] << 8) | ((uint32_t)ur[6] << 16) | ((uint32_t)ur[7] << 24);
-        *reinterpret_cast<uint2*>(uround_dbg + i * n + j0) = pu;
+    } else {
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i >= d) break;
+        float umin, umax;
+        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const MulParams P = mul_params(umin, umax, qmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+          sbar_out[i] = P.sbar;
+          zbar_out[i] = P.zbar;
+        }
+        const int zi = z[i];
+        for (int e = 0; e < kQElems; ++e) {
+          const int64_t j = j0 + e;
+          if (j >= n) break;
+          int uv;
+          const int mv = mul_merge(code_at<W4>(wround, i, n, j) - zi, U[i * n + j], P, qmax, uv, nsat);
+          m[i * n + j] = (int16_t)mv;
+          if (uround_dbg) uround_dbg[i * n + j] = (uint8_t)uv;
+        }
       }
-    }
-  } else {
-    for (int e = 0; e < kQuantElems; ++e) {
-      const int64_t j = j0 + e;
-      if (j >= n) break;
-      int code;
-      if (W4) {
-        const uint8_t byte = wround[i * ((n + 1) >> 1) + (j >> 1)];
-        code = (j & 1) ? (byte >> 4) : (byte & 15);
-      } else {
-        code = wround[i * n + j];
-      }
-      const int w = code - zi;
-      int mv = 0, uv = P.zbar;
-      if (w != 0) {
-        uv = mul_code(U[i * n + j], P.sbar, P.zbar, qmax);
-        mv = (uv - P.zbar) * w;
-      }
-      if (mv > 32767) { mv = 32767; ++nsat; }
-      if (mv < -32768) { mv = -32768; ++nsat; }
-      m[i * n + j] = (int16_t)mv;
-      if (uround_dbg) uround_dbg[i * n + j] = (uint8_t)uv;
     }
   }
   add_saturations(sat, nsat);
 }
 
-// ---------------------------------------------------------------------------------
-// K4: SHIFT quantize.  s_bar = max(|U_min|, |U_max|) (1 for an empty / zero row),
-// V = U / s_bar, shift = clamp(-round(log2|V|), 0, 2^bV - 1) (V == 0: largest code,
-// m = 0), m = sign(V) (w >> shift) (arithmetic), saturated to bW signed bits.
-// Output int8 (bW = 8) or packed int4 nibbles (bW = 4, low nibble = even column).
-// ---------------------------------------------------------------------------------
+// SHIFT: s_bar = max(|U_min|, |U_max|) (1 for an empty / zero row), V = U / s_bar,
+// shift = clamp(-round(log2|V|), 0, 2^bV - 1) (V == 0: largest code, m = 0),
+// m = sign(V) (w >> shift) (arithmetic), saturated to bW signed bits.  Output int8
+// (bW = 8) or packed int4 nibbles (bW = 4, low nibble = even column).
 __device__ __forceinline__ float shift_scale(float umin, float umax) {
   float sb = fmaxf(fabsf(umin), fabsf(umax));
   if (!(sb > 0.0f) || isinf(sb)) sb = 1.0f;
@@ -580,95 +611,99 @@ __device__ __forceinline__ int shift_merge(int w, float u, float sbar, int smax,
 }
 
 template <bool W4>
-__global__ __launch_bounds__(256) void k_quant_shift(int64_t d, int64_t n, int v_bits,
-                                                    const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
-                                                    const float* __restrict__ U, const int* __restrict__ pmin,
-                                                    const int* __restrict__ pmax, int ntiles,
-                                                    uint8_t* __restrict__ m, float* __restrict__ sbar_out,
-                                                    uint8_t* __restrict__ shift_dbg,
-                                                    unsigned long long* __restrict__ sat) {
-  const int64_t i = blockIdx.y;
+__global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n, int v_bits,
+                                                          const uint8_t* __restrict__ wround,
+                                                          const int32_t* __restrict__ z, const float* __restrict__ U,
+                                                          const int* __restrict__ pmin, const int* __restrict__ pmax,
+                                                          int ntiles, uint8_t* __restrict__ m,
+                                                          float* __restrict__ sbar_out,
+                                                          uint8_t* __restrict__ shift_dbg,
+                                                          unsigned long long* __restrict__ sat) {
   const int smax = (1 << v_bits) - 1;
   const int mhi = W4 ? 7 : 127, mlo = W4 ? -8 : -128;
-  float umin, umax;
-  row_range(pmin, pmax, i, ntiles, umin, umax);
-  const float sbar = shift_scale(umin, umax);
-  if (blockIdx.x == 0 && threadIdx.x == 0) sbar_out[i] = sbar;
-  const int zi = z[i];
+  const int64_t j0 = (int64_t)blockIdx.x * kQCols + (int64_t)threadIdx.x * kQElems;
+  const int64_t ngroups = (d + kQRows - 1) / kQRows;
   int nsat = 0;
-  const int64_t j0 = (int64_t)blockIdx.x * kQuantCols + (int64_t)threadIdx.x * kQuantElems;
-  if ((n & 7) == 0) {
-    if (j0 < n) {
-      int code[8];
-      if (W4) {
-        const uint32_t v = *reinterpret_cast<const uint32_t*>(wround + i * (n >> 1) + (j0 >> 1));
+  for (int64_t g = blockIdx.y; g < ngroups; g += gridDim.y) {
+    const int64_t i0 = g * kQRows;
+    if ((n & 7) == 0) {
+      float4 ua[kQRows], ub[kQRows];
+      uint2 cw[kQRows];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) code[e] = (int)((v >> (4 * e)) & 15u);
-      } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(wround + i * n + j0);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          code[e] = (int)((v.x >> (8 * e)) & 255u);
-          code[4 + e] = (int)((v.y >> (8 * e)) & 255u);
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i < d && j0 < n) {
+          cw[rr] = load_codes8<W4>(wround, i, n, j0);
+          ua[rr] = *reinterpret_cast<const float4*>(U + i * n + j0);
+          ub[rr] = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
         }
       }
-      const float4 ua = *reinterpret_cast<const float4*>(U + i * n + j0);
-      const float4 ub = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
-      const float uu[8] = {ua.x, ua.y, ua.z, ua.w, ub.x, ub.y, ub.z, ub.w};
-      int mm[8], sh[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) mm[e] = shift_merge(code[e] - zi, uu[e], sbar, smax, mlo, mhi, sh[e], nsat);
-      if (W4) {
-        uint32_t pk = 0;
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i >= d) break;
+        float umin, umax;
+        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const float sbar = shift_scale(umin, umax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) sbar_out[i] = sbar;
+        if (j0 >= n) continue;
+        const int zi = z[i];
+        const float uu[8] = {ua[rr].x, ua[rr].y, ua[rr].z, ua[rr].w, ub[rr].x, ub[rr].y, ub[rr].z, ub[rr].w};
+        int mm[8], sh[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pk |= ((uint32_t)mm[e] & 15u) << (4 * e);
-        *reinterpret_cast<uint32_t*>(m + i * (n >> 1) + (j0 >> 1)) = pk;
-      } else {
-        uint2 pk;
-        pk.x = ((uint32_t)mm[0] & 255u) | (((uint32_t)mm[1] & 255u) << 8) | (((uint32_t)mm[2] & 255u) << 16) |
-               ((uint32_t)mm[3] << 24);
-        pk.y = ((uint32_t)mm[4] & 255u) | (((uint32_t)mm[5] & 255u) << 8) | (((uint32_t)mm[6] & 255u) << 16) |
-               ((uint32_t)mm[7] << 24);
-        *reinterpret_cast<uint2*>(m + i * n + j0) = pk;
-      }
-      if (shift_dbg) {
-        uint2 ps;
-        ps.x = (uint32_t)sh[0] | ((uint32_t)sh[1] << 8) | ((uint32_t)sh[2] << 16) | ((uint32_t)sh[3] << 24);
-        ps.y = (uint32_t)sh[4] | ((uint32_t)sh[5] << 8) | ((uint32_t)sh[6] << 16) | ((uint32_t)sh[7] << 24);
-        *reinterpret_cast<uint2*>(shift_dbg + i * n + j0) = ps;
-      }
-    }
-  } else {
-    // general n: W4 needs even n (validated); handle pairs so a byte is written whole
-    for (int e = 0; e < kQuantElems; e += 2) {
-      const int64_t j = j0 + e;
-      if (j >= n) break;
-      int mm2[2], sh2[2];
-      for (int h = 0; h < 2; ++h) {
-        const int64_t jj = j + h;
-        if (jj >= n) {
-          mm2[h] = 0;
-          sh2[h] = 255;
-          continue;
-        }
-        int code;
+        for (int e = 0; e < 8; ++e)
+          mm[e] = shift_merge(code_of<W4>(cw[rr], e) - zi, uu[e], sbar, smax, mlo, mhi, sh[e], nsat);
         if (W4) {
-          const uint8_t byte = wround[i * (n >> 1) + (jj >> 1)];
-          code = (jj & 1) ? (byte >> 4) : (byte & 15);
+          uint32_t pk = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk |= ((uint32_t)mm[e] & 15u) << (4 * e);
+          *reinterpret_cast<uint32_t*>(m + i * (n >> 1) + (j0 >> 1)) = pk;
         } else {
-          code = wround[i * n + jj];
+          uint2 pk;
+          pk.x = ((uint32_t)mm[0] & 255u) | (((uint32_t)mm[1] & 255u) << 8) | (((uint32_t)mm[2] & 255u) << 16) |
+                 ((uint32_t)mm[3] << 24);
+          pk.y = ((uint32_t)mm[4] & 255u) | (((uint32_t)mm[5] & 255u) << 8) | (((uint32_t)mm[6] & 255u) << 16) |
+                 ((uint32_t)mm[7] << 24);
+          *reinterpret_cast<uint2*>(m + i * n + j0) = pk;
         }
-        mm2[h] = shift_merge(code - zi, U[i * n + jj], sbar, smax, mlo, mhi, sh2[h], nsat);
+        if (shift_dbg) {
+          uint2 ps;
+          ps.x = (uint32_t)sh[0] | ((uint32_t)sh[1] << 8) | ((uint32_t)sh[2] << 16) | ((uint32_t)sh[3] << 24);
+          ps.y = (uint32_t)sh[4] | ((uint32_t)sh[5] << 8) | ((uint32_t)sh[6] << 16) | ((uint32_t)sh[7] << 24);
+          *reinterpret_cast<uint2*>(shift_dbg + i * n + j0) = ps;
+        }
       }
-      if (W4) {
-        m[i * (n >> 1) + (j >> 1)] = (uint8_t)(((uint32_t)mm2[0] & 15u) | (((uint32_t)mm2[1] & 15u) << 4));
-      } else {
-        m[i * n + j] = (uint8_t)mm2[0];
-        if (j + 1 < n) m[i * n + j + 1] = (uint8_t)mm2[1];
-      }
-      if (shift_dbg) {
-        shift_dbg[i * n + j] = (uint8_t)sh2[0];
-        if (j + 1 < n) shift_dbg[i * n + j + 1] = (uint8_t)sh2[1];
+    } else {
+      // general n (W4 needs even n, validated): pairs, so that a packed byte is written whole
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i >= d) break;
+        float umin, umax;
+        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const float sbar = shift_scale(umin, umax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) sbar_out[i] = sbar;
+        const int zi = z[i];
+        for (int e = 0; e < kQElems; e += 2) {
+          const int64_t j = j0 + e;
+          if (j >= n) break;
+          int mm2[2] = {0, 0}, sh2[2] = {255, 255};
+          for (int h = 0; h < 2; ++h) {
+            const int64_t jj = j + h;
+            if (jj < n)
+              mm2[h] = shift_merge(code_at<W4>(wround, i, n, jj) - zi, U[i * n + jj], sbar, smax, mlo, mhi, sh2[h],
+                                   nsat);
+          }
+          if (W4) {
+            m[i * (n >> 1) + (j >> 1)] = (uint8_t)(((uint32_t)mm2[0] & 15u) | (((uint32_t)mm2[1] & 15u) << 4));
+          } else {
+            m[i * n + j] = (uint8_t)mm2[0];
+            if (j + 1 < n) m[i * n + j + 1] = (uint8_t)mm2[1];
+          }
+          if (shift_dbg) {
+            shift_dbg[i * n + j] = (uint8_t)sh2[0];
+            if (j + 1 < n) shift_dbg[i * n + j + 1] = (uint8_t)sh2[1];
+          }
+        }
       }
     }
   }
@@ -733,13 +768,19 @@ static hipError_t launch_adapt_r(const AdaptArgs& a, int* ntiles_out, hipStream_
   const int cols = 256 * CPT;
   const int ntiles = (int)((a.n + cols - 1) / cols);
   *ntiles_out = ntiles;
-  dim3 grid((unsigned)ntiles, (unsigned)((a.d + kAdaptRows - 1) / kAdaptRows));
-  if (a.w_bits == 4)
-    hipLaunchKernelGGL((k_adapt_fast<R, CPT, true>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
-                       a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
-  else
-    hipLaunchKernelGGL((k_adapt_fast<R, CPT, false>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
-                       a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
+  const int64_t nrb = (a.d + kAdaptRows - 1) / kAdaptRows;
+  // grid.y is limited to 65535: very tall matrices take several launches
+  for (int64_t rb0 = 0; rb0 < nrb; rb0 += 65535) {
+    const int64_t cnt = nrb - rb0 < 65535 ? nrb - rb0 : 65535;
+    const dim3 grid((unsigned)ntiles, (unsigned)cnt);
+    unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
+    if (a.w_bits == 4)
+      hipLaunchKernelGGL((k_adapt_fast<R, CPT, true>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
+                         a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rb0, sz);
+    else
+      hipLaunchKernelGGL((k_adapt_fast<R, CPT, false>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
+                         a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rb0, sz);
+  }
   return hipGetLastError();
 }
 
@@ -758,7 +799,7 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   }
   const int ntiles = (int)((a.n + kAdaptCols - 1) / kAdaptCols);
   *ntiles_out = ntiles;
-  dim3 grid((unsigned)ntiles, (unsigned)a.d);
+  dim3 grid((unsigned)ntiles, (unsigned)(a.d < 65535 ? (a.d ? a.d : 1) : 65535));
   hipLaunchKernelGGL(k_adapt_generic, grid, dim3(256), 0, st, a.d, a.n, a.r, a.w_bits, a.seed, a.layer_id, a.wround,
                      a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
   return hipGetLastError();
@@ -770,30 +811,35 @@ hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* p
   return hipGetLastError();
 }
 
+static dim3 quant_grid(int64_t d, int64_t n) {
+  const int64_t groups = (d + kQRows - 1) / kQRows;
+  return dim3((unsigned)((n + kQCols - 1) / kQCols), (unsigned)(groups < 65535 ? (groups ? groups : 1) : 65535));
+}
+
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
                             const float* U, const int* pmin, const int* pmax, int ntiles, int16_t* m,
                             float* sbar, int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat,
                             hipStream_t st) {
-  dim3 grid((unsigned)((n + kQuantCols - 1) / kQuantCols), (unsigned)d);
+  const dim3 grid = quant_grid(d, n);
   if (w_bits == 4)
-    hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(256), 0, st, d, n, u_bits, wround, z, U, pmin, pmax, ntiles, m,
-                       sbar, zbar, uround_dbg, sat);
+    hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, pmin, pmax, ntiles,
+                       m, sbar, zbar, uround_dbg, sat);
   else
-    hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(256), 0, st, d, n, u_bits, wround, z, U, pmin, pmax, ntiles, m,
-                       sbar, zbar, uround_dbg, sat);
+    hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, pmin, pmax,
+                       ntiles, m, sbar, zbar, uround_dbg, sat);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
                               const float* U, const int* pmin, const int* pmax, int ntiles, uint8_t* m,
                               float* sbar, uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st) {
-  dim3 grid((unsigned)((n + kQuantCols - 1) / kQuantCols), (unsigned)d);
+  const dim3 grid = quant_grid(d, n);
   if (w_bits == 4)
-    hipLaunchKernelGGL(k_quant_shift<true>, grid, dim3(256), 0, st, d, n, v_bits, wround, z, U, pmin, pmax, ntiles, m,
-                       sbar, shift_dbg, sat);
+    hipLaunchKernelGGL(k_quant_shift<true>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, pmin, pmax,
+                       ntiles, m, sbar, shift_dbg, sat);
   else
-    hipLaunchKernelGGL(k_quant_shift<false>, grid, dim3(256), 0, st, d, n, v_bits, wround, z, U, pmin, pmax, ntiles,
-                       m, sbar, shift_dbg, sat);
+    hipLaunchKernelGGL(k_quant_shift<false>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, pmin, pmax,
+                       ntiles, m, sbar, shift_dbg, sat);
   return hipGetLastError();
 }
 

@@ -201,6 +201,32 @@ def test_merge_degenerate_rows(ops):
     assert np.array_equal(bits(host(g2["sbar"])), bits(ref2["sbar"]))
 
 
+@pytest.mark.parametrize("d,n,w_bits", [(600_000, 8, 4), (600_000, 8, 8), (70_000, 6, 8)])
+def test_merge_tall_matrices(ops, d, n, w_bits):
+    """More rows than one grid dimension holds (65535 row blocks of the adaptation
+    kernel, 65535 row pairs of the quantize kernels, 65535 rows of the general path):
+    sampled rows, including those at the chunk boundaries, match the oracle."""
+    r = 4
+    wr, z, s, c, A, Bm = random_state(31 + n, d, n, r, w_bits)
+    st = gpu_state(wr, z, s, c, w_bits)
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), w_bits, w_bits, 5, 2, dbg=True)
+    h = ops.merge_shift(st, cuda(A), cuda(Bm), w_bits, 4, 5, 2)
+    edges = [0, 1, 65534, 65535, 65536, 2 * 65535 - 1, 2 * 65535, 2 * 65535 + 1, 8 * 65535 - 1, 8 * 65535,
+             8 * 65535 + 1, d - 2, d - 1]
+    rng = np.random.Generator(np.random.PCG64(d + n))
+    rows = np.array(sorted({e for e in edges if e < d} | set(rng.choice(d, 8, replace=False).tolist())))
+    R = np.concatenate([oracle.gen_r_rows(int(i), 1, n, 5, 2, c[i:i + 1]) for i in rows])
+    ref = oracle.merge_mul(wr[rows], z[rows], s[rows], R, A[rows], Bm, w_bits)
+    assert np.array_equal(host(g["m"])[rows], ref["m"])
+    assert np.array_equal(host(g["uround"])[rows], ref["uround"])
+    assert np.array_equal(bits(host(g["sbar"])[rows]), bits(ref["sbar"]))
+    ref2 = oracle.merge_shift(wr[rows], z[rows], s[rows], R, A[rows], Bm, w_bits, 4)
+    m2 = host(h["m"])
+    m2 = unpack4s(m2) if w_bits == 4 else m2.view(np.int8)
+    assert np.array_equal(m2[rows], ref2["m"])
+    assert np.array_equal(bits(host(h["sbar"])[rows]), bits(ref2["sbar"]))
+
+
 def test_merge_is_deterministic(ops):
     wr, z, s, c, A, Bm = random_state(9, 64, 3072, 32, 4)
     st = gpu_state(wr, z, s, c, 4)
