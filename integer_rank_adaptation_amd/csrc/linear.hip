@@ -13,22 +13,30 @@
 //                            accumulator is 16 * exact and is shifted back exactly;
 //   INT16 (MUL)              bias byte split after the LDS read:
 //                            hi = m >> 8, lo = (m & 0xFF) - 128, two int8 planes,
-//                            exact = 256 acc_hi + acc_lo + 128 rowsum(X_q) (int64).
+//                            exact = 256 acc_hi + acc_lo + 128 rowsum(X_q), formed
+//                            exactly in binary64 (|exact| < 2^53).
 //
 // Data path: every operand goes from HBM straight into LDS with buffer_load ... lds
 // (16 bytes per lane, no VGPR staging) through a 4-stage ring, so the loads of stages
-// k+2 and k+3 are in flight while stage k computes.  Out-of-range rows and K chunks read as
-// zero through the buffer descriptor.  LDS rows are XOR-swizzled in 16-byte chunks
-// (conflict-free fragment reads); the swizzle is realized by the global address each
-// lane fetches, since a direct load writes lane l's 16 bytes at base + 16 l.
+// k+2 and k+3 are in flight while stage k computes.  Each stage gets buffer
+// descriptors based at its first K element, so a lane's offsets are fixed for the
+// whole loop; rows past the end and stages past n read zeros through the descriptor
+// range.  LDS rows are XOR-swizzled in 16-byte chunks (conflict-free fragment reads);
+// the swizzle is realized by the global address each lane fetches, since a direct
+// load writes lane l's 16 bytes at base + 16 l.
 //
 // Tiling: a 256-thread block (4 waves, 2 x 2) computes 256 tokens x 256 MFMA columns
 // (256 outputs, or 128 outputs x 2 planes); each wave owns 128 x 128 = 4 x 4 tiles of
 // v_mfma_i32_32x32x32_i8 (256 accumulators, one wave per SIMD) with the weight
 // fragment as the A operand, so a lane's four consecutive accumulators are four
-// consecutive outputs of one token.  A 4-stage ring keeps two stages of loads in
-// flight; the barrier of iteration k publishes stage k+1, so the first fragments of
-// the next stage are read while the current stage's MFMAs run.
+// consecutive outputs of one token.  Two operand register sets alternate: while the
+// 16 MFMAs of one 32-deep K sub-step run on one set, the other is read from LDS (one
+// read per MFMA) and format-converted, and the stage's direct loads are issued, in an
+// order pinned with sched_barrier.  The barrier of iteration k publishes stage k+1.
+//
+// Epilogue: per-token scales / row sums and per-output scales go to LDS once; the
+// accumulators pass through a padded LDS region per wave so that each lane writes four
+// consecutive bf16 outputs of one row (hardware round-to-nearest-even conversion).
 #include "device_common.h"
 #include "intlora_internal.h"
 
@@ -36,6 +44,8 @@ namespace intlora {
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float f2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16 };
@@ -76,66 +86,97 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 constexpr uint32_t kOOB = 0x80000000u;  // a buffer offset past every record: the lane reads zeros
 
-// Offset `off` if the chunk starting at K element `k` lies inside the row, else an
-// out-of-range offset (the lane reads zeros).  Branch-free 32-bit arithmetic.
-__device__ __forceinline__ uint32_t in_row(uint32_t off, int k, int n) {
-  const uint32_t keep = (uint32_t)((k - n) >> 31);  // all ones when k < n
-  return (off & keep) | (kOOB & ~keep);
-}
-
-// Issue the direct loads of one K stage into one LDS stage buffer.  Row and column
-// offsets fit in 32 bits (the descriptors are based at the block's first row).
+// Per-lane byte offsets of the lane's 16-byte chunks inside one K stage, relative to
+// the stage's first K element: they do not change from stage to stage (each stage
+// gets a buffer descriptor based at its first K element), so the main loop spends no
+// vector instructions on addresses.  `akk` is the lane's first K element of each A
+// chunk (for the zero fill of a partial last stage).
 template <int F>
-__device__ __forceinline__ void issue_stage(int kt, int n, __amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                            uint8_t* stage) {
+struct Plan {
+  uint32_t a[lin::Cfg<F>::A_LOADS];
+  uint32_t b[lin::Cfg<F>::B_LOADS];
+  int akk[lin::Cfg<F>::A_LOADS];
+};
+
+template <int F>
+__device__ __forceinline__ void make_plan(int n, Plan<F>& p) {
   using namespace lin;
   const int lane = threadIdx.x & 63;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int k0 = kt * BK;
-  // A (tokens): 16 rows of 64 bytes per direct load
 #pragma unroll
-  for (int q = 0; q < Cfg<F>::A_LOADS; ++q) {
+  for (int q = 0; q < Cfg<F>::A_LOADS; ++q) {  // A (tokens): 16 rows of 64 bytes per load
     const int g = wid * Cfg<F>::A_LOADS + q;
     const int row = 16 * g + (lane >> 2);
-    const int k = k0 + 16 * ((lane & 3) ^ swz64(row));
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + g * 1024), 16,
-                                             in_row((uint32_t)(row * n + k), k, n), 0, 0, 0);
+    const int kk = 16 * ((lane & 3) ^ swz64(row));
+    p.a[q] = (uint32_t)(row * n + kk);
+    p.akk[q] = kk;
   }
-  uint8_t* Bs = stage + A_BYTES;
-  if (F == F_INT8) {
 #pragma unroll
-    for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
-      const int g = wid * Cfg<F>::B_LOADS + q;
+  for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
+    const int g = wid * Cfg<F>::B_LOADS + q;
+    if (F == F_INT8) {           // 64-byte rows
       const int row = 16 * g + (lane >> 2);
-      const int k = k0 + 16 * ((lane & 3) ^ swz64(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16,
-                                               in_row((uint32_t)(row * n + k), k, n), 0, 0, 0);
-    }
-  } else if (F == F_INT16) {
-#pragma unroll
-    for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
-      const int g = wid * Cfg<F>::B_LOADS + q;
-      const int row = 8 * g + (lane >> 3);          // 128-byte rows (64 int16)
-      const int k = k0 + 8 * ((lane & 7) ^ swz128(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16,
-                                               in_row((uint32_t)(2 * (row * n + k)), k, n), 0, 0, 0);
-    }
-  } else {  // F_INT4: 32-byte rows (64 nibbles)
-#pragma unroll
-    for (int q = 0; q < Cfg<F>::B_LOADS; ++q) {
-      const int g = wid * Cfg<F>::B_LOADS + q;
+      p.b[q] = (uint32_t)(row * n + 16 * ((lane & 3) ^ swz64(row)));
+    } else if (F == F_INT16) {   // 128-byte rows (64 int16)
+      const int row = 8 * g + (lane >> 3);
+      p.b[q] = (uint32_t)(2 * (row * n + 8 * ((lane & 7) ^ swz128(row))));
+    } else {                     // F_INT4: 32-byte rows (64 nibbles)
       const int row = 32 * g + (lane >> 1);
-      const int k = k0 + 32 * ((lane & 1) ^ swz32(row));
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(Bs + g * 1024), 16,
-                                               in_row((uint32_t)(row * (n >> 1) + (k >> 1)), k, n), 0, 0, 0);
+      p.b[q] = (uint32_t)(row * (n >> 1) + 16 * ((lane & 1) ^ swz32(row)));
     }
   }
+}
+
+// Descriptors of K stage kt: based at the stage's first K element, so that the
+// per-lane offsets of the plan stay fixed.  Rows past the end of the operand and
+// stages past n fall outside the record count and read zeros.
+template <int F>
+__device__ __forceinline__ void stage_rsrc(int kt, const int8_t* a_tile, int64_t a_bytes, const uint8_t* b_tile,
+                                           int64_t b_bytes, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
+  using namespace lin;
+  const int k0 = kt * BK;
+  const int64_t kb = F == F_INT16 ? 2 * (int64_t)k0 : (F == F_INT8 ? (int64_t)k0 : (int64_t)(k0 >> 1));
+  ra = make_rsrc(a_tile + k0, a_bytes - k0);
+  rb = make_rsrc(b_tile + kb, b_bytes - kb);
+}
+
+// Direct load number q (A loads first, then B) of one stage into the stage buffer.
+// With KTAIL (n not a multiple of BK) the A chunks past n in a partial stage read
+// zeros, which zeroes their products whatever the B bytes there are.
+template <int F, bool KTAIL>
+__device__ __forceinline__ void issue_load(int q, int n, int kt, const int8_t* a_tile, int64_t a_bytes,
+                                           const uint8_t* b_tile, int64_t b_bytes, const Plan<F>& p,
+                                           uint8_t* stage) {
+  using namespace lin;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  stage_rsrc<F>(kt, a_tile, a_bytes, b_tile, b_bytes, ra, rb);
+  const int k0 = kt * BK;
+  const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (q < Cfg<F>::A_LOADS) {
+    const int g = wid * Cfg<F>::A_LOADS + q;
+    uint32_t off = p.a[q];
+    if (KTAIL) off = p.akk[q] < n - k0 ? off : kOOB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + g * 1024), 16, off, 0, 0, 0);
+  } else {
+    const int qb = q - Cfg<F>::A_LOADS;
+    const int g = wid * Cfg<F>::B_LOADS + qb;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + A_BYTES + g * 1024), 16, p.b[qb], 0, 0, 0);
+  }
+}
+
+template <int F, bool KTAIL>
+__device__ __forceinline__ void issue_stage(int kt, int n, const int8_t* a_tile, int64_t a_bytes,
+                                            const uint8_t* b_tile, int64_t b_bytes, const Plan<F>& p,
+                                            uint8_t* stage) {
+#pragma unroll
+  for (int q = 0; q < lin::Cfg<F>::LOADS; ++q) issue_load<F, KTAIL>(q, n, kt, a_tile, a_bytes, b_tile, b_bytes, p, stage);
 }
 
 // vmcnt-only wait (expcnt / lgkmcnt left unconstrained), N <= 15.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8));
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // INT4 fragment: 8 packed bytes (16 nibbles, K order) -> 16 int8 holding 16 * w.
@@ -146,32 +187,60 @@ __device__ __forceinline__ void unpack4(uint32_t x, uint32_t& o0, uint32_t& o1) 
   o1 = __builtin_amdgcn_perm(H, L, 0x07030602u);
 }
 
-// Fragments of one K sub-step: A (tokens) for 4 tiles and B (weights) for 4 MFMA
-// column tiles; sub-step ks of lane half h covers K 32 h + 16 ks .. + 16 of the stage.
+// Raw B fragment bytes of one K sub-step (LDS read), before format conversion.
 template <int F>
-__device__ __forceinline__ void read_frags(const uint8_t* __restrict__ As, int wm, int wn, int ks, int fr, int h,
-                                           v4i (&af)[4], v4i (&bf)[4]) {
-  using namespace lin;
-  const uint8_t* Bs = As + A_BYTES;
+struct RawB {
+  v4i v[4];
+};
+
+// A (tokens) fragments of one K sub-step: 4 tiles; sub-step ks of lane half h covers
+// K 32 h + 16 ks .. + 16 of the stage.
+__device__ __forceinline__ void read_a(const uint8_t* __restrict__ As, int wm, int ks, int fr, int h, v4i (&af)[4]) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = wm * 128 + i * 32 + fr;
     af[i] = *reinterpret_cast<const v4i*>(As + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
   }
+}
+
+template <int F>
+__device__ __forceinline__ void read_b(const uint8_t* __restrict__ Bs, int wn, int ks, int fr, int h, RawB<F>& rw) {
   if (F == F_INT8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int row = wn * 128 + j * 32 + fr;
-      bf[j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
+      rw.v[j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
     }
   } else if (F == F_INT16) {
-    // two output tiles of 32; tile q gives MFMA column tiles 2q (hi plane), 2q+1 (lo plane)
+    // two output tiles of 32 rows, 32 int16 (two 16-byte chunks) per lane and sub-step
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int row = wn * 64 + q * 32 + fr;
       const int c0 = 4 * h + 2 * ks;
-      const v4i r0 = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c0 ^ swz128(row)) << 4));
-      const v4i r1 = *reinterpret_cast<const v4i*>(Bs + row * 128 + (((c0 + 1) ^ swz128(row)) << 4));
+      rw.v[2 * q] = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c0 ^ swz128(row)) << 4));
+      rw.v[2 * q + 1] = *reinterpret_cast<const v4i*>(Bs + row * 128 + (((c0 + 1) ^ swz128(row)) << 4));
+    }
+  } else {  // F_INT4: 8 packed bytes per lane and sub-step (half of the lane's 16-byte chunk)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = wn * 128 + j * 32 + fr;
+      const uint2 r = *reinterpret_cast<const uint2*>(Bs + row * 32 + ((h ^ swz32(row)) << 4) + 8 * ks);
+      rw.v[j] = v4i{(int)r.x, (int)r.y, 0, 0};
+    }
+  }
+}
+
+// B (weight) MFMA operands for 4 column tiles from the raw bytes.  INT16: tile q of
+// outputs gives MFMA column tiles 2q (hi plane) and 2q+1 (lo plane).
+template <int F>
+__device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4]) {
+  if (F == F_INT8) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = rw.v[j];
+  } else if (F == F_INT16) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const v4i r0 = rw.v[2 * q], r1 = rw.v[2 * q + 1];
       const uint32_t x[8] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w,
                              (uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
       // little-endian int16: the high byte of each value is byte 1 or 3 of its dword
@@ -181,20 +250,71 @@ __device__ __forceinline__ void read_frags(const uint8_t* __restrict__ As, int w
         bf[2 * q + 1][e] = (int)(__builtin_amdgcn_perm(x[2 * e + 1], x[2 * e], 0x06040200u) ^ 0x80808080u);
       }
     }
-  } else {  // F_INT4: 8 packed bytes per lane and sub-step (half of the lane's 16-byte chunk)
+  } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int row = wn * 128 + j * 32 + fr;
-      const uint2 r = *reinterpret_cast<const uint2*>(Bs + row * 32 + ((h ^ swz32(row)) << 4) + 8 * ks);
       uint32_t o0_, o1_, o2_, o3_;
-      unpack4(r.x, o0_, o1_);
-      unpack4(r.y, o2_, o3_);
+      unpack4((uint32_t)rw.v[j].x, o0_, o1_);
+      unpack4((uint32_t)rw.v[j].y, o2_, o3_);
       bf[j] = v4i{(int)o0_, (int)o1_, (int)o2_, (int)o3_};
     }
   }
 }
 
+// One LDS read of a sub-step: reads 0..3 are the A fragments, 4..7 the raw B chunks.
 template <int F>
+__device__ __forceinline__ void read_piece(int q, const uint8_t* __restrict__ S, int wm, int wn, int ks, int fr,
+                                           int h, v4i (&af)[4], RawB<F>& rw) {
+  using namespace lin;
+  if (q >= 4) {
+    const int row = wm * 128 + (q - 4) * 32 + fr;
+    af[q - 4] = *reinterpret_cast<const v4i*>(S + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
+    return;
+  }
+  const uint8_t* Bs = S + A_BYTES;
+  const int j = q;
+  if (F == F_INT8) {
+    const int row = wn * 128 + j * 32 + fr;
+    rw.v[j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
+  } else if (F == F_INT16) {
+    const int qq = j >> 1, c = 4 * h + 2 * ks + (j & 1);
+    const int row = wn * 64 + qq * 32 + fr;
+    rw.v[j] = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c ^ swz128(row)) << 4));
+  } else {
+    const int row = wn * 128 + j * 32 + fr;
+    const uint2 r = *reinterpret_cast<const uint2*>(Bs + row * 32 + ((h ^ swz32(row)) << 4) + 8 * ks);
+    rw.v[j] = v4i{(int)r.x, (int)r.y, 0, 0};
+  }
+}
+
+// Conversion piece p (0..7) of the raw B bytes into MFMA operands.
+template <int F>
+__device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf)[4]) {
+  if (F == F_INT8) {
+    if (p < 4) bf[p] = rw.v[p];
+  } else if (F == F_INT16) {
+    const int q = p >> 2, e = p & 3;  // output tile q, dword pair e
+    const v4i& lo16 = rw.v[2 * q + (e >> 1)];
+    const uint32_t x0 = (uint32_t)lo16[2 * (e & 1)], x1 = (uint32_t)lo16[2 * (e & 1) + 1];
+    bf[2 * q][e] = (int)__builtin_amdgcn_perm(x1, x0, 0x07050301u);
+    bf[2 * q + 1][e] = (int)(__builtin_amdgcn_perm(x1, x0, 0x06040200u) ^ 0x80808080u);
+  } else {
+    const int j = p >> 1, w = p & 1;
+    uint32_t o0_, o1_;
+    unpack4((uint32_t)rw.v[j][w], o0_, o1_);
+    bf[j][2 * w] = (int)o0_;
+    bf[j][2 * w + 1] = (int)o1_;
+  }
+}
+
+__device__ __forceinline__ void mfma16(const v4i (&af)[4], const v4i (&bf)[4], v16i (&acc)[4][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
+}
+
+template <int F, bool KTAIL>
 __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t d, int64_t n,
                                                             const int8_t* __restrict__ xq,
                                                             const float* __restrict__ sx,
@@ -229,10 +349,14 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   const int64_t t0 = (int64_t)tm * BM;
   const int64_t o0 = (int64_t)tn * OUT;
 
-  // Buffer descriptors based at this block's first token row / first output row.
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(xq + t0 * n, (M - t0) * n);
+  // Operand tiles: this block's first token row / first output row.
+  const int8_t* a_tile = xq + t0 * n;
+  const int64_t a_bytes = (M - t0) * n;
   const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(m + o0 * wrow, (d - o0) * wrow);
+  const uint8_t* b_tile = m + o0 * wrow;
+  const int64_t b_bytes = (d - o0) * wrow;
+  Plan<F> plan;
+  make_plan<F>((int)n, plan);
 
   v16i acc[4][4];
 #pragma unroll
@@ -245,71 +369,84 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   const int KT = (int)((n + BK - 1) / BK);
   const int fr = lane & 31, h = lane >> 5;
   // The loop body is one basic block so that the schedule below holds: stages past
-  // the end are still issued, every lane of them reading zeros (out-of-range offset)
-  // into a ring buffer that is never read again, and the fragment reads of stage k+1
-  // at the last iteration fetch unused data.  vmcnt accounting is then uniform.
-  issue_stage<F>(0, (int)n, ra, rb, lds);
-  issue_stage<F>(1, (int)n, ra, rb, lds + STAGE);
-  issue_stage<F>(2, (int)n, ra, rb, lds + 2 * STAGE);
+  // the end are still issued, reading zeros (empty descriptor range) into a ring
+  // buffer that is never read again, and the fragment reads of stage k+1 at the last
+  // iteration fetch unused data.  vmcnt accounting is then uniform.
+  issue_stage<F, KTAIL>(0, (int)n, a_tile, a_bytes, b_tile, b_bytes, plan, lds);
+  issue_stage<F, KTAIL>(1, (int)n, a_tile, a_bytes, b_tile, b_bytes, plan, lds + STAGE);
+  issue_stage<F, KTAIL>(2, (int)n, a_tile, a_bytes, b_tile, b_bytes, plan, lds + 2 * STAGE);
   wait_vmcnt<2 * Cfg<F>::LOADS>();
   __builtin_amdgcn_s_barrier();
-  v4i af0[4], bf0[4], af1[4], bf1[4];
-  read_frags<F>(lds, wm, wn, 0, fr, h, af0, bf0);
+  // Two operand sets: set 0 feeds the MFMAs of sub-step 0 of a stage while set 1 is
+  // read from LDS and converted, and the other way round for sub-step 1.
+  v4i a0[4], b0[4], a1[4], b1[4];
+  RawB<F> rw;
+  read_a(lds, wm, 0, fr, h, a0);
+  read_b<F>(lds + A_BYTES, wn, 0, fr, h, rw);
+  convert_b<F>(rw, b0);
 
-  // Per iteration: the loads of stage k+3 and the reads of sub-step 1 are issued in
-  // the shadow of the first eight MFMAs of sub-step 0; the reads of stage k+1 sub-step
-  // 0 in the shadow of the first eight MFMAs of sub-step 1; VALU fragment conversion
-  // (INT16 byte split, INT4 unpack) after them.
-  constexpr int kValu = F == F_INT16 ? 3 : (F == F_INT4 ? 5 : 0);
   for (int kt = 0; kt < KT; ++kt) {
     // stage kt+1 has landed (loads of kt+2 may still be in flight); after the barrier
     // it is visible to all waves and nobody reads stage kt-1, whose buffer kt+3 reuses
     wait_vmcnt<Cfg<F>::LOADS>();
     __builtin_amdgcn_s_barrier();
-    issue_stage<F>(kt + 3, (int)n, ra, rb, lds + ((kt + 3) % kStages) * STAGE);
-    const uint8_t* As = lds + (kt % kStages) * STAGE;
-    read_frags<F>(As, wm, wn, 1, fr, h, af1, bf1);
+    uint8_t* ldst = lds + ((kt + 3) % kStages) * STAGE;
+    const uint8_t* S0 = lds + (kt % kStages) * STAGE;
+    const uint8_t* S1 = lds + ((kt + 1) % kStages) * STAGE;
+    // Each half (one 32-deep K sub-step): 16 MFMAs on the current operand set,
+    // interleaved one by one with the LDS reads of the next set (first eight MFMAs),
+    // the stage's direct loads (first half, one per MFMA) and the conversion of the
+    // next set (last eight MFMAs).  sched_barrier fixes the order.
+    // sub-step 0 of stage kt on set 0; set 1 <- sub-step 1 of stage kt; loads of kt+3
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf0[j], af0[i], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    for (int q = 0; q < 16; ++q) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[q & 3], a0[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
+      if (q < 8) read_piece<F>(q, S0, wm, wn, 1, fr, h, a1, rw);
+      if (q >= 8 && q - 8 < (Cfg<F>::LOADS + 1) / 2)
+        issue_load<F, KTAIL>(q - 8, (int)n, kt + 3, a_tile, a_bytes, b_tile, b_bytes, plan, ldst);
+      if (q >= 8) convert_piece<F>(q - 8, rw, b1);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // sub-step 1 of stage kt on set 1; set 0 <- sub-step 0 of stage kt+1
 #pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
-    }
-    read_frags<F>(lds + ((kt + 1) % kStages) * STAGE, wm, wn, 0, fr, h, af0, bf0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf1[j], af1[i], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 1);
-    }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 1);
-      if (kValu) __builtin_amdgcn_sched_group_barrier(0x002, kValu, 1);
+    for (int q = 0; q < 16; ++q) {
+      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[q & 3], a1[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
+      if (q < 8) read_piece<F>(q, S1, wm, wn, 0, fr, h, a0, rw);
+      if (q >= 8 && q - 8 + (Cfg<F>::LOADS + 1) / 2 < Cfg<F>::LOADS)
+        issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kt + 3, a_tile, a_bytes, b_tile, b_bytes, plan, ldst);
+      if (q >= 8) convert_piece<F>(q - 8, rw, b0);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
   wait_vmcnt<0>();  // the trailing zero-reading loads land before LDS is reused
 
-  // Epilogue, one 32-token slab (i) at a time through LDS: each wave writes its 32 x 128
-  // int32 accumulators as 16-byte groups (lane l, registers 4a..4a+3 of tile j are
-  // token l % 32, MFMA columns 32 j + 8 a + 4 (l / 32) + 0..3) into a padded region of
-  // its own, then reads them back row-contiguously; each lane finishes four outputs.
+  // Epilogue.  The block's per-token scales / row sums and per-output scales are
+  // staged in LDS first, so the conversion loop below issues no global loads.  Then
+  // one 32-token slab (i) at a time: each wave writes its 32 x 128 int32 accumulators
+  // as 16-byte groups (lane l, registers 4a..4a+3 of tile j are token l % 32, MFMA
+  // columns 32 j + 8 a + 4 (l / 32) + 0..3) into a padded region of its own, then
+  // reads them back row-contiguously; each lane finishes four outputs per row.
   __syncthreads();
-  constexpr int RS = 132;  // padded row stride (ints): conflict-free 16-byte accesses
+  constexpr int RS = 132;                              // padded row stride (ints): conflict-free
+  constexpr int kVec = 4 * 32 * RS * 4;                // after the four wave regions
+  float* tok_sx = reinterpret_cast<float*>(lds + kVec);
+  int32_t* tok_rs = reinterpret_cast<int32_t*>(lds + kVec + 4 * BM);
+  float* col_sb = reinterpret_cast<float*>(lds + kVec + 8 * BM);
+  {
+    const int64_t t = t0 + tid;
+    tok_sx[tid] = t < M ? sx[t] : 0.0f;
+    if (F == F_INT16) tok_rs[tid] = t < M ? rowsum[t] : 0;
+    if (tid < OUT) col_sb[tid] = o0 + tid < d ? sbar[o0 + tid] : 0.0f;
+  }
+  __syncthreads();
   int32_t* R = reinterpret_cast<int32_t*>(lds) + wid * (32 * RS);
   const bool vec_ok = (d & 3) == 0;
+  // the lane's four output columns are fixed for the whole epilogue
+  const int lc = F == F_INT16 ? 4 * (lane & 15) : 4 * (lane & 31);   // first column in the wave's tile
+  const int64_t c0 = o0 + (F == F_INT16 ? wn * 64 : wn * 128) + lc;
+  const float4 sb4 = *reinterpret_cast<const float4*>(col_sb + (F == F_INT16 ? wn * 64 : wn * 128) + lc);
+  const float sb[4] = {sb4.x, sb4.y, sb4.z, sb4.w};
+  const bool full = vec_ok && c0 + 3 < d;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
 #pragma unroll
@@ -319,42 +456,40 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
         *reinterpret_cast<v4i*>(R + fr * RS + j * 32 + 8 * a + 4 * h) =
             v4i{acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
     // (a wave's LDS accesses complete in order: its own reads below see these writes)
-    const int64_t tok_base = t0 + wm * 128 + i * 32;
+    const int tl_base = wm * 128 + i * 32;               // token index inside the block
     if (F == F_INT16) {
       // region row: [hi 0..31 | lo 0..31 | hi 32..63 | lo 32..63] of the wave's 64 outputs
-      const int o = 4 * (lane & 15);                 // first of four outputs of this lane
-      const int hcol = (o >> 5) * 64 + (o & 31);
-      const int64_t c0 = o0 + wn * 64 + o;
-      const bool full = vec_ok && c0 + 3 < d;
+      const int hcol = (lc >> 5) * 64 + (lc & 31);
       for (int rr = 0; rr < 32; rr += 4) {
         const int row = rr + (lane >> 4);
-        const int64_t tok = tok_base + row;
+        const int64_t tok = t0 + tl_base + row;
         if (tok >= M || c0 >= d) continue;
         const v4i hi = *reinterpret_cast<const v4i*>(R + row * RS + hcol);
         const v4i lo = *reinterpret_cast<const v4i*>(R + row * RS + hcol + 32);
-        const int64_t rs128 = 128 * (int64_t)rowsum[tok];
-        const float sxt = sx[tok];
-        uint32_t hv[4];
+        const float sxt = tok_sx[tl_base + row];
+        const double rs128 = 128.0 * (double)tok_rs[tl_base + row];
+        float y[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int64_t exact = 256 * (int64_t)hi[b] + (int64_t)lo[b] + rs128;
-          float y = (float)(double)exact;
-          y = y * sxt;
-          y = y * (c0 + b < d ? sbar[c0 + b] : 0.0f);
-          hv[b] = bf16_rne(y);
+          // exact = 256 acc_hi + acc_lo + 128 rowsum, exact in binary64 (|exact| < 2^53)
+          const double e = fma(256.0, (double)hi[b], (double)lo[b]) + rs128;
+          y[b] = ((float)e * sxt) * sb[b];
         }
+        const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[0], y[1]}, bf2));
+        const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2], y[3]}, bf2));
         uint16_t* Yp = Y + tok * d + c0;
         if (full) {
-          *reinterpret_cast<uint2*>(Yp) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+          *reinterpret_cast<uint2*>(Yp) = make_uint2(p01, p23);
           if (acc_dbg) {
             *reinterpret_cast<v4i*>(acc_dbg + tok * d + c0) = hi;
             *reinterpret_cast<v4i*>(acc_dbg + M * d + tok * d + c0) = lo;
           }
         } else {
+          const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             if (c0 + b < d) {
-              Yp[b] = (uint16_t)hv[b];
+              Yp[b] = hv[b];
               if (acc_dbg) {
                 acc_dbg[tok * d + c0 + b] = hi[b];
                 acc_dbg[M * d + tok * d + c0 + b] = lo[b];
@@ -363,34 +498,31 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
         }
       }
     } else {
-      const int cc = 4 * (lane & 31);                // first of four columns of this lane
-      const int64_t c0 = o0 + wn * 128 + cc;
-      const bool full = vec_ok && c0 + 3 < d;
       for (int rr = 0; rr < 32; rr += 2) {
         const int row = rr + (lane >> 5);
-        const int64_t tok = tok_base + row;
+        const int64_t tok = t0 + tl_base + row;
         if (tok >= M || c0 >= d) continue;
-        const v4i v = *reinterpret_cast<const v4i*>(R + row * RS + cc);
-        const float sxt = sx[tok];
+        const v4i v = *reinterpret_cast<const v4i*>(R + row * RS + lc);
+        const float sxt = tok_sx[tl_base + row];
         int ex[4];
-        uint32_t hv[4];
+        float y[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           ex[b] = (F == F_INT4) ? (v[b] >> 4) : v[b];
-          float y = (float)ex[b];
-          y = y * sxt;
-          y = y * (c0 + b < d ? sbar[c0 + b] : 0.0f);
-          hv[b] = bf16_rne(y);
+          y[b] = ((float)ex[b] * sxt) * sb[b];
         }
+        const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[0], y[1]}, bf2));
+        const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2], y[3]}, bf2));
         uint16_t* Yp = Y + tok * d + c0;
         if (full) {
-          *reinterpret_cast<uint2*>(Yp) = make_uint2(hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16));
+          *reinterpret_cast<uint2*>(Yp) = make_uint2(p01, p23);
           if (acc_dbg) *reinterpret_cast<v4i*>(acc_dbg + tok * d + c0) = v4i{ex[0], ex[1], ex[2], ex[3]};
         } else {
+          const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
 #pragma unroll
           for (int b = 0; b < 4; ++b)
             if (c0 + b < d) {
-              Yp[b] = (uint16_t)hv[b];
+              Yp[b] = hv[b];
               if (acc_dbg) acc_dbg[tok * d + c0 + b] = ex[b];
             }
         }
@@ -398,6 +530,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     }
   }
 }
+
 
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st) {
@@ -409,31 +542,36 @@ hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, cons
   const uint8_t* mb = static_cast<const uint8_t*>(m);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear<F_INT8>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<F_INT8>::LDS);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear<F_INT4>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<F_INT4>::LDS);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_linear<F_INT16>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Cfg<F_INT16>::LDS);
-    if (e != hipSuccess) return e;
+    const void* fns[6] = {reinterpret_cast<const void*>(&k_linear<F_INT8, false>),
+                          reinterpret_cast<const void*>(&k_linear<F_INT8, true>),
+                          reinterpret_cast<const void*>(&k_linear<F_INT4, false>),
+                          reinterpret_cast<const void*>(&k_linear<F_INT4, true>),
+                          reinterpret_cast<const void*>(&k_linear<F_INT16, false>),
+                          reinterpret_cast<const void*>(&k_linear<F_INT16, true>)};
+    const int lds_of[6] = {Cfg<F_INT8>::LDS, Cfg<F_INT8>::LDS, Cfg<F_INT4>::LDS,
+                           Cfg<F_INT4>::LDS, Cfg<F_INT16>::LDS, Cfg<F_INT16>::LDS};
+    for (int k = 0; k < 6; ++k) {
+      const hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, lds_of[k]);
+      if (e != hipSuccess) return e;
+    }
     attr_set = true;
   }
+  const bool tail = (n % BK) != 0;
+#define INTLORA_LAUNCH_LINEAR(FMT)                                                                              \
+  do {                                                                                                        \
+    if (tail)                                                                                                 \
+      hipLaunchKernelGGL((k_linear<FMT, true>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx,      \
+                         rowsum, mb, sbar, Y, acc_dbg, tiles_m, tiles_n);                                     \
+    else                                                                                                      \
+      hipLaunchKernelGGL((k_linear<FMT, false>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx,     \
+                         rowsum, mb, sbar, Y, acc_dbg, tiles_m, tiles_n);                                     \
+  } while (0)
   switch (wfmt) {
-    case F_INT8:
-      hipLaunchKernelGGL(k_linear<F_INT8>, grid, dim3(kThreads), Cfg<F_INT8>::LDS, st, M, d, n, xq, sx, rowsum, mb,
-                         sbar, Y, acc_dbg, tiles_m, tiles_n);
-      break;
-    case F_INT4:
-      hipLaunchKernelGGL(k_linear<F_INT4>, grid, dim3(kThreads), Cfg<F_INT4>::LDS, st, M, d, n, xq, sx, rowsum, mb,
-                         sbar, Y, acc_dbg, tiles_m, tiles_n);
-      break;
-    default:
-      hipLaunchKernelGGL(k_linear<F_INT16>, grid, dim3(kThreads), Cfg<F_INT16>::LDS, st, M, d, n, xq, sx, rowsum, mb,
-                         sbar, Y, acc_dbg, tiles_m, tiles_n);
-      break;
+    case F_INT8: INTLORA_LAUNCH_LINEAR(F_INT8); break;
+    case F_INT4: INTLORA_LAUNCH_LINEAR(F_INT4); break;
+    default: INTLORA_LAUNCH_LINEAR(F_INT16); break;
   }
+#undef INTLORA_LAUNCH_LINEAR
   return hipGetLastError();
 }
 
