@@ -60,13 +60,21 @@ __device__ __forceinline__ uint32_t pick_word(const U4& v, unsigned idx) {
 // units of 2^-53 relative of ln g, far inside the distance of every ln g on this
 // domain from a binary32 rounding midpoint, so the final conversion gives RN32(ln g).
 // --------------------------------------------------------------------------------
-struct LnEntry {
+struct LnEntry {  // as stored (generated table)
   double neg_ln_r_hi;
   float neg_ln_r_lo;
   float r;
 };
 
-__device__ __forceinline__ float ln_odd_g(uint32_t G, const LnEntry* __restrict__ tab) {
+struct LnLds {  // as used, in LDS: every field binary64, r pre-scaled by 2^-24 (exact)
+  double hi, lo, r24;
+};
+
+__device__ __forceinline__ LnLds ln_lds_entry(const LnEntry& e) {
+  return LnLds{e.neg_ln_r_hi, (double)e.neg_ln_r_lo, (double)e.r * 0x1p-24};
+}
+
+__device__ __forceinline__ float ln_odd_g(uint32_t G, const LnLds* __restrict__ tab) {
   // leading-bit position p (0..22); m24 = G << (23 - p) in [2^23, 2^24)
   const int p = 31 - __clz(G);
   uint32_t m24 = G << (23 - p);
@@ -79,9 +87,8 @@ __device__ __forceinline__ float ln_odd_g(uint32_t G, const LnEntry* __restrict_
     F = m24 << 1;
   }
   const int k = (int)((F - 0xC00000u) >> 17);
-  const LnEntry t = tab[k];
-  const double m = (double)F * 0x1p-24;
-  const double f = fma(m, (double)t.r, -1.0);  // exact
+  const LnLds t = tab[k];
+  const double f = fma((double)F, t.r24, -1.0);  // m r_k - 1, exact
   // log1p(f) = f - f^2/2 + ... - f^8/8 truncated after f^7: |f| <= 2^-7 leaves a
   // relative error below 2^-52, far under the 2^-47.6 the rounding needs.
   double p7 = 1.0 / 7.0;
@@ -95,8 +102,8 @@ __device__ __forceinline__ float ln_odd_g(uint32_t G, const LnEntry* __restrict_
   const double LN2_HI = 0x1.62e42fefa3800p-1;
   const double LN2_LO = 0x1.ef35793c76730p-45;
   const double ed = (double)e;
-  const double head = fma(ed, LN2_HI, t.neg_ln_r_hi);
-  const double tail = fma(ed, LN2_LO, (double)t.neg_ln_r_lo);
+  const double head = fma(ed, LN2_HI, t.hi);
+  const double tail = fma(ed, LN2_LO, t.lo);
   const double res = head + (lp + tail);
   return (float)res;
 }
@@ -104,7 +111,7 @@ __device__ __forceinline__ float ln_odd_g(uint32_t G, const LnEntry* __restrict_
 // Laplace(0, 1) sample from one word: u = (2 floor(x / 2^9) + 1) 2^-24, v = u - 1/2,
 // g = 1 - 2|v|, L = -sign(v) ln g.  Computed on integers: N = 2a + 1 - 2^23 is the odd
 // numerator of v (in units of 2^-24), G = 2^23 - |N| the odd numerator of g.
-__device__ __forceinline__ float laplace_from_word(uint32_t x, const LnEntry* __restrict__ tab) {
+__device__ __forceinline__ float laplace_from_word(uint32_t x, const LnLds* __restrict__ tab) {
   const int32_t a = (int32_t)(x >> 9);
   const int32_t N = 2 * a + 1 - (1 << 23);
   const uint32_t G = (uint32_t)((1 << 23) - (N < 0 ? -N : N));
@@ -148,15 +155,28 @@ __device__ __forceinline__ int f32_key(float v) {
   return b ^ ((b >> 31) & 0x7FFFFFFF);
 }
 __device__ __forceinline__ float key_f32(int k) { return __int_as_float(k ^ ((k >> 31) & 0x7FFFFFFF)); }
+// Minimum / maximum over the 64 lanes: DPP row shifts (1, 2, 4, 8) reduce each row of
+// 16 lanes into its lane 15, two row broadcasts fold the rows into lane 63, whose
+// value is returned to every lane.
 __device__ __forceinline__ int wave_min_i32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
-  return v;
+  constexpr int I = 0x7FFFFFFF;
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = min(v, __builtin_amdgcn_update_dpp(I, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 __device__ __forceinline__ int wave_max_i32(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
-  return v;
+  constexpr int I = (int)0x80000000;
+  v = max(v, __builtin_amdgcn_update_dpp(I, v, 0x111, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(I, v, 0x112, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(I, v, 0x114, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(I, v, 0x118, 0xf, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(I, v, 0x142, 0xa, 0xf, false));
+  v = max(v, __builtin_amdgcn_update_dpp(I, v, 0x143, 0xc, 0xf, false));
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 // binary32 -> bfloat16, round to nearest even (inputs are finite).

@@ -22,13 +22,13 @@ __device__ const LnEntry kLnTable[96] = {
 #include "ln_table.inc"
 };
 
-__device__ __forceinline__ void load_ln_table(LnEntry* dst) {
-  for (int t = threadIdx.x; t < 96; t += blockDim.x) dst[t] = kLnTable[t];
+__device__ __forceinline__ void load_ln_table(LnLds* dst) {
+  for (int t = threadIdx.x; t < 96; t += blockDim.x) dst[t] = ln_lds_entry(kLnTable[t]);
 }
 
 // R*_ij for one element (general path).
 __device__ __forceinline__ float rstar_element(uint64_t q, float ci, uint32_t layer_id, uint64_t seed,
-                                               const LnEntry* tab) {
+                                               const LnLds* tab) {
   const U4 blk = philox_block(q >> 2, layer_id, seed);
   return ci * laplace_from_word(pick_word(blk, (unsigned)(q & 3)), tab);
 }
@@ -39,7 +39,7 @@ __device__ __forceinline__ float rstar_element(uint64_t q, float ci, uint32_t la
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
                                               const float* __restrict__ c, float* __restrict__ out) {
-  __shared__ LnEntry tab[96];
+  __shared__ LnLds tab[96];
   load_ln_table(tab);
   __syncthreads();
   const uint64_t total = (uint64_t)d * (uint64_t)n;
@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256) void k_gen_r(int64_t d, int64_t n, uint64_t se
 // Debug: binary32 natural log on odd multiples of 2^-23 (input G, output ln(G 2^-23)).
 __global__ __launch_bounds__(256) void k_ln_odd(int64_t count, const uint32_t* __restrict__ G,
                                                float* __restrict__ out) {
-  __shared__ LnEntry tab[96];
+  __shared__ LnLds tab[96];
   load_ln_table(tab);
   __syncthreads();
   for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < count; t += (int64_t)gridDim.x * blockDim.x)
@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_base_quant(int64_t n, int bits, uint64_
                                                    uint8_t* __restrict__ wround, int32_t* __restrict__ z_out,
                                                    float* __restrict__ s_out) {
   extern __shared__ float xs[];  // n floats
-  __shared__ LnEntry tab[96];
+  __shared__ LnLds tab[96];
   __shared__ float red[4];
   load_ln_table(tab);
   __syncthreads();
@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256) void k_quant_act(int64_t n, const float* __res
 // ---------------------------------------------------------------------------------
 constexpr int kAdaptCols = 1024;  // tile width of the generic path and of CPT = 4
 constexpr int kAdaptMinCols = 512;
-constexpr int kAdaptRows = 8;
+constexpr int kAdaptMaxRows = 16;  // rows per block of the fast path: 8..16, chosen per launch
 
 // Reciprocals RN32(1/w) of the signed pretrained integers w in [-255, 255] (0 for
 // w = 0), for the division t / w below.
@@ -232,14 +232,16 @@ __device__ __forceinline__ void load_rcp_table(float* rcp) {
 // q0 = RN(t y), r = t - q0 w (exact with a fused multiply-add), q = RN(q0 + r y).
 // An exhaustive check over every binary32 significand of t and every such w shows
 // q == RN(t / w); every step scales exactly with t's exponent, so this holds for all
-// |t| in [2^-100, 2^100].  Outside that range the IEEE division is used.
+// |t| in [2^-100, 2^100].  Outside that range (div_small_int_ok false) the caller
+// uses the IEEE division.
 __device__ __forceinline__ float div_small_int(float t, float wf, float y) {
   const float q0 = t * y;
   const float r = fmaf(-q0, wf, t);
-  float q = fmaf(r, y, q0);
+  return fmaf(r, y, q0);
+}
+__device__ __forceinline__ bool div_small_int_ok(float t) {
   const float at = fabsf(t);
-  if (!(at >= 0x1p-100f && at <= 0x1p100f)) q = t / wf;
-  return q;
+  return at >= 0x1p-100f && at <= 0x1p100f;
 }
 
 constexpr int kKeyPosInf = 0x7F800000;  // order key of +inf (identity of min)
@@ -251,11 +253,11 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
                                                    const float* __restrict__ s, const float* __restrict__ c,
                                                    const float* __restrict__ A, const float* __restrict__ B,
                                                    float* __restrict__ U, int* __restrict__ pmin,
-                                                   int* __restrict__ pmax, int ntiles, int64_t rb0,
+                                                   int* __restrict__ pmax, int ntiles, int rows, int64_t rb0,
                                                    unsigned long long* __restrict__ sat_zero) {
-  __shared__ LnEntry tab[96];
+  __shared__ LnLds tab[96];
   __shared__ float rcp[511];
-  __shared__ int smin[4][kAdaptRows], smax[4][kAdaptRows];
+  __shared__ int smin[4][kAdaptMaxRows], smax[4][kAdaptMaxRows];
   load_ln_table(tab);
   load_rcp_table(rcp);
   if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
@@ -276,8 +278,8 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
       b[k][0] = v.x; b[k][1] = v.y;
     }
   }
-  const int64_t i_begin = (rb0 + (int64_t)blockIdx.y) * kAdaptRows;
-  for (int ii = 0; ii < kAdaptRows; ++ii) {
+  const int64_t i_begin = (rb0 + (int64_t)blockIdx.y) * rows;
+  for (int ii = 0; ii < rows; ++ii) {
     const int64_t i = i_begin + ii;
     if (i >= d) break;
     int kmin = kKeyPosInf, kmax = kKeyNegInf;
@@ -300,7 +302,8 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
       const unsigned wsel = CPT == 4 ? 0u : (unsigned)(q0 & 3);  // first word of this thread (0 or 2 when CPT = 2)
       const float ci = c[i], si = s[i];
       const float* Ai = A + i * R;
-      float u[CPT];
+      float u[CPT], t[CPT], q[CPT];
+      bool slow = false;
 #pragma unroll
       for (int e = 0; e < CPT; ++e) {
         float acc = 0.0f;
@@ -308,10 +311,17 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
         for (int k = 0; k < R; ++k) acc = fmaf(Ai[k], b[k][e], acc);
         const uint32_t word = CPT == 4 ? pick_word(rnd, e) : (wsel == 0 ? pick_word(rnd, e) : pick_word(rnd, 2 + e));
         const float rs = ci * laplace_from_word(word, tab);
-        const float t = rs + acc;
+        t[e] = rs + acc;
+        q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+        slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+      }
+#pragma unroll
+      for (int e = 0; e < CPT; ++e)
+        if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+#pragma unroll
+      for (int e = 0; e < CPT; ++e) {
         const bool valid = w[e] != 0;
-        const float q = div_small_int(t, (float)w[e], rcp[w[e] + 255]);
-        const float uu = si + q;
+        const float uu = si + q[e];
         u[e] = valid ? uu : 0.0f;
         const int key = f32_key(uu);
         kmin = valid ? min(kmin, key) : kmin;
@@ -330,7 +340,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
     }
   }
   __syncthreads();
-  if (threadIdx.x < kAdaptRows) {
+  if (threadIdx.x < rows) {
     const int64_t i = i_begin + threadIdx.x;
     if (i < d) {
       const int t = threadIdx.x;
@@ -349,7 +359,7 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
                                                       const float* __restrict__ B, float* __restrict__ U,
                                                       int* __restrict__ pmin, int* __restrict__ pmax, int ntiles,
                                                       unsigned long long* __restrict__ sat_zero) {
-  __shared__ LnEntry tab[96];
+  __shared__ LnLds tab[96];
   __shared__ int smin[4], smax[4];
   load_ln_table(tab);
   if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
@@ -763,25 +773,61 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
 
 int adapt_max_ntiles(int64_t n) { return (int)((n + kAdaptMinCols - 1) / kAdaptMinCols); }
 
-template <int R, int CPT>
-static hipError_t launch_adapt_r(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+// Rows per block of the fast path: the count in 8..16 whose grid best fills the
+// resident block slots of the device (ties go to more rows, which reuse the B
+// columns held in registers over more rows).
+static int adapt_rows(int64_t d, int ntiles, int64_t slots) {
+  int best = 8;
+  double best_eff = -1.0;
+  for (int rows = 8; rows <= kAdaptMaxRows; ++rows) {
+    const int64_t blocks = ((d + rows - 1) / rows) * (int64_t)ntiles;
+    const int64_t rounds = (blocks + slots - 1) / slots;
+    const double eff = (double)blocks / (double)(rounds * slots);
+    if (eff >= best_eff - 1e-9) {
+      best_eff = eff;
+      best = rows;
+    }
+  }
+  return best;
+}
+
+template <int R, int CPT, bool W4>
+static int64_t adapt_slots() {
+  static int64_t slots = 0;
+  if (slots == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_fast<R, CPT, W4>),
+                                                     256, 0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 768;
+    slots = (int64_t)cus * per_cu;
+  }
+  return slots;
+}
+
+template <int R, int CPT, bool W4>
+static hipError_t launch_adapt_rw(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   const int cols = 256 * CPT;
   const int ntiles = (int)((a.n + cols - 1) / cols);
   *ntiles_out = ntiles;
-  const int64_t nrb = (a.d + kAdaptRows - 1) / kAdaptRows;
+  const int rows = adapt_rows(a.d, ntiles, adapt_slots<R, CPT, W4>());
+  const int64_t nrb = (a.d + rows - 1) / rows;
   // grid.y is limited to 65535: very tall matrices take several launches
   for (int64_t rb0 = 0; rb0 < nrb; rb0 += 65535) {
     const int64_t cnt = nrb - rb0 < 65535 ? nrb - rb0 : 65535;
     const dim3 grid((unsigned)ntiles, (unsigned)cnt);
     unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
-    if (a.w_bits == 4)
-      hipLaunchKernelGGL((k_adapt_fast<R, CPT, true>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
-                         a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rb0, sz);
-    else
-      hipLaunchKernelGGL((k_adapt_fast<R, CPT, false>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
-                         a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rb0, sz);
+    hipLaunchKernelGGL((k_adapt_fast<R, CPT, W4>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
+                       a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rows, rb0, sz);
   }
   return hipGetLastError();
+}
+
+template <int R, int CPT>
+static hipError_t launch_adapt_r(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+  return a.w_bits == 4 ? launch_adapt_rw<R, CPT, true>(a, ntiles_out, st) : launch_adapt_rw<R, CPT, false>(a, ntiles_out, st);
 }
 
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
