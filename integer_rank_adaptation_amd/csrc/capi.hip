@@ -73,11 +73,14 @@ int check_opt(const void* p, const char* what) {
   return INTLORA_OK;
 }
 
-// Workspace layout of the merge / U statistics: U (d*n fp32) | pmin | pmax (d*ntiles fp32 each)
+// Workspace layout of the merge / U statistics: U (d*n fp32) | pmin | pmax (d*ntiles
+// order keys each) | umin | umax (d fp32 each)
 struct MergeWs {
   float* U;
   int* pmin;
   int* pmax;
+  float* umin;
+  float* umax;
   int ntiles;
 };
 
@@ -85,7 +88,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t merge_ws_bytes(int64_t d, int64_t n) {
   const size_t nt = (size_t)intlora::adapt_max_ntiles(n);
-  return align256((size_t)d * (size_t)n * 4) + 2 * align256((size_t)d * nt * 4);
+  return align256((size_t)d * (size_t)n * 4) + 2 * align256((size_t)d * nt * 4) + 2 * align256((size_t)d * 4);
 }
 
 MergeWs carve(void* ws, int64_t d, int64_t n) {
@@ -97,6 +100,10 @@ MergeWs carve(void* ws, int64_t d, int64_t n) {
   w.pmin = reinterpret_cast<int*>(p);
   p += align256((size_t)d * (size_t)w.ntiles * 4);  // capacity; the kernels use <= ntiles per row
   w.pmax = reinterpret_cast<int*>(p);
+  p += align256((size_t)d * (size_t)w.ntiles * 4);
+  w.umin = reinterpret_cast<float*>(p);
+  p += align256((size_t)d * 4);
+  w.umax = reinterpret_cast<float*>(p);
   return w;
 }
 
@@ -249,9 +256,12 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
   hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
+  if ((s = launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, st),
+                         "row range")))
+    return s;
   return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
-                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.pmin,
-                                                 w.pmax, w.ntiles, m, s_bar, z_bar, u_round_dbg, sat_count, st),
+                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
+                                                 w.umax, m, s_bar, z_bar, u_round_dbg, sat_count, st),
                        "quant_mul");
 }
 
@@ -270,10 +280,12 @@ int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
+  if ((s = launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, st),
+                         "row range")))
+    return s;
   return launch_status(intlora::launch_quant_shift(desc->d, desc->n, desc->w_bits, v_bits,
-                                                   static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.pmin,
-                                                   w.pmax, w.ntiles, static_cast<uint8_t*>(m), s_bar, shift_dbg,
-                                                   sat_count, st),
+                                                   static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
+                                                   w.umax, static_cast<uint8_t*>(m), s_bar, shift_dbg, sat_count, st),
                        "quant_shift");
 }
 

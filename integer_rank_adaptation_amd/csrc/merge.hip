@@ -216,7 +216,6 @@ __global__ __launch_bounds__(256) void k_quant_act(int64_t n, const float* __res
 // (needs n % 4 == 0).  U is written for every element (0 where w == 0).
 // ---------------------------------------------------------------------------------
 constexpr int kAdaptCols = 1024;  // tile width of the generic path and of CPT = 4
-constexpr int kAdaptMinCols = 512;
 constexpr int kAdaptMaxRows = 16;  // rows per block of the fast path: 8..16, chosen per launch
 
 // Reciprocals RN32(1/w) of the signed pretrained integers w in [-255, 255] (0 for
@@ -347,6 +346,122 @@ __global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uin
       pmin[i * ntiles + blockIdx.x] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
       pmax[i * ntiles + blockIdx.x] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
     }
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// Adaptation with the rank-r product on the matrix cores.  v_mfma_f32_32x32x1f32
+// adds one product per output per instruction as a fused multiply-add (one
+// rounding), so a chain of r of them in k order reproduces the fmaf chain of the
+// definition exactly.  The product is taken transposed (MFMA rows = columns j of U,
+// MFMA columns = rows i), so each lane receives, per group of four accumulators,
+// four consecutive columns of one row: one Philox block per group.  A wave covers
+// 32 rows x 64 columns per row tile (two 32-column MFMA blocks over the same rows);
+// a block of 4 waves covers 256 columns and `rtiles` row tiles, keeping its B
+// columns in registers across them.
+// ---------------------------------------------------------------------------------
+typedef float v32f __attribute__((ext_vector_type(32)));
+constexpr int kMfmaCols = 256;
+constexpr int kMfmaMaxRowTiles = 8;
+
+template <int R, bool W4>
+__global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
+                                                    const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
+                                                    const float* __restrict__ s, const float* __restrict__ c,
+                                                    const float* __restrict__ A, const float* __restrict__ B,
+                                                    float* __restrict__ U, int* __restrict__ pmin,
+                                                    int* __restrict__ pmax, int ntiles, int rtiles, int64_t rb0,
+                                                    unsigned long long* __restrict__ sat_zero) {
+  __shared__ LnLds tab[96];
+  __shared__ float rcp[511];
+  __shared__ int smin[4][32], smax[4][32];
+  load_ln_table(tab);
+  load_rcp_table(rcp);
+  if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int h = lane >> 5, li = lane & 31;
+  const int64_t jw = (int64_t)blockIdx.x * kMfmaCols + wid * 64;  // the wave's first column
+  // MFMA A operand: lane l holds B[k][jw + l] for every k
+  float bcol[R];
+  {
+    const int64_t jl = jw + lane;
+#pragma unroll
+    for (int k = 0; k < R; ++k) bcol[k] = jl < n ? B[(int64_t)k * n + jl] : 0.0f;
+  }
+  for (int rt = 0; rt < rtiles; ++rt) {
+    const int64_t i0 = ((rb0 + (int64_t)blockIdx.y) * rtiles + rt) * 32;
+    if (i0 >= d) break;  // uniform over the block
+    const int64_t i = i0 + li;
+    const bool row_ok = i < d;
+    // MFMA B operand: lane l holds A[i0 + l % 32][k]
+    const float* Ai = A + (row_ok ? i : 0) * R;
+    v32f acc;
+#pragma unroll
+    for (int r = 0; r < 32; ++r) acc[r] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < R; k += 4) {
+      float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (row_ok) a4 = *reinterpret_cast<const float4*>(Ai + k);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k], a4.x, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k + 1], a4.y, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k + 2], a4.z, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k + 3], a4.w, acc, 0, 0, 0);
+    }
+    int kmin = kKeyPosInf, kmax = kKeyNegInf;
+    if (row_ok) {
+      const int zi = z[i];
+      const float ci = c[i], si = s[i];
+      // accumulator group g = 4 blk + q: columns jw + 32 blk + 8 q + 4 h + 0..3
+#pragma unroll
+      for (int g = 0; g < 8; ++g) {
+        const int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
+        if (jg >= n) continue;  // n % 4 == 0: a group is entirely inside or outside
+        int w[4];
+        if (W4) {
+          const uint32_t v = *reinterpret_cast<const uint16_t*>(wround + i * (n >> 1) + (jg >> 1));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (int)((v >> (4 * e)) & 15u) - zi;
+        } else {
+          const uint32_t v = *reinterpret_cast<const uint32_t*>(wround + i * n + jg);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (int)((v >> (8 * e)) & 255u) - zi;
+        }
+        const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
+        float u[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
+          const float t = rs + acc[4 * g + e];
+          float q = div_small_int(t, (float)w[e], rcp[w[e] + 255]);
+          if (w[e] != 0 && !div_small_int_ok(t)) q = t / (float)w[e];
+          const bool valid = w[e] != 0;
+          const float uu = si + q;
+          u[e] = valid ? uu : 0.0f;
+          const int key = f32_key(uu);
+          kmin = valid ? min(kmin, key) : kmin;
+          kmax = valid ? max(kmax, key) : kmax;
+        }
+        *reinterpret_cast<float4*>(U + i * n + jg) = make_float4(u[0], u[1], u[2], u[3]);
+      }
+    }
+    // lanes l and l ^ 32 hold the same row
+    kmin = min(kmin, __shfl_xor(kmin, 32, kWave));
+    kmax = max(kmax, __shfl_xor(kmax, 32, kWave));
+    if (h == 0) {
+      smin[wid][li] = kmin;
+      smax[wid][li] = kmax;
+    }
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int t = threadIdx.x;
+      const int64_t row = i0 + t;
+      if (row < d) {
+        pmin[row * ntiles + blockIdx.x] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
+        pmax[row * ntiles + blockIdx.x] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
+      }
+    }
+    __syncthreads();  // smin / smax are reused by the next row tile
   }
 }
 
@@ -509,8 +624,8 @@ template <bool W4>
 __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, int u_bits,
                                                         const uint8_t* __restrict__ wround,
                                                         const int32_t* __restrict__ z, const float* __restrict__ U,
-                                                        const int* __restrict__ pmin, const int* __restrict__ pmax,
-                                                        int ntiles, int16_t* __restrict__ m,
+                                                        const float* __restrict__ umin_r,
+                                                        const float* __restrict__ umax_r, int16_t* __restrict__ m,
                                                         float* __restrict__ sbar_out, int32_t* __restrict__ zbar_out,
                                                         uint8_t* __restrict__ uround_dbg,
                                                         unsigned long long* __restrict__ sat) {
@@ -536,8 +651,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
         if (i >= d) break;
-        float umin, umax;
-        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const float umin = umin_r[i], umax = umax_r[i];
         const MulParams P = mul_params(umin, umax, qmax);
         if (blockIdx.x == 0 && threadIdx.x == 0) {
           sbar_out[i] = P.sbar;
@@ -566,8 +680,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
         if (i >= d) break;
-        float umin, umax;
-        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const float umin = umin_r[i], umax = umax_r[i];
         const MulParams P = mul_params(umin, umax, qmax);
         if (blockIdx.x == 0 && threadIdx.x == 0) {
           sbar_out[i] = P.sbar;
@@ -624,8 +737,8 @@ template <bool W4>
 __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n, int v_bits,
                                                           const uint8_t* __restrict__ wround,
                                                           const int32_t* __restrict__ z, const float* __restrict__ U,
-                                                          const int* __restrict__ pmin, const int* __restrict__ pmax,
-                                                          int ntiles, uint8_t* __restrict__ m,
+                                                          const float* __restrict__ umin_r,
+                                                          const float* __restrict__ umax_r, uint8_t* __restrict__ m,
                                                           float* __restrict__ sbar_out,
                                                           uint8_t* __restrict__ shift_dbg,
                                                           unsigned long long* __restrict__ sat) {
@@ -652,8 +765,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
         if (i >= d) break;
-        float umin, umax;
-        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const float umin = umin_r[i], umax = umax_r[i];
         const float sbar = shift_scale(umin, umax);
         if (blockIdx.x == 0 && threadIdx.x == 0) sbar_out[i] = sbar;
         if (j0 >= n) continue;
@@ -688,8 +800,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
         if (i >= d) break;
-        float umin, umax;
-        row_range(pmin, pmax, i, ntiles, umin, umax);
+        const float umin = umin_r[i], umax = umax_r[i];
         const float sbar = shift_scale(umin, umax);
         if (blockIdx.x == 0 && threadIdx.x == 0) sbar_out[i] = sbar;
         const int zi = z[i];
@@ -771,7 +882,7 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
   return hipGetLastError();
 }
 
-int adapt_max_ntiles(int64_t n) { return (int)((n + kAdaptMinCols - 1) / kAdaptMinCols); }
+int adapt_max_ntiles(int64_t n) { return (int)((n + kMfmaCols - 1) / kMfmaCols); }
 
 // Rows per block of the fast path: the count in 8..16 whose grid best fills the
 // resident block slots of the device (ties go to more rows, which reuse the B
@@ -830,16 +941,67 @@ static hipError_t launch_adapt_r(const AdaptArgs& a, int* ntiles_out, hipStream_
   return a.w_bits == 4 ? launch_adapt_rw<R, CPT, true>(a, ntiles_out, st) : launch_adapt_rw<R, CPT, false>(a, ntiles_out, st);
 }
 
+template <int R, bool W4>
+static int64_t mfma_slots() {
+  static int64_t slots = 0;
+  if (slots == 0) {
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_mfma<R, W4>), 256,
+                                                     0) != hipSuccess ||
+        cus <= 0 || per_cu <= 0)
+      return 1024;
+    slots = (int64_t)cus * per_cu;
+  }
+  return slots;
+}
+
+template <int R, bool W4>
+static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+  const int ntiles = (int)((a.n + kMfmaCols - 1) / kMfmaCols);
+  *ntiles_out = ntiles;
+  const int64_t row_tiles = (a.d + 31) / 32;
+  const int64_t slots = mfma_slots<R, W4>();
+  // row tiles per block (1..8): the count whose grid best fills the resident slots
+  int rtiles = 1;
+  double best = -1.0;
+  for (int rt = 1; rt <= kMfmaMaxRowTiles; ++rt) {
+    const int64_t blocks = ((row_tiles + rt - 1) / rt) * (int64_t)ntiles;
+    const int64_t rounds = (blocks + slots - 1) / slots;
+    const double eff = (double)blocks / (double)(rounds * slots);
+    if (eff >= best - 1e-9) {
+      best = eff;
+      rtiles = rt;
+    }
+  }
+  const int64_t nrb = (row_tiles + rtiles - 1) / rtiles;
+  for (int64_t rb0 = 0; rb0 < nrb; rb0 += 65535) {
+    const int64_t cnt = nrb - rb0 < 65535 ? nrb - rb0 : 65535;
+    const dim3 grid((unsigned)ntiles, (unsigned)cnt);
+    unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
+    hipLaunchKernelGGL((k_adapt_mfma<R, W4>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround, a.z,
+                       a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rtiles, rb0, sz);
+  }
+  return hipGetLastError();
+}
+
+template <int R>
+static hipError_t launch_adapt_m(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+  return a.w_bits == 4 ? launch_adapt_mfma<R, true>(a, ntiles_out, st) : launch_adapt_mfma<R, false>(a, ntiles_out, st);
+}
+
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   const bool fast_ok = (a.n % 4) == 0 && ((reinterpret_cast<uintptr_t>(a.B) | reinterpret_cast<uintptr_t>(a.U)) & 15) == 0 &&
-                       (reinterpret_cast<uintptr_t>(a.wround) & 3) == 0;
+                       (reinterpret_cast<uintptr_t>(a.wround) & 3) == 0 &&
+                       (reinterpret_cast<uintptr_t>(a.A) & 15) == 0;
   if (fast_ok && !a.force_generic) {
     switch (a.r) {
-      case 4: return launch_adapt_r<4, 4>(a, ntiles_out, st);
-      case 8: return launch_adapt_r<8, 4>(a, ntiles_out, st);
-      case 16: return launch_adapt_r<16, 4>(a, ntiles_out, st);
-      case 32: return launch_adapt_r<32, 4>(a, ntiles_out, st);
-      case 64: return launch_adapt_r<64, 2>(a, ntiles_out, st);
+      case 4: return launch_adapt_m<4>(a, ntiles_out, st);
+      case 8: return launch_adapt_m<8>(a, ntiles_out, st);
+      case 16: return launch_adapt_m<16>(a, ntiles_out, st);
+      case 32: return launch_adapt_m<32>(a, ntiles_out, st);
+      case 64: return launch_adapt_m<64>(a, ntiles_out, st);
       default: break;
     }
   }
@@ -863,29 +1025,28 @@ static dim3 quant_grid(int64_t d, int64_t n) {
 }
 
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
-                            const float* U, const int* pmin, const int* pmax, int ntiles, int16_t* m,
-                            float* sbar, int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat,
-                            hipStream_t st) {
+                            const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
+                            int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st) {
   const dim3 grid = quant_grid(d, n);
   if (w_bits == 4)
-    hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, pmin, pmax, ntiles,
-                       m, sbar, zbar, uround_dbg, sat);
+    hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
+                       sbar, zbar, uround_dbg, sat);
   else
-    hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, pmin, pmax,
-                       ntiles, m, sbar, zbar, uround_dbg, sat);
+    hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
+                       sbar, zbar, uround_dbg, sat);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
-                              const float* U, const int* pmin, const int* pmax, int ntiles, uint8_t* m,
-                              float* sbar, uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st) {
+                              const float* U, const float* umin, const float* umax, uint8_t* m, float* sbar,
+                              uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st) {
   const dim3 grid = quant_grid(d, n);
   if (w_bits == 4)
-    hipLaunchKernelGGL(k_quant_shift<true>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, pmin, pmax,
-                       ntiles, m, sbar, shift_dbg, sat);
+    hipLaunchKernelGGL(k_quant_shift<true>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, umin, umax, m,
+                       sbar, shift_dbg, sat);
   else
-    hipLaunchKernelGGL(k_quant_shift<false>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, pmin, pmax,
-                       ntiles, m, sbar, shift_dbg, sat);
+    hipLaunchKernelGGL(k_quant_shift<false>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, umin, umax, m,
+                       sbar, shift_dbg, sat);
   return hipGetLastError();
 }
 
