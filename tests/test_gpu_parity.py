@@ -227,6 +227,29 @@ def test_merge_tall_matrices(ops, d, n, w_bits):
     assert np.array_equal(bits(host(h["sbar"])[rows]), bits(ref2["sbar"]))
 
 
+@pytest.mark.parametrize("scale_a,scale_b,scale_c", [(2.0**-70, 2.0**-72, 2.0**-140), (2.0**-60, 2.0**-60, 0.0),
+                                                     (2.0**55, 2.0**52, 2.0**100), (1.0, 1.0, 0.0)])
+def test_merge_extreme_magnitudes(ops, scale_a, scale_b, scale_c):
+    """Products A_ik B_kj in the subnormal range, sums past 2^100 and R* = 0: the
+    matrix-core product chain, the division (its reciprocal path and the IEEE fallback
+    outside 2^-100 .. 2^100) and the range reduction all match the oracle bit for bit."""
+    d, n, r, w_bits = 40, 512, 32, 8
+    wr, z, s, c, A, Bm = random_state(77, d, n, r, w_bits)
+    A = (A * np.float32(scale_a)).astype(np.float32)
+    Bm = (Bm * np.float32(scale_b)).astype(np.float32)
+    c = np.full(d, scale_c, np.float32)
+    st = gpu_state(wr, z, s, c, w_bits)
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), w_bits, 8, 9, 4, dbg=True)
+    umin, umax = ops.u_minmax(st, cuda(A), cuda(Bm), w_bits, 9, 4)
+    R = oracle.gen_r_rows(0, d, n, 9, 4, c)
+    ref = oracle.merge_mul(wr, z, s, R, A, Bm, 8)
+    assert np.array_equal(bits(host(umin)), bits(ref["umin"]))
+    assert np.array_equal(bits(host(umax)), bits(ref["umax"]))
+    assert np.array_equal(host(g["uround"]), ref["uround"])
+    assert np.array_equal(host(g["m"]), ref["m"])
+    assert int(host(g["sat"])[0]) == ref["sat"]
+
+
 def test_merge_is_deterministic(ops):
     wr, z, s, c, A, Bm = random_state(9, 64, 3072, 32, 4)
     st = gpu_state(wr, z, s, c, 4)
