@@ -428,15 +428,26 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
           for (int e = 0; e < 4; ++e) w[e] = (int)((v >> (8 * e)) & 255u) - zi;
         }
         const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
-        float u[4];
+        float u[4], t[4], q[4];
+        bool slow = false;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
-          const float t = rs + acc[4 * g + e];
-          float q = div_small_int(t, (float)w[e], rcp[w[e] + 255]);
-          if (w[e] != 0 && !div_small_int_ok(t)) q = t / (float)w[e];
+          t[e] = rs + acc[4 * g + e];
+          q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+          slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+        }
+        // the IEEE division runs only in waves where some lane needs it
+        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+          __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
           const bool valid = w[e] != 0;
-          const float uu = si + q;
+          const float uu = si + q[e];
           u[e] = valid ? uu : 0.0f;
           const int key = f32_key(uu);
           kmin = valid ? min(kmin, key) : kmin;
