@@ -18,7 +18,7 @@ struct AdaptArgs {
   const float* A;
   const float* B;
   float* U;
-  int* pmin;  // per (row, column tile) order keys of the U range
+  int* pmin;  // order keys of the U range per (column tile, row), tile-major: pmin[tile * d + row]
   int* pmax;
   unsigned long long* sat_zero;  // zeroed by the adaptation kernel (nullable)
   bool force_generic;

@@ -216,7 +216,6 @@ __global__ __launch_bounds__(256) void k_quant_act(int64_t n, const float* __res
 // (needs n % 4 == 0).  U is written for every element (0 where w == 0).
 // ---------------------------------------------------------------------------------
 constexpr int kAdaptCols = 1024;  // tile width of the generic path and of CPT = 4
-constexpr int kAdaptMaxRows = 16;  // rows per block of the fast path: 8..16, chosen per launch
 
 // Reciprocals RN32(1/w) of the signed pretrained integers w in [-255, 255] (0 for
 // w = 0), for the division t / w below.
@@ -245,109 +244,6 @@ __device__ __forceinline__ bool div_small_int_ok(float t) {
 
 constexpr int kKeyPosInf = 0x7F800000;  // order key of +inf (identity of min)
 constexpr int kKeyNegInf = (int)0x807FFFFF;  // order key of -inf (identity of max)
-
-template <int R, int CPT, bool W4>
-__global__ __launch_bounds__(256, 3) void k_adapt_fast(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
-                                                   const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
-                                                   const float* __restrict__ s, const float* __restrict__ c,
-                                                   const float* __restrict__ A, const float* __restrict__ B,
-                                                   float* __restrict__ U, int* __restrict__ pmin,
-                                                   int* __restrict__ pmax, int ntiles, int rows, int64_t rb0,
-                                                   unsigned long long* __restrict__ sat_zero) {
-  __shared__ LnLds tab[96];
-  __shared__ float rcp[511];
-  __shared__ int smin[4][kAdaptMaxRows], smax[4][kAdaptMaxRows];
-  load_ln_table(tab);
-  load_rcp_table(rcp);
-  if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
-  __syncthreads();
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-  const int64_t j0 = (int64_t)blockIdx.x * (256 * CPT) + (int64_t)threadIdx.x * CPT;
-  const bool active = j0 < n;
-  float b[R][CPT];
-#pragma unroll
-  for (int k = 0; k < R; ++k) {
-    if (CPT == 4) {
-      float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (active) v = *reinterpret_cast<const float4*>(B + (int64_t)k * n + j0);
-      b[k][0] = v.x; b[k][1] = v.y; b[k][2 % CPT] = v.z; b[k][3 % CPT] = v.w;
-    } else {
-      float2 v = make_float2(0.f, 0.f);
-      if (active) v = *reinterpret_cast<const float2*>(B + (int64_t)k * n + j0);
-      b[k][0] = v.x; b[k][1] = v.y;
-    }
-  }
-  const int64_t i_begin = (rb0 + (int64_t)blockIdx.y) * rows;
-  for (int ii = 0; ii < rows; ++ii) {
-    const int64_t i = i_begin + ii;
-    if (i >= d) break;
-    int kmin = kKeyPosInf, kmax = kKeyNegInf;
-    if (active) {
-      int w[CPT];
-      const int zi = z[i];
-      if (W4) {
-        const uint32_t v = CPT == 4 ? *reinterpret_cast<const uint16_t*>(wround + i * (n >> 1) + (j0 >> 1))
-                                    : wround[i * (n >> 1) + (j0 >> 1)];
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) w[e] = (int)((v >> (4 * e)) & 15u) - zi;
-      } else {
-        const uint32_t v = CPT == 4 ? *reinterpret_cast<const uint32_t*>(wround + i * n + j0)
-                                    : *reinterpret_cast<const uint16_t*>(wround + i * n + j0);
-#pragma unroll
-        for (int e = 0; e < CPT; ++e) w[e] = (int)((v >> (8 * e)) & 255u) - zi;
-      }
-      const uint64_t q0 = (uint64_t)i * (uint64_t)n + (uint64_t)j0;
-      const U4 rnd = philox_block(q0 >> 2, layer_id, seed);
-      const unsigned wsel = CPT == 4 ? 0u : (unsigned)(q0 & 3);  // first word of this thread (0 or 2 when CPT = 2)
-      const float ci = c[i], si = s[i];
-      const float* Ai = A + i * R;
-      float u[CPT], t[CPT], q[CPT];
-      bool slow = false;
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < R; ++k) acc = fmaf(Ai[k], b[k][e], acc);
-        const uint32_t word = CPT == 4 ? pick_word(rnd, e) : (wsel == 0 ? pick_word(rnd, e) : pick_word(rnd, 2 + e));
-        const float rs = ci * laplace_from_word(word, tab);
-        t[e] = rs + acc;
-        q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
-        slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
-      }
-#pragma unroll
-      for (int e = 0; e < CPT; ++e)
-        if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
-#pragma unroll
-      for (int e = 0; e < CPT; ++e) {
-        const bool valid = w[e] != 0;
-        const float uu = si + q[e];
-        u[e] = valid ? uu : 0.0f;
-        const int key = f32_key(uu);
-        kmin = valid ? min(kmin, key) : kmin;
-        kmax = valid ? max(kmax, key) : kmax;
-      }
-      if (CPT == 4)
-        *reinterpret_cast<float4*>(U + i * n + j0) = make_float4(u[0], u[1], u[2 % CPT], u[3 % CPT]);
-      else
-        *reinterpret_cast<float2*>(U + i * n + j0) = make_float2(u[0], u[1]);
-    }
-    kmin = wave_min_i32(kmin);
-    kmax = wave_max_i32(kmax);
-    if (lane == 0) {
-      smin[wid][ii] = kmin;
-      smax[wid][ii] = kmax;
-    }
-  }
-  __syncthreads();
-  if (threadIdx.x < rows) {
-    const int64_t i = i_begin + threadIdx.x;
-    if (i < d) {
-      const int t = threadIdx.x;
-      pmin[i * ntiles + blockIdx.x] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
-      pmax[i * ntiles + blockIdx.x] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------------
 // Adaptation with the rank-r product on the matrix cores.  v_mfma_f32_32x32x1f32
@@ -468,8 +364,8 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
       const int t = threadIdx.x;
       const int64_t row = i0 + t;
       if (row < d) {
-        pmin[row * ntiles + blockIdx.x] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
-        pmax[row * ntiles + blockIdx.x] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
+        pmin[(int64_t)blockIdx.x * d + row] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
+        pmax[(int64_t)blockIdx.x * d + row] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
       }
     }
     __syncthreads();  // smin / smax are reused by the next row tile
@@ -524,8 +420,8 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
   }
   __syncthreads();
   if (threadIdx.x == 0) {
-    pmin[i * ntiles + blockIdx.x] = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
-    pmax[i * ntiles + blockIdx.x] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
+    pmin[(int64_t)blockIdx.x * d + i] = min(min(smin[0], smin[1]), min(smin[2], smin[3]));
+    pmax[(int64_t)blockIdx.x * d + i] = max(max(smax[0], smax[1]), max(smax[2], smax[3]));
   }
   __syncthreads();  // smin / smax are reused by the next row
   }
@@ -534,12 +430,13 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
 // Row range from the tile partials (order keys; uniform per block).  U_min / U_max
 // are the least / greatest valid U of the row in the IEEE total order (+inf / -inf
 // for a row without valid elements).
-__device__ __forceinline__ void row_range(const int* __restrict__ pmin, const int* __restrict__ pmax, int64_t i,
-                                          int ntiles, float& umin, float& umax) {
+__device__ __forceinline__ void row_range(const int* __restrict__ pmin, const int* __restrict__ pmax, int64_t d,
+                                          int64_t i, int ntiles, float& umin, float& umax) {
   int kmin = kKeyPosInf, kmax = kKeyNegInf;
+#pragma unroll 8
   for (int t = 0; t < ntiles; ++t) {
-    kmin = min(kmin, pmin[i * ntiles + t]);
-    kmax = max(kmax, pmax[i * ntiles + t]);
+    kmin = min(kmin, pmin[(int64_t)t * d + i]);
+    kmax = max(kmax, pmax[(int64_t)t * d + i]);
   }
   umin = key_f32(kmin);
   umax = key_f32(kmax);
@@ -552,7 +449,7 @@ __global__ __launch_bounds__(256) void k_row_range(int64_t d, int ntiles, const 
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < d) {
     float a, b;
-    row_range(pmin, pmax, i, ntiles, a, b);
+    row_range(pmin, pmax, d, i, ntiles, a, b);
     umin[i] = a;
     umax[i] = b;
   }
@@ -576,6 +473,7 @@ constexpr int kQRows = 2;
 
 struct MulParams {
   float sbar;
+  float rsbar;  // RN(1 / s_bar)
   int zbar;
 };
 
@@ -587,7 +485,7 @@ __device__ __forceinline__ MulParams mul_params(float umin, float umax, int qmax
   if (!(sbar > 0.0f)) sbar = 1.0f;
   const float zf = rintf(-lo / sbar);
   const int zbar = zf < 0.0f ? 0 : (zf > (float)qmax ? qmax : (int)zf);
-  return MulParams{sbar, zbar};
+  return MulParams{sbar, 1.0f / sbar, zbar};
 }
 
 // U_round = clamp(rint(U / s_bar) + z_bar, 0, 2^bU - 1)
@@ -595,6 +493,23 @@ __device__ __forceinline__ int mul_code(float u, float sbar, int zbar, int qmax)
   float q = rintf(u / sbar);
   q = fminf(fmaxf(q, -65536.0f), 65536.0f);
   const int v = (int)q + zbar;
+  return v < 0 ? 0 : (v > qmax ? qmax : v);
+}
+
+// U_round from q = U * RN(1/s_bar) instead of RN(U / s_bar).  With RN(1/s_bar) a
+// normal number, q lies within (2^-23 + 2^-48) |U/s_bar| of U/s_bar and RN(U/s_bar)
+// within 2^-24 |U/s_bar|, so for |q| < 512 the two are less than 2^-13 apart; when q
+// is farther than 2^-11 from every half-integer they round to the same integer.
+// `exact` is false otherwise (also for a non-finite q or a subnormal RN(1/s_bar)),
+// and the caller then recomputes the code with the IEEE division.
+// (Every valid U lies in [lo, hi], so |U / s_bar| <= 2^bU - 1 < 512 whenever s_bar
+// is the row's own scale.)
+__device__ __forceinline__ int mul_code_fast(float u, const MulParams& P, int qmax, bool& exact) {
+  const float qt = u * P.rsbar;
+  const float fr = qt - floorf(qt);
+  exact = fabsf(qt) < 512.0f && fabsf(fr - 0.5f) > 0x1p-11f && P.rsbar >= 0x1p-126f;
+  const float q = fminf(fmaxf(rintf(qt), -65536.0f), 65536.0f);
+  const int v = (int)q + P.zbar;
   return v < 0 ? 0 : (v > qmax ? qmax : v);
 }
 
@@ -671,9 +586,30 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         if (j0 >= n) continue;
         const int zi = z[i];
         const float uu[8] = {ua[rr].x, ua[rr].y, ua[rr].z, ua[rr].w, ub[rr].x, ub[rr].y, ub[rr].z, ub[rr].w};
-        int mm[8], ur[8];
+        int mm[8], ur[8], w[8];
+        bool redo[8], any = false;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mm[e] = mul_merge(code_of<W4>(cw[rr], e) - zi, uu[e], P, qmax, ur[e], nsat);
+        for (int e = 0; e < 8; ++e) {
+          w[e] = code_of<W4>(cw[rr], e) - zi;
+          bool exact = true;
+          ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, qmax, exact) : P.zbar;
+          redo[e] = !exact;
+          any = any || redo[e];
+        }
+        // the IEEE division runs only in waves where some lane needs it
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+          __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (redo[e]) ur[e] = mul_code(uu[e], P.sbar, P.zbar, qmax);
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          int mv = w[e] != 0 ? (ur[e] - P.zbar) * w[e] : 0;
+          if (mv > 32767) { mv = 32767; ++nsat; }
+          if (mv < -32768) { mv = -32768; ++nsat; }
+          mm[e] = mv;
+        }
         int4 pk;
         pk.x = (mm[0] & 0xFFFF) | (mm[1] << 16);
         pk.y = (mm[2] & 0xFFFF) | (mm[3] << 16);
@@ -894,63 +830,6 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
 }
 
 int adapt_max_ntiles(int64_t n) { return (int)((n + kMfmaCols - 1) / kMfmaCols); }
-
-// Rows per block of the fast path: the count in 8..16 whose grid best fills the
-// resident block slots of the device (ties go to more rows, which reuse the B
-// columns held in registers over more rows).
-static int adapt_rows(int64_t d, int ntiles, int64_t slots) {
-  int best = 8;
-  double best_eff = -1.0;
-  for (int rows = 8; rows <= kAdaptMaxRows; ++rows) {
-    const int64_t blocks = ((d + rows - 1) / rows) * (int64_t)ntiles;
-    const int64_t rounds = (blocks + slots - 1) / slots;
-    const double eff = (double)blocks / (double)(rounds * slots);
-    if (eff >= best_eff - 1e-9) {
-      best_eff = eff;
-      best = rows;
-    }
-  }
-  return best;
-}
-
-template <int R, int CPT, bool W4>
-static int64_t adapt_slots() {
-  static int64_t slots = 0;
-  if (slots == 0) {
-    int dev = 0, cus = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_fast<R, CPT, W4>),
-                                                     256, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0)
-      return 768;
-    slots = (int64_t)cus * per_cu;
-  }
-  return slots;
-}
-
-template <int R, int CPT, bool W4>
-static hipError_t launch_adapt_rw(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
-  const int cols = 256 * CPT;
-  const int ntiles = (int)((a.n + cols - 1) / cols);
-  *ntiles_out = ntiles;
-  const int rows = adapt_rows(a.d, ntiles, adapt_slots<R, CPT, W4>());
-  const int64_t nrb = (a.d + rows - 1) / rows;
-  // grid.y is limited to 65535: very tall matrices take several launches
-  for (int64_t rb0 = 0; rb0 < nrb; rb0 += 65535) {
-    const int64_t cnt = nrb - rb0 < 65535 ? nrb - rb0 : 65535;
-    const dim3 grid((unsigned)ntiles, (unsigned)cnt);
-    unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
-    hipLaunchKernelGGL((k_adapt_fast<R, CPT, W4>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround,
-                       a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rows, rb0, sz);
-  }
-  return hipGetLastError();
-}
-
-template <int R, int CPT>
-static hipError_t launch_adapt_r(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
-  return a.w_bits == 4 ? launch_adapt_rw<R, CPT, true>(a, ntiles_out, st) : launch_adapt_rw<R, CPT, false>(a, ntiles_out, st);
-}
 
 template <int R, bool W4>
 static int64_t mfma_slots() {
