@@ -45,6 +45,9 @@ def parse():
                    help="fraction of rows/tokens the oracle processes (0: auto, about 15 s)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--json-out", default="")
+    p.add_argument("--overlap", action="store_true",
+                   help="also time a pipelined step: merges on a second stream, each layer's linear layer "
+                        "waiting only for its own merge")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -192,6 +195,44 @@ def main():
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
 
+    # ---------------------------------------------------------------- pipelined step (optional)
+    overlap_ms = None
+    if args.overlap:
+        ms_stream = torch.cuda.Stream()
+        done_merge = [torch.cuda.Event() for _ in layers]
+        done_gemm = [torch.cuda.Event() for _ in layers]
+
+        def step_overlap():
+            for k, lay in enumerate(layers):
+                with torch.cuda.stream(ms_stream):
+                    ms_stream.wait_event(done_gemm[k])  # the previous step's reader of out[k]
+                    if mode == "mul":
+                        ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
+                                      lay["lid"], ws=ws, out=lay["out"])
+                    else:
+                        ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
+                                        lay["lid"], ws=ws, out=lay["out"])
+                    done_merge[k].record(ms_stream)
+                stream.wait_event(done_merge[k])
+                ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"],
+                           lay["L"].d, out=lay["Y"])
+                done_gemm[k].record(stream)
+
+        for ev_ in done_gemm:
+            ev_.record(stream)
+        for _ in range(args.warmup):
+            step_overlap()
+        torch.cuda.synchronize()
+        t0_ = torch.cuda.Event(enable_timing=True)
+        t1_ = torch.cuda.Event(enable_timing=True)
+        t0_.record(stream)
+        ms_stream.wait_event(t0_)
+        for _ in range(args.steps):
+            step_overlap()
+        t1_.record(stream)
+        torch.cuda.synchronize()
+        overlap_ms = t0_.elapsed_time(t1_) / args.steps
+
     # ---------------------------------------------------------------- per-layer figures
     per_layer = []
     roof_ms = 0.0
@@ -244,6 +285,7 @@ def main():
                  "effective_TOPS": round(gemm_ops_tot / (2 if mode == "mul" else 1) / (gemm_ms_tot * 1e-3) / 1e12, 1),
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
         "per_layer": per_layer,
+        "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
         "setup_s": round(setup_s, 1),
     }
 
