@@ -60,11 +60,16 @@ constexpr int A_BYTES = BM * BK;                // 16 KB
 constexpr int B_BYTES_8 = 256 * BK;             // 16 KB: 256 output rows x 64 int8
 constexpr int B_BYTES_16 = 128 * BK * 2;        // 16 KB: 128 output rows x 64 int16
 constexpr int B_BYTES_4 = 256 * BK / 2;         // 8 KB: 256 output rows x 64 nibbles
+constexpr int EPI_RS = 64 * 2 + 16;             // epilogue staging row: 64 bf16 outputs + 16 bytes pad
+constexpr int EPI_WAVE = 32 * EPI_RS;           // one wave's 32 tokens x 64 outputs
+constexpr int EPI_VEC = 4 * EPI_WAVE;           // offset of the per-tile vectors in the epilogue region
+constexpr int EPI_BYTES = EPI_VEC + 3 * 4 * 256;
 template <int F>
 struct Cfg {
   static constexpr int B_BYTES = F == F_INT16 ? B_BYTES_16 : (F == F_INT8 ? B_BYTES_8 : B_BYTES_4);
   static constexpr int STAGE = A_BYTES + B_BYTES;
-  static constexpr int LDS = kStages * STAGE;
+  static constexpr int RING = kStages * STAGE;
+  static constexpr int LDS = RING + EPI_BYTES;
   static constexpr int OUT = F == F_INT16 ? 128 : 256;         // outputs per block
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;           // direct loads per wave per stage
   static constexpr int B_LOADS = B_BYTES / 1024 / 4;
@@ -314,6 +319,34 @@ __device__ __forceinline__ void mfma16(const v4i (&af)[4], const v4i (&bf)[4], v
     for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(bf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
+// Reads an accumulator where it is used: without this the compiler copies all 256
+// accumulators out of the AGPRs at once after the main loop (and spills them).
+__device__ __forceinline__ int acc_read(int v) {
+  int r;
+  __asm__ volatile("v_accvgpr_read_b32 %0, %1" : "=v"(r) : "a"(v));
+  return r;
+}
+
+// Tile id -> (token tile, weight tile): tile ids are walked in groups of kGroupM token
+// tiles (token tile fastest inside a group), so consecutive ids form near-square
+// patches that share operands in L2.
+__device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, int& tm, int& tn) {
+  using namespace lin;
+  const int group = tile / (kGroupM * tiles_n);
+  const int tm_first = group * kGroupM;
+  const int gsize = (tiles_m - tm_first) < kGroupM ? (tiles_m - tm_first) : kGroupM;
+  const int in_group = tile - group * kGroupM * tiles_n;
+  tm = tm_first + in_group % gsize;
+  tn = in_group / gsize;
+}
+
+// Persistent kernel: each block owns the tiles r * G + slot (r = 0, 1, ...), where G is
+// the grid size and slot renumbers the block so that each of the 8 XCDs (blocks are
+// dealt to them round-robin) receives a contiguous range of slots, i.e. a compact
+// patch of tiles in every round.  The K stages of a block's consecutive tiles form one
+// continuous stream through the LDS ring: the loads of the next tile's first stages
+// are issued during the current tile's last iterations, and the epilogue (which has
+// an LDS region of its own) runs while they are in flight.
 template <int F, bool KTAIL>
 __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t d, int64_t n,
                                                             const int8_t* __restrict__ xq,
@@ -328,209 +361,230 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   const int wm = wid >> 1, wn = wid & 1;
   constexpr int OUT = Cfg<F>::OUT;
   constexpr int STAGE = Cfg<F>::STAGE;
-
-  // Blocks are dealt round-robin to the 8 XCDs; renumber so that each XCD receives a
-  // contiguous range of tile ids, then walk tile ids in groups of kGroupM token tiles
-  // (weight-tile index fastest inside a group), so that the blocks resident on one XCD
-  // at a time cover a near-square patch of tiles and share operands in its L2.
-  const int nblk = tiles_m * tiles_n;
-  int bid = blockIdx.x;
+  const int ntile = tiles_m * tiles_n;
+  const int G = gridDim.x;
+  int slot = blockIdx.x;
   {
-    const int per = nblk / 8, rem = nblk % 8;
-    const int x = bid % 8, loc = bid / 8;
+    const int per = G / 8, rem = G % 8;
+    const int x = slot % 8, loc = slot / 8;
     const int base = x * per + (x < rem ? x : rem);
-    if (loc < per + (x < rem ? 1 : 0)) bid = base + loc;
+    if (loc < per + (x < rem ? 1 : 0)) slot = base + loc;
   }
-  const int group = bid / (kGroupM * tiles_n);
-  const int tm_first = group * kGroupM;
-  const int gsize = (tiles_m - tm_first) < kGroupM ? (tiles_m - tm_first) : kGroupM;
-  const int in_group = bid - group * kGroupM * tiles_n;
-  const int tm = tm_first + in_group % gsize, tn = in_group / gsize;
-  const int64_t t0 = (int64_t)tm * BM;
-  const int64_t o0 = (int64_t)tn * OUT;
-
-  // Operand tiles: this block's first token row / first output row.
-  const int8_t* a_tile = xq + t0 * n;
-  const int64_t a_bytes = (M - t0) * n;
+  const int my_tiles = slot < ntile ? (ntile - slot + G - 1) / G : 0;
   const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
-  const uint8_t* b_tile = m + o0 * wrow;
-  const int64_t b_bytes = (d - o0) * wrow;
+  const int KT = (int)((n + BK - 1) / BK);
+  const int fr = lane & 31, h = lane >> 5;
   Plan<F> plan;
   make_plan<F>((int)n, plan);
 
-  v16i acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+  // operand tiles of local tile lt (null range past the block's last tile: zero loads)
+  auto tile_ptrs = [&](int lt, const int8_t*& at, int64_t& ab, const uint8_t*& bt, int64_t& bb) {
+    if (lt < my_tiles) {
+      int tm, tn;
+      tile_coords(lt * G + slot, tiles_m, tiles_n, tm, tn);
+      at = xq + (int64_t)tm * BM * n;
+      ab = (M - (int64_t)tm * BM) * n;
+      bt = m + (int64_t)tn * OUT * wrow;
+      bb = (d - (int64_t)tn * OUT) * wrow;
+    } else {
+      at = xq;
+      ab = 0;
+      bt = m;
+      bb = 0;
+    }
+  };
+  const int8_t* a_cur;
+  const uint8_t* b_cur;
+  int64_t ab_cur, bb_cur;
+  const int8_t* a_nxt;
+  const uint8_t* b_nxt;
+  int64_t ab_nxt, bb_nxt;
+  tile_ptrs(0, a_cur, ab_cur, b_cur, bb_cur);
+  tile_ptrs(1, a_nxt, ab_nxt, b_nxt, bb_nxt);
 
-  const int KT = (int)((n + BK - 1) / BK);
-  const int fr = lane & 31, h = lane >> 5;
-  // The loop body is one basic block so that the schedule below holds: stages past
-  // the end are still issued, reading zeros (empty descriptor range) into a ring
-  // buffer that is never read again, and the fragment reads of stage k+1 at the last
-  // iteration fetch unused data.  vmcnt accounting is then uniform.
-  issue_stage<F, KTAIL>(0, (int)n, a_tile, a_bytes, b_tile, b_bytes, plan, lds);
-  issue_stage<F, KTAIL>(1, (int)n, a_tile, a_bytes, b_tile, b_bytes, plan, lds + STAGE);
-  issue_stage<F, KTAIL>(2, (int)n, a_tile, a_bytes, b_tile, b_bytes, plan, lds + 2 * STAGE);
+  // stages 0..2 of the stream (KT >= 3 whenever a block owns more than one tile)
+#pragma unroll
+  for (int g = 0; g < 3; ++g) {
+    if (g < KT)
+      issue_stage<F, KTAIL>(g, (int)n, a_cur, ab_cur, b_cur, bb_cur, plan, lds + g * STAGE);
+    else
+      issue_stage<F, KTAIL>(g - KT, (int)n, a_nxt, ab_nxt, b_nxt, bb_nxt, plan, lds + g * STAGE);
+  }
   wait_vmcnt<2 * Cfg<F>::LOADS>();
   __builtin_amdgcn_s_barrier();
-  // Two operand sets: set 0 feeds the MFMAs of sub-step 0 of a stage while set 1 is
-  // read from LDS and converted, and the other way round for sub-step 1.
   v4i a0[4], b0[4], a1[4], b1[4];
   RawB<F> rw;
   read_a(lds, wm, 0, fr, h, a0);
   read_b<F>(lds + A_BYTES, wn, 0, fr, h, rw);
   convert_b<F>(rw, b0);
 
-  for (int kt = 0; kt < KT; ++kt) {
-    // stage kt+1 has landed (loads of kt+2 may still be in flight); after the barrier
-    // it is visible to all waves and nobody reads stage kt-1, whose buffer kt+3 reuses
-    wait_vmcnt<Cfg<F>::LOADS>();
-    __builtin_amdgcn_s_barrier();
-    uint8_t* ldst = lds + ((kt + 3) % kStages) * STAGE;
-    const uint8_t* S0 = lds + (kt % kStages) * STAGE;
-    const uint8_t* S1 = lds + ((kt + 1) % kStages) * STAGE;
-    // Each half (one 32-deep K sub-step): 16 MFMAs on the current operand set,
-    // interleaved one by one with the LDS reads of the next set (first eight MFMAs),
-    // the stage's direct loads (first half, one per MFMA) and the conversion of the
-    // next set (last eight MFMAs).  sched_barrier fixes the order.
-    // sub-step 0 of stage kt on set 0; set 1 <- sub-step 1 of stage kt; loads of kt+3
+  uint8_t* epi = lds + Cfg<F>::RING;
+  int g = 0;  // global stage index of the stream
+  for (int lt = 0; lt < my_tiles; ++lt) {
+    v16i acc[4][4];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[q & 3], a0[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
-      if (q < 8) read_piece<F>(q, S0, wm, wn, 1, fr, h, a1, rw);
-      if (q >= 8 && q - 8 < (Cfg<F>::LOADS + 1) / 2)
-        issue_load<F, KTAIL>(q - 8, (int)n, kt + 3, a_tile, a_bytes, b_tile, b_bytes, plan, ldst);
-      if (q >= 8) convert_piece<F>(q - 8, rw, b1);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // sub-step 1 of stage kt on set 1; set 0 <- sub-step 0 of stage kt+1
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[q & 3], a1[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
-      if (q < 8) read_piece<F>(q, S1, wm, wn, 0, fr, h, a0, rw);
-      if (q >= 8 && q - 8 + (Cfg<F>::LOADS + 1) / 2 < Cfg<F>::LOADS)
-        issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kt + 3, a_tile, a_bytes, b_tile, b_bytes, plan, ldst);
-      if (q >= 8) convert_piece<F>(q - 8, rw, b0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+    for (int kt = 0; kt < KT; ++kt, ++g) {
+      // stage g+1 has landed (loads of g+2 may still be in flight); after the barrier it
+      // is visible to all waves and nobody reads stage g-1, whose buffer g+3 reuses
+      wait_vmcnt<Cfg<F>::LOADS>();
+      __builtin_amdgcn_s_barrier();
+      // stage g+3 is stage kt+3 of this tile or stage kt+3-KT of the next one
+      const bool same = kt + 3 < KT;
+      const int kl = same ? kt + 3 : kt + 3 - KT;
+      const int8_t* al = same ? a_cur : a_nxt;
+      const uint8_t* bl = same ? b_cur : b_nxt;
+      const int64_t abl = same ? ab_cur : ab_nxt;
+      const int64_t bbl = same ? bb_cur : bb_nxt;
+      uint8_t* ldst = lds + ((g + 3) % kStages) * STAGE;
+      const uint8_t* S0 = lds + (g % kStages) * STAGE;
+      const uint8_t* S1 = lds + ((g + 1) % kStages) * STAGE;
+      // Each half (one 32-deep K sub-step): 16 MFMAs on the current operand set,
+      // interleaved one by one with the LDS reads of the next set (first eight MFMAs),
+      // the stage's direct loads (spread over both halves) and the conversion of the
+      // next set (last eight MFMAs).  sched_barrier fixes the order.
+      // sub-step 0 of stage g on set 0; set 1 <- sub-step 1 of stage g
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[q & 3], a0[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
+        if (q < 8) read_piece<F>(q, S0, wm, wn, 1, fr, h, a1, rw);
+        if (q >= 8 && q - 8 < (Cfg<F>::LOADS + 1) / 2)
+          issue_load<F, KTAIL>(q - 8, (int)n, kl, al, abl, bl, bbl, plan, ldst);
+        if (q >= 8) convert_piece<F>(q - 8, rw, b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // sub-step 1 of stage g on set 1; set 0 <- sub-step 0 of stage g+1
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[q & 3], a1[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
+        if (q < 8) read_piece<F>(q, S1, wm, wn, 0, fr, h, a0, rw);
+        if (q >= 8 && q - 8 + (Cfg<F>::LOADS + 1) / 2 < Cfg<F>::LOADS)
+          issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kl, al, abl, bl, bbl, plan, ldst);
+        if (q >= 8) convert_piece<F>(q - 8, rw, b0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
-  }
-  wait_vmcnt<0>();  // the trailing zero-reading loads land before LDS is reused
 
-  // Epilogue.  The block's per-token scales / row sums and per-output scales are
-  // staged in LDS first, so the conversion loop below issues no global loads.  Then
-  // one 32-token slab (i) at a time: each wave writes its 32 x 128 int32 accumulators
-  // as 16-byte groups (lane l, registers 4a..4a+3 of tile j are token l % 32, MFMA
-  // columns 32 j + 8 a + 4 (l / 32) + 0..3) into a padded region of its own, then
-  // reads them back row-contiguously; each lane finishes four outputs per row.
-  __syncthreads();
-  constexpr int RS = 132;                              // padded row stride (ints): conflict-free
-  constexpr int kVec = 4 * 32 * RS * 4;                // after the four wave regions
-  float* tok_sx = reinterpret_cast<float*>(lds + kVec);
-  int32_t* tok_rs = reinterpret_cast<int32_t*>(lds + kVec + 4 * BM);
-  float* col_sb = reinterpret_cast<float*>(lds + kVec + 8 * BM);
-  {
-    const int64_t t = t0 + tid;
-    tok_sx[tid] = t < M ? sx[t] : 0.0f;
-    if (F == F_INT16) tok_rs[tid] = t < M ? rowsum[t] : 0;
-    if (tid < OUT) col_sb[tid] = o0 + tid < d ? sbar[o0 + tid] : 0.0f;
-  }
-  __syncthreads();
-  int32_t* R = reinterpret_cast<int32_t*>(lds) + wid * (32 * RS);
-  const bool vec_ok = (d & 3) == 0;
-  // the lane's four output columns are fixed for the whole epilogue
-  const int lc = F == F_INT16 ? 4 * (lane & 15) : 4 * (lane & 31);   // first column in the wave's tile
-  const int64_t c0 = o0 + (F == F_INT16 ? wn * 64 : wn * 128) + lc;
-  const float4 sb4 = *reinterpret_cast<const float4*>(col_sb + (F == F_INT16 ? wn * 64 : wn * 128) + lc);
-  const float sb[4] = {sb4.x, sb4.y, sb4.z, sb4.w};
-  const bool full = vec_ok && c0 + 3 < d;
+    // ------------------------------------------------------------ epilogue of tile lt
+    int tm, tn;
+    tile_coords(lt * G + slot, tiles_m, tiles_n, tm, tn);
+    const int64_t t0 = (int64_t)tm * BM;
+    const int64_t o0 = (int64_t)tn * OUT;
+    float* tok_sx = reinterpret_cast<float*>(epi + EPI_VEC);
+    int32_t* tok_rs = reinterpret_cast<int32_t*>(epi + EPI_VEC + 4 * BM);
+    float* col_sb = reinterpret_cast<float*>(epi + EPI_VEC + 8 * BM);
+    {
+      const int64_t t = t0 + tid;
+      tok_sx[tid] = t < M ? sx[t] : 0.0f;
+      if (F == F_INT16) tok_rs[tid] = t < M ? rowsum[t] : 0;
+      if (tid < OUT) col_sb[tid] = o0 + tid < d ? sbar[o0 + tid] : 0.0f;
+    }
+    __syncthreads();
+    uint8_t* stg = epi + wid * EPI_WAVE;
+    constexpr int PASSES = F == F_INT16 ? 1 : 2;  // 64 outputs of the wave per pass
+    const bool vec_ok = (d & 7) == 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 4; ++i) {
+      __builtin_amdgcn_sched_barrier(0);  // read one slab's accumulators at a time
+      const int tl = wm * 128 + i * 32 + fr;  // this lane's token inside the block
+      const float sxt = tok_sx[tl];
+      const double rs128 = F == F_INT16 ? 128.0 * (double)tok_rs[tl] : 0.0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+      for (int p = 0; p < PASSES; ++p) {
+        __builtin_amdgcn_sched_barrier(0);
+        // outputs of this pass, in MFMA layout: lane l, registers 4a..4a+3 of column tile
+        // j are token l % 32 and MFMA columns 32 j + 8 a + 4 (l / 32) + 0..3
 #pragma unroll
-      for (int a = 0; a < 4; ++a)
-        *reinterpret_cast<v4i*>(R + fr * RS + j * 32 + 8 * a + 4 * h) =
-            v4i{acc[i][j][4 * a], acc[i][j][4 * a + 1], acc[i][j][4 * a + 2], acc[i][j][4 * a + 3]};
-    // (a wave's LDS accesses complete in order: its own reads below see these writes)
-    const int tl_base = wm * 128 + i * 32;               // token index inside the block
-    if (F == F_INT16) {
-      // region row: [hi 0..31 | lo 0..31 | hi 32..63 | lo 32..63] of the wave's 64 outputs
-      const int hcol = (lc >> 5) * 64 + (lc & 31);
-      for (int rr = 0; rr < 32; rr += 4) {
-        const int row = rr + (lane >> 4);
-        const int64_t tok = t0 + tl_base + row;
-        if (tok >= M || c0 >= d) continue;
-        const v4i hi = *reinterpret_cast<const v4i*>(R + row * RS + hcol);
-        const v4i lo = *reinterpret_cast<const v4i*>(R + row * RS + hcol + 32);
-        const float sxt = tok_sx[tl_base + row];
-        const double rs128 = 128.0 * (double)tok_rs[tl_base + row];
-        float y[4];
+        for (int jj = 0; jj < 2; ++jj) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          // exact = 256 acc_hi + acc_lo + 128 rowsum, exact in binary64 (|exact| < 2^53)
-          const double e = fma(256.0, (double)hi[b], (double)lo[b]) + rs128;
-          y[b] = ((float)e * sxt) * sb[b];
-        }
-        const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[0], y[1]}, bf2));
-        const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2], y[3]}, bf2));
-        uint16_t* Yp = Y + tok * d + c0;
-        if (full) {
-          *reinterpret_cast<uint2*>(Yp) = make_uint2(p01, p23);
-          if (acc_dbg) {
-            *reinterpret_cast<v4i*>(acc_dbg + tok * d + c0) = hi;
-            *reinterpret_cast<v4i*>(acc_dbg + M * d + tok * d + c0) = lo;
-          }
-        } else {
-          const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
+          for (int a = 0; a < 4; ++a) {
+            __builtin_amdgcn_sched_barrier(0);
+            const int oc = 32 * jj + 8 * a + 4 * h;                       // output column in the pass
+            const int ow = (F == F_INT16 ? 0 : 64 * p) + oc;              // output column in the wave
+            const float4 sb = *reinterpret_cast<const float4*>(col_sb + (F == F_INT16 ? wn * 64 : wn * 128) + ow);
+            const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
+            float y[4];
 #pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (c0 + b < d) {
-              Yp[b] = hv[b];
-              if (acc_dbg) {
-                acc_dbg[tok * d + c0 + b] = hi[b];
-                acc_dbg[M * d + tok * d + c0 + b] = lo[b];
+            for (int e = 0; e < 4; ++e) {
+              if (F == F_INT16) {
+                const int hi = acc_read(acc[i][2 * jj][4 * a + e]), lo = acc_read(acc[i][2 * jj + 1][4 * a + e]);
+                // exact = 256 acc_hi + acc_lo + 128 rowsum, exact in binary64 (|exact| < 2^53)
+                const double ex = fma(256.0, (double)hi, (double)lo) + rs128;
+                y[e] = ((float)ex * sxt) * sbv[e];
+              } else {
+                const int v = acc_read(acc[i][2 * p + jj][4 * a + e]);
+                y[e] = ((float)(F == F_INT4 ? (v >> 4) : v) * sxt) * sbv[e];
               }
             }
-        }
-      }
-    } else {
-      for (int rr = 0; rr < 32; rr += 2) {
-        const int row = rr + (lane >> 5);
-        const int64_t tok = t0 + tl_base + row;
-        if (tok >= M || c0 >= d) continue;
-        const v4i v = *reinterpret_cast<const v4i*>(R + row * RS + lc);
-        const float sxt = tok_sx[tl_base + row];
-        int ex[4];
-        float y[4];
+            const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[0], y[1]}, bf2));
+            const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2], y[3]}, bf2));
+            *reinterpret_cast<uint2*>(stg + fr * EPI_RS + 2 * oc) = make_uint2(p01, p23);
+            if (acc_dbg) {
+              const int64_t tok = t0 + tl;
+              const int64_t c = o0 + (F == F_INT16 ? wn * 64 : wn * 128) + ow;
+              if (tok < M) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          ex[b] = (F == F_INT4) ? (v[b] >> 4) : v[b];
-          y[b] = ((float)ex[b] * sxt) * sb[b];
-        }
-        const uint32_t p01 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[0], y[1]}, bf2));
-        const uint32_t p23 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y[2], y[3]}, bf2));
-        uint16_t* Yp = Y + tok * d + c0;
-        if (full) {
-          *reinterpret_cast<uint2*>(Yp) = make_uint2(p01, p23);
-          if (acc_dbg) *reinterpret_cast<v4i*>(acc_dbg + tok * d + c0) = v4i{ex[0], ex[1], ex[2], ex[3]};
-        } else {
-          const uint16_t hv[4] = {(uint16_t)p01, (uint16_t)(p01 >> 16), (uint16_t)p23, (uint16_t)(p23 >> 16)};
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (c0 + b < d) {
-              Yp[b] = hv[b];
-              if (acc_dbg) acc_dbg[tok * d + c0 + b] = ex[b];
+                for (int e = 0; e < 4; ++e) {
+                  if (c + e >= d) continue;
+                  if (F == F_INT16) {
+                    acc_dbg[tok * d + c + e] = acc_read(acc[i][2 * jj][4 * a + e]);
+                    acc_dbg[M * d + tok * d + c + e] = acc_read(acc[i][2 * jj + 1][4 * a + e]);
+                  } else {
+                    const int v = acc_read(acc[i][2 * p + jj][4 * a + e]);
+                    acc_dbg[tok * d + c + e] = F == F_INT4 ? (v >> 4) : v;
+                  }
+                }
+              }
             }
+          }
+        }
+        // (a wave's LDS accesses complete in order: its reads below see its writes)
+        // 32 tokens x 64 outputs, read back row-contiguously: 8 lanes x 16 bytes per row
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          const int row = s4 * 8 + (lane >> 3);
+          const int col8 = 8 * (lane & 7);
+          const int64_t tok = t0 + wm * 128 + i * 32 + row;
+          const int64_t c = o0 + (F == F_INT16 ? wn * 64 : wn * 128 + 64 * p) + col8;
+          const uint4 v = *reinterpret_cast<const uint4*>(stg + row * EPI_RS + 2 * col8);
+          if (tok < M && c < d) {
+            uint16_t* Yp = Y + tok * d + c;
+            if (vec_ok && c + 7 < d) {
+              *reinterpret_cast<uint4*>(Yp) = v;
+            } else {
+              const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (c + e < d) Yp[e] = (uint16_t)(w4[e >> 1] >> (16 * (e & 1)));
+            }
+          }
         }
       }
     }
+    // the next tile streams in; the one after it becomes "next"
+    a_cur = a_nxt;
+    b_cur = b_nxt;
+    ab_cur = ab_nxt;
+    bb_cur = bb_nxt;
+    tile_ptrs(lt + 2, a_nxt, ab_nxt, b_nxt, bb_nxt);
   }
+  wait_vmcnt<0>();  // trailing (zero-reading) loads land before the block's LDS is released
 }
 
+static int device_cus() {
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                 hipSuccess || cus <= 0)
+      cus = 256;
+  }
+  return cus;
+}
 
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st) {
@@ -538,7 +592,12 @@ hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, cons
   const int out_per_block = (wfmt == F_INT16) ? Cfg<F_INT16>::OUT : Cfg<F_INT8>::OUT;
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((d + out_per_block - 1) / out_per_block);
-  const dim3 grid((unsigned)(tiles_m * tiles_n));
+  const int ntile = tiles_m * tiles_n;
+  const int KT = (int)((n + BK - 1) / BK);
+  // one block per compute unit, each streaming several tiles; with fewer than three K
+  // stages per tile the stream cannot span tiles, so every block takes one tile
+  const int cus = device_cus();
+  const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
   const uint8_t* mb = static_cast<const uint8_t*>(m);
   static bool attr_set = false;
   if (!attr_set) {
