@@ -466,6 +466,13 @@ __device__ __forceinline__ void add_saturations(unsigned long long* sat, int loc
 // all of its loads (U, W_round codes) are issued before any element is computed.
 // Row groups are walked grid-stride, so any d fits the grid.
 // ---------------------------------------------------------------------------------
+typedef float vf4 __attribute__((ext_vector_type(4)));
+// 16-byte load that does not keep the line in the caches (U is read once).
+__device__ __forceinline__ float4 load_once4(const float* p) {
+  const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+
 constexpr int kQThreads = 128;
 constexpr int kQElems = 8;
 constexpr int kQCols = kQThreads * kQElems;
@@ -569,8 +576,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         const int64_t i = i0 + rr;
         if (i < d && j0 < n) {
           cw[rr] = load_codes8<W4>(wround, i, n, j0);
-          ua[rr] = *reinterpret_cast<const float4*>(U + i * n + j0);
-          ub[rr] = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
+          ua[rr] = load_once4(U + i * n + j0);
+          ub[rr] = load_once4(U + i * n + j0 + 4);
         }
       }
 #pragma unroll
@@ -704,8 +711,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
         const int64_t i = i0 + rr;
         if (i < d && j0 < n) {
           cw[rr] = load_codes8<W4>(wround, i, n, j0);
-          ua[rr] = *reinterpret_cast<const float4*>(U + i * n + j0);
-          ub[rr] = *reinterpret_cast<const float4*>(U + i * n + j0 + 4);
+          ua[rr] = load_once4(U + i * n + j0);
+          ub[rr] = load_once4(U + i * n + j0 + 4);
         }
       }
 #pragma unroll
