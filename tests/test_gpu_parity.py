@@ -309,6 +309,43 @@ def test_linear_bitexact(ops, wfmt, M, d, n):
     _linear_case(ops, M, d, n, wfmt, seed=M * 7 + d * 3 + n + wfmt)
 
 
+@pytest.mark.parametrize("M,d,n,wfmt", [
+    (2600, 4000, 224, 16),  # 352 tiles: blocks own 1 or 2 tiles; partial last K stage; ragged M and d
+    (5000, 4000, 224, 8),   # 320 tiles, partial last K stage
+    (5000, 4000, 192, 4),   # 320 tiles, K an exact multiple of the stage depth
+    (4100, 9000, 96, 16),   # 1207 tiles with only two K stages each: one tile per block
+])
+def test_linear_many_tiles(ops, M, d, n, wfmt):
+    """More tiles than compute units (each block streams several tiles' K stages through
+    one LDS ring), K tails and ragged edges; every output is compared with the oracle, and
+    the run without the accumulator dump gives the same outputs."""
+    rng = np.random.Generator(np.random.PCG64(M + d + n + wfmt))
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(M + 1, M, 1e-3, 0.1)
+    sbar = synth.random_positive(d + 2, d, 1e-5, 1e-2)
+    rs = xq.astype(np.int32).sum(axis=1).astype(np.int32)
+    if wfmt == 16:
+        m = rng.integers(-32768, 32768, size=(d, n)).astype(np.int16)
+        mg = cuda(m)
+    elif wfmt == 8:
+        m = rng.integers(-128, 128, size=(d, n)).astype(np.int8)
+        mg = cuda(m)
+    else:
+        m = rng.integers(-8, 8, size=(d, n)).astype(np.int8)
+        mg = cuda(pack4(m.astype(np.uint8) & 15))
+    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, acc_dbg=True)
+    Y2, _ = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d)
+    exact, _, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
+    acc = host(acc).astype(np.int64)
+    if wfmt == 16:
+        got = 256 * acc[0] + acc[1] + 128 * rs.astype(np.int64)[:, None]
+    else:
+        got = acc[0]
+    assert np.array_equal(got, exact)
+    assert np.array_equal(host(Y).view(np.uint16), yref)
+    assert np.array_equal(host(Y2).view(np.uint16), yref)
+
+
 # ----------------------------------------------------------------------------- workloads
 def _gpu_pipeline(ops, wl, li, d, n, M, mode, bits_):
     W = synth.weight(wl, li, d=d, n=n)
