@@ -150,6 +150,7 @@ def main():
             lay["out"] = dict(m=torch.empty((L.d, L.n), dtype=torch.int16, device=dev),
                               sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
                               zbar=torch.empty(L.d, dtype=torch.int32, device=dev),
+                              split=torch.empty(L.d, dtype=torch.uint8, device=dev),
                               sat=torch.zeros(2, dtype=torch.int64, device=dev))
             lay["wfmt"] = B.INTLORA_W_INT16
         else:
@@ -176,7 +177,7 @@ def main():
             if events is not None:
                 events[k][1].record(stream)
             ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"], lay["L"].d,
-                       out=lay["Y"])
+                       out=lay["Y"], split=lay["out"].get("split"))
             if events is not None:
                 events[k][2].record(stream)
 
@@ -215,7 +216,7 @@ def main():
                     done_merge[k].record(ms_stream)
                 stream.wait_event(done_merge[k])
                 ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"],
-                           lay["L"].d, out=lay["Y"])
+                           lay["L"].d, out=lay["Y"], split=lay["out"].get("split"))
                 done_gemm[k].record(stream)
 
         for ev_ in done_gemm:

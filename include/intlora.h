@@ -159,10 +159,12 @@ int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vm
  * (counted).  Reading for w == 0 (zero MLA denominator): excluded from the range,
  * U_round = z_bar, m = 0.  The merged weight is s_bar_i * m_ij.
  * Outputs: m (int16 d x n), s_bar[d], z_bar[d]; optional (NULL to skip):
- * u_round_dbg (uint8 d x n), sat_count (one uint64, overwritten with the number of
- * saturated elements).  u_bits in [2, 8].  Workspace: INTLORA_OP_MERGE_MUL. */
+ * m_split[d] (uint8 per row: 1 if some m of the row is >= 32640, else 0 -- the split
+ * codes intlora_linear_fwd takes), u_round_dbg (uint8 d x n), sat_count (one uint64,
+ * overwritten with the number of saturated elements).  u_bits in [2, 8].
+ * Workspace: INTLORA_OP_MERGE_MUL. */
 int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
-                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* u_round_dbg,
+                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
                       unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
 
 /* IntLoRA_SHIFT merge (section "two implementation variants", SHIFT).  U as for MUL.
@@ -189,16 +191,25 @@ int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s
  *   exact = sum_j xq[t,j] * m[i,j] (integer);
  *   y = RN32(RN32(float(exact) * s_x[t]) * s_bar[i]),  Y = bf16 round-to-nearest-even.
  * wfmt INTLORA_W_INT8 / INTLORA_W_INT4 (SHIFT merged integers): one int8 MFMA pass.
- * wfmt INTLORA_W_INT16 (MUL merged integers): bias byte split hi = m >> 8,
- * lo = (m & 0xFF) - 128, two int8 MFMA passes, exact = 256 acc_hi + acc_lo +
- * 128 x_rowsum[t] in int64 (x_rowsum required).
+ * wfmt INTLORA_W_INT16 (MUL merged integers): two int8 MFMA passes over a byte split
+ * of m (x_rowsum required), one split for the whole call, chosen from the split codes
+ * m_split[i] (uint8 per row, 0 or 1; NULL = all 1):
+ *   some row coded 1 (any int16): bias split hi = m >> 8, lo = (m & 0xFF) - 128,
+ *      exact = 256 acc_hi + acc_lo + 128 x_rowsum[t];
+ *   every row coded 0 (the caller guarantees each m[i, j] <= 32639, as the codes
+ *      written by intlora_merge_mul do): balanced split hi = (m + 128) >> 8,
+ *      lo = m - 256 hi, exact = 256 acc_hi + acc_lo;
+ * combined exactly (int64-exact binary64).  Both give the same Y; the balanced split
+ * leaves the high plane zero for |m| < 128, which the matrix cores run at lower power.
+ * Codes of 0 on a matrix holding m >= 32640 give unspecified outputs.
+ * m_split must be NULL for the other formats (INTLORA_EINVAL).
  * xq: M x n int8; m: d x n (layout per wfmt); Y_bf16: M x d (bf16 bits, row-major);
  * acc_dbg (optional): planes x M x d int32 raw accumulators (planes = 2 for INT16:
- * hi then lo; 1 otherwise).  n must be a multiple of 32 and <= 131071 (no int32
+ * hi then lo of the split applied; 1 otherwise).  n must be a multiple of 32 and <= 131071 (no int32
  * overflow).  No workspace. */
 int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x, const int32_t* x_rowsum,
-                       int wfmt, const void* m, const float* s_bar, uint16_t* Y_bf16, int32_t* acc_dbg, void* ws,
-                       size_t ws_bytes, void* stream);
+                       int wfmt, const void* m, const uint8_t* m_split, const float* s_bar, uint16_t* Y_bf16,
+                       int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream);
 
 /* Diagnostic: the binary32 natural log used by intlora_gen_r, on g = G * 2^-23 for
  * odd G in [1, 2^23) (the only values it is ever given): out[t] = RN32(ln(G[t] 2^-23)).

@@ -56,11 +56,11 @@ _SIG = {
     "intlora_vmc_scale": (_INT, [_I64, _P, ctypes.c_double, _P, _P]),
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
-                                 _P, _P, _P, ctypes.c_size_t, _P]),
+                                 _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_shift": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_quant_act": (_INT, [_I64, _I64, _P, _P, _P, _P, _P]),
-    "intlora_linear_fwd": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "intlora_linear_fwd": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_debug_ln": (_INT, [_I64, _P, _P, _P]),
 }
 
@@ -149,12 +149,12 @@ def intlora_base_quant(dsc: Desc, W, vmc_c, w_round_out, z_out, s_out, stream=No
                                     _ptr(s_out), _stream(stream)), "intlora_base_quant")
 
 
-def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, u_round_dbg=None, sat_count=None,
-                      ws=None, stream=None):
+def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None, u_round_dbg=None,
+                      sat_count=None, ws=None, stream=None):
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(m),
-                                   _ptr(s_bar), _ptr(z_bar), _ptr(u_round_dbg), _ptr(sat_count), _ptr(ws), wsb,
-                                   _stream(stream)), "intlora_merge_mul")
+                                   _ptr(s_bar), _ptr(z_bar), _ptr(m_split), _ptr(u_round_dbg), _ptr(sat_count),
+                                   _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
 
 
 def intlora_merge_shift(dsc: Desc, bs: Base, lr: Lora, v_bits: int, m, s_bar, shift_dbg=None, sat_count=None, ws=None,
@@ -170,11 +170,11 @@ def intlora_quant_act(M: int, n: int, X, xq, s_x, x_rowsum=None, stream=None):
            "intlora_quant_act")
 
 
-def intlora_linear_fwd(M: int, d: int, n: int, xq, s_x, x_rowsum, wfmt: int, m, s_bar, Y_bf16, acc_dbg=None, ws=None,
-                       stream=None):
+def intlora_linear_fwd(M: int, d: int, n: int, xq, s_x, x_rowsum, wfmt: int, m, m_split, s_bar, Y_bf16, acc_dbg=None,
+                       ws=None, stream=None):
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().intlora_linear_fwd(M, d, n, _ptr(xq), _ptr(s_x), _ptr(x_rowsum), wfmt, _ptr(m), _ptr(s_bar),
-                                    _ptr(Y_bf16), _ptr(acc_dbg), _ptr(ws), wsb, _stream(stream)),
+    _check(lib().intlora_linear_fwd(M, d, n, _ptr(xq), _ptr(s_x), _ptr(x_rowsum), wfmt, _ptr(m), _ptr(m_split),
+                                    _ptr(s_bar), _ptr(Y_bf16), _ptr(acc_dbg), _ptr(ws), wsb, _stream(stream)),
            "intlora_linear_fwd")
 
 

@@ -164,7 +164,7 @@ const char* intlora_status_string(int status) {
 
 const char* intlora_last_error(void) { return g_err; }
 
-int intlora_version(void) { return 100; }
+int intlora_version(void) { return 101; }
 
 size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
   (void)M;
@@ -213,7 +213,8 @@ int intlora_stats(const intlora_desc* desc, int mode, const float* W, const intl
   if ((s = ensure_device())) return s;
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, nullptr, st))) return s;
-  return launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, out0, out1, st), "row range");
+  return launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, out0, out1, nullptr, st),
+                       "row range");
 }
 
 int intlora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_out, void* stream) {
@@ -242,26 +243,28 @@ int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vm
 }
 
 int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
-                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* u_round_dbg, unsigned long long* sat_count,
-                      void* ws, size_t ws_bytes, void* stream) {
+                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
+                      unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(desc, true);
   if (s) return s;
   if (u_bits < 2 || u_bits > 8) return fail(INTLORA_EINVAL, "u_bits must be in [2, 8] (got %d)", u_bits);
   if (desc->d == 0) return ok();
   if ((s = check_base_lora(base, lora))) return s;
   if ((s = check_ptrs({m, s_bar, z_bar}, "merge_mul"))) return s;
-  if ((s = check_opt(u_round_dbg, "u_round_dbg")) || (s = check_opt(sat_count, "sat_count"))) return s;
+  if ((s = check_opt(m_split, "m_split")) || (s = check_opt(u_round_dbg, "u_round_dbg")) ||
+      (s = check_opt(sat_count, "sat_count")))
+    return s;
   if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
   if ((s = ensure_device())) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
-  if ((s = launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, st),
-                         "row range")))
+  if ((s = launch_status(
+           intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, m_split, st), "row range")))
     return s;
   return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
                                                  static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
-                                                 w.umax, m, s_bar, z_bar, u_round_dbg, sat_count, st),
+                                                 w.umax, m, s_bar, z_bar, m_split, u_round_dbg, sat_count, st),
                        "quant_mul");
 }
 
@@ -280,8 +283,8 @@ int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
-  if ((s = launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, st),
-                         "row range")))
+  if ((s = launch_status(
+           intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, nullptr, st), "row range")))
     return s;
   return launch_status(intlora::launch_quant_shift(desc->d, desc->n, desc->w_bits, v_bits,
                                                    static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
@@ -303,8 +306,8 @@ int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s
 }
 
 int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x, const int32_t* x_rowsum,
-                       int wfmt, const void* m, const float* s_bar, uint16_t* Y_bf16, int32_t* acc_dbg, void* ws,
-                       size_t ws_bytes, void* stream) {
+                       int wfmt, const void* m, const uint8_t* m_split, const float* s_bar, uint16_t* Y_bf16,
+                       int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
   if (wfmt != INTLORA_W_INT4 && wfmt != INTLORA_W_INT8 && wfmt != INTLORA_W_INT16)
@@ -318,9 +321,10 @@ int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const 
   int s = check_ptrs({xq, s_x, m, s_bar, Y_bf16}, "linear_fwd");
   if (s) return s;
   if (wfmt == INTLORA_W_INT16 && (s = check_ptrs({x_rowsum}, "linear_fwd x_rowsum (INT16)"))) return s;
-  if ((s = check_opt(acc_dbg, "acc_dbg"))) return s;
+  if ((s = check_opt(acc_dbg, "acc_dbg")) || (s = check_opt(m_split, "m_split"))) return s;
+  if (m_split && wfmt != INTLORA_W_INT16) return fail(INTLORA_EINVAL, "m_split applies to INTLORA_W_INT16 only");
   if ((s = ensure_device())) return s;
-  return launch_status(intlora::launch_linear(M, d, n, xq, s_x, x_rowsum, wfmt, m, s_bar, Y_bf16, acc_dbg,
+  return launch_status(intlora::launch_linear(M, d, n, xq, s_x, x_rowsum, wfmt, m, m_split, s_bar, Y_bf16, acc_dbg,
                                               static_cast<hipStream_t>(stream)),
                        "linear");
 }

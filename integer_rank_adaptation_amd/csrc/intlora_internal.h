@@ -39,14 +39,16 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
                             hipStream_t st);
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st);
 hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
-                            hipStream_t st);
+                            uint8_t* split, hipStream_t st);
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
                             const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
-                            int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st);
+                            int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
+                            hipStream_t st);
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
                               const float* U, const float* umin, const float* umax, uint8_t* m, float* sbar,
                               uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st);
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
-                         int wfmt, const void* m, const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st);
+                         int wfmt, const void* m, const uint8_t* split, const float* sbar, uint16_t* Y,
+                         int32_t* acc_dbg, hipStream_t st);
 
 }  // namespace intlora

@@ -11,10 +11,19 @@
 //   INT4  (SHIFT, b_W = 4)   packed nibbles, unpacked after the LDS read as 16*w
 //                            (nibble in the high half of each byte), so the
 //                            accumulator is 16 * exact and is shifted back exactly;
-//   INT16 (MUL)              bias byte split after the LDS read:
-//                            hi = m >> 8, lo = (m & 0xFF) - 128, two int8 planes,
-//                            exact = 256 acc_hi + acc_lo + 128 rowsum(X_q), formed
-//                            exactly in binary64 (|exact| < 2^53).
+//   INT16 (MUL)              byte split into two int8 planes after the LDS read, one
+//                            split per launch, chosen from the rows' split codes:
+//                            bias (some code 1, any int16): hi = m >> 8,
+//                              lo = (m & 0xFF) - 128, exact = 256 acc_hi + acc_lo +
+//                              128 rowsum(X_q);
+//                            balanced (all codes 0: every m <= 32639):
+//                              hi = (m + 128) >> 8, lo = m - 256 hi,
+//                              exact = 256 acc_hi + acc_lo;
+//                            formed exactly in binary64 (|exact| < 2^53).  For merged
+//                            integers of small magnitude the balanced high plane is all
+//                            zeros, which lowers the matrix cores' switching power (the
+//                            chip runs at a higher clock).  Each split has its own copy
+//                            of the K loop.
 //
 // Data path: every operand goes from HBM straight into LDS with buffer_load ... lds
 // (16 bytes per lane, no VGPR staging) through a 4-stage ring, so the loads of stages
@@ -37,6 +46,8 @@
 // Epilogue: per-token scales / row sums and per-output scales go to LDS once; the
 // accumulators pass through a padded LDS region per wave so that each lane writes four
 // consecutive bf16 outputs of one row (hardware round-to-nearest-even conversion).
+#include <type_traits>
+
 #include "device_common.h"
 #include "intlora_internal.h"
 
@@ -198,46 +209,84 @@ struct RawB {
   v4i v[4];
 };
 
+// Per-lane byte offsets of the fragment reads inside an LDS stage, for sub-steps ks = 0, 1
+// (second index: the two 16-byte chunks of an INT16 row).  The swizzles depend only on
+// row bits 0..4, i.e. on the lane's row within a 32-row tile, so the other fragments of
+// a sub-step lie at constant distances (2048 bytes per A tile and per INT8 B tile, 4096
+// per INT16 B tile, 1024 per INT4 B tile) and the reads fold them into their offsets.
+struct LdsLane {
+  uint32_t a[2];
+  uint32_t b[2][2];
+};
+
+template <int F>
+__device__ __forceinline__ LdsLane lds_lane(int wm, int wn, int fr, int h) {
+  using namespace lin;
+  LdsLane ll;
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    ll.a[ks] = (uint32_t)((wm * 128 + fr) * 64 + (((2 * h + ks) ^ swz64(fr)) << 4));
+    if (F == F_INT8) {
+      ll.b[ks][0] = (uint32_t)(A_BYTES + (wn * 128 + fr) * 64 + (((2 * h + ks) ^ swz64(fr)) << 4));
+      ll.b[ks][1] = 0;
+    } else if (F == F_INT16) {
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        ll.b[ks][jj] = (uint32_t)(A_BYTES + (wn * 64 + fr) * 128 + (((4 * h + 2 * ks + jj) ^ swz128(fr)) << 4));
+    } else {
+      ll.b[ks][0] = (uint32_t)(A_BYTES + (wn * 128 + fr) * 32 + ((h ^ swz32(fr)) << 4) + 8 * ks);
+      ll.b[ks][1] = 0;
+    }
+  }
+  return ll;
+}
+
 // A (tokens) fragments of one K sub-step: 4 tiles; sub-step ks of lane half h covers
 // K 32 h + 16 ks .. + 16 of the stage.
-__device__ __forceinline__ void read_a(const uint8_t* __restrict__ As, int wm, int ks, int fr, int h, v4i (&af)[4]) {
+__device__ __forceinline__ void read_a(const uint8_t* __restrict__ S, const LdsLane& ll, int ks, v4i (&af)[4]) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int row = wm * 128 + i * 32 + fr;
-    af[i] = *reinterpret_cast<const v4i*>(As + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
-  }
+  for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const v4i*>(S + ll.a[ks] + i * 2048);
+}
+
+// Raw B chunk j (0..3) of sub-step ks.  INT16: two output tiles of 32 rows, 32 int16
+// (two 16-byte chunks) per lane and sub-step; INT4: 8 packed bytes per lane and
+// sub-step (half of the lane's 16-byte chunk).
+template <int F>
+__device__ __forceinline__ v4i read_b_chunk(const uint8_t* __restrict__ S, const LdsLane& ll, int ks, int j) {
+  if (F == F_INT8) return *reinterpret_cast<const v4i*>(S + ll.b[ks][0] + j * 2048);
+  if (F == F_INT16) return *reinterpret_cast<const v4i*>(S + ll.b[ks][j & 1] + (j >> 1) * 4096);
+  const uint2 r = *reinterpret_cast<const uint2*>(S + ll.b[ks][0] + j * 1024);
+  return v4i{(int)r.x, (int)r.y, 0, 0};
 }
 
 template <int F>
-__device__ __forceinline__ void read_b(const uint8_t* __restrict__ Bs, int wn, int ks, int fr, int h, RawB<F>& rw) {
-  if (F == F_INT8) {
+__device__ __forceinline__ void read_b(const uint8_t* __restrict__ S, const LdsLane& ll, int ks, RawB<F>& rw) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wn * 128 + j * 32 + fr;
-      rw.v[j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
-    }
-  } else if (F == F_INT16) {
-    // two output tiles of 32 rows, 32 int16 (two 16-byte chunks) per lane and sub-step
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int row = wn * 64 + q * 32 + fr;
-      const int c0 = 4 * h + 2 * ks;
-      rw.v[2 * q] = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c0 ^ swz128(row)) << 4));
-      rw.v[2 * q + 1] = *reinterpret_cast<const v4i*>(Bs + row * 128 + (((c0 + 1) ^ swz128(row)) << 4));
-    }
-  } else {  // F_INT4: 8 packed bytes per lane and sub-step (half of the lane's 16-byte chunk)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = wn * 128 + j * 32 + fr;
-      const uint2 r = *reinterpret_cast<const uint2*>(Bs + row * 32 + ((h ^ swz32(row)) << 4) + 8 * ks);
-      rw.v[j] = v4i{(int)r.x, (int)r.y, 0, 0};
-    }
-  }
+  for (int j = 0; j < 4; ++j) rw.v[j] = read_b_chunk<F>(S, ll, ks, j);
+}
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+// two int16 + add (per 16-bit half, no carry between them)
+__device__ __forceinline__ uint32_t add16x2(uint32_t x, uint32_t a) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(us2, x) + __builtin_bit_cast(us2, a));
+}
+
+// The two int8 planes (x: high, y: low) of the four int16 in (x0, x1), little-endian:
+// the high byte of each value is byte 1 or 3 of its dword.  Bias split: the high bytes,
+// and the low bytes with bit 7 flipped; balanced split: the high bytes of m + 128 and
+// the low bytes as they are.
+template <bool BIAS>
+__device__ __forceinline__ uint2 split16(uint32_t x0, uint32_t x1) {
+  if (BIAS)
+    return make_uint2(__builtin_amdgcn_perm(x1, x0, 0x07050301u),
+                      __builtin_amdgcn_perm(x1, x0, 0x06040200u) ^ 0x80808080u);
+  return make_uint2(__builtin_amdgcn_perm(add16x2(x1, 0x00800080u), add16x2(x0, 0x00800080u), 0x07050301u),
+                    __builtin_amdgcn_perm(x1, x0, 0x06040200u));
 }
 
 // B (weight) MFMA operands for 4 column tiles from the raw bytes.  INT16: tile q of
 // outputs gives MFMA column tiles 2q (hi plane) and 2q+1 (lo plane).
-template <int F>
+template <int F, bool BIAS>
 __device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4]) {
   if (F == F_INT8) {
 #pragma unroll
@@ -248,11 +297,11 @@ __device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4]) {
       const v4i r0 = rw.v[2 * q], r1 = rw.v[2 * q + 1];
       const uint32_t x[8] = {(uint32_t)r0.x, (uint32_t)r0.y, (uint32_t)r0.z, (uint32_t)r0.w,
                              (uint32_t)r1.x, (uint32_t)r1.y, (uint32_t)r1.z, (uint32_t)r1.w};
-      // little-endian int16: the high byte of each value is byte 1 or 3 of its dword
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        bf[2 * q][e] = (int)__builtin_amdgcn_perm(x[2 * e + 1], x[2 * e], 0x07050301u);
-        bf[2 * q + 1][e] = (int)(__builtin_amdgcn_perm(x[2 * e + 1], x[2 * e], 0x06040200u) ^ 0x80808080u);
+        const uint2 hl = split16<BIAS>(x[2 * e], x[2 * e + 1]);
+        bf[2 * q][e] = (int)hl.x;
+        bf[2 * q + 1][e] = (int)hl.y;
       }
     }
   } else {
@@ -266,34 +315,18 @@ __device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4]) {
   }
 }
 
-// One LDS read of a sub-step: reads 0..3 are the A fragments, 4..7 the raw B chunks.
+// One LDS read of a sub-step: reads 0..3 are the raw B chunks, 4..7 the A fragments.
 template <int F>
-__device__ __forceinline__ void read_piece(int q, const uint8_t* __restrict__ S, int wm, int wn, int ks, int fr,
-                                           int h, v4i (&af)[4], RawB<F>& rw) {
-  using namespace lin;
-  if (q >= 4) {
-    const int row = wm * 128 + (q - 4) * 32 + fr;
-    af[q - 4] = *reinterpret_cast<const v4i*>(S + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
-    return;
-  }
-  const uint8_t* Bs = S + A_BYTES;
-  const int j = q;
-  if (F == F_INT8) {
-    const int row = wn * 128 + j * 32 + fr;
-    rw.v[j] = *reinterpret_cast<const v4i*>(Bs + row * 64 + (((2 * h + ks) ^ swz64(row)) << 4));
-  } else if (F == F_INT16) {
-    const int qq = j >> 1, c = 4 * h + 2 * ks + (j & 1);
-    const int row = wn * 64 + qq * 32 + fr;
-    rw.v[j] = *reinterpret_cast<const v4i*>(Bs + row * 128 + ((c ^ swz128(row)) << 4));
-  } else {
-    const int row = wn * 128 + j * 32 + fr;
-    const uint2 r = *reinterpret_cast<const uint2*>(Bs + row * 32 + ((h ^ swz32(row)) << 4) + 8 * ks);
-    rw.v[j] = v4i{(int)r.x, (int)r.y, 0, 0};
-  }
+__device__ __forceinline__ void read_piece(int q, const uint8_t* __restrict__ S, const LdsLane& ll, int ks,
+                                           v4i (&af)[4], RawB<F>& rw) {
+  if (q >= 4)
+    af[q - 4] = *reinterpret_cast<const v4i*>(S + ll.a[ks] + (q - 4) * 2048);
+  else
+    rw.v[q] = read_b_chunk<F>(S, ll, ks, q);
 }
 
 // Conversion piece p (0..7) of the raw B bytes into MFMA operands.
-template <int F>
+template <int F, bool BIAS>
 __device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf)[4]) {
   if (F == F_INT8) {
     if (p < 4) bf[p] = rw.v[p];
@@ -301,8 +334,9 @@ __device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf
     const int q = p >> 2, e = p & 3;  // output tile q, dword pair e
     const v4i& lo16 = rw.v[2 * q + (e >> 1)];
     const uint32_t x0 = (uint32_t)lo16[2 * (e & 1)], x1 = (uint32_t)lo16[2 * (e & 1) + 1];
-    bf[2 * q][e] = (int)__builtin_amdgcn_perm(x1, x0, 0x07050301u);
-    bf[2 * q + 1][e] = (int)(__builtin_amdgcn_perm(x1, x0, 0x06040200u) ^ 0x80808080u);
+    const uint2 hl = split16<BIAS>(x0, x1);
+    bf[2 * q][e] = (int)hl.x;
+    bf[2 * q + 1][e] = (int)hl.y;
   } else {
     const int j = p >> 1, w = p & 1;
     uint32_t o0_, o1_;
@@ -353,6 +387,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
                                                             const float* __restrict__ sx,
                                                             const int32_t* __restrict__ rowsum,
                                                             const uint8_t* __restrict__ m,
+                                                            const uint8_t* __restrict__ split,
                                                             const float* __restrict__ sbar, uint16_t* __restrict__ Y,
                                                             int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
   using namespace lin;
@@ -402,6 +437,25 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   tile_ptrs(0, a_cur, ab_cur, b_cur, bb_cur);
   tile_ptrs(1, a_nxt, ab_nxt, b_nxt, bb_nxt);
 
+  // INT16 split of the launch: bias when some row's code is 1 (or there are no codes),
+  // else balanced.  The codes are read before the first stages are issued and voted
+  // on at the prologue's barrier.
+  int fl = 0;
+  if (F == F_INT16) {
+    if (split == nullptr) {
+      fl = 1;
+    } else {
+      for (int64_t i = 16 * (int64_t)tid; i < d; i += 16 * kThreads) {
+        if (i + 16 <= d) {
+          const uint4 v = *reinterpret_cast<const uint4*>(split + i);
+          fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
+        } else {
+          for (int64_t k = i; k < d; ++k) fl |= (int)(split[k] != 0);
+        }
+      }
+    }
+  }
+
   // stages 0..2 of the stream (KT >= 3 whenever a block owns more than one tile)
 #pragma unroll
   for (int g = 0; g < 3; ++g) {
@@ -410,15 +464,24 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     else
       issue_stage<F, KTAIL>(g - KT, (int)n, a_nxt, ab_nxt, b_nxt, bb_nxt, plan, lds + g * STAGE);
   }
+  uint8_t* epi = lds + Cfg<F>::RING;
+  int* vote = reinterpret_cast<int*>(epi + EPI_VEC);  // free until the first epilogue
+  if (F == F_INT16 && lane == 0) vote[wid] = __builtin_amdgcn_ballot_w64(fl != 0) != 0 ? 1 : 0;
   wait_vmcnt<2 * Cfg<F>::LOADS>();
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the vote is in LDS before the barrier
   __builtin_amdgcn_s_barrier();
+  const bool bias = F == F_INT16 && (vote[0] | vote[1] | vote[2] | vote[3]) != 0;
+
   v4i a0[4], b0[4], a1[4], b1[4];
   RawB<F> rw;
-  read_a(lds, wm, 0, fr, h, a0);
-  read_b<F>(lds + A_BYTES, wn, 0, fr, h, rw);
-  convert_b<F>(rw, b0);
+  const LdsLane ll = lds_lane<F>(wm, wn, fr, h);
+  read_a(lds, ll, 0, a0);
+  read_b<F>(lds, ll, 0, rw);
+  if (F == F_INT16 && bias)
+    convert_b<F, true>(rw, b0);
+  else
+    convert_b<F, false>(rw, b0);
 
-  uint8_t* epi = lds + Cfg<F>::RING;
   int g = 0;  // global stage index of the stream
   for (int lt = 0; lt < my_tiles; ++lt) {
     v16i acc[4][4];
@@ -428,46 +491,55 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
-    for (int kt = 0; kt < KT; ++kt, ++g) {
-      // stage g+1 has landed (loads of g+2 may still be in flight); after the barrier it
-      // is visible to all waves and nobody reads stage g-1, whose buffer g+3 reuses
-      wait_vmcnt<Cfg<F>::LOADS>();
-      __builtin_amdgcn_s_barrier();
-      // stage g+3 is stage kt+3 of this tile or stage kt+3-KT of the next one
-      const bool same = kt + 3 < KT;
-      const int kl = same ? kt + 3 : kt + 3 - KT;
-      const int8_t* al = same ? a_cur : a_nxt;
-      const uint8_t* bl = same ? b_cur : b_nxt;
-      const int64_t abl = same ? ab_cur : ab_nxt;
-      const int64_t bbl = same ? bb_cur : bb_nxt;
-      uint8_t* ldst = lds + ((g + 3) % kStages) * STAGE;
-      const uint8_t* S0 = lds + (g % kStages) * STAGE;
-      const uint8_t* S1 = lds + ((g + 1) % kStages) * STAGE;
-      // Each half (one 32-deep K sub-step): 16 MFMAs on the current operand set,
-      // interleaved one by one with the LDS reads of the next set (first eight MFMAs),
-      // the stage's direct loads (spread over both halves) and the conversion of the
-      // next set (last eight MFMAs).  sched_barrier fixes the order.
-      // sub-step 0 of stage g on set 0; set 1 <- sub-step 1 of stage g
+    // the K loop, one copy per split (uniform over the launch)
+    auto k_loop = [&](auto bias_tag) {
+      constexpr bool BIAS = decltype(bias_tag)::value;
+      for (int kt = 0; kt < KT; ++kt, ++g) {
+        // stage g+1 has landed (loads of g+2 may still be in flight); after the barrier it
+        // is visible to all waves and nobody reads stage g-1, whose buffer g+3 reuses
+        wait_vmcnt<Cfg<F>::LOADS>();
+        __builtin_amdgcn_s_barrier();
+        // stage g+3 is stage kt+3 of this tile or stage kt+3-KT of the next one
+        const bool same = kt + 3 < KT;
+        const int kl = same ? kt + 3 : kt + 3 - KT;
+        const int8_t* al = same ? a_cur : a_nxt;
+        const uint8_t* bl = same ? b_cur : b_nxt;
+        const int64_t abl = same ? ab_cur : ab_nxt;
+        const int64_t bbl = same ? bb_cur : bb_nxt;
+        uint8_t* ldst = lds + ((g + 3) % kStages) * STAGE;
+        const uint8_t* S0 = lds + (g % kStages) * STAGE;
+        const uint8_t* S1 = lds + ((g + 1) % kStages) * STAGE;
+        // Each half (one 32-deep K sub-step): 16 MFMAs on the current operand set,
+        // interleaved one by one with the LDS reads of the next set (first eight MFMAs),
+        // the stage's direct loads (spread over both halves) and the conversion of the
+        // next set (last eight MFMAs).  sched_barrier fixes the order.
+        // sub-step 0 of stage g on set 0; set 1 <- sub-step 1 of stage g
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[q & 3], a0[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
-        if (q < 8) read_piece<F>(q, S0, wm, wn, 1, fr, h, a1, rw);
-        if (q >= 8 && q - 8 < (Cfg<F>::LOADS + 1) / 2)
-          issue_load<F, KTAIL>(q - 8, (int)n, kl, al, abl, bl, bbl, plan, ldst);
-        if (q >= 8) convert_piece<F>(q - 8, rw, b1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // sub-step 1 of stage g on set 1; set 0 <- sub-step 0 of stage g+1
+        for (int q = 0; q < 16; ++q) {
+          acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[q & 3], a0[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
+          if (q < 8) read_piece<F>(q, S0, ll, 1, a1, rw);
+          if (q >= 8 && q - 8 < (Cfg<F>::LOADS + 1) / 2)
+            issue_load<F, KTAIL>(q - 8, (int)n, kl, al, abl, bl, bbl, plan, ldst);
+          if (q >= 8) convert_piece<F, BIAS>(q - 8, rw, b1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // sub-step 1 of stage g on set 1; set 0 <- sub-step 0 of stage g+1 (the next
+        // tile's first stage after the last stage of this one)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[q & 3], a1[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
-        if (q < 8) read_piece<F>(q, S1, wm, wn, 0, fr, h, a0, rw);
-        if (q >= 8 && q - 8 + (Cfg<F>::LOADS + 1) / 2 < Cfg<F>::LOADS)
-          issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kl, al, abl, bl, bbl, plan, ldst);
-        if (q >= 8) convert_piece<F>(q - 8, rw, b0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 16; ++q) {
+          acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[q & 3], a1[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
+          if (q < 8) read_piece<F>(q, S1, ll, 0, a0, rw);
+          if (q >= 8 && q - 8 + (Cfg<F>::LOADS + 1) / 2 < Cfg<F>::LOADS)
+            issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kl, al, abl, bl, bbl, plan, ldst);
+          if (q >= 8) convert_piece<F, BIAS>(q - 8, rw, b0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-    }
+    };
+    if (F == F_INT16 && bias)
+      k_loop(std::true_type{});
+    else
+      k_loop(std::false_type{});
 
     // ------------------------------------------------------------ epilogue of tile lt
     int tm, tn;
@@ -492,7 +564,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
       __builtin_amdgcn_sched_barrier(0);  // read one slab's accumulators at a time
       const int tl = wm * 128 + i * 32 + fr;  // this lane's token inside the block
       const float sxt = tok_sx[tl];
-      const double rs128 = F == F_INT16 ? 128.0 * (double)tok_rs[tl] : 0.0;
+      const double rs128 = F == F_INT16 && bias ? 128.0 * (double)tok_rs[tl] : 0.0;  // bias split
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         __builtin_amdgcn_sched_barrier(0);
@@ -512,7 +584,8 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
             for (int e = 0; e < 4; ++e) {
               if (F == F_INT16) {
                 const int hi = acc_read(acc[i][2 * jj][4 * a + e]), lo = acc_read(acc[i][2 * jj + 1][4 * a + e]);
-                // exact = 256 acc_hi + acc_lo + 128 rowsum, exact in binary64 (|exact| < 2^53)
+                // exact = 256 acc_hi + acc_lo (+ 128 rowsum for the bias split), exact in
+                // binary64 (|exact| < 2^53)
                 const double ex = fma(256.0, (double)hi, (double)lo) + rs128;
                 y[e] = ((float)ex * sxt) * sbv[e];
               } else {
@@ -587,7 +660,8 @@ static int device_cus() {
 }
 
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
-                         int wfmt, const void* m, const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st) {
+                         int wfmt, const void* m, const uint8_t* split, const float* sbar, uint16_t* Y,
+                         int32_t* acc_dbg, hipStream_t st) {
   using namespace lin;
   const int out_per_block = (wfmt == F_INT16) ? Cfg<F_INT16>::OUT : Cfg<F_INT8>::OUT;
   const int tiles_m = (int)((M + BM - 1) / BM);
@@ -620,10 +694,10 @@ hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, cons
   do {                                                                                                        \
     if (tail)                                                                                                 \
       hipLaunchKernelGGL((k_linear<FMT, true>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx,      \
-                         rowsum, mb, sbar, Y, acc_dbg, tiles_m, tiles_n);                                     \
+                         rowsum, mb, split, sbar, Y, acc_dbg, tiles_m, tiles_n);                              \
     else                                                                                                      \
       hipLaunchKernelGGL((k_linear<FMT, false>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx,     \
-                         rowsum, mb, sbar, Y, acc_dbg, tiles_m, tiles_n);                                     \
+                         rowsum, mb, split, sbar, Y, acc_dbg, tiles_m, tiles_n);                              \
   } while (0)
   switch (wfmt) {
     case F_INT8: INTLORA_LAUNCH_LINEAR(F_INT8); break;

@@ -442,16 +442,19 @@ __device__ __forceinline__ void row_range(const int* __restrict__ pmin, const in
   umax = key_f32(kmax);
 }
 
-// Exposes U_min / U_max (the statistics entry point).
+// Exposes U_min / U_max (the statistics entry point).  `split` (nullable) is the
+// per-row plane-split code of the MUL merge, cleared here and raised by the quantize
+// kernel for rows holding some m >= 32640.
 __global__ __launch_bounds__(256) void k_row_range(int64_t d, int ntiles, const int* __restrict__ pmin,
                                                   const int* __restrict__ pmax, float* __restrict__ umin,
-                                                  float* __restrict__ umax) {
+                                                  float* __restrict__ umax, uint8_t* __restrict__ split) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < d) {
     float a, b;
     row_range(pmin, pmax, d, i, ntiles, a, b);
     umin[i] = a;
     umax[i] = b;
+    if (split) split[i] = 0;
   }
 }
 
@@ -477,6 +480,10 @@ constexpr int kQThreads = 128;
 constexpr int kQElems = 8;
 constexpr int kQCols = kQThreads * kQElems;
 constexpr int kQRows = 2;
+
+// Smallest int16 whose row needs the bias byte split in the GEMM: the balanced split
+// hi = (m + 128) >> 8 leaves the int8 range above 32639.
+constexpr int kSplitBiasMin = 32640;
 
 struct MulParams {
   float sbar;
@@ -560,7 +567,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
                                                         const float* __restrict__ umin_r,
                                                         const float* __restrict__ umax_r, int16_t* __restrict__ m,
                                                         float* __restrict__ sbar_out, int32_t* __restrict__ zbar_out,
-                                                        uint8_t* __restrict__ uround_dbg,
+                                                        uint8_t* __restrict__ split, uint8_t* __restrict__ uround_dbg,
                                                         unsigned long long* __restrict__ sat) {
   const int qmax = (1 << u_bits) - 1;
   const int64_t j0 = (int64_t)blockIdx.x * kQCols + (int64_t)threadIdx.x * kQElems;
@@ -623,6 +630,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         pk.z = (mm[4] & 0xFFFF) | (mm[5] << 16);
         pk.w = (mm[6] & 0xFFFF) | (mm[7] << 16);
         *reinterpret_cast<int4*>(m + i * n + j0) = pk;
+        if (split) {  // the balanced byte split of the int16 GEMM needs m <= 32639
+          int mx = mm[0];
+#pragma unroll
+          for (int e = 1; e < 8; ++e) mx = max(mx, mm[e]);
+          if (mx >= kSplitBiasMin) split[i] = 1;
+        }
         if (uround_dbg) {
           uint2 pu;
           pu.x = (uint32_t)ur[0] | ((uint32_t)ur[1] << 8) | ((uint32_t)ur[2] << 16) | ((uint32_t)ur[3] << 24);
@@ -647,6 +660,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           int uv;
           const int mv = mul_merge(code_at<W4>(wround, i, n, j) - zi, U[i * n + j], P, qmax, uv, nsat);
           m[i * n + j] = (int16_t)mv;
+          if (split && mv >= kSplitBiasMin) split[i] = 1;
           if (uround_dbg) uround_dbg[i * n + j] = (uint8_t)uv;
         }
       }
@@ -911,8 +925,9 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
 }
 
 hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
-                            hipStream_t st) {
-  hipLaunchKernelGGL(k_row_range, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin, umax);
+                            uint8_t* split, hipStream_t st) {
+  hipLaunchKernelGGL(k_row_range, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin, umax,
+                     split);
   return hipGetLastError();
 }
 
@@ -923,14 +938,15 @@ static dim3 quant_grid(int64_t d, int64_t n) {
 
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
                             const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
-                            int32_t* zbar, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st) {
+                            int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
+                            hipStream_t st) {
   const dim3 grid = quant_grid(d, n);
   if (w_bits == 4)
     hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
-                       sbar, zbar, uround_dbg, sat);
+                       sbar, zbar, split, uround_dbg, sat);
   else
     hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
-                       sbar, zbar, uround_dbg, sat);
+                       sbar, zbar, split, uround_dbg, sat);
   return hipGetLastError();
 }
 

@@ -78,11 +78,13 @@ def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out
     o = out or dict(m=torch.empty((d, n), dtype=torch.int16, device=dev),
                     sbar=torch.empty(d, dtype=torch.float32, device=dev),
                     zbar=torch.empty(d, dtype=torch.int32, device=dev),
+                    split=torch.empty(d, dtype=torch.uint8, device=dev),
                     sat=torch.zeros(2, dtype=torch.int64, device=dev))
     if dbg and "uround" not in o:
         o["uround"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
     B.intlora_merge_mul(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), u_bits, o["m"],
-                        o["sbar"], o["zbar"], o.get("uround") if dbg else None, o["sat"], ws)
+                        o["sbar"], o["zbar"], m_split=o.get("split"), u_round_dbg=o.get("uround") if dbg else None,
+                        sat_count=o["sat"], ws=ws)
     return o
 
 
@@ -111,10 +113,12 @@ def quant_act(X):
     return xq, sx, rs
 
 
-def linear(xq, sx, rowsum, wfmt, m, sbar, d, acc_dbg=False, out=None):
+def linear(xq, sx, rowsum, wfmt, m, sbar, d, acc_dbg=False, out=None, split=None):
+    """split: the MUL merge's per-row split codes (INT16 only); None = bias split for
+    every row."""
     M, n = xq.shape
     Y = torch.empty((M, d), dtype=torch.int16, device=xq.device) if out is None else out
     planes = 2 if wfmt == B.INTLORA_W_INT16 else 1
     acc = torch.empty((planes, M, d), dtype=torch.int32, device=xq.device) if acc_dbg else None
-    B.intlora_linear_fwd(M, d, n, xq, sx, rowsum, wfmt, m, sbar, Y, acc)
+    B.intlora_linear_fwd(M, d, n, xq, sx, rowsum, wfmt, m, split, sbar, Y, acc)
     return Y, acc

@@ -300,10 +300,32 @@ def linear_sampled(ts, is_, xq, sx, m, sbar):
     return exact, y
 
 
-def byte_planes(m):
-    """Bias byte split of int16 merged integers: hi = m >> 8, lo = (m & 0xFF) - 128,
-    so that m = 256*hi + lo + 128 for every int16 (the two int8 GEMM planes)."""
+def byte_planes(m, split=None):
+    """Byte split of int16 merged integers into the two int8 GEMM planes, per row.
+
+    Bias split (split 1, and every row when `split` is None): hi = m >> 8,
+    lo = (m & 0xFF) - 128, so m = 256*hi + lo + 128 for every int16.
+    Balanced split (split 0): hi = (m + 128) >> 8, lo = m - 256*hi, so m = 256*hi + lo;
+    both fit int8 only when m <= 32639, which is what a row's split code 0 asserts.
+    """
     m = np.asarray(m).astype(np.int32)
     hi = m >> 8
     lo = (m & 0xFF) - 128
+    if split is not None:
+        bal = np.asarray(split).reshape(-1) == 0
+        if m.ndim == 1:
+            bal = bal[0] if bal.size == 1 else bal
+        else:
+            bal = bal[:, None]
+        hb = (m + 128) >> 8
+        hi = np.where(bal, hb, hi)
+        lo = np.where(bal, m - 256 * hb, lo)
+    assert hi.min(initial=0) >= -128 and hi.max(initial=0) <= 127, "a balanced row holds m > 32639"
     return hi.astype(np.int8), lo.astype(np.int8)
+
+
+def plane_split(m):
+    """Per-row split code for the int16 GEMM: 0 (balanced) when every m of the row is at
+    most 32639, else 1 (bias)."""
+    m = np.asarray(m).astype(np.int32)
+    return (m >= 32640).any(axis=1).astype(np.uint8)

@@ -74,7 +74,7 @@ def _merge_mul(lib, dsc, u_bits=8, m=FAKE, ws=FAKE, ws_bytes=1 << 40, base=None,
     base = base or _base()
     lora = lora or _lora()
     return lib.intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), u_bits, m, FAKE, FAKE,
-                                 None, None, ws, ws_bytes, None)
+                                 None, None, None, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -119,15 +119,15 @@ def test_other_entry_points_validation(lib):
     big = B.desc(8, 40000, 4, 8)
     assert lib.intlora_base_quant(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, None) == B.INTLORA_ESHAPE
     assert lib.intlora_quant_act(-1, 8, FAKE, FAKE, FAKE, None, None) == B.INTLORA_ESHAPE
-    # linear: bad format, K not a multiple of 32, INT16 without the row sums
-    assert lib.intlora_linear_fwd(4, 4, 64, FAKE, FAKE, FAKE, 7, FAKE, FAKE, FAKE, None, None, 0, None) == \
-        B.INTLORA_EINVAL
-    assert lib.intlora_linear_fwd(4, 4, 48, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None, None, 0, None) == \
-        B.INTLORA_ESHAPE
-    assert lib.intlora_linear_fwd(4, 4, 64, FAKE, FAKE, None, 16, FAKE, FAKE, FAKE, None, None, 0, None) == \
-        B.INTLORA_EINVAL
-    assert lib.intlora_linear_fwd(4, 4, 131072, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, None, None, 0, None) == \
-        B.INTLORA_ESHAPE
+    # linear: bad format, K not a multiple of 32, INT16 without the row sums, split codes
+    # with a one-plane format, misaligned split codes
+    lf = lib.intlora_linear_fwd
+    assert lf(4, 4, 64, FAKE, FAKE, FAKE, 7, FAKE, None, FAKE, FAKE, None, None, 0, None) == B.INTLORA_EINVAL
+    assert lf(4, 4, 48, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE, FAKE, None, None, 0, None) == B.INTLORA_ESHAPE
+    assert lf(4, 4, 64, FAKE, FAKE, None, 16, FAKE, None, FAKE, FAKE, None, None, 0, None) == B.INTLORA_EINVAL
+    assert lf(4, 4, 131072, FAKE, FAKE, FAKE, 8, FAKE, None, FAKE, FAKE, None, None, 0, None) == B.INTLORA_ESHAPE
+    assert lf(4, 4, 64, FAKE, FAKE, FAKE, 8, FAKE, FAKE, FAKE, FAKE, None, None, 0, None) == B.INTLORA_EINVAL
+    assert lf(4, 4, 64, FAKE, FAKE, FAKE, 16, FAKE, FAKE + 1, FAKE, FAKE, None, None, 0, None) == B.INTLORA_EALIGN
     assert lib.intlora_debug_ln(-1, FAKE, FAKE, None) == B.INTLORA_ESHAPE
 
 

@@ -61,6 +61,7 @@ def check_layer(ops, wl, li, L, Ms, mode, mbits, block=0, n_rows=6, n_tok=6):
         m_all = host(g["m"])
         assert np.array_equal(host(g["uround"])[rows], ref["uround"])
         assert np.array_equal(host(g["zbar"])[rows], ref["zbar"])
+        assert np.array_equal(host(g["split"])[rows], oracle.plane_split(ref["m"]))
         m_rows = m_all[rows]
         wfmt = 16
     else:
@@ -76,7 +77,10 @@ def check_layer(ops, wl, li, L, Ms, mode, mbits, block=0, n_rows=6, n_tok=6):
     for M in Ms:
         X = synth.activations(wl, L.n, M, li)
         xq, sx, rs = ops.quant_act(cuda(X))
-        Y, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], L.d)
+        Y, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], L.d, split=g.get("split"))
+        if mode == "mul":  # the bias split on every row gives the same outputs
+            Yb, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], L.d)
+            assert torch.equal(Y, Yb), (wl.name, L.name, M)
         toks = sample_rows(M, n_tok, 11 * li + M)
         oxq, osx, _ = oracle.quant_act(X[toks])
         assert np.array_equal(host(xq)[toks], oxq)

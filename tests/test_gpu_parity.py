@@ -152,6 +152,7 @@ def test_merge_mul_bitexact(ops, d, n, r, w_bits):
         assert np.array_equal(host(g["uround"]), ref["uround"])
         assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
         assert np.array_equal(host(g["zbar"]), ref["zbar"])
+        assert np.array_equal(host(g["split"]), oracle.plane_split(ref["m"]))
         assert np.array_equal(bits(host(umin)), bits(ref["umin"]))
         assert np.array_equal(bits(host(umax)), bits(ref["umax"]))
         assert int(host(g["sat"])[0]) == ref["sat"]
@@ -191,6 +192,7 @@ def test_merge_degenerate_rows(ops):
     ref = oracle.merge_mul(wr, z, s, R, A, Bm, 8)
     for k in ("m", "uround", "zbar"):
         assert np.array_equal(host(g[k]), ref[k]), k
+    assert np.array_equal(host(g["split"]), oracle.plane_split(ref["m"]))
     assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
     umin, umax = ops.u_minmax(st, cuda(A), cuda(Bm), 8, 0, 0)
     assert np.all(np.isposinf(host(umin)[:2])) and np.all(np.isneginf(host(umax)[:2]))
@@ -218,6 +220,7 @@ def test_merge_tall_matrices(ops, d, n, w_bits):
     R = np.concatenate([oracle.gen_r_rows(int(i), 1, n, 5, 2, c[i:i + 1]) for i in rows])
     ref = oracle.merge_mul(wr[rows], z[rows], s[rows], R, A[rows], Bm, w_bits)
     assert np.array_equal(host(g["m"])[rows], ref["m"])
+    assert np.array_equal(host(g["split"])[rows], oracle.plane_split(ref["m"]))
     assert np.array_equal(host(g["uround"])[rows], ref["uround"])
     assert np.array_equal(bits(host(g["sbar"])[rows]), bits(ref["sbar"]))
     ref2 = oracle.merge_shift(wr[rows], z[rows], s[rows], R, A[rows], Bm, w_bits, 4)
@@ -247,6 +250,7 @@ def test_merge_extreme_magnitudes(ops, scale_a, scale_b, scale_c):
     assert np.array_equal(bits(host(umax)), bits(ref["umax"]))
     assert np.array_equal(host(g["uround"]), ref["uround"])
     assert np.array_equal(host(g["m"]), ref["m"])
+    assert np.array_equal(host(g["split"]), oracle.plane_split(ref["m"]))
     assert int(host(g["sat"])[0]) == ref["sat"]
 
 
@@ -271,6 +275,26 @@ def test_quant_act(ops, M, n):
     assert np.array_equal(host(rs), rrs)
 
 
+def _int16_weights(rng, d, n, capped):
+    """int16 merged integers: over the whole int16 range (some m >= 32640, so the MUL
+    merge's split codes are 1 for those rows), or capped at 32639 (every code 0, so the
+    GEMM takes the balanced split), with every fourth row of small magnitude (the
+    balanced high plane is then zero) and one row at the cap."""
+    m = rng.integers(-32768, 32768, size=(d, n))
+    if capped:
+        m = np.minimum(m, 32639)
+        m[0::4] = rng.integers(-20, 21, size=m[0::4].shape)
+        m[d // 2, n // 2] = 32639
+    elif d > 1 and n > 1:
+        m[d - 1, 1] = 32767
+    return m.astype(np.int16)
+
+
+def launch_split(sp):
+    """The split the GEMM applies to every row: bias (1) when some row's code is 1."""
+    return np.full(np.asarray(sp).size, int(np.asarray(sp).any()), np.uint8)
+
+
 def _linear_case(ops, M, d, n, wfmt, seed):
     rng = np.random.Generator(np.random.PCG64(seed))
     xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
@@ -278,29 +302,33 @@ def _linear_case(ops, M, d, n, wfmt, seed):
     sbar = synth.random_positive(seed + 2, d, 1e-5, 1e-2)
     rs = xq.astype(np.int32).sum(axis=1).astype(np.int32)
     if wfmt == 16:
-        m = rng.integers(-32768, 32768, size=(d, n)).astype(np.int16)
-        mg = cuda(m)
+        # (weights, split codes): no codes (bias), codes with some 1 (bias), all 0 (balanced)
+        mf = _int16_weights(rng, d, n, capped=False)
+        mc = _int16_weights(rng, d, n, capped=True)
+        cases = [(mf, None), (mf, oracle.plane_split(mf)), (mc, oracle.plane_split(mc))]
+        assert not cases[2][1].any()
     elif wfmt == 8:
-        m = rng.integers(-128, 128, size=(d, n)).astype(np.int8)
-        mg = cuda(m)
+        cases = [(rng.integers(-128, 128, size=(d, n)).astype(np.int8), None)]
     else:
-        m = rng.integers(-8, 8, size=(d, n)).astype(np.int8)
-        mg = cuda(pack4(m.astype(np.uint8) & 15))
-    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, acc_dbg=True)
-    exact, y32, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
-    Yh = host(Y).view(np.uint16)
-    acc = host(acc)
-    if wfmt == 16:
-        hi, lo = oracle.byte_planes(m)
-        assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
-        assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
-    else:
-        assert np.array_equal(acc[0].astype(np.int64), exact)
-    # bf16: bit-identical expected; the 1e-3 relative rule as a backstop
-    ybf = torch.from_numpy(Yh.view(np.int16)).view(torch.bfloat16).float().numpy()
-    rbf = torch.from_numpy(yref.view(np.int16)).view(torch.bfloat16).float().numpy()
-    assert np.all(np.abs(ybf - rbf) <= 1e-3 * np.abs(rbf) + 1e-30)
-    assert np.array_equal(Yh, yref)
+        cases = [(rng.integers(-8, 8, size=(d, n)).astype(np.int8), None)]
+    for m, sp in cases:
+        mg = cuda(pack4(m.astype(np.uint8) & 15)) if wfmt == 4 else cuda(m)
+        exact, y32, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
+        Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, acc_dbg=True,
+                            split=None if sp is None else cuda(sp))
+        Yh = host(Y).view(np.uint16)
+        acc = host(acc)
+        if wfmt == 16:
+            hi, lo = oracle.byte_planes(m, split=None if sp is None else launch_split(sp))
+            assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
+            assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
+        else:
+            assert np.array_equal(acc[0].astype(np.int64), exact)
+        # bf16: bit-identical expected; the 1e-3 relative rule as a backstop
+        ybf = torch.from_numpy(Yh.view(np.int16)).view(torch.bfloat16).float().numpy()
+        rbf = torch.from_numpy(yref.view(np.int16)).view(torch.bfloat16).float().numpy()
+        assert np.all(np.abs(ybf - rbf) <= 1e-3 * np.abs(rbf) + 1e-30)
+        assert np.array_equal(Yh, yref)
 
 
 @pytest.mark.parametrize("wfmt", [8, 4, 16])
@@ -309,23 +337,30 @@ def test_linear_bitexact(ops, wfmt, M, d, n):
     _linear_case(ops, M, d, n, wfmt, seed=M * 7 + d * 3 + n + wfmt)
 
 
-@pytest.mark.parametrize("M,d,n,wfmt", [
-    (2600, 4000, 224, 16),  # 352 tiles: blocks own 1 or 2 tiles; partial last K stage; ragged M and d
-    (5000, 4000, 224, 8),   # 320 tiles, partial last K stage
-    (5000, 4000, 192, 4),   # 320 tiles, K an exact multiple of the stage depth
-    (4100, 9000, 96, 16),   # 1207 tiles with only two K stages each: one tile per block
+@pytest.mark.parametrize("M,d,n,wfmt,capped", [
+    (2600, 4000, 224, 16, True),    # 352 tiles: blocks own 1 or 2 tiles; partial last K stage; ragged M and d
+    (2600, 4000, 224, 16, False),   # the same with the bias split
+    (5000, 4000, 224, 8, False),    # 320 tiles, partial last K stage
+    (5000, 4000, 192, 4, False),    # 320 tiles, K an exact multiple of the stage depth
+    (4100, 9000, 96, 16, True),     # 1207 tiles with only two K stages each: one tile per block
+    (4100, 9000, 96, 16, False),
 ])
-def test_linear_many_tiles(ops, M, d, n, wfmt):
+def test_linear_many_tiles(ops, M, d, n, wfmt, capped):
     """More tiles than compute units (each block streams several tiles' K stages through
     one LDS ring), K tails and ragged edges; every output is compared with the oracle, and
-    the run without the accumulator dump gives the same outputs."""
+    the run without the accumulator dump gives the same outputs.  INT16 runs with the
+    merge's split codes (balanced split for capped weights, bias split otherwise) and
+    without them (bias split)."""
     rng = np.random.Generator(np.random.PCG64(M + d + n + wfmt))
     xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
     sx = synth.random_positive(M + 1, M, 1e-3, 0.1)
     sbar = synth.random_positive(d + 2, d, 1e-5, 1e-2)
     rs = xq.astype(np.int32).sum(axis=1).astype(np.int32)
+    sp = None
     if wfmt == 16:
-        m = rng.integers(-32768, 32768, size=(d, n)).astype(np.int16)
+        m = _int16_weights(rng, d, n, capped)
+        sp = oracle.plane_split(m)
+        assert sp.any() != capped
         mg = cuda(m)
     elif wfmt == 8:
         m = rng.integers(-128, 128, size=(d, n)).astype(np.int8)
@@ -333,12 +368,15 @@ def test_linear_many_tiles(ops, M, d, n, wfmt):
     else:
         m = rng.integers(-8, 8, size=(d, n)).astype(np.int8)
         mg = cuda(pack4(m.astype(np.uint8) & 15))
-    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, acc_dbg=True)
+    spg = None if sp is None else cuda(sp)
+    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, acc_dbg=True, split=spg)
     Y2, _ = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d)
     exact, _, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
     acc = host(acc).astype(np.int64)
     if wfmt == 16:
-        got = 256 * acc[0] + acc[1] + 128 * rs.astype(np.int64)[:, None]
+        got = 256 * acc[0] + acc[1] + 128 * rs.astype(np.int64)[:, None] * int(not capped)
+        Y3, _ = ops.linear(cuda(xq), cuda(sx), cuda(rs), wfmt, mg, cuda(sbar), d, split=spg)
+        assert np.array_equal(host(Y3).view(np.uint16), yref)
     else:
         got = acc[0]
     assert np.array_equal(got, exact)
@@ -360,7 +398,7 @@ def _gpu_pipeline(ops, wl, li, d, n, M, mode, bits_):
         g = ops.merge_shift(st, cuda(A), cuda(Bm), wl.w_bits, bits_, seed, lid, dbg=True)
         wfmt = wl.w_bits
     xq, sx, rs = ops.quant_act(cuda(X))
-    Y, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], d)
+    Y, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], d, split=g.get("split"))
     return dict(W=W, A=A, B=Bm, X=X, st=st, g=g, Y=Y, xq=xq, sx=sx)
 
 

@@ -9,6 +9,7 @@ weight scales at 8 bits.
 from fractions import Fraction
 
 import numpy as np
+import pytest
 import torch
 
 from integer_rank_adaptation_amd import synth
@@ -60,6 +61,32 @@ def test_byte_planes_identity(ora):
     mm = rng.integers(-32768, 32768, size=(7, 64))
     h, l = ora.byte_planes(mm)
     comb = 256 * (xq @ h.T.astype(np.int64)) + xq @ l.T.astype(np.int64) + 128 * xq.sum(axis=1)[:, None]
+    assert np.array_equal(comb, xq @ mm.T)
+
+
+def test_balanced_planes_identity(ora):
+    """Split code 0: m = 256*hi + lo exactly, both planes int8, for every m <= 32639; the
+    last 128 int16 values need the bias split (code 1), which plane_split selects."""
+    m = np.arange(-32768, 32640, dtype=np.int32)
+    hi, lo = ora.byte_planes(m, split=np.zeros(1, np.uint8))
+    assert np.array_equal(256 * hi.astype(np.int64) + lo.astype(np.int64), m)
+    assert hi.min() == -128 and hi.max() == 127 and lo.min() == -128 and lo.max() == 127
+    # small magnitudes leave the high plane at zero
+    h0, l0 = ora.byte_planes(np.arange(-128, 128), split=np.zeros(1, np.uint8))
+    assert not h0.any() and np.array_equal(l0, np.arange(-128, 128))
+    with pytest.raises(AssertionError):
+        ora.byte_planes(np.array([[32640]]), split=np.zeros(1, np.uint8))
+    # mixed rows: each row reconstructs with its own correction term
+    rng = np.random.Generator(np.random.PCG64(6))
+    mm = rng.integers(-32768, 32640, size=(6, 64))
+    mm[1, 7] = 32767
+    mm[4, 0] = 32640
+    sp = ora.plane_split(mm)
+    assert sp.tolist() == [0, 1, 0, 0, 1, 0]
+    h, l = ora.byte_planes(mm, split=sp)
+    xq = rng.integers(-127, 128, size=(5, 64)).astype(np.int64)
+    comb = (256 * (xq @ h.T.astype(np.int64)) + xq @ l.T.astype(np.int64)
+            + 128 * xq.sum(axis=1)[:, None] * sp[None, :].astype(np.int64))
     assert np.array_equal(comb, xq @ mm.T)
 
 
