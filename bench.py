@@ -254,7 +254,9 @@ def main():
                               merge_pct_hbm=round(100 * mb / (mms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                               gemm_us=round(gms * 1e3, 2), gemm_TOPS=round(gops / (gms * 1e-3) / 1e12, 1),
                               gemm_pct_int8_peak=round(100 * gops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
-                              sat=int(lay["out"]["sat"][0].item())))
+                              sat=int(lay["out"]["sat"][0].item()),
+                              int16_split=("balanced" if not bool(lay["out"]["split"].any()) else "bias")
+                              if "split" in lay["out"] else None))
     value = 100.0 * roof_ms / ms_per_step
     gemm_avg_ms = gemm_ms_tot / len(layers)
     achieved = gemm_ops_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e12
