@@ -470,10 +470,22 @@ __device__ __forceinline__ void add_saturations(unsigned long long* sat, int loc
 // Row groups are walked grid-stride, so any d fits the grid.
 // ---------------------------------------------------------------------------------
 typedef float vf4 __attribute__((ext_vector_type(4)));
+typedef int vi4 __attribute__((ext_vector_type(4)));
+typedef unsigned int vu2 __attribute__((ext_vector_type(2)));
 // 16-byte load that does not keep the line in the caches (U is read once).
 __device__ __forceinline__ float4 load_once4(const float* p) {
   const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
   return make_float4(v.x, v.y, v.z, v.w);
+}
+// Streaming stores of the merged integers (written once, read by a later kernel).
+__device__ __forceinline__ void store_once16(void* p, int4 v) {
+  __builtin_nontemporal_store(vi4{v.x, v.y, v.z, v.w}, reinterpret_cast<vi4*>(p));
+}
+__device__ __forceinline__ void store_once8(void* p, uint2 v) {
+  __builtin_nontemporal_store(vu2{v.x, v.y}, reinterpret_cast<vu2*>(p));
+}
+__device__ __forceinline__ void store_once4(void* p, uint32_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
 }
 
 constexpr int kQThreads = 128;
@@ -629,7 +641,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         pk.y = (mm[2] & 0xFFFF) | (mm[3] << 16);
         pk.z = (mm[4] & 0xFFFF) | (mm[5] << 16);
         pk.w = (mm[6] & 0xFFFF) | (mm[7] << 16);
-        *reinterpret_cast<int4*>(m + i * n + j0) = pk;
+        store_once16(m + i * n + j0, pk);
         if (split) {  // the balanced byte split of the int16 GEMM needs m <= 32639
           int mx = mm[0];
 #pragma unroll
@@ -747,14 +759,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
           uint32_t pk = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk |= ((uint32_t)mm[e] & 15u) << (4 * e);
-          *reinterpret_cast<uint32_t*>(m + i * (n >> 1) + (j0 >> 1)) = pk;
+          store_once4(m + i * (n >> 1) + (j0 >> 1), pk);
         } else {
           uint2 pk;
           pk.x = ((uint32_t)mm[0] & 255u) | (((uint32_t)mm[1] & 255u) << 8) | (((uint32_t)mm[2] & 255u) << 16) |
                  ((uint32_t)mm[3] << 24);
           pk.y = ((uint32_t)mm[4] & 255u) | (((uint32_t)mm[5] & 255u) << 8) | (((uint32_t)mm[6] & 255u) << 16) |
                  ((uint32_t)mm[7] << 24);
-          *reinterpret_cast<uint2*>(m + i * n + j0) = pk;
+          store_once8(m + i * n + j0, pk);
         }
         if (shift_dbg) {
           uint2 ps;
