@@ -76,6 +76,7 @@ def _declare(L):
         "ora_log2_round": (_I32, [_F32]),
         "ora_shift_scale": (_F32, [_F32, _F32]),
         "ora_merge_shift": (_I64, [_I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_ptq_merge": (None, [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "ora_quant_act": (None, [_I64, _I64, _P, _P, _P, _P]),
         "ora_bf16_rne": (ctypes.c_uint16, [_F32]),
         "ora_linear": (None, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
@@ -255,6 +256,25 @@ def merge_shift(wround, z, s, rstar, A, B, w_bits, v_bits):
     sat = lib().ora_merge_shift(rows, n, r, w_bits, v_bits, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(m),
                                 _p(sh), _p(sbar), _p(umin), _p(umax))
     return dict(m=m, shift=sh, sbar=sbar, umin=umin, umax=umax, sat=int(sat))
+
+
+def ptq_merge(wround, z, s, rstar, A, B, bits, want_x=False):
+    """QLoRA-style comparison path: x = (s*(W_round - z) + R*) + AB in binary32, then
+    the base quantizer per row at `bits` (codes, s', z').  The flow IntLoRA removes."""
+    wround = _c(wround, np.uint8)
+    rows, n = wround.shape
+    A = _c(A, np.float32)
+    B = _c(B, np.float32)
+    r = A.shape[1]
+    assert A.shape == (rows, r) and B.shape == (r, n)
+    z, s, rstar = _c(z, np.int32), _c(s, np.float32), _c(rstar, np.float32)
+    code = np.empty((rows, n), np.uint8)
+    sq = np.empty(rows, np.float32)
+    zq = np.empty(rows, np.int32)
+    x = np.empty((rows, n), np.float32) if want_x else None
+    lib().ora_ptq_merge(rows, n, r, bits, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(code), _p(sq),
+                        _p(zq), _p(x))
+    return dict(code=code, s=sq, z=zq, x=x)
 
 
 # --------------------------------------------------------------------------- linear

@@ -327,6 +327,61 @@ ORA_API int64_t ora_merge_mul(int64_t rows, int64_t n, int r, int u_bits, const 
 }
 
 /* ------------------------------------------------------------------------- */
+/* QLoRA-style comparison path (the flow IntLoRA removes, [IntLoRA notes]      */
+/* research background): dequantize the base, add the auxiliary matrix and    */
+/* the adapter in floating point, then re-quantize each row post-training.    */
+/* Reading (binary32, round to nearest even, in this order):                  */
+/*   deq = s_i * (W_round - z_i);  t = deq + R*_ij;                           */
+/*   acc = the fused multiply-add chain of A[i,k] B[k,j] over k from +0 (the  */
+/*   same product as the MLA term);  x = t + acc;                             */
+/* then the base quantizer of "1. AQS" (ora_base_quant's reading) on x at     */
+/* `bits`: lo = min(0, min x), hi = max(0, max x), s' = (hi - lo)/(2^b - 1)   */
+/* (1 if 0), z' = clamp(rint(-lo / s')), code = clamp(rint(x / s') + z').     */
+/* Every element takes part (no zero-denominator exclusion: there is none).   */
+/* x_out (optional) receives x.                                               */
+/* ------------------------------------------------------------------------- */
+static float ptq_element(int64_t i, int64_t j, int64_t n, int r, const uint8_t* wround, const int32_t* z,
+                         const float* s, const float* rstar, const float* A, const float* B) {
+    int w = (int)wround[i * n + j] - z[i];
+    float deq = s[i] * (float)w;
+    float t = deq + rstar[i * n + j];
+    float acc = 0.0f;
+    for (int k = 0; k < r; ++k) acc = fmaf(A[i * r + k], B[(int64_t)k * n + j], acc);
+    return t + acc;
+}
+
+ORA_API void ora_ptq_merge(int64_t rows, int64_t n, int r, int bits, const uint8_t* wround, const int32_t* z,
+                           const float* s, const float* rstar, const float* A, const float* B, uint8_t* code_out,
+                           float* s_out, int32_t* z_out, float* x_out) {
+    const int qmax = (1 << bits) - 1;
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < rows; ++i) {
+        float lo = 0.0f, hi = 0.0f;
+        for (int64_t j = 0; j < n; ++j) {
+            float x = ptq_element(i, j, n, r, wround, z, s, rstar, A, B);
+            if (x_out) x_out[i * n + j] = x;
+            if (x < lo) lo = x;
+            if (x > hi) hi = x;
+        }
+        float sq = (hi - lo) / (float)qmax;
+        if (!(sq > 0.0f)) sq = 1.0f;
+        float zf = rintf(-lo / sq);
+        int zq = (int)zf;
+        if (zq < 0) zq = 0;
+        if (zq > qmax) zq = qmax;
+        s_out[i] = sq;
+        z_out[i] = zq;
+        for (int64_t j = 0; j < n; ++j) {
+            float x = ptq_element(i, j, n, r, wround, z, s, rstar, A, B);
+            double code = (double)rintf(x / sq) + (double)zq;
+            if (code < 0.0) code = 0.0;
+            if (code > (double)qmax) code = (double)qmax;
+            code_out[i * n + j] = (uint8_t)code;
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* IntLoRA_SHIFT merge:  W' = sign(V) (.) [(W_round - z) >> shift].           */
 /* Reading: V = U / s_bar with s_bar = max |U| over the row's valid elements  */
 /*   (s_bar := 1 for an empty or all-zero row), so |V| <= 1 and only right     */
