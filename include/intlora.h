@@ -76,7 +76,8 @@ enum {
   INTLORA_OP_MERGE_MUL = 2,
   INTLORA_OP_MERGE_SHIFT = 3,
   INTLORA_OP_LINEAR = 4,
-  INTLORA_OP_BASE_QUANT = 5
+  INTLORA_OP_BASE_QUANT = 5,
+  INTLORA_OP_MERGE_PTQ = 6
 };
 
 /* One pretrained layer.  r is the LoRA rank (1..128); w_bits the base code width
@@ -180,6 +181,20 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
 int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int v_bits,
                         void* m, float* s_bar, uint8_t* shift_dbg, unsigned long long* sat_count, void* ws,
                         size_t ws_bytes, void* stream);
+
+/* QLoRA-style comparison path: the flow IntLoRA removes ([IntLoRA notes] research
+ * background; its PTQ step is what "training and inference efficiency" says IntLoRA
+ * avoids).  Per element, in binary32 and in this order:
+ *   x = (s_i * (W_round - z_i) + R*_ij) + acc,  acc = the fma chain of A[i,k] B[k,j]
+ *   over k from +0 (the same product as the MLA term);
+ * then the base quantizer of "1. AQS" on each row of x at `bits` (4 or 8): lo =
+ * min(0, min x), hi = max(0, max x), s' = (hi - lo)/(2^b - 1) (1 unless positive),
+ * z' = clamp(rint(-lo / s')), code = clamp(rint(x / s') + z') (IEEE division).  Every
+ * element takes part.  Outputs: code (uint8 d x n for 8 bits; packed nibbles d x n/2,
+ * low nibble = even column, for 4 bits), s_out[d], z_out[d].  The requantized weight
+ * is s'_i (code - z'_i).  Workspace: INTLORA_OP_MERGE_PTQ (x as fp32 scratch). */
+int intlora_merge_ptq(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int bits,
+                      void* code, float* s_out, int32_t* z_out, void* ws, size_t ws_bytes, void* stream);
 
 /* Per-token symmetric int8 activation quantization: s_x[t] = max_j |X[t,j]| / 127
  * (1 for an all-zero token), xq = clamp(rint(X / s_x), -127, 127), x_rowsum[t] =

@@ -116,7 +116,7 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 int run_adapt(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, MergeWs& w,
-              unsigned long long* sat_zero, hipStream_t st) {
+              unsigned long long* sat_zero, hipStream_t st, bool ptq = false) {
   intlora::AdaptArgs a;
   a.d = desc->d;
   a.n = desc->n;
@@ -134,6 +134,7 @@ int run_adapt(const intlora_desc* desc, const intlora_base* base, const intlora_
   a.pmin = w.pmin;
   a.pmax = w.pmax;
   a.sat_zero = sat_zero;
+  a.ptq = ptq;
   a.force_generic = false;
   return launch_status(intlora::launch_adapt(a, &w.ntiles, st), "adaptation kernel");
 }
@@ -173,6 +174,7 @@ size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
     case INTLORA_OP_STATS_UMINMAX:
     case INTLORA_OP_MERGE_MUL:
     case INTLORA_OP_MERGE_SHIFT:
+    case INTLORA_OP_MERGE_PTQ:
       return merge_ws_bytes(desc->d, desc->n);
     default:
       return 0;
@@ -290,6 +292,28 @@ int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, cons
                                                    static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
                                                    w.umax, static_cast<uint8_t*>(m), s_bar, shift_dbg, sat_count, st),
                        "quant_shift");
+}
+
+int intlora_merge_ptq(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int bits,
+                      void* code, float* s_out, int32_t* z_out, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (bits != 4 && bits != 8) return fail(INTLORA_EINVAL, "bits must be 4 or 8 (got %d)", bits);
+  if (bits == 4 && (desc->n & 1)) return fail(INTLORA_ESHAPE, "4-bit codes need even n");
+  if (desc->d == 0) return ok();
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_ptrs({code, s_out, z_out}, "merge_ptq"))) return s;
+  if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
+  if ((s = ensure_device())) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MergeWs w = carve(ws, desc->d, desc->n);
+  if ((s = run_adapt(desc, base, lora, w, nullptr, st, true))) return s;
+  if ((s = launch_status(intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, nullptr, st),
+                         "row range")))
+    return s;
+  return launch_status(intlora::launch_quant_ptq(desc->d, desc->n, bits, w.U, w.umin, w.umax,
+                                                 static_cast<uint8_t*>(code), s_out, z_out, st),
+                       "quant_ptq");
 }
 
 int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s_x, int32_t* x_rowsum,

@@ -21,6 +21,7 @@ struct AdaptArgs {
   int* pmin;  // order keys of the U range per (column tile, row), tile-major: pmin[tile * d + row]
   int* pmax;
   unsigned long long* sat_zero;  // zeroed by the adaptation kernel (nullable)
+  bool ptq;                      // x = (s w + R*) + AB for every element (comparison path) instead of U
   bool force_generic;
 };
 
@@ -44,6 +45,8 @@ hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const 
                             const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
                             int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
                             hipStream_t st);
+hipError_t launch_quant_ptq(int64_t d, int64_t n, int bits, const float* X, const float* xmin, const float* xmax,
+                            uint8_t* code, float* s_out, int32_t* z_out, hipStream_t st);
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
                               const float* U, const float* umin, const float* umax, uint8_t* m, float* sbar,
                               uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st);

@@ -260,7 +260,9 @@ typedef float v32f __attribute__((ext_vector_type(32)));
 constexpr int kMfmaCols = 256;
 constexpr int kMfmaMaxRowTiles = 8;
 
-template <int R, bool W4>
+// PTQ (the QLoRA-style comparison path): x = (s w + R*) + AB for every element instead
+// of U, with no division and no excluded elements.
+template <int R, bool W4, bool PTQ>
 __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
                                                     const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
                                                     const float* __restrict__ s, const float* __restrict__ c,
@@ -325,25 +327,33 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
         }
         const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
         float u[4], t[4], q[4];
-        bool slow = false;
+        if (PTQ) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
+            q[e] = (si * (float)w[e] + rs) + acc[4 * g + e];  // binary32 steps in this order
+          }
+        } else {
+          bool slow = false;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
+            t[e] = rs + acc[4 * g + e];
+            q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+            slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+          }
+          // the IEEE division runs only in waves where some lane needs it
+          if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+            __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+          }
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
-          t[e] = rs + acc[4 * g + e];
-          q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
-          slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
-        }
-        // the IEEE division runs only in waves where some lane needs it
-        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-          __asm__ volatile("");  // keeps the branch: the division is not speculated
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool valid = w[e] != 0;
-          const float uu = si + q[e];
+          const bool valid = PTQ || w[e] != 0;
+          const float uu = PTQ ? q[e] : si + q[e];
           u[e] = valid ? uu : 0.0f;
           const int key = f32_key(uu);
           kmin = valid ? min(kmin, key) : kmin;
@@ -380,7 +390,7 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
                                                       const float* __restrict__ c, const float* __restrict__ A,
                                                       const float* __restrict__ B, float* __restrict__ U,
                                                       int* __restrict__ pmin, int* __restrict__ pmax, int ntiles,
-                                                      unsigned long long* __restrict__ sat_zero) {
+                                                      unsigned long long* __restrict__ sat_zero, bool ptq) {
   __shared__ LnLds tab[96];
   __shared__ int smin[4], smax[4];
   load_ln_table(tab);
@@ -403,9 +413,9 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
     for (int k = 0; k < r; ++k) acc = fmaf(A[i * r + k], B[(int64_t)k * n + j], acc);
     const float rs = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, c[i], layer_id, seed, tab);
     const float t = rs + acc;
-    const bool valid = w != 0;
-    const float q = t / (float)(valid ? w : 1);
-    const float uu = s[i] + q;
+    const bool valid = ptq || w != 0;
+    const float q = t / (float)(w != 0 ? w : 1);
+    const float uu = ptq ? (s[i] * (float)w + rs) + acc : s[i] + q;
     U[i * n + j] = valid ? uu : 0.0f;
     if (valid) {
       kmin = min(kmin, f32_key(uu));
@@ -681,6 +691,97 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
   add_saturations(sat, nsat);
 }
 
+// QLoRA-style requant of x (the comparison path): the base quantizer of "1. AQS" per
+// row at `bits`, over every element.  Its parameters follow the same formulas as the
+// MUL quantizer (lo = min(x_min, 0), hi = max(x_max, 0), s' = (hi - lo)/(2^b - 1),
+// z' = clamp(rint(-lo/s')), code = clamp(rint(x/s') + z')), so the same helpers serve.
+// Output: uint8 codes (8 bits) or packed nibbles, low nibble = even column (4 bits).
+template <bool OUT4>
+__global__ __launch_bounds__(kQThreads) void k_quant_ptq(int64_t d, int64_t n, int bits, const float* __restrict__ X,
+                                                        const float* __restrict__ xmin_r,
+                                                        const float* __restrict__ xmax_r, uint8_t* __restrict__ code,
+                                                        float* __restrict__ s_out, int32_t* __restrict__ z_out) {
+  const int qmax = (1 << bits) - 1;
+  const int64_t j0 = (int64_t)blockIdx.x * kQCols + (int64_t)threadIdx.x * kQElems;
+  const int64_t ngroups = (d + kQRows - 1) / kQRows;
+  for (int64_t g = blockIdx.y; g < ngroups; g += gridDim.y) {
+    const int64_t i0 = g * kQRows;
+    if ((n & 7) == 0) {
+      float4 xa[kQRows], xb[kQRows];
+#pragma unroll
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i < d && j0 < n) {
+          xa[rr] = load_once4(X + i * n + j0);
+          xb[rr] = load_once4(X + i * n + j0 + 4);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i >= d) break;
+        const MulParams P = mul_params(xmin_r[i], xmax_r[i], qmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+          s_out[i] = P.sbar;
+          z_out[i] = P.zbar;
+        }
+        if (j0 >= n) continue;
+        const float xx[8] = {xa[rr].x, xa[rr].y, xa[rr].z, xa[rr].w, xb[rr].x, xb[rr].y, xb[rr].z, xb[rr].w};
+        int cd[8];
+        bool redo[8], any = false;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          bool exact = true;
+          cd[e] = mul_code_fast(xx[e], P, qmax, exact);
+          redo[e] = !exact;
+          any = any || redo[e];
+        }
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+          __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (redo[e]) cd[e] = mul_code(xx[e], P.sbar, P.zbar, qmax);
+        }
+        if (OUT4) {
+          uint32_t pk = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk |= (uint32_t)cd[e] << (4 * e);
+          store_once4(code + i * (n >> 1) + (j0 >> 1), pk);
+        } else {
+          uint2 pk;
+          pk.x = (uint32_t)cd[0] | ((uint32_t)cd[1] << 8) | ((uint32_t)cd[2] << 16) | ((uint32_t)cd[3] << 24);
+          pk.y = (uint32_t)cd[4] | ((uint32_t)cd[5] << 8) | ((uint32_t)cd[6] << 16) | ((uint32_t)cd[7] << 24);
+          store_once8(code + i * n + j0, pk);
+        }
+      }
+    } else {
+      // general n (4-bit output needs even n, validated): pairs, so a packed byte is whole
+      for (int rr = 0; rr < kQRows; ++rr) {
+        const int64_t i = i0 + rr;
+        if (i >= d) break;
+        const MulParams P = mul_params(xmin_r[i], xmax_r[i], qmax);
+        if (blockIdx.x == 0 && threadIdx.x == 0) {
+          s_out[i] = P.sbar;
+          z_out[i] = P.zbar;
+        }
+        for (int e = 0; e < kQElems; e += 2) {
+          const int64_t j = j0 + e;
+          if (j >= n) break;
+          int c2[2] = {0, 0};
+          for (int h = 0; h < 2; ++h)
+            if (j + h < n) c2[h] = mul_code(X[i * n + j + h], P.sbar, P.zbar, qmax);
+          if (OUT4) {
+            code[i * (n >> 1) + (j >> 1)] = (uint8_t)(c2[0] | (c2[1] << 4));
+          } else {
+            code[i * n + j] = (uint8_t)c2[0];
+            if (j + 1 < n) code[i * n + j + 1] = (uint8_t)c2[1];
+          }
+        }
+      }
+    }
+  }
+}
+
 // SHIFT: s_bar = max(|U_min|, |U_max|) (1 for an empty / zero row), V = U / s_bar,
 // shift = clamp(-round(log2|V|), 0, 2^bV - 1) (V == 0: largest code, m = 0),
 // m = sign(V) (w >> shift) (arithmetic), saturated to bW signed bits.  Output int8
@@ -864,14 +965,14 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
 
 int adapt_max_ntiles(int64_t n) { return (int)((n + kMfmaCols - 1) / kMfmaCols); }
 
-template <int R, bool W4>
+template <int R, bool W4, bool PTQ>
 static int64_t mfma_slots() {
   static int64_t slots = 0;
   if (slots == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_mfma<R, W4>), 256,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_mfma<R, W4, PTQ>), 256,
                                                      0) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
       return 1024;
@@ -880,12 +981,12 @@ static int64_t mfma_slots() {
   return slots;
 }
 
-template <int R, bool W4>
+template <int R, bool W4, bool PTQ>
 static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   const int ntiles = (int)((a.n + kMfmaCols - 1) / kMfmaCols);
   *ntiles_out = ntiles;
   const int64_t row_tiles = (a.d + 31) / 32;
-  const int64_t slots = mfma_slots<R, W4>();
+  const int64_t slots = mfma_slots<R, W4, PTQ>();
   // row tiles per block (1..8): the count whose grid best fills the resident slots
   int rtiles = 1;
   double best = -1.0;
@@ -903,7 +1004,7 @@ static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStre
     const int64_t cnt = nrb - rb0 < 65535 ? nrb - rb0 : 65535;
     const dim3 grid((unsigned)ntiles, (unsigned)cnt);
     unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
-    hipLaunchKernelGGL((k_adapt_mfma<R, W4>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround, a.z,
+    hipLaunchKernelGGL((k_adapt_mfma<R, W4, PTQ>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround, a.z,
                        a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rtiles, rb0, sz);
   }
   return hipGetLastError();
@@ -911,7 +1012,11 @@ static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStre
 
 template <int R>
 static hipError_t launch_adapt_m(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
-  return a.w_bits == 4 ? launch_adapt_mfma<R, true>(a, ntiles_out, st) : launch_adapt_mfma<R, false>(a, ntiles_out, st);
+  if (a.ptq)
+    return a.w_bits == 4 ? launch_adapt_mfma<R, true, true>(a, ntiles_out, st)
+                         : launch_adapt_mfma<R, false, true>(a, ntiles_out, st);
+  return a.w_bits == 4 ? launch_adapt_mfma<R, true, false>(a, ntiles_out, st)
+                       : launch_adapt_mfma<R, false, false>(a, ntiles_out, st);
 }
 
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
@@ -932,7 +1037,7 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   *ntiles_out = ntiles;
   dim3 grid((unsigned)ntiles, (unsigned)(a.d < 65535 ? (a.d ? a.d : 1) : 65535));
   hipLaunchKernelGGL(k_adapt_generic, grid, dim3(256), 0, st, a.d, a.n, a.r, a.w_bits, a.seed, a.layer_id, a.wround,
-                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero);
+                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero, a.ptq);
   return hipGetLastError();
 }
 
@@ -959,6 +1064,17 @@ hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const 
   else
     hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
                        sbar, zbar, split, uround_dbg, sat);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_ptq(int64_t d, int64_t n, int bits, const float* X, const float* xmin, const float* xmax,
+                            uint8_t* code, float* s_out, int32_t* z_out, hipStream_t st) {
+  const dim3 grid = quant_grid(d, n);
+  if (bits == 4)
+    hipLaunchKernelGGL(k_quant_ptq<true>, grid, dim3(kQThreads), 0, st, d, n, bits, X, xmin, xmax, code, s_out, z_out);
+  else
+    hipLaunchKernelGGL(k_quant_ptq<false>, grid, dim3(kQThreads), 0, st, d, n, bits, X, xmin, xmax, code, s_out,
+                       z_out);
   return hipGetLastError();
 }
 

@@ -104,6 +104,21 @@ def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, o
     return o
 
 
+def merge_ptq(st, A, Bm, w_bits, bits, seed, layer_id, ws=None, out=None):
+    """QLoRA-style comparison path: x = (s w + R*) + AB, per-row requant at `bits`."""
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    ws = workspace(B.INTLORA_OP_MERGE_PTQ, d, n, r, w_bits, dev) if ws is None else ws
+    o = out or dict(code=torch.empty(code_bytes(d, n, bits), dtype=torch.uint8, device=dev),
+                    s=torch.empty(d, dtype=torch.float32, device=dev),
+                    z=torch.empty(d, dtype=torch.int32, device=dev))
+    B.intlora_merge_ptq(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), bits, o["code"], o["s"],
+                        o["z"], ws)
+    return o
+
+
 def quant_act(X):
     M, n = X.shape
     xq = torch.empty((M, n), dtype=torch.int8, device=X.device)

@@ -131,6 +131,22 @@ def test_other_entry_points_validation(lib):
     assert lib.intlora_debug_ln(-1, FAKE, FAKE, None) == B.INTLORA_ESHAPE
 
 
+def test_merge_ptq_validation(lib):
+    dsc = B.desc(8, 8, 4, 8)
+    base, lora = B.Base(FAKE, FAKE, FAKE, FAKE), B.Lora(FAKE, FAKE)
+    mp = lib.intlora_merge_ptq
+    assert mp(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 6, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_EINVAL  # bits not 4 / 8
+    odd = B.desc(8, 7, 4, 8)
+    assert mp(ctypes.byref(odd), ctypes.byref(base), ctypes.byref(lora), 4, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_ESHAPE  # 4-bit codes with odd n
+    assert mp(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 8, 0, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_EINVAL  # NULL output
+    assert mp(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 8, FAKE, FAKE, FAKE, 0, 0,
+              None) == B.INTLORA_EWORKSPACE
+    assert B.intlora_workspace_bytes(B.INTLORA_OP_MERGE_PTQ, B.desc(64, 256, 4, 8)) >= 64 * 256 * 4
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(B.IntLoraError) as ei:
         B._check(lib.intlora_vmc_scale(8, FAKE, -1.0, FAKE, None), "intlora_vmc_scale")

@@ -111,3 +111,29 @@ def test_llama_sweep_blocks_sampled(ops, block):
     for li, L in enumerate(wl.layers):
         check_layer(ops, wl, li, L, (16,), mode, mbits, block=block, n_rows=4, n_tok=2)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl_index,li", [(3, 0), (3, 3), (4, 4)])
+def test_ptq_path_full_size_sampled(ops, wl_index, li):
+    """The QLoRA-style comparison path at full layer size (FLUX qkv and mlp_out, Llama
+    gate): sampled rows of codes, s' and z' equal the oracle's, at the base's bit width."""
+    wl = synth.WORKLOADS[wl_index]
+    L = wl.layers[li]
+    lid = synth.layer_id(wl.index, li)
+    W = synth.weight(wl, li)
+    A, Bm = synth.lora(wl, li)
+    seed = synth.PHILOX_SEED
+    st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+    g = ops.merge_ptq(st, cuda(A), cuda(Bm), wl.w_bits, wl.w_bits, seed, lid)
+    rows = sample_rows(L.d, 6, 13 * li + wl_index)
+    sig = oracle.sigma_w(W[rows])
+    c = oracle.vmc_scale(sig, synth.ALPHA)
+    R = np.concatenate([oracle.gen_r_rows(int(i), 1, L.n, seed, lid, c[k:k + 1]) for k, i in enumerate(rows)])
+    wr, z, s = oracle.base_quant(W[rows], R, wl.w_bits)
+    ref = oracle.ptq_merge(wr, z, s, R, A[rows], Bm, wl.w_bits)
+    code = host(g["code"])
+    code = unpack4(code) if wl.w_bits == 4 else code
+    assert np.array_equal(code[rows], ref["code"])
+    assert np.array_equal(bits(host(g["s"])[rows]), bits(ref["s"]))
+    assert np.array_equal(host(g["z"])[rows], ref["z"])
+    torch.cuda.empty_cache()

@@ -57,6 +57,9 @@ def bits(a):
     return a.view(np.uint32) if a.dtype == np.float32 else a
 
 
+bits_of = bits  # for tests whose loop variable is called bits
+
+
 def random_state(seed, d, n, r, w_bits):
     """Synthetic stored state of a quantized layer plus LoRA factors."""
     wr = synth.random_codes(seed, (d, n), w_bits)
@@ -173,6 +176,26 @@ def test_merge_shift_bitexact(ops, d, n, r, w_bits):
         assert np.array_equal(host(g["shift"]), ref["shift"])
         assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
         assert int(host(g["sat"])[0]) == ref["sat"]
+
+
+@pytest.mark.parametrize("d,n,r,w_bits", MERGE_CASES)
+def test_merge_ptq_bitexact(ops, d, n, r, w_bits):
+    """QLoRA-style comparison path: x = (s w + R*) + AB and the per-row requant, codes,
+    s' and z' bit for bit, at 4 and 8 bits (both adaptation and quantize paths)."""
+    seed = 300 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    st = gpu_state(wr, z, s, c, w_bits)
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+    for bits in (4, 8):
+        if bits == 4 and n % 2:
+            continue
+        g = ops.merge_ptq(st, cuda(A), cuda(Bm), w_bits, bits, 77, 5)
+        ref = oracle.ptq_merge(wr, z, s, R, A, Bm, bits)
+        code = host(g["code"])
+        code = unpack4(code) if bits == 4 else code
+        assert np.array_equal(code, ref["code"]), bits
+        assert np.array_equal(bits_of(host(g["s"])), bits_of(ref["s"]))
+        assert np.array_equal(host(g["z"]), ref["z"])
 
 
 def test_merge_degenerate_rows(ops):
