@@ -48,6 +48,9 @@ def parse():
     p.add_argument("--overlap", action="store_true",
                    help="also time a pipelined step: merges on a second stream, each layer's linear layer "
                         "waiting only for its own merge")
+    p.add_argument("--no-ptq", action="store_true",
+                   help="skip the QLoRA-style comparison (MUL workloads): the dequantize / add / requant "
+                        "path timed on the same layers, and both paths' weight error")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -98,6 +101,58 @@ def traffic_from_profile(workload_name):
     if rec.get("kernel_source_sha") != kernel_source_sha() or rec.get("workload") != workload_name:
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows_per_layer=64):
+    """The flow IntLoRA removes, on the same layers: dequantize, add R* + AB in binary32,
+    requantize each row at the base's bit width (intlora_merge_ptq).  Times it like the
+    merge (whole layers, events on the same stream) and compares both paths' merged
+    weights with the binary64 adapted weight s w + R* + AB on sampled rows."""
+    outs = [None] * len(layers)
+
+    def run():
+        for k, lay in enumerate(layers):
+            outs[k] = ops.merge_ptq(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, wl.w_bits, synth.PHILOX_SEED,
+                                    lay["lid"], ws=ws, out=outs[k])
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ptq_ms = e0.elapsed_time(e1) / args.steps
+
+    def unpack(codes, n):
+        if codes.shape[1] == n:
+            return codes.to(torch.int64)
+        c = codes.to(torch.int64)
+        return torch.stack([c & 15, c >> 4], dim=2).reshape(codes.shape[0], n)
+
+    per = []
+    for k, lay in enumerate(layers):
+        L = lay["L"]
+        rows = torch.linspace(0, L.d - 1, rows_per_layer, device=dev).round().to(torch.int64).unique()
+        c = lay["st"]["c"]
+        R = torch.empty((L.d, L.n), dtype=torch.float32, device=dev)
+        B.intlora_gen_r(B.desc(L.d, L.n, wl.r, wl.w_bits, synth.PHILOX_SEED, lay["lid"]), c, R)
+        w = unpack(lay["st"]["wround"][rows], L.n) - lay["st"]["z"][rows].to(torch.int64)[:, None]
+        target = (lay["st"]["s"][rows].double()[:, None] * w.double() + R[rows].double()
+                  + lay["Ag"][rows].double() @ lay["Bg"].double())
+        m = lay["out"]["m"][rows].double()
+        intlora = lay["out"]["sbar"][rows].double()[:, None] * m
+        code = unpack(outs[k]["code"][rows], L.n)
+        ptqw = outs[k]["s"][rows].double()[:, None] * (code - outs[k]["z"][rows].to(torch.int64)[:, None]).double()
+        tn = torch.linalg.norm(target)
+        per.append(dict(layer=L.name, rel_err_intlora=float(torch.linalg.norm(intlora - target) / tn),
+                        rel_err_ptq=float(torch.linalg.norm(ptqw - target) / tn), rows=int(rows.numel())))
+        del R
+    return dict(kind="dequantize + add R* + AB (binary32) + per-row RTN requant at %d bits" % wl.w_bits,
+                ptq_merge_us_per_step=round(ptq_ms * 1e3, 1), per_layer=per)
 
 
 def main():
@@ -234,6 +289,11 @@ def main():
         torch.cuda.synchronize()
         overlap_ms = t0_.elapsed_time(t1_) / args.steps
 
+    # ---------------------------------------------------------------- QLoRA-style comparison
+    ptq = None
+    if mode == "mul" and not args.no_ptq:
+        ptq = ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream)
+
     # ---------------------------------------------------------------- per-layer figures
     per_layer = []
     roof_ms = 0.0
@@ -289,6 +349,7 @@ def main():
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
+        "ptq_comparison": ptq,
         "setup_s": round(setup_s, 1),
     }
 
