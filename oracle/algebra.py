@@ -50,3 +50,17 @@ def dequant_mul(sbar, m):
 def dequant_shift(sbar, m):
     """Merged SHIFT weight s_bar * m (m = sign(V) * (w >> shift))."""
     return np.asarray(sbar, np.float64)[:, None] * np.asarray(m, np.float64)
+
+
+def ste_backward(wround, z, A, B, G):
+    """Straight-through backward of the MUL / SHIFT fake-quant merge to the LoRA factors,
+    in binary64 ([IntLoRA notes], "two implementation variants": training uses the STE).
+
+    Reading: the rounding of U (MUL) and of log2|V| (SHIFT) pass gradients unchanged,
+    s_bar and z_bar are constants, and R* takes none (sg(R), "1. AQS").  Then the merged
+    weight behaves as U (.) w = s*w + R* + AB where w != 0, and is the constant 0 where
+    w == 0, so with G = dL/dW' and the mask M = [w != 0]:
+        dL/d(AB) = G (.) M,   dA = (G (.) M) B^T,   dB = A^T (G (.) M).
+    Returns (dA, dB) as float64."""
+    D = np.asarray(G, np.float64) * (signed_base(wround, z) != 0)
+    return D @ np.asarray(B, np.float64).T, np.asarray(A, np.float64).T @ D
