@@ -77,7 +77,8 @@ enum {
   INTLORA_OP_MERGE_SHIFT = 3,
   INTLORA_OP_LINEAR = 4,
   INTLORA_OP_BASE_QUANT = 5,
-  INTLORA_OP_MERGE_PTQ = 6
+  INTLORA_OP_MERGE_PTQ = 6,
+  INTLORA_OP_STE_BACKWARD = 7
 };
 
 /* One pretrained layer.  r is the LoRA rank (1..128); w_bits the base code width
@@ -195,6 +196,22 @@ int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, cons
  * is s'_i (code - z'_i).  Workspace: INTLORA_OP_MERGE_PTQ (x as fp32 scratch). */
 int intlora_merge_ptq(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int bits,
                       void* code, float* s_out, int32_t* z_out, void* ws, size_t ws_bytes, void* stream);
+
+/* Straight-through backward of the MUL / SHIFT fake-quant merge to the LoRA factors
+ * ([IntLoRA notes] "two implementation variants": training back-propagates through the
+ * quantizers with the STE; "1. AQS": R takes no gradient).  Reading: the roundings
+ * pass gradients unchanged and s_bar, z_bar are constants, so the merged weight acts as
+ * U (.) w = s w + R* + AB where w = W_round - z != 0 and as the constant 0 where w = 0.
+ * With G = dL/dW' (fp32 d x n) and D = G (.) [w != 0]:
+ *   dA = D B^T (fp32 d x r),  dB = A^T D (fp32 r x n),
+ * accumulated in binary32 on the matrix cores in an order fixed by (d, n) alone
+ * (deterministic; each output within the binary32 summation bound of its exact value).
+ * w_round: the base codes (uint8 d x n, or packed d x n/2 for w_bits 4), z[d]; A d x r,
+ * B r x n (as for the merge).  r <= 128.  Workspace: INTLORA_OP_STE_BACKWARD (partial
+ * sums; 0 bytes for small shapes). */
+int intlora_ste_backward(const intlora_desc* desc, const void* w_round, const int32_t* z, const float* A,
+                         const float* B, const float* G, float* dA, float* dB, void* ws, size_t ws_bytes,
+                         void* stream);
 
 /* Per-token symmetric int8 activation quantization: s_x[t] = max_j |X[t,j]| / 127
  * (1 for an all-zero token), xq = clamp(rint(X / s_x), -127, 127), x_rowsum[t] =

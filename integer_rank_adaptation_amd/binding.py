@@ -18,7 +18,7 @@ INTLORA_OK, INTLORA_EINVAL, INTLORA_ESHAPE, INTLORA_EALIGN, INTLORA_EWORKSPACE, 
 INTLORA_SIGMA_W, INTLORA_U_MINMAX = 0, 1
 INTLORA_W_INT4, INTLORA_W_INT8, INTLORA_W_INT16 = 4, 8, 16
 INTLORA_OP_STATS_UMINMAX, INTLORA_OP_MERGE_MUL, INTLORA_OP_MERGE_SHIFT, INTLORA_OP_LINEAR, INTLORA_OP_BASE_QUANT = 1, 2, 3, 4, 5
-INTLORA_OP_MERGE_PTQ = 6
+INTLORA_OP_MERGE_PTQ, INTLORA_OP_STE_BACKWARD = 6, 7
 
 
 class IntLoraError(RuntimeError):
@@ -62,6 +62,7 @@ _SIG = {
                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_ptq": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, ctypes.c_size_t, _P]),
+    "intlora_ste_backward": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_quant_act": (_INT, [_I64, _I64, _P, _P, _P, _P, _P]),
     "intlora_linear_fwd": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_debug_ln": (_INT, [_I64, _P, _P, _P]),
@@ -172,6 +173,12 @@ def intlora_merge_ptq(dsc: Desc, bs: Base, lr: Lora, bits: int, code, s_out, z_o
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
     _check(lib().intlora_merge_ptq(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), bits, _ptr(code),
                                    _ptr(s_out), _ptr(z_out), _ptr(ws), wsb, _stream(stream)), "intlora_merge_ptq")
+
+
+def intlora_ste_backward(dsc: Desc, w_round, z, A, B, G, dA, dB, ws=None, stream=None):
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().intlora_ste_backward(ctypes.byref(dsc), _ptr(w_round), _ptr(z), _ptr(A), _ptr(B), _ptr(G), _ptr(dA),
+                                      _ptr(dB), _ptr(ws), wsb, _stream(stream)), "intlora_ste_backward")
 
 
 def intlora_quant_act(M: int, n: int, X, xq, s_x, x_rowsum=None, stream=None):

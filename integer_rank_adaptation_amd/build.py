@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libintlora.so")
-SOURCES = ["capi.hip", "merge.hip", "linear.hip"]
+SOURCES = ["capi.hip", "merge.hip", "linear.hip", "ste.hip"]
 
 # -ffp-contract=off: no implicit multiply-add fusion (every fp32 step is the IEEE
 # operation written); packed fp32 instructions are disabled for all device code.

@@ -176,6 +176,8 @@ size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
     case INTLORA_OP_MERGE_SHIFT:
     case INTLORA_OP_MERGE_PTQ:
       return merge_ws_bytes(desc->d, desc->n);
+    case INTLORA_OP_STE_BACKWARD:
+      return intlora::ste_ws_bytes(desc->d, desc->n, desc->r);
     default:
       return 0;
   }
@@ -314,6 +316,21 @@ int intlora_merge_ptq(const intlora_desc* desc, const intlora_base* base, const 
   return launch_status(intlora::launch_quant_ptq(desc->d, desc->n, bits, w.U, w.umin, w.umax,
                                                  static_cast<uint8_t*>(code), s_out, z_out, st),
                        "quant_ptq");
+}
+
+int intlora_ste_backward(const intlora_desc* desc, const void* w_round, const int32_t* z, const float* A,
+                         const float* B, const float* G, float* dA, float* dB, void* ws, size_t ws_bytes,
+                         void* stream) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (desc->d == 0) return ok();
+  if ((s = check_ptrs({w_round, z, A, B, G, dA, dB}, "ste_backward"))) return s;
+  if ((s = check_ws(ws, ws_bytes, intlora::ste_ws_bytes(desc->d, desc->n, desc->r)))) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_ste_backward(desc->d, desc->n, desc->r, desc->w_bits,
+                                                    static_cast<const uint8_t*>(w_round), z, A, B, G, dA, dB, ws,
+                                                    static_cast<hipStream_t>(stream)),
+                       "ste_backward");
 }
 
 int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s_x, int32_t* x_rowsum,

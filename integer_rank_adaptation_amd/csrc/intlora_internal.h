@@ -50,6 +50,18 @@ hipError_t launch_quant_ptq(int64_t d, int64_t n, int bits, const float* X, cons
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
                               const float* U, const float* umin, const float* umax, uint8_t* m, float* sbar,
                               uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st);
+// Straight-through backward (ste.hip): launch geometry, workspace and launcher.
+struct SteSplits {
+  int S;                   // column ranges of the dA reduction
+  int64_t cols_per_split;  // a multiple of 32
+  int S2;                  // row ranges of the dB reduction
+  int64_t rows_per_split;  // a multiple of 8
+};
+SteSplits ste_splits(int64_t d, int64_t n);
+size_t ste_ws_bytes(int64_t d, int64_t n, int r);
+hipError_t launch_ste_backward(int64_t d, int64_t n, int r, int w_bits, const uint8_t* wround, const int32_t* z,
+                               const float* A, const float* B, const float* G, float* dA, float* dB, void* ws,
+                               hipStream_t st);
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const uint8_t* split, const float* sbar, uint16_t* Y,
                          int32_t* acc_dbg, hipStream_t st);

@@ -119,6 +119,21 @@ def merge_ptq(st, A, Bm, w_bits, bits, seed, layer_id, ws=None, out=None):
     return o
 
 
+def ste_backward(st, A, Bm, G, w_bits, ws=None, out=None):
+    """Straight-through backward to the LoRA factors: dA = (G.[w != 0]) B^T, dB = A^T (G.[w != 0])."""
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits)
+    if ws is None:
+        nb = B.intlora_workspace_bytes(B.INTLORA_OP_STE_BACKWARD, dsc)
+        ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
+    o = out or dict(dA=torch.empty((d, r), dtype=torch.float32, device=dev),
+                    dB=torch.empty((r, n), dtype=torch.float32, device=dev))
+    B.intlora_ste_backward(dsc, st["wround"], st["z"], A, Bm, G, o["dA"], o["dB"], ws)
+    return o
+
+
 def quant_act(X):
     M, n = X.shape
     xq = torch.empty((M, n), dtype=torch.int8, device=X.device)

@@ -147,6 +147,20 @@ def test_merge_ptq_validation(lib):
     assert B.intlora_workspace_bytes(B.INTLORA_OP_MERGE_PTQ, B.desc(64, 256, 4, 8)) >= 64 * 256 * 4
 
 
+def test_ste_backward_validation(lib):
+    sb = lib.intlora_ste_backward
+    bad_r = B.desc(8, 8, 129, 8)
+    assert sb(ctypes.byref(bad_r), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None) == B.INTLORA_EINVAL
+    dsc = B.desc(8, 8, 4, 8)
+    assert sb(ctypes.byref(dsc), FAKE, FAKE, FAKE, FAKE, 0, FAKE, FAKE, None, 0, None) == B.INTLORA_EINVAL
+    assert sb(ctypes.byref(dsc), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, None, 0, None) == B.INTLORA_EALIGN
+    big = B.desc(4096, 4096, 32, 4)
+    need = B.intlora_workspace_bytes(B.INTLORA_OP_STE_BACKWARD, big)
+    assert need > 0
+    assert sb(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, need - 1, None) == \
+        B.INTLORA_EWORKSPACE
+
+
 def test_binding_raises_with_message(lib):
     with pytest.raises(B.IntLoraError) as ei:
         B._check(lib.intlora_vmc_scale(8, FAKE, -1.0, FAKE, None), "intlora_vmc_scale")

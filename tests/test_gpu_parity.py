@@ -198,6 +198,45 @@ def test_merge_ptq_bitexact(ops, d, n, r, w_bits):
         assert np.array_equal(host(g["z"]), ref["z"])
 
 
+STE_CASES = [
+    # d, n, r, w_bits: general-column path (n % 8 != 0), 1..4 k tiles, split reductions
+    (1, 8, 1, 8),
+    (17, 100, 4, 8),
+    (40, 520, 8, 4),
+    (33, 1024, 32, 4),
+    (64, 2048, 64, 8),
+    (100, 3000, 96, 8),
+    (20, 256, 128, 4),
+    (600, 4096, 32, 4),
+    (2000, 512, 16, 8),
+]
+
+
+@pytest.mark.parametrize("d,n,r,w_bits", STE_CASES)
+def test_ste_backward(ops, d, n, r, w_bits):
+    """Straight-through backward: dA = D B^T and dB = A^T D with D = G.[w != 0], against
+    the binary64 oracle within the binary32 summation bound (K + 16) 2^-23 sum|terms|,
+    and bit-identical on a second call (fixed reduction order)."""
+    from oracle import algebra
+
+    seed = 500 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    wr[0, : min(n, 5)] = z[0]  # some w == 0 in every case
+    G = synth.random_matrix(seed + 9, (d, n), 1.0)
+    st = gpu_state(wr, z, s, c, w_bits)
+    g = ops.ste_backward(st, cuda(A), cuda(Bm), cuda(G), w_bits)
+    g2 = ops.ste_backward(st, cuda(A), cuda(Bm), cuda(G), w_bits)
+    dA, dB = host(g["dA"]).astype(np.float64), host(g["dB"]).astype(np.float64)
+    assert torch.equal(g["dA"], g2["dA"]) and torch.equal(g["dB"], g2["dB"])
+    rA, rB = algebra.ste_backward(wr, z, A, Bm, G)
+    mask = (wr.astype(np.int64) - z.astype(np.int64)[:, None]) != 0
+    absD = np.abs(G.astype(np.float64)) * mask
+    boundA = (n + 16) * 2.0**-23 * (absD @ np.abs(Bm.astype(np.float64)).T) + 1e-30
+    boundB = (d + 16) * 2.0**-23 * (np.abs(A.astype(np.float64)).T @ absD) + 1e-30
+    assert np.all(np.abs(dA - rA) <= boundA)
+    assert np.all(np.abs(dB - rB) <= boundB)
+
+
 def test_merge_degenerate_rows(ops):
     """Rows with no valid element (w == 0 everywhere) and rows with U == s everywhere."""
     d, n, r = 4, 64, 4
