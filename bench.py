@@ -51,6 +51,8 @@ def parse():
     p.add_argument("--no-ptq", action="store_true",
                    help="skip the QLoRA-style comparison (MUL workloads): the dequantize / add / requant "
                         "path timed on the same layers, and both paths' weight error")
+    p.add_argument("--no-ste", action="store_true",
+                   help="skip the straight-through backward (a synthetic dL/dW' per layer, dA and dB)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -153,6 +155,40 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
         del R
     return dict(kind="dequantize + add R* + AB (binary32) + per-row RTN requant at %d bits" % wl.w_bits,
                 ptq_merge_us_per_step=round(ptq_ms * 1e3, 1), per_layer=per)
+
+
+def ste_measure(args, wl, layers, ops, torch, dev, stream):
+    """The straight-through backward of every layer (dA = D B^T, dB = A^T D with
+    D = G.[w != 0]) on a seeded synthetic gradient G ~ N(0, 1e-6) per layer, timed like
+    the merge.  Bytes per element: one pass over G (4 B) and the codes is the least any
+    implementation reads; the two product kernels read them twice."""
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(1234)
+    Gs = [torch.randn((lay["L"].d, lay["L"].n), generator=gen, device=dev, dtype=torch.float32) * 1e-3
+          for lay in layers]
+    outs = [None] * len(layers)
+
+    def run():
+        for k, lay in enumerate(layers):
+            outs[k] = ops.ste_backward(lay["st"], lay["Ag"], lay["Bg"], Gs[k], wl.w_bits, out=outs[k])
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(args.steps):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    code_b = 0.5 if wl.w_bits == 4 else 1.0
+    one_pass = sum(lay["L"].d * lay["L"].n * (4 + code_b) for lay in layers)
+    del Gs
+    return dict(us_per_step=round(ms * 1e3, 1), one_pass_GBps=round(one_pass / (ms * 1e-3) / 1e9, 1),
+                one_pass_pct_hbm=round(100 * one_pass / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                note="G and the codes are read by both product kernels (twice)")
 
 
 def main():
@@ -294,6 +330,10 @@ def main():
     if mode == "mul" and not args.no_ptq:
         ptq = ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream)
 
+    ste = None
+    if not args.no_ste:
+        ste = ste_measure(args, wl, layers, ops, torch, dev, stream)
+
     # ---------------------------------------------------------------- per-layer figures
     per_layer = []
     roof_ms = 0.0
@@ -350,6 +390,7 @@ def main():
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
         "ptq_comparison": ptq,
+        "ste_backward": ste,
         "setup_s": round(setup_s, 1),
     }
 

@@ -137,3 +137,30 @@ def test_ptq_path_full_size_sampled(ops, wl_index, li):
     assert np.array_equal(bits(host(g["s"])[rows]), bits(ref["s"]))
     assert np.array_equal(host(g["z"])[rows], ref["z"])
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl_index,li", [(3, 0), (3, 3), (4, 6)])
+def test_ste_backward_full_size(ops, wl_index, li):
+    """The straight-through backward at full layer size (FLUX qkv and mlp_out, Llama
+    down): every output of dA and dB within the binary32 summation bound of the binary64
+    oracle."""
+    from oracle import algebra
+
+    wl = synth.WORKLOADS[wl_index]
+    L = wl.layers[li]
+    lid = synth.layer_id(wl.index, li)
+    W = synth.weight(wl, li)
+    A, Bm = synth.lora(wl, li)
+    G = synth.random_matrix(900 + li, (L.d, L.n), 1e-3)
+    st = ops.setup_layer(cuda(W), wl.w_bits, synth.PHILOX_SEED, lid, synth.ALPHA)
+    g = ops.ste_backward(st, cuda(A), cuda(Bm), cuda(G), wl.w_bits)
+    wr = host(st["wround"])
+    wr = unpack4(wr) if wl.w_bits == 4 else wr
+    z = host(st["z"])
+    rA, rB = algebra.ste_backward(wr, z, A, Bm, G)
+    absD = np.abs(G.astype(np.float64)) * ((wr.astype(np.int64) - z.astype(np.int64)[:, None]) != 0)
+    boundA = (L.n + 16) * 2.0**-23 * (absD @ np.abs(Bm.astype(np.float64)).T) + 1e-30
+    boundB = (L.d + 16) * 2.0**-23 * (np.abs(A.astype(np.float64)).T @ absD) + 1e-30
+    assert np.all(np.abs(host(g["dA"]).astype(np.float64) - rA) <= boundA)
+    assert np.all(np.abs(host(g["dB"]).astype(np.float64) - rB) <= boundB)
+    torch.cuda.empty_cache()
