@@ -32,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "merge GB/s + W8A8/W4A8 GEMM int8 TOPS (% of MI355X peak) per layer shape"
 HBM_PEAK_GBPS = 8000.0
 INT8_PEAK_TOPS = 5000.0
+FP32_MFMA_TFLOPS = 157.3
 
 
 def parse():
@@ -160,8 +161,9 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
 def ste_measure(args, wl, layers, ops, torch, dev, stream):
     """The straight-through backward of every layer (dA = D B^T, dB = A^T D with
     D = G.[w != 0]) on a seeded synthetic gradient G ~ N(0, 1e-6) per layer, timed like
-    the merge.  Bytes per element: one pass over G (4 B) and the codes is the least any
-    implementation reads; the two product kernels read them twice."""
+    the merge.  Two bounds per element: one pass over G (4 B) and its code (HBM), and
+    the two products' 4 r flops on the fp32 matrix cores (157.3 TFLOP/s); the fused
+    kernel reads G and the codes once."""
     gen = torch.Generator(device=dev)
     gen.manual_seed(1234)
     Gs = [torch.randn((lay["L"].d, lay["L"].n), generator=gen, device=dev, dtype=torch.float32) * 1e-3
@@ -185,10 +187,15 @@ def ste_measure(args, wl, layers, ops, torch, dev, stream):
     ms = e0.elapsed_time(e1) / args.steps
     code_b = 0.5 if wl.w_bits == 4 else 1.0
     one_pass = sum(lay["L"].d * lay["L"].n * (4 + code_b) for lay in layers)
+    flops = sum(4.0 * lay["L"].d * lay["L"].n * wl.r for lay in layers)
     del Gs
+    t_hbm = one_pass / (HBM_PEAK_GBPS * 1e9)
+    t_mfma = flops / (FP32_MFMA_TFLOPS * 1e12)
     return dict(us_per_step=round(ms * 1e3, 1), one_pass_GBps=round(one_pass / (ms * 1e-3) / 1e9, 1),
                 one_pass_pct_hbm=round(100 * one_pass / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-                note="G and the codes are read by both product kernels (twice)")
+                fp32_mfma_TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
+                bound="mfma" if t_mfma >= t_hbm else "hbm",
+                frac_of_bound=round(max(t_hbm, t_mfma) / (ms * 1e-3), 3))
 
 
 def main():

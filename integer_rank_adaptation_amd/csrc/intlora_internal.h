@@ -52,12 +52,12 @@ hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, cons
                               uint8_t* shift_dbg, unsigned long long* sat, hipStream_t st);
 // Straight-through backward (ste.hip): launch geometry, workspace and launcher.
 struct SteSplits {
-  int S;                   // column ranges of the dA reduction
-  int64_t cols_per_split;  // a multiple of 32
-  int S2;                  // row ranges of the dB reduction
-  int64_t rows_per_split;  // a multiple of 8
+  int S;                   // column chunks (partial sums of dA)
+  int64_t cols_per_split;  // the chunk width
+  int S2;                  // row ranges (partial sums of dB)
+  int64_t rows_per_split;  // a multiple of the row tile
 };
-SteSplits ste_splits(int64_t d, int64_t n);
+SteSplits ste_splits(int64_t d, int64_t n, int r);
 size_t ste_ws_bytes(int64_t d, int64_t n, int r);
 hipError_t launch_ste_backward(int64_t d, int64_t n, int r, int w_bits, const uint8_t* wround, const int32_t* z,
                                const float* A, const float* B, const float* G, float* dA, float* dB, void* ws,
