@@ -204,7 +204,7 @@ int intlora_merge_ptq(const intlora_desc* desc, const intlora_base* base, const 
  * U (.) w = s w + R* + AB where w = W_round - z != 0 and as the constant 0 where w = 0.
  * With G = dL/dW' (fp32 d x n) and D = G (.) [w != 0]:
  *   dA = D B^T (fp32 d x r),  dB = A^T D (fp32 r x n),
- * accumulated in binary32 on the matrix cores in an order fixed by (d, n) alone
+ * accumulated in binary32 on the matrix cores in an order fixed by (d, n, r) alone
  * (deterministic; each output within the binary32 summation bound of its exact value).
  * w_round: the base codes (uint8 d x n, or packed d x n/2 for w_bits 4), z[d]; A d x r,
  * B r x n (as for the merge).  r <= 128.  Workspace: INTLORA_OP_STE_BACKWARD (partial
