@@ -349,3 +349,19 @@ def plane_split(m):
     most 32639, else 1 (bias)."""
     m = np.asarray(m).astype(np.int32)
     return (m >= 32640).any(axis=1).astype(np.uint8)
+
+
+def merged_from_codes(ucode, wround, z, zbar):
+    """The merged integers re-formed from stored codes ([IntLoRA notes] "两种实现版本",
+    MUL: W' = s_bar (U_round - z_bar) (.) (W_round - z)): m = (U_round - z_bar) *
+    (W_round - z) per element, saturated to int16 as the merge stores it.  The codes
+    are unpacked (one code per element); z, zbar are per row."""
+    u = np.asarray(ucode).astype(np.int64) - np.asarray(zbar).astype(np.int64)[:, None]
+    w = np.asarray(wround).astype(np.int64) - np.asarray(z).astype(np.int64)[:, None]
+    return np.clip(u * w, -32768, 32767).astype(np.int16)
+
+
+def linear_from_codes(xq, sx, ucode, wround, z, zbar, sbar, want_exact=True):
+    """Merge-on-load linear layer: the integer linear layer (``linear``) on the merged
+    integers formed from U's codes and the base codes (``merged_from_codes``)."""
+    return linear(xq, sx, merged_from_codes(ucode, wround, z, zbar), sbar, want_exact)
