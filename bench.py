@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--no-ptq", action="store_true",
                    help="skip the QLoRA-style comparison (MUL workloads): the dequantize / add / requant "
                         "path timed on the same layers, and both paths' weight error")
+    p.add_argument("--no-codes", action="store_true",
+                   help="skip the merge-on-load path (MUL, 4-bit U and base codes): the merge keeping U's "
+                        "codes and the linear layer forming m from them, timed on the same layers")
     p.add_argument("--no-ste", action="store_true",
                    help="skip the straight-through backward (a synthetic dL/dW' per layer, dA and dB)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -156,6 +159,55 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
         del R
     return dict(kind="dequantize + add R* + AB (binary32) + per-row RTN requant at %d bits" % wl.w_bits,
                 ptq_merge_us_per_step=round(ptq_ms * 1e3, 1), per_layer=per)
+
+
+def codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits):
+    """Merge-on-load path on the same layers and tokens: the MUL merge storing U's 4-bit
+    codes (no int16 m) and the linear layer forming m = (U_round - z_bar)(W_round - z)
+    per tile.  Timed like the main step; its outputs are checked equal to the main
+    path's (same Y bits), layer by layer."""
+    outs = []
+    for lay in layers:
+        L = lay["L"]
+        outs.append(dict(ucode=torch.empty((L.d, L.n // 2), dtype=torch.uint8, device=dev),
+                         sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
+                         zbar=torch.empty(L.d, dtype=torch.int32, device=dev)))
+    Ys = [torch.empty_like(lay["Y"]) for lay in layers]
+
+    def step(events=None):
+        for k, lay in enumerate(layers):
+            if events is not None:
+                events[k][0].record(stream)
+            ops.merge_mul_codes(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
+                                ws=ws, out=outs[k])
+            if events is not None:
+                events[k][1].record(stream)
+            ops.linear_codes(lay["xq"], lay["sx"], outs[k]["ucode"], lay["st"]["wround"], lay["st"]["z"],
+                             outs[k]["zbar"], outs[k]["sbar"], lay["L"].d, out=Ys[k])
+            if events is not None:
+                events[k][2].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in layers] for _ in range(args.steps)]
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for s_ in range(args.steps):
+        step(ev[s_])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    per = []
+    for k, lay in enumerate(layers):
+        mm = sum(ev[s_][k][0].elapsed_time(ev[s_][k][1]) for s_ in range(args.steps)) / args.steps
+        gm = sum(ev[s_][k][1].elapsed_time(ev[s_][k][2]) for s_ in range(args.steps)) / args.steps
+        same = bool(torch.equal(Ys[k], lay["Y"]))
+        per.append(dict(layer=lay["L"].name, merge_codes_us=round(mm * 1e3, 2), gemm_codes_us=round(gm * 1e3, 2),
+                        same_Y_as_int16_path=same))
+    return dict(ms_per_step=round(ms, 4), per_layer=per,
+                weight_bytes_per_adapter="0.5 B/weight (U codes) vs 2 B/weight (int16 m)")
 
 
 def ste_measure(args, wl, layers, ops, torch, dev, stream):
@@ -337,6 +389,10 @@ def main():
     if mode == "mul" and not args.no_ptq:
         ptq = ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream)
 
+    codes = None
+    if mode == "mul" and wl.w_bits == 4 and mbits <= 4 and not args.no_codes:
+        codes = codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits)
+
     ste = None
     if not args.no_ste:
         ste = ste_measure(args, wl, layers, ops, torch, dev, stream)
@@ -397,6 +453,7 @@ def main():
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
         "ptq_comparison": ptq,
+        "merge_on_load": codes,
         "ste_backward": ste,
         "setup_s": round(setup_s, 1),
     }

@@ -169,6 +169,17 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
                       int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
                       unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
 
+/* MUL merge that keeps U's codes instead of the merged integers, for the merge-on-load
+ * linear layer (intlora_linear_fwd_codes): the same computation as intlora_merge_mul up
+ * to U_round ([IntLoRA notes] "两种实现版本", MUL), which is stored as packed nibbles
+ * (u_code d x n/2, low nibble = even column; z_bar where w = 0), with s_bar[d] and
+ * z_bar[d].  The merged integers are m = (U_round - z_bar) (W_round - z); with u_bits
+ * <= 4 and 4-bit base codes |m| <= 225.  u_bits in [2, 4]; n even.  Workspace:
+ * INTLORA_OP_MERGE_MUL.  Serving several adapters on one base stores one u_code per
+ * adapter (half a byte per weight) next to the shared base codes. */
+int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                            uint8_t* u_code, float* s_bar, int32_t* z_bar, void* ws, size_t ws_bytes, void* stream);
+
 /* IntLoRA_SHIFT merge (section "two implementation variants", SHIFT).  U as for MUL.
  * Reading: s_bar = max |U| over the row's valid elements (1 for an empty or all-zero
  * row) and V = U / s_bar, so |V| <= 1 and only right shifts occur;
@@ -242,6 +253,20 @@ int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s
 int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x, const int32_t* x_rowsum,
                        int wfmt, const void* m, const uint8_t* m_split, const float* s_bar, uint16_t* Y_bf16,
                        int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream);
+
+/* Merge-on-load integer linear layer (MUL with U's codes kept, see
+ * intlora_merge_mul_codes; [IntLoRA notes] "两种实现版本", MUL, and "training and
+ * inference efficiency"): Y is exactly intlora_linear_fwd's INT16 output for the merged
+ * integers m = (U_round - z_bar) (W_round - z), formed per tile after the weights' LDS
+ * read and never stored.  u_code, w_round: packed nibbles d x n/2 (low nibble = even
+ * column; U's codes of u_bits <= 4, 4-bit base codes); z[d], z_bar[d]: their zero
+ * points; s_bar[d].  With these widths |m| <= 225, so the balanced byte split applies
+ * (exact = 256 acc_hi + acc_lo) and no row sums are needed.  xq: M x n int8; Y_bf16: M x
+ * d; acc_dbg (optional): 2 x M x d int32 (hi then lo plane).  n a multiple of 32 and <=
+ * 131071.  No workspace. */
+int intlora_linear_fwd_codes(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x,
+                             const uint8_t* u_code, const uint8_t* w_round, const int32_t* z, const int32_t* z_bar,
+                             const float* s_bar, uint16_t* Y_bf16, int32_t* acc_dbg, void* stream);
 
 /* Diagnostic: the binary32 natural log used by intlora_gen_r, on g = G * 2^-23 for
  * odd G in [1, 2^23) (the only values it is ever given): out[t] = RN32(ln(G[t] 2^-23)).

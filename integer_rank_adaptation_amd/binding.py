@@ -58,6 +58,8 @@ _SIG = {
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "intlora_merge_mul_codes": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
+                                       _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_shift": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P,
                                    _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_ptq": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
@@ -65,6 +67,7 @@ _SIG = {
     "intlora_ste_backward": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_quant_act": (_INT, [_I64, _I64, _P, _P, _P, _P, _P]),
     "intlora_linear_fwd": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "intlora_linear_fwd_codes": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "intlora_debug_ln": (_INT, [_I64, _P, _P, _P]),
 }
 
@@ -161,6 +164,13 @@ def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_ba
                                    _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
 
 
+def intlora_merge_mul_codes(dsc: Desc, bs: Base, lr: Lora, u_bits: int, u_code, s_bar, z_bar, ws=None, stream=None):
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().intlora_merge_mul_codes(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(u_code),
+                                         _ptr(s_bar), _ptr(z_bar), _ptr(ws), wsb, _stream(stream)),
+           "intlora_merge_mul_codes")
+
+
 def intlora_merge_shift(dsc: Desc, bs: Base, lr: Lora, v_bits: int, m, s_bar, shift_dbg=None, sat_count=None, ws=None,
                         stream=None):
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
@@ -192,6 +202,13 @@ def intlora_linear_fwd(M: int, d: int, n: int, xq, s_x, x_rowsum, wfmt: int, m, 
     _check(lib().intlora_linear_fwd(M, d, n, _ptr(xq), _ptr(s_x), _ptr(x_rowsum), wfmt, _ptr(m), _ptr(m_split),
                                     _ptr(s_bar), _ptr(Y_bf16), _ptr(acc_dbg), _ptr(ws), wsb, _stream(stream)),
            "intlora_linear_fwd")
+
+
+def intlora_linear_fwd_codes(M: int, d: int, n: int, xq, s_x, u_code, w_round, z, z_bar, s_bar, Y_bf16, acc_dbg=None,
+                             stream=None):
+    _check(lib().intlora_linear_fwd_codes(M, d, n, _ptr(xq), _ptr(s_x), _ptr(u_code), _ptr(w_round), _ptr(z),
+                                          _ptr(z_bar), _ptr(s_bar), _ptr(Y_bf16), _ptr(acc_dbg), _stream(stream)),
+           "intlora_linear_fwd_codes")
 
 
 def intlora_debug_ln(count: int, G, out, stream=None):

@@ -268,8 +268,32 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
     return s;
   return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
                                                  static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
-                                                 w.umax, m, s_bar, z_bar, m_split, u_round_dbg, sat_count, st),
+                                                 w.umax, m, s_bar, z_bar, m_split, u_round_dbg, sat_count, nullptr,
+                                                 st),
                        "quant_mul");
+}
+
+int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                            uint8_t* u_code, float* s_bar, int32_t* z_bar, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (u_bits < 2 || u_bits > 4) return fail(INTLORA_EINVAL, "merge_mul_codes: u_bits must be in [2, 4] (got %d)", u_bits);
+  if (desc->n & 1) return fail(INTLORA_ESHAPE, "merge_mul_codes: packed 4-bit codes need an even n");
+  if (desc->d == 0) return ok();
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_ptrs({u_code, s_bar, z_bar}, "merge_mul_codes"))) return s;
+  if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
+  if ((s = ensure_device())) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  MergeWs w = carve(ws, desc->d, desc->n);
+  if ((s = run_adapt(desc, base, lora, w, nullptr, st))) return s;
+  if ((s = launch_status(
+           intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, nullptr, st), "row range")))
+    return s;
+  return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
+                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
+                                                 w.umax, nullptr, s_bar, z_bar, nullptr, nullptr, nullptr, u_code, st),
+                       "quant_mul codes");
 }
 
 int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int v_bits,
@@ -368,6 +392,24 @@ int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const 
   return launch_status(intlora::launch_linear(M, d, n, xq, s_x, x_rowsum, wfmt, m, m_split, s_bar, Y_bf16, acc_dbg,
                                               static_cast<hipStream_t>(stream)),
                        "linear");
+}
+
+int intlora_linear_fwd_codes(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* s_x,
+                             const uint8_t* u_code, const uint8_t* w_round, const int32_t* z, const int32_t* z_bar,
+                             const float* s_bar, uint16_t* Y_bf16, int32_t* acc_dbg, void* stream) {
+  if (M < 0 || d < 0 || n < 1 || M >= kMaxDim || d >= kMaxDim) return fail(INTLORA_ESHAPE, "bad shape");
+  if (n % 32 != 0 || n > 131071)
+    return fail(INTLORA_ESHAPE, "linear_fwd_codes needs n a multiple of 32 and <= 131071 (got %lld)", (long long)n);
+  if ((int64_t)((M + 255) / 256) * (int64_t)((d + 127) / 128) >= (int64_t(1) << 31))
+    return fail(INTLORA_ESHAPE, "too many tiles");
+  if (M == 0 || d == 0) return ok();
+  int s = check_ptrs({xq, s_x, u_code, w_round, z, z_bar, s_bar, Y_bf16}, "linear_fwd_codes");
+  if (s) return s;
+  if ((s = check_opt(acc_dbg, "acc_dbg"))) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_linear_codes(M, d, n, xq, s_x, u_code, w_round, z, z_bar, s_bar, Y_bf16,
+                                                    acc_dbg, static_cast<hipStream_t>(stream)),
+                       "linear_codes");
 }
 
 int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream) {

@@ -44,7 +44,7 @@ hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* p
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
                             const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
                             int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
-                            hipStream_t st);
+                            uint8_t* ucode, hipStream_t st);
 hipError_t launch_quant_ptq(int64_t d, int64_t n, int bits, const float* X, const float* xmin, const float* xmax,
                             uint8_t* code, float* s_out, int32_t* z_out, hipStream_t st);
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,
@@ -65,5 +65,8 @@ hipError_t launch_ste_backward(int64_t d, int64_t n, int r, int w_bits, const ui
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const uint8_t* split, const float* sbar, uint16_t* Y,
                          int32_t* acc_dbg, hipStream_t st);
+hipError_t launch_linear_codes(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx,
+                               const uint8_t* ucode, const uint8_t* wcode, const int32_t* z, const int32_t* zbar,
+                               const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st);
 
 }  // namespace intlora

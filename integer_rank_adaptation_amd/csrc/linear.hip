@@ -24,6 +24,13 @@
 //                            zeros, which lowers the matrix cores' switching power (the
 //                            chip runs at a higher clock).  Each split has its own copy
 //                            of the K loop.
+//   UW4 (MUL, merge on load) U's 4-bit codes and the 4-bit base codes (packed nibbles),
+//                            with the per-row zero points z_bar, z: m = (U_round -
+//                            z_bar) (W_round - z) is formed after the LDS read in
+//                            packed 16-bit lanes (|m| <= 225, exact) and split like
+//                            INT16 with the balanced split (always valid here).  The
+//                            merged integers never exist in memory; several adapters
+//                            share one copy of the base codes.
 //
 // Data path: every operand goes from HBM straight into LDS with buffer_load ... lds
 // (16 bytes per lane, no VGPR staging) through a 4-stage ring, so the loads of stages
@@ -59,7 +66,7 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16 };
+enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16, F_UW4 = 44 };
 
 namespace lin {
 constexpr int kThreads = 256;  // 4 waves: 2 (tokens) x 2 (MFMA columns), 128 x 128 per wave
@@ -71,17 +78,20 @@ constexpr int A_BYTES = BM * BK;                // 16 KB
 constexpr int B_BYTES_8 = 256 * BK;             // 16 KB: 256 output rows x 64 int8
 constexpr int B_BYTES_16 = 128 * BK * 2;        // 16 KB: 128 output rows x 64 int16
 constexpr int B_BYTES_4 = 256 * BK / 2;         // 8 KB: 256 output rows x 64 nibbles
+constexpr int B_BYTES_UW4 = 2 * 128 * BK / 2;   // 8 KB: U then W codes, 128 output rows x 64 nibbles each
 constexpr int EPI_RS = 64 * 2 + 16;             // epilogue staging row: 64 bf16 outputs + 16 bytes pad
 constexpr int EPI_WAVE = 32 * EPI_RS;           // one wave's 32 tokens x 64 outputs
 constexpr int EPI_VEC = 4 * EPI_WAVE;           // offset of the per-tile vectors in the epilogue region
 constexpr int EPI_BYTES = EPI_VEC + 3 * 4 * 256;
 template <int F>
 struct Cfg {
-  static constexpr int B_BYTES = F == F_INT16 ? B_BYTES_16 : (F == F_INT8 ? B_BYTES_8 : B_BYTES_4);
+  static constexpr int B_BYTES =
+      F == F_INT16 ? B_BYTES_16 : (F == F_INT8 ? B_BYTES_8 : (F == F_UW4 ? B_BYTES_UW4 : B_BYTES_4));
+  static constexpr bool TWO = F == F_INT16 || F == F_UW4;      // two byte planes of int16 values
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int RING = kStages * STAGE;
   static constexpr int LDS = RING + EPI_BYTES;
-  static constexpr int OUT = F == F_INT16 ? 128 : 256;         // outputs per block
+  static constexpr int OUT = TWO ? 128 : 256;                  // outputs per block
   static constexpr int A_LOADS = A_BYTES / 1024 / 4;           // direct loads per wave per stage
   static constexpr int B_LOADS = B_BYTES / 1024 / 4;
   static constexpr int LOADS = A_LOADS + B_LOADS;
@@ -136,6 +146,9 @@ __device__ __forceinline__ void make_plan(int n, Plan<F>& p) {
     } else if (F == F_INT16) {   // 128-byte rows (64 int16)
       const int row = 8 * g + (lane >> 3);
       p.b[q] = (uint32_t)(2 * (row * n + 8 * ((lane & 7) ^ swz128(row))));
+    } else if (F == F_UW4) {     // 32-byte rows: loads 0..3 U's 128 rows, 4..7 W's (same offsets)
+      const int row = 32 * (g & 3) + (lane >> 1);
+      p.b[q] = (uint32_t)(row * (n >> 1) + 16 * ((lane & 1) ^ swz32(row)));
     } else {                     // F_INT4: 32-byte rows (64 nibbles)
       const int row = 32 * g + (lane >> 1);
       p.b[q] = (uint32_t)(row * (n >> 1) + 16 * ((lane & 1) ^ swz32(row)));
@@ -159,16 +172,18 @@ __device__ __forceinline__ void stage_rsrc(int kt, const int8_t* a_tile, int64_t
 // Direct load number q (A loads first, then B) of one stage into the stage buffer.
 // With KTAIL (n not a multiple of BK) the A chunks past n in a partial stage read
 // zeros, which zeroes their products whatever the B bytes there are.
+// UW4: b_tile is the tile of U's codes; the base codes lie wdelta bytes after it (the
+// same layout), so one extra descriptor reaches them.
 template <int F, bool KTAIL>
 __device__ __forceinline__ void issue_load(int q, int n, int kt, const int8_t* a_tile, int64_t a_bytes,
                                            const uint8_t* b_tile, int64_t b_bytes, const Plan<F>& p,
-                                           uint8_t* stage) {
+                                           uint8_t* stage, int64_t wdelta) {
   using namespace lin;
-  __amdgpu_buffer_rsrc_t ra, rb;
-  stage_rsrc<F>(kt, a_tile, a_bytes, b_tile, b_bytes, ra, rb);
   const int k0 = kt * BK;
   const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   if (q < Cfg<F>::A_LOADS) {
+    __amdgpu_buffer_rsrc_t ra, rb;
+    stage_rsrc<F>(kt, a_tile, a_bytes, b_tile, b_bytes, ra, rb);
     const int g = wid * Cfg<F>::A_LOADS + q;
     uint32_t off = p.a[q];
     if (KTAIL) off = p.akk[q] < n - k0 ? off : kOOB;
@@ -176,6 +191,11 @@ __device__ __forceinline__ void issue_load(int q, int n, int kt, const int8_t* a
   } else {
     const int qb = q - Cfg<F>::A_LOADS;
     const int g = wid * Cfg<F>::B_LOADS + qb;
+    __amdgpu_buffer_rsrc_t ra, rb;
+    const uint8_t* bsrc = (F == F_UW4 && g >= 4)
+                              ? reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(b_tile) + (uintptr_t)wdelta)
+                              : b_tile;
+    stage_rsrc<F>(kt, a_tile, a_bytes, bsrc, b_bytes, ra, rb);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + A_BYTES + g * 1024), 16, p.b[qb], 0, 0, 0);
   }
 }
@@ -183,9 +203,10 @@ __device__ __forceinline__ void issue_load(int q, int n, int kt, const int8_t* a
 template <int F, bool KTAIL>
 __device__ __forceinline__ void issue_stage(int kt, int n, const int8_t* a_tile, int64_t a_bytes,
                                             const uint8_t* b_tile, int64_t b_bytes, const Plan<F>& p,
-                                            uint8_t* stage) {
+                                            uint8_t* stage, int64_t wdelta) {
 #pragma unroll
-  for (int q = 0; q < lin::Cfg<F>::LOADS; ++q) issue_load<F, KTAIL>(q, n, kt, a_tile, a_bytes, b_tile, b_bytes, p, stage);
+  for (int q = 0; q < lin::Cfg<F>::LOADS; ++q)
+    issue_load<F, KTAIL>(q, n, kt, a_tile, a_bytes, b_tile, b_bytes, p, stage, wdelta);
 }
 
 // vmcnt-only wait (expcnt / lgkmcnt left unconstrained), N <= 15.
@@ -233,6 +254,9 @@ __device__ __forceinline__ LdsLane lds_lane(int wm, int wn, int fr, int h) {
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
         ll.b[ks][jj] = (uint32_t)(A_BYTES + (wn * 64 + fr) * 128 + (((4 * h + 2 * ks + jj) ^ swz128(fr)) << 4));
+    } else if (F == F_UW4) {  // U's row of the lane's first output tile; W 4096 bytes on
+      ll.b[ks][0] = (uint32_t)(A_BYTES + (wn * 64 + fr) * 32 + ((h ^ swz32(fr)) << 4) + 8 * ks);
+      ll.b[ks][1] = 0;
     } else {
       ll.b[ks][0] = (uint32_t)(A_BYTES + (wn * 128 + fr) * 32 + ((h ^ swz32(fr)) << 4) + 8 * ks);
       ll.b[ks][1] = 0;
@@ -255,7 +279,9 @@ template <int F>
 __device__ __forceinline__ v4i read_b_chunk(const uint8_t* __restrict__ S, const LdsLane& ll, int ks, int j) {
   if (F == F_INT8) return *reinterpret_cast<const v4i*>(S + ll.b[ks][0] + j * 2048);
   if (F == F_INT16) return *reinterpret_cast<const v4i*>(S + ll.b[ks][j & 1] + (j >> 1) * 4096);
-  const uint2 r = *reinterpret_cast<const uint2*>(S + ll.b[ks][0] + j * 1024);
+  // INT4: tile j; UW4: chunk 2 q holds U's and 2 q + 1 W's 16 nibbles of output tile q
+  const uint32_t off = F == F_UW4 ? (uint32_t)((j >> 1) * 1024 + (j & 1) * 4096) : (uint32_t)(j * 1024);
+  const uint2 r = *reinterpret_cast<const uint2*>(S + ll.b[ks][0] + off);
   return v4i{(int)r.x, (int)r.y, 0, 0};
 }
 
@@ -284,10 +310,42 @@ __device__ __forceinline__ uint2 split16(uint32_t x0, uint32_t x1) {
                     __builtin_amdgcn_perm(x1, x0, 0x06040200u));
 }
 
-// B (weight) MFMA operands for 4 column tiles from the raw bytes.  INT16: tile q of
-// outputs gives MFMA column tiles 2q (hi plane) and 2q+1 (lo plane).
+typedef short s2v __attribute__((ext_vector_type(2)));
+
+// UW4: the four merged integers of K 4 h' .. 4 h' + 3 of one output row (h' = 2 x +
+// half within the 8-K dword pair), as two dwords of int16 pairs in K order, from the
+// dwords u, w of 8 nibbles each (byte b holds K 2b in its low nibble, 2b + 1 in its
+// high one) and the row's zero points broadcast to both 16-bit halves (zb2, zw2):
+// m = (u - z_bar) (w - z) in packed 16-bit lanes, exact since |m| <= 225.
+__device__ __forceinline__ uint2 uw4_m(uint32_t u, uint32_t w, uint32_t zb2, uint32_t zw2, int half) {
+  const uint32_t ul = u & 0x0F0F0F0Fu, uh = (u >> 4) & 0x0F0F0F0Fu;
+  const uint32_t wl = w & 0x0F0F0F0Fu, wh = (w >> 4) & 0x0F0F0F0Fu;
+  const uint32_t b0 = 2u * (uint32_t)half, b1 = b0 + 1u;
+  // output bytes: (low byte of K even, 0, low byte of K odd, 0); selector 12 gives 0
+  const uint32_t s0 = 0x0C000C00u | b0 | ((4u + b0) << 16);
+  const uint32_t s1 = 0x0C000C00u | b1 | ((4u + b1) << 16);
+  const s2v zb = __builtin_bit_cast(s2v, zb2), zw = __builtin_bit_cast(s2v, zw2);
+  const s2v u0 = __builtin_bit_cast(s2v, __builtin_amdgcn_perm(uh, ul, s0)) - zb;
+  const s2v u1 = __builtin_bit_cast(s2v, __builtin_amdgcn_perm(uh, ul, s1)) - zb;
+  const s2v w0 = __builtin_bit_cast(s2v, __builtin_amdgcn_perm(wh, wl, s0)) - zw;
+  const s2v w1 = __builtin_bit_cast(s2v, __builtin_amdgcn_perm(wh, wl, s1)) - zw;
+  return make_uint2(__builtin_bit_cast(uint32_t, u0 * w0), __builtin_bit_cast(uint32_t, u1 * w1));
+}
+
+// B (weight) MFMA operands for 4 column tiles from the raw bytes.  INT16 and UW4: tile
+// q of outputs gives MFMA column tiles 2q (hi plane) and 2q+1 (lo plane).  zp (UW4
+// only): z_bar and z of the lane's rows in output tiles 0 and 1, broadcast to both
+// 16-bit halves.
 template <int F, bool BIAS>
-__device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4]) {
+__device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf)[4], const uint32_t (&zp)[4]);
+
+template <int F, bool BIAS>
+__device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4], const uint32_t (&zp)[4]) {
+  if (F == F_UW4) {
+#pragma unroll
+    for (int p = 0; p < 8; ++p) convert_piece<F, BIAS>(p, rw, bf, zp);
+    return;
+  }
   if (F == F_INT8) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = rw.v[j];
@@ -327,9 +385,16 @@ __device__ __forceinline__ void read_piece(int q, const uint8_t* __restrict__ S,
 
 // Conversion piece p (0..7) of the raw B bytes into MFMA operands.
 template <int F, bool BIAS>
-__device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf)[4]) {
+__device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf)[4], const uint32_t (&zp)[4]) {
   if (F == F_INT8) {
     if (p < 4) bf[p] = rw.v[p];
+  } else if (F == F_UW4) {
+    const int q = p >> 2, e = p & 3;  // output tile q, K 4e .. 4e + 3 of the sub-step
+    const uint2 mm = uw4_m((uint32_t)rw.v[2 * q][e >> 1], (uint32_t)rw.v[2 * q + 1][e >> 1], zp[2 * q],
+                           zp[2 * q + 1], e & 1);
+    const uint2 hl = split16<false>(mm.x, mm.y);
+    bf[2 * q][e] = (int)hl.x;
+    bf[2 * q + 1][e] = (int)hl.y;
   } else if (F == F_INT16) {
     const int q = p >> 2, e = p & 3;  // output tile q, dword pair e
     const v4i& lo16 = rw.v[2 * q + (e >> 1)];
@@ -389,7 +454,9 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
                                                             const uint8_t* __restrict__ m,
                                                             const uint8_t* __restrict__ split,
                                                             const float* __restrict__ sbar, uint16_t* __restrict__ Y,
-                                                            int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n) {
+                                                            int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n,
+                                                            int64_t wdelta, const int32_t* __restrict__ zbar_p,
+                                                            const int32_t* __restrict__ zw_p) {
   using namespace lin;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -406,7 +473,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     if (loc < per + (x < rem ? 1 : 0)) slot = base + loc;
   }
   const int my_tiles = slot < ntile ? (ntile - slot + G - 1) / G : 0;
-  const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
+  const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);  // bytes per weight row
   const int KT = (int)((n + BK - 1) / BK);
   const int fr = lane & 31, h = lane >> 5;
   Plan<F> plan;
@@ -437,6 +504,28 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   tile_ptrs(0, a_cur, ab_cur, b_cur, bb_cur);
   tile_ptrs(1, a_nxt, ab_nxt, b_nxt, bb_nxt);
 
+  // UW4: the zero points of the lane's rows (output tiles q = 0, 1) of local tile lt,
+  // each broadcast to both 16-bit halves: zp = {z_bar q0, z q0, z_bar q1, z q1}.  The
+  // current tile's set converts its stages; the next tile's set converts that tile's
+  // first sub-step, at the end of the current tile.  The next set is loaded right
+  // after the first barrier of a tile, between two stages' direct loads, so the
+  // in-order load counter covers it without extra waits.
+  uint32_t zpc[4] = {0, 0, 0, 0}, zpn[4] = {0, 0, 0, 0};
+  auto load_zp = [&](int lt, uint32_t (&zp)[4]) {
+    if (lt < my_tiles) {
+      int tm, tn;
+      tile_coords(lt * G + slot, tiles_m, tiles_n, tm, tn);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int64_t o = (int64_t)tn * OUT + wn * 64 + 32 * q + fr;
+        const uint32_t zb = o < d ? (uint32_t)zbar_p[o] : 0u, zw = o < d ? (uint32_t)zw_p[o] : 0u;
+        zp[2 * q] = zb | (zb << 16);
+        zp[2 * q + 1] = zw | (zw << 16);
+      }
+    }
+  };
+  if (F == F_UW4) load_zp(0, zpc);
+
   // INT16 split of the launch: bias when some row's code is 1 (or there are no codes),
   // else balanced.  The codes are read before the first stages are issued and voted
   // on at the prologue's barrier.
@@ -460,9 +549,9 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
 #pragma unroll
   for (int g = 0; g < 3; ++g) {
     if (g < KT)
-      issue_stage<F, KTAIL>(g, (int)n, a_cur, ab_cur, b_cur, bb_cur, plan, lds + g * STAGE);
+      issue_stage<F, KTAIL>(g, (int)n, a_cur, ab_cur, b_cur, bb_cur, plan, lds + g * STAGE, wdelta);
     else
-      issue_stage<F, KTAIL>(g - KT, (int)n, a_nxt, ab_nxt, b_nxt, bb_nxt, plan, lds + g * STAGE);
+      issue_stage<F, KTAIL>(g - KT, (int)n, a_nxt, ab_nxt, b_nxt, bb_nxt, plan, lds + g * STAGE, wdelta);
   }
   uint8_t* epi = lds + Cfg<F>::RING;
   int* vote = reinterpret_cast<int*>(epi + EPI_VEC);  // free until the first epilogue
@@ -478,9 +567,9 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   read_a(lds, ll, 0, a0);
   read_b<F>(lds, ll, 0, rw);
   if (F == F_INT16 && bias)
-    convert_b<F, true>(rw, b0);
+    convert_b<F, true>(rw, b0, zpc);
   else
-    convert_b<F, false>(rw, b0);
+    convert_b<F, false>(rw, b0, zpc);
 
   int g = 0;  // global stage index of the stream
   for (int lt = 0; lt < my_tiles; ++lt) {
@@ -499,6 +588,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
         // is visible to all waves and nobody reads stage g-1, whose buffer g+3 reuses
         wait_vmcnt<Cfg<F>::LOADS>();
         __builtin_amdgcn_s_barrier();
+        if (F == F_UW4 && kt == 0) load_zp(lt + 1, zpn);
         // stage g+3 is stage kt+3 of this tile or stage kt+3-KT of the next one
         const bool same = kt + 3 < KT;
         const int kl = same ? kt + 3 : kt + 3 - KT;
@@ -519,19 +609,27 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
           acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b0[q & 3], a0[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
           if (q < 8) read_piece<F>(q, S0, ll, 1, a1, rw);
           if (q >= 8 && q - 8 < (Cfg<F>::LOADS + 1) / 2)
-            issue_load<F, KTAIL>(q - 8, (int)n, kl, al, abl, bl, bbl, plan, ldst);
-          if (q >= 8) convert_piece<F, BIAS>(q - 8, rw, b1);
+            issue_load<F, KTAIL>(q - 8, (int)n, kl, al, abl, bl, bbl, plan, ldst, wdelta);
+          if (q >= 8) convert_piece<F, BIAS>(q - 8, rw, b1, zpc);
           __builtin_amdgcn_sched_barrier(0);
         }
         // sub-step 1 of stage g on set 1; set 0 <- sub-step 0 of stage g+1 (the next
         // tile's first stage after the last stage of this one)
+        // (the next tile's set is read only in the last iteration, long after its loads
+        // landed: a select in every iteration would wait for them in the first)
+        uint32_t zs[4] = {zpc[0], zpc[1], zpc[2], zpc[3]};
+        if (F == F_UW4 && kt + 1 == KT) {
+          __asm__ volatile("");
+#pragma unroll
+          for (int u = 0; u < 4; ++u) zs[u] = zpn[u];
+        }
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           acc[q >> 2][q & 3] = __builtin_amdgcn_mfma_i32_32x32x32_i8(b1[q & 3], a1[q >> 2], acc[q >> 2][q & 3], 0, 0, 0);
           if (q < 8) read_piece<F>(q, S1, ll, 0, a0, rw);
           if (q >= 8 && q - 8 + (Cfg<F>::LOADS + 1) / 2 < Cfg<F>::LOADS)
-            issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kl, al, abl, bl, bbl, plan, ldst);
-          if (q >= 8) convert_piece<F, BIAS>(q - 8, rw, b0);
+            issue_load<F, KTAIL>(q - 8 + (Cfg<F>::LOADS + 1) / 2, (int)n, kl, al, abl, bl, bbl, plan, ldst, wdelta);
+          if (q >= 8) convert_piece<F, BIAS>(q - 8, rw, b0, zs);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -557,7 +655,8 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     }
     __syncthreads();
     uint8_t* stg = epi + wid * EPI_WAVE;
-    constexpr int PASSES = F == F_INT16 ? 1 : 2;  // 64 outputs of the wave per pass
+    constexpr bool TWO = Cfg<F>::TWO;
+    constexpr int PASSES = TWO ? 1 : 2;  // 64 outputs of the wave per pass
     const bool vec_ok = (d & 7) == 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -576,13 +675,13 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
           for (int a = 0; a < 4; ++a) {
             __builtin_amdgcn_sched_barrier(0);
             const int oc = 32 * jj + 8 * a + 4 * h;                       // output column in the pass
-            const int ow = (F == F_INT16 ? 0 : 64 * p) + oc;              // output column in the wave
-            const float4 sb = *reinterpret_cast<const float4*>(col_sb + (F == F_INT16 ? wn * 64 : wn * 128) + ow);
+            const int ow = (TWO ? 0 : 64 * p) + oc;                       // output column in the wave
+            const float4 sb = *reinterpret_cast<const float4*>(col_sb + (TWO ? wn * 64 : wn * 128) + ow);
             const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
             float y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              if (F == F_INT16) {
+              if (TWO) {
                 const int hi = acc_read(acc[i][2 * jj][4 * a + e]), lo = acc_read(acc[i][2 * jj + 1][4 * a + e]);
                 // exact = 256 acc_hi + acc_lo (+ 128 rowsum for the bias split), exact in
                 // binary64 (|exact| < 2^53)
@@ -598,12 +697,12 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
             *reinterpret_cast<uint2*>(stg + fr * EPI_RS + 2 * oc) = make_uint2(p01, p23);
             if (acc_dbg) {
               const int64_t tok = t0 + tl;
-              const int64_t c = o0 + (F == F_INT16 ? wn * 64 : wn * 128) + ow;
+              const int64_t c = o0 + (TWO ? wn * 64 : wn * 128) + ow;
               if (tok < M) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                   if (c + e >= d) continue;
-                  if (F == F_INT16) {
+                  if (TWO) {
                     acc_dbg[tok * d + c + e] = acc_read(acc[i][2 * jj][4 * a + e]);
                     acc_dbg[M * d + tok * d + c + e] = acc_read(acc[i][2 * jj + 1][4 * a + e]);
                   } else {
@@ -622,7 +721,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
           const int row = s4 * 8 + (lane >> 3);
           const int col8 = 8 * (lane & 7);
           const int64_t tok = t0 + wm * 128 + i * 32 + row;
-          const int64_t c = o0 + (F == F_INT16 ? wn * 64 : wn * 128 + 64 * p) + col8;
+          const int64_t c = o0 + (TWO ? wn * 64 : wn * 128 + 64 * p) + col8;
           const uint4 v = *reinterpret_cast<const uint4*>(stg + row * EPI_RS + 2 * col8);
           if (tok < M && c < d) {
             uint16_t* Yp = Y + tok * d + c;
@@ -644,6 +743,10 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     ab_cur = ab_nxt;
     bb_cur = bb_nxt;
     tile_ptrs(lt + 2, a_nxt, ab_nxt, b_nxt, bb_nxt);
+    if (F == F_UW4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) zpc[u] = zpn[u];
+    }
   }
   wait_vmcnt<0>();  // trailing (zero-reading) loads land before the block's LDS is released
 }
@@ -659,53 +762,72 @@ static int device_cus() {
   return cus;
 }
 
+static hipError_t set_linear_attrs() {
+  using namespace lin;
+  static bool attr_set = false;
+  if (attr_set) return hipSuccess;
+  const void* fns[8] = {reinterpret_cast<const void*>(&k_linear<F_INT8, false>),
+                        reinterpret_cast<const void*>(&k_linear<F_INT8, true>),
+                        reinterpret_cast<const void*>(&k_linear<F_INT4, false>),
+                        reinterpret_cast<const void*>(&k_linear<F_INT4, true>),
+                        reinterpret_cast<const void*>(&k_linear<F_INT16, false>),
+                        reinterpret_cast<const void*>(&k_linear<F_INT16, true>),
+                        reinterpret_cast<const void*>(&k_linear<F_UW4, false>),
+                        reinterpret_cast<const void*>(&k_linear<F_UW4, true>)};
+  const int lds_of[8] = {Cfg<F_INT8>::LDS, Cfg<F_INT8>::LDS, Cfg<F_INT4>::LDS, Cfg<F_INT4>::LDS,
+                         Cfg<F_INT16>::LDS, Cfg<F_INT16>::LDS, Cfg<F_UW4>::LDS, Cfg<F_UW4>::LDS};
+  for (int k = 0; k < 8; ++k) {
+    const hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, lds_of[k]);
+    if (e != hipSuccess) return e;
+  }
+  attr_set = true;
+  return hipSuccess;
+}
+
+// One block per compute unit, each streaming several tiles; with fewer than three K
+// stages per tile the stream cannot span tiles, so every block takes one tile.
+template <int FMT>
+static hipError_t launch_fmt(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx,
+                             const int32_t* rowsum, const uint8_t* mb, const uint8_t* split, const float* sbar,
+                             uint16_t* Y, int32_t* acc_dbg, int64_t wdelta, const int32_t* zbar,
+                             const int32_t* zw, hipStream_t st) {
+  using namespace lin;
+  const hipError_t e = set_linear_attrs();
+  if (e != hipSuccess) return e;
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int tiles_n = (int)((d + Cfg<FMT>::OUT - 1) / Cfg<FMT>::OUT);
+  const int ntile = tiles_m * tiles_n;
+  const int KT = (int)((n + BK - 1) / BK);
+  const int cus = device_cus();
+  const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
+  if ((n % BK) != 0)
+    hipLaunchKernelGGL((k_linear<FMT, true>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx, rowsum, mb,
+                       split, sbar, Y, acc_dbg, tiles_m, tiles_n, wdelta, zbar, zw);
+  else
+    hipLaunchKernelGGL((k_linear<FMT, false>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx, rowsum, mb,
+                       split, sbar, Y, acc_dbg, tiles_m, tiles_n, wdelta, zbar, zw);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const uint8_t* split, const float* sbar, uint16_t* Y,
                          int32_t* acc_dbg, hipStream_t st) {
-  using namespace lin;
-  const int out_per_block = (wfmt == F_INT16) ? Cfg<F_INT16>::OUT : Cfg<F_INT8>::OUT;
-  const int tiles_m = (int)((M + BM - 1) / BM);
-  const int tiles_n = (int)((d + out_per_block - 1) / out_per_block);
-  const int ntile = tiles_m * tiles_n;
-  const int KT = (int)((n + BK - 1) / BK);
-  // one block per compute unit, each streaming several tiles; with fewer than three K
-  // stages per tile the stream cannot span tiles, so every block takes one tile
-  const int cus = device_cus();
-  const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
   const uint8_t* mb = static_cast<const uint8_t*>(m);
-  static bool attr_set = false;
-  if (!attr_set) {
-    const void* fns[6] = {reinterpret_cast<const void*>(&k_linear<F_INT8, false>),
-                          reinterpret_cast<const void*>(&k_linear<F_INT8, true>),
-                          reinterpret_cast<const void*>(&k_linear<F_INT4, false>),
-                          reinterpret_cast<const void*>(&k_linear<F_INT4, true>),
-                          reinterpret_cast<const void*>(&k_linear<F_INT16, false>),
-                          reinterpret_cast<const void*>(&k_linear<F_INT16, true>)};
-    const int lds_of[6] = {Cfg<F_INT8>::LDS, Cfg<F_INT8>::LDS, Cfg<F_INT4>::LDS,
-                           Cfg<F_INT4>::LDS, Cfg<F_INT16>::LDS, Cfg<F_INT16>::LDS};
-    for (int k = 0; k < 6; ++k) {
-      const hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, lds_of[k]);
-      if (e != hipSuccess) return e;
-    }
-    attr_set = true;
-  }
-  const bool tail = (n % BK) != 0;
-#define INTLORA_LAUNCH_LINEAR(FMT)                                                                              \
-  do {                                                                                                        \
-    if (tail)                                                                                                 \
-      hipLaunchKernelGGL((k_linear<FMT, true>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx,      \
-                         rowsum, mb, split, sbar, Y, acc_dbg, tiles_m, tiles_n);                              \
-    else                                                                                                      \
-      hipLaunchKernelGGL((k_linear<FMT, false>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx,     \
-                         rowsum, mb, split, sbar, Y, acc_dbg, tiles_m, tiles_n);                              \
-  } while (0)
   switch (wfmt) {
-    case F_INT8: INTLORA_LAUNCH_LINEAR(F_INT8); break;
-    case F_INT4: INTLORA_LAUNCH_LINEAR(F_INT4); break;
-    default: INTLORA_LAUNCH_LINEAR(F_INT16); break;
+    case F_INT8:
+      return launch_fmt<F_INT8>(M, d, n, xq, sx, rowsum, mb, split, sbar, Y, acc_dbg, 0, nullptr, nullptr, st);
+    case F_INT4:
+      return launch_fmt<F_INT4>(M, d, n, xq, sx, rowsum, mb, split, sbar, Y, acc_dbg, 0, nullptr, nullptr, st);
+    default:
+      return launch_fmt<F_INT16>(M, d, n, xq, sx, rowsum, mb, split, sbar, Y, acc_dbg, 0, nullptr, nullptr, st);
   }
-#undef INTLORA_LAUNCH_LINEAR
-  return hipGetLastError();
+}
+
+hipError_t launch_linear_codes(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx,
+                               const uint8_t* ucode, const uint8_t* wcode, const int32_t* z, const int32_t* zbar,
+                               const float* sbar, uint16_t* Y, int32_t* acc_dbg, hipStream_t st) {
+  const int64_t wdelta = (int64_t)(reinterpret_cast<uintptr_t>(wcode) - reinterpret_cast<uintptr_t>(ucode));
+  return launch_fmt<F_UW4>(M, d, n, xq, sx, nullptr, ucode, nullptr, sbar, Y, acc_dbg, wdelta, zbar, z, st);
 }
 
 }  // namespace intlora

@@ -582,7 +582,10 @@ __device__ __forceinline__ int code_at(const uint8_t* __restrict__ wround, int64
   return wround[i * n + j];
 }
 
-template <bool W4>
+// CODES: instead of m (and the split codes), store U_round itself as packed nibbles
+// (u_bits <= 4, n even; low nibble = even column), for a linear layer that forms m on
+// load.
+template <bool W4, bool CODES>
 __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, int u_bits,
                                                         const uint8_t* __restrict__ wround,
                                                         const int32_t* __restrict__ z, const float* __restrict__ U,
@@ -590,7 +593,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
                                                         const float* __restrict__ umax_r, int16_t* __restrict__ m,
                                                         float* __restrict__ sbar_out, int32_t* __restrict__ zbar_out,
                                                         uint8_t* __restrict__ split, uint8_t* __restrict__ uround_dbg,
-                                                        unsigned long long* __restrict__ sat) {
+                                                        unsigned long long* __restrict__ sat,
+                                                        uint8_t* __restrict__ ucode) {
   const int qmax = (1 << u_bits) - 1;
   const int64_t j0 = (int64_t)blockIdx.x * kQCols + (int64_t)threadIdx.x * kQElems;
   const int64_t ngroups = (d + kQRows - 1) / kQRows;
@@ -639,6 +643,13 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           for (int e = 0; e < 8; ++e)
             if (redo[e]) ur[e] = mul_code(uu[e], P.sbar, P.zbar, qmax);
         }
+        if (CODES) {
+          uint32_t pk = 0;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) pk |= (uint32_t)ur[e] << (4 * e);
+          store_once4(ucode + ((i * n + j0) >> 1), pk);
+          continue;
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           int mv = w[e] != 0 ? (ur[e] - P.zbar) * w[e] : 0;
@@ -676,11 +687,19 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           zbar_out[i] = P.zbar;
         }
         const int zi = z[i];
+        int lo_code = 0;
         for (int e = 0; e < kQElems; ++e) {
           const int64_t j = j0 + e;
           if (j >= n) break;
           int uv;
           const int mv = mul_merge(code_at<W4>(wround, i, n, j) - zi, U[i * n + j], P, qmax, uv, nsat);
+          if (CODES) {  // n is even: the odd column of every pair exists
+            if ((j & 1) == 0)
+              lo_code = uv;
+            else
+              ucode[(i * n + j) >> 1] = (uint8_t)(lo_code | (uv << 4));
+            continue;
+          }
           m[i * n + j] = (int16_t)mv;
           if (split && mv >= kSplitBiasMin) split[i] = 1;
           if (uround_dbg) uround_dbg[i * n + j] = (uint8_t)uv;
@@ -1056,14 +1075,23 @@ static dim3 quant_grid(int64_t d, int64_t n) {
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
                             const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
                             int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
-                            hipStream_t st) {
+                            uint8_t* ucode, hipStream_t st) {
   const dim3 grid = quant_grid(d, n);
-  if (w_bits == 4)
-    hipLaunchKernelGGL(k_quant_mul<true>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
-                       sbar, zbar, split, uround_dbg, sat);
-  else
-    hipLaunchKernelGGL(k_quant_mul<false>, grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, umax, m,
-                       sbar, zbar, split, uround_dbg, sat);
+#define INTLORA_QMUL(W4, CODES)                                                                                  \
+  hipLaunchKernelGGL((k_quant_mul<W4, CODES>), grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, \
+                     umax, m, sbar, zbar, split, uround_dbg, sat, ucode)
+  if (ucode) {
+    if (w_bits == 4)
+      INTLORA_QMUL(true, true);
+    else
+      INTLORA_QMUL(false, true);
+  } else {
+    if (w_bits == 4)
+      INTLORA_QMUL(true, false);
+    else
+      INTLORA_QMUL(false, false);
+  }
+#undef INTLORA_QMUL
   return hipGetLastError();
 }
 

@@ -88,6 +88,22 @@ def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out
     return o
 
 
+def merge_mul_codes(st, A, Bm, w_bits, u_bits, seed, layer_id, ws=None, out=None):
+    """MUL merge keeping U's codes (packed nibbles d x n/2) with s_bar, z_bar, for the
+    merge-on-load linear layer."""
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    ws = workspace(B.INTLORA_OP_MERGE_MUL, d, n, r, w_bits, dev) if ws is None else ws
+    o = out or dict(ucode=torch.empty((d, n // 2), dtype=torch.uint8, device=dev),
+                    sbar=torch.empty(d, dtype=torch.float32, device=dev),
+                    zbar=torch.empty(d, dtype=torch.int32, device=dev))
+    B.intlora_merge_mul_codes(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), u_bits, o["ucode"],
+                              o["sbar"], o["zbar"], ws=ws)
+    return o
+
+
 def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, out=None):
     d, r = A.shape
     n = Bm.shape[1]
@@ -151,4 +167,14 @@ def linear(xq, sx, rowsum, wfmt, m, sbar, d, acc_dbg=False, out=None, split=None
     planes = 2 if wfmt == B.INTLORA_W_INT16 else 1
     acc = torch.empty((planes, M, d), dtype=torch.int32, device=xq.device) if acc_dbg else None
     B.intlora_linear_fwd(M, d, n, xq, sx, rowsum, wfmt, m, split, sbar, Y, acc)
+    return Y, acc
+
+
+def linear_codes(xq, sx, ucode, wcode, z, zbar, sbar, d, acc_dbg=False, out=None):
+    """Merge-on-load linear layer: m = (U_round - z_bar) (W_round - z) formed in the GEMM
+    from the packed 4-bit codes (d x n/2 each)."""
+    M, n = xq.shape
+    Y = torch.empty((M, d), dtype=torch.int16, device=xq.device) if out is None else out
+    acc = torch.empty((2, M, d), dtype=torch.int32, device=xq.device) if acc_dbg else None
+    B.intlora_linear_fwd_codes(M, d, n, xq, sx, ucode, wcode, z, zbar, sbar, Y, acc)
     return Y, acc

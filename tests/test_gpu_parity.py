@@ -161,6 +161,24 @@ def test_merge_mul_bitexact(ops, d, n, r, w_bits):
         assert int(host(g["sat"])[0]) == ref["sat"]
 
 
+@pytest.mark.parametrize("d,n,r,w_bits", [c for c in MERGE_CASES if c[1] % 2 == 0])
+def test_merge_mul_codes_bitexact(ops, d, n, r, w_bits):
+    """MUL merge keeping U's codes (packed nibbles, for the merge-on-load linear layer):
+    U_round, s_bar and z_bar bit for bit, on both quantize paths (n % 8 != 0 too)."""
+    seed = 150 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    if d > 0:
+        wr[0, : min(n, 6)] = z[0]  # some w == 0: the stored code is z_bar there
+    st = gpu_state(wr, z, s, c, w_bits)
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+    for u_bits in (2, 3, 4):
+        g = ops.merge_mul_codes(st, cuda(A), cuda(Bm), w_bits, u_bits, 77, 5)
+        ref = oracle.merge_mul(wr, z, s, R, A, Bm, u_bits)
+        assert np.array_equal(unpack4(host(g["ucode"])), ref["uround"]), u_bits
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert np.array_equal(host(g["zbar"]), ref["zbar"])
+
+
 @pytest.mark.parametrize("d,n,r,w_bits", MERGE_CASES)
 def test_merge_shift_bitexact(ops, d, n, r, w_bits):
     seed = 200 + d + n + r
@@ -444,6 +462,76 @@ def test_linear_many_tiles(ops, M, d, n, wfmt, capped):
     assert np.array_equal(got, exact)
     assert np.array_equal(host(Y).view(np.uint16), yref)
     assert np.array_equal(host(Y2).view(np.uint16), yref)
+
+
+def _codes_case(rng, d, n, zero_rows=True):
+    """4-bit U and base codes with their per-row zero points (some rows where every
+    code equals its zero point, and extremes 0 / 15 in both)."""
+    u = rng.integers(0, 16, size=(d, n)).astype(np.uint8)
+    w = rng.integers(0, 16, size=(d, n)).astype(np.uint8)
+    zb = rng.integers(0, 16, size=d).astype(np.int32)
+    zw = rng.integers(0, 16, size=d).astype(np.int32)
+    zb[0], zw[0] = 0, 15
+    if d > 2:
+        zb[1], zw[1] = 15, 0
+        u[1, :] = 0
+        w[1, :] = 15       # m = (0 - 15)(15 - 0) = -225 across the row
+    if zero_rows and d > 3:
+        w[2, :] = zw[2]    # w == 0 everywhere in row 2
+    return u, w, zb, zw
+
+
+@pytest.mark.parametrize("M,d,n", [(1, 1, 32), (37, 100, 96), (300, 260, 512), (257, 129, 320), (64, 520, 1280)])
+def test_linear_codes_bitexact(ops, M, d, n):
+    """Merge-on-load linear layer: outputs and both accumulator planes bit for bit
+    against the oracle (m formed from the codes, balanced split)."""
+    rng = np.random.Generator(np.random.PCG64(M * 5 + d + n))
+    u, w, zb, zw = _codes_case(rng, d, n)
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(M + 3, M, 1e-3, 0.1)
+    sbar = synth.random_positive(d + 4, d, 1e-5, 1e-2)
+    Y, acc = ops.linear_codes(cuda(xq), cuda(sx), cuda(pack4(u)), cuda(pack4(w)), cuda(zw), cuda(zb), cuda(sbar), d,
+                              acc_dbg=True)
+    m = oracle.merged_from_codes(u, w, zw, zb)
+    exact, _, yref = oracle.linear_from_codes(xq, sx, u, w, zw, zb, sbar)
+    hi, lo = oracle.byte_planes(m, split=np.zeros(d, np.uint8))
+    acc = host(acc).astype(np.int64)
+    assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
+    assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
+    assert np.array_equal(256 * acc[0] + acc[1], exact)
+    assert np.array_equal(host(Y).view(np.uint16), yref)
+
+
+@pytest.mark.parametrize("M,d,n", [(2600, 4000, 224), (5000, 2000, 320), (4100, 9000, 96)])
+def test_linear_codes_many_tiles(ops, M, d, n):
+    """More tiles than compute units: each block streams several tiles' stages, and the
+    zero points of the next tile are taken for its first sub-step; ragged M, d and a
+    partial last K stage (224, 96), two K stages per tile (96: one tile per block)."""
+    rng = np.random.Generator(np.random.PCG64(M + d + n))
+    u, w, zb, zw = _codes_case(rng, d, n)
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(M + 5, M, 1e-3, 0.1)
+    sbar = synth.random_positive(d + 6, d, 1e-5, 1e-2)
+    Y, _ = ops.linear_codes(cuda(xq), cuda(sx), cuda(pack4(u)), cuda(pack4(w)), cuda(zw), cuda(zb), cuda(sbar), d)
+    exact, _, yref = oracle.linear_from_codes(xq, sx, u, w, zw, zb, sbar)
+    assert np.array_equal(host(Y).view(np.uint16), yref)
+
+
+def test_merge_on_load_matches_materialized(ops):
+    """End to end on one layer: merge keeping U's codes + merge-on-load linear layer
+    gives the same outputs as the MUL merge + INT16 linear layer."""
+    d, n, r, M = 300, 1024, 16, 513
+    wr, z, s, c, A, Bm = random_state(4242, d, n, r, 4)
+    st = gpu_state(wr, z, s, c, 4)
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), 4, 4, 9, 2)
+    gc = ops.merge_mul_codes(st, cuda(A), cuda(Bm), 4, 4, 9, 2)
+    assert np.array_equal(host(gc["zbar"]), host(g["zbar"]))
+    rng = np.random.Generator(np.random.PCG64(7))
+    X = rng.normal(0.0, 1.0, (M, n)).astype(np.float32)
+    xq, sx, rs = ops.quant_act(cuda(X))
+    Y1, _ = ops.linear(xq, sx, rs, 16, g["m"], g["sbar"], d, split=g["split"])
+    Y2, _ = ops.linear_codes(xq, sx, gc["ucode"], st["wround"], st["z"], gc["zbar"], gc["sbar"], d)
+    assert np.array_equal(host(Y1).view(np.uint16), host(Y2).view(np.uint16))
 
 
 # ----------------------------------------------------------------------------- workloads
