@@ -164,3 +164,42 @@ def test_ste_backward_full_size(ops, wl_index, li):
     assert np.all(np.abs(host(g["dA"]).astype(np.float64) - rA) <= boundA)
     assert np.all(np.abs(host(g["dB"]).astype(np.float64) - rB) <= boundB)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("li", [0, 3])
+def test_merge_on_load_full_size(ops, li):
+    """FLUX qkv (9216 x 3072) and mlp_out (3072 x 12288) at full size, 4608 tokens: the
+    merge keeping U's codes stores exactly the MUL merge's U_round, and the merge-on-load
+    linear layer gives the INT16 path's outputs bit for bit; sampled outputs against the
+    oracle on m formed from the codes."""
+    wl = synth.WORKLOADS[3]
+    L = wl.layers[li]
+    M = wl.tokens[0]
+    lid = synth.layer_id(wl.index, li)
+    seed = synth.PHILOX_SEED
+    W = synth.weight(wl, li)
+    A, Bm = synth.lora(wl, li)
+    st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+    _, ubits = wl.modes[0]
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, ubits, seed, lid, dbg=True)
+    gc = ops.merge_mul_codes(st, cuda(A), cuda(Bm), wl.w_bits, ubits, seed, lid)
+    ucode = unpack4(host(gc["ucode"]))
+    assert np.array_equal(ucode, host(g["uround"]))
+    assert np.array_equal(host(gc["zbar"]), host(g["zbar"]))
+    assert np.array_equal(bits(host(gc["sbar"])), bits(host(g["sbar"])))
+    X = synth.activations(wl, L.n, M, li)
+    xq, sx, rs = ops.quant_act(cuda(X))
+    Y1, _ = ops.linear(xq, sx, rs, 16, g["m"], g["sbar"], L.d, split=g["split"])
+    Y2, _ = ops.linear_codes(xq, sx, gc["ucode"], st["wround"], st["z"], gc["zbar"], gc["sbar"], L.d)
+    Y2h = host(Y2).view(np.uint16)
+    assert np.array_equal(host(Y1).view(np.uint16), Y2h)
+    rng = np.random.Generator(np.random.PCG64(31 + li))
+    ts = rng.integers(0, M, 64)
+    is_ = rng.integers(0, L.d, 64)
+    m = oracle.merged_from_codes(ucode[is_], unpack4(host(st["wround"]))[is_], host(st["z"])[is_],
+                                 host(gc["zbar"])[is_])
+    mfull = np.zeros((L.d, L.n), np.int16)
+    mfull[is_] = m
+    _, y = oracle.linear_sampled(ts, is_, host(xq), host(sx), mfull, host(gc["sbar"]))
+    assert np.array_equal(Y2h[ts, is_], y)
+    torch.cuda.empty_cache()
