@@ -52,6 +52,9 @@ def parse():
     p.add_argument("--no-ptq", action="store_true",
                    help="skip the QLoRA-style comparison (MUL workloads): the dequantize / add / requant "
                         "path timed on the same layers, and both paths' weight error")
+    p.add_argument("--no-fused", action="store_true",
+                   help="skip the fused single-pass MUL merge (U kept on chip, no workspace), timed on the same "
+                        "layers against the three-kernel merge")
     p.add_argument("--no-codes", action="store_true",
                    help="skip the merge-on-load path (MUL, 4-bit U and base codes): the merge keeping U's "
                         "codes and the linear layer forming m from them, timed on the same layers")
@@ -159,6 +162,38 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
         del R
     return dict(kind="dequantize + add R* + AB (binary32) + per-row RTN requant at %d bits" % wl.w_bits,
                 ptq_merge_us_per_step=round(ptq_ms * 1e3, 1), per_layer=per)
+
+
+def fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits):
+    """Fused single-pass MUL merge on the same layers (no workspace: U stays on chip),
+    timed like the main step's merges; its merged integers are checked equal to the main
+    path's, layer by layer."""
+    outs = [None] * len(layers)
+
+    def run(events=None):
+        for k, lay in enumerate(layers):
+            if events is not None:
+                events[k][0].record(stream)
+            outs[k] = ops.merge_mul_fused(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
+                                          lay["lid"], out=outs[k])
+            if events is not None:
+                events[k][1].record(stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in layers] for _ in range(args.steps)]
+    for s_ in range(args.steps):
+        run(ev[s_])
+    torch.cuda.synchronize()
+    per = []
+    tot = 0.0
+    for k, lay in enumerate(layers):
+        us = sum(ev[s_][k][0].elapsed_time(ev[s_][k][1]) for s_ in range(args.steps)) / args.steps * 1e3
+        tot += us
+        per.append(dict(layer=lay["L"].name, fused_merge_us=round(us, 2),
+                        same_m_as_three_kernel_merge=bool(torch.equal(outs[k]["m"], lay["out"]["m"]))))
+    return dict(us_per_step=round(tot, 1), per_layer=per)
 
 
 def codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits):
@@ -389,6 +424,10 @@ def main():
     if mode == "mul" and not args.no_ptq:
         ptq = ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream)
 
+    fused = None
+    if mode == "mul" and max(lay["L"].n for lay in layers) <= 16384 and not args.no_fused:
+        fused = fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits)
+
     codes = None
     if mode == "mul" and wl.w_bits == 4 and mbits <= 4 and not args.no_codes:
         codes = codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits)
@@ -453,6 +492,7 @@ def main():
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
         "ptq_comparison": ptq,
+        "merge_fused": fused,
         "merge_on_load": codes,
         "ste_backward": ste,
         "setup_s": round(setup_s, 1),

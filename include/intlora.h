@@ -169,6 +169,16 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
                       int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
                       unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
 
+/* Fused single-pass MUL merge with no scratch memory: the same outputs, bit for bit, as
+ * intlora_merge_mul ([IntLoRA notes] "1. AQS", "2. MLA", "两种实现版本" MUL), computed
+ * by one kernel in which a block keeps whole rows of U on chip, so U is never written
+ * to memory and no workspace is taken.  The rank-r term runs on the vector ALU (the
+ * same fma chain as the definition).  n <= 16384 (INTLORA_ESHAPE otherwise); other
+ * arguments as intlora_merge_mul. */
+int intlora_merge_mul_fused(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                            int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
+                            unsigned long long* sat_count, void* stream);
+
 /* MUL merge that keeps U's codes instead of the merged integers, for the merge-on-load
  * linear layer (intlora_linear_fwd_codes): the same computation as intlora_merge_mul up
  * to U_round ([IntLoRA notes] "两种实现版本", MUL), which is stored as packed nibbles

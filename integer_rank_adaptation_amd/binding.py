@@ -58,6 +58,8 @@ _SIG = {
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "intlora_merge_mul_fused": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
+                                       _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul_codes": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_shift": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P,
@@ -162,6 +164,13 @@ def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_ba
     _check(lib().intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(m),
                                    _ptr(s_bar), _ptr(z_bar), _ptr(m_split), _ptr(u_round_dbg), _ptr(sat_count),
                                    _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
+
+
+def intlora_merge_mul_fused(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None,
+                            u_round_dbg=None, sat_count=None, stream=None):
+    _check(lib().intlora_merge_mul_fused(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(m),
+                                         _ptr(s_bar), _ptr(z_bar), _ptr(m_split), _ptr(u_round_dbg),
+                                         _ptr(sat_count), _stream(stream)), "intlora_merge_mul_fused")
 
 
 def intlora_merge_mul_codes(dsc: Desc, bs: Base, lr: Lora, u_bits: int, u_code, s_bar, z_bar, ws=None, stream=None):

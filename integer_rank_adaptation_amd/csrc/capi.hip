@@ -273,6 +273,45 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
                        "quant_mul");
 }
 
+int intlora_merge_mul_fused(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                            int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
+                            unsigned long long* sat_count, void* stream) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (u_bits < 2 || u_bits > 8) return fail(INTLORA_EINVAL, "u_bits must be in [2, 8] (got %d)", u_bits);
+  if (desc->n > 16384)
+    return fail(INTLORA_ESHAPE, "merge_mul_fused keeps whole rows on chip: n <= 16384 (got %lld)",
+                (long long)desc->n);
+  if (desc->d == 0) return ok();
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_ptrs({m, s_bar, z_bar}, "merge_mul_fused"))) return s;
+  if ((s = check_opt(m_split, "m_split")) || (s = check_opt(u_round_dbg, "u_round_dbg")) ||
+      (s = check_opt(sat_count, "sat_count")))
+    return s;
+  if ((s = ensure_device())) return s;
+  intlora::AdaptArgs a;
+  a.d = desc->d;
+  a.n = desc->n;
+  a.r = desc->r;
+  a.w_bits = desc->w_bits;
+  a.seed = desc->seed;
+  a.layer_id = desc->layer_id;
+  a.wround = static_cast<const uint8_t*>(base->w_round);
+  a.z = base->z;
+  a.s = base->s;
+  a.c = base->vmc_c;
+  a.A = lora->A;
+  a.B = lora->B;
+  a.U = nullptr;
+  a.pmin = a.pmax = nullptr;
+  a.sat_zero = nullptr;
+  a.ptq = false;
+  a.force_generic = false;
+  return launch_status(intlora::launch_merge_fused(a, u_bits, m, s_bar, z_bar, m_split, u_round_dbg, sat_count,
+                                                   static_cast<hipStream_t>(stream)),
+                       "merge_mul_fused");
+}
+
 int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
                             uint8_t* u_code, float* s_bar, int32_t* z_bar, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(desc, true);

@@ -25,6 +25,10 @@ struct AdaptArgs {
   bool force_generic;
 };
 
+// Fused single-pass MUL merge (no scratch); hipErrorInvalidValue for n > 16384.
+hipError_t launch_merge_fused(const AdaptArgs& a, int u_bits, int16_t* m, float* sbar, int32_t* zbar,
+                              uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st);
+
 // Upper bound of the number of column tiles of the adaptation kernel (sizes the
 // workspace of row partials).
 int adapt_max_ntiles(int64_t n);

@@ -1067,6 +1067,224 @@ hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* p
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------
+// Fused single-pass MUL merge with no scratch memory.  A block owns RB = 16 / NG whole
+// rows (8 for NG = 1; n <= 1024 NG) and keeps their U in LDS (RB x 1024 NG floats, at
+// most 64 KB), so each
+// row's range is complete (block reduction) before any of its elements is quantized
+// and U never leaves the chip.  Thread t computes columns 4 (t + 256 g) .. + 3 of
+// every row of the block (and quantizes the same ones).  The rank-r term is the fmaf
+// chain of the definition on the vector ALU: B[k][4 columns] is read once (from L2)
+// per column group and k and serves all RB rows.  Every other step is the one of the
+// adaptation and quantize kernels, in the same order, so the outputs are the same bits.
+// ---------------------------------------------------------------------------------
+template <int NG>
+struct FusedLds {
+  static constexpr int RB = NG == 1 ? 8 : 16 / NG;  // rows per block
+  static constexpr int COLS = 1024 * NG;
+  static constexpr int BYTES = RB * COLS * 4;
+};
+
+template <int NG, bool W4>
+__global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r, int u_bits, uint64_t seed,
+                                                    uint32_t layer_id, const uint8_t* __restrict__ wround,
+                                                    const int32_t* __restrict__ z, const float* __restrict__ s,
+                                                    const float* __restrict__ c, const float* __restrict__ A,
+                                                    const float* __restrict__ B, int16_t* __restrict__ m,
+                                                    float* __restrict__ sbar_out, int32_t* __restrict__ zbar_out,
+                                                    uint8_t* __restrict__ split, uint8_t* __restrict__ uround_dbg,
+                                                    unsigned long long* __restrict__ sat) {
+  constexpr int RB = FusedLds<NG>::RB;
+  constexpr int COLS = FusedLds<NG>::COLS;
+  extern __shared__ __attribute__((aligned(16))) float sU[];  // RB x COLS
+  __shared__ LnLds tab[96];
+  __shared__ float rcp[511];
+  __shared__ float sA[RB * 128];
+  __shared__ int smin[4][RB], smax[4][RB];
+  __shared__ int sflag[RB];
+  load_ln_table(tab);
+  load_rcp_table(rcp);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int qmax = (1 << u_bits) - 1;
+  const bool quad = (n & 3) == 0;
+  int nsat = 0;
+  for (int64_t i0 = (int64_t)blockIdx.x * RB; i0 < d; i0 += (int64_t)gridDim.x * RB) {
+    __syncthreads();  // tables in place; the previous rows' LDS reads are done
+    for (int x = tid; x < RB * r; x += 256) {
+      const int rr = x / r, k = x - rr * r;
+      sA[rr * r + k] = i0 + rr < d ? A[(i0 + rr) * r + k] : 0.0f;
+    }
+    if (tid < RB) sflag[tid] = 0;
+    __syncthreads();
+    int kmin[RB], kmax[RB];
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      kmin[rr] = kKeyPosInf;
+      kmax[rr] = kKeyNegInf;
+    }
+    for (int g = 0; g < NG; ++g) {
+      const int64_t j0 = 4 * ((int64_t)tid + 256 * g);
+      if (j0 >= n) break;
+      float acc[RB][4];
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[rr][e] = 0.0f;
+      for (int k = 0; k < r; ++k) {
+        float b[4];
+        if (quad) {
+          const float4 b4 = *reinterpret_cast<const float4*>(B + (int64_t)k * n + j0);
+          b[0] = b4.x;
+          b[1] = b4.y;
+          b[2] = b4.z;
+          b[3] = b4.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b[e] = j0 + e < n ? B[(int64_t)k * n + j0 + e] : 0.0f;
+        }
+#pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          const float a = sA[rr * r + k];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(a, b[e], acc[rr][e]);
+        }
+      }
+#pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const bool row_ok = i0 + rr < d;
+        const int64_t i = row_ok ? i0 + rr : d - 1;  // a row past d is computed, never stored
+        const int zi = z[i];
+        const float ci = c[i], si = s[i];
+        int w[4];
+        float rs[4];
+        if (quad) {
+          const uint32_t cv = W4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(wround + ((i * n + j0) >> 1))
+                                 : *reinterpret_cast<const uint32_t*>(wround + i * n + j0);
+          const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)j0) >> 2, layer_id, seed);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zi;
+            rs[e] = ci * laplace_from_word(pick_word(rnd, e), tab);
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t j = j0 + e < n ? j0 + e : n - 1;
+            w[e] = code_at<W4>(wround, i, n, j) - zi;
+            rs[e] = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab);
+          }
+        }
+        float t[4], q[4];
+        bool slow = false;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          t[e] = rs[e] + acc[rr][e];
+          q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+          slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+        }
+        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+          __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float uu = si + q[e];
+          sU[rr * COLS + j0 + e] = uu;
+          if (row_ok && w[e] != 0 && j0 + e < n) {
+            const int key = f32_key(uu);
+            kmin[rr] = min(kmin[rr], key);
+            kmax[rr] = max(kmax[rr], key);
+          }
+        }
+      }
+    }
+    // each row's range over the block (order keys)
+#pragma unroll
+    for (int rr = 0; rr < RB; ++rr) {
+      const int a = wave_min_i32(kmin[rr]), b = wave_max_i32(kmax[rr]);
+      if (lane == 0) {
+        smin[wid][rr] = a;
+        smax[wid][rr] = b;
+      }
+    }
+    __syncthreads();
+    for (int rr = 0; rr < RB; ++rr) {
+      if (i0 + rr >= d) break;
+      const int64_t i = i0 + rr;
+      const int a = min(min(smin[0][rr], smin[1][rr]), min(smin[2][rr], smin[3][rr]));
+      const int b = max(max(smax[0][rr], smax[1][rr]), max(smax[2][rr], smax[3][rr]));
+      const MulParams P = mul_params(key_f32(a), key_f32(b), qmax);
+      if (tid == 0) {
+        sbar_out[i] = P.sbar;
+        zbar_out[i] = P.zbar;
+      }
+      const int zi = z[i];
+      for (int g = 0; g < NG; ++g) {
+        const int64_t j0 = 4 * ((int64_t)tid + 256 * g);
+        if (j0 >= n) break;
+        int w[4], ur[4], mm[4];
+        float uu[4];
+        bool redo[4], any = false;
+        if (quad) {
+          const uint32_t cv = W4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(wround + ((i * n + j0) >> 1))
+                                 : *reinterpret_cast<const uint32_t*>(wround + i * n + j0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zi;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = (j0 + e < n ? code_at<W4>(wround, i, n, j0 + e) : zi) - zi;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uu[e] = sU[rr * COLS + j0 + e];
+          bool exact = true;
+          ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, qmax, exact) : P.zbar;
+          redo[e] = !exact;
+          any = any || redo[e];
+        }
+        if (__builtin_amdgcn_ballot_w64(any) != 0) {
+          __asm__ volatile("");
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (redo[e]) ur[e] = mul_code(uu[e], P.sbar, P.zbar, qmax);
+        }
+        int mx = -32768;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          int mv = w[e] != 0 ? (ur[e] - P.zbar) * w[e] : 0;
+          if (j0 + e < n) {
+            if (mv > 32767) { mv = 32767; ++nsat; }
+            if (mv < -32768) { mv = -32768; ++nsat; }
+            mx = max(mx, mv);
+          }
+          mm[e] = mv;
+        }
+        if (quad) {
+          store_once8(m + i * n + j0, make_uint2((uint32_t)(mm[0] & 0xFFFF) | ((uint32_t)mm[1] << 16),
+                                                 (uint32_t)(mm[2] & 0xFFFF) | ((uint32_t)mm[3] << 16)));
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < n) m[i * n + j0 + e] = (int16_t)mm[e];
+        }
+        if (mx >= kSplitBiasMin) sflag[rr] = 1;
+        if (uround_dbg) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (j0 + e < n) uround_dbg[i * n + j0 + e] = (uint8_t)ur[e];
+        }
+      }
+    }
+    __syncthreads();
+    if (split && tid < RB && i0 + tid < d) split[i0 + tid] = (uint8_t)sflag[tid];
+  }
+  add_saturations(sat, nsat);
+}
+
+__global__ void k_zero_u64(unsigned long long* p) { *p = 0ull; }
+
 static dim3 quant_grid(int64_t d, int64_t n) {
   const int64_t groups = (d + kQRows - 1) / kQRows;
   return dim3((unsigned)((n + kQCols - 1) / kQCols), (unsigned)(groups < 65535 ? (groups ? groups : 1) : 65535));
@@ -1116,6 +1334,45 @@ hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, cons
   else
     hipLaunchKernelGGL(k_quant_shift<false>, grid, dim3(kQThreads), 0, st, d, n, v_bits, wround, z, U, umin, umax, m,
                        sbar, shift_dbg, sat);
+  return hipGetLastError();
+}
+
+// Fused MUL merge: NG = columns / 1024 rounded up to a power of two (n <= 16384).
+hipError_t launch_merge_fused(const AdaptArgs& a, int u_bits, int16_t* m, float* sbar, int32_t* zbar,
+                              uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st) {
+  int ng = 1;
+  while (ng < 16 && (int64_t)ng * 1024 < a.n) ng *= 2;
+  if ((int64_t)ng * 1024 < a.n) return hipErrorInvalidValue;
+  const int rb = ng == 1 ? 8 : 16 / ng;
+  const int64_t groups = (a.d + rb - 1) / rb;
+  const dim3 grid((unsigned)(groups < 8192 ? (groups > 0 ? groups : 1) : 8192));
+  if (sat) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, sat);
+#define INTLORA_FUSED(NG, W4)                                                                                   \
+  do {                                                                                                          \
+    static bool attr = false;                                                                                   \
+    if (!attr) {                                                                                                \
+      const hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge_fused<NG, W4>),           \
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, FusedLds<NG>::BYTES); \
+      if (e_ != hipSuccess) return e_;                                                                          \
+      attr = true;                                                                                              \
+    }                                                                                                           \
+    hipLaunchKernelGGL((k_merge_fused<NG, W4>), grid, dim3(256), FusedLds<NG>::BYTES, st, a.d, a.n, a.r, u_bits, \
+                       a.seed, a.layer_id, a.wround, a.z, a.s, a.c, a.A, a.B, m, sbar, zbar, split, uround_dbg, sat); \
+  } while (0)
+#define INTLORA_FUSED_W(NG) \
+  if (a.w_bits == 4)        \
+    INTLORA_FUSED(NG, true); \
+  else                      \
+    INTLORA_FUSED(NG, false)
+  switch (ng) {
+    case 1: INTLORA_FUSED_W(1); break;
+    case 2: INTLORA_FUSED_W(2); break;
+    case 4: INTLORA_FUSED_W(4); break;
+    case 8: INTLORA_FUSED_W(8); break;
+    default: INTLORA_FUSED_W(16); break;
+  }
+#undef INTLORA_FUSED_W
+#undef INTLORA_FUSED
   return hipGetLastError();
 }
 

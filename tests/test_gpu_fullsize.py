@@ -203,3 +203,25 @@ def test_merge_on_load_full_size(ops, li):
     _, y = oracle.linear_sampled(ts, is_, host(xq), host(sx), mfull, host(gc["sbar"]))
     assert np.array_equal(Y2h[ts, is_], y)
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("wl_index,li", [(3, 1), (3, 3), (4, 0), (1, 4)])
+def test_merge_fused_full_size(ops, wl_index, li):
+    """The fused single-pass MUL merge at full layer size equals the three-kernel merge
+    (adaptation, row range, quantize) bit for bit on every output (FLUX out and mlp_out,
+    Llama q, SD feed-forward)."""
+    wl = synth.WORKLOADS[wl_index]
+    L = wl.layers[li]
+    lid = synth.layer_id(wl.index, li)
+    seed = synth.PHILOX_SEED
+    W = synth.weight(wl, li)
+    A, Bm = synth.lora(wl, li)
+    st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+    ubits = [b for mode, b in wl.modes if mode == "mul"][0]
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, ubits, seed, lid, dbg=True)
+    f = ops.merge_mul_fused(st, cuda(A), cuda(Bm), wl.w_bits, ubits, seed, lid, dbg=True)
+    for k in ("m", "uround", "zbar", "split"):
+        assert torch.equal(g[k], f[k]), k
+    assert np.array_equal(bits(host(g["sbar"])), bits(host(f["sbar"])))
+    assert int(host(g["sat"])[0]) == int(host(f["sat"])[0])
+    torch.cuda.empty_cache()

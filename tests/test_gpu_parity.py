@@ -161,6 +161,28 @@ def test_merge_mul_bitexact(ops, d, n, r, w_bits):
         assert int(host(g["sat"])[0]) == ref["sat"]
 
 
+@pytest.mark.parametrize("d,n,r,w_bits", MERGE_CASES + [(50, 5000, 32, 4), (7, 12288, 16, 8), (19, 16384, 3, 4)])
+def test_merge_mul_fused_bitexact(ops, d, n, r, w_bits):
+    """Fused single-pass MUL merge (U kept on chip): m, U_round, s_bar, z_bar, split
+    codes and the saturation count bit for bit against the oracle, over every row-block
+    width (n up to 16384) and the element path (n % 4 != 0)."""
+    seed = 170 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    if d > 0:
+        wr[0, : min(n, 6)] = z[0]
+    st = gpu_state(wr, z, s, c, w_bits)
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+    for u_bits in sorted({2, w_bits, 8}):
+        g = ops.merge_mul_fused(st, cuda(A), cuda(Bm), w_bits, u_bits, 77, 5, dbg=True)
+        ref = oracle.merge_mul(wr, z, s, R, A, Bm, u_bits)
+        assert np.array_equal(host(g["m"]), ref["m"]), u_bits
+        assert np.array_equal(host(g["uround"]), ref["uround"])
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert np.array_equal(host(g["zbar"]), ref["zbar"])
+        assert np.array_equal(host(g["split"]), oracle.plane_split(ref["m"]))
+        assert int(host(g["sat"])[0]) == ref["sat"]
+
+
 @pytest.mark.parametrize("d,n,r,w_bits", [c for c in MERGE_CASES if c[1] % 2 == 0])
 def test_merge_mul_codes_bitexact(ops, d, n, r, w_bits):
     """MUL merge keeping U's codes (packed nibbles, for the merge-on-load linear layer):
