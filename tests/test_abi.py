@@ -166,3 +166,46 @@ def test_binding_raises_with_message(lib):
         B._check(lib.intlora_vmc_scale(8, FAKE, -1.0, FAKE, None), "intlora_vmc_scale")
     assert ei.value.status == B.INTLORA_EINVAL
     assert "alpha" in str(ei.value)
+
+
+def test_merge_mul_codes_validation(lib):
+    mc = lib.intlora_merge_mul_codes
+    base, lora = B.Base(FAKE, FAKE, FAKE, FAKE), B.Lora(FAKE, FAKE)
+    dsc = B.desc(8, 8, 4, 4)
+    assert mc(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 5, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_EINVAL  # packed codes need u_bits <= 4
+    assert mc(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 1, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_EINVAL
+    odd = B.desc(8, 7, 4, 8)
+    assert mc(ctypes.byref(odd), ctypes.byref(base), ctypes.byref(lora), 4, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_ESHAPE
+    assert mc(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 4, 0, FAKE, FAKE, FAKE, 1 << 40,
+              None) == B.INTLORA_EINVAL  # NULL codes
+    assert mc(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 4, FAKE, FAKE, FAKE, FAKE, 16,
+              None) == B.INTLORA_EWORKSPACE
+
+
+def test_merge_mul_fused_validation(lib):
+    mf = lib.intlora_merge_mul_fused
+    base, lora = B.Base(FAKE, FAKE, FAKE, FAKE), B.Lora(FAKE, FAKE)
+    wide = B.desc(8, 16386, 4, 8)
+    assert mf(ctypes.byref(wide), ctypes.byref(base), ctypes.byref(lora), 8, FAKE, FAKE, FAKE, None, None, None,
+              None) == B.INTLORA_ESHAPE  # whole rows on chip: n <= 16384
+    dsc = B.desc(8, 8, 4, 8)
+    assert mf(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 9, FAKE, FAKE, FAKE, None, None, None,
+              None) == B.INTLORA_EINVAL
+    assert mf(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), 8, FAKE + 8, FAKE, FAKE, None, None, None,
+              None) == B.INTLORA_EALIGN
+    assert mf(ctypes.byref(dsc), ctypes.byref(B.Base(FAKE, FAKE, 0, FAKE)), ctypes.byref(lora), 8, FAKE, FAKE, FAKE,
+              None, None, None, None) == B.INTLORA_EINVAL
+
+
+def test_linear_fwd_codes_validation(lib):
+    lc = lib.intlora_linear_fwd_codes
+    assert lc(4, 4, 48, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.INTLORA_ESHAPE  # n % 32
+    assert lc(4, 4, 131104, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.INTLORA_ESHAPE
+    assert lc(-1, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.INTLORA_ESHAPE
+    assert lc(4, 4, 64, FAKE, FAKE, FAKE, 0, FAKE, FAKE, FAKE, FAKE, None, None) == B.INTLORA_EINVAL  # NULL base codes
+    assert lc(4, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 4, FAKE, FAKE, None, None) == B.INTLORA_EALIGN
+    assert lc(4, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE + 2, None) == B.INTLORA_EALIGN
+    assert lc(0, 4, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == B.INTLORA_OK  # no tokens
