@@ -160,8 +160,13 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
         per.append(dict(layer=L.name, rel_err_intlora=float(torch.linalg.norm(intlora - target) / tn),
                         rel_err_ptq=float(torch.linalg.norm(ptqw - target) / tn), rows=int(rows.numel())))
         del R
+    code_b = 0.5 if wl.w_bits == 4 else 1.0
+    alg = sum(lay["L"].d * lay["L"].n * 2 * code_b for lay in layers)  # base codes in, new codes out
     return dict(kind="dequantize + add R* + AB (binary32) + per-row RTN requant at %d bits" % wl.w_bits,
-                ptq_merge_us_per_step=round(ptq_ms * 1e3, 1), per_layer=per)
+                ptq_merge_us_per_step=round(ptq_ms * 1e3, 1),
+                alg_GBps=round(alg / (ptq_ms * 1e-3) / 1e9, 1),
+                pct_hbm_peak=round(100 * alg / (ptq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                bound="alu (the adaptation kernel's Philox, ln and rank-r work)", per_layer=per)
 
 
 def fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits):
@@ -193,7 +198,11 @@ def fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits):
         tot += us
         per.append(dict(layer=lay["L"].name, fused_merge_us=round(us, 2),
                         same_m_as_three_kernel_merge=bool(torch.equal(outs[k]["m"], lay["out"]["m"]))))
-    return dict(us_per_step=round(tot, 1), per_layer=per)
+    code_b = 0.5 if wl.w_bits == 4 else 1.0
+    alg = sum(lay["L"].d * lay["L"].n * (code_b + 2.0) for lay in layers)  # base codes in, int16 m out
+    return dict(us_per_step=round(tot, 1), alg_GBps=round(alg / (tot * 1e-6) / 1e9, 1),
+                pct_hbm_peak=round(100 * alg / (tot * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                bound="L2 and alu (B re-read per row block; rank-r chain on the vector ALU)", per_layer=per)
 
 
 def codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits):
@@ -241,8 +250,16 @@ def codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits):
         same = bool(torch.equal(Ys[k], lay["Y"]))
         per.append(dict(layer=lay["L"].name, merge_codes_us=round(mm * 1e3, 2), gemm_codes_us=round(gm * 1e3, 2),
                         same_Y_as_int16_path=same))
-    return dict(ms_per_step=round(ms, 4), per_layer=per,
-                weight_bytes_per_adapter="0.5 B/weight (U codes) vs 2 B/weight (int16 m)")
+    merge_us = sum(p["merge_codes_us"] for p in per)
+    gemm_us = sum(p["gemm_codes_us"] for p in per)
+    alg = sum(lay["L"].d * lay["L"].n * 1.0 for lay in layers)  # 4-bit base codes in, 4-bit U codes out
+    ops_exec = sum(2.0 * 2 * lay["xq"].shape[0] * lay["L"].d * lay["L"].n for lay in layers)  # two int8 planes
+    return dict(ms_per_step=round(ms, 4), merge_codes_us_per_step=round(merge_us, 1),
+                merge_codes_alg_GBps=round(alg / (merge_us * 1e-6) / 1e9, 1),
+                gemm_codes_us_per_step=round(gemm_us, 1),
+                gemm_codes_exec_TOPS=round(ops_exec / (gemm_us * 1e-6) / 1e12, 1),
+                gemm_codes_pct_int8_peak=round(100 * ops_exec / (gemm_us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 2),
+                per_layer=per, weight_bytes_per_adapter="0.5 B/weight (U codes) vs 2 B/weight (int16 m)")
 
 
 def ste_measure(args, wl, layers, ops, torch, dev, stream):
@@ -548,7 +565,55 @@ def cpu_baseline(wl, layers, M, mode, mbits, roof_ms, frac):
             "cores": threads, "kind": "oracle",
             "sample": "every layer: merge of the first %.4g of rows, linear on the first %.4g of tokens; "
                       "scaled to a full step (%.1f s per full step)" % (frac, frac, t_total),
-            "step_s": round(t_total, 2)}
+            "step_s": round(t_total, 2),
+            "next_rows_s_per_step": cpu_next_rows(wl, layers, M, mode, mbits, t_total)}
+
+
+def cpu_next_rows(wl, layers, M, mode, mbits, merge_linear_s, frac=0.02):
+    """The oracle of each path beyond the main step, untuned, on the first `frac` of each
+    layer's rows (tokens for the linear layer), scaled to a full step: the QLoRA-style
+    comparison path (f4), the straight-through backward (f3, binary64), the merge-on-load
+    linear layer (f2: merged integers formed from codes + the linear layer).  The fused
+    merge (f1) has the same oracle as the MUL merge."""
+    import oracle
+    from oracle import algebra
+    from integer_rank_adaptation_amd import synth
+
+    out = {"f1_fused_merge": "same oracle as the MUL merge (part of step_s)"}
+    t_ptq = t_ste = t_codes = 0.0
+    for lay in layers:
+        L = lay["L"]
+        ost = oracle.setup_layer(lay["W"], synth.PHILOX_SEED, lay["lid"], wl.w_bits, synth.ALPHA)
+        rows = max(1, int(round(L.d * frac)))
+        R = oracle.gen_r_rows(0, rows, L.n, synth.PHILOX_SEED, lay["lid"], ost["c"][:rows])
+        t0 = time.perf_counter()
+        oracle.ptq_merge(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows], lay["B"],
+                         wl.w_bits)
+        t_ptq += (time.perf_counter() - t0) * (L.d / rows)
+        G = synth.random_matrix(900 + lay["li"], (rows, L.n), 1e-3)
+        t0 = time.perf_counter()
+        algebra.ste_backward(ost["wround"][:rows], ost["z"][:rows], lay["A"][:rows], lay["B"], G)
+        t_ste += (time.perf_counter() - t0) * (L.d / rows)
+        if mode == "mul" and wl.w_bits == 4 and mbits <= 4:
+            ref = oracle.merge_mul(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows],
+                                   lay["B"], mbits)
+            toks = max(1, int(round(M * frac)))
+            xq, sx, _ = oracle.quant_act(lay["X"][:toks])
+            ur = np.resize(ref["uround"], (L.d, L.n))
+            zb = np.resize(ref["zbar"], L.d)
+            sb = np.resize(ref["sbar"], L.d)
+            t0 = time.perf_counter()
+            m = oracle.merged_from_codes(ur, ost["wround"], ost["z"], zb)
+            t1 = time.perf_counter()
+            oracle.linear(xq, sx, m, sb, want_exact=False)
+            t2 = time.perf_counter()
+            t_codes += (t1 - t0) + (t2 - t1) * (M / toks)
+    out["f4_ptq_merge"] = round(t_ptq, 3)
+    out["f3_ste_backward"] = round(t_ste, 3)
+    if t_codes > 0.0:
+        out["f2_merge_on_load_linear"] = round(t_codes, 3)
+    out["sample"] = "first %.3g of each layer's rows (and tokens), scaled to a full step" % frac
+    return out
 
 
 if __name__ == "__main__":
