@@ -751,6 +751,181 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   wait_vmcnt<0>();  // trailing (zero-reading) loads land before the block's LDS is released
 }
 
+// ---------------------------------------------------------------------------------
+// Few-token linear layer (M <= 16 TT tokens: decode), bound by streaming the weights.
+// A block owns 16 output rows and its 4 waves split K into quarters.  Each 64-deep K
+// step is one v_mfma_i32_16x16x64_i8 per plane and token tile, with the weights as the
+// A operand (lane l: row l % 16, K 16 (l / 16) .. + 15 of the step) and 16 tokens as B
+// (lane l: token l % 16, same K); lane l, register v of the result hold output row
+// 4 (l / 16) + v and token l % 16.  Formats as in the tiled kernel: INT16 through the
+// same byte split (one split per launch, voted from the split codes), INT4 through the
+// same 16 w unpack.  Loads run four steps ahead from clamped (always valid) addresses;
+// K chunks past n, and the steps that pad a wave's quarter to a multiple of four, are
+// zeroed on the token side.  The four waves' int32 sums are added
+// through LDS (exact) and the epilogue is the tiled kernel's.
+// ---------------------------------------------------------------------------------
+namespace sk {
+constexpr int kAhead = 4;  // K steps in flight per wave
+}
+
+template <int F, int TT>
+__global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int64_t n, const int8_t* __restrict__ xq,
+                                                      const float* __restrict__ sx,
+                                                      const int32_t* __restrict__ rowsum,
+                                                      const uint8_t* __restrict__ m,
+                                                      const uint8_t* __restrict__ split,
+                                                      const float* __restrict__ sbar, uint16_t* __restrict__ Y,
+                                                      int32_t* __restrict__ acc_dbg) {
+  constexpr int PL = F == F_INT16 ? 2 : 1;  // byte planes
+  __shared__ int red[4][PL * TT][4][64];
+  __shared__ int vote;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int64_t i0 = (int64_t)blockIdx.x * 16;
+  const int rl = lane & 15, kg = lane >> 4;
+  const int64_t wr = i0 + rl < d ? i0 + rl : d - 1;  // rows past d: loaded, never stored
+  const int64_t KT = (n + 63) / 64;
+  const int64_t per = (KT + 3) / 4;
+  const int64_t s0 = (int64_t)wid * per;
+  const int64_t s1 = s0 + per < KT ? s0 + per : KT;
+  const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
+
+  struct Step {
+    v4i w[2];
+    v4i x[TT];
+  };
+  // loads of step st (clamped into [0, KT) and the matrices; the caller never uses a
+  // step outside [s0, s1))
+  auto load = [&](int64_t st, Step& S) {
+    st = st < KT ? st : KT - 1;
+    int64_t k = st * 64 + 16 * kg;
+    k = k < n ? k : n - 16;  // n is a multiple of 32: chunks are whole
+    if (F == F_INT16) {
+      const v4i* pw = reinterpret_cast<const v4i*>(m + wr * wrow + 2 * k);
+      S.w[0] = pw[0];
+      S.w[1] = pw[1];
+    } else if (F == F_INT8) {
+      S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + k);
+      S.w[1] = v4i{0, 0, 0, 0};
+    } else {
+      const uint2 q = *reinterpret_cast<const uint2*>(m + wr * wrow + (k >> 1));
+      S.w[0] = v4i{(int)q.x, (int)q.y, 0, 0};
+      S.w[1] = v4i{0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const int64_t t = 16 * tt + rl < M ? 16 * tt + rl : M - 1;  // tokens past M: never stored
+      S.x[tt] = *reinterpret_cast<const v4i*>(xq + t * n + k);
+    }
+  };
+
+  bool bias = false;
+  if (F == F_INT16) {
+    if (tid == 0) vote = split == nullptr ? 1 : 0;
+    __syncthreads();
+    int fl = 0;
+    if (split) {
+      for (int64_t x = 16 * (int64_t)tid; x < d; x += 16 * 256) {
+        if (x + 16 <= d) {
+          const uint4 v = *reinterpret_cast<const uint4*>(split + x);
+          fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
+        } else {
+          for (int64_t k = x; k < d; ++k) fl |= (int)(split[k] != 0);
+        }
+      }
+    }
+    if (fl) vote = 1;  // every writer stores 1
+    __syncthreads();
+    bias = vote != 0;
+  }
+  v4i acc[PL][TT];
+#pragma unroll
+  for (int p = 0; p < PL; ++p)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) acc[p][tt] = v4i{0, 0, 0, 0};
+
+  auto compute = [&](int64_t st, const Step& S, auto bias_tag) {
+    constexpr bool BIAS = decltype(bias_tag)::value;
+    const bool kin = st < s1 && st * 64 + 16 * kg < n;  // padded steps past the quarter add zeros
+    v4i a[PL];
+    if (F == F_INT16) {
+      const uint32_t x[8] = {(uint32_t)S.w[0].x, (uint32_t)S.w[0].y, (uint32_t)S.w[0].z, (uint32_t)S.w[0].w,
+                             (uint32_t)S.w[1].x, (uint32_t)S.w[1].y, (uint32_t)S.w[1].z, (uint32_t)S.w[1].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 hl = split16<BIAS>(x[2 * e], x[2 * e + 1]);
+        a[0][e] = (int)hl.x;
+        a[PL - 1][e] = (int)hl.y;
+      }
+    } else if (F == F_INT8) {
+      a[0] = S.w[0];
+    } else {
+      uint32_t o0, o1, o2, o3;
+      unpack4((uint32_t)S.w[0].x, o0, o1);
+      unpack4((uint32_t)S.w[0].y, o2, o3);
+      a[0] = v4i{(int)o0, (int)o1, (int)o2, (int)o3};
+    }
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt) {
+      const v4i xv = kin ? S.x[tt] : v4i{0, 0, 0, 0};
+#pragma unroll
+      for (int p = 0; p < PL; ++p) acc[p][tt] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[p], xv, acc[p][tt], 0, 0, 0);
+    }
+  };
+
+  // a ring of kAhead steps: each step's buffer is refilled with the step kAhead later
+  // as soon as it has been used (no branch in the body, so the loads stay in flight)
+  auto k_loop = [&](auto bias_tag) {
+    Step buf[sk::kAhead];
+#pragma unroll
+    for (int q = 0; q < sk::kAhead; ++q) load(s0 + q, buf[q]);
+    for (int64_t st = s0; st < s1; st += sk::kAhead) {
+#pragma unroll
+      for (int q = 0; q < sk::kAhead; ++q) {
+        compute(st + q, buf[q], bias_tag);
+        load(st + q + sk::kAhead, buf[q]);
+      }
+    }
+  };
+  if (F == F_INT16 && bias)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
+
+  // the four K quarters, added in LDS (exact)
+#pragma unroll
+  for (int p = 0; p < PL; ++p)
+#pragma unroll
+    for (int tt = 0; tt < TT; ++tt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[wid][p * TT + tt][v][lane] = acc[p][tt][v];
+  __syncthreads();
+  for (int x = tid; x < TT * 4 * 64; x += 256) {
+    const int tt = x / 256, v = (x / 64) & 3, l = x & 63;
+    const int64_t row = i0 + 4 * (l >> 4) + v;
+    const int64_t t = 16 * tt + (l & 15);
+    if (row >= d || t >= M) continue;
+    int pv[PL];
+#pragma unroll
+    for (int p = 0; p < PL; ++p)
+      pv[p] = red[0][p * TT + tt][v][l] + red[1][p * TT + tt][v][l] + red[2][p * TT + tt][v][l] +
+              red[3][p * TT + tt][v][l];
+    float y;
+    if (F == F_INT16) {
+      const double rs128 = bias ? 128.0 * (double)rowsum[t] : 0.0;
+      const double ex = fma(256.0, (double)pv[0], (double)pv[PL - 1]) + rs128;
+      y = ((float)ex * sx[t]) * sbar[row];
+    } else {
+      y = ((float)(F == F_INT4 ? (pv[0] >> 4) : pv[0]) * sx[t]) * sbar[row];
+    }
+    const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y, y}, bf2));
+    Y[t * d + row] = (uint16_t)(b2 & 0xFFFFu);
+    if (acc_dbg) {
+#pragma unroll
+      for (int p = 0; p < PL; ++p) acc_dbg[(int64_t)p * M * d + t * d + row] = F == F_INT4 ? (pv[p] >> 4) : pv[p];
+    }
+  }
+}
+
 static int device_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -794,6 +969,16 @@ static hipError_t launch_fmt(int64_t M, int64_t d, int64_t n, const int8_t* xq, 
   using namespace lin;
   const hipError_t e = set_linear_attrs();
   if (e != hipSuccess) return e;
+  if (FMT != F_UW4 && M <= 32) {  // few tokens: weight streaming
+    const dim3 g((unsigned)((d + 15) / 16));
+    if (M <= 16)
+      hipLaunchKernelGGL((k_linear_skinny<FMT == F_UW4 ? F_INT16 : FMT, 1>), g, dim3(256), 0, st, M, d, n, xq, sx,
+                         rowsum, mb, split, sbar, Y, acc_dbg);
+    else
+      hipLaunchKernelGGL((k_linear_skinny<FMT == F_UW4 ? F_INT16 : FMT, 2>), g, dim3(256), 0, st, M, d, n, xq, sx,
+                         rowsum, mb, split, sbar, Y, acc_dbg);
+    return hipGetLastError();
+  }
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int tiles_n = (int)((d + Cfg<FMT>::OUT - 1) / Cfg<FMT>::OUT);
   const int ntile = tiles_m * tiles_n;

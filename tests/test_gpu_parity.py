@@ -439,6 +439,16 @@ def test_linear_bitexact(ops, wfmt, M, d, n):
     _linear_case(ops, M, d, n, wfmt, seed=M * 7 + d * 3 + n + wfmt)
 
 
+@pytest.mark.parametrize("wfmt", [8, 4, 16])
+@pytest.mark.parametrize("M,d,n", [(1, 7, 32), (5, 100, 96), (16, 300, 4128), (17, 129, 320), (32, 1000, 1024),
+                                   (3, 2, 14336)])
+def test_linear_few_tokens_bitexact(ops, wfmt, M, d, n):
+    """Few tokens (M <= 32: the weight-streaming kernel, K split over four waves): every
+    output and accumulator plane against the oracle, with every split choice for INT16,
+    ragged rows, K a multiple of 32 but not of 64, K quarters of unequal length."""
+    _linear_case(ops, M, d, n, wfmt, seed=M * 11 + d + n + wfmt)
+
+
 @pytest.mark.parametrize("M,d,n,wfmt,capped", [
     (2600, 4000, 224, 16, True),    # 352 tiles: blocks own 1 or 2 tiles; partial last K stage; ragged M and d
     (2600, 4000, 224, 16, False),   # the same with the bias split
