@@ -775,8 +775,10 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
                                                       const uint8_t* __restrict__ m,
                                                       const uint8_t* __restrict__ split,
                                                       const float* __restrict__ sbar, uint16_t* __restrict__ Y,
-                                                      int32_t* __restrict__ acc_dbg) {
-  constexpr int PL = F == F_INT16 ? 2 : 1;  // byte planes
+                                                      int32_t* __restrict__ acc_dbg, int64_t wdelta,
+                                                      const int32_t* __restrict__ zbar_p,
+                                                      const int32_t* __restrict__ zw_p) {
+  constexpr int PL = (F == F_INT16 || F == F_UW4) ? 2 : 1;  // byte planes
   __shared__ int red[4][PL * TT][4][64];
   __shared__ int vote;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -788,6 +790,13 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
   const int64_t s0 = (int64_t)wid * per;
   const int64_t s1 = s0 + per < KT ? s0 + per : KT;
   const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
+  // UW4: the base codes lie wdelta bytes after U's; the lane's row zero points are fixed
+  uint32_t zb2 = 0, zw2 = 0;
+  if (F == F_UW4) {
+    const uint32_t zb = (uint32_t)zbar_p[wr], zw = (uint32_t)zw_p[wr];
+    zb2 = zb | (zb << 16);
+    zw2 = zw | (zw << 16);
+  }
 
   struct Step {
     v4i w[2];
@@ -806,6 +815,12 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
     } else if (F == F_INT8) {
       S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + k);
       S.w[1] = v4i{0, 0, 0, 0};
+    } else if (F == F_UW4) {
+      const uint2 qu = *reinterpret_cast<const uint2*>(m + wr * wrow + (k >> 1));
+      const uint2 qw = *reinterpret_cast<const uint2*>(
+          reinterpret_cast<const uint8_t*>(reinterpret_cast<uintptr_t>(m) + (uintptr_t)wdelta) + wr * wrow + (k >> 1));
+      S.w[0] = v4i{(int)qu.x, (int)qu.y, 0, 0};
+      S.w[1] = v4i{(int)qw.x, (int)qw.y, 0, 0};
     } else {
       const uint2 q = *reinterpret_cast<const uint2*>(m + wr * wrow + (k >> 1));
       S.w[0] = v4i{(int)q.x, (int)q.y, 0, 0};
@@ -853,6 +868,14 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const uint2 hl = split16<BIAS>(x[2 * e], x[2 * e + 1]);
+        a[0][e] = (int)hl.x;
+        a[PL - 1][e] = (int)hl.y;
+      }
+    } else if (F == F_UW4) {  // m = (u - z_bar)(w - z), balanced split (|m| <= 225)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint2 mm = uw4_m((uint32_t)S.w[0][e >> 1], (uint32_t)S.w[1][e >> 1], zb2, zw2, e & 1);
+        const uint2 hl = split16<false>(mm.x, mm.y);
         a[0][e] = (int)hl.x;
         a[PL - 1][e] = (int)hl.y;
       }
@@ -910,7 +933,7 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
       pv[p] = red[0][p * TT + tt][v][l] + red[1][p * TT + tt][v][l] + red[2][p * TT + tt][v][l] +
               red[3][p * TT + tt][v][l];
     float y;
-    if (F == F_INT16) {
+    if (F == F_INT16 || F == F_UW4) {
       const double rs128 = bias ? 128.0 * (double)rowsum[t] : 0.0;
       const double ex = fma(256.0, (double)pv[0], (double)pv[PL - 1]) + rs128;
       y = ((float)ex * sx[t]) * sbar[row];
@@ -969,14 +992,14 @@ static hipError_t launch_fmt(int64_t M, int64_t d, int64_t n, const int8_t* xq, 
   using namespace lin;
   const hipError_t e = set_linear_attrs();
   if (e != hipSuccess) return e;
-  if (FMT != F_UW4 && M <= 32) {  // few tokens: weight streaming
+  if (M <= 32) {  // few tokens: weight streaming
     const dim3 g((unsigned)((d + 15) / 16));
     if (M <= 16)
-      hipLaunchKernelGGL((k_linear_skinny<FMT == F_UW4 ? F_INT16 : FMT, 1>), g, dim3(256), 0, st, M, d, n, xq, sx,
-                         rowsum, mb, split, sbar, Y, acc_dbg);
+      hipLaunchKernelGGL((k_linear_skinny<FMT, 1>), g, dim3(256), 0, st, M, d, n, xq, sx, rowsum, mb, split, sbar, Y,
+                         acc_dbg, wdelta, zbar, zw);
     else
-      hipLaunchKernelGGL((k_linear_skinny<FMT == F_UW4 ? F_INT16 : FMT, 2>), g, dim3(256), 0, st, M, d, n, xq, sx,
-                         rowsum, mb, split, sbar, Y, acc_dbg);
+      hipLaunchKernelGGL((k_linear_skinny<FMT, 2>), g, dim3(256), 0, st, M, d, n, xq, sx, rowsum, mb, split, sbar, Y,
+                         acc_dbg, wdelta, zbar, zw);
     return hipGetLastError();
   }
   const int tiles_m = (int)((M + BM - 1) / BM);

@@ -534,6 +534,26 @@ def test_linear_codes_bitexact(ops, M, d, n):
     assert np.array_equal(host(Y).view(np.uint16), yref)
 
 
+@pytest.mark.parametrize("M,d,n", [(5, 100, 96), (16, 300, 4128), (17, 129, 320), (32, 1000, 1024), (3, 2, 12288)])
+def test_linear_codes_few_tokens(ops, M, d, n):
+    """Merge-on-load at few tokens (the weight-streaming kernel forms m from the codes):
+    outputs and both accumulator planes bit for bit against the oracle."""
+    rng = np.random.Generator(np.random.PCG64(M * 13 + d + n))
+    u, w, zb, zw = _codes_case(rng, d, n)
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(M + 7, M, 1e-3, 0.1)
+    sbar = synth.random_positive(d + 8, d, 1e-5, 1e-2)
+    Y, acc = ops.linear_codes(cuda(xq), cuda(sx), cuda(pack4(u)), cuda(pack4(w)), cuda(zw), cuda(zb), cuda(sbar), d,
+                              acc_dbg=True)
+    m = oracle.merged_from_codes(u, w, zw, zb)
+    exact, _, yref = oracle.linear_from_codes(xq, sx, u, w, zw, zb, sbar)
+    hi, lo = oracle.byte_planes(m, split=np.zeros(d, np.uint8))
+    acc = host(acc).astype(np.int64)
+    assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
+    assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
+    assert np.array_equal(host(Y).view(np.uint16), yref)
+
+
 @pytest.mark.parametrize("M,d,n", [(2600, 4000, 224), (5000, 2000, 320), (4100, 9000, 96)])
 def test_linear_codes_many_tiles(ops, M, d, n):
     """More tiles than compute units: each block streams several tiles' stages, and the
