@@ -79,12 +79,14 @@ __global__ __launch_bounds__(ste::kThreads) void k_ste(int64_t d, int64_t n, int
 #pragma unroll
       for (int v = 0; v < 16; ++v) accB[t][q][v] = 0.0f;
 
-  // The next tile in flight in registers: wave wid holds rows wid + 4 yy of the tile,
-  // lane the columns c0 + 4 lane .. + 3 (G, their codes, the row's zero point), and
-  // 4 RT values of A's rows.  Row indices are clamped into the block's range; rows past
-  // it, and A's entries past r, are zeroed when the tile is staged in LDS, so no load
-  // result is used before the next tile.  The element path (not FAST) masks columns
-  // past n on load and sets the zero point to -1, which no code equals.
+  // A tile's loads, all issued before any is used (no branch between them): wave wid
+  // takes rows wid + 4 yy of the tile, lane the columns c0 + 4 lane .. + 3 (G, their
+  // codes, the row's zero point), and 4 RT values of A's rows.  Row indices are clamped
+  // into the block's range; rows past it, and A's entries past r, are zeroed when the
+  // tile is staged in LDS.  The element path (not FAST) masks columns past n on load
+  // and sets the zero point to -1, which no code equals.  (Holding the next tile in
+  // registers during the products was measured slower: the other block on the compute
+  // unit covers the load latency.)
   constexpr int AQ = 4 * RT;
   float4 pg[8];
   uint32_t pc[8];
@@ -151,7 +153,6 @@ __global__ __launch_bounds__(ste::kThreads) void k_ste(int64_t d, int64_t n, int
     }
   };
 
-  fetch(r_lo);
 
   // dA's B operand for every MFMA of the walk (loaded after the first tile's fetch is
   // in flight): step s8 (8 columns), MFMA e, k tile t -> B[32 t + li][c0 + 64 wid +
@@ -181,6 +182,7 @@ __global__ __launch_bounds__(ste::kThreads) void k_ste(int64_t d, int64_t n, int
   }
   for (int64_t i0 = r_lo; i0 < r_hi; i0 += kRows) {
     __syncthreads();  // the previous tile's D and A reads and dA buffer writes are done
+    fetch(i0);
 #pragma unroll
     for (int yy = 0; yy < 8; ++yy) {
       const float g[4] = {pg[yy].x, pg[yy].y, pg[yy].z, pg[yy].w};
@@ -200,7 +202,6 @@ __global__ __launch_bounds__(ste::kThreads) void k_ste(int64_t d, int64_t n, int
       sA[x] = (i0 + y < r_hi && k < r) ? pa_[u] : 0.0f;
     }
     __syncthreads();
-    if (i0 + kRows < r_hi) fetch(i0 + kRows);
     if (i0 > r_lo) flush_dA(i0 - kRows);
 
     // dA over this wave's 64 columns: MFMA e of step s8 takes columns 8 s8 + 4 hk + e
