@@ -165,7 +165,7 @@ const char* intlora_status_string(int status) {
 
 const char* intlora_last_error(void) { return g_err; }
 
-int intlora_version(void) { return 101; }
+int intlora_version(void) { return 102; }
 
 size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
   (void)M;
