@@ -60,6 +60,8 @@ def parse():
                         "codes and the linear layer forming m from them, timed on the same layers")
     p.add_argument("--no-ste", action="store_true",
                    help="skip the straight-through backward (a synthetic dL/dW' per layer, dA and dB)")
+    p.add_argument("--no-graph", action="store_true",
+                   help="skip the step captured in a HIP graph and replayed (reported beside the eager step)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -436,6 +438,11 @@ def main():
         torch.cuda.synchronize()
         overlap_ms = t0_.elapsed_time(t1_) / args.steps
 
+    # ---------------------------------------------------------------- the step as a HIP graph (optional)
+    graph = None
+    if not args.no_graph:
+        graph = graph_measure(args, layers, step, torch, stream)
+
     # ---------------------------------------------------------------- QLoRA-style comparison
     ptq = None
     if mode == "mul" and not args.no_ptq:
@@ -508,6 +515,7 @@ def main():
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
+        "graph": graph,
         "ptq_comparison": ptq,
         "merge_fused": fused,
         "merge_on_load": codes,
@@ -523,6 +531,42 @@ def main():
     if args.json_out:
         with open(args.json_out, "w") as fh:
             fh.write(line + "\n")
+
+
+def graph_measure(args, layers, step, torch, stream):
+    """The same step captured once in a HIP graph and replayed: the library launches
+    only kernels (no memset, copy or allocation), so the whole step captures. Each
+    timed replay's outputs are checked against the eager step's before timing."""
+    torch.cuda.synchronize()
+    ref = [lay["Y"].clone() for lay in layers]
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(cap):
+        step()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            step()
+    stream.wait_stream(cap)
+    torch.cuda.synchronize()
+    for lay in layers:
+        lay["Y"].zero_()
+    g.replay()
+    torch.cuda.synchronize()
+    same = all(torch.equal(lay["Y"], r) for lay, r in zip(layers, ref))
+    for _ in range(args.warmup):
+        g.replay()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for _ in range(args.steps):
+        g.replay()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / args.steps
+    del g
+    return {"ms_per_step": round(ms, 4), "replay_equals_eager": bool(same)}
 
 
 def cpu_baseline(wl, layers, M, mode, mbits, roof_ms, frac):

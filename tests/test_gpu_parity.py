@@ -639,3 +639,53 @@ def test_workload_end_to_end_reduced(ops, wl_index):
             assert np.array_equal(host(P["xq"]), xq)
             _, _, y = oracle.linear(xq, sx, ref["m"].astype(np.int32), ref["sbar"])
             assert np.array_equal(host(P["Y"]).view(np.uint16), y), (wl.name, L.name, mode)
+
+
+def test_graph_replay_matches_eager(ops):
+    """The library only launches kernels (no memset, copy or allocation), so a step can
+    be captured in a HIP graph: MUL merge + INT16 linear layer, merge keeping U's codes
+    + merge-on-load layer, and the few-token layer, captured once and replayed three
+    times with eager work in between; every replay equals the eager outputs."""
+    d, n, r, M = 260, 1024, 8, 300
+    wr, z, s, c, A, Bm = random_state(777, d, n, r, 4)
+    st = gpu_state(wr, z, s, c, 4)
+    Ag, Bg = cuda(A), cuda(Bm)
+    rng = np.random.Generator(np.random.PCG64(5))
+    X = rng.normal(0.0, 1.0, (M, n)).astype(np.float32)
+    xq, sx, rs = ops.quant_act(cuda(X))
+    ws = ops.workspace(ops.B.INTLORA_OP_MERGE_MUL, d, n, r, 4, xq.device)
+    out = ops.merge_mul(st, Ag, Bg, 4, 4, 9, 2, ws=ws)
+    outc = ops.merge_mul_codes(st, Ag, Bg, 4, 4, 9, 2, ws=ws)
+    Y = torch.empty((M, d), dtype=torch.int16, device=xq.device)
+    Yc = torch.empty_like(Y)
+    Ys = torch.empty((16, d), dtype=torch.int16, device=xq.device)
+
+    def step():
+        ops.merge_mul(st, Ag, Bg, 4, 4, 9, 2, ws=ws, out=out)
+        ops.linear(xq, sx, rs, 16, out["m"], out["sbar"], d, out=Y, split=out["split"])
+        ops.merge_mul_codes(st, Ag, Bg, 4, 4, 9, 2, ws=ws, out=outc)
+        ops.linear_codes(xq, sx, outc["ucode"], st["wround"], st["z"], outc["zbar"], outc["sbar"], d, out=Yc)
+        ops.linear(xq[:16], sx[:16], rs[:16], 16, out["m"], out["sbar"], d, out=Ys, split=out["split"])
+
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (out["m"], out["sbar"], out["split"], Y, outc["ucode"], Yc, Ys)]
+    s_ = torch.cuda.Stream()
+    s_.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_):
+        step()  # warm-up on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s_):
+            step()
+    torch.cuda.current_stream().wait_stream(s_)
+    for rep in range(3):
+        for t in (out["m"], Y, outc["ucode"], Yc, Ys):
+            t.zero_()
+        ops.quant_act(cuda(X))  # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = (out["m"], out["sbar"], out["split"], Y, outc["ucode"], Yc, Ys)
+        for a, b in zip(got, ref):
+            assert torch.equal(a, b), rep
