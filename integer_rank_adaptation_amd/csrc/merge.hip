@@ -292,24 +292,43 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
     if (i0 >= d) break;  // uniform over the block
     const int64_t i = i0 + li;
     const bool row_ok = i < d;
-    // MFMA B operand: lane l holds A[i0 + l % 32][k]
-    const float* Ai = A + (row_ok ? i : 0) * R;
+    // Every load of the tile is issued here, without branches (a row past d reads row
+    // d - 1 and a group past n reads column 0; their results are never used), so the
+    // loads are in flight together instead of each waiting behind a branch.
+    const int64_t ic = row_ok ? i : d - 1;
+    const int zi = z[ic];
+    const float ci = c[ic], si = s[ic];
+    uint32_t wcode[8];
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
+      jg = jg < n ? jg : 0;
+      if (W4)
+        wcode[g] = *reinterpret_cast<const uint16_t*>(wround + ic * (n >> 1) + (jg >> 1));
+      else
+        wcode[g] = *reinterpret_cast<const uint32_t*>(wround + ic * n + jg);
+    }
+    // MFMA B operand: lane l holds A[i0 + l % 32][k], loaded 32 values at a time
+    const float* Ai = A + ic * R;
     v32f acc;
 #pragma unroll
     for (int r = 0; r < 32; ++r) acc[r] = 0.0f;
+    constexpr int KC = R < 32 ? R : 32;
 #pragma unroll
-    for (int k = 0; k < R; k += 4) {
-      float4 a4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (row_ok) a4 = *reinterpret_cast<const float4*>(Ai + k);
-      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k], a4.x, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k + 1], a4.y, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k + 2], a4.z, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k + 3], a4.w, acc, 0, 0, 0);
+    for (int k0 = 0; k0 < R; k0 += KC) {
+      float4 a4[KC / 4];
+#pragma unroll
+      for (int k = 0; k < KC / 4; ++k) a4[k] = *reinterpret_cast<const float4*>(Ai + k0 + 4 * k);
+#pragma unroll
+      for (int k = 0; k < KC / 4; ++k) {
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k0 + 4 * k], a4[k].x, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k0 + 4 * k + 1], a4[k].y, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k0 + 4 * k + 2], a4[k].z, acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_32x32x1f32(bcol[k0 + 4 * k + 3], a4[k].w, acc, 0, 0, 0);
+      }
     }
     int kmin = kKeyPosInf, kmax = kKeyNegInf;
     if (row_ok) {
-      const int zi = z[i];
-      const float ci = c[i], si = s[i];
       // accumulator group g = 4 blk + q: columns jw + 32 blk + 8 q + 4 h + 0..3
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
@@ -317,13 +336,11 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
         if (jg >= n) continue;  // n % 4 == 0: a group is entirely inside or outside
         int w[4];
         if (W4) {
-          const uint32_t v = *reinterpret_cast<const uint16_t*>(wround + i * (n >> 1) + (jg >> 1));
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (int)((v >> (4 * e)) & 15u) - zi;
+          for (int e = 0; e < 4; ++e) w[e] = (int)((wcode[g] >> (4 * e)) & 15u) - zi;
         } else {
-          const uint32_t v = *reinterpret_cast<const uint32_t*>(wround + i * n + jg);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (int)((v >> (8 * e)) & 255u) - zi;
+          for (int e = 0; e < 4; ++e) w[e] = (int)((wcode[g] >> (8 * e)) & 255u) - zi;
         }
         const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
         float u[4], t[4], q[4];
@@ -1099,7 +1116,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
   extern __shared__ __attribute__((aligned(16))) float sU[];  // RB x COLS
   __shared__ LnLds tab[96];
   __shared__ float rcp[511];
-  __shared__ float sA[RB * 128];
+  __shared__ __attribute__((aligned(16))) float sA[RB * 128];
   __shared__ int smin[4][RB], smax[4][RB];
   __shared__ int sflag[RB];
   load_ln_table(tab);
@@ -1110,9 +1127,10 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
   int nsat = 0;
   for (int64_t i0 = (int64_t)blockIdx.x * RB; i0 < d; i0 += (int64_t)gridDim.x * RB) {
     __syncthreads();  // tables in place; the previous rows' LDS reads are done
-    for (int x = tid; x < RB * r; x += 256) {
-      const int rr = x / r, k = x - rr * r;
-      sA[rr * r + k] = i0 + rr < d ? A[(i0 + rr) * r + k] : 0.0f;
+    const int RP = (r + 3) & ~3;  // A's row pitch in LDS: rows start 16-byte aligned
+    for (int x = tid; x < RB * RP; x += 256) {
+      const int rr = x / RP, k = x - rr * RP;
+      sA[x] = i0 + rr < d && k < r ? A[(i0 + rr) * r + k] : 0.0f;
     }
     if (tid < RB) sflag[tid] = 0;
     __syncthreads();
@@ -1130,23 +1148,66 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
       for (int rr = 0; rr < RB; ++rr)
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[rr][e] = 0.0f;
-      for (int k = 0; k < r; ++k) {
-        float b[4];
-        if (quad) {
-          const float4 b4 = *reinterpret_cast<const float4*>(B + (int64_t)k * n + j0);
-          b[0] = b4.x;
-          b[1] = b4.y;
-          b[2] = b4.z;
-          b[3] = b4.w;
-        } else {
+      if (quad) {
+        // B is read in chunks of KU rows, all loads of a chunk issued together and the
+        // next chunk's issued before the current one's products, so the L2 latency is
+        // paid once per chunk instead of once per k.  k is clamped to r - 1 so the
+        // loads need no branch; a clamped k is never used.
+        constexpr int KU = RB >= 8 ? 2 : RB >= 4 ? 4 : 8;  // shorter chunks where more rows share a load
+        float4 bc[KU], bn[KU];
+#pragma unroll
+        for (int kk = 0; kk < KU; ++kk)
+          bc[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(kk < r ? kk : r - 1) * n + j0);
+        for (int k0 = 0; k0 < r; k0 += KU) {
+#pragma unroll
+          for (int kk = 0; kk < KU; ++kk) {
+            const int k = k0 + KU + kk;
+            bn[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(k < r ? k : r - 1) * n + j0);
+          }
+          // A[rows][k0 .. k0 + KU) with vector LDS reads (k0 is a multiple of KU, the
+          // pitch a multiple of 4; entries past r are read but never used)
+          float av[RB][KU];
+#pragma unroll
+          for (int rr = 0; rr < RB; ++rr) {
+#pragma unroll
+            for (int c = 0; c < KU; c += (KU >= 4 ? 4 : 2)) {
+              if (KU >= 4) {
+                const float4 v = *reinterpret_cast<const float4*>(sA + rr * RP + k0 + c);
+                av[rr][c] = v.x;
+                av[rr][c + 1] = v.y;
+                av[rr][c + 2] = v.z;
+                av[rr][c + 3] = v.w;
+              } else {
+                const float2 v = *reinterpret_cast<const float2*>(sA + rr * RP + k0 + c);
+                av[rr][c] = v.x;
+                av[rr][c + 1] = v.y;
+              }
+            }
+          }
+#pragma unroll
+          for (int kk = 0; kk < KU; ++kk) {
+            if (k0 + kk < r) {  // uniform over the block
+              const float b[4] = {bc[kk].x, bc[kk].y, bc[kk].z, bc[kk].w};
+#pragma unroll
+              for (int rr = 0; rr < RB; ++rr)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(av[rr][kk], b[e], acc[rr][e]);
+            }
+          }
+#pragma unroll
+          for (int kk = 0; kk < KU; ++kk) bc[kk] = bn[kk];
+        }
+      } else {
+        for (int k = 0; k < r; ++k) {
+          float b[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) b[e] = j0 + e < n ? B[(int64_t)k * n + j0 + e] : 0.0f;
-        }
 #pragma unroll
-        for (int rr = 0; rr < RB; ++rr) {
-          const float a = sA[rr * r + k];
+          for (int rr = 0; rr < RB; ++rr) {
+            const float a = sA[rr * RP + k];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(a, b[e], acc[rr][e]);
+            for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(a, b[e], acc[rr][e]);
+          }
         }
       }
 #pragma unroll
