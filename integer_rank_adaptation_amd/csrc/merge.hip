@@ -1086,8 +1086,9 @@ hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* p
 
 // ---------------------------------------------------------------------------------
 // Fused single-pass MUL merge with no scratch memory.  A block owns RB = 16 / NG whole
-// rows (8 for NG = 1; n <= 1024 NG) and keeps their U in LDS (RB x 1024 NG floats, at
-// most 64 KB), so each
+// rows (8 for NG = 1; n <= 1024 NG) and keeps their U in LDS (RB rows at a pitch of n
+// rounded up to 4 floats, at most 64 KB, sized to n so that three blocks share a
+// compute unit where they fit; A's rows follow), so each
 // row's range is complete (block reduction) before any of its elements is quantized
 // and U never leaves the chip.  Thread t computes columns 4 (t + 256 g) .. + 3 of
 // every row of the block (and quantizes the same ones).  The rank-r term is the fmaf
@@ -1099,7 +1100,11 @@ template <int NG>
 struct FusedLds {
   static constexpr int RB = NG == 1 ? 8 : 16 / NG;  // rows per block
   static constexpr int COLS = 1024 * NG;
-  static constexpr int BYTES = RB * COLS * 4;
+  // U rows + A rows (+ 8 floats: the last row's vector reads may run up to 7 past r)
+  static constexpr int MAX_BYTES = RB * COLS * 4 + (RB * 128 + 8) * 4;
+  static int64_t bytes(int64_t n, int r) {
+    return (int64_t)RB * ((n + 3) & ~(int64_t)3) * 4 + ((int64_t)RB * ((r + 3) & ~3) + 8) * 4;
+  }
 };
 
 template <int NG, bool W4>
@@ -1112,11 +1117,13 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
                                                     uint8_t* __restrict__ split, uint8_t* __restrict__ uround_dbg,
                                                     unsigned long long* __restrict__ sat) {
   constexpr int RB = FusedLds<NG>::RB;
-  constexpr int COLS = FusedLds<NG>::COLS;
-  extern __shared__ __attribute__((aligned(16))) float sU[];  // RB x COLS
+  extern __shared__ __attribute__((aligned(16))) float dyn[];
+  const int64_t pitch = (n + 3) & ~(int64_t)3;  // U's row pitch in LDS
+  const int RP = (r + 3) & ~3;                  // A's row pitch in LDS: rows start 16-byte aligned
+  float* __restrict__ sU = dyn;                 // RB x pitch
+  float* __restrict__ sA = dyn + RB * pitch;    // RB x RP
   __shared__ LnLds tab[96];
   __shared__ float rcp[511];
-  __shared__ __attribute__((aligned(16))) float sA[RB * 128];
   __shared__ int smin[4][RB], smax[4][RB];
   __shared__ int sflag[RB];
   load_ln_table(tab);
@@ -1127,7 +1134,6 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
   int nsat = 0;
   for (int64_t i0 = (int64_t)blockIdx.x * RB; i0 < d; i0 += (int64_t)gridDim.x * RB) {
     __syncthreads();  // tables in place; the previous rows' LDS reads are done
-    const int RP = (r + 3) & ~3;  // A's row pitch in LDS: rows start 16-byte aligned
     for (int x = tid; x < RB * RP; x += 256) {
       const int rr = x / RP, k = x - rr * RP;
       sA[x] = i0 + rr < d && k < r ? A[(i0 + rr) * r + k] : 0.0f;
@@ -1252,7 +1258,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const float uu = si + q[e];
-          sU[rr * COLS + j0 + e] = uu;
+          sU[rr * pitch + j0 + e] = uu;
           if (row_ok && w[e] != 0 && j0 + e < n) {
             const int key = f32_key(uu);
             kmin[rr] = min(kmin[rr], key);
@@ -1299,7 +1305,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
         }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          uu[e] = sU[rr * COLS + j0 + e];
+          uu[e] = sU[rr * pitch + j0 + e];
           bool exact = true;
           ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, qmax, exact) : P.zbar;
           redo[e] = !exact;
@@ -1413,11 +1419,12 @@ hipError_t launch_merge_fused(const AdaptArgs& a, int u_bits, int16_t* m, float*
     static bool attr = false;                                                                                   \
     if (!attr) {                                                                                                \
       const hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge_fused<NG, W4>),           \
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, FusedLds<NG>::BYTES); \
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, FusedLds<NG>::MAX_BYTES); \
       if (e_ != hipSuccess) return e_;                                                                          \
       attr = true;                                                                                              \
     }                                                                                                           \
-    hipLaunchKernelGGL((k_merge_fused<NG, W4>), grid, dim3(256), FusedLds<NG>::BYTES, st, a.d, a.n, a.r, u_bits, \
+    hipLaunchKernelGGL((k_merge_fused<NG, W4>), grid, dim3(256), (unsigned)FusedLds<NG>::bytes(a.n, a.r), st, a.d, \
+                       a.n, a.r, u_bits,                                                                        \
                        a.seed, a.layer_id, a.wround, a.z, a.s, a.c, a.A, a.B, m, sbar, zbar, split, uround_dbg, sat); \
   } while (0)
 #define INTLORA_FUSED_W(NG) \
