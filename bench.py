@@ -46,9 +46,9 @@ def parse():
                    help="fraction of rows/tokens the oracle processes (0: auto, about 15 s)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--json-out", default="")
-    p.add_argument("--overlap", action="store_true",
-                   help="also time a pipelined step: merges on a second stream, each layer's linear layer "
-                        "waiting only for its own merge")
+    p.add_argument("--no-overlap", action="store_true",
+                   help="skip the pipelined step (merges on a second stream, each layer's linear layer "
+                        "waiting only for its own merge), which is timed beside the sequential one")
     p.add_argument("--no-ptq", action="store_true",
                    help="skip the QLoRA-style comparison (MUL workloads): the dequantize / add / requant "
                         "path timed on the same layers, and both paths' weight error")
@@ -401,37 +401,38 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # ---------------------------------------------------------------- pipelined step (optional)
+    # The merges run on a side stream, each layer's linear layer waiting only for its own
+    # merge; the side stream forks from the step's stream at the start of the step (so a
+    # merge never overwrites m while the previous step's linear layer still reads it) and
+    # joins it at the end.  The same function is captured in a graph below.
+    ms_stream = torch.cuda.Stream()
+    done_merge = [torch.cuda.Event() for _ in layers]
+
+    def step_overlap():
+        cur = torch.cuda.current_stream()
+        ms_stream.wait_stream(cur)
+        for k, lay in enumerate(layers):
+            with torch.cuda.stream(ms_stream):
+                if mode == "mul":
+                    ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
+                                  ws=ws, out=lay["out"])
+                else:
+                    ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
+                                    lay["lid"], ws=ws, out=lay["out"])
+                done_merge[k].record(ms_stream)
+            cur.wait_event(done_merge[k])
+            ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"],
+                       lay["L"].d, out=lay["Y"], split=lay["out"].get("split"))
+        cur.wait_stream(ms_stream)
+
     overlap_ms = None
-    if args.overlap:
-        ms_stream = torch.cuda.Stream()
-        done_merge = [torch.cuda.Event() for _ in layers]
-        done_gemm = [torch.cuda.Event() for _ in layers]
-
-        def step_overlap():
-            for k, lay in enumerate(layers):
-                with torch.cuda.stream(ms_stream):
-                    ms_stream.wait_event(done_gemm[k])  # the previous step's reader of out[k]
-                    if mode == "mul":
-                        ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
-                                      lay["lid"], ws=ws, out=lay["out"])
-                    else:
-                        ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
-                                        lay["lid"], ws=ws, out=lay["out"])
-                    done_merge[k].record(ms_stream)
-                stream.wait_event(done_merge[k])
-                ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"],
-                           lay["L"].d, out=lay["Y"], split=lay["out"].get("split"))
-                done_gemm[k].record(stream)
-
-        for ev_ in done_gemm:
-            ev_.record(stream)
+    if not args.no_overlap:
         for _ in range(args.warmup):
             step_overlap()
         torch.cuda.synchronize()
         t0_ = torch.cuda.Event(enable_timing=True)
         t1_ = torch.cuda.Event(enable_timing=True)
         t0_.record(stream)
-        ms_stream.wait_event(t0_)
         for _ in range(args.steps):
             step_overlap()
         t1_.record(stream)
@@ -442,6 +443,9 @@ def main():
     graph = None
     if not args.no_graph:
         graph = graph_measure(args, layers, step, torch, stream)
+        graph_ov = graph_measure(args, layers, step_overlap, torch, stream)
+        graph = {"ms_per_step": graph["ms_per_step"], "overlap_ms_per_step": graph_ov["ms_per_step"],
+                 "replay_equals_eager": graph["replay_equals_eager"] and graph_ov["replay_equals_eager"]}
 
     # ---------------------------------------------------------------- QLoRA-style comparison
     ptq = None
