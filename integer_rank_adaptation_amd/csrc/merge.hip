@@ -257,6 +257,7 @@ constexpr int kKeyNegInf = (int)0x807FFFFF;  // order key of -inf (identity of m
 // columns in registers across them.
 // ---------------------------------------------------------------------------------
 typedef float v32f __attribute__((ext_vector_type(32)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 constexpr int kMfmaCols = 256;
 constexpr int kMfmaMaxRowTiles = 8;
 
@@ -1140,140 +1141,269 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
     }
     if (tid < RB) sflag[tid] = 0;
     __syncthreads();
-    int kmin[RB], kmax[RB];
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      kmin[rr] = kKeyPosInf;
-      kmax[rr] = kKeyNegInf;
-    }
-    for (int g = 0; g < NG; ++g) {
-      const int64_t j0 = 4 * ((int64_t)tid + 256 * g);
-      if (j0 >= n) break;
-      float acc[RB][4];
-#pragma unroll
-      for (int rr = 0; rr < RB; ++rr)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[rr][e] = 0.0f;
+    bool done = false;
+    if constexpr (RB == 8) {  // measured: at RB = 4 the vector-ALU chain below is faster
       if (quad) {
-        // B is read in chunks of KU rows, all loads of a chunk issued together and the
-        // next chunk's issued before the current one's products, so the L2 latency is
-        // paid once per chunk instead of once per k.  k is clamped to r - 1 so the
-        // loads need no branch; a clamped k is never used.
-        constexpr int KU = RB >= 8 ? 2 : RB >= 4 ? 4 : 8;  // shorter chunks where more rows share a load
-        float4 bc[KU], bn[KU];
+        // Rank-r term on the matrix cores: v_mfma_f32_4x4x1f32 forms 16 blocks of 4 x 4
+        // outer products with one rounding per k, so a chain of r of them in k order is
+        // the fmaf chain of the definition.  Taken transposed (MFMA rows = columns j,
+        // MFMA columns = rows i), lane 4b + q ends with row q of its row group and the 4
+        // consecutive columns of block b: one Philox block per lane and chunk.  A wave
+        // covers 4 chunks of 64 columns per column group.
+        constexpr int RG = RB / 4;  // row groups of 4
+        const int jr = lane & 3, bq = lane >> 2;
+        int kmn[RG], kmx[RG], zr[RG];
+        float cr[RG], sr[RG];
+        int64_t ir[RG];
+        bool okr[RG];
 #pragma unroll
-        for (int kk = 0; kk < KU; ++kk)
-          bc[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(kk < r ? kk : r - 1) * n + j0);
-        for (int k0 = 0; k0 < r; k0 += KU) {
+        for (int rg = 0; rg < RG; ++rg) {
+          okr[rg] = i0 + 4 * rg + jr < d;
+          ir[rg] = okr[rg] ? i0 + 4 * rg + jr : d - 1;  // a row past d is computed, never stored
+          zr[rg] = z[ir[rg]];
+          cr[rg] = c[ir[rg]];
+          sr[rg] = s[ir[rg]];
+          kmn[rg] = kKeyPosInf;
+          kmx[rg] = kKeyNegInf;
+        }
+        for (int g = 0; g < NG; ++g) {
+          const int64_t cw = 1024 * (int64_t)g + 256 * wid;  // the wave's first column
+          if (cw >= n) break;                                // uniform over the wave
+          int64_t colc[4];  // MFMA A operand: lane l holds B[k][cw + 64 ch + l] (clamped)
 #pragma unroll
-          for (int kk = 0; kk < KU; ++kk) {
-            const int k = k0 + KU + kk;
-            bn[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(k < r ? k : r - 1) * n + j0);
-          }
-          // A[rows][k0 .. k0 + KU) with vector LDS reads (k0 is a multiple of KU, the
-          // pitch a multiple of 4; entries past r are read but never used)
-          float av[RB][KU];
+          for (int ch = 0; ch < 4; ++ch) colc[ch] = cw + 64 * ch + lane < n ? cw + 64 * ch + lane : n - 1;
+          v4f acc[4][RG];
 #pragma unroll
-          for (int rr = 0; rr < RB; ++rr) {
+          for (int ch = 0; ch < 4; ++ch)
 #pragma unroll
-            for (int c = 0; c < KU; c += (KU >= 4 ? 4 : 2)) {
-              if (KU >= 4) {
-                const float4 v = *reinterpret_cast<const float4*>(sA + rr * RP + k0 + c);
-                av[rr][c] = v.x;
-                av[rr][c + 1] = v.y;
-                av[rr][c + 2] = v.z;
-                av[rr][c + 3] = v.w;
-              } else {
-                const float2 v = *reinterpret_cast<const float2*>(sA + rr * RP + k0 + c);
-                av[rr][c] = v.x;
-                av[rr][c + 1] = v.y;
+            for (int rg = 0; rg < RG; ++rg) acc[ch][rg] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+          constexpr int KU = 4;
+          float bc[KU][4], bn[KU][4];
+#pragma unroll
+          for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+            for (int ch = 0; ch < 4; ++ch) bc[kk][ch] = B[(int64_t)(kk < r ? kk : r - 1) * n + colc[ch]];
+          for (int k0 = 0; k0 < r; k0 += KU) {
+#pragma unroll
+            for (int kk = 0; kk < KU; ++kk) {
+              const int k = k0 + KU + kk;
+#pragma unroll
+              for (int ch = 0; ch < 4; ++ch) bn[kk][ch] = B[(int64_t)(k < r ? k : r - 1) * n + colc[ch]];
+            }
+            float4 av[RG];  // MFMA B operand: lane 4b + q holds A[row 4 rg + q][k]
+#pragma unroll
+            for (int rg = 0; rg < RG; ++rg) av[rg] = *reinterpret_cast<const float4*>(sA + (4 * rg + jr) * RP + k0);
+#pragma unroll
+            for (int kk = 0; kk < KU; ++kk) {
+              if (k0 + kk < r) {  // uniform over the block
+#pragma unroll
+                for (int rg = 0; rg < RG; ++rg) {
+                  const float a = kk == 0 ? av[rg].x : kk == 1 ? av[rg].y : kk == 2 ? av[rg].z : av[rg].w;
+#pragma unroll
+                  for (int ch = 0; ch < 4; ++ch)
+                    acc[ch][rg] = __builtin_amdgcn_mfma_f32_4x4x1f32(bc[kk][ch], a, acc[ch][rg], 0, 0, 0);
+                }
               }
             }
+#pragma unroll
+            for (int kk = 0; kk < KU; ++kk)
+#pragma unroll
+              for (int ch = 0; ch < 4; ++ch) bc[kk][ch] = bn[kk][ch];
           }
 #pragma unroll
-          for (int kk = 0; kk < KU; ++kk) {
-            if (k0 + kk < r) {  // uniform over the block
-              const float b[4] = {bc[kk].x, bc[kk].y, bc[kk].z, bc[kk].w};
+          for (int ch = 0; ch < 4; ++ch) {
+            const int64_t j0 = cw + 64 * ch + 4 * bq;
+            if (j0 >= n) continue;  // n % 4 == 0: the 4 columns are all inside or all outside
 #pragma unroll
-              for (int rr = 0; rr < RB; ++rr)
+            for (int rg = 0; rg < RG; ++rg) {
+              const int64_t i = ir[rg];
+              const uint32_t cv = W4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(wround + ((i * n + j0) >> 1))
+                                     : *reinterpret_cast<const uint32_t*>(wround + i * n + j0);
+              const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)j0) >> 2, layer_id, seed);
+              int w[4];
+              float t[4], q[4];
+              bool slow = false;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(av[rr][kk], b[e], acc[rr][e]);
+              for (int e = 0; e < 4; ++e) {
+                w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zr[rg];
+                const float rs = cr[rg] * laplace_from_word(pick_word(rnd, e), tab);
+                t[e] = rs + acc[ch][rg][e];
+                q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+                slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+              }
+              if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+                __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+              }
+              float uu[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                uu[e] = sr[rg] + q[e];
+                if (okr[rg] && w[e] != 0) {
+                  const int key = f32_key(uu[e]);
+                  kmn[rg] = min(kmn[rg], key);
+                  kmx[rg] = max(kmx[rg], key);
+                }
+              }
+              *reinterpret_cast<float4*>(sU + (4 * rg + jr) * pitch + j0) = make_float4(uu[0], uu[1], uu[2], uu[3]);
             }
           }
-#pragma unroll
-          for (int kk = 0; kk < KU; ++kk) bc[kk] = bn[kk];
         }
-      } else {
-        for (int k = 0; k < r; ++k) {
-          float b[4];
+        // each row's range over the wave: lanes with the same q hold the same row
 #pragma unroll
-          for (int e = 0; e < 4; ++e) b[e] = j0 + e < n ? B[(int64_t)k * n + j0 + e] : 0.0f;
+        for (int rg = 0; rg < RG; ++rg) {
+          int a = kmn[rg], b = kmx[rg];
 #pragma unroll
-          for (int rr = 0; rr < RB; ++rr) {
-            const float a = sA[rr * RP + k];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(a, b[e], acc[rr][e]);
+          for (int o = 4; o < 64; o <<= 1) {
+            a = min(a, __shfl_xor(a, o, kWave));
+            b = max(b, __shfl_xor(b, o, kWave));
+          }
+          if (lane < 4) {
+            smin[wid][4 * rg + lane] = a;
+            smax[wid][4 * rg + lane] = b;
           }
         }
-      }
-#pragma unroll
-      for (int rr = 0; rr < RB; ++rr) {
-        const bool row_ok = i0 + rr < d;
-        const int64_t i = row_ok ? i0 + rr : d - 1;  // a row past d is computed, never stored
-        const int zi = z[i];
-        const float ci = c[i], si = s[i];
-        int w[4];
-        float rs[4];
-        if (quad) {
-          const uint32_t cv = W4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(wround + ((i * n + j0) >> 1))
-                                 : *reinterpret_cast<const uint32_t*>(wround + i * n + j0);
-          const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)j0) >> 2, layer_id, seed);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zi;
-            rs[e] = ci * laplace_from_word(pick_word(rnd, e), tab);
-          }
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int64_t j = j0 + e < n ? j0 + e : n - 1;
-            w[e] = code_at<W4>(wround, i, n, j) - zi;
-            rs[e] = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab);
-          }
-        }
-        float t[4], q[4];
-        bool slow = false;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          t[e] = rs[e] + acc[rr][e];
-          q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
-          slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
-        }
-        if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-          __asm__ volatile("");  // keeps the branch: the division is not speculated
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
-        }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float uu = si + q[e];
-          sU[rr * pitch + j0 + e] = uu;
-          if (row_ok && w[e] != 0 && j0 + e < n) {
-            const int key = f32_key(uu);
-            kmin[rr] = min(kmin[rr], key);
-            kmax[rr] = max(kmax[rr], key);
-          }
-        }
+        done = true;
       }
     }
-    // each row's range over the block (order keys)
-#pragma unroll
-    for (int rr = 0; rr < RB; ++rr) {
-      const int a = wave_min_i32(kmin[rr]), b = wave_max_i32(kmax[rr]);
-      if (lane == 0) {
-        smin[wid][rr] = a;
-        smax[wid][rr] = b;
+    if (!done) {
+      int kmin[RB], kmax[RB];
+  #pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        kmin[rr] = kKeyPosInf;
+        kmax[rr] = kKeyNegInf;
+      }
+      for (int g = 0; g < NG; ++g) {
+        const int64_t j0 = 4 * ((int64_t)tid + 256 * g);
+        if (j0 >= n) break;
+        float acc[RB][4];
+  #pragma unroll
+        for (int rr = 0; rr < RB; ++rr)
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) acc[rr][e] = 0.0f;
+        if (quad) {
+          // B is read in chunks of KU rows, all loads of a chunk issued together and the
+          // next chunk's issued before the current one's products, so the L2 latency is
+          // paid once per chunk instead of once per k.  k is clamped to r - 1 so the
+          // loads need no branch; a clamped k is never used.
+          constexpr int KU = RB >= 8 ? 2 : RB >= 4 ? 4 : 8;  // shorter chunks where more rows share a load
+          float4 bc[KU], bn[KU];
+  #pragma unroll
+          for (int kk = 0; kk < KU; ++kk)
+            bc[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(kk < r ? kk : r - 1) * n + j0);
+          for (int k0 = 0; k0 < r; k0 += KU) {
+  #pragma unroll
+            for (int kk = 0; kk < KU; ++kk) {
+              const int k = k0 + KU + kk;
+              bn[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(k < r ? k : r - 1) * n + j0);
+            }
+            // A[rows][k0 .. k0 + KU) with vector LDS reads (k0 is a multiple of KU, the
+            // pitch a multiple of 4; entries past r are read but never used)
+            float av[RB][KU];
+  #pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+  #pragma unroll
+              for (int c = 0; c < KU; c += (KU >= 4 ? 4 : 2)) {
+                if (KU >= 4) {
+                  const float4 v = *reinterpret_cast<const float4*>(sA + rr * RP + k0 + c);
+                  av[rr][c] = v.x;
+                  av[rr][c + 1] = v.y;
+                  av[rr][c + 2] = v.z;
+                  av[rr][c + 3] = v.w;
+                } else {
+                  const float2 v = *reinterpret_cast<const float2*>(sA + rr * RP + k0 + c);
+                  av[rr][c] = v.x;
+                  av[rr][c + 1] = v.y;
+                }
+              }
+            }
+  #pragma unroll
+            for (int kk = 0; kk < KU; ++kk) {
+              if (k0 + kk < r) {  // uniform over the block
+                const float b[4] = {bc[kk].x, bc[kk].y, bc[kk].z, bc[kk].w};
+  #pragma unroll
+                for (int rr = 0; rr < RB; ++rr)
+  #pragma unroll
+                  for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(av[rr][kk], b[e], acc[rr][e]);
+              }
+            }
+  #pragma unroll
+            for (int kk = 0; kk < KU; ++kk) bc[kk] = bn[kk];
+          }
+        } else {
+          for (int k = 0; k < r; ++k) {
+            float b[4];
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) b[e] = j0 + e < n ? B[(int64_t)k * n + j0 + e] : 0.0f;
+  #pragma unroll
+            for (int rr = 0; rr < RB; ++rr) {
+              const float a = sA[rr * RP + k];
+  #pragma unroll
+              for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(a, b[e], acc[rr][e]);
+            }
+          }
+        }
+  #pragma unroll
+        for (int rr = 0; rr < RB; ++rr) {
+          const bool row_ok = i0 + rr < d;
+          const int64_t i = row_ok ? i0 + rr : d - 1;  // a row past d is computed, never stored
+          const int zi = z[i];
+          const float ci = c[i], si = s[i];
+          int w[4];
+          float rs[4];
+          if (quad) {
+            const uint32_t cv = W4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(wround + ((i * n + j0) >> 1))
+                                   : *reinterpret_cast<const uint32_t*>(wround + i * n + j0);
+            const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)j0) >> 2, layer_id, seed);
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zi;
+              rs[e] = ci * laplace_from_word(pick_word(rnd, e), tab);
+            }
+          } else {
+  #pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int64_t j = j0 + e < n ? j0 + e : n - 1;
+              w[e] = code_at<W4>(wround, i, n, j) - zi;
+              rs[e] = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab);
+            }
+          }
+          float t[4], q[4];
+          bool slow = false;
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            t[e] = rs[e] + acc[rr][e];
+            q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+            slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+          }
+          if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+            __asm__ volatile("");  // keeps the branch: the division is not speculated
+  #pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+          }
+  #pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float uu = si + q[e];
+            sU[rr * pitch + j0 + e] = uu;
+            if (row_ok && w[e] != 0 && j0 + e < n) {
+              const int key = f32_key(uu);
+              kmin[rr] = min(kmin[rr], key);
+              kmax[rr] = max(kmax[rr], key);
+            }
+          }
+        }
+      }
+      // each row's range over the block (order keys)
+  #pragma unroll
+      for (int rr = 0; rr < RB; ++rr) {
+        const int a = wave_min_i32(kmin[rr]), b = wave_max_i32(kmax[rr]);
+        if (lane == 0) {
+          smin[wid][rr] = a;
+          smax[wid][rr] = b;
+        }
       }
     }
     __syncthreads();
