@@ -85,6 +85,14 @@ def _declare(L):
         "ora_laplace_batch": (None, [_I64, _P, _P]),
         "ora_ln_batch": (None, [_I64, _P, _P]),
         "ora_log2_round_batch": (None, [_I64, _P, _P]),
+        "ora_cospi": (_F64, [_F64]),
+        "ora_sinpi": (_F64, [_F64]),
+        "ora_tanpi": (_F64, [_F64]),
+        "ora_aux": (_F32, [_P, _I32, _I32]),
+        "ora_trig_batch": (None, [_I64, _P, _I32, _P]),
+        "ora_aux_batch": (None, [_I64, _P, _I32, _P]),
+        "ora_gen_r_dist": (None, [_I64, _I64, _I64, _U64, _U32, _I32, _P, _P]),
+        "ora_vmc_scale_dist": (None, [_I64, _P, _F64, _I32, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -130,19 +138,44 @@ def laplace(words):
     return out
 
 
-def gen_r(d, n, seed, layer_id, c):
+def gen_r(d, n, seed, layer_id, c, aux_dist=0):
+    """R* = c * sample, the sample under law aux_dist (0 Laplace, 1 Gaussian, 2 Cauchy,
+    3 Student-t(2); IntLoRA "1. AQS" and the summary table's distribution ablation)."""
     c = _c(c, np.float32)
     assert c.shape == (d,)
     out = np.empty((d, n), np.float32)
-    lib().ora_gen_r(d, n, seed, layer_id, _p(c), _p(out))
+    if aux_dist == 0:
+        lib().ora_gen_r(d, n, seed, layer_id, _p(c), _p(out))
+    else:
+        lib().ora_gen_r_dist(0, d, n, seed, layer_id, int(aux_dist), _p(c), _p(out))
     return out
 
 
-def gen_r_rows(row0, rows, n, seed, layer_id, c_rows):
+def aux_samples(words, aux_dist):
+    """The unscaled sample of every element of the Philox blocks `words` (..., 4)."""
+    words = _c(words, np.uint32).reshape(-1, 4)
+    out = np.empty(words.shape, np.float32)
+    lib().ora_aux_batch(words.shape[0], _p(words), int(aux_dist), _p(out))
+    return out
+
+
+def trig_pi(v, kind):
+    """binary64 cos(pi v) (kind 0), sin(pi v) (1) for 0 < v < 2, tan(pi v) (2) for |v| < 1/2,
+    v with at most 24 significant bits (the arguments the samplers produce)."""
+    v = _c(v, np.float64)
+    out = np.empty_like(v)
+    lib().ora_trig_batch(v.size, _p(v), int(kind), _p(out))
+    return out
+
+
+def gen_r_rows(row0, rows, n, seed, layer_id, c_rows, aux_dist=0):
     c_rows = _c(c_rows, np.float32)
     assert c_rows.shape == (rows,)
     out = np.empty((rows, n), np.float32)
-    lib().ora_gen_r_rows(row0, rows, n, seed, layer_id, _p(c_rows), _p(out))
+    if aux_dist == 0:
+        lib().ora_gen_r_rows(row0, rows, n, seed, layer_id, _p(c_rows), _p(out))
+    else:
+        lib().ora_gen_r_dist(row0, rows, n, seed, layer_id, int(aux_dist), _p(c_rows), _p(out))
     return out
 
 
@@ -155,10 +188,15 @@ def sigma_w(W):
     return out
 
 
-def vmc_scale(sigma, alpha):
+def vmc_scale(sigma, alpha, aux_dist=0):
+    """c = RN32((sigma_W / sigma_R)^alpha): sigma_R = sqrt(2) for Laplace(0, 1), 1 for the
+    other laws of the auxiliary-matrix ablation (IntLoRA, "3. VMC")."""
     sigma = _c(sigma, np.float32)
     out = np.empty_like(sigma)
-    lib().ora_vmc_scale(sigma.size, _p(sigma), float(alpha), _p(out))
+    if aux_dist == 0:
+        lib().ora_vmc_scale(sigma.size, _p(sigma), float(alpha), _p(out))
+    else:
+        lib().ora_vmc_scale_dist(sigma.size, _p(sigma), float(alpha), int(aux_dist), _p(out))
     return out
 
 

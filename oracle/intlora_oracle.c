@@ -124,6 +124,78 @@ ORA_API void ora_laplace_batch(int64_t count, const uint32_t* words, float* out)
     for (int64_t i = 0; i < count; ++i) out[i] = ora_laplace(words[i]);
 }
 
+/* ------------------------------------------------------------------------- */
+/* The other laws of the auxiliary-matrix ablation (IntLoRA summary table,    */
+/* "Measured effects": Gaussian, Cauchy and Student-t samples against the     */
+/* Laplace one).  The pages name the laws only; readings:                     */
+/*  - every law takes the Laplace sampler's uniform u = (2 floor(x/2^9)+1)2^-24 */
+/*    of the element's word x;                                                 */
+/*  - Gaussian: the Box-Muller transform on the word pairs (0, 1) and (2, 3)   */
+/*    of the element's Philox block (u1 from the first word, u2 from the       */
+/*    second; element 2p takes the cosine, 2p + 1 the sine):                   */
+/*      L = RN32(ln u1), S = RN32(sqrt(-2 L)), C = RN32(cos(2 pi u2)) or       */
+/*      RN32(sin(2 pi u2)), sample = RN32(S C);                                */
+/*  - Cauchy(0, 1): RN32(tan(pi (u - 1/2)));                                   */
+/*  - Student-t with 2 degrees of freedom (its inverse distribution function   */
+/*    is algebraic): RN32((2u - 1) / sqrt(2 u (1 - u))).                       */
+/* Each RN32(f) is the binary64 value rounded once; the arguments are reduced  */
+/* exactly (v has at most 24 significant bits) to [0, 1/4] before libm's sin,  */
+/* cos or tan, so the binary64 value is within a few units of 2^-53 and the    */
+/* test suite decides every point near a binary32 midpoint with 40 digits.     */
+/* ------------------------------------------------------------------------- */
+static double sinpi_small(double a) { return sin(M_PI * a); } /* 0 <= a <= 1/4 */
+static double cospi_small(double a) { return cos(M_PI * a); } /* 0 <= a <= 1/4 */
+
+/* cos(pi v), sin(pi v) for 0 < v < 2 */
+ORA_API double ora_cospi(double v) {
+    double a = v > 1.0 ? 2.0 - v : v; /* cos(pi v) = cos(pi (2 - v)) */
+    double sign = 1.0;
+    if (a > 0.5) { a = 1.0 - a; sign = -1.0; } /* cos(pi a) = -cos(pi (1 - a)) */
+    return sign * (a <= 0.25 ? cospi_small(a) : sinpi_small(0.5 - a));
+}
+ORA_API double ora_sinpi(double v) {
+    double sign = 1.0, a = v;
+    if (a > 1.0) { a = a - 1.0; sign = -1.0; } /* sin(pi v) = -sin(pi (v - 1)) */
+    if (a > 0.5) a = 1.0 - a;                  /* sin(pi a) = sin(pi (1 - a)) */
+    return sign * (a <= 0.25 ? sinpi_small(a) : cospi_small(0.5 - a));
+}
+/* tan(pi v) for |v| < 1/2 */
+ORA_API double ora_tanpi(double v) {
+    double a = fabs(v), t;
+    if (a <= 0.25) t = tan(M_PI * a);
+    else t = cospi_small(0.5 - a) / sinpi_small(0.5 - a); /* cot(pi (1/2 - a)) */
+    return v < 0.0 ? -t : t;
+}
+
+ORA_API void ora_trig_batch(int64_t count, const double* v, int kind, double* out) {
+    for (int64_t i = 0; i < count; ++i)
+        out[i] = kind == 0 ? ora_cospi(v[i]) : kind == 1 ? ora_sinpi(v[i]) : ora_tanpi(v[i]);
+}
+
+static double uniform24(uint32_t x) { return (double)(2u * (x >> 9) + 1u) * 0x1p-24; }
+
+/* element e (0..3) of the block of four words w under law `dist` (0 Laplace,
+ * 1 Gaussian, 2 Cauchy, 3 Student-t(2)), before the VMC scale */
+ORA_API float ora_aux(const uint32_t w[4], int e, int dist) {
+    if (dist == 0) return ora_laplace(w[e]);
+    if (dist == 1) {
+        double u1 = uniform24(w[e & 2]), u2 = uniform24(w[(e & 2) | 1]);
+        float L = (float)log(u1);
+        float S = sqrtf(-2.0f * L);
+        float C = (float)((e & 1) ? ora_sinpi(2.0 * u2) : ora_cospi(2.0 * u2));
+        return S * C;
+    }
+    double v = uniform24(w[e]) - 0.5; /* exact */
+    if (dist == 2) return (float)ora_tanpi(v);
+    double u = uniform24(w[e]);
+    return (float)((2.0 * u - 1.0) / sqrt(2.0 * u * (1.0 - u)));
+}
+
+ORA_API void ora_aux_batch(int64_t blocks, const uint32_t* words, int dist, float* out) {
+    for (int64_t t = 0; t < blocks; ++t)
+        for (int e = 0; e < 4; ++e) out[4 * t + e] = ora_aux(words + 4 * t, e, dist);
+}
+
 /* R*_ij = c_i * L_ij  (VMC: R* = r^alpha R with c_i = r_i^alpha passed in). */
 ORA_API void ora_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* r_out) {
 #pragma omp parallel for schedule(static)
@@ -132,6 +204,24 @@ ORA_API void ora_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, c
             uint64_t q = (uint64_t)i * (uint64_t)n + (uint64_t)j;
             float L = ora_laplace(element_word(seed, layer_id, q));
             r_out[i * n + j] = c[i] * L;
+        }
+    }
+}
+
+/* Rows [row0, row0 + rows) of R* under law `dist`: the element's whole Philox block
+ * (the Gaussian pairs two of its words). */
+ORA_API void ora_gen_r_dist(int64_t row0, int64_t rows, int64_t n, uint64_t seed, uint32_t layer_id, int dist,
+                            const float* c, float* r_out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t ii = 0; ii < rows; ++ii) {
+        int64_t i = row0 + ii;
+        for (int64_t j = 0; j < n; ++j) {
+            uint64_t q = (uint64_t)i * (uint64_t)n + (uint64_t)j;
+            uint32_t ctr[4] = {(uint32_t)(q >> 2), (uint32_t)(q >> 34), layer_id, 0u};
+            uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+            uint32_t w[4];
+            ora_philox4x32_10(ctr, key, w);
+            r_out[ii * n + j] = c[ii] * ora_aux(w, (int)(q & 3), dist);
         }
     }
 }
@@ -174,6 +264,16 @@ ORA_API void ora_sigma_w(int64_t d, int64_t n, const float* W, float* sigma_out)
 
 ORA_API void ora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_out) {
     for (int64_t i = 0; i < d; ++i) c_out[i] = (float)pow((double)sigma_w[i] / sqrt(2.0), alpha);
+}
+
+/* sigma_R = 1 for the other laws: the Gaussian's standard deviation, and the unit scale
+ * of the Cauchy and Student-t(2) laws, whose variance is not finite (a reading). */
+ORA_API void ora_vmc_scale_dist(int64_t d, const float* sigma_w, double alpha, int dist, float* c_out) {
+    if (dist == 0) {
+        ora_vmc_scale(d, sigma_w, alpha, c_out);
+        return;
+    }
+    for (int64_t i = 0; i < d; ++i) c_out[i] = (float)pow((double)sigma_w[i], alpha);
 }
 
 /* ------------------------------------------------------------------------- */
