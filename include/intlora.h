@@ -81,16 +81,26 @@ enum {
   INTLORA_OP_STE_BACKWARD = 7
 };
 
+/* Auxiliary-matrix distributions (the pages' IntLoRA ablation on the law of R, summary
+ * table "Measured effects": Laplace against Gaussian, Cauchy and Student-t samples).
+ * Laplace is the method's choice and the default (0). */
+enum {
+  INTLORA_AUX_LAPLACE = 0,   /* Laplace(0, 1)                                                  */
+  INTLORA_AUX_GAUSS = 1,     /* N(0, 1), Box-Muller                                            */
+  INTLORA_AUX_CAUCHY = 2,    /* Cauchy(0, 1)                                                   */
+  INTLORA_AUX_STUDENT_T2 = 3 /* Student-t with 2 degrees of freedom                            */
+};
+
 /* One pretrained layer.  r is the LoRA rank (1..128); w_bits the base code width
- * (4 or 8); (seed, layer_id) select the auxiliary-matrix stream. */
+ * (4 or 8); (seed, layer_id) select the auxiliary-matrix stream and aux_dist its law. */
 typedef struct intlora_desc {
-  int64_t d;         /* out_features (rows)          */
-  int64_t n;         /* in_features (columns)        */
-  int32_t r;         /* LoRA rank                    */
-  int32_t w_bits;    /* 4 or 8                       */
-  uint64_t seed;     /* Philox key                   */
-  uint32_t layer_id; /* Philox counter word 2        */
-  uint32_t reserved; /* must be 0                    */
+  int64_t d;         /* out_features (rows)                             */
+  int64_t n;         /* in_features (columns)                           */
+  int32_t r;         /* LoRA rank                                       */
+  int32_t w_bits;    /* 4 or 8                                          */
+  uint64_t seed;     /* Philox key                                      */
+  uint32_t layer_id; /* Philox counter word 2                           */
+  uint32_t aux_dist; /* INTLORA_AUX_*; other values give INTLORA_EINVAL */
 } intlora_desc;
 
 /* Stored state of a quantized base layer (AQS: Q[W - R*] with R* regenerated). */
@@ -125,7 +135,14 @@ size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M);
  *   L = -sign(v) ln(1 - 2|v|), v = u - 1/2, u = (2 floor(x / 2^9) + 1) 2^-24,
  *   x = word (q & 3) of Philox4x32-10 with counter (q >> 2 [64 bits], layer_id, 0)
  *   and key (seed low, seed high), q = i*n + j.  ln is correctly rounded to binary32,
- *   R* = RN32(c_i * L).  r_out: d x n fp32.  Uses desc->d, n, seed, layer_id. */
+ *   R* = RN32(c_i * L).  r_out: d x n fp32.  Uses desc->d, n, seed, layer_id, aux_dist.
+ * The other laws (desc->aux_dist) take the same u of each element; every step below is
+ * one binary32 rounding of the exact value (ln, cos, sin, tan correctly rounded):
+ *   Gaussian: Box-Muller within word pairs (0, 1) and (2, 3) of the block: with u1 from
+ *     the pair's first word and u2 from its second, S = sqrt(-2 ln u1), element 2p gets
+ *     S cos(2 pi u2) and element 2p + 1 gets S sin(2 pi u2);
+ *   Cauchy: tan(pi (u - 1/2));
+ *   Student-t(2): (2u - 1) / sqrt(2u (1 - u)), its inverse distribution function. */
 int intlora_gen_r(const intlora_desc* desc, const float* vmc_c, float* r_out, void* stream);
 
 /* Per-row statistics.
@@ -142,6 +159,12 @@ int intlora_stats(const intlora_desc* desc, int mode, const float* W, const intl
 /* VMC scale (section "3. VMC"): c_out[i] = RN32((sigma_w[i] / sqrt(2))^alpha); sigma_R =
  * sqrt(2) is the standard deviation of the unit Laplace law.  alpha in [0, 8]. */
 int intlora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_out, void* stream);
+
+/* The same for the auxiliary law aux_dist: sigma_R = sqrt(2) for Laplace, 1 for the
+ * others (the Gaussian's standard deviation; the unit scale of the Cauchy and Student-t(2)
+ * laws, which have no finite variance).  INTLORA_EINVAL for an unknown law. */
+int intlora_vmc_scale_dist(int64_t d, const float* sigma_w, double alpha, uint32_t aux_dist, float* c_out,
+                           void* stream);
 
 /* Base quantization Q[W - R*] (section "1. AQS"), per row, asymmetric with a range
  * that always contains 0:  x = W - R*, lo = min(0, min x), hi = max(0, max x),
@@ -282,6 +305,11 @@ int intlora_linear_fwd_codes(int64_t M, int64_t d, int64_t n, const int8_t* xq, 
  * odd G in [1, 2^23) (the only values it is ever given): out[t] = RN32(ln(G[t] 2^-23)).
  * Inputs outside that set give unspecified values. */
 int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream);
+
+/* Diagnostic: the unscaled auxiliary sample (c = 1) of each element of `blocks` given
+ * Philox output blocks words[4 t .. 4 t + 3] under law aux_dist: out[4 t + e] is what
+ * intlora_gen_r computes for element e of a block with those words.  Device pointers. */
+int intlora_debug_aux(int64_t blocks, const uint32_t* words, uint32_t aux_dist, float* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libintlora.so")
 INTLORA_OK, INTLORA_EINVAL, INTLORA_ESHAPE, INTLORA_EALIGN, INTLORA_EWORKSPACE, INTLORA_EDEVICE, INTLORA_ELAUNCH = range(7)
 INTLORA_SIGMA_W, INTLORA_U_MINMAX = 0, 1
 INTLORA_W_INT4, INTLORA_W_INT8, INTLORA_W_INT16 = 4, 8, 16
+INTLORA_AUX_LAPLACE, INTLORA_AUX_GAUSS, INTLORA_AUX_CAUCHY, INTLORA_AUX_STUDENT_T2 = 0, 1, 2, 3
 INTLORA_OP_STATS_UMINMAX, INTLORA_OP_MERGE_MUL, INTLORA_OP_MERGE_SHIFT, INTLORA_OP_LINEAR, INTLORA_OP_BASE_QUANT = 1, 2, 3, 4, 5
 INTLORA_OP_MERGE_PTQ, INTLORA_OP_STE_BACKWARD = 6, 7
 
@@ -29,7 +30,7 @@ class IntLoraError(RuntimeError):
 
 class Desc(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int64), ("n", ctypes.c_int64), ("r", ctypes.c_int32), ("w_bits", ctypes.c_int32),
-                ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+                ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_uint32), ("aux_dist", ctypes.c_uint32)]
 
 
 class Base(ctypes.Structure):
@@ -55,6 +56,7 @@ _SIG = {
     "intlora_stats": (_INT, [ctypes.POINTER(Desc), _INT, _P, ctypes.POINTER(Base), ctypes.POINTER(Lora), _P, _P, _P,
                              ctypes.c_size_t, _P]),
     "intlora_vmc_scale": (_INT, [_I64, _P, ctypes.c_double, _P, _P]),
+    "intlora_vmc_scale_dist": (_INT, [_I64, _P, ctypes.c_double, ctypes.c_uint32, _P, _P]),
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -71,6 +73,7 @@ _SIG = {
     "intlora_linear_fwd": (_INT, [_I64, _I64, _I64, _P, _P, _P, _INT, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_linear_fwd_codes": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "intlora_debug_ln": (_INT, [_I64, _P, _P, _P]),
+    "intlora_debug_aux": (_INT, [_I64, _P, ctypes.c_uint32, _P, _P]),
 }
 
 
@@ -116,8 +119,8 @@ def _check(status: int, where: str):
         raise IntLoraError(status, where, detail or lib().intlora_status_string(status).decode())
 
 
-def desc(d: int, n: int, r: int, w_bits: int, seed: int = 0, layer_id: int = 0) -> Desc:
-    return Desc(d, n, r, w_bits, seed, layer_id, 0)
+def desc(d: int, n: int, r: int, w_bits: int, seed: int = 0, layer_id: int = 0, aux_dist: int = 0) -> Desc:
+    return Desc(d, n, r, w_bits, seed, layer_id, aux_dist)
 
 
 def base(w_round, z, s, vmc_c) -> Base:
@@ -151,6 +154,11 @@ def intlora_stats(dsc: Desc, mode: int, W=None, bs: Base | None = None, lr: Lora
 def intlora_vmc_scale(d: int, sigma_w, alpha: float, c_out, stream=None):
     _check(lib().intlora_vmc_scale(d, _ptr(sigma_w), float(alpha), _ptr(c_out), _stream(stream)),
            "intlora_vmc_scale")
+
+
+def intlora_vmc_scale_dist(d: int, sigma_w, alpha: float, aux_dist: int, c_out, stream=None):
+    _check(lib().intlora_vmc_scale_dist(d, _ptr(sigma_w), float(alpha), aux_dist, _ptr(c_out), _stream(stream)),
+           "intlora_vmc_scale_dist")
 
 
 def intlora_base_quant(dsc: Desc, W, vmc_c, w_round_out, z_out, s_out, stream=None):
@@ -222,3 +230,7 @@ def intlora_linear_fwd_codes(M: int, d: int, n: int, xq, s_x, u_code, w_round, z
 
 def intlora_debug_ln(count: int, G, out, stream=None):
     _check(lib().intlora_debug_ln(count, _ptr(G), _ptr(out), _stream(stream)), "intlora_debug_ln")
+
+
+def intlora_debug_aux(blocks: int, words, aux_dist: int, out, stream=None):
+    _check(lib().intlora_debug_aux(blocks, _ptr(words), aux_dist, _ptr(out), _stream(stream)), "intlora_debug_aux")

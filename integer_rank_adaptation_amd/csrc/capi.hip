@@ -51,7 +51,8 @@ int check_desc(const intlora_desc* d, bool need_rank) {
   if (!d) return fail(INTLORA_EINVAL, "desc is NULL");
   if (d->w_bits != 4 && d->w_bits != 8) return fail(INTLORA_EINVAL, "w_bits must be 4 or 8 (got %d)", d->w_bits);
   if (need_rank && (d->r < 1 || d->r > 128)) return fail(INTLORA_EINVAL, "rank r must be in [1, 128] (got %d)", d->r);
-  if (d->reserved != 0) return fail(INTLORA_EINVAL, "desc.reserved must be 0");
+  if (d->aux_dist > INTLORA_AUX_STUDENT_T2)
+    return fail(INTLORA_EINVAL, "desc.aux_dist must be 0..3 (got %u)", d->aux_dist);
   if (d->d < 0 || d->n < 1 || d->d >= kMaxDim || d->n >= kMaxDim)
     return fail(INTLORA_ESHAPE, "bad shape d=%lld n=%lld", (long long)d->d, (long long)d->n);
   if (d->w_bits == 4 && (d->n & 1)) return fail(INTLORA_ESHAPE, "4-bit codes need an even n (got %lld)", (long long)d->n);
@@ -136,6 +137,7 @@ int run_adapt(const intlora_desc* desc, const intlora_base* base, const intlora_
   a.sat_zero = sat_zero;
   a.ptq = ptq;
   a.force_generic = false;
+  a.dist = (int)desc->aux_dist;
   return launch_status(intlora::launch_adapt(a, &w.ntiles, st), "adaptation kernel");
 }
 
@@ -165,7 +167,7 @@ const char* intlora_status_string(int status) {
 
 const char* intlora_last_error(void) { return g_err; }
 
-int intlora_version(void) { return 102; }
+int intlora_version(void) { return 103; }
 
 size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
   (void)M;
@@ -190,7 +192,7 @@ int intlora_gen_r(const intlora_desc* desc, const float* vmc_c, float* r_out, vo
   if ((s = check_ptrs({vmc_c, r_out}, "gen_r"))) return s;
   if ((s = ensure_device())) return s;
   return launch_status(intlora::launch_gen_r(desc->d, desc->n, desc->seed, desc->layer_id, vmc_c, r_out,
-                                             static_cast<hipStream_t>(stream)),
+                                             (int)desc->aux_dist, static_cast<hipStream_t>(stream)),
                        "gen_r");
 }
 
@@ -228,8 +230,23 @@ int intlora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_ou
   int s = check_ptrs({sigma_w, c_out}, "vmc_scale");
   if (s) return s;
   if ((s = ensure_device())) return s;
-  return launch_status(intlora::launch_vmc_scale(d, sigma_w, alpha, c_out, static_cast<hipStream_t>(stream)),
+  return launch_status(intlora::launch_vmc_scale(d, sigma_w, alpha, c_out, INTLORA_AUX_LAPLACE,
+                                                 static_cast<hipStream_t>(stream)),
                        "vmc_scale");
+}
+
+int intlora_vmc_scale_dist(int64_t d, const float* sigma_w, double alpha, uint32_t aux_dist, float* c_out,
+                           void* stream) {
+  if (d < 0) return fail(INTLORA_ESHAPE, "d < 0");
+  if (!(alpha >= 0.0 && alpha <= 8.0)) return fail(INTLORA_EINVAL, "alpha must be in [0, 8]");
+  if (aux_dist > INTLORA_AUX_STUDENT_T2) return fail(INTLORA_EINVAL, "aux_dist must be 0..3 (got %u)", aux_dist);
+  if (d == 0) return ok();
+  int s = check_ptrs({sigma_w, c_out}, "vmc_scale_dist");
+  if (s) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_vmc_scale(d, sigma_w, alpha, c_out, (int)aux_dist,
+                                                 static_cast<hipStream_t>(stream)),
+                       "vmc_scale_dist");
 }
 
 int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vmc_c, void* w_round_out,
@@ -241,7 +258,7 @@ int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vm
   if ((s = check_ptrs({W, vmc_c, w_round_out, z_out, s_out}, "base_quant"))) return s;
   if ((s = ensure_device())) return s;
   return launch_status(intlora::launch_base_quant(desc->d, desc->n, desc->w_bits, desc->seed, desc->layer_id, W, vmc_c,
-                                                  static_cast<uint8_t*>(w_round_out), z_out, s_out,
+                                                  static_cast<uint8_t*>(w_round_out), z_out, s_out, (int)desc->aux_dist,
                                                   static_cast<hipStream_t>(stream)),
                        "base_quant");
 }
@@ -307,6 +324,7 @@ int intlora_merge_mul_fused(const intlora_desc* desc, const intlora_base* base, 
   a.sat_zero = nullptr;
   a.ptq = false;
   a.force_generic = false;
+  a.dist = (int)desc->aux_dist;
   return launch_status(intlora::launch_merge_fused(a, u_bits, m, s_bar, z_bar, m_split, u_round_dbg, sat_count,
                                                    static_cast<hipStream_t>(stream)),
                        "merge_mul_fused");
@@ -458,6 +476,17 @@ int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream)
   if (s) return s;
   if ((s = ensure_device())) return s;
   return launch_status(intlora::launch_ln_odd(count, G, out, static_cast<hipStream_t>(stream)), "debug_ln");
+}
+
+int intlora_debug_aux(int64_t blocks, const uint32_t* words, uint32_t aux_dist, float* out, void* stream) {
+  if (blocks < 0) return fail(INTLORA_ESHAPE, "blocks < 0");
+  if (aux_dist > INTLORA_AUX_STUDENT_T2) return fail(INTLORA_EINVAL, "aux_dist must be 0..3 (got %u)", aux_dist);
+  if (blocks == 0) return ok();
+  int s = check_ptrs({words, out}, "debug_aux");
+  if (s) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_aux_debug(blocks, words, (int)aux_dist, out, static_cast<hipStream_t>(stream)),
+                       "debug_aux");
 }
 
 }  // extern "C"

@@ -83,11 +83,13 @@ __device__ __forceinline__ LnLds ln_lds_entry(const LnEntry& e) {
   return LnLds{e.neg_ln_r_hi, (double)e.neg_ln_r_lo, (double)e.r * 0x1p-24};
 }
 
-__device__ __forceinline__ float ln_odd_g(uint32_t G, const LnLds* __restrict__ tab) {
+// ln(G 2^-bias) for odd G < 2^bias, bias 23 or 24, as the binary64 value before the
+// final rounding (the Gaussian sampler takes its logarithm at bias 24).
+__device__ __forceinline__ double ln_odd_d(uint32_t G, int bias, const LnLds* __restrict__ tab) {
   // leading-bit position p (0..22); m24 = G << (23 - p) in [2^23, 2^24)
   const int p = 31 - __clz(G);
   uint32_t m24 = G << (23 - p);
-  int e = p - 23;                  // g = (m24 * 2^-23) * 2^e
+  int e = p - bias;                // g = (m24 * 2^-23) * 2^e
   uint32_t F;                      // m * 2^24 as an integer, m in [0.75, 1.5)
   if (m24 >= 0xC00000u) {          // m >= 1.5: halve
     F = m24;                       // (m/2) * 2^24 = m24
@@ -113,8 +115,11 @@ __device__ __forceinline__ float ln_odd_g(uint32_t G, const LnLds* __restrict__ 
   const double ed = (double)e;
   const double head = fma(ed, LN2_HI, t.hi);
   const double tail = fma(ed, LN2_LO, t.lo);
-  const double res = head + (lp + tail);
-  return (float)res;
+  return head + (lp + tail);
+}
+
+__device__ __forceinline__ float ln_odd_g(uint32_t G, const LnLds* __restrict__ tab) {
+  return (float)ln_odd_d(G, 23, tab);
 }
 
 // Laplace(0, 1) sample from one word: u = (2 floor(x / 2^9) + 1) 2^-24, v = u - 1/2,
@@ -126,6 +131,96 @@ __device__ __forceinline__ float laplace_from_word(uint32_t x, const LnLds* __re
   const uint32_t G = (uint32_t)((1 << 23) - (N < 0 ? -N : N));
   const float lg = ln_odd_g(G, tab);
   return (N < 0) ? lg : -lg;
+}
+
+// --------------------------------------------------------------------------------
+// Other auxiliary-matrix distributions (the ablation that swaps Laplace for a Gaussian,
+// a Cauchy or a Student-t sample).  Every one is built from the same uniform as the
+// Laplace sampler, u = (2 floor(x / 2^9) + 1) 2^-24, and every transcendental step is
+// rounded once from a binary64 value accurate to a few units of 2^-53; exhaustive
+// device checks over each input domain show that each rounding is the correct one.
+// --------------------------------------------------------------------------------
+enum { kAuxLaplace = 0, kAuxGauss = 1, kAuxCauchy = 2, kAuxStudentT2 = 3 };
+
+// sin(pi x) and cos(pi x) for 0 <= x <= 1/4: Taylor polynomials in y = pi x (the
+// first omitted terms are below 2^-53 of the result on this interval).
+__device__ __forceinline__ double sinpi_q(double x) {
+  const double y = x * 3.141592653589793, y2 = y * y;
+  double p = -1.0 / 1307674368000.0;  // -1/15!
+  p = fma(p, y2, 1.0 / 6227020800.0);
+  p = fma(p, y2, -1.0 / 39916800.0);
+  p = fma(p, y2, 1.0 / 362880.0);
+  p = fma(p, y2, -1.0 / 5040.0);
+  p = fma(p, y2, 1.0 / 120.0);
+  p = fma(p, y2, -1.0 / 6.0);
+  return fma(y * y2, p, y);
+}
+__device__ __forceinline__ double cospi_q(double x) {
+  const double y = x * 3.141592653589793, y2 = y * y;
+  double p = 1.0 / 20922789888000.0;  // 1/16!
+  p = fma(p, y2, -1.0 / 87178291200.0);
+  p = fma(p, y2, 1.0 / 479001600.0);
+  p = fma(p, y2, -1.0 / 3628800.0);
+  p = fma(p, y2, 1.0 / 40320.0);
+  p = fma(p, y2, -1.0 / 720.0);
+  p = fma(p, y2, 1.0 / 24.0);
+  p = fma(p, y2, -0.5);
+  return fma(y2, p, 1.0);
+}
+// cos(pi v) and sin(pi v) for 0 < v < 2 with at most 24 significant bits: the
+// reductions (2 - v, 1 - a, 1/2 - a) are exact.
+__device__ __forceinline__ double cospi_v(double v) {
+  double a = v > 1.0 ? 2.0 - v : v;
+  const bool neg = a > 0.5;
+  if (neg) a = 1.0 - a;
+  const double r = a <= 0.25 ? cospi_q(a) : sinpi_q(0.5 - a);
+  return neg ? -r : r;
+}
+__device__ __forceinline__ double sinpi_v(double v) {
+  const bool neg = v > 1.0;
+  double a = neg ? v - 1.0 : v;
+  if (a > 0.5) a = 1.0 - a;
+  const double r = a <= 0.25 ? sinpi_q(a) : cospi_q(0.5 - a);
+  return neg ? -r : r;
+}
+// tan(pi v) for |v| < 1/2 (exact reduction to [0, 1/4] through cot(pi (1/2 - a))).
+__device__ __forceinline__ double tanpi_h(double v) {
+  const double a = fabs(v);
+  const double r = a <= 0.25 ? sinpi_q(a) / cospi_q(a) : cospi_q(0.5 - a) / sinpi_q(0.5 - a);
+  return v < 0.0 ? -r : r;
+}
+
+// Element e (0..3) of a Philox block under distribution DIST.
+//  Gaussian: Box-Muller over the word pairs (0, 1) and (2, 3); u1 from the first word
+//    of the pair and u2 from the second; element 2p gets S cos(2 pi u2), element 2p + 1
+//    S sin(2 pi u2), S = sqrt(-2 L), L = RN32(ln u1); each step rounded to binary32.
+//  Cauchy: tan(pi (u - 1/2)).
+//  Student-t with 2 degrees of freedom: its inverse distribution function,
+//    (2u - 1) / sqrt(2u(1 - u)) = 2N / sqrt(2^47 - 2N^2) with u - 1/2 = N 2^-24.
+template <int DIST>
+__device__ __forceinline__ float aux_sample(const U4& rnd, unsigned e, const LnLds* __restrict__ tab) {
+  if (DIST == kAuxLaplace) return laplace_from_word(pick_word(rnd, e), tab);
+  if (DIST == kAuxGauss) {
+    const uint32_t w1 = pick_word(rnd, e & 2u), w2 = pick_word(rnd, (e & 2u) | 1u);
+    const float L = (float)ln_odd_d(2u * (w1 >> 9) + 1u, 24, tab);
+    const float S = sqrtf(-2.0f * L);
+    const double v = (double)(2u * (w2 >> 9) + 1u) * 0x1p-23;  // 2 u2, exact
+    const float C = (float)((e & 1u) ? sinpi_v(v) : cospi_v(v));
+    return S * C;
+  }
+  const int32_t N = 2 * (int32_t)(pick_word(rnd, e) >> 9) + 1 - (1 << 23);  // u - 1/2 = N 2^-24
+  if (DIST == kAuxCauchy) return (float)tanpi_h((double)N * 0x1p-24);
+  const int64_t D = ((int64_t)1 << 47) - 2 * (int64_t)N * (int64_t)N;  // exact, 2^25 - 2 <= D < 2^47
+  return (float)(2.0 * (double)N / sqrt((double)D));
+}
+
+__device__ __forceinline__ float aux_sample_rt(int dist, const U4& rnd, unsigned e, const LnLds* __restrict__ tab) {
+  switch (dist) {
+    case kAuxGauss: return aux_sample<kAuxGauss>(rnd, e, tab);
+    case kAuxCauchy: return aux_sample<kAuxCauchy>(rnd, e, tab);
+    case kAuxStudentT2: return aux_sample<kAuxStudentT2>(rnd, e, tab);
+    default: return aux_sample<kAuxLaplace>(rnd, e, tab);
+  }
 }
 
 // --------------------------------------------------------------------------------

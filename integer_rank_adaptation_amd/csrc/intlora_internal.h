@@ -23,6 +23,7 @@ struct AdaptArgs {
   unsigned long long* sat_zero;  // zeroed by the adaptation kernel (nullable)
   bool ptq;                      // x = (s w + R*) + AB for every element (comparison path) instead of U
   bool force_generic;
+  int dist;                      // auxiliary-matrix distribution (kAuxLaplace ... kAuxStudentT2)
 };
 
 // Fused single-pass MUL merge (no scratch); hipErrorInvalidValue for n > 16384.
@@ -33,13 +34,14 @@ hipError_t launch_merge_fused(const AdaptArgs& a, int u_bits, int16_t* m, float*
 // workspace of row partials).
 int adapt_max_ntiles(int64_t n);
 
-hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out,
+hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out, int dist,
                         hipStream_t st);
 hipError_t launch_ln_odd(int64_t count, const uint32_t* G, float* out, hipStream_t st);
+hipError_t launch_aux_debug(int64_t blocks, const uint32_t* words, int dist, float* out, hipStream_t st);
 hipError_t launch_sigma_w(int64_t d, int64_t n, const float* W, float* sigma, hipStream_t st);
-hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, hipStream_t st);
+hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, int dist, hipStream_t st);
 hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint32_t layer_id, const float* W,
-                             const float* c, uint8_t* wround, int32_t* z, float* s, hipStream_t st);
+                             const float* c, uint8_t* wround, int32_t* z, float* s, int dist, hipStream_t st);
 hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* sx, int32_t* rowsum,
                             hipStream_t st);
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st);

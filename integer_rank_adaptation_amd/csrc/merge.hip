@@ -28,17 +28,18 @@ __device__ __forceinline__ void load_ln_table(LnLds* dst) {
 
 // R*_ij for one element (general path).
 __device__ __forceinline__ float rstar_element(uint64_t q, float ci, uint32_t layer_id, uint64_t seed,
-                                               const LnLds* tab) {
+                                               const LnLds* tab, int dist) {
   const U4 blk = philox_block(q >> 2, layer_id, seed);
-  return ci * laplace_from_word(pick_word(blk, (unsigned)(q & 3)), tab);
+  return ci * aux_sample_rt(dist, blk, (unsigned)(q & 3), tab);
 }
 
 // ---------------------------------------------------------------------------------
-// K1: R*_ij = c_i * Laplace(Philox(seed, layer, i*n + j)); one thread per counter
-// block of four consecutive linear elements.
+// K1: R*_ij = c_i * Laplace(Philox(seed, layer, i*n + j)) (or another distribution of
+// the sampler ablation); one thread per counter block of four consecutive linear
+// elements.
 // ---------------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
-                                              const float* __restrict__ c, float* __restrict__ out) {
+                                              const float* __restrict__ c, float* __restrict__ out, int dist) {
   __shared__ LnLds tab[96];
   load_ln_table(tab);
   __syncthreads();
@@ -54,7 +55,7 @@ __global__ __launch_bounds__(256) void k_gen_r(int64_t d, int64_t n, uint64_t se
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       if (q0 + e < total) {
-        r[e] = c[i] * laplace_from_word(pick_word(v, e), tab);
+        r[e] = c[i] * aux_sample_rt(dist, v, (unsigned)e, tab);
       }
       if (++j == (uint64_t)n) {
         j = 0;
@@ -119,10 +120,12 @@ __global__ __launch_bounds__(256) void k_sigma_w(int64_t n, const float* __restr
 }
 
 // VMC scale c_i = RN32((sigma_W,i / sqrt 2)^alpha) (sigma_R = sqrt 2 for unit Laplace).
+// sigma_R = sqrt(2) for Laplace(0, 1); 1 (the standard deviation of the Gaussian, the
+// scale of the Cauchy and Student-t samples) for the other distributions.
 __global__ __launch_bounds__(256) void k_vmc_scale(int64_t d, const float* __restrict__ sigma, double alpha,
-                                                  float* __restrict__ c) {
+                                                  float* __restrict__ c, bool unit_sigma_r) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < d) c[i] = (float)pow((double)sigma[i] / sqrt(2.0), alpha);
+  if (i < d) c[i] = (float)pow(unit_sigma_r ? (double)sigma[i] : (double)sigma[i] / sqrt(2.0), alpha);
 }
 
 // ---------------------------------------------------------------------------------
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(256) void k_vmc_scale(int64_t d, const float* __res
 __global__ __launch_bounds__(256) void k_base_quant(int64_t n, int bits, uint64_t seed, uint32_t layer_id,
                                                    const float* __restrict__ W, const float* __restrict__ c,
                                                    uint8_t* __restrict__ wround, int32_t* __restrict__ z_out,
-                                                   float* __restrict__ s_out) {
+                                                   float* __restrict__ s_out, int dist) {
   extern __shared__ float xs[];  // n floats
   __shared__ LnLds tab[96];
   __shared__ float red[4];
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256) void k_base_quant(int64_t n, int bits, uint64_
   const float ci = c[i];
   float lo = 0.0f, hi = 0.0f;
   for (int64_t j = threadIdx.x; j < n; j += 256) {
-    const float r = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab);
+    const float r = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab, dist);
     const float x = W[i * n + j] - r;
     xs[j] = x;
     lo = fminf(lo, x);
@@ -263,7 +266,7 @@ constexpr int kMfmaMaxRowTiles = 8;
 
 // PTQ (the QLoRA-style comparison path): x = (s w + R*) + AB for every element instead
 // of U, with no division and no excluded elements.
-template <int R, bool W4, bool PTQ>
+template <int R, bool W4, bool PTQ, int DIST>
 __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
                                                     const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
                                                     const float* __restrict__ s, const float* __restrict__ c,
@@ -348,14 +351,14 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
         if (PTQ) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
+            const float rs = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
             q[e] = (si * (float)w[e] + rs) + acc[4 * g + e];  // binary32 steps in this order
           }
         } else {
           bool slow = false;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float rs = ci * laplace_from_word(pick_word(rnd, e), tab);
+            const float rs = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
             t[e] = rs + acc[4 * g + e];
             q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
             slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
@@ -408,7 +411,7 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
                                                       const float* __restrict__ c, const float* __restrict__ A,
                                                       const float* __restrict__ B, float* __restrict__ U,
                                                       int* __restrict__ pmin, int* __restrict__ pmax, int ntiles,
-                                                      unsigned long long* __restrict__ sat_zero, bool ptq) {
+                                                      unsigned long long* __restrict__ sat_zero, bool ptq, int dist) {
   __shared__ LnLds tab[96];
   __shared__ int smin[4], smax[4];
   load_ln_table(tab);
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
     const int w = code - z[i];
     float acc = 0.0f;
     for (int k = 0; k < r; ++k) acc = fmaf(A[i * r + k], B[(int64_t)k * n + j], acc);
-    const float rs = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, c[i], layer_id, seed, tab);
+    const float rs = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, c[i], layer_id, seed, tab, dist);
     const float t = rs + acc;
     const bool valid = ptq || w != 0;
     const float q = t / (float)(w != 0 ? w : 1);
@@ -958,10 +961,29 @@ static inline unsigned grid1(uint64_t work, unsigned block) {
   return (unsigned)(g ? g : 1);
 }
 
-hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out,
+hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out, int dist,
                         hipStream_t st) {
   const uint64_t blocks4 = ((uint64_t)d * (uint64_t)n + 3) / 4;
-  hipLaunchKernelGGL(k_gen_r, dim3(grid1(blocks4, 256)), dim3(256), 0, st, d, n, seed, layer_id, c, out);
+  hipLaunchKernelGGL(k_gen_r, dim3(grid1(blocks4, 256)), dim3(256), 0, st, d, n, seed, layer_id, c, out, dist);
+  return hipGetLastError();
+}
+
+// Debug: the auxiliary sample of each element of `blocks` given Philox blocks (4 words
+// each) under distribution `dist`.
+__global__ __launch_bounds__(256) void k_aux_debug(int64_t blocks, const uint32_t* __restrict__ words, int dist,
+                                                  float* __restrict__ out) {
+  __shared__ LnLds tab[96];
+  load_ln_table(tab);
+  __syncthreads();
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < blocks; t += (int64_t)gridDim.x * blockDim.x) {
+    const U4 v{words[4 * t], words[4 * t + 1], words[4 * t + 2], words[4 * t + 3]};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[4 * t + e] = aux_sample_rt(dist, v, (unsigned)e, tab);
+  }
+}
+
+hipError_t launch_aux_debug(int64_t blocks, const uint32_t* words, int dist, float* out, hipStream_t st) {
+  hipLaunchKernelGGL(k_aux_debug, dim3(grid1((uint64_t)blocks, 256)), dim3(256), 0, st, blocks, words, dist, out);
   return hipGetLastError();
 }
 
@@ -975,13 +997,14 @@ hipError_t launch_sigma_w(int64_t d, int64_t n, const float* W, float* sigma, hi
   return hipGetLastError();
 }
 
-hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, hipStream_t st) {
-  hipLaunchKernelGGL(k_vmc_scale, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, sigma, alpha, c);
+hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, int dist, hipStream_t st) {
+  hipLaunchKernelGGL(k_vmc_scale, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, sigma, alpha, c,
+                     dist != kAuxLaplace);
   return hipGetLastError();
 }
 
 hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint32_t layer_id, const float* W,
-                             const float* c, uint8_t* wround, int32_t* z, float* s, hipStream_t st) {
+                             const float* c, uint8_t* wround, int32_t* z, float* s, int dist, hipStream_t st) {
   const size_t lds = (size_t)n * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
@@ -990,7 +1013,8 @@ hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipLaunchKernelGGL(k_base_quant, dim3((unsigned)d), dim3(256), lds, st, n, bits, seed, layer_id, W, c, wround, z, s);
+  hipLaunchKernelGGL(k_base_quant, dim3((unsigned)d), dim3(256), lds, st, n, bits, seed, layer_id, W, c, wround, z, s,
+                     dist);
   return hipGetLastError();
 }
 
@@ -1002,14 +1026,14 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
 
 int adapt_max_ntiles(int64_t n) { return (int)((n + kMfmaCols - 1) / kMfmaCols); }
 
-template <int R, bool W4, bool PTQ>
+template <int R, bool W4, bool PTQ, int DIST>
 static int64_t mfma_slots() {
   static int64_t slots = 0;
   if (slots == 0) {
     int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_mfma<R, W4, PTQ>), 256,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_adapt_mfma<R, W4, PTQ, DIST>), 256,
                                                      0) != hipSuccess ||
         cus <= 0 || per_cu <= 0)
       return 1024;
@@ -1018,12 +1042,12 @@ static int64_t mfma_slots() {
   return slots;
 }
 
-template <int R, bool W4, bool PTQ>
+template <int R, bool W4, bool PTQ, int DIST>
 static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   const int ntiles = (int)((a.n + kMfmaCols - 1) / kMfmaCols);
   *ntiles_out = ntiles;
   const int64_t row_tiles = (a.d + 31) / 32;
-  const int64_t slots = mfma_slots<R, W4, PTQ>();
+  const int64_t slots = mfma_slots<R, W4, PTQ, DIST>();
   // row tiles per block (1..8): the count whose grid best fills the resident slots
   int rtiles = 1;
   double best = -1.0;
@@ -1041,19 +1065,29 @@ static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStre
     const int64_t cnt = nrb - rb0 < 65535 ? nrb - rb0 : 65535;
     const dim3 grid((unsigned)ntiles, (unsigned)cnt);
     unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
-    hipLaunchKernelGGL((k_adapt_mfma<R, W4, PTQ>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround, a.z,
+    hipLaunchKernelGGL((k_adapt_mfma<R, W4, PTQ, DIST>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround, a.z,
                        a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rtiles, rb0, sz);
   }
   return hipGetLastError();
 }
 
+template <int R, int DIST>
+static hipError_t launch_adapt_md(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
+  if (a.ptq)
+    return a.w_bits == 4 ? launch_adapt_mfma<R, true, true, DIST>(a, ntiles_out, st)
+                         : launch_adapt_mfma<R, false, true, DIST>(a, ntiles_out, st);
+  return a.w_bits == 4 ? launch_adapt_mfma<R, true, false, DIST>(a, ntiles_out, st)
+                       : launch_adapt_mfma<R, false, false, DIST>(a, ntiles_out, st);
+}
+
 template <int R>
 static hipError_t launch_adapt_m(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
-  if (a.ptq)
-    return a.w_bits == 4 ? launch_adapt_mfma<R, true, true>(a, ntiles_out, st)
-                         : launch_adapt_mfma<R, false, true>(a, ntiles_out, st);
-  return a.w_bits == 4 ? launch_adapt_mfma<R, true, false>(a, ntiles_out, st)
-                       : launch_adapt_mfma<R, false, false>(a, ntiles_out, st);
+  switch (a.dist) {
+    case kAuxGauss: return launch_adapt_md<R, kAuxGauss>(a, ntiles_out, st);
+    case kAuxCauchy: return launch_adapt_md<R, kAuxCauchy>(a, ntiles_out, st);
+    case kAuxStudentT2: return launch_adapt_md<R, kAuxStudentT2>(a, ntiles_out, st);
+    default: return launch_adapt_md<R, kAuxLaplace>(a, ntiles_out, st);
+  }
 }
 
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
@@ -1074,7 +1108,7 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   *ntiles_out = ntiles;
   dim3 grid((unsigned)ntiles, (unsigned)(a.d < 65535 ? (a.d ? a.d : 1) : 65535));
   hipLaunchKernelGGL(k_adapt_generic, grid, dim3(256), 0, st, a.d, a.n, a.r, a.w_bits, a.seed, a.layer_id, a.wround,
-                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero, a.ptq);
+                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero, a.ptq, a.dist);
   return hipGetLastError();
 }
 
@@ -1108,7 +1142,7 @@ struct FusedLds {
   }
 };
 
-template <int NG, bool W4>
+template <int NG, bool W4, int DIST>
 __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r, int u_bits, uint64_t seed,
                                                     uint32_t layer_id, const uint8_t* __restrict__ wround,
                                                     const int32_t* __restrict__ z, const float* __restrict__ s,
@@ -1226,7 +1260,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zr[rg];
-                const float rs = cr[rg] * laplace_from_word(pick_word(rnd, e), tab);
+                const float rs = cr[rg] * aux_sample<DIST>(rnd, (unsigned)e, tab);
                 t[e] = rs + acc[ch][rg][e];
                 q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
                 slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
@@ -1360,14 +1394,14 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
   #pragma unroll
             for (int e = 0; e < 4; ++e) {
               w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zi;
-              rs[e] = ci * laplace_from_word(pick_word(rnd, e), tab);
+              rs[e] = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
             }
           } else {
   #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int64_t j = j0 + e < n ? j0 + e : n - 1;
               w[e] = code_at<W4>(wround, i, n, j) - zi;
-              rs[e] = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab);
+              rs[e] = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, ci, layer_id, seed, tab, DIST);
             }
           }
           float t[4], q[4];
@@ -1534,6 +1568,39 @@ hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, cons
   return hipGetLastError();
 }
 
+template <int NG, bool W4, int DIST>
+static hipError_t launch_fused_t(const AdaptArgs& a, dim3 grid, int u_bits, int16_t* m, float* sbar, int32_t* zbar,
+                                 uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st) {
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge_fused<NG, W4, DIST>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, FusedLds<NG>::MAX_BYTES);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_merge_fused<NG, W4, DIST>), grid, dim3(256), (unsigned)FusedLds<NG>::bytes(a.n, a.r), st, a.d,
+                     a.n, a.r, u_bits, a.seed, a.layer_id, a.wround, a.z, a.s, a.c, a.A, a.B, m, sbar, zbar, split,
+                     uround_dbg, sat);
+  return hipSuccess;
+}
+
+template <int DIST>
+static hipError_t launch_fused_d(const AdaptArgs& a, int ng, dim3 grid, int u_bits, int16_t* m, float* sbar,
+                                 int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
+                                 hipStream_t st) {
+#define INTLORA_FUSED(NG)                                                                                      \
+  return a.w_bits == 4 ? launch_fused_t<NG, true, DIST>(a, grid, u_bits, m, sbar, zbar, split, uround_dbg, sat, st) \
+                       : launch_fused_t<NG, false, DIST>(a, grid, u_bits, m, sbar, zbar, split, uround_dbg, sat, st)
+  switch (ng) {
+    case 1: INTLORA_FUSED(1);
+    case 2: INTLORA_FUSED(2);
+    case 4: INTLORA_FUSED(4);
+    case 8: INTLORA_FUSED(8);
+    default: INTLORA_FUSED(16);
+  }
+#undef INTLORA_FUSED
+}
+
 // Fused MUL merge: NG = columns / 1024 rounded up to a power of two (n <= 16384).
 hipError_t launch_merge_fused(const AdaptArgs& a, int u_bits, int16_t* m, float* sbar, int32_t* zbar,
                               uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat, hipStream_t st) {
@@ -1544,33 +1611,16 @@ hipError_t launch_merge_fused(const AdaptArgs& a, int u_bits, int16_t* m, float*
   const int64_t groups = (a.d + rb - 1) / rb;
   const dim3 grid((unsigned)(groups < 8192 ? (groups > 0 ? groups : 1) : 8192));
   if (sat) hipLaunchKernelGGL(k_zero_u64, dim3(1), dim3(1), 0, st, sat);
-#define INTLORA_FUSED(NG, W4)                                                                                   \
-  do {                                                                                                          \
-    static bool attr = false;                                                                                   \
-    if (!attr) {                                                                                                \
-      const hipError_t e_ = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_merge_fused<NG, W4>),           \
-                                                hipFuncAttributeMaxDynamicSharedMemorySize, FusedLds<NG>::MAX_BYTES); \
-      if (e_ != hipSuccess) return e_;                                                                          \
-      attr = true;                                                                                              \
-    }                                                                                                           \
-    hipLaunchKernelGGL((k_merge_fused<NG, W4>), grid, dim3(256), (unsigned)FusedLds<NG>::bytes(a.n, a.r), st, a.d, \
-                       a.n, a.r, u_bits,                                                                        \
-                       a.seed, a.layer_id, a.wround, a.z, a.s, a.c, a.A, a.B, m, sbar, zbar, split, uround_dbg, sat); \
-  } while (0)
-#define INTLORA_FUSED_W(NG) \
-  if (a.w_bits == 4)        \
-    INTLORA_FUSED(NG, true); \
-  else                      \
-    INTLORA_FUSED(NG, false)
-  switch (ng) {
-    case 1: INTLORA_FUSED_W(1); break;
-    case 2: INTLORA_FUSED_W(2); break;
-    case 4: INTLORA_FUSED_W(4); break;
-    case 8: INTLORA_FUSED_W(8); break;
-    default: INTLORA_FUSED_W(16); break;
+  hipError_t e;
+  switch (a.dist) {
+    case kAuxGauss: e = launch_fused_d<kAuxGauss>(a, ng, grid, u_bits, m, sbar, zbar, split, uround_dbg, sat, st); break;
+    case kAuxCauchy: e = launch_fused_d<kAuxCauchy>(a, ng, grid, u_bits, m, sbar, zbar, split, uround_dbg, sat, st); break;
+    case kAuxStudentT2:
+      e = launch_fused_d<kAuxStudentT2>(a, ng, grid, u_bits, m, sbar, zbar, split, uround_dbg, sat, st);
+      break;
+    default: e = launch_fused_d<kAuxLaplace>(a, ng, grid, u_bits, m, sbar, zbar, split, uround_dbg, sat, st); break;
   }
-#undef INTLORA_FUSED_W
-#undef INTLORA_FUSED
+  if (e != hipSuccess) return e;
   return hipGetLastError();
 }
 

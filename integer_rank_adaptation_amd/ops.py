@@ -12,9 +12,9 @@ def _dev(t):
     return t.device
 
 
-def gen_r(d, n, seed, layer_id, c):
+def gen_r(d, n, seed, layer_id, c, aux_dist=0):
     out = torch.empty((d, n), dtype=torch.float32, device=_dev(c))
-    B.intlora_gen_r(B.desc(d, n, 1, 8, seed, layer_id), c, out)
+    B.intlora_gen_r(B.desc(d, n, 1, 8, seed, layer_id, aux_dist), c, out)
     return out
 
 
@@ -25,9 +25,12 @@ def sigma_w(W):
     return out
 
 
-def vmc_scale(sigma, alpha):
+def vmc_scale(sigma, alpha, aux_dist=0):
     c = torch.empty_like(sigma)
-    B.intlora_vmc_scale(sigma.numel(), sigma, alpha, c)
+    if aux_dist == 0:
+        B.intlora_vmc_scale(sigma.numel(), sigma, alpha, c)
+    else:
+        B.intlora_vmc_scale_dist(sigma.numel(), sigma, alpha, aux_dist, c)
     return c
 
 
@@ -35,21 +38,22 @@ def code_bytes(d, n, w_bits):
     return (d, n) if w_bits == 8 else (d, n // 2)
 
 
-def base_quant(W, c, w_bits, seed, layer_id):
+def base_quant(W, c, w_bits, seed, layer_id, aux_dist=0):
     d, n = W.shape
     wr = torch.empty(code_bytes(d, n, w_bits), dtype=torch.uint8, device=_dev(W))
     z = torch.empty(d, dtype=torch.int32, device=_dev(W))
     s = torch.empty(d, dtype=torch.float32, device=_dev(W))
-    B.intlora_base_quant(B.desc(d, n, 1, w_bits, seed, layer_id), W, c, wr, z, s)
+    B.intlora_base_quant(B.desc(d, n, 1, w_bits, seed, layer_id, aux_dist), W, c, wr, z, s)
     return wr, z, s
 
 
-def setup_layer(W, w_bits, seed, layer_id, alpha=1.5):
-    """AQS + VMC set-up of a pretrained layer on the GPU: sigma_W, c, Q[W - R*]."""
+def setup_layer(W, w_bits, seed, layer_id, alpha=1.5, aux_dist=0):
+    """AQS + VMC set-up of a pretrained layer on the GPU: sigma_W, c, Q[W - R*].  The
+    auxiliary law (aux_dist) is kept with the state and used by every merge of it."""
     sig = sigma_w(W)
-    c = vmc_scale(sig, alpha)
-    wr, z, s = base_quant(W, c, w_bits, seed, layer_id)
-    return dict(sigma=sig, c=c, wround=wr, z=z, s=s)
+    c = vmc_scale(sig, alpha, aux_dist)
+    wr, z, s = base_quant(W, c, w_bits, seed, layer_id, aux_dist)
+    return dict(sigma=sig, c=c, wround=wr, z=z, s=s, aux_dist=aux_dist)
 
 
 def workspace(op, d, n, r, w_bits, device):
@@ -60,7 +64,7 @@ def workspace(op, d, n, r, w_bits, device):
 def u_minmax(st, A, Bm, w_bits, seed, layer_id, ws=None):
     d, r = A.shape
     n = Bm.shape[1]
-    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
     ws = workspace(B.INTLORA_OP_STATS_UMINMAX, d, n, r, w_bits, A.device) if ws is None else ws
     umin = torch.empty(d, dtype=torch.float32, device=A.device)
     umax = torch.empty_like(umin)
@@ -73,7 +77,7 @@ def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
-    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
     ws = workspace(B.INTLORA_OP_MERGE_MUL, d, n, r, w_bits, dev) if ws is None else ws
     o = out or dict(m=torch.empty((d, n), dtype=torch.int16, device=dev),
                     sbar=torch.empty(d, dtype=torch.float32, device=dev),
@@ -93,7 +97,7 @@ def merge_mul_fused(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, out=No
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
-    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
     o = out or dict(m=torch.empty((d, n), dtype=torch.int16, device=dev),
                     sbar=torch.empty(d, dtype=torch.float32, device=dev),
                     zbar=torch.empty(d, dtype=torch.int32, device=dev),
@@ -113,7 +117,7 @@ def merge_mul_codes(st, A, Bm, w_bits, u_bits, seed, layer_id, ws=None, out=None
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
-    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
     ws = workspace(B.INTLORA_OP_MERGE_MUL, d, n, r, w_bits, dev) if ws is None else ws
     o = out or dict(ucode=torch.empty((d, n // 2), dtype=torch.uint8, device=dev),
                     sbar=torch.empty(d, dtype=torch.float32, device=dev),
@@ -127,7 +131,7 @@ def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, o
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
-    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
     ws = workspace(B.INTLORA_OP_MERGE_SHIFT, d, n, r, w_bits, dev) if ws is None else ws
     o = out or dict(m=torch.empty(code_bytes(d, n, w_bits), dtype=torch.uint8, device=dev),
                     sbar=torch.empty(d, dtype=torch.float32, device=dev),
@@ -144,7 +148,7 @@ def merge_ptq(st, A, Bm, w_bits, bits, seed, layer_id, ws=None, out=None):
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
-    dsc = B.desc(d, n, r, w_bits, seed, layer_id)
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
     ws = workspace(B.INTLORA_OP_MERGE_PTQ, d, n, r, w_bits, dev) if ws is None else ws
     o = out or dict(code=torch.empty(code_bytes(d, n, bits), dtype=torch.uint8, device=dev),
                     s=torch.empty(d, dtype=torch.float32, device=dev),

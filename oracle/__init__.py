@@ -211,12 +211,12 @@ def base_quant(W, rstar, bits):
     return wr, z, s
 
 
-def setup_layer(W, seed, layer_id, bits, alpha=1.5):
+def setup_layer(W, seed, layer_id, bits, alpha=1.5, aux_dist=0):
     """AQS + VMC set-up of one pretrained layer: sigma_W -> c -> R* -> Q[W - R*]."""
     d, n = W.shape
     sig = sigma_w(W)
-    c = vmc_scale(sig, alpha)
-    rstar = gen_r(d, n, seed, layer_id, c)
+    c = vmc_scale(sig, alpha, aux_dist)
+    rstar = gen_r(d, n, seed, layer_id, c, aux_dist)
     wr, z, s = base_quant(W, rstar, bits)
     return dict(sigma=sig, c=c, rstar=rstar, wround=wr, z=z, s=s)
 

@@ -99,11 +99,19 @@ def test_merge_mul_validation(lib, case, expect):
     assert lib.intlora_last_error()  # a message is left for the caller
 
 
-def test_reserved_field_and_null_desc(lib):
+def test_aux_dist_field_and_null_desc(lib):
     d = B.desc(8, 8, 4, 8)
-    d.reserved = 1
+    d.aux_dist = 4  # the laws are 0..3
     assert _merge_mul(lib, d) == B.INTLORA_EINVAL
+    assert lib.intlora_gen_r(ctypes.byref(d), FAKE, FAKE, None) == B.INTLORA_EINVAL
     assert lib.intlora_gen_r(None, FAKE, FAKE, None) == B.INTLORA_EINVAL
+    assert lib.intlora_vmc_scale_dist(8, FAKE, 1.5, 4, FAKE, None) == B.INTLORA_EINVAL
+    assert lib.intlora_vmc_scale_dist(8, FAKE, 9.0, 1, FAKE, None) == B.INTLORA_EINVAL
+    assert lib.intlora_debug_aux(4, FAKE, 4, FAKE, None) == B.INTLORA_EINVAL
+    assert lib.intlora_debug_aux(-1, FAKE, 0, FAKE, None) == B.INTLORA_ESHAPE
+    # zero-sized calls succeed without touching a device
+    assert lib.intlora_debug_aux(0, None, 2, None, None) == B.INTLORA_OK
+    assert lib.intlora_vmc_scale_dist(0, None, 1.5, 3, None, None) == B.INTLORA_OK
 
 
 def test_other_entry_points_validation(lib):

@@ -689,3 +689,85 @@ def test_graph_replay_matches_eager(ops):
         got = (out["m"], out["sbar"], out["split"], Y, outc["ucode"], Yc, Ys)
         for a, b in zip(got, ref):
             assert torch.equal(a, b), rep
+
+
+# ----------------------------------------------------------------------------- auxiliary laws
+# The distribution ablation of the auxiliary matrix ([IntLoRA summary], "Measured
+# effects": Laplace against Gaussian, Cauchy and Student-t samples).
+AUX_LAWS = [1, 2, 3]
+
+
+@pytest.mark.parametrize("dist", [0] + AUX_LAWS)
+def test_aux_sampler_exhaustive(ops, dist):
+    """Every uniform index a (2^23 of them) in every word position of a block, so each
+    correctly rounded step (ln at both biases, cos / sin / tan of pi v, the Student-t
+    expression) meets its whole input domain: bit for bit against the oracle."""
+    t = np.arange(2**23, dtype=np.uint64)
+    perm = [t, (t * 2654435761) % 2**23, (t * 40503 + 12345) % 2**23, (2**23 - 1) - t]
+    rng = np.random.Generator(np.random.PCG64(dist))
+    words = np.stack([((p.astype(np.uint32) << np.uint32(9)) | rng.integers(0, 512, t.size, dtype=np.uint32))
+                      for p in perm], axis=1)
+    out = torch.empty(words.shape, dtype=torch.float32, device="cuda")
+    ops.B.intlora_debug_aux(t.size, cuda(words), dist, out)
+    got = host(out)
+    ref = oracle.aux_samples(words, dist)
+    bad = np.nonzero(bits(got).ravel() != bits(ref).ravel())[0]
+    assert bad.size == 0, (bad.size, words.ravel()[bad[:4]], got.ravel()[bad[:4]], ref.ravel()[bad[:4]])
+
+
+@pytest.mark.parametrize("dist", AUX_LAWS)
+@pytest.mark.parametrize("d,n", [(1, 8), (5, 37), (33, 1000)])
+def test_gen_r_laws(ops, dist, d, n):
+    c = synth.random_positive(d + n, d, 1e-3, 2.0)
+    got = host(ops.gen_r(d, n, 9, 4, cuda(c), aux_dist=dist))
+    assert np.array_equal(bits(got), bits(oracle.gen_r(d, n, 9, 4, c, dist)))
+
+
+@pytest.mark.parametrize("dist", AUX_LAWS)
+def test_setup_layer_laws(ops, dist):
+    W = synth.weight(synth.WORKLOADS[0], 0, d=24, n=256)
+    st = ops.setup_layer(cuda(W), 4, 11, 6, 1.5, aux_dist=dist)
+    sig = host(st["sigma"])
+    c = oracle.vmc_scale(sig, 1.5, dist)
+    assert np.array_equal(bits(host(st["c"])), bits(c))
+    R = oracle.gen_r(24, 256, 11, 6, c, dist)
+    ref_wr, ref_z, ref_s = oracle.base_quant(W, R, 4)
+    assert np.array_equal(unpack4(host(st["wround"])), ref_wr)
+    assert np.array_equal(host(st["z"]), ref_z)
+    assert np.array_equal(bits(host(st["s"])), bits(ref_s))
+
+
+@pytest.mark.parametrize("dist", AUX_LAWS)
+@pytest.mark.parametrize("d,n,r,w_bits", [(33, 1024, 32, 4), (9, 102, 4, 4), (11, 3072, 32, 4), (16, 2048, 64, 8),
+                                          (40, 520, 8, 4)])
+def test_merges_laws(ops, dist, d, n, r, w_bits):
+    """MUL (three-kernel, fused, keeping U's codes), SHIFT and the comparison path under
+    each auxiliary law: every output bit for bit against the oracle fed the same law's
+    R* (the matrix-core and general adaptation paths, every fused row-block width used)."""
+    seed = 400 + d + n + r + dist
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    wr[0, : min(n, 6)] = z[0]
+    st = gpu_state(wr, z, s, c, w_bits)
+    st["aux_dist"] = dist
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c, dist)
+    Ag, Bg = cuda(A), cuda(Bm)
+    ref = oracle.merge_mul(wr, z, s, R, A, Bm, 4)
+    for g in (ops.merge_mul(st, Ag, Bg, w_bits, 4, 77, 5, dbg=True),
+              ops.merge_mul_fused(st, Ag, Bg, w_bits, 4, 77, 5, dbg=True)):
+        assert np.array_equal(host(g["m"]), ref["m"])
+        assert np.array_equal(host(g["uround"]), ref["uround"])
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert np.array_equal(host(g["zbar"]), ref["zbar"])
+        assert int(host(g["sat"])[0]) == ref["sat"]
+    if n % 2 == 0:
+        g = ops.merge_mul_codes(st, Ag, Bg, w_bits, 4, 77, 5)
+        assert np.array_equal(unpack4(host(g["ucode"])), ref["uround"])
+    g = ops.merge_shift(st, Ag, Bg, w_bits, 4, 77, 5, dbg=True)
+    ref_s = oracle.merge_shift(wr, z, s, R, A, Bm, w_bits, 4)
+    m = host(g["m"])
+    assert np.array_equal(unpack4s(m) if w_bits == 4 else m.view(np.int8), ref_s["m"])
+    assert np.array_equal(bits(host(g["sbar"])), bits(ref_s["sbar"]))
+    g = ops.merge_ptq(st, Ag, Bg, w_bits, 8, 77, 5)
+    ref_p = oracle.ptq_merge(wr, z, s, R, A, Bm, 8)
+    assert np.array_equal(host(g["code"]), ref_p["code"])
+    assert np.array_equal(bits(host(g["s"])), bits(ref_p["s"]))
