@@ -62,6 +62,8 @@ def parse():
                    help="skip the straight-through backward (a synthetic dL/dW' per layer, dA and dB)")
     p.add_argument("--no-graph", action="store_true",
                    help="skip the step captured in a HIP graph and replayed (reported beside the eager step)")
+    p.add_argument("--no-aux-laws", action="store_true",
+                   help="skip the merge timed under the other auxiliary laws (Gaussian, Cauchy, Student-t(2))")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -169,6 +171,49 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
                 alg_GBps=round(alg / (ptq_ms * 1e-3) / 1e9, 1),
                 pct_hbm_peak=round(100 * alg / (ptq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                 bound="alu (the adaptation kernel's Philox, ln and rank-r work)", per_layer=per)
+
+
+AUX_LAW_NAMES = {1: "gaussian", 2: "cauchy", 3: "student_t2"}
+
+
+def aux_laws_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mode, mbits):
+    """The step's merge under each other auxiliary law of the distribution ablation: the
+    same layers set up again with that law (untimed), then the MUL or SHIFT merge timed
+    like the main step's (whole layers, events on the same stream)."""
+    res = {}
+    for dist, name in AUX_LAW_NAMES.items():
+        sts, outs = [], []
+        for lay in layers:
+            Wg = torch.from_numpy(lay["W"]).to(dev)
+            sts.append(ops.setup_layer(Wg, wl.w_bits, synth.PHILOX_SEED, lay["lid"], synth.ALPHA, aux_dist=dist))
+            del Wg
+            outs.append(None)
+
+        def run():
+            for k, lay in enumerate(layers):
+                if mode == "mul":
+                    outs[k] = ops.merge_mul(sts[k], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
+                                            lay["lid"], ws=ws, out=outs[k])
+                else:
+                    outs[k] = ops.merge_shift(sts[k], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
+                                              lay["lid"], ws=ws, out=outs[k])
+
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        alg = sum(merge_alg_bytes(lay["L"].d, lay["L"].n, wl.r, wl.w_bits, mode) for lay in layers)
+        res[name] = {"merge_us_per_step": round(ms * 1e3, 1), "alg_GBps": round(alg / (ms * 1e-3) / 1e9, 1)}
+        del sts, outs
+    res["bound"] = "alu (the sampler's ln, sqrt, cos / sin / tan in binary64 replace the Laplace ln)"
+    return res
 
 
 def fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits):
@@ -460,6 +505,10 @@ def main():
     if mode == "mul" and wl.w_bits == 4 and mbits <= 4 and not args.no_codes:
         codes = codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits)
 
+    aux_laws = None
+    if not args.no_aux_laws:
+        aux_laws = aux_laws_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mode, mbits)
+
     ste = None
     if not args.no_ste:
         ste = ste_measure(args, wl, layers, ops, torch, dev, stream)
@@ -524,6 +573,7 @@ def main():
         "merge_fused": fused,
         "merge_on_load": codes,
         "ste_backward": ste,
+        "aux_laws": aux_laws,
         "setup_s": round(setup_s, 1),
     }
 
@@ -656,6 +706,18 @@ def cpu_next_rows(wl, layers, M, mode, mbits, merge_linear_s, frac=0.02):
             oracle.linear(xq, sx, m, sb, want_exact=False)
             t2 = time.perf_counter()
             t_codes += (t1 - t0) + (t2 - t1) * (M / toks)
+    # the other auxiliary laws: R generation under each law on the same rows (the merge
+    # after it is the Laplace merge's oracle, part of step_s)
+    for dist, name in AUX_LAW_NAMES.items():
+        t = 0.0
+        for lay in layers:
+            L = lay["L"]
+            rows = max(1, int(round(L.d * frac)))
+            c = np.ones(rows, np.float32)
+            t0 = time.perf_counter()
+            oracle.gen_r_rows(0, rows, L.n, synth.PHILOX_SEED, lay["lid"], c, dist)
+            t += (time.perf_counter() - t0) * (L.d / rows)
+        out["f4_aux_law_r_generation_" + name] = round(t, 3)
     out["f4_ptq_merge"] = round(t_ptq, 3)
     out["f3_ste_backward"] = round(t_ste, 3)
     if t_codes > 0.0:
