@@ -471,10 +471,17 @@ def main():
         cur.wait_stream(ms_stream)
 
     overlap_ms = None
+    overlap_same = None
     if not args.no_overlap:
+        torch.cuda.synchronize()
+        ref_y = [lay["Y"].clone() for lay in layers]
+        for lay in layers:
+            lay["Y"].zero_()
         for _ in range(args.warmup):
             step_overlap()
         torch.cuda.synchronize()
+        overlap_same = all(torch.equal(lay["Y"], r) for lay, r in zip(layers, ref_y))
+        del ref_y
         t0_ = torch.cuda.Event(enable_timing=True)
         t1_ = torch.cuda.Event(enable_timing=True)
         t0_.record(stream)
@@ -568,6 +575,7 @@ def main():
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
+        "overlap_equals_sequential": overlap_same,
         "graph": graph,
         "ptq_comparison": ptq,
         "merge_fused": fused,
