@@ -355,9 +355,9 @@ def main():
         copy_probe(args.copy_probe)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus %d is not supported "
-                                   "(the merge shards by rows and the GEMM by columns with no exchange; "
-                                   "see DESIGN.md)" % args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus %d is not supported (the merge "
+                                   "would shard by rows and the GEMM by columns, with no exchange between GPUs)"
+                                   % args.gpus}))
         sys.exit(2)
 
     import torch
@@ -569,7 +569,7 @@ def main():
                      "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profile(wl.name)},
         "merge": {"alg_GBps": round(merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9, 1),
                   "pct_hbm_peak": round(100 * merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-                  "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (see DESIGN.md)"},
+                  "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (Philox, the Laplace ln and the division per element in the adaptation kernel)"},
         "gemm": {"exec_TOPS": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
                  "effective_TOPS": round(gemm_ops_tot / (2 if mode == "mul" else 1) / (gemm_ms_tot * 1e-3) / 1e12, 1),
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
