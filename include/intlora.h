@@ -160,9 +160,13 @@ int intlora_stats(const intlora_desc* desc, int mode, const float* W, const intl
  * sqrt(2) is the standard deviation of the unit Laplace law.  alpha in [0, 8]. */
 int intlora_vmc_scale(int64_t d, const float* sigma_w, double alpha, float* c_out, void* stream);
 
-/* The same for the auxiliary law aux_dist: sigma_R = sqrt(2) for Laplace, 1 for the
- * others (the Gaussian's standard deviation; the unit scale of the Cauchy and Student-t(2)
- * laws, which have no finite variance).  INTLORA_EINVAL for an unknown law. */
+/* The same for the auxiliary law aux_dist (the IntLoRA summary's distribution ablation;
+ * section "3. VMC" for the scale): c_out[i] = RN32((sigma_w[i] / sigma_R)^alpha) in
+ * binary64, sigma_R = sqrt(2) for Laplace and 1 for the others (the Gaussian's standard
+ * deviation; the unit scale of the Cauchy and Student-t(2) laws, which have no finite
+ * variance).  sigma_w and c_out: d fp32 device values, caller-owned.  INTLORA_EINVAL for
+ * an unknown law or alpha outside [0, 8]; d = 0 returns INTLORA_OK without touching the
+ * device. */
 int intlora_vmc_scale_dist(int64_t d, const float* sigma_w, double alpha, uint32_t aux_dist, float* c_out,
                            void* stream);
 
@@ -308,7 +312,9 @@ int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream)
 
 /* Diagnostic: the unscaled auxiliary sample (c = 1) of each element of `blocks` given
  * Philox output blocks words[4 t .. 4 t + 3] under law aux_dist: out[4 t + e] is what
- * intlora_gen_r computes for element e of a block with those words.  Device pointers. */
+ * intlora_gen_r computes for element e of a block with those words.  words (4 * blocks
+ * uint32) and out (4 * blocks fp32) are caller-owned device buffers.  INTLORA_EINVAL for
+ * an unknown law, INTLORA_ESHAPE for blocks < 0; blocks = 0 returns INTLORA_OK. */
 int intlora_debug_aux(int64_t blocks, const uint32_t* words, uint32_t aux_dist, float* out, void* stream);
 
 #ifdef __cplusplus
