@@ -106,7 +106,10 @@ typedef struct intlora_desc {
 /* Stored state of a quantized base layer (AQS: Q[W - R*] with R* regenerated). */
 typedef struct intlora_base {
   const void* w_round;  /* codes of W - R*: uint8 d x n (w_bits 8) or packed d x n/2 (w_bits 4) */
-  const int32_t* z;     /* [d] zero points                                                       */
+  const int32_t* z;     /* [d] zero points, each in [0, 2^w_bits - 1] as intlora_base_quant
+                           writes them.  The merges stay exact for any int32 z (rows whose z
+                           is outside [0, 255] take the IEEE division); the merge-on-load
+                           linear layer needs z in [0, 15].                                 */
   const float* s;       /* [d] scales                                                            */
   const float* vmc_c;   /* [d] VMC scale c_i = (sigma_W,i / sigma_R)^alpha, from intlora_vmc_scale */
 } intlora_base;
@@ -181,7 +184,10 @@ int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vm
 
 /* IntLoRA_MUL merge (section "two implementation variants", MUL).  Per element with
  * w = W_round - z != 0: acc = fma chain of A[i,k] B[k,j] for k = 0..r-1 from +0,
- * U = s_i + (R*_ij + acc) / w (binary32, IEEE division).  Per row: lo = min(U_min, 0),
+ * U = s_i + (R*_ij + acc) / w (binary32, IEEE division).  Per row, over the range
+ * (U_min, U_max) -- the least and greatest valid U of the row, or, when the caller
+ * passes u_min and u_max ([d] fp32 each; both or neither), those values instead (for
+ * a caller that already holds the range, e.g. from intlora_stats): lo = min(U_min, 0),
  * hi = max(U_max, 0), s_bar = (hi - lo) / (2^u_bits - 1) (1 unless positive),
  * z_bar = clamp(rint(-lo / s_bar), 0, 2^u_bits - 1); U_round = clamp(rint(U / s_bar) +
  * z_bar, 0, 2^u_bits - 1); m = (U_round - z_bar) * w stored as int16, saturating
@@ -193,8 +199,9 @@ int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vm
  * overwritten with the number of saturated elements).  u_bits in [2, 8].
  * Workspace: INTLORA_OP_MERGE_MUL. */
 int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
-                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
-                      unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
+                      const float* u_min, const float* u_max, int16_t* m, float* s_bar, int32_t* z_bar,
+                      uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count, void* ws,
+                      size_t ws_bytes, void* stream);
 
 /* Fused single-pass MUL merge with no scratch memory: the same outputs, bit for bit, as
  * intlora_merge_mul ([IntLoRA notes] "1. AQS", "2. MLA", "两种实现版本" MUL), computed
@@ -218,8 +225,10 @@ int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, 
                             uint8_t* u_code, float* s_bar, int32_t* z_bar, void* ws, size_t ws_bytes, void* stream);
 
 /* IntLoRA_SHIFT merge (section "two implementation variants", SHIFT).  U as for MUL.
- * Reading: s_bar = max |U| over the row's valid elements (1 for an empty or all-zero
- * row) and V = U / s_bar, so |V| <= 1 and only right shifts occur;
+ * Reading: s_bar = max(|U_min|, |U_max|), the largest |U| over the row's valid elements
+ * (1 for an empty or all-zero row), with (U_min, U_max) the row's range or the caller's
+ * u_min / u_max (both or neither, as for MUL); V = U / s_bar, so |V| <= 1 for every U in
+ * the range and only right shifts occur;
  * shift = clamp(-round(log2 |V|), 0, 2^v_bits - 1), exact from the bits (no ties);
  * m = sign(V) * (w >> shift), ">>" arithmetic (floor); V == 0 gives m = 0 and the
  * largest shift code; m saturates to the signed w_bits range (counted); w == 0 gives
@@ -228,8 +237,8 @@ int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, 
  * s_bar[d]; optional shift_dbg (uint8 d x n), sat_count.  v_bits in [1, 8].
  * Workspace: INTLORA_OP_MERGE_SHIFT. */
 int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int v_bits,
-                        void* m, float* s_bar, uint8_t* shift_dbg, unsigned long long* sat_count, void* ws,
-                        size_t ws_bytes, void* stream);
+                        const float* u_min, const float* u_max, void* m, float* s_bar, uint8_t* shift_dbg,
+                        unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
 
 /* QLoRA-style comparison path: the flow IntLoRA removes ([IntLoRA notes] research
  * background; its PTQ step is what "training and inference efficiency" says IntLoRA
@@ -261,13 +270,23 @@ int intlora_ste_backward(const intlora_desc* desc, const void* w_round, const in
                          const float* B, const float* G, float* dA, float* dB, void* ws, size_t ws_bytes,
                          void* stream);
 
-/* Per-token symmetric int8 activation quantization: s_x[t] = max_j |X[t,j]| / 127
- * (1 for an all-zero token), xq = clamp(rint(X / s_x), -127, 127), x_rowsum[t] =
- * sum_j xq[t,j] (x_rowsum may be NULL).  X: M x n fp32. */
+/* Per-token symmetric int8 activation quantization, the activation side of the W8A8 /
+ * W4A8 layer: the IntLoRA notes ("training and inference efficiency") keep the
+ * activations' quantization conventional, and the SVDQuant article ("5 Experiments",
+ * "Setups", 8-bit implementation details) takes per-token dynamic activation scales.
+ *   s_x[t] = max_j |X[t,j]| / 127 (1 for an all-zero token),
+ *   xq = clamp(rint(X / s_x), -127, 127) (rint half to even, IEEE division),
+ *   x_rowsum[t] = sum_j xq[t,j] (x_rowsum may be NULL).
+ * X: M x n fp32 row-major; xq: M x n int8; s_x: [M] fp32; x_rowsum: [M] int32; all
+ * caller-owned device memory.  M = 0 is a no-op; INTLORA_ESHAPE for M < 0 or n < 1. */
 int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s_x, int32_t* x_rowsum,
                       void* stream);
 
-/* Integer linear layer on merged integers: Y[t, i] for t < M tokens, i < d outputs.
+/* Integer linear layer on merged integers ([IntLoRA notes] "training and inference
+ * efficiency": the merged integers are the deployed W8A8 / W4A8 weights, used with no
+ * post-training quantization; "two implementation variants": the merged weight is
+ * s_bar_i m_ij; per-token activation and per-channel weight scales as in the SVDQuant
+ * article's 8-bit setting):  Y[t, i] for t < M tokens, i < d outputs.
  *   exact = sum_j xq[t,j] * m[i,j] (integer);
  *   y = RN32(RN32(float(exact) * s_x[t]) * s_bar[i]),  Y = bf16 round-to-nearest-even.
  * wfmt INTLORA_W_INT8 / INTLORA_W_INT4 (SHIFT merged integers): one int8 MFMA pass.

@@ -59,13 +59,13 @@ _SIG = {
     "intlora_vmc_scale_dist": (_INT, [_I64, _P, ctypes.c_double, ctypes.c_uint32, _P, _P]),
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
-                                 _P, _P, _P, _P, ctypes.c_size_t, _P]),
+                                 _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_mul_fused": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
                                        _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul_codes": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
                                        _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_shift": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P,
-                                   _P, _P, _P, ctypes.c_size_t, _P]),
+                                   _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_ptq": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, ctypes.c_size_t, _P]),
     "intlora_ste_backward": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -167,11 +167,11 @@ def intlora_base_quant(dsc: Desc, W, vmc_c, w_round_out, z_out, s_out, stream=No
 
 
 def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None, u_round_dbg=None,
-                      sat_count=None, ws=None, stream=None):
+                      sat_count=None, ws=None, stream=None, u_min=None, u_max=None):
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(m),
-                                   _ptr(s_bar), _ptr(z_bar), _ptr(m_split), _ptr(u_round_dbg), _ptr(sat_count),
-                                   _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
+    _check(lib().intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(u_min),
+                                   _ptr(u_max), _ptr(m), _ptr(s_bar), _ptr(z_bar), _ptr(m_split), _ptr(u_round_dbg),
+                                   _ptr(sat_count), _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
 
 
 def intlora_merge_mul_fused(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None,
@@ -189,11 +189,11 @@ def intlora_merge_mul_codes(dsc: Desc, bs: Base, lr: Lora, u_bits: int, u_code, 
 
 
 def intlora_merge_shift(dsc: Desc, bs: Base, lr: Lora, v_bits: int, m, s_bar, shift_dbg=None, sat_count=None, ws=None,
-                        stream=None):
+                        stream=None, u_min=None, u_max=None):
     wsb = 0 if ws is None else ws.numel() * ws.element_size()
-    _check(lib().intlora_merge_shift(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), v_bits, _ptr(m),
-                                     _ptr(s_bar), _ptr(shift_dbg), _ptr(sat_count), _ptr(ws), wsb, _stream(stream)),
-           "intlora_merge_shift")
+    _check(lib().intlora_merge_shift(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), v_bits, _ptr(u_min),
+                                     _ptr(u_max), _ptr(m), _ptr(s_bar), _ptr(shift_dbg), _ptr(sat_count), _ptr(ws),
+                                     wsb, _stream(stream)), "intlora_merge_shift")
 
 
 def intlora_merge_ptq(dsc: Desc, bs: Base, lr: Lora, bits: int, code, s_out, z_out, ws=None, stream=None):

@@ -117,7 +117,7 @@ int check_ws(void* ws, size_t ws_bytes, size_t need) {
 }
 
 int run_adapt(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, MergeWs& w,
-              unsigned long long* sat_zero, hipStream_t st, bool ptq = false) {
+              unsigned long long* sat_zero, hipStream_t st, bool ptq = false, int64_t row0 = 0) {
   intlora::AdaptArgs a;
   a.d = desc->d;
   a.n = desc->n;
@@ -138,6 +138,7 @@ int run_adapt(const intlora_desc* desc, const intlora_base* base, const intlora_
   a.ptq = ptq;
   a.force_generic = false;
   a.dist = (int)desc->aux_dist;
+  a.row0 = row0;
   return launch_status(intlora::launch_adapt(a, &w.ntiles, st), "adaptation kernel");
 }
 
@@ -146,6 +147,63 @@ int check_base_lora(const intlora_base* base, const intlora_lora* lora) {
   int s = check_ptrs({base->w_round, base->z, base->s, base->vmc_c}, "base");
   if (s) return s;
   return check_ptrs({lora->A, lora->B}, "lora");
+}
+
+// The optional caller-supplied row range: both NULL (computed here) or both given.
+int check_range(const float* u_min, const float* u_max) {
+  if ((u_min == nullptr) != (u_max == nullptr)) return fail(INTLORA_EINVAL, "u_min and u_max: give both or neither");
+  if (u_min) return check_ptrs({u_min, u_max}, "u_min / u_max");
+  return INTLORA_OK;
+}
+
+// Row range of the merge: the caller's (u_min, u_max), or the reduction of the
+// adaptation kernel's tile partials into the workspace.  `split` (nullable) is cleared
+// either way; the quantize kernel raises it for rows that need the bias byte split.
+int merge_range(int64_t d, const MergeWs& w, const float* u_min, const float* u_max, uint8_t* split,
+                const float** lo, const float** hi, hipStream_t st) {
+  if (u_min) {
+    *lo = u_min;
+    *hi = u_max;
+    if (!split) return INTLORA_OK;
+    return launch_status(intlora::launch_fill_u8(d, split, 0, st), "split codes");
+  }
+  *lo = w.umin;
+  *hi = w.umax;
+  return launch_status(intlora::launch_row_range(d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, split, st),
+                       "row range");
+}
+
+// The three-kernel MUL merge of rows [0, desc->d) of the pointers given, whose row 0 is
+// row `row0` of the layer (R's counter); `sat_zero` is the counter the adaptation
+// kernel clears first (NULL: not cleared here).  Arguments are validated by the caller.
+int merge_mul_rows(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                   const float* u_min, const float* u_max, int16_t* m, float* s_bar, int32_t* z_bar,
+                   uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count,
+                   unsigned long long* sat_zero, MergeWs& w, int64_t row0, hipStream_t st) {
+  int s = run_adapt(desc, base, lora, w, sat_zero, st, false, row0);
+  if (s) return s;
+  const float *lo, *hi;
+  if ((s = merge_range(desc->d, w, u_min, u_max, m_split, &lo, &hi, st))) return s;
+  return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
+                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, lo, hi, m,
+                                                 s_bar, z_bar, m_split, u_round_dbg, sat_count, nullptr, st),
+                       "quant_mul");
+}
+
+int check_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
+                    const float* u_min, const float* u_max, int16_t* m, float* s_bar, int32_t* z_bar,
+                    uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count, const char* what) {
+  int s = check_desc(desc, true);
+  if (s) return s;
+  if (u_bits < 2 || u_bits > 8) return fail(INTLORA_EINVAL, "u_bits must be in [2, 8] (got %d)", u_bits);
+  if (desc->d == 0) return INTLORA_OK;
+  if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_range(u_min, u_max))) return s;
+  if ((s = check_ptrs({m, s_bar, z_bar}, what))) return s;
+  if ((s = check_opt(m_split, "m_split")) || (s = check_opt(u_round_dbg, "u_round_dbg")) ||
+      (s = check_opt(sat_count, "sat_count")))
+    return s;
+  return INTLORA_OK;
 }
 
 }  // namespace
@@ -167,7 +225,7 @@ const char* intlora_status_string(int status) {
 
 const char* intlora_last_error(void) { return g_err; }
 
-int intlora_version(void) { return 103; }
+int intlora_version(void) { return 104; }
 
 size_t intlora_workspace_bytes(int op, const intlora_desc* desc, int64_t M) {
   (void)M;
@@ -263,31 +321,22 @@ int intlora_base_quant(const intlora_desc* desc, const float* W, const float* vm
                        "base_quant");
 }
 
+
 int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
-                      int16_t* m, float* s_bar, int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg,
-                      unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream) {
-  int s = check_desc(desc, true);
+                      const float* u_min, const float* u_max, int16_t* m, float* s_bar, int32_t* z_bar,
+                      uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count, void* ws,
+                      size_t ws_bytes, void* stream) {
+  int s = check_merge_mul(desc, base, lora, u_bits, u_min, u_max, m, s_bar, z_bar, m_split, u_round_dbg, sat_count,
+                          "merge_mul");
   if (s) return s;
-  if (u_bits < 2 || u_bits > 8) return fail(INTLORA_EINVAL, "u_bits must be in [2, 8] (got %d)", u_bits);
   if (desc->d == 0) return ok();
-  if ((s = check_base_lora(base, lora))) return s;
-  if ((s = check_ptrs({m, s_bar, z_bar}, "merge_mul"))) return s;
-  if ((s = check_opt(m_split, "m_split")) || (s = check_opt(u_round_dbg, "u_round_dbg")) ||
-      (s = check_opt(sat_count, "sat_count")))
-    return s;
   if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
   if ((s = ensure_device())) return s;
-  hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
-  if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
-  if ((s = launch_status(
-           intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, m_split, st), "row range")))
+  if ((s = merge_mul_rows(desc, base, lora, u_bits, u_min, u_max, m, s_bar, z_bar, m_split, u_round_dbg, sat_count,
+                          sat_count, w, 0, static_cast<hipStream_t>(stream))))
     return s;
-  return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
-                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
-                                                 w.umax, m, s_bar, z_bar, m_split, u_round_dbg, sat_count, nullptr,
-                                                 st),
-                       "quant_mul");
+  return ok();
 }
 
 int intlora_merge_mul_fused(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
@@ -354,13 +403,14 @@ int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, 
 }
 
 int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int v_bits,
-                        void* m, float* s_bar, uint8_t* shift_dbg, unsigned long long* sat_count, void* ws,
-                        size_t ws_bytes, void* stream) {
+                        const float* u_min, const float* u_max, void* m, float* s_bar, uint8_t* shift_dbg,
+                        unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream) {
   int s = check_desc(desc, true);
   if (s) return s;
   if (v_bits < 1 || v_bits > 8) return fail(INTLORA_EINVAL, "v_bits must be in [1, 8] (got %d)", v_bits);
   if (desc->d == 0) return ok();
   if ((s = check_base_lora(base, lora))) return s;
+  if ((s = check_range(u_min, u_max))) return s;
   if ((s = check_ptrs({m, s_bar}, "merge_shift"))) return s;
   if ((s = check_opt(shift_dbg, "shift_dbg")) || (s = check_opt(sat_count, "sat_count"))) return s;
   if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
@@ -368,12 +418,11 @@ int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, cons
   hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
-  if ((s = launch_status(
-           intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, nullptr, st), "row range")))
-    return s;
+  const float *lo, *hi;
+  if ((s = merge_range(desc->d, w, u_min, u_max, nullptr, &lo, &hi, st))) return s;
   return launch_status(intlora::launch_quant_shift(desc->d, desc->n, desc->w_bits, v_bits,
-                                                   static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
-                                                   w.umax, static_cast<uint8_t*>(m), s_bar, shift_dbg, sat_count, st),
+                                                   static_cast<const uint8_t*>(base->w_round), base->z, w.U, lo, hi,
+                                                   static_cast<uint8_t*>(m), s_bar, shift_dbg, sat_count, st),
                        "quant_shift");
 }
 

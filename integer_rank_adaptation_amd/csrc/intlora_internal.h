@@ -24,6 +24,7 @@ struct AdaptArgs {
   bool ptq;                      // x = (s w + R*) + AB for every element (comparison path) instead of U
   bool force_generic;
   int dist;                      // auxiliary-matrix distribution (kAuxLaplace ... kAuxStudentT2)
+  int64_t row0 = 0;              // global index of row 0 of these pointers (R's counter uses i + row0)
 };
 
 // Fused single-pass MUL merge (no scratch); hipErrorInvalidValue for n > 16384.
@@ -45,6 +46,8 @@ hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint
 hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* sx, int32_t* rowsum,
                             hipStream_t st);
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st);
+// p[0 .. count) = v (a kernel, so that a captured graph holds no memset node).
+hipError_t launch_fill_u8(int64_t count, uint8_t* p, uint8_t v, hipStream_t st);
 hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
                             uint8_t* split, hipStream_t st);
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,

@@ -244,6 +244,11 @@ __device__ __forceinline__ bool div_small_int_ok(float t) {
   const float at = fabsf(t);
   return at >= 0x1p-100f && at <= 0x1p100f;
 }
+// Entry of w's reciprocal in the 511-entry table.  The index is clamped so that a zero
+// point outside the code range (|w| > 255 is then possible) never reads past the table;
+// rows with such a zero point (zero_point_ok false) take the IEEE division instead.
+__device__ __forceinline__ int rcp_index(int w) { return min(max(w, -255), 255) + 255; }
+__device__ __forceinline__ bool zero_point_ok(int z) { return (unsigned)z <= 255u; }
 
 constexpr int kKeyPosInf = 0x7F800000;  // order key of +inf (identity of min)
 constexpr int kKeyNegInf = (int)0x807FFFFF;  // order key of -inf (identity of max)
@@ -273,7 +278,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
                                                     const float* __restrict__ A, const float* __restrict__ B,
                                                     float* __restrict__ U, int* __restrict__ pmin,
                                                     int* __restrict__ pmax, int ntiles, int rtiles, int64_t rb0,
-                                                    unsigned long long* __restrict__ sat_zero) {
+                                                    unsigned long long* __restrict__ sat_zero, int64_t row0) {
   __shared__ LnLds tab[96];
   __shared__ float rcp[511];
   __shared__ int smin[4][32], smax[4][32];
@@ -301,6 +306,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
     // loads are in flight together instead of each waiting behind a branch.
     const int64_t ic = row_ok ? i : d - 1;
     const int zi = z[ic];
+    const bool zok = zero_point_ok(zi);
     const float ci = c[ic], si = s[ic];
     uint32_t wcode[8];
 #pragma unroll
@@ -346,7 +352,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
 #pragma unroll
           for (int e = 0; e < 4; ++e) w[e] = (int)((wcode[g] >> (8 * e)) & 255u) - zi;
         }
-        const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
+        const U4 rnd = philox_block(((uint64_t)(i + row0) * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
         float u[4], t[4], q[4];
         if (PTQ) {
 #pragma unroll
@@ -355,12 +361,12 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
             q[e] = (si * (float)w[e] + rs) + acc[4 * g + e];  // binary32 steps in this order
           }
         } else {
-          bool slow = false;
+          bool slow = !zok;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float rs = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
             t[e] = rs + acc[4 * g + e];
-            q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+            q[e] = div_small_int(t[e], (float)w[e], rcp[rcp_index(w[e])]);
             slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
           }
           // the IEEE division runs only in waves where some lane needs it
@@ -368,7 +374,7 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
             __asm__ volatile("");  // keeps the branch: the division is not speculated
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+              if (w[e] != 0 && (!zok || !div_small_int_ok(t[e]))) q[e] = t[e] / (float)w[e];
           }
         }
 #pragma unroll
@@ -411,7 +417,8 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
                                                       const float* __restrict__ c, const float* __restrict__ A,
                                                       const float* __restrict__ B, float* __restrict__ U,
                                                       int* __restrict__ pmin, int* __restrict__ pmax, int ntiles,
-                                                      unsigned long long* __restrict__ sat_zero, bool ptq, int dist) {
+                                                      unsigned long long* __restrict__ sat_zero, bool ptq, int dist,
+                                                      int64_t row0) {
   __shared__ LnLds tab[96];
   __shared__ int smin[4], smax[4];
   load_ln_table(tab);
@@ -432,7 +439,7 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
     const int w = code - z[i];
     float acc = 0.0f;
     for (int k = 0; k < r; ++k) acc = fmaf(A[i * r + k], B[(int64_t)k * n + j], acc);
-    const float rs = rstar_element((uint64_t)i * (uint64_t)n + (uint64_t)j, c[i], layer_id, seed, tab, dist);
+    const float rs = rstar_element((uint64_t)(i + row0) * (uint64_t)n + (uint64_t)j, c[i], layer_id, seed, tab, dist);
     const float t = rs + acc;
     const bool valid = ptq || w != 0;
     const float q = t / (float)(w != 0 ? w : 1);
@@ -1066,7 +1073,7 @@ static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStre
     const dim3 grid((unsigned)ntiles, (unsigned)cnt);
     unsigned long long* sz = rb0 == 0 ? a.sat_zero : nullptr;
     hipLaunchKernelGGL((k_adapt_mfma<R, W4, PTQ, DIST>), grid, dim3(256), 0, st, a.d, a.n, a.seed, a.layer_id, a.wround, a.z,
-                       a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rtiles, rb0, sz);
+                       a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, rtiles, rb0, sz, a.row0);
   }
   return hipGetLastError();
 }
@@ -1108,7 +1115,7 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   *ntiles_out = ntiles;
   dim3 grid((unsigned)ntiles, (unsigned)(a.d < 65535 ? (a.d ? a.d : 1) : 65535));
   hipLaunchKernelGGL(k_adapt_generic, grid, dim3(256), 0, st, a.d, a.n, a.r, a.w_bits, a.seed, a.layer_id, a.wround,
-                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero, a.ptq, a.dist);
+                     a.z, a.s, a.c, a.A, a.B, a.U, a.pmin, a.pmax, ntiles, a.sat_zero, a.ptq, a.dist, a.row0);
   return hipGetLastError();
 }
 
@@ -1262,14 +1269,14 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
                 w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zr[rg];
                 const float rs = cr[rg] * aux_sample<DIST>(rnd, (unsigned)e, tab);
                 t[e] = rs + acc[ch][rg][e];
-                q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+                q[e] = div_small_int(t[e], (float)w[e], rcp[rcp_index(w[e])]);
                 slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
               }
-              if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+              if (__builtin_amdgcn_ballot_w64(slow || !zero_point_ok(zr[rg])) != 0) {
                 __asm__ volatile("");  // keeps the branch: the division is not speculated
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                  if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+                  if (w[e] != 0 && (!zero_point_ok(zr[rg]) || !div_small_int_ok(t[e]))) q[e] = t[e] / (float)w[e];
               }
               float uu[4];
 #pragma unroll
@@ -1405,18 +1412,19 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
             }
           }
           float t[4], q[4];
-          bool slow = false;
+          const bool zok = zero_point_ok(zi);
+          bool slow = !zok;
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
             t[e] = rs[e] + acc[rr][e];
-            q[e] = div_small_int(t[e], (float)w[e], rcp[w[e] + 255]);
+            q[e] = div_small_int(t[e], (float)w[e], rcp[rcp_index(w[e])]);
             slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
           }
           if (__builtin_amdgcn_ballot_w64(slow) != 0) {
             __asm__ volatile("");  // keeps the branch: the division is not speculated
   #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (w[e] != 0 && !div_small_int_ok(t[e])) q[e] = t[e] / (float)w[e];
+              if (w[e] != 0 && (!zok || !div_small_int_ok(t[e]))) q[e] = t[e] / (float)w[e];
           }
   #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -1515,6 +1523,17 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
 }
 
 __global__ void k_zero_u64(unsigned long long* p) { *p = 0ull; }
+
+__global__ __launch_bounds__(256) void k_fill_u8(int64_t count, uint8_t* __restrict__ p, uint8_t v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+hipError_t launch_fill_u8(int64_t count, uint8_t* p, uint8_t v, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_u8, dim3(grid1((uint64_t)count, 256)), dim3(256), 0, st, count, p, v);
+  return hipGetLastError();
+}
 
 static dim3 quant_grid(int64_t d, int64_t n) {
   const int64_t groups = (d + kQRows - 1) / kQRows;

@@ -73,7 +73,8 @@ def u_minmax(st, A, Bm, w_bits, seed, layer_id, ws=None):
     return umin, umax
 
 
-def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out=None):
+def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out=None, u_range=None):
+    """u_range: optional (u_min, u_max) device tensors [d] used in place of the row range."""
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
@@ -88,7 +89,8 @@ def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out
         o["uround"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
     B.intlora_merge_mul(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), u_bits, o["m"],
                         o["sbar"], o["zbar"], m_split=o.get("split"), u_round_dbg=o.get("uround") if dbg else None,
-                        sat_count=o["sat"], ws=ws)
+                        sat_count=o["sat"], ws=ws, u_min=u_range[0] if u_range else None,
+                        u_max=u_range[1] if u_range else None)
     return o
 
 
@@ -127,7 +129,8 @@ def merge_mul_codes(st, A, Bm, w_bits, u_bits, seed, layer_id, ws=None, out=None
     return o
 
 
-def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, out=None):
+def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, out=None, u_range=None):
+    """u_range: optional (u_min, u_max) device tensors [d] used in place of the row range."""
     d, r = A.shape
     n = Bm.shape[1]
     dev = A.device
@@ -139,7 +142,8 @@ def merge_shift(st, A, Bm, w_bits, v_bits, seed, layer_id, dbg=False, ws=None, o
     if dbg and "shift" not in o:
         o["shift"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
     B.intlora_merge_shift(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), v_bits, o["m"],
-                          o["sbar"], o.get("shift") if dbg else None, o["sat"], ws)
+                          o["sbar"], o.get("shift") if dbg else None, o["sat"], ws,
+                          u_min=u_range[0] if u_range else None, u_max=u_range[1] if u_range else None)
     return o
 
 

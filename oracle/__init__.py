@@ -72,10 +72,10 @@ def _declare(L):
         "ora_base_quant": (None, [_I64, _I64, _I32, _P, _P, _P, _P, _P]),
         "ora_adaptation": (None, [_I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "ora_mul_params": (None, [_I64, _I32, _P, _P, _P, _P]),
-        "ora_merge_mul": (_I64, [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_merge_mul": (_I64, [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32]),
         "ora_log2_round": (_I32, [_F32]),
         "ora_shift_scale": (_F32, [_F32, _F32]),
-        "ora_merge_shift": (_I64, [_I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "ora_merge_shift": (_I64, [_I64, _I64, _I32, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I32]),
         "ora_ptq_merge": (None, [_I64, _I64, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "ora_quant_act": (None, [_I64, _I64, _P, _P, _P, _P]),
         "ora_bf16_rne": (ctypes.c_uint16, [_F32]),
@@ -248,7 +248,8 @@ def mul_params(umin, umax, u_bits):
     return sbar, zbar
 
 
-def merge_mul(wround, z, s, rstar, A, B, u_bits):
+def merge_mul(wround, z, s, rstar, A, B, u_bits, u_range=None):
+    """u_range: optional (u_min, u_max) per row, used in place of the row's own range."""
     wround = _c(wround, np.uint8)
     rows, n = wround.shape
     A = _c(A, np.float32)
@@ -260,10 +261,10 @@ def merge_mul(wround, z, s, rstar, A, B, u_bits):
     ur = np.empty((rows, n), np.uint8)
     sbar = np.empty(rows, np.float32)
     zbar = np.empty(rows, np.int32)
-    umin = np.empty(rows, np.float32)
-    umax = np.empty(rows, np.float32)
+    umin = np.empty(rows, np.float32) if u_range is None else _c(u_range[0], np.float32).copy()
+    umax = np.empty(rows, np.float32) if u_range is None else _c(u_range[1], np.float32).copy()
     sat = lib().ora_merge_mul(rows, n, r, u_bits, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(m), _p(ur),
-                              _p(sbar), _p(zbar), _p(umin), _p(umax))
+                              _p(sbar), _p(zbar), _p(umin), _p(umax), 0 if u_range is None else 1)
     return dict(m=m, uround=ur, sbar=sbar, zbar=zbar, umin=umin, umax=umax, sat=int(sat))
 
 
@@ -278,7 +279,8 @@ def log2_round_batch(a):
     return out
 
 
-def merge_shift(wround, z, s, rstar, A, B, w_bits, v_bits):
+def merge_shift(wround, z, s, rstar, A, B, w_bits, v_bits, u_range=None):
+    """u_range: optional (u_min, u_max) per row, used in place of the row's own range."""
     wround = _c(wround, np.uint8)
     rows, n = wround.shape
     A = _c(A, np.float32)
@@ -289,10 +291,10 @@ def merge_shift(wround, z, s, rstar, A, B, w_bits, v_bits):
     m = np.empty((rows, n), np.int8)
     sh = np.empty((rows, n), np.uint8)
     sbar = np.empty(rows, np.float32)
-    umin = np.empty(rows, np.float32)
-    umax = np.empty(rows, np.float32)
+    umin = np.empty(rows, np.float32) if u_range is None else _c(u_range[0], np.float32).copy()
+    umax = np.empty(rows, np.float32) if u_range is None else _c(u_range[1], np.float32).copy()
     sat = lib().ora_merge_shift(rows, n, r, w_bits, v_bits, _p(wround), _p(z), _p(s), _p(rstar), _p(A), _p(B), _p(m),
-                                _p(sh), _p(sbar), _p(umin), _p(umax))
+                                _p(sh), _p(sbar), _p(umin), _p(umax), 0 if u_range is None else 1)
     return dict(m=m, shift=sh, sbar=sbar, umin=umin, umax=umax, sat=int(sat))
 
 

@@ -374,6 +374,10 @@ ORA_API void ora_adaptation(int64_t rows, int64_t n, int r, const uint8_t* wroun
 /*   U_round = clamp(rint(U / s_bar) + z_bar, 0, 2^bU - 1)  (IEEE division);   */
 /*   m = (U_round - z_bar) * w exactly, stored as int16 with saturation       */
 /*   (counted).  w == 0: U_round = z_bar, m = 0.                               */
+/* The range is the row's own (U_min, U_max) unless range_given is nonzero:    */
+/* then umin_out / umax_out hold a caller's range on entry and are used as it  */
+/* is (s_bar and z_bar only need some range of U; the MUL equation does not   */
+/* say where it comes from).                                                  */
 /* Returns the number of saturated elements.                                  */
 /* ------------------------------------------------------------------------- */
 ORA_API void ora_mul_params(int64_t rows, int u_bits, const float* umin, const float* umax, float* sbar_out,
@@ -394,10 +398,10 @@ ORA_API void ora_mul_params(int64_t rows, int u_bits, const float* umin, const f
 ORA_API int64_t ora_merge_mul(int64_t rows, int64_t n, int r, int u_bits, const uint8_t* wround, const int32_t* z,
                               const float* s, const float* rstar, const float* A, const float* B, int16_t* m_out,
                               uint8_t* uround_out, float* sbar_out, int32_t* zbar_out, float* umin_out,
-                              float* umax_out) {
+                              float* umax_out, int range_given) {
     const int qmax = (1 << u_bits) - 1;
     int64_t sat_total = 0;
-    ora_adaptation(rows, n, r, wround, z, s, rstar, A, B, NULL, umin_out, umax_out);
+    if (!range_given) ora_adaptation(rows, n, r, wround, z, s, rstar, A, B, NULL, umin_out, umax_out);
     ora_mul_params(rows, u_bits, umin_out, umax_out, sbar_out, zbar_out);
 #pragma omp parallel for schedule(static) reduction(+ : sat_total)
     for (int64_t i = 0; i < rows; ++i) {
@@ -490,6 +494,8 @@ ORA_API void ora_ptq_merge(int64_t rows, int64_t n, int r, int bits, const uint8
 /*   arithmetic shift, i.e. floor(w / 2^shift);  V == 0 gives m = 0 and the    */
 /*   largest shift code; m saturates to the signed bW-bit range (counted).    */
 /*   w == 0: m = 0, shift code 255 (marker).                                    */
+/* range_given: as for ora_merge_mul (s_bar = max(|U_min|, |U_max|) of the     */
+/* caller's range).                                                           */
 /* ------------------------------------------------------------------------- */
 ORA_API int ora_log2_round(float a) {
     /* round(log2 a) for finite a > 0, in binary64: the binary32 nearest to a
@@ -512,11 +518,11 @@ ORA_API float ora_shift_scale(float umin, float umax) {
 ORA_API int64_t ora_merge_shift(int64_t rows, int64_t n, int r, int w_bits, int v_bits, const uint8_t* wround,
                                 const int32_t* z, const float* s, const float* rstar, const float* A, const float* B,
                                 int8_t* m_out, uint8_t* shift_out, float* sbar_out, float* umin_out,
-                                float* umax_out) {
+                                float* umax_out, int range_given) {
     const int smax = (1 << v_bits) - 1;
     const int mhi = (1 << (w_bits - 1)) - 1, mlo = -(1 << (w_bits - 1));
     int64_t sat_total = 0;
-    ora_adaptation(rows, n, r, wround, z, s, rstar, A, B, NULL, umin_out, umax_out);
+    if (!range_given) ora_adaptation(rows, n, r, wround, z, s, rstar, A, B, NULL, umin_out, umax_out);
     for (int64_t i = 0; i < rows; ++i) sbar_out[i] = ora_shift_scale(umin_out[i], umax_out[i]);
 #pragma omp parallel for schedule(static) reduction(+ : sat_total)
     for (int64_t i = 0; i < rows; ++i) {

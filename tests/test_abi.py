@@ -70,11 +70,12 @@ def _lora(ptr=FAKE):
     return B.Lora(ptr, ptr)
 
 
-def _merge_mul(lib, dsc, u_bits=8, m=FAKE, ws=FAKE, ws_bytes=1 << 40, base=None, lora=None):
+def _merge_mul(lib, dsc, u_bits=8, m=FAKE, ws=FAKE, ws_bytes=1 << 40, base=None, lora=None, u_min=None,
+               u_max=None):
     base = base or _base()
     lora = lora or _lora()
-    return lib.intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), u_bits, m, FAKE, FAKE,
-                                 None, None, None, ws, ws_bytes, None)
+    return lib.intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(base), ctypes.byref(lora), u_bits, u_min, u_max, m,
+                                 FAKE, FAKE, None, None, None, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("case,expect", [
@@ -92,6 +93,9 @@ def _merge_mul(lib, dsc, u_bits=8, m=FAKE, ws=FAKE, ws_bytes=1 << 40, base=None,
     (dict(dsc=B.desc(8, 8, 4, 8), ws_bytes=64), B.INTLORA_EWORKSPACE),
     (dict(dsc=B.desc(8, 8, 4, 8), base=B.Base(FAKE, 0, FAKE, FAKE)), B.INTLORA_EINVAL),
     (dict(dsc=B.desc(8, 8, 4, 8), lora=B.Lora(FAKE, FAKE + 8)), B.INTLORA_EALIGN),
+    (dict(dsc=B.desc(8, 8, 4, 8), u_min=FAKE), B.INTLORA_EINVAL),             # range: both or neither
+    (dict(dsc=B.desc(8, 8, 4, 8), u_max=FAKE), B.INTLORA_EINVAL),
+    (dict(dsc=B.desc(8, 8, 4, 8), u_min=FAKE, u_max=FAKE + 4), B.INTLORA_EALIGN),
 ])
 def test_merge_mul_validation(lib, case, expect):
     st = _merge_mul(lib, **case)
@@ -117,8 +121,10 @@ def test_aux_dist_field_and_null_desc(lib):
 def test_other_entry_points_validation(lib):
     d = B.desc(8, 8, 4, 8)
     base, lora = _base(), _lora()
-    assert lib.intlora_merge_shift(ctypes.byref(d), ctypes.byref(base), ctypes.byref(lora), 0, FAKE, FAKE, None,
-                                   None, FAKE, 1 << 40, None) == B.INTLORA_EINVAL  # v_bits 0
+    assert lib.intlora_merge_shift(ctypes.byref(d), ctypes.byref(base), ctypes.byref(lora), 0, None, None, FAKE, FAKE,
+                                   None, None, FAKE, 1 << 40, None) == B.INTLORA_EINVAL  # v_bits 0
+    assert lib.intlora_merge_shift(ctypes.byref(d), ctypes.byref(base), ctypes.byref(lora), 4, FAKE, None, FAKE, FAKE,
+                                   None, None, FAKE, 1 << 40, None) == B.INTLORA_EINVAL  # one range bound only
     assert lib.intlora_stats(ctypes.byref(d), 7, FAKE, None, None, FAKE, FAKE, None, 0, None) == B.INTLORA_EINVAL
     assert lib.intlora_stats(ctypes.byref(d), B.INTLORA_U_MINMAX, None, ctypes.byref(base), ctypes.byref(lora),
                              FAKE, FAKE, FAKE, 16, None) == B.INTLORA_EWORKSPACE

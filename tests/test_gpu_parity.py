@@ -218,6 +218,66 @@ def test_merge_shift_bitexact(ops, d, n, r, w_bits):
         assert int(host(g["sat"])[0]) == ref["sat"]
 
 
+@pytest.mark.parametrize("d,n,r,w_bits", [(37, 1000, 8, 8), (64, 777, 4, 4), (96, 3072, 32, 4)])
+def test_merge_caller_range(ops, d, n, r, w_bits):
+    """u_min / u_max given by the caller: the row range of intlora_stats gives the same
+    bits as the merge's own; a narrower caller range (codes clamp, SHIFT sees |V| > 1)
+    matches the oracle run on that range.  The split codes are still written."""
+    seed = 260 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    st = gpu_state(wr, z, s, c, w_bits)
+    Ag, Bg = cuda(A), cuda(Bm)
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+    umin, umax = ops.u_minmax(st, Ag, Bg, w_bits, 77, 5)
+    own = ops.merge_mul(st, Ag, Bg, w_bits, 4, 77, 5, dbg=True)
+    given = ops.merge_mul(st, Ag, Bg, w_bits, 4, 77, 5, dbg=True, u_range=(umin, umax))
+    for k in ("m", "uround", "sbar", "zbar", "split", "sat"):
+        assert torch.equal(own[k], given[k]), k
+    nmin = (umin * 0.5).contiguous()
+    nmax = (umax * 0.25).contiguous()
+    g = ops.merge_mul(st, Ag, Bg, w_bits, 4, 77, 5, dbg=True, u_range=(nmin, nmax))
+    ref = oracle.merge_mul(wr, z, s, R, A, Bm, 4, u_range=(host(nmin), host(nmax)))
+    assert np.array_equal(host(g["m"]), ref["m"])
+    assert np.array_equal(host(g["uround"]), ref["uround"])
+    assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+    assert np.array_equal(host(g["zbar"]), ref["zbar"])
+    assert np.array_equal(host(g["split"]), oracle.plane_split(ref["m"]))
+    for v_bits in (4,):
+        g = ops.merge_shift(st, Ag, Bg, w_bits, v_bits, 77, 5, dbg=True, u_range=(nmin, nmax))
+        ref = oracle.merge_shift(wr, z, s, R, A, Bm, w_bits, v_bits, u_range=(host(nmin), host(nmax)))
+        m = host(g["m"])
+        m = unpack4s(m) if w_bits == 4 else m.view(np.int8)
+        assert np.array_equal(m, ref["m"])
+        assert np.array_equal(host(g["shift"]), ref["shift"])
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert int(host(g["sat"])[0]) == ref["sat"]
+
+
+@pytest.mark.parametrize("w_bits", [4, 8])
+def test_merge_zero_point_outside_code_range(ops, w_bits):
+    """Zero points outside [0, 2^w_bits - 1] (|W_round - z| up to 2^20 here) take the
+    IEEE division in every merge, and the results still equal the oracle's."""
+    d, n, r = 64, 520, 8
+    wr, z, s, c, A, Bm = random_state(290 + w_bits, d, n, r, w_bits)
+    z = z.copy()
+    z[::3] = np.array([-300, 1 << 20, 256, -(1 << 20)] * 8, np.int32)[: len(z[::3])]
+    st = gpu_state(wr, z, s, c, w_bits)
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+    ref = oracle.merge_mul(wr, z, s, R, A, Bm, 8)
+    for fn in (ops.merge_mul, ops.merge_mul_fused):
+        g = fn(st, cuda(A), cuda(Bm), w_bits, 8, 77, 5, dbg=True)
+        assert np.array_equal(host(g["m"]), ref["m"]), fn.__name__
+        assert np.array_equal(host(g["uround"]), ref["uround"])
+        assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+        assert int(host(g["sat"])[0]) == ref["sat"]
+    g = ops.merge_shift(st, cuda(A), cuda(Bm), w_bits, 4, 77, 5, dbg=True)
+    refs = oracle.merge_shift(wr, z, s, R, A, Bm, w_bits, 4)
+    m = host(g["m"])
+    m = unpack4s(m) if w_bits == 4 else m.view(np.int8)
+    assert np.array_equal(m, refs["m"])
+    assert np.array_equal(host(g["shift"]), refs["shift"])
+
+
 @pytest.mark.parametrize("d,n,r,w_bits", MERGE_CASES)
 def test_merge_ptq_bitexact(ops, d, n, r, w_bits):
     """QLoRA-style comparison path: x = (s w + R*) + AB and the per-row requant, codes,

@@ -133,17 +133,25 @@ def test_mul_quantization_error_bound(ora):
         assert np.all(out["uround"] <= qmax)
 
 
-def test_mul_exhaustive_4bit_grid(ora):
+@pytest.mark.parametrize("given", ["own", "caller_narrow", "caller_wide"])
+def test_mul_exhaustive_4bit_grid(ora, given):
     """Every (W_round, z) pair of 4-bit codes, random U: codes follow the definition
-    computed with exact rationals (IEEE divide, half-even rint, clamps)."""
+    computed with exact rationals (IEEE divide, half-even rint, clamps).  The row range
+    is the row's own, or a range the caller supplies: a narrower one (codes clamp) and
+    a wider one."""
     z = np.repeat(np.arange(16, dtype=np.int32), 1)
     wr = np.tile(np.arange(16, dtype=np.uint8), (16, 1))  # row i: z = i, all W_round
     s = synth.random_positive(40, 16, 1e-3, 1e-1)
     Rs = synth.random_matrix(41, (16, 16), 0.01)
     A = synth.random_matrix(42, (16, 2), 0.5)
     B = synth.random_matrix(43, (2, 16), 0.03)
-    out = ora.merge_mul(wr, z, s, Rs, A, B, 4)
     u, umin, umax = ora.adaptation(wr, z, s, Rs, A, B)
+    if given == "caller_narrow":
+        umin, umax = (umin * np.float32(0.5)).astype(np.float32), (umax * np.float32(0.25)).astype(np.float32)
+    elif given == "caller_wide":
+        umin, umax = (umin * np.float32(3.0) - np.float32(0.01)).astype(np.float32), \
+            (umax * np.float32(2.0) + np.float32(0.02)).astype(np.float32)
+    out = ora.merge_mul(wr, z, s, Rs, A, B, 4, u_range=None if given == "own" else (umin, umax))
     for i in range(16):
         lo = min(umin[i], np.float32(0.0))
         hi = max(umax[i], np.float32(0.0))
@@ -223,18 +231,24 @@ def test_shift_special_case_u_equals_s(ora):
         assert out["sat"] == int(np.sum((w > lim_hi) | (w < lim_lo)))
 
 
-def test_shift_merge_against_definition(ora):
-    """Arithmetic shift (numpy right_shift), sign of V and the exact log2 rule."""
+@pytest.mark.parametrize("given", [False, True])
+def test_shift_merge_against_definition(ora, given):
+    """Arithmetic shift (numpy right_shift), sign of V and the exact log2 rule; with the
+    row's own range, or a caller's narrower one (then |V| > 1 occurs, and a shift clamps
+    at 0)."""
     for wl_index, bits in ((1, 4), (2, 8)):
         W, A, B, st = _layer(ora, wl_index, 16, 257, 4)
-        out = ora.merge_shift(st["wround"], st["z"], st["s"], st["rstar"], A, B, bits, 4)
         u, umin, umax = ora.adaptation(st["wround"], st["z"], st["s"], st["rstar"], A, B)
+        if given:
+            umin, umax = (umin * np.float32(0.5)).astype(np.float32), (umax * np.float32(0.5)).astype(np.float32)
+        out = ora.merge_shift(st["wround"], st["z"], st["s"], st["rstar"], A, B, bits, 4,
+                              u_range=(umin, umax) if given else None)
         w = algebra.signed_base(st["wround"], st["z"])
         valid = w != 0
         sbar = np.maximum(np.abs(umin), np.abs(umax))
         assert np.array_equal(out["sbar"], sbar)
         V = (u / sbar[:, None]).astype(np.float32)
-        assert np.all(np.abs(V[valid]) <= 1.0)
+        assert given or np.all(np.abs(V[valid]) <= 1.0)
         k = np.where(valid & (V != 0), _log2_round_exact(np.abs(np.where(valid & (V != 0), V, 1.0)).astype(np.float32)), 0)
         sh = np.clip(-k, 0, 15)
         sh = np.where(V == 0, 15, sh)
