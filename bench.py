@@ -64,6 +64,14 @@ def parse():
                    help="skip the step captured in a HIP graph and replayed (reported beside the eager step)")
     p.add_argument("--no-aux-laws", action="store_true",
                    help="skip the merge timed under the other auxiliary laws (Gaussian, Cauchy, Student-t(2))")
+    p.add_argument("--kernel-runs", type=int, default=100,
+                   help="runs per kernel for the per-kernel medians (merge warm, merge cold, linear layer)")
+    p.add_argument("--flush-mib", type=int, default=1024,
+                   help="bytes streamed through HBM before each cold merge run (defeats the 256 MB Infinity Cache)")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="skip the merge-only sweep over the 32 transformer blocks x 7 matrices of the "
+                        "Llama-3-8B-shaped workload")
+    p.add_argument("--sweep-blocks", type=int, default=32, help="transformer blocks in the merge-only sweep")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -167,6 +175,10 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
     code_b = 0.5 if wl.w_bits == 4 else 1.0
     alg = sum(lay["L"].d * lay["L"].n * 2 * code_b for lay in layers)  # base codes in, new codes out
     return dict(kind="dequantize + add R* + AB (binary32) + per-row RTN requant at %d bits" % wl.w_bits,
+                error_note="errors against s w + R* + AB with the synthetic adapter, whose B has variance 1e-3 "
+                           "(the workload's N(0, 1e-3) read as a variance): AB is then several times larger than "
+                           "W, which widens U's range and the MUL step s_bar; they say little about the method, "
+                           "whose training starts from B = 0",
                 ptq_merge_us_per_step=round(ptq_ms * 1e3, 1),
                 alg_GBps=round(alg / (ptq_ms * 1e-3) / 1e9, 1),
                 pct_hbm_peak=round(100 * alg / (ptq_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
@@ -278,6 +290,20 @@ def codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits):
             if events is not None:
                 events[k][2].record(stream)
 
+    def merge_fn(k):
+        lay = layers[k]
+        if mode == "mul":
+            ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws,
+                          out=lay["out"])
+        else:
+            ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws,
+                            out=lay["out"])
+
+    def gemm_fn(k):
+        lay = layers[k]
+        ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"], lay["L"].d,
+                   out=lay["Y"], split=lay["out"].get("split"))
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -347,6 +373,135 @@ def ste_measure(args, wl, layers, ops, torch, dev, stream):
                 fp32_mfma_TFLOPs=round(flops / (ms * 1e-3) / 1e12, 1),
                 bound="mfma" if t_mfma >= t_hbm else "hbm",
                 frac_of_bound=round(max(t_hbm, t_mfma) / (ms * 1e-3), 3))
+
+
+def kernel_medians(args, layers, merge_fn, gemm_fn, torch, dev, stream):
+    """Per-layer kernel times, median of `args.kernel_runs` runs each (after 10 untimed
+    ones): the merge warm (back to back, so a layer's inputs may sit in the 256 MB
+    Infinity Cache), the merge cold (a 1 GiB buffer is written through HBM before each
+    run, evicting L2 and the Infinity Cache), and the linear layer (warm: it is bound by
+    the matrix cores).  HIP events on the stream the kernels run on."""
+    runs = max(1, args.kernel_runs)
+    flush = torch.empty(max(1, args.flush_mib) << 20, dtype=torch.uint8, device=dev)
+
+    def timed(fn, k, cold):
+        for _ in range(10):
+            fn(k)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(runs)]
+        for e0, e1 in ev:
+            if cold:
+                flush.fill_(1)
+            e0.record(stream)
+            fn(k)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        return float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3
+
+    out = []
+    for k in range(len(layers)):
+        out.append(dict(merge_warm_us=round(timed(merge_fn, k, False), 2),
+                        merge_cold_us=round(timed(merge_fn, k, True), 2),
+                        gemm_us=round(timed(gemm_fn, k, False), 2)))
+    del flush
+    return out
+
+
+def profile_counters(workload_name):
+    """Per-kernel counter figures from the committed rocprofv3 summary of this workload
+    (profiles/<workload>_counters.json), if it was taken on the current kernel sources;
+    else None."""
+    path = os.path.join(ROOT, "profiles", workload_name + "_counters.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        rec = json.load(open(path))
+    except Exception:
+        return None
+    from integer_rank_adaptation_amd.profiling import library_source_sha
+
+    if rec.get("library_source_sha") != library_source_sha() or rec.get("workload") != workload_name:
+        return None
+    return rec
+
+
+def sweep_measure(args, ops, B, synth, torch, dev, stream):
+    """The merge-only sweep of the Llama-3-8B-shaped workload: the MUL merge (U 8-bit,
+    r = 64) of every matrix of `args.sweep_blocks` transformer blocks (7 matrices each,
+    6.98 G weights over 32 blocks), each with its own weights, factors and layer id.
+    Inputs are set up on the GPU first (untimed); one sweep merges every matrix back to
+    back into its own output, so the 21 GB of codes and merged integers stream through
+    HBM.  Several sweeps are timed; per-shape figures are medians over the matrices of
+    that shape and the sweeps."""
+    wl = synth.WORKLOADS[4]
+    mode, mbits = wl.modes[0]
+    nb = max(1, min(args.sweep_blocks, wl.sweep_layers))
+    t0 = time.time()
+    mats = []
+    ws_bytes = 0
+    for blk in range(nb):
+        for li, L in enumerate(wl.layers):
+            lid = synth.layer_id(wl.index, li, blk)
+            Wg = torch.from_numpy(synth.sweep_weight(wl, li, blk)).to(dev)
+            st = ops.setup_layer(Wg, wl.w_bits, synth.PHILOX_SEED, lid, synth.ALPHA)
+            del Wg
+            A, Bm = synth.lora(wl, li, block=blk)
+            ws_bytes = max(ws_bytes, B.intlora_workspace_bytes(B.INTLORA_OP_MERGE_MUL, B.desc(L.d, L.n, wl.r,
+                                                                                               wl.w_bits)))
+            st.pop("sigma", None)
+            mats.append(dict(L=L, lid=lid, st=st, Ag=torch.from_numpy(A).to(dev), Bg=torch.from_numpy(Bm).to(dev),
+                             out=dict(m=torch.empty((L.d, L.n), dtype=torch.int16, device=dev),
+                                      sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
+                                      zbar=torch.empty(L.d, dtype=torch.int32, device=dev),
+                                      split=torch.empty(L.d, dtype=torch.uint8, device=dev),
+                                      sat=torch.zeros(2, dtype=torch.int64, device=dev))))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def one(mt):
+        ops.merge_mul(mt["st"], mt["Ag"], mt["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, mt["lid"], ws=ws,
+                      out=mt["out"])
+
+    for mt in mats:  # warm-up sweep
+        one(mt)
+    torch.cuda.synchronize()
+    sweeps = 5
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in mats]
+          for _ in range(sweeps)]
+    tot = []
+    for sw in range(sweeps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for k, mt in enumerate(mats):
+            ev[sw][k][0].record(stream)
+            one(mt)
+            ev[sw][k][1].record(stream)
+        b.record(stream)
+        tot.append((a, b))
+    torch.cuda.synchronize()
+    sweep_ms = float(np.median([a.elapsed_time(b) for a, b in tot]))
+    elems = sum(mt["L"].d * mt["L"].n for mt in mats)
+    alg = sum(merge_alg_bytes(mt["L"].d, mt["L"].n, wl.r, wl.w_bits, mode) for mt in mats)
+    per_shape = []
+    for L in wl.layers:
+        ks = [k for k, mt in enumerate(mats) if mt["L"] is L]
+        us = float(np.median([ev[sw][k][0].elapsed_time(ev[sw][k][1]) for sw in range(sweeps) for k in ks])) * 1e3
+        mb = merge_alg_bytes(L.d, L.n, wl.r, wl.w_bits, mode)
+        per_shape.append(dict(matrix=L.name, d=L.d, n=L.n, count=len(ks), merge_us_median=round(us, 2),
+                              alg_GBps=round(mb / (us * 1e-6) / 1e9, 1),
+                              pct_hbm_peak=round(100 * mb / (us * 1e-6) / 1e9 / HBM_PEAK_GBPS, 2),
+                              G_weights_per_s=round(L.d * L.n / (us * 1e-6) / 1e9, 1)))
+    sat = int(sum(int(mt["out"]["sat"][0].item()) for mt in mats))
+    del mats, ws
+    torch.cuda.empty_cache()
+    return dict(blocks=nb, matrices=nb * len(wl.layers), weights=elems, sweeps_timed=sweeps,
+                sweep_ms_median=round(sweep_ms, 3), alg_GBps=round(alg / (sweep_ms * 1e-3) / 1e9, 1),
+                pct_hbm_peak=round(100 * alg / (sweep_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                G_weights_per_s=round(elems / (sweep_ms * 1e-3) / 1e9, 1), saturated=sat,
+                setup_s=round(setup_s, 1), per_shape=per_shape,
+                inputs="W per matrix drawn by synth.sweep_weight (row chunks seeded per block and matrix), "
+                       "set up on the GPU; layer id 7 * block + matrix")
 
 
 def main():
@@ -430,6 +585,20 @@ def main():
             if events is not None:
                 events[k][2].record(stream)
 
+    def merge_fn(k):
+        lay = layers[k]
+        if mode == "mul":
+            ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws,
+                          out=lay["out"])
+        else:
+            ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws,
+                            out=lay["out"])
+
+    def gemm_fn(k):
+        lay = layers[k]
+        ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"], lay["L"].d,
+                   out=lay["Y"], split=lay["out"].get("split"))
+
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -444,6 +613,9 @@ def main():
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+
+    # ---------------------------------------------------------------- per-kernel medians (untimed region)
+    medians = kernel_medians(args, layers, merge_fn, gemm_fn, torch, dev, stream) if args.kernel_runs > 0 else None
 
     # ---------------------------------------------------------------- pipelined step (optional)
     # The merges run on a side stream, each layer's linear layer waiting only for its own
@@ -520,7 +692,12 @@ def main():
     if not args.no_ste:
         ste = ste_measure(args, wl, layers, ops, torch, dev, stream)
 
+    sweep = None
+    if not args.no_sweep and M > 32:
+        sweep = sweep_measure(args, ops, B, synth, torch, dev, stream)
+
     # ---------------------------------------------------------------- per-layer figures
+    counters = profile_counters(wl.name)
     per_layer = []
     roof_ms = 0.0
     merge_bytes_tot = merge_ms_tot = gemm_ops_tot = gemm_ms_tot = 0.0
@@ -530,19 +707,31 @@ def main():
         gms = float(np.mean([ev[s][k][1].elapsed_time(ev[s][k][2]) for s in range(args.steps)]))
         mb = merge_alg_bytes(L.d, L.n, wl.r, wl.w_bits, mode)
         gops = gemm_exec_ops(M, L.d, L.n, mode)
+        eops = 2.0 * M * L.d * L.n  # the method's int16 x int8 (or int8 x int8) products, once
         roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + gops / (INT8_PEAK_TOPS * 1e12) * 1e3
         merge_bytes_tot += mb
         merge_ms_tot += mms
         gemm_ops_tot += gops
         gemm_ms_tot += gms
-        per_layer.append(dict(layer=L.name, d=L.d, n=L.n, merge_us=round(mms * 1e3, 2),
-                              merge_alg_GBps=round(mb / (mms * 1e-3) / 1e9, 1),
-                              merge_pct_hbm=round(100 * mb / (mms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
-                              gemm_us=round(gms * 1e3, 2), gemm_TOPS=round(gops / (gms * 1e-3) / 1e12, 1),
-                              gemm_pct_int8_peak=round(100 * gops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
-                              sat=int(lay["out"]["sat"][0].item()),
-                              int16_split=("balanced" if not bool(lay["out"]["split"].any()) else "bias")
-                              if "split" in lay["out"] else None))
+        row = dict(layer=L.name, d=L.d, n=L.n, merge_us=round(mms * 1e3, 2),
+                   merge_alg_GBps=round(mb / (mms * 1e-3) / 1e9, 1),
+                   merge_pct_hbm=round(100 * mb / (mms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+                   gemm_us=round(gms * 1e3, 2), gemm_exec_TOPS=round(gops / (gms * 1e-3) / 1e12, 1),
+                   gemm_exec_pct_int8_peak=round(100 * gops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+                   gemm_effective_TOPS=round(eops / (gms * 1e-3) / 1e12, 1),
+                   gemm_effective_pct_int8_peak=round(100 * eops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+                   sat=int(lay["out"]["sat"][0].item()),
+                   int16_split=("balanced" if not bool(lay["out"]["split"].any()) else "bias")
+                   if "split" in lay["out"] else None)
+        if medians is not None:
+            md = medians[k]
+            row.update(merge_warm_us_median=md["merge_warm_us"], merge_cold_us_median=md["merge_cold_us"],
+                       merge_cold_alg_GBps=round(mb / (md["merge_cold_us"] * 1e-6) / 1e9, 1),
+                       gemm_us_median=md["gemm_us"],
+                       gemm_exec_TOPS_median=round(gops / (md["gemm_us"] * 1e-6) / 1e12, 1))
+        if counters is not None:
+            row["counters"] = counters["per_layer"].get(L.name)
+        per_layer.append(row)
     value = 100.0 * roof_ms / ms_per_step
     gemm_avg_ms = gemm_ms_tot / len(layers)
     achieved = gemm_ops_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e12
@@ -571,8 +760,18 @@ def main():
                   "pct_hbm_peak": round(100 * merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                   "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (Philox, the Laplace ln and the division per element in the adaptation kernel)"},
         "gemm": {"exec_TOPS": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
+                 "exec_frac_int8_peak": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                  "effective_TOPS": round(gemm_ops_tot / (2 if mode == "mul" else 1) / (gemm_ms_tot * 1e-3) / 1e12, 1),
+                 "effective_frac_int8_peak": round(gemm_ops_tot / (2 if mode == "mul" else 1) /
+                                                   (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                 "exec_vs_effective": "exec counts the int8 MFMA operations run (two byte planes per int16 "
+                                      "merged integer for MUL); effective counts each int16 x int8 product once",
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
+        "kernel_timing": {"runs": args.kernel_runs, "statistic": "median",
+                          "cold": "a %d MiB buffer written through HBM before each cold merge run" % args.flush_mib}
+        if medians is not None else None,
+        "counters": {k: counters[k] for k in ("command", "calibration", "roofline_merge", "roofline_adapt")
+                     if k in counters} if counters is not None else None,
         "per_layer": per_layer,
         "overlap_ms_per_step": round(overlap_ms, 4) if overlap_ms is not None else None,
         "overlap_equals_sequential": overlap_same,
@@ -582,8 +781,13 @@ def main():
         "merge_on_load": codes,
         "ste_backward": ste,
         "aux_laws": aux_laws,
+        "sweep": sweep,
         "setup_s": round(setup_s, 1),
     }
+    if counters is not None:
+        for key in ("roofline_merge", "roofline_adapt"):
+            if key in counters:
+                result[key] = counters[key]
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
     if not args.no_cpu_baseline:
@@ -641,37 +845,65 @@ def cpu_baseline(wl, layers, M, mode, mbits, roof_ms, frac):
     threads = oracle.num_threads()
     if frac <= 0.0:
         frac = 1.0 / 3.0
-    t_total = 0.0
-    for lay in layers:
-        L = lay["L"]
-        # stored state of the oracle's own set-up (untimed)
-        ost = oracle.setup_layer(lay["W"], synth.PHILOX_SEED, lay["lid"], wl.w_bits, synth.ALPHA)
-        rows = max(1, int(round(L.d * frac)))
-        toks = max(1, int(round(M * frac)))
-        xq, sx, _ = oracle.quant_act(lay["X"][:toks])
-        t0 = time.perf_counter()
-        R = oracle.gen_r_rows(0, rows, L.n, synth.PHILOX_SEED, lay["lid"], ost["c"][:rows])
-        if mode == "mul":
-            ref = oracle.merge_mul(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows], lay["B"],
-                                   mbits)
-        else:
-            ref = oracle.merge_shift(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows],
-                                     lay["B"], wl.w_bits, mbits)
-        t1 = time.perf_counter()
-        # the linear layer over all outputs needs every merged row: use the sampled rows'
-        # merged integers tiled to d rows (same cost as the true d x n product)
-        m_full = np.resize(ref["m"].astype(np.int32), (L.d, L.n))
-        sbar_full = np.resize(ref["sbar"], L.d)
-        t2 = time.perf_counter()
-        oracle.linear(xq, sx, m_full, sbar_full, want_exact=False)
-        t3 = time.perf_counter()
-        t_total += (t1 - t0) * (L.d / rows) + (t3 - t2) * (M / toks)
+    osts = [oracle.setup_layer(lay["W"], synth.PHILOX_SEED, lay["lid"], wl.w_bits, synth.ALPHA)
+            for lay in layers]  # the oracle's own stored state (untimed)
+
+    def step_time(fr):
+        """Oracle time of the step's merges on the first `fr` of each layer's rows and its
+        linear layers on the first `fr` of the tokens, scaled to a full step."""
+        t_total = 0.0
+        for lay, ost in zip(layers, osts):
+            L = lay["L"]
+            rows = max(1, int(round(L.d * fr)))
+            toks = max(1, int(round(M * fr)))
+            xq, sx, _ = oracle.quant_act(lay["X"][:toks])
+            t0 = time.perf_counter()
+            R = oracle.gen_r_rows(0, rows, L.n, synth.PHILOX_SEED, lay["lid"], ost["c"][:rows])
+            if mode == "mul":
+                ref = oracle.merge_mul(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows],
+                                       lay["B"], mbits)
+            else:
+                ref = oracle.merge_shift(ost["wround"][:rows], ost["z"][:rows], ost["s"][:rows], R, lay["A"][:rows],
+                                         lay["B"], wl.w_bits, mbits)
+            t1 = time.perf_counter()
+            # the linear layer over all outputs needs every merged row: the sampled rows'
+            # merged integers tiled to d rows (the same cost as the true d x n product)
+            m_full = np.resize(ref["m"].astype(np.int32), (L.d, L.n))
+            sbar_full = np.resize(ref["sbar"], L.d)
+            t2 = time.perf_counter()
+            oracle.linear(xq, sx, m_full, sbar_full, want_exact=False)
+            t3 = time.perf_counter()
+            t_total += (t1 - t0) * (L.d / rows) + (t3 - t2) * (M / toks)
+        return t_total
+
+    t_total = step_time(frac)
+    repeats = 1
+    if t_total < 2.0:  # small workloads: best of 3
+        t_total = min([t_total] + [step_time(frac) for _ in range(2)])
+        repeats = 3
+    frac1 = frac if t_total < 2.0 else frac / 16.0
+    oracle.set_threads(1)
+    try:
+        t_single = step_time(frac1)
+    finally:
+        oracle.set_threads(threads)
     value = 100.0 * roof_ms / (t_total * 1e3)
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": round(value, 6), "unit": "% of MI355X peak (same definition; oracle step time)",
             "cores": threads, "kind": "oracle",
-            "sample": "every layer: merge of the first %.4g of rows, linear on the first %.4g of tokens; "
-                      "scaled to a full step (%.1f s per full step)" % (frac, frac, t_total),
+            "sample": "fraction %.4g of every layer's rows (merge) and tokens (linear), scaled to a full step "
+                      "(%.1f s per full step on %d threads)" % (frac, t_total, threads),
+            "sample_fraction": round(frac, 6), "repeats": repeats,
             "step_s": round(t_total, 2),
+            "single_thread_step_s": round(t_single, 2), "single_thread_sample_fraction": round(frac1, 6),
+            "cpu_model": model, "omp_num_threads_env": os.environ.get("OMP_NUM_THREADS"),
             "next_rows_s_per_step": cpu_next_rows(wl, layers, M, mode, mbits, t_total)}
 
 

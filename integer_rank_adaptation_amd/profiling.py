@@ -39,6 +39,18 @@ def kernel_source_sha():
     return h.hexdigest()[:16]
 
 
+def library_source_sha():
+    """Hash of every source of the library; the per-kernel counter summary records it,
+    so figures taken on other kernels are not reused."""
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "integer_rank_adaptation_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h", ".inc")):
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
 def short_name(full):
     m = OURS.search(full)
     if m:
@@ -136,6 +148,119 @@ def traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, workload, kernel):
                 hbm_bytes_per_launch=round(avg) if avg is not None else None, kernels=kernels)
 
 
+# The kernels of one step of the benchmark, in launch order per layer (the merge's three
+# kernels, then the linear layer).  Their launches cycle through the layers in order, so
+# launch k of a kernel belongs to layer k mod L.
+STEP_KERNELS = ("k_adapt_mfma", "k_adapt_generic", "k_row_range", "k_quant_mul", "k_quant_shift", "k_linear")
+CLOCK_HZ = 2.4e9
+SIMDS = 256 * 4
+
+
+def _by_layer(rows, layers, value):
+    """{kernel base name: [per-layer list of values]} for the step kernels, launch k of a
+    kernel -> layer k mod len(layers); other kernels (set-up) are left out."""
+    seq = collections.OrderedDict()
+    for r in sorted(rows, key=lambda r: r["dispatch"]):
+        base = r["name"].split("<")[0]
+        if base not in STEP_KERNELS:
+            continue
+        seq.setdefault(r["name"], []).append(value(r))
+    out = {}
+    for name, vals in seq.items():
+        per = [[] for _ in layers]
+        for k, v in enumerate(vals):
+            per[k % len(layers)].append(v)
+        out[name] = per
+    return out
+
+
+def read_trace_rows(d):
+    rows = list(csv.DictReader(open(_one(d, "*kernel_trace.csv"))))
+    return [dict(name=short_name(r["Kernel_Name"]), us=(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3,
+                 dispatch=int(r["Dispatch_Id"])) for r in rows]
+
+
+def read_counter_rows(d):
+    rows = list(csv.DictReader(open(_one(d, "*counter_collection.csv"))))
+    return [dict(name=short_name(r["Kernel_Name"]), counter=r["Counter_Name"], v=float(r["Counter_Value"]),
+                 dispatch=int(r["Dispatch_Id"])) for r in rows]
+
+
+def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, commands):
+    """Per layer and kernel of the step: median duration (kernel trace), HBM bytes
+    (FETCH_SIZE / WRITE_SIZE scaled by a plain copy of known size), and the SQ / GRBM
+    counters of the other runs; derived: counter GB/s, the clock during the kernel
+    (GRBM_GUI_ACTIVE / duration), the vector-ALU issue fraction (4 cycles per wave64
+    VALU instruction on a 16-lane SIMD; of the cycles at the measured clock, and of the
+    2.4 GHz peak) and the matrix-core busy fraction."""
+    import statistics
+
+    ff, fk = copy_factor(cf_dir, "FETCH_SIZE", copy_bytes)
+    wf, wk = copy_factor(cw_dir, "WRITE_SIZE", copy_bytes)
+    dur = _by_layer(read_trace_rows(trace_dir), layers, lambda r: r["us"])
+    vals = collections.defaultdict(dict)  # kernel -> counter -> per-layer lists
+    for d in pmc_dirs:
+        rows = read_counter_rows(d)
+        for cname in sorted({r["counter"] for r in rows}):
+            sel = [r for r in rows if r["counter"] == cname]
+            for kname, per in _by_layer(sel, layers, lambda r: r["v"]).items():
+                vals[kname][cname] = per
+    med = lambda xs: statistics.median(xs) if xs else None
+    per_layer = {L: {} for L in layers}
+    for kname, per in dur.items():
+        for li, L in enumerate(layers):
+            rec = dict(us=round(med(per[li]), 3) if per[li] else None, launches=len(per[li]))
+            cv = {c: med(v[li]) for c, v in vals.get(kname, {}).items() if v[li]}
+            if "FETCH_SIZE" in cv:
+                rec["fetch_bytes"] = round(cv["FETCH_SIZE"] * 1024 * ff)
+            if "WRITE_SIZE" in cv:
+                rec["write_bytes"] = round(cv["WRITE_SIZE"] * 1024 * wf)
+            if rec["us"] and "fetch_bytes" in rec and "write_bytes" in rec:
+                rec["hbm_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+                rec["counter_GBps"] = round(rec["hbm_bytes"] / (rec["us"] * 1e-6) / 1e9, 1)
+                rec["counter_pct_hbm_peak"] = round(100 * rec["counter_GBps"] / 8000.0, 2)
+            for c, v in cv.items():
+                if c not in ("FETCH_SIZE", "WRITE_SIZE"):
+                    rec[c] = v
+            if rec["us"] and cv.get("GRBM_GUI_ACTIVE"):
+                rec["clock_GHz"] = round(cv["GRBM_GUI_ACTIVE"] / (rec["us"] * 1e-6) / 1e9, 3)
+            if rec["us"] and cv.get("SQ_INSTS_VALU"):
+                rec["valu_frac_of_peak"] = round(cv["SQ_INSTS_VALU"] * 4 / (rec["us"] * 1e-6 * CLOCK_HZ * SIMDS), 4)
+                if cv.get("GRBM_GUI_ACTIVE"):
+                    rec["valu_frac_at_clock"] = round(cv["SQ_INSTS_VALU"] * 4 / (cv["GRBM_GUI_ACTIVE"] * SIMDS), 4)
+            if cv.get("SQ_VALU_MFMA_BUSY_CYCLES") and cv.get("GRBM_GUI_ACTIVE"):
+                rec["mfma_busy_frac"] = round(cv["SQ_VALU_MFMA_BUSY_CYCLES"] / (cv["GRBM_GUI_ACTIVE"] * SIMDS), 4)
+            per_layer[L][kname] = rec
+    out = dict(workload=workload, library_source_sha=library_source_sha(), command=commands,
+               calibration=dict(copy_bytes=copy_bytes, copy_fetch_kib=fk, copy_write_kib=wk,
+                                fetch_scale=round(ff, 6), write_scale=round(wf, 6)),
+               per_layer=per_layer)
+    # rooflines of the merge's quantize kernel (HBM) and adaptation kernel (vector ALU),
+    # aggregated over the step's layers
+    for key, prefix, unit in (("roofline_merge", ("k_quant_mul", "k_quant_shift"), "GB/s"),
+                              ("roofline_adapt", ("k_adapt_mfma", "k_adapt_generic"), "valu")):
+        keyed = [(k, r) for L in layers for k, r in per_layer[L].items() if k.startswith(prefix) and r.get("us")]
+        if not keyed:
+            continue
+        recs = [r for _, r in keyed]
+        kname = ", ".join(sorted({k for k, _ in keyed}))
+        t = sum(r["us"] for r in recs) * 1e-6
+        if unit == "GB/s" and all("hbm_bytes" in r for r in recs):
+            b = sum(r["hbm_bytes"] for r in recs)
+            out[key] = dict(bound="hbm", kernel=kname, achieved=round(b / t / 1e9, 1), peak=8000.0,
+                            unit="GB/s", frac=round(b / t / 1e9 / 8000.0, 4), traffic=round(b / len(layers)),
+                            source="rocprofv3 FETCH_SIZE + WRITE_SIZE (copy-calibrated) over kernel-trace time, "
+                                   "summed over the step's layers")
+        elif unit == "valu" and all("SQ_INSTS_VALU" in r for r in recs):
+            n = sum(r["SQ_INSTS_VALU"] for r in recs)
+            lane = n * 64 / t / 1e12
+            out[key] = dict(bound="alu", kernel=kname, achieved=round(lane, 2), peak=39.32,
+                            unit="T lane-instructions/s (vector ALU)", frac=round(lane / 39.32, 4), traffic=None,
+                            source="rocprofv3 SQ_INSTS_VALU (wave64 instructions) x 64 lanes over kernel-trace "
+                                   "time; peak 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz")
+    return out
+
+
 def traffic_md(rec, commands):
     lines = ["Commands (from the repository root, on one MI355X):", ""]
     lines += ["    " + c for c in commands]
@@ -167,7 +292,26 @@ def main(argv=None):
     t.add_argument("--json-out", default="")
     t.add_argument("--md-out", default="")
     t.add_argument("--commands", nargs="*", default=[])
+    c = sub.add_parser("counters")
+    c.add_argument("--trace", required=True)
+    c.add_argument("--pmc", nargs="+", required=True)
+    c.add_argument("--copy-fetch", required=True)
+    c.add_argument("--copy-write", required=True)
+    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--workload", required=True)
+    c.add_argument("--layers", required=True, help="comma-separated layer names in step order")
+    c.add_argument("--json-out", default="")
+    c.add_argument("--commands", nargs="*", default=[])
     a = p.parse_args(argv)
+    if a.cmd == "counters":
+        rec = counters(a.trace, a.pmc, a.copy_fetch, a.copy_write, a.copy_bytes, a.workload, a.layers.split(","),
+                       a.commands)
+        text = json.dumps(rec, indent=1)
+        if a.json_out:
+            with open(a.json_out, "w") as fh:
+                fh.write(text + "\n")
+        print(text)
+        return
     if a.cmd == "stats":
         sys.stdout.write(stats(a.dir, a.commands))
     else:

@@ -110,6 +110,37 @@ def weight(wl: Workload, layer_index: int, d: int | None = None, n: int | None =
     return W
 
 
+SWEEP_CHUNK = 256  # rows per independently seeded chunk of a sweep weight
+
+
+def sweep_weight(wl: Workload, layer_index: int, block: int, rows=None, threads: int = 16) -> np.ndarray:
+    """Pretrained fp32 weight of matrix `layer_index` of transformer block `block` in the
+    merge-only sweep (same law as weight()).  Rows are drawn in chunks of SWEEP_CHUNK,
+    each from its own seed, so that chunks are drawn in parallel threads and a sample of
+    rows is drawn without the rest.  rows: None for the whole d x n matrix, else the
+    sorted row indices wanted (returned in that order)."""
+    L = wl.layers[layer_index]
+    chunks = range((L.d + SWEEP_CHUNK - 1) // SWEEP_CHUNK) if rows is None else \
+        sorted({int(i) // SWEEP_CHUNK for i in rows})
+
+    def draw(ch):
+        rng = np.random.Generator(np.random.PCG64(np.random.SeedSequence((wl.index, layer_index, block, ch, 7))))
+        h = min(SWEEP_CHUNK, L.d - ch * SWEEP_CHUNK)
+        Wc = rng.standard_normal((h, L.n), dtype=np.float32) * np.float32(wl.w_std)
+        if wl.tail_p > 0.0:
+            mask = rng.random((h, L.n), dtype=np.float32) < np.float32(wl.tail_p)
+            Wc[mask] *= np.float32(wl.tail_scale)
+        return Wc
+
+    from concurrent.futures import ThreadPoolExecutor
+
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        parts = dict(zip(chunks, ex.map(draw, chunks)))
+    if rows is None:
+        return np.concatenate([parts[ch] for ch in chunks])
+    return np.stack([parts[int(i) // SWEEP_CHUNK][int(i) % SWEEP_CHUNK] for i in rows])
+
+
 def lora(wl: Workload, layer_index: int, d: int | None = None, n: int | None = None, r: int | None = None,
          block: int = 0):
     """LoRA factors A (d x r) ~ N(0, 1/4) and B (r x n) ~ N(0, 1e-3), fp32."""

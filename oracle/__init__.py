@@ -82,6 +82,7 @@ def _declare(L):
         "ora_linear": (None, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
         "ora_linear_sampled": (None, [_I64, _P, _P, _I64, _P, _P, _P, _P, _P, _P]),
         "ora_num_threads": (_I32, []),
+        "ora_set_threads": (None, [_I32]),
         "ora_laplace_batch": (None, [_I64, _P, _P]),
         "ora_ln_batch": (None, [_I64, _P, _P]),
         "ora_log2_round_batch": (None, [_I64, _P, _P]),
@@ -111,6 +112,11 @@ def _p(a):
 
 def num_threads() -> int:
     return int(lib().ora_num_threads())
+
+
+def set_threads(t: int) -> None:
+    """Threads of the oracle's row / token loops (t >= 1)."""
+    lib().ora_set_threads(int(t))
 
 
 # --------------------------------------------------------------------------- RNG

@@ -646,3 +646,13 @@ ORA_API int ora_num_threads(void) {
     return 1;
 #endif
 }
+
+/* Threads of the row / token loops from now on (the CPU-baseline timing runs the
+ * oracle on one thread as well as on all host cores). */
+ORA_API void ora_set_threads(int t) {
+#ifdef _OPENMP
+    if (t > 0) omp_set_num_threads(t);
+#else
+    (void)t;
+#endif
+}

@@ -225,3 +225,121 @@ def test_merge_fused_full_size(ops, wl_index, li):
     assert np.array_equal(bits(host(g["sbar"])), bits(host(f["sbar"])))
     assert int(host(g["sat"])[0]) == int(host(f["sat"])[0])
     torch.cuda.empty_cache()
+
+
+# ----------------------------------------------------------------------------- every output
+def check_layer_full(ops, wl, li, M):
+    """Every output of one layer at its full size against the oracle run on the whole
+    layer: set-up (c, W_round, z, s), the MUL merge (m, U_round, s_bar, z_bar, split
+    codes, saturations) and the linear layer's bf16 outputs for all M tokens."""
+    L = wl.layers[li]
+    lid = synth.layer_id(wl.index, li)
+    W = synth.weight(wl, li)
+    A, Bm = synth.lora(wl, li)
+    X = synth.activations(wl, L.n, M, li)
+    seed = synth.PHILOX_SEED
+    mode, mbits = wl.modes[0]
+    assert mode == "mul"
+    print(f"full-output check: {wl.name} {L.name} {L.d}x{L.n} M={M}", flush=True)
+    st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+    g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid, dbg=True)
+    xq, sx, rs = ops.quant_act(cuda(X))
+    Y, _ = ops.linear(xq, sx, rs, 16, g["m"], g["sbar"], L.d, split=g["split"])
+    ost = oracle.setup_layer(W, seed, lid, wl.w_bits, synth.ALPHA)
+    gwr = host(st["wround"])
+    gwr = unpack4(gwr) if wl.w_bits == 4 else gwr
+    assert np.array_equal(bits(host(st["c"])), bits(ost["c"]))
+    assert np.array_equal(gwr, ost["wround"])
+    assert np.array_equal(host(st["z"]), ost["z"])
+    assert np.array_equal(bits(host(st["s"])), bits(ost["s"]))
+    ref = oracle.merge_mul(ost["wround"], ost["z"], ost["s"], ost["rstar"], A, Bm, mbits)
+    del ost
+    assert np.array_equal(host(g["m"]), ref["m"])
+    assert np.array_equal(host(g["uround"]), ref["uround"])
+    assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+    assert np.array_equal(host(g["zbar"]), ref["zbar"])
+    assert np.array_equal(host(g["split"]), oracle.plane_split(ref["m"]))
+    assert int(host(g["sat"])[0]) == ref["sat"]
+    oxq, osx, ors = oracle.quant_act(X)
+    assert np.array_equal(host(xq), oxq)
+    assert np.array_equal(bits(host(sx)), bits(osx))
+    _, _, oy = oracle.linear(oxq, osx, ref["m"].astype(np.int32), ref["sbar"], want_exact=False)
+    assert np.array_equal(host(Y).view(np.uint16), oy), (wl.name, L.name, M)
+    del g, st, Y, xq
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("li", [0, 1, 2, 3])
+def test_flux_block_every_output(ops, li):
+    """FLUX-like DiT block (W4A8, MUL U 4-bit, r = 32, 4608 tokens): each of the four
+    layers in full."""
+    wl = synth.WORKLOADS[3]
+    check_layer_full(ops, wl, li, wl.tokens[0])
+
+
+@pytest.mark.timeout(300)
+def test_llama_gate_every_output(ops):
+    """Llama-3-8B gate projection (14336 x 4096, W8A8, MUL U 8-bit, r = 64) at M = 2048,
+    in full."""
+    wl = synth.WORKLOADS[4]
+    check_layer_full(ops, wl, 4, 2048)
+
+
+def sweep_rows(d):
+    """The sweep's row sample: every 64th row, and the last."""
+    return np.array(sorted(set(range(0, d, 64)) | {d - 1}))
+
+
+def check_sweep_block(ops, block, full):
+    """The merge-only sweep of the Llama-shaped workload, transformer block `block`: all
+    seven matrices merged on the GPU in full; the oracle checks every row (full) or the
+    row sample (rows are independent: set-up and merge are row-local and R depends on
+    (seed, layer, i, j) only)."""
+    wl = synth.WORKLOADS[4]
+    mode, mbits = wl.modes[0]
+    seed = synth.PHILOX_SEED
+    for li, L in enumerate(wl.layers):
+        lid = synth.layer_id(wl.index, li, block)
+        W = synth.sweep_weight(wl, li, block)
+        A, Bm = synth.lora(wl, li, block=block)
+        st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
+        del W
+        g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid, dbg=True)
+        rows = np.arange(L.d) if full else sweep_rows(L.d)
+        Wr = synth.sweep_weight(wl, li, block, None if full else rows)
+        c = oracle.vmc_scale(oracle.sigma_w(Wr), synth.ALPHA)
+        if full:
+            R = oracle.gen_r(L.d, L.n, seed, lid, c)
+        else:
+            R = np.concatenate([oracle.gen_r_rows(int(i), 1, L.n, seed, lid, c[k:k + 1]) for k, i in enumerate(rows)])
+        wr, z, s = oracle.base_quant(Wr, R, wl.w_bits)
+        ref = oracle.merge_mul(wr, z, s, R, A[rows], Bm, mbits)
+        rt = torch.from_numpy(rows).cuda()
+        pick = lambda t: t.index_select(0, rt).cpu().numpy()
+        assert np.array_equal(bits(pick(st["c"])), bits(c)), (block, L.name)
+        assert np.array_equal(pick(st["wround"]), wr)
+        assert np.array_equal(pick(st["z"]), z)
+        assert np.array_equal(bits(pick(st["s"])), bits(s))
+        assert np.array_equal(pick(g["m"]), ref["m"]), (block, L.name)
+        assert np.array_equal(pick(g["uround"]), ref["uround"])
+        assert np.array_equal(bits(pick(g["sbar"])), bits(ref["sbar"]))
+        assert np.array_equal(pick(g["zbar"]), ref["zbar"])
+        assert np.array_equal(pick(g["split"]), oracle.plane_split(ref["m"]))
+        if full:
+            assert int(host(g["sat"])[0]) == ref["sat"]
+        del g, st, R, ref
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(300)
+def test_llama_sweep_block0_every_row(ops):
+    check_sweep_block(ops, 0, True)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("blocks", [(1, 11), (11, 21), (21, 32)])
+def test_llama_sweep_blocks_row_sample(ops, blocks):
+    for b in range(*blocks):
+        print(f"sweep block {b}", flush=True)
+        check_sweep_block(ops, b, False)

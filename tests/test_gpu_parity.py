@@ -218,7 +218,7 @@ def test_merge_shift_bitexact(ops, d, n, r, w_bits):
         assert int(host(g["sat"])[0]) == ref["sat"]
 
 
-@pytest.mark.parametrize("d,n,r,w_bits", [(37, 1000, 8, 8), (64, 777, 4, 4), (96, 3072, 32, 4)])
+@pytest.mark.parametrize("d,n,r,w_bits", [(37, 1001, 8, 8), (64, 778, 4, 4), (96, 3072, 32, 4)])
 def test_merge_caller_range(ops, d, n, r, w_bits):
     """u_min / u_max given by the caller: the row range of intlora_stats gives the same
     bits as the merge's own; a narrower caller range (codes clamp, SHIFT sees |V| > 1)
