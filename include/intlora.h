@@ -203,6 +203,22 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
                       uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count, void* ws,
                       size_t ws_bytes, void* stream);
 
+/* Allocation-free MUL merge, for callers that cannot allocate device memory or pass a
+ * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation).  The same computation and outputs, bit for bit, as intlora_merge_mul
+ * (every argument as there), with the scratch taken from a 64 MiB array the library
+ * holds on each device until the process ends; nothing is allocated.  Layers whose
+ * scratch does not fit are merged in row chunks (R depends on (seed, layer_id, i, j)
+ * only, so a chunk regenerates its own rows).  INTLORA_ESHAPE when 32 rows do not fit
+ * (n above about 500 000).  Every call on a device shares that device's array, so
+ * calls that overlap on one device (other streams, other host threads) race and give
+ * wrong results; calls ordered on one stream are safe.  The first call on a device
+ * looks the array's address up (hipGetSymbolAddress). */
+int intlora_merge_mul_noalloc(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora,
+                              int u_bits, const float* u_min, const float* u_max, int16_t* m, float* s_bar,
+                              int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count,
+                              void* stream);
+
 /* Fused single-pass MUL merge with no scratch memory: the same outputs, bit for bit, as
  * intlora_merge_mul ([IntLoRA notes] "1. AQS", "2. MLA", "两种实现版本" MUL), computed
  * by one kernel in which a block keeps whole rows of U on chip, so U is never written

@@ -60,6 +60,8 @@ _SIG = {
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "intlora_merge_mul_noalloc": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
+                                         _P, _P, _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul_fused": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
                                        _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul_codes": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
@@ -172,6 +174,14 @@ def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_ba
     _check(lib().intlora_merge_mul(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(u_min),
                                    _ptr(u_max), _ptr(m), _ptr(s_bar), _ptr(z_bar), _ptr(m_split), _ptr(u_round_dbg),
                                    _ptr(sat_count), _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
+
+
+def intlora_merge_mul_noalloc(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None,
+                              u_round_dbg=None, sat_count=None, stream=None, u_min=None, u_max=None):
+    _check(lib().intlora_merge_mul_noalloc(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(u_min),
+                                           _ptr(u_max), _ptr(m), _ptr(s_bar), _ptr(z_bar), _ptr(m_split),
+                                           _ptr(u_round_dbg), _ptr(sat_count), _stream(stream)),
+           "intlora_merge_mul_noalloc")
 
 
 def intlora_merge_mul_fused(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None,

@@ -3,9 +3,17 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/intlora.h"
 #include "intlora_internal.h"
+
+// Scratch memory of intlora_merge_mul_noalloc: U and the row partials of one row chunk.
+// One copy per device, held until the process ends.  Host code never passes the
+// array's name to a kernel: it passes the device address taken once per device with
+// hipGetSymbolAddress (scratch_on_device below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 namespace {
 
@@ -206,6 +214,39 @@ int check_merge_mul(const intlora_desc* desc, const intlora_base* base, const in
   return INTLORA_OK;
 }
 
+// Device address of `scratch` on the current device, looked up once per device.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_on_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(INTLORA_EDEVICE, "no HIP device");
+  if (dev >= kMaxDevices) return fail(INTLORA_EDEVICE, "device %d: at most %d devices are supported", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(INTLORA_EDEVICE, "device %d: scratch address: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return INTLORA_OK;
+}
+
+// Rows per chunk of the allocation-free merge: the most rows whose workspace fits the
+// scratch, a multiple of 32 (one adaptation row tile; it also keeps every row offset of
+// the chunked pointers 16-byte aligned) unless the whole layer fits.  0 if not even 32
+// rows fit.
+int64_t noalloc_rows(int64_t d, int64_t n) {
+  if (merge_ws_bytes(d, n) <= kScratchBytes) return d;
+  const size_t per_row = (size_t)n * 4 + 8 * (size_t)intlora::adapt_max_ntiles(n) + 8;
+  int64_t rows = (int64_t)((kScratchBytes - 5 * 256) / per_row) & ~int64_t(31);
+  while (rows > 0 && merge_ws_bytes(rows, n) > kScratchBytes) rows -= 32;
+  return rows;
+}
+
 }  // namespace
 
 extern "C" {
@@ -336,6 +377,47 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
   if ((s = merge_mul_rows(desc, base, lora, u_bits, u_min, u_max, m, s_bar, z_bar, m_split, u_round_dbg, sat_count,
                           sat_count, w, 0, static_cast<hipStream_t>(stream))))
     return s;
+  return ok();
+}
+
+int intlora_merge_mul_noalloc(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora,
+                              int u_bits, const float* u_min, const float* u_max, int16_t* m, float* s_bar,
+                              int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count,
+                              void* stream) {
+  int s = check_merge_mul(desc, base, lora, u_bits, u_min, u_max, m, s_bar, z_bar, m_split, u_round_dbg, sat_count,
+                          "merge_mul_noalloc");
+  if (s) return s;
+  if (desc->d == 0) return ok();
+  const int64_t d = desc->d, n = desc->n;
+  const int64_t rows = noalloc_rows(d, n);
+  if (rows <= 0)
+    return fail(INTLORA_ESHAPE,
+                "merge_mul_noalloc: 32 rows of n = %lld need %zu bytes of scratch; the library holds %zu per device",
+                (long long)n, merge_ws_bytes(32, n), kScratchBytes);
+  if ((s = ensure_device())) return s;
+  void* sp = nullptr;
+  if ((s = scratch_on_device(&sp))) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int64_t code_row = desc->w_bits == 4 ? n / 2 : n;  // bytes per row of base codes
+  for (int64_t r0 = 0; r0 < d; r0 += rows) {
+    const int64_t dc = d - r0 < rows ? d - r0 : rows;
+    intlora_desc dk = *desc;
+    dk.d = dc;
+    intlora_base bk = *base;
+    bk.w_round = static_cast<const uint8_t*>(base->w_round) + r0 * code_row;
+    bk.z = base->z + r0;
+    bk.s = base->s + r0;
+    bk.vmc_c = base->vmc_c + r0;
+    intlora_lora lk = *lora;
+    lk.A = lora->A + r0 * desc->r;
+    MergeWs w = carve(sp, dc, n);
+    // the first chunk's adaptation kernel clears the saturation counter; later chunks add
+    s = merge_mul_rows(&dk, &bk, &lk, u_bits, u_min ? u_min + r0 : nullptr, u_max ? u_max + r0 : nullptr,
+                       m + r0 * n, s_bar + r0, z_bar + r0, m_split ? m_split + r0 : nullptr,
+                       u_round_dbg ? u_round_dbg + r0 * n : nullptr, sat_count, r0 == 0 ? sat_count : nullptr, w, r0,
+                       st);
+    if (s) return s;
+  }
   return ok();
 }
 

@@ -94,6 +94,27 @@ def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out
     return o
 
 
+def merge_mul_noalloc(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, out=None, u_range=None):
+    """MUL merge with the library's own per-device scratch (no workspace); same outputs
+    as merge_mul."""
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
+    o = out or dict(m=torch.empty((d, n), dtype=torch.int16, device=dev),
+                    sbar=torch.empty(d, dtype=torch.float32, device=dev),
+                    zbar=torch.empty(d, dtype=torch.int32, device=dev),
+                    split=torch.empty(d, dtype=torch.uint8, device=dev),
+                    sat=torch.zeros(2, dtype=torch.int64, device=dev))
+    if dbg and "uround" not in o:
+        o["uround"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
+    B.intlora_merge_mul_noalloc(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), u_bits, o["m"],
+                                o["sbar"], o["zbar"], m_split=o.get("split"),
+                                u_round_dbg=o.get("uround") if dbg else None, sat_count=o["sat"],
+                                u_min=u_range[0] if u_range else None, u_max=u_range[1] if u_range else None)
+    return o
+
+
 def merge_mul_fused(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, out=None):
     """Fused single-pass MUL merge (no workspace); same outputs as merge_mul."""
     d, r = A.shape
