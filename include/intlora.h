@@ -67,7 +67,9 @@ enum { INTLORA_SIGMA_W = 0, INTLORA_U_MINMAX = 1 };
 enum {
   INTLORA_W_INT4 = 4,  /* SHIFT, b_W = 4: packed signed nibbles (two's complement)            */
   INTLORA_W_INT8 = 8,  /* SHIFT, b_W = 8: int8                                                */
-  INTLORA_W_INT16 = 16 /* MUL: int16 merged integers (U_round - z_bar) * (W_round - z)        */
+  INTLORA_W_INT16 = 16, /* MUL: int16 merged integers (U_round - z_bar) * (W_round - z)       */
+  INTLORA_W_INT16_PLANES = 17 /* MUL: the same integers stored as their two int8 byte planes,
+                                 as intlora_merge_mul_planes writes them                      */
 };
 
 /* operations for intlora_workspace_bytes */
@@ -202,6 +204,26 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
                       const float* u_min, const float* u_max, int16_t* m, float* s_bar, int32_t* z_bar,
                       uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count, void* ws,
                       size_t ws_bytes, void* stream);
+
+/* MUL merge writing the merged integers already split into the two int8 planes the
+ * integer linear layer multiplies ([IntLoRA notes] "two implementation variants", MUL;
+ * the int16 merged integers go through the int8 matrix cores as two byte planes), so
+ * the layer reads them without any conversion (format INTLORA_W_INT16_PLANES).  The
+ * same computation as intlora_merge_mul up to m; then, per row, the split is chosen
+ * before any element is written, from a bound on the row's merged integers:
+ *   bound_i = max(|z_i|, |2^w_bits - 1 - z_i|) * max(z_bar_i, 2^u_bits - 1 - z_bar_i);
+ *   bound_i <= 32639: balanced split hi = (m + 128) >> 8, lo = m - 256 hi (m = 256 hi + lo);
+ *   otherwise:        bias split hi = m >> 8, lo = (m & 0xFF) - 128 (m = 256 hi + lo + 128).
+ * Layout m_planes (uint8, d x 2n): per row, for each group of 16 consecutive columns,
+ * the 16 high bytes then the 16 low bytes (two's complement).  plane_code[d] (uint8):
+ * 0 = balanced and every high byte of the row is zero (|m| <= 127: the high plane adds
+ * nothing), 1 = balanced, 3 = bias split.  n must be a multiple of 16 (INTLORA_ESHAPE).
+ * Other arguments, outputs and workspace as intlora_merge_mul (whose split codes
+ * plane_code replaces). */
+int intlora_merge_mul_planes(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora,
+                             int u_bits, const float* u_min, const float* u_max, uint8_t* m_planes, float* s_bar,
+                             int32_t* z_bar, uint8_t* plane_code, uint8_t* u_round_dbg,
+                             unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream);
 
 /* Allocation-free MUL merge, for callers that cannot allocate device memory or pass a
  * workspace (code under HIP graph capture, tight serving loops, harnesses that forbid
@@ -351,6 +373,16 @@ int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream)
  * uint32) and out (4 * blocks fp32) are caller-owned device buffers.  INTLORA_EINVAL for
  * an unknown law, INTLORA_ESHAPE for blocks < 0; blocks = 0 returns INTLORA_OK. */
 int intlora_debug_aux(int64_t blocks, const uint32_t* words, uint32_t aux_dist, float* out, void* stream);
+
+/* Diagnostic: the rank-r product acc = A B (A: d x r, B: r x n, fp32 row-major; acc:
+ * d x n) formed on the matrix cores exactly as the merges form the MLA term's AB
+ * ([IntLoRA notes] "2. MLA": an fma chain over k from +0, one rounding per k), one
+ * matrix-core instruction per k in increasing k: form 0 is v_mfma_f32_32x32x1f32 taken
+ * transposed (the adaptation kernel), form 1 v_mfma_f32_4x4x1f32 (the fused merge).
+ * d must be a multiple of 32 (form 0) or 4 (form 1), n of 64; r in [1, 128].  Tests
+ * pin it against a plain fmaf chain.  INTLORA_EINVAL / INTLORA_ESHAPE otherwise. */
+int intlora_debug_mfma_chain(int form, int64_t d, int64_t n, int r, const float* A, const float* B, float* acc,
+                             void* stream);
 
 #ifdef __cplusplus
 }

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libintlora.so")
 # status codes / enums (mirror include/intlora.h)
 INTLORA_OK, INTLORA_EINVAL, INTLORA_ESHAPE, INTLORA_EALIGN, INTLORA_EWORKSPACE, INTLORA_EDEVICE, INTLORA_ELAUNCH = range(7)
 INTLORA_SIGMA_W, INTLORA_U_MINMAX = 0, 1
-INTLORA_W_INT4, INTLORA_W_INT8, INTLORA_W_INT16 = 4, 8, 16
+INTLORA_W_INT4, INTLORA_W_INT8, INTLORA_W_INT16, INTLORA_W_INT16_PLANES = 4, 8, 16, 17
 INTLORA_AUX_LAPLACE, INTLORA_AUX_GAUSS, INTLORA_AUX_CAUCHY, INTLORA_AUX_STUDENT_T2 = 0, 1, 2, 3
 INTLORA_OP_STATS_UMINMAX, INTLORA_OP_MERGE_MUL, INTLORA_OP_MERGE_SHIFT, INTLORA_OP_LINEAR, INTLORA_OP_BASE_QUANT = 1, 2, 3, 4, 5
 INTLORA_OP_MERGE_PTQ, INTLORA_OP_STE_BACKWARD = 6, 7
@@ -60,6 +60,8 @@ _SIG = {
     "intlora_base_quant": (_INT, [ctypes.POINTER(Desc), _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P, _P, _P,
                                  _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "intlora_merge_mul_planes": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
+                                        _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "intlora_merge_mul_noalloc": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
                                          _P, _P, _P, _P, _P, _P, _P, _P]),
     "intlora_merge_mul_fused": (_INT, [ctypes.POINTER(Desc), ctypes.POINTER(Base), ctypes.POINTER(Lora), _INT, _P,
@@ -76,6 +78,7 @@ _SIG = {
     "intlora_linear_fwd_codes": (_INT, [_I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "intlora_debug_ln": (_INT, [_I64, _P, _P, _P]),
     "intlora_debug_aux": (_INT, [_I64, _P, ctypes.c_uint32, _P, _P]),
+    "intlora_debug_mfma_chain": (_INT, [_INT, _I64, _I64, _INT, _P, _P, _P, _P]),
 }
 
 
@@ -176,6 +179,15 @@ def intlora_merge_mul(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_ba
                                    _ptr(sat_count), _ptr(ws), wsb, _stream(stream)), "intlora_merge_mul")
 
 
+def intlora_merge_mul_planes(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m_planes, s_bar, z_bar, plane_code,
+                             u_round_dbg=None, sat_count=None, ws=None, stream=None, u_min=None, u_max=None):
+    wsb = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(lib().intlora_merge_mul_planes(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(u_min),
+                                          _ptr(u_max), _ptr(m_planes), _ptr(s_bar), _ptr(z_bar), _ptr(plane_code),
+                                          _ptr(u_round_dbg), _ptr(sat_count), _ptr(ws), wsb, _stream(stream)),
+           "intlora_merge_mul_planes")
+
+
 def intlora_merge_mul_noalloc(dsc: Desc, bs: Base, lr: Lora, u_bits: int, m, s_bar, z_bar, m_split=None,
                               u_round_dbg=None, sat_count=None, stream=None, u_min=None, u_max=None):
     _check(lib().intlora_merge_mul_noalloc(ctypes.byref(dsc), ctypes.byref(bs), ctypes.byref(lr), u_bits, _ptr(u_min),
@@ -244,3 +256,8 @@ def intlora_debug_ln(count: int, G, out, stream=None):
 
 def intlora_debug_aux(blocks: int, words, aux_dist: int, out, stream=None):
     _check(lib().intlora_debug_aux(blocks, _ptr(words), aux_dist, _ptr(out), _stream(stream)), "intlora_debug_aux")
+
+
+def intlora_debug_mfma_chain(form: int, d: int, n: int, r: int, A, B, acc, stream=None):
+    _check(lib().intlora_debug_mfma_chain(form, d, n, r, _ptr(A), _ptr(B), _ptr(acc), _stream(stream)),
+           "intlora_debug_mfma_chain")

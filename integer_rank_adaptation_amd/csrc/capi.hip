@@ -83,13 +83,16 @@ int check_opt(const void* p, const char* what) {
 }
 
 // Workspace layout of the merge / U statistics: U (d*n fp32) | pmin | pmax (d*ntiles
-// order keys each) | umin | umax (d fp32 each)
+// order keys each) | umin | umax | rs | small (d 4-byte values each: the row range, and
+// the MUL quantizer's RN(1/s_bar) and small-row flag)
 struct MergeWs {
   float* U;
   int* pmin;
   int* pmax;
   float* umin;
   float* umax;
+  float* rs;
+  int* small;
   int ntiles;
 };
 
@@ -97,7 +100,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 size_t merge_ws_bytes(int64_t d, int64_t n) {
   const size_t nt = (size_t)intlora::adapt_max_ntiles(n);
-  return align256((size_t)d * (size_t)n * 4) + 2 * align256((size_t)d * nt * 4) + 2 * align256((size_t)d * 4);
+  return align256((size_t)d * (size_t)n * 4) + 2 * align256((size_t)d * nt * 4) + 4 * align256((size_t)d * 4);
 }
 
 MergeWs carve(void* ws, int64_t d, int64_t n) {
@@ -113,6 +116,10 @@ MergeWs carve(void* ws, int64_t d, int64_t n) {
   w.umin = reinterpret_cast<float*>(p);
   p += align256((size_t)d * 4);
   w.umax = reinterpret_cast<float*>(p);
+  p += align256((size_t)d * 4);
+  w.rs = reinterpret_cast<float*>(p);
+  p += align256((size_t)d * 4);
+  w.small = reinterpret_cast<int*>(p);
   return w;
 }
 
@@ -164,37 +171,40 @@ int check_range(const float* u_min, const float* u_max) {
   return INTLORA_OK;
 }
 
-// Row range of the merge: the caller's (u_min, u_max), or the reduction of the
-// adaptation kernel's tile partials into the workspace.  `split` (nullable) is cleared
-// either way; the quantize kernel raises it for rows that need the bias byte split.
-int merge_range(int64_t d, const MergeWs& w, const float* u_min, const float* u_max, uint8_t* split,
-                const float** lo, const float** hi, hipStream_t st) {
+// Row range of the SHIFT merge: the caller's (u_min, u_max), or the reduction of the
+// adaptation kernel's tile partials into the workspace.
+int merge_range(int64_t d, const MergeWs& w, const float* u_min, const float* u_max, const float** lo,
+                const float** hi, hipStream_t st) {
   if (u_min) {
     *lo = u_min;
     *hi = u_max;
-    if (!split) return INTLORA_OK;
-    return launch_status(intlora::launch_fill_u8(d, split, 0, st), "split codes");
+    return INTLORA_OK;
   }
   *lo = w.umin;
   *hi = w.umax;
-  return launch_status(intlora::launch_row_range(d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, split, st),
+  return launch_status(intlora::launch_row_range(d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, nullptr, st),
                        "row range");
 }
 
 // The three-kernel MUL merge of rows [0, desc->d) of the pointers given, whose row 0 is
 // row `row0` of the layer (R's counter); `sat_zero` is the counter the adaptation
 // kernel clears first (NULL: not cleared here).  Arguments are validated by the caller.
+// planes: m is the byte-plane layout (d x 2n bytes) and m_split the plane codes.
 int merge_mul_rows(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora, int u_bits,
-                   const float* u_min, const float* u_max, int16_t* m, float* s_bar, int32_t* z_bar,
+                   const float* u_min, const float* u_max, void* m, float* s_bar, int32_t* z_bar,
                    uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count,
-                   unsigned long long* sat_zero, MergeWs& w, int64_t row0, hipStream_t st) {
+                   unsigned long long* sat_zero, MergeWs& w, int64_t row0, hipStream_t st, bool planes = false) {
   int s = run_adapt(desc, base, lora, w, sat_zero, st, false, row0);
   if (s) return s;
-  const float *lo, *hi;
-  if ((s = merge_range(desc->d, w, u_min, u_max, m_split, &lo, &hi, st))) return s;
+  if ((s = launch_status(intlora::launch_mul_params(desc->d, w.ntiles, w.pmin, w.pmax, u_min, u_max, w.umin, w.umax,
+                                                    u_bits, desc->w_bits, base->z, s_bar, z_bar, w.rs, w.small,
+                                                    m_split, planes, st),
+                         "MUL row parameters")))
+    return s;
   return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
-                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, lo, hi, m,
-                                                 s_bar, z_bar, m_split, u_round_dbg, sat_count, nullptr, st),
+                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, s_bar,
+                                                 z_bar, w.rs, w.small, m, m_split, u_round_dbg, sat_count, nullptr,
+                                                 planes, st),
                        "quant_mul");
 }
 
@@ -241,8 +251,8 @@ int scratch_on_device(void** out) {
 // rows fit.
 int64_t noalloc_rows(int64_t d, int64_t n) {
   if (merge_ws_bytes(d, n) <= kScratchBytes) return d;
-  const size_t per_row = (size_t)n * 4 + 8 * (size_t)intlora::adapt_max_ntiles(n) + 8;
-  int64_t rows = (int64_t)((kScratchBytes - 5 * 256) / per_row) & ~int64_t(31);
+  const size_t per_row = (size_t)n * 4 + 8 * (size_t)intlora::adapt_max_ntiles(n) + 16;
+  int64_t rows = (int64_t)((kScratchBytes - 7 * 256) / per_row) & ~int64_t(31);
   while (rows > 0 && merge_ws_bytes(rows, n) > kScratchBytes) rows -= 32;
   return rows;
 }
@@ -380,6 +390,26 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
   return ok();
 }
 
+int intlora_merge_mul_planes(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora,
+                             int u_bits, const float* u_min, const float* u_max, uint8_t* m_planes, float* s_bar,
+                             int32_t* z_bar, uint8_t* plane_code, uint8_t* u_round_dbg,
+                             unsigned long long* sat_count, void* ws, size_t ws_bytes, void* stream) {
+  int s = check_merge_mul(desc, base, lora, u_bits, u_min, u_max, reinterpret_cast<int16_t*>(m_planes), s_bar, z_bar,
+                          plane_code, u_round_dbg, sat_count, "merge_mul_planes");
+  if (s) return s;
+  if (desc->n % 16 != 0)
+    return fail(INTLORA_ESHAPE, "merge_mul_planes: n must be a multiple of 16 (got %lld)", (long long)desc->n);
+  if (desc->d == 0) return ok();
+  if ((s = check_ptrs({plane_code}, "merge_mul_planes plane_code"))) return s;
+  if ((s = check_ws(ws, ws_bytes, merge_ws_bytes(desc->d, desc->n)))) return s;
+  if ((s = ensure_device())) return s;
+  MergeWs w = carve(ws, desc->d, desc->n);
+  if ((s = merge_mul_rows(desc, base, lora, u_bits, u_min, u_max, m_planes, s_bar, z_bar, plane_code, u_round_dbg,
+                          sat_count, sat_count, w, 0, static_cast<hipStream_t>(stream), true)))
+    return s;
+  return ok();
+}
+
 int intlora_merge_mul_noalloc(const intlora_desc* desc, const intlora_base* base, const intlora_lora* lora,
                               int u_bits, const float* u_min, const float* u_max, int16_t* m, float* s_bar,
                               int32_t* z_bar, uint8_t* m_split, uint8_t* u_round_dbg, unsigned long long* sat_count,
@@ -475,12 +505,15 @@ int intlora_merge_mul_codes(const intlora_desc* desc, const intlora_base* base, 
   hipStream_t st = static_cast<hipStream_t>(stream);
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, nullptr, st))) return s;
-  if ((s = launch_status(
-           intlora::launch_row_range(desc->d, w.ntiles, w.pmin, w.pmax, w.umin, w.umax, nullptr, st), "row range")))
+  if ((s = launch_status(intlora::launch_mul_params(desc->d, w.ntiles, w.pmin, w.pmax, nullptr, nullptr, w.umin,
+                                                    w.umax, u_bits, desc->w_bits, base->z, s_bar, z_bar, w.rs,
+                                                    w.small, nullptr, false, st),
+                         "MUL row parameters")))
     return s;
   return launch_status(intlora::launch_quant_mul(desc->d, desc->n, desc->w_bits, u_bits,
-                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, w.umin,
-                                                 w.umax, nullptr, s_bar, z_bar, nullptr, nullptr, nullptr, u_code, st),
+                                                 static_cast<const uint8_t*>(base->w_round), base->z, w.U, s_bar,
+                                                 z_bar, w.rs, w.small, nullptr, nullptr, nullptr, nullptr, u_code,
+                                                 false, st),
                        "quant_mul codes");
 }
 
@@ -501,7 +534,7 @@ int intlora_merge_shift(const intlora_desc* desc, const intlora_base* base, cons
   MergeWs w = carve(ws, desc->d, desc->n);
   if ((s = run_adapt(desc, base, lora, w, sat_count, st))) return s;
   const float *lo, *hi;
-  if ((s = merge_range(desc->d, w, u_min, u_max, nullptr, &lo, &hi, st))) return s;
+  if ((s = merge_range(desc->d, w, u_min, u_max, &lo, &hi, st))) return s;
   return launch_status(intlora::launch_quant_shift(desc->d, desc->n, desc->w_bits, v_bits,
                                                    static_cast<const uint8_t*>(base->w_round), base->z, w.U, lo, hi,
                                                    static_cast<uint8_t*>(m), s_bar, shift_dbg, sat_count, st),
@@ -563,8 +596,8 @@ int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const 
                        int32_t* acc_dbg, void* ws, size_t ws_bytes, void* stream) {
   (void)ws;
   (void)ws_bytes;
-  if (wfmt != INTLORA_W_INT4 && wfmt != INTLORA_W_INT8 && wfmt != INTLORA_W_INT16)
-    return fail(INTLORA_EINVAL, "wfmt must be INTLORA_W_INT4, _INT8 or _INT16 (got %d)", wfmt);
+  if (wfmt != INTLORA_W_INT4 && wfmt != INTLORA_W_INT8 && wfmt != INTLORA_W_INT16 && wfmt != INTLORA_W_INT16_PLANES)
+    return fail(INTLORA_EINVAL, "wfmt must be INTLORA_W_INT4, _INT8, _INT16 or _INT16_PLANES (got %d)", wfmt);
   if (M < 0 || d < 0 || n < 1 || M >= kMaxDim || d >= kMaxDim) return fail(INTLORA_ESHAPE, "bad shape");
   if (n % 32 != 0 || n > 131071)
     return fail(INTLORA_ESHAPE, "linear needs n a multiple of 32 and <= 131071 (got %lld)", (long long)n);
@@ -573,9 +606,13 @@ int intlora_linear_fwd(int64_t M, int64_t d, int64_t n, const int8_t* xq, const 
   if (M == 0 || d == 0) return ok();
   int s = check_ptrs({xq, s_x, m, s_bar, Y_bf16}, "linear_fwd");
   if (s) return s;
-  if (wfmt == INTLORA_W_INT16 && (s = check_ptrs({x_rowsum}, "linear_fwd x_rowsum (INT16)"))) return s;
+  if ((wfmt == INTLORA_W_INT16 || wfmt == INTLORA_W_INT16_PLANES) &&
+      (s = check_ptrs({x_rowsum}, "linear_fwd x_rowsum (INT16)")))
+    return s;
+  if (wfmt == INTLORA_W_INT16_PLANES && (s = check_ptrs({m_split}, "linear_fwd plane codes (INT16_PLANES)"))) return s;
   if ((s = check_opt(acc_dbg, "acc_dbg")) || (s = check_opt(m_split, "m_split"))) return s;
-  if (m_split && wfmt != INTLORA_W_INT16) return fail(INTLORA_EINVAL, "m_split applies to INTLORA_W_INT16 only");
+  if (m_split && wfmt != INTLORA_W_INT16 && wfmt != INTLORA_W_INT16_PLANES)
+    return fail(INTLORA_EINVAL, "m_split applies to INTLORA_W_INT16 and _INT16_PLANES only");
   if ((s = ensure_device())) return s;
   return launch_status(intlora::launch_linear(M, d, n, xq, s_x, x_rowsum, wfmt, m, m_split, s_bar, Y_bf16, acc_dbg,
                                               static_cast<hipStream_t>(stream)),
@@ -607,6 +644,21 @@ int intlora_debug_ln(int64_t count, const uint32_t* G, float* out, void* stream)
   if (s) return s;
   if ((s = ensure_device())) return s;
   return launch_status(intlora::launch_ln_odd(count, G, out, static_cast<hipStream_t>(stream)), "debug_ln");
+}
+
+int intlora_debug_mfma_chain(int form, int64_t d, int64_t n, int r, const float* A, const float* B, float* acc,
+                             void* stream) {
+  if (form != 0 && form != 1) return fail(INTLORA_EINVAL, "form must be 0 (32x32x1) or 1 (4x4x1) (got %d)", form);
+  if (r < 1 || r > 128) return fail(INTLORA_EINVAL, "rank r must be in [1, 128] (got %d)", r);
+  const int64_t rows = form == 0 ? 32 : 4;
+  if (d < 0 || n < 0 || d % rows != 0 || n % 64 != 0 || d >= kMaxDim || n >= kMaxDim || d / rows > 65535)
+    return fail(INTLORA_ESHAPE, "debug_mfma_chain: d a multiple of %lld (tiles <= 65535), n of 64", (long long)rows);
+  if (d == 0 || n == 0) return ok();
+  int s = check_ptrs({A, B, acc}, "debug_mfma_chain");
+  if (s) return s;
+  if ((s = ensure_device())) return s;
+  return launch_status(intlora::launch_debug_mfma_chain(form, d, n, r, A, B, acc, static_cast<hipStream_t>(stream)),
+                       "debug_mfma_chain");
 }
 
 int intlora_debug_aux(int64_t blocks, const uint32_t* words, uint32_t aux_dist, float* out, void* stream) {

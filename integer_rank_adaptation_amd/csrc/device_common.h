@@ -83,22 +83,36 @@ __device__ __forceinline__ LnLds ln_lds_entry(const LnEntry& e) {
   return LnLds{e.neg_ln_r_hi, (double)e.neg_ln_r_lo, (double)e.r * 0x1p-24};
 }
 
-// ln(G 2^-bias) for odd G < 2^bias, bias 23 or 24, as the binary64 value before the
-// final rounding (the Gaussian sampler takes its logarithm at bias 24).
-__device__ __forceinline__ double ln_odd_d(uint32_t G, int bias, const LnLds* __restrict__ tab) {
+// The integer part of the logarithm below: g = (F 2^-24) 2^e with F 2^-24 in
+// [0.75, 1.5), and the table entry k of F.
+struct LnPrep {
+  uint32_t F;
+  int e;
+  int k;
+};
+
+__device__ __forceinline__ LnPrep ln_prep(uint32_t G, int bias) {
   // leading-bit position p (0..22); m24 = G << (23 - p) in [2^23, 2^24)
   const int p = 31 - __clz(G);
-  uint32_t m24 = G << (23 - p);
-  int e = p - bias;                // g = (m24 * 2^-23) * 2^e
-  uint32_t F;                      // m * 2^24 as an integer, m in [0.75, 1.5)
+  const uint32_t m24 = G << (23 - p);
+  LnPrep r;
+  r.e = p - bias;                  // g = (m24 * 2^-23) * 2^e
   if (m24 >= 0xC00000u) {          // m >= 1.5: halve
-    F = m24;                       // (m/2) * 2^24 = m24
-    e += 1;
+    r.F = m24;                     // (m/2) * 2^24 = m24
+    r.e += 1;
   } else {
-    F = m24 << 1;
+    r.F = m24 << 1;
   }
-  const int k = (int)((F - 0xC00000u) >> 17);
-  const LnLds t = tab[k];
+  r.k = (int)((r.F - 0xC00000u) >> 17);
+  return r;
+}
+
+// ln(G 2^-bias) for odd G < 2^bias, bias 23 or 24, as the binary64 value before the
+// final rounding (the Gaussian sampler takes its logarithm at bias 24), from its
+// integer part and table entry t = tab[P.k].
+__device__ __forceinline__ double ln_finish(const LnPrep& P, const LnLds& t) {
+  const uint32_t F = P.F;
+  const int e = P.e;
   const double f = fma((double)F, t.r24, -1.0);  // m r_k - 1, exact
   // log1p(f) = f - f^2/2 + ... - f^8/8 truncated after f^7: |f| <= 2^-7 leaves a
   // relative error below 2^-52, far under the 2^-47.6 the rounding needs.
@@ -118,6 +132,11 @@ __device__ __forceinline__ double ln_odd_d(uint32_t G, int bias, const LnLds* __
   return head + (lp + tail);
 }
 
+__device__ __forceinline__ double ln_odd_d(uint32_t G, int bias, const LnLds* __restrict__ tab) {
+  const LnPrep P = ln_prep(G, bias);
+  return ln_finish(P, tab[P.k]);
+}
+
 __device__ __forceinline__ float ln_odd_g(uint32_t G, const LnLds* __restrict__ tab) {
   return (float)ln_odd_d(G, 23, tab);
 }
@@ -131,6 +150,29 @@ __device__ __forceinline__ float laplace_from_word(uint32_t x, const LnLds* __re
   const uint32_t G = (uint32_t)((1 << 23) - (N < 0 ? -N : N));
   const float lg = ln_odd_g(G, tab);
   return (N < 0) ? lg : -lg;
+}
+
+// The Laplace samples of the four words of a Philox block, the same values as
+// laplace_from_word on each: the integer steps of all four come first, then their four
+// table reads (in flight together), then the four binary64 evaluations.
+__device__ __forceinline__ void laplace4(const U4& rnd, const LnLds* __restrict__ tab, float (&L)[4]) {
+  const uint32_t x[4] = {rnd.x, rnd.y, rnd.z, rnd.w};
+  LnPrep P[4];
+  bool neg[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int32_t N = 2 * (int32_t)(x[e] >> 9) + 1 - (1 << 23);
+    neg[e] = N < 0;
+    P[e] = ln_prep((uint32_t)((1 << 23) - (N < 0 ? -N : N)), 23);
+  }
+  LnLds t[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[e] = tab[P[e].k];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float lg = (float)ln_finish(P[e], t[e]);
+    L[e] = neg[e] ? lg : -lg;
+  }
 }
 
 // --------------------------------------------------------------------------------

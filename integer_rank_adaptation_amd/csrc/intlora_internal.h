@@ -18,7 +18,7 @@ struct AdaptArgs {
   const float* A;
   const float* B;
   float* U;
-  int* pmin;  // order keys of the U range per (column tile, row), tile-major: pmin[tile * d + row]
+  int* pmin;  // order keys of the U range per (partial column, row), column-major: pmin[col * d + row]
   int* pmax;
   unsigned long long* sat_zero;  // zeroed by the adaptation kernel (nullable)
   bool ptq;                      // x = (s w + R*) + AB for every element (comparison path) instead of U
@@ -38,6 +38,8 @@ int adapt_max_ntiles(int64_t n);
 hipError_t launch_gen_r(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id, const float* c, float* out, int dist,
                         hipStream_t st);
 hipError_t launch_ln_odd(int64_t count, const uint32_t* G, float* out, hipStream_t st);
+hipError_t launch_debug_mfma_chain(int form, int64_t d, int64_t n, int r, const float* A, const float* B, float* out,
+                                   hipStream_t st);
 hipError_t launch_aux_debug(int64_t blocks, const uint32_t* words, int dist, float* out, hipStream_t st);
 hipError_t launch_sigma_w(int64_t d, int64_t n, const float* W, float* sigma, hipStream_t st);
 hipError_t launch_vmc_scale(int64_t d, const float* sigma, double alpha, float* c, int dist, hipStream_t st);
@@ -46,14 +48,19 @@ hipError_t launch_base_quant(int64_t d, int64_t n, int bits, uint64_t seed, uint
 hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* sx, int32_t* rowsum,
                             hipStream_t st);
 hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st);
-// p[0 .. count) = v (a kernel, so that a captured graph holds no memset node).
-hipError_t launch_fill_u8(int64_t count, uint8_t* p, uint8_t v, hipStream_t st);
 hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
                             uint8_t* split, hipStream_t st);
+// Per-row MUL quantizer parameters (range, s_bar, z_bar, RN(1/s_bar), small-row flag);
+// umin_in / umax_in: the caller's range, or NULL to reduce the partials.
+hipError_t launch_mul_params(int64_t d, int ntiles, const int* pmin, const int* pmax, const float* umin_in,
+                             const float* umax_in, float* umin_out, float* umax_out, int u_bits, int w_bits,
+                             const int32_t* z, float* sbar, int32_t* zbar, float* rs, int* small, uint8_t* split,
+                             bool planes, hipStream_t st);
+// m: int16 d x n, or (planes) the byte-plane layout d x 2n with split = the plane codes.
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
-                            const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
-                            int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
-                            uint8_t* ucode, hipStream_t st);
+                            const float* U, const float* sbar, const int32_t* zbar, const float* rs,
+                            const int* small, void* m, uint8_t* split, uint8_t* uround_dbg,
+                            unsigned long long* sat, uint8_t* ucode, bool planes, hipStream_t st);
 hipError_t launch_quant_ptq(int64_t d, int64_t n, int bits, const float* X, const float* xmin, const float* xmax,
                             uint8_t* code, float* s_out, int32_t* z_out, hipStream_t st);
 hipError_t launch_quant_shift(int64_t d, int64_t n, int w_bits, int v_bits, const uint8_t* wround, const int32_t* z,

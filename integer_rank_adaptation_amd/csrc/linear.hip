@@ -66,7 +66,15 @@ typedef float f2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16, F_UW4 = 44 };
+// F_P16T / F_P16N: the int16 merged integers stored as their two byte planes (per row,
+// each group of 16 columns holds 16 high bytes then 16 low bytes); F_P16T multiplies
+// both planes, F_P16N only the low plane (every high byte of the call is zero).
+enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16, F_P16T = 17, F_P16N = 18, F_UW4 = 44 };
+// B-tile layout families in LDS: 128-byte rows (64 int16, or 64 high + 64 low bytes)
+// for 128 outputs; 64-byte rows (64 int8) for 256 outputs.
+constexpr bool is_l16(int F) { return F == F_INT16 || F == F_P16T; }
+constexpr bool is_l8(int F) { return F == F_INT8 || F == F_P16N; }
+constexpr bool planar(int F) { return F == F_P16T || F == F_P16N; }
 
 namespace lin {
 constexpr int kThreads = 256;  // 4 waves: 2 (tokens) x 2 (MFMA columns), 128 x 128 per wave
@@ -82,12 +90,12 @@ constexpr int B_BYTES_UW4 = 2 * 128 * BK / 2;   // 8 KB: U then W codes, 128 out
 constexpr int EPI_RS = 64 * 2 + 16;             // epilogue staging row: 64 bf16 outputs + 16 bytes pad
 constexpr int EPI_WAVE = 32 * EPI_RS;           // one wave's 32 tokens x 64 outputs
 constexpr int EPI_VEC = 4 * EPI_WAVE;           // offset of the per-tile vectors in the epilogue region
-constexpr int EPI_BYTES = EPI_VEC + 3 * 4 * 256;
+constexpr int EPI_BYTES = EPI_VEC + 4 * 4 * 256;
 template <int F>
 struct Cfg {
   static constexpr int B_BYTES =
-      F == F_INT16 ? B_BYTES_16 : (F == F_INT8 ? B_BYTES_8 : (F == F_UW4 ? B_BYTES_UW4 : B_BYTES_4));
-  static constexpr bool TWO = F == F_INT16 || F == F_UW4;      // two byte planes of int16 values
+      is_l16(F) ? B_BYTES_16 : (is_l8(F) ? B_BYTES_8 : (F == F_UW4 ? B_BYTES_UW4 : B_BYTES_4));
+  static constexpr bool TWO = F == F_INT16 || F == F_UW4 || F == F_P16T;  // two byte planes of int16 values
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int RING = kStages * STAGE;
   static constexpr int LDS = RING + EPI_BYTES;
@@ -143,7 +151,10 @@ __device__ __forceinline__ void make_plan(int n, Plan<F>& p) {
     if (F == F_INT8) {           // 64-byte rows
       const int row = 16 * g + (lane >> 2);
       p.b[q] = (uint32_t)(row * n + 16 * ((lane & 3) ^ swz64(row)));
-    } else if (F == F_INT16) {   // 128-byte rows (64 int16)
+    } else if (F == F_P16N) {    // the low bytes of each 16-column group: 16 bytes at stride 32
+      const int row = 16 * g + (lane >> 2);
+      p.b[q] = (uint32_t)(row * 2 * n + 32 * ((lane & 3) ^ swz64(row)) + 16);
+    } else if (is_l16(F)) {      // 128-byte rows (64 int16, or 4 groups of 16 high + 16 low bytes)
       const int row = 8 * g + (lane >> 3);
       p.b[q] = (uint32_t)(2 * (row * n + 8 * ((lane & 7) ^ swz128(row))));
     } else if (F == F_UW4) {     // 32-byte rows: loads 0..3 U's 128 rows, 4..7 W's (same offsets)
@@ -164,7 +175,7 @@ __device__ __forceinline__ void stage_rsrc(int kt, const int8_t* a_tile, int64_t
                                            int64_t b_bytes, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
   using namespace lin;
   const int k0 = kt * BK;
-  const int64_t kb = F == F_INT16 ? 2 * (int64_t)k0 : (F == F_INT8 ? (int64_t)k0 : (int64_t)(k0 >> 1));
+  const int64_t kb = (F == F_INT16 || planar(F)) ? 2 * (int64_t)k0 : (F == F_INT8 ? (int64_t)k0 : (int64_t)(k0 >> 1));
   ra = make_rsrc(a_tile + k0, a_bytes - k0);
   rb = make_rsrc(b_tile + kb, b_bytes - kb);
 }
@@ -247,10 +258,10 @@ __device__ __forceinline__ LdsLane lds_lane(int wm, int wn, int fr, int h) {
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks) {
     ll.a[ks] = (uint32_t)((wm * 128 + fr) * 64 + (((2 * h + ks) ^ swz64(fr)) << 4));
-    if (F == F_INT8) {
+    if (is_l8(F)) {
       ll.b[ks][0] = (uint32_t)(A_BYTES + (wn * 128 + fr) * 64 + (((2 * h + ks) ^ swz64(fr)) << 4));
       ll.b[ks][1] = 0;
-    } else if (F == F_INT16) {
+    } else if (is_l16(F)) {  // INT16: the two chunks of 8 values; P16T: high then low bytes of 16
 #pragma unroll
       for (int jj = 0; jj < 2; ++jj)
         ll.b[ks][jj] = (uint32_t)(A_BYTES + (wn * 64 + fr) * 128 + (((4 * h + 2 * ks + jj) ^ swz128(fr)) << 4));
@@ -277,8 +288,8 @@ __device__ __forceinline__ void read_a(const uint8_t* __restrict__ S, const LdsL
 // sub-step (half of the lane's 16-byte chunk).
 template <int F>
 __device__ __forceinline__ v4i read_b_chunk(const uint8_t* __restrict__ S, const LdsLane& ll, int ks, int j) {
-  if (F == F_INT8) return *reinterpret_cast<const v4i*>(S + ll.b[ks][0] + j * 2048);
-  if (F == F_INT16) return *reinterpret_cast<const v4i*>(S + ll.b[ks][j & 1] + (j >> 1) * 4096);
+  if (is_l8(F)) return *reinterpret_cast<const v4i*>(S + ll.b[ks][0] + j * 2048);
+  if (is_l16(F)) return *reinterpret_cast<const v4i*>(S + ll.b[ks][j & 1] + (j >> 1) * 4096);
   // INT4: tile j; UW4: chunk 2 q holds U's and 2 q + 1 W's 16 nibbles of output tile q
   const uint32_t off = F == F_UW4 ? (uint32_t)((j >> 1) * 1024 + (j & 1) * 4096) : (uint32_t)(j * 1024);
   const uint2 r = *reinterpret_cast<const uint2*>(S + ll.b[ks][0] + off);
@@ -346,7 +357,7 @@ __device__ __forceinline__ void convert_b(const RawB<F>& rw, v4i (&bf)[4], const
     for (int p = 0; p < 8; ++p) convert_piece<F, BIAS>(p, rw, bf, zp);
     return;
   }
-  if (F == F_INT8) {
+  if (is_l8(F) || F == F_P16T) {  // already int8 operands (P16T: chunk 2q high, 2q + 1 low of tile q)
 #pragma unroll
     for (int j = 0; j < 4; ++j) bf[j] = rw.v[j];
   } else if (F == F_INT16) {
@@ -386,8 +397,12 @@ __device__ __forceinline__ void read_piece(int q, const uint8_t* __restrict__ S,
 // Conversion piece p (0..7) of the raw B bytes into MFMA operands.
 template <int F, bool BIAS>
 __device__ __forceinline__ void convert_piece(int p, const RawB<F>& rw, v4i (&bf)[4], const uint32_t (&zp)[4]) {
-  if (F == F_INT8) {
+  if (is_l8(F)) {
     if (p < 4) bf[p] = rw.v[p];
+  } else if (F == F_P16T) {
+    const int q = p >> 2, e = p & 3;
+    bf[2 * q][e] = rw.v[2 * q][e];
+    bf[2 * q + 1][e] = rw.v[2 * q + 1][e];
   } else if (F == F_UW4) {
     const int q = p >> 2, e = p & 3;  // output tile q, K 4e .. 4e + 3 of the sub-step
     const uint2 mm = uw4_m((uint32_t)rw.v[2 * q][e >> 1], (uint32_t)rw.v[2 * q + 1][e >> 1], zp[2 * q],
@@ -446,19 +461,18 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
 // continuous stream through the LDS ring: the loads of the next tile's first stages
 // are issued during the current tile's last iterations, and the epilogue (which has
 // an LDS region of its own) runs while they are in flight.
+// The body of the kernel for format F, on the block's dynamic LDS `lds`.  split: the
+// INT16 split codes, or (byte planes) the plane codes, whose bit 1 marks a row stored in
+// the bias split.
 template <int F, bool KTAIL>
-__global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t d, int64_t n,
-                                                            const int8_t* __restrict__ xq,
-                                                            const float* __restrict__ sx,
-                                                            const int32_t* __restrict__ rowsum,
-                                                            const uint8_t* __restrict__ m,
-                                                            const uint8_t* __restrict__ split,
-                                                            const float* __restrict__ sbar, uint16_t* __restrict__ Y,
-                                                            int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n,
-                                                            int64_t wdelta, const int32_t* __restrict__ zbar_p,
-                                                            const int32_t* __restrict__ zw_p) {
+__device__ __forceinline__ void linear_body(uint8_t* __restrict__ lds, int64_t M, int64_t d, int64_t n,
+                                            const int8_t* __restrict__ xq, const float* __restrict__ sx,
+                                            const int32_t* __restrict__ rowsum, const uint8_t* __restrict__ m,
+                                            const uint8_t* __restrict__ split, const float* __restrict__ sbar,
+                                            uint16_t* __restrict__ Y, int32_t* __restrict__ acc_dbg, int tiles_m,
+                                            int tiles_n, int64_t wdelta, const int32_t* __restrict__ zbar_p,
+                                            const int32_t* __restrict__ zw_p) {
   using namespace lin;
-  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   constexpr int OUT = Cfg<F>::OUT;
@@ -473,7 +487,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     if (loc < per + (x < rem ? 1 : 0)) slot = base + loc;
   }
   const int my_tiles = slot < ntile ? (ntile - slot + G - 1) / G : 0;
-  const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);  // bytes per weight row
+  const int64_t wrow = (F == F_INT16 || planar(F)) ? 2 * n : (F == F_INT8 ? n : n / 2);  // bytes per weight row
   const int KT = (int)((n + BK - 1) / BK);
   const int fr = lane & 31, h = lane >> 5;
   Plan<F> plan;
@@ -647,11 +661,13 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
     float* tok_sx = reinterpret_cast<float*>(epi + EPI_VEC);
     int32_t* tok_rs = reinterpret_cast<int32_t*>(epi + EPI_VEC + 4 * BM);
     float* col_sb = reinterpret_cast<float*>(epi + EPI_VEC + 8 * BM);
+    int* col_bias = reinterpret_cast<int*>(epi + EPI_VEC + 12 * BM);  // P16T: rows in the bias split
     {
       const int64_t t = t0 + tid;
       tok_sx[tid] = t < M ? sx[t] : 0.0f;
-      if (F == F_INT16) tok_rs[tid] = t < M ? rowsum[t] : 0;
+      if (F == F_INT16 || F == F_P16T) tok_rs[tid] = t < M ? rowsum[t] : 0;
       if (tid < OUT) col_sb[tid] = o0 + tid < d ? sbar[o0 + tid] : 0.0f;
+      if (F == F_P16T && tid < OUT) col_bias[tid] = o0 + tid < d ? (int)((split[o0 + tid] >> 1) & 1u) : 0;
     }
     __syncthreads();
     uint8_t* stg = epi + wid * EPI_WAVE;
@@ -663,7 +679,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
       __builtin_amdgcn_sched_barrier(0);  // read one slab's accumulators at a time
       const int tl = wm * 128 + i * 32 + fr;  // this lane's token inside the block
       const float sxt = tok_sx[tl];
-      const double rs128 = F == F_INT16 && bias ? 128.0 * (double)tok_rs[tl] : 0.0;  // bias split
+      const double rs128 = (F == F_INT16 && bias) || F == F_P16T ? 128.0 * (double)tok_rs[tl] : 0.0;  // bias split
 #pragma unroll
       for (int p = 0; p < PASSES; ++p) {
         __builtin_amdgcn_sched_barrier(0);
@@ -678,6 +694,14 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
             const int ow = (TWO ? 0 : 64 * p) + oc;                       // output column in the wave
             const float4 sb = *reinterpret_cast<const float4*>(col_sb + (TWO ? wn * 64 : wn * 128) + ow);
             const float sbv[4] = {sb.x, sb.y, sb.z, sb.w};
+            int cb[4] = {1, 1, 1, 1};  // INT16: the launch's split applies to every row
+            if (F == F_P16T) {
+              const int4 b4 = *reinterpret_cast<const int4*>(col_bias + wn * 64 + ow);
+              cb[0] = b4.x;
+              cb[1] = b4.y;
+              cb[2] = b4.z;
+              cb[3] = b4.w;
+            }
             float y[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -685,7 +709,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
                 const int hi = acc_read(acc[i][2 * jj][4 * a + e]), lo = acc_read(acc[i][2 * jj + 1][4 * a + e]);
                 // exact = 256 acc_hi + acc_lo (+ 128 rowsum for the bias split), exact in
                 // binary64 (|exact| < 2^53)
-                const double ex = fma(256.0, (double)hi, (double)lo) + rs128;
+                const double ex = fma(256.0, (double)hi, (double)lo) + (cb[e] ? rs128 : 0.0);
                 y[e] = ((float)ex * sxt) * sbv[e];
               } else {
                 const int v = acc_read(acc[i][2 * p + jj][4 * a + e]);
@@ -705,6 +729,9 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
                   if (TWO) {
                     acc_dbg[tok * d + c + e] = acc_read(acc[i][2 * jj][4 * a + e]);
                     acc_dbg[M * d + tok * d + c + e] = acc_read(acc[i][2 * jj + 1][4 * a + e]);
+                  } else if (F == F_P16N) {  // the high plane (all zero) and the low plane
+                    acc_dbg[tok * d + c + e] = 0;
+                    acc_dbg[M * d + tok * d + c + e] = acc_read(acc[i][2 * p + jj][4 * a + e]);
                   } else {
                     const int v = acc_read(acc[i][2 * p + jj][4 * a + e]);
                     acc_dbg[tok * d + c + e] = F == F_INT4 ? (v >> 4) : v;
@@ -751,6 +778,62 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
   wait_vmcnt<0>();  // trailing (zero-reading) loads land before the block's LDS is released
 }
 
+template <int F, bool KTAIL>
+__global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t d, int64_t n,
+                                                            const int8_t* __restrict__ xq,
+                                                            const float* __restrict__ sx,
+                                                            const int32_t* __restrict__ rowsum,
+                                                            const uint8_t* __restrict__ m,
+                                                            const uint8_t* __restrict__ split,
+                                                            const float* __restrict__ sbar, uint16_t* __restrict__ Y,
+                                                            int32_t* __restrict__ acc_dbg, int tiles_m, int tiles_n,
+                                                            int64_t wdelta, const int32_t* __restrict__ zbar_p,
+                                                            const int32_t* __restrict__ zw_p) {
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  linear_body<F, KTAIL>(lds, M, d, n, xq, sx, rowsum, m, split, sbar, Y, acc_dbg, tiles_m, tiles_n, wdelta, zbar_p,
+                        zw_p);
+}
+
+// Byte-plane merged integers: when every row's plane code is 0 (all high bytes zero) the
+// launch multiplies the low planes alone as int8 weights (256 outputs per tile, the
+// high planes never loaded); otherwise both planes, with the bias correction on the rows
+// whose code says so.  Every block reads the codes and votes before its first load.
+template <bool KTAIL>
+__global__ __launch_bounds__(lin::kThreads, 1) void k_linear_planes(int64_t M, int64_t d, int64_t n,
+                                                                   const int8_t* __restrict__ xq,
+                                                                   const float* __restrict__ sx,
+                                                                   const int32_t* __restrict__ rowsum,
+                                                                   const uint8_t* __restrict__ m,
+                                                                   const uint8_t* __restrict__ code,
+                                                                   const float* __restrict__ sbar,
+                                                                   uint16_t* __restrict__ Y,
+                                                                   int32_t* __restrict__ acc_dbg, int tiles_m) {
+  using namespace lin;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
+  __shared__ int vote[4];
+  const int tid = threadIdx.x;
+  int fl = 0;
+  for (int64_t i = 16 * (int64_t)tid; i < d; i += 16 * kThreads) {
+    if (i + 16 <= d) {
+      const uint4 v = *reinterpret_cast<const uint4*>(code + i);
+      fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
+    } else {
+      for (int64_t k = i; k < d; ++k) fl |= (int)(code[k] != 0);
+    }
+  }
+  if ((tid & 63) == 0) vote[tid >> 6] = 0;
+  __syncthreads();
+  if (__builtin_amdgcn_ballot_w64(fl != 0) != 0 && (tid & 63) == 0) vote[tid >> 6] = 1;
+  __syncthreads();
+  const bool narrow = (vote[0] | vote[1] | vote[2] | vote[3]) == 0;
+  if (narrow)
+    linear_body<F_P16N, KTAIL>(lds, M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, tiles_m,
+                               (int)((d + Cfg<F_P16N>::OUT - 1) / Cfg<F_P16N>::OUT), 0, nullptr, nullptr);
+  else
+    linear_body<F_P16T, KTAIL>(lds, M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, tiles_m,
+                               (int)((d + Cfg<F_P16T>::OUT - 1) / Cfg<F_P16T>::OUT), 0, nullptr, nullptr);
+}
+
 // ---------------------------------------------------------------------------------
 // Few-token linear layer (M <= 16 TT tokens: decode), bound by streaming the weights.
 // A block owns 16 output rows and its 4 waves split K into quarters.  Each 64-deep K
@@ -768,17 +851,16 @@ namespace sk {
 constexpr int kAhead = 4;  // K steps in flight per wave
 }
 
+// Byte planes: P16T multiplies both planes (a row whose plane code has bit 1 set is in
+// the bias split); P16N the low planes alone (every high byte of the call is zero).
 template <int F, int TT>
-__global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int64_t n, const int8_t* __restrict__ xq,
-                                                      const float* __restrict__ sx,
-                                                      const int32_t* __restrict__ rowsum,
-                                                      const uint8_t* __restrict__ m,
-                                                      const uint8_t* __restrict__ split,
-                                                      const float* __restrict__ sbar, uint16_t* __restrict__ Y,
-                                                      int32_t* __restrict__ acc_dbg, int64_t wdelta,
-                                                      const int32_t* __restrict__ zbar_p,
-                                                      const int32_t* __restrict__ zw_p) {
-  constexpr int PL = (F == F_INT16 || F == F_UW4) ? 2 : 1;  // byte planes
+__device__ __forceinline__ void skinny_body(int64_t M, int64_t d, int64_t n, const int8_t* __restrict__ xq,
+                                            const float* __restrict__ sx, const int32_t* __restrict__ rowsum,
+                                            const uint8_t* __restrict__ m, const uint8_t* __restrict__ split,
+                                            const float* __restrict__ sbar, uint16_t* __restrict__ Y,
+                                            int32_t* __restrict__ acc_dbg, int64_t wdelta,
+                                            const int32_t* __restrict__ zbar_p, const int32_t* __restrict__ zw_p) {
+  constexpr int PL = (F == F_INT16 || F == F_UW4 || F == F_P16T) ? 2 : 1;  // byte planes
   __shared__ int red[4][PL * TT][4][64];
   __shared__ int vote;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -789,7 +871,7 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
   const int64_t per = (KT + 3) / 4;
   const int64_t s0 = (int64_t)wid * per;
   const int64_t s1 = s0 + per < KT ? s0 + per : KT;
-  const int64_t wrow = F == F_INT16 ? 2 * n : (F == F_INT8 ? n : n / 2);
+  const int64_t wrow = (F == F_INT16 || planar(F)) ? 2 * n : (F == F_INT8 ? n : n / 2);
   // UW4: the base codes lie wdelta bytes after U's; the lane's row zero points are fixed
   uint32_t zb2 = 0, zw2 = 0;
   if (F == F_UW4) {
@@ -808,10 +890,13 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
     st = st < KT ? st : KT - 1;
     int64_t k = st * 64 + 16 * kg;
     k = k < n ? k : n - 16;  // n is a multiple of 32: chunks are whole
-    if (F == F_INT16) {
+    if (F == F_INT16 || F == F_P16T) {  // 16 int16, or 16 high then 16 low bytes
       const v4i* pw = reinterpret_cast<const v4i*>(m + wr * wrow + 2 * k);
       S.w[0] = pw[0];
       S.w[1] = pw[1];
+    } else if (F == F_P16N) {  // the 16 low bytes
+      S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + 2 * k + 16);
+      S.w[1] = v4i{0, 0, 0, 0};
     } else if (F == F_INT8) {
       S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + k);
       S.w[1] = v4i{0, 0, 0, 0};
@@ -879,7 +964,10 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
         a[0][e] = (int)hl.x;
         a[PL - 1][e] = (int)hl.y;
       }
-    } else if (F == F_INT8) {
+    } else if (F == F_P16T) {
+      a[0] = S.w[0];
+      a[PL - 1] = S.w[1];
+    } else if (F == F_INT8 || F == F_P16N) {
       a[0] = S.w[0];
     } else {
       uint32_t o0, o1, o2, o3;
@@ -933,8 +1021,9 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
       pv[p] = red[0][p * TT + tt][v][l] + red[1][p * TT + tt][v][l] + red[2][p * TT + tt][v][l] +
               red[3][p * TT + tt][v][l];
     float y;
-    if (F == F_INT16 || F == F_UW4) {
-      const double rs128 = bias ? 128.0 * (double)rowsum[t] : 0.0;
+    if (F == F_INT16 || F == F_UW4 || F == F_P16T) {
+      const bool brow = F == F_P16T ? ((split[row] >> 1) & 1u) != 0 : bias;
+      const double rs128 = brow ? 128.0 * (double)rowsum[t] : 0.0;
       const double ex = fma(256.0, (double)pv[0], (double)pv[PL - 1]) + rs128;
       y = ((float)ex * sx[t]) * sbar[row];
     } else {
@@ -943,10 +1032,59 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
     const uint32_t b2 = __builtin_bit_cast(uint32_t, __builtin_convertvector((f2){y, y}, bf2));
     Y[t * d + row] = (uint16_t)(b2 & 0xFFFFu);
     if (acc_dbg) {
+      if (F == F_P16N) {  // the high plane (all zero) and the low plane
+        acc_dbg[t * d + row] = 0;
+        acc_dbg[M * d + t * d + row] = pv[0];
+      } else {
 #pragma unroll
-      for (int p = 0; p < PL; ++p) acc_dbg[(int64_t)p * M * d + t * d + row] = F == F_INT4 ? (pv[p] >> 4) : pv[p];
+        for (int p = 0; p < PL; ++p) acc_dbg[(int64_t)p * M * d + t * d + row] = F == F_INT4 ? (pv[p] >> 4) : pv[p];
+      }
     }
   }
+}
+
+template <int F, int TT>
+__global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int64_t n, const int8_t* __restrict__ xq,
+                                                      const float* __restrict__ sx,
+                                                      const int32_t* __restrict__ rowsum,
+                                                      const uint8_t* __restrict__ m,
+                                                      const uint8_t* __restrict__ split,
+                                                      const float* __restrict__ sbar, uint16_t* __restrict__ Y,
+                                                      int32_t* __restrict__ acc_dbg, int64_t wdelta,
+                                                      const int32_t* __restrict__ zbar_p,
+                                                      const int32_t* __restrict__ zw_p) {
+  skinny_body<F, TT>(M, d, n, xq, sx, rowsum, m, split, sbar, Y, acc_dbg, wdelta, zbar_p, zw_p);
+}
+
+// Byte planes at few tokens: the low planes alone when every plane code is 0.
+template <int TT>
+__global__ __launch_bounds__(256) void k_linear_skinny_planes(int64_t M, int64_t d, int64_t n,
+                                                             const int8_t* __restrict__ xq,
+                                                             const float* __restrict__ sx,
+                                                             const int32_t* __restrict__ rowsum,
+                                                             const uint8_t* __restrict__ m,
+                                                             const uint8_t* __restrict__ code,
+                                                             const float* __restrict__ sbar, uint16_t* __restrict__ Y,
+                                                             int32_t* __restrict__ acc_dbg) {
+  __shared__ int nz;
+  const int tid = threadIdx.x;
+  if (tid == 0) nz = 0;
+  __syncthreads();
+  int fl = 0;
+  for (int64_t x = 16 * (int64_t)tid; x < d; x += 16 * 256) {
+    if (x + 16 <= d) {
+      const uint4 v = *reinterpret_cast<const uint4*>(code + x);
+      fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
+    } else {
+      for (int64_t k = x; k < d; ++k) fl |= (int)(code[k] != 0);
+    }
+  }
+  if (fl) nz = 1;  // every writer stores 1
+  __syncthreads();
+  if (nz == 0)
+    skinny_body<F_P16N, TT>(M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, 0, nullptr, nullptr);
+  else
+    skinny_body<F_P16T, TT>(M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, 0, nullptr, nullptr);
 }
 
 static int device_cus() {
@@ -964,17 +1102,21 @@ static hipError_t set_linear_attrs() {
   using namespace lin;
   static bool attr_set = false;
   if (attr_set) return hipSuccess;
-  const void* fns[8] = {reinterpret_cast<const void*>(&k_linear<F_INT8, false>),
+  const void* fns[10] = {reinterpret_cast<const void*>(&k_linear<F_INT8, false>),
                         reinterpret_cast<const void*>(&k_linear<F_INT8, true>),
                         reinterpret_cast<const void*>(&k_linear<F_INT4, false>),
                         reinterpret_cast<const void*>(&k_linear<F_INT4, true>),
                         reinterpret_cast<const void*>(&k_linear<F_INT16, false>),
                         reinterpret_cast<const void*>(&k_linear<F_INT16, true>),
                         reinterpret_cast<const void*>(&k_linear<F_UW4, false>),
-                        reinterpret_cast<const void*>(&k_linear<F_UW4, true>)};
-  const int lds_of[8] = {Cfg<F_INT8>::LDS, Cfg<F_INT8>::LDS, Cfg<F_INT4>::LDS, Cfg<F_INT4>::LDS,
-                         Cfg<F_INT16>::LDS, Cfg<F_INT16>::LDS, Cfg<F_UW4>::LDS, Cfg<F_UW4>::LDS};
-  for (int k = 0; k < 8; ++k) {
+                        reinterpret_cast<const void*>(&k_linear<F_UW4, true>),
+                        reinterpret_cast<const void*>(&k_linear_planes<false>),
+                        reinterpret_cast<const void*>(&k_linear_planes<true>)};
+  static_assert(Cfg<F_P16T>::LDS >= Cfg<F_P16N>::LDS, "the planes kernel sizes its LDS for both forms");
+  const int lds_of[10] = {Cfg<F_INT8>::LDS, Cfg<F_INT8>::LDS, Cfg<F_INT4>::LDS, Cfg<F_INT4>::LDS,
+                          Cfg<F_INT16>::LDS, Cfg<F_INT16>::LDS, Cfg<F_UW4>::LDS, Cfg<F_UW4>::LDS,
+                          Cfg<F_P16T>::LDS, Cfg<F_P16T>::LDS};
+  for (int k = 0; k < 10; ++k) {
     const hipError_t e = hipFuncSetAttribute(fns[k], hipFuncAttributeMaxDynamicSharedMemorySize, lds_of[k]);
     if (e != hipSuccess) return e;
   }
@@ -1017,11 +1159,45 @@ static hipError_t launch_fmt(int64_t M, int64_t d, int64_t n, const int8_t* xq, 
   return hipGetLastError();
 }
 
+// Byte-plane merged integers: the grid is sized for the two-plane tiles (128 outputs);
+// the low-plane form has half as many tiles and the extra blocks find none.
+static hipError_t launch_planes(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx,
+                                const int32_t* rowsum, const uint8_t* mb, const uint8_t* code, const float* sbar,
+                                uint16_t* Y, int32_t* acc_dbg, hipStream_t st) {
+  using namespace lin;
+  const hipError_t e = set_linear_attrs();
+  if (e != hipSuccess) return e;
+  if (M <= 32) {
+    const dim3 g((unsigned)((d + 15) / 16));
+    if (M <= 16)
+      hipLaunchKernelGGL((k_linear_skinny_planes<1>), g, dim3(256), 0, st, M, d, n, xq, sx, rowsum, mb, code, sbar, Y,
+                         acc_dbg);
+    else
+      hipLaunchKernelGGL((k_linear_skinny_planes<2>), g, dim3(256), 0, st, M, d, n, xq, sx, rowsum, mb, code, sbar, Y,
+                         acc_dbg);
+    return hipGetLastError();
+  }
+  const int tiles_m = (int)((M + BM - 1) / BM);
+  const int ntile = tiles_m * (int)((d + Cfg<F_P16T>::OUT - 1) / Cfg<F_P16T>::OUT);
+  const int KT = (int)((n + BK - 1) / BK);
+  const int cus = device_cus();
+  const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
+  if ((n % BK) != 0)
+    hipLaunchKernelGGL((k_linear_planes<true>), grid, dim3(kThreads), Cfg<F_P16T>::LDS, st, M, d, n, xq, sx, rowsum,
+                       mb, code, sbar, Y, acc_dbg, tiles_m);
+  else
+    hipLaunchKernelGGL((k_linear_planes<false>), grid, dim3(kThreads), Cfg<F_P16T>::LDS, st, M, d, n, xq, sx, rowsum,
+                       mb, code, sbar, Y, acc_dbg, tiles_m);
+  return hipGetLastError();
+}
+
 hipError_t launch_linear(int64_t M, int64_t d, int64_t n, const int8_t* xq, const float* sx, const int32_t* rowsum,
                          int wfmt, const void* m, const uint8_t* split, const float* sbar, uint16_t* Y,
                          int32_t* acc_dbg, hipStream_t st) {
   const uint8_t* mb = static_cast<const uint8_t*>(m);
   switch (wfmt) {
+    case F_P16T:
+      return launch_planes(M, d, n, xq, sx, rowsum, mb, split, sbar, Y, acc_dbg, st);
     case F_INT8:
       return launch_fmt<F_INT8>(M, d, n, xq, sx, rowsum, mb, split, sbar, Y, acc_dbg, 0, nullptr, nullptr, st);
     case F_INT4:

@@ -212,13 +212,10 @@ __global__ __launch_bounds__(256) void k_quant_act(int64_t n, const float* __res
 }
 
 // ---------------------------------------------------------------------------------
-// K2 (fast path): adaptation term U and per-tile row range.
-// Block = 256 threads x 4 consecutive columns (1024-column tile) x kRows rows.
-// B[:, j..j+3] stays in registers for all kRows rows; A[i, :] is uniform per row
-// (scalar loads).  One Philox block serves the 4 elements of a thread's row segment
-// (needs n % 4 == 0).  U is written for every element (0 where w == 0).
+// K2: adaptation term U and per-tile row range.  U is written for every element; the
+// value at a w == 0 element is not specified (the quantize kernels never read it).
 // ---------------------------------------------------------------------------------
-constexpr int kAdaptCols = 1024;  // tile width of the generic path and of CPT = 4
+constexpr int kAdaptCols = 1024;  // column-tile width of the general path
 
 // Reciprocals RN32(1/w) of the signed pretrained integers w in [-255, 255] (0 for
 // w = 0), for the division t / w below.
@@ -281,7 +278,6 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
                                                     unsigned long long* __restrict__ sat_zero, int64_t row0) {
   __shared__ LnLds tab[96];
   __shared__ float rcp[511];
-  __shared__ int smin[4][32], smax[4][32];
   load_ln_table(tab);
   load_rcp_table(rcp);
   if (sat_zero && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *sat_zero = 0ull;
@@ -339,36 +335,54 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
     }
     int kmin = kKeyPosInf, kmax = kKeyNegInf;
     if (row_ok) {
+      const uint64_t qrow = (uint64_t)(i + row0) * (uint64_t)n;  // R's linear index of the row's column 0
+      // reciprocal-table entry of w = code - zi is code + (255 - zc): exact when zi is in
+      // [0, 255]; other rows take the IEEE division and only need an index in range
+      const int rbase = 255 - min(max(zi, 0), 255);
       // accumulator group g = 4 blk + q: columns jw + 32 blk + 8 q + 4 h + 0..3
 #pragma unroll
       for (int g = 0; g < 8; ++g) {
         const int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
         if (jg >= n) continue;  // n % 4 == 0: a group is entirely inside or outside
-        int w[4];
-        if (W4) {
+        int code[4], w[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (int)((wcode[g] >> (4 * e)) & 15u) - zi;
+        for (int e = 0; e < 4; ++e) {
+          code[e] = W4 ? (int)((wcode[g] >> (4 * e)) & 15u) : (int)((wcode[g] >> (8 * e)) & 255u);
+          w[e] = code[e] - zi;
+        }
+        float y[4];  // reciprocals of w, read first: the Philox rounds cover the LDS latency
+        if (!PTQ) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) y[e] = rcp[code[e] + rbase];
+        }
+        const U4 rnd = philox_block((qrow + (uint64_t)jg) >> 2, layer_id, seed);
+        float rs[4];
+        if (DIST == kAuxLaplace) {
+          float L[4];
+          laplace4(rnd, tab, L);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) rs[e] = ci * L[e];
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) w[e] = (int)((wcode[g] >> (8 * e)) & 255u) - zi;
+          for (int e = 0; e < 4; ++e) rs[e] = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
         }
-        const U4 rnd = philox_block(((uint64_t)(i + row0) * (uint64_t)n + (uint64_t)jg) >> 2, layer_id, seed);
         float u[4], t[4], q[4];
         if (PTQ) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float rs = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
-            q[e] = (si * (float)w[e] + rs) + acc[4 * g + e];  // binary32 steps in this order
-          }
+          for (int e = 0; e < 4; ++e) q[e] = (si * (float)w[e] + rs[e]) + acc[4 * g + e];  // binary32, in this order
         } else {
-          bool slow = !zok;
+          // the steps of div_small_int are exact for 2^-100 <= |t| < 2^100, i.e. biased
+          // exponents 27 .. 226 (NaN and inf have 255); the group's extremes decide
+          int emin = 255, emax = 0;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float rs = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
-            t[e] = rs + acc[4 * g + e];
-            q[e] = div_small_int(t[e], (float)w[e], rcp[rcp_index(w[e])]);
-            slow = slow || (w[e] != 0 && !div_small_int_ok(t[e]));
+            t[e] = rs[e] + acc[4 * g + e];
+            q[e] = div_small_int(t[e], (float)w[e], y[e]);
+            const int ex = (int)((__float_as_uint(t[e]) >> 23) & 0xFFu);
+            emin = min(emin, ex);
+            emax = max(emax, ex);
           }
+          const bool slow = !zok || emin < 27 || emax > 226;
           // the IEEE division runs only in waves where some lane needs it
           if (__builtin_amdgcn_ballot_w64(slow) != 0) {
             __asm__ volatile("");  // keeps the branch: the division is not speculated
@@ -380,32 +394,23 @@ __global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uin
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const bool valid = PTQ || w[e] != 0;
-          const float uu = PTQ ? q[e] : si + q[e];
-          u[e] = valid ? uu : 0.0f;
-          const int key = f32_key(uu);
+          u[e] = PTQ ? q[e] : si + q[e];  // U of a w == 0 element is written but never read
+          const int key = f32_key(u[e]);
           kmin = valid ? min(kmin, key) : kmin;
           kmax = valid ? max(kmax, key) : kmax;
         }
         *reinterpret_cast<float4*>(U + i * n + jg) = make_float4(u[0], u[1], u[2], u[3]);
       }
     }
-    // lanes l and l ^ 32 hold the same row
+    // lanes l and l ^ 32 hold the same row; each wave writes the partial of its own 64
+    // columns (partial column 4 blockIdx.x + wid), so the waves never wait for each other
     kmin = min(kmin, __shfl_xor(kmin, 32, kWave));
     kmax = max(kmax, __shfl_xor(kmax, 32, kWave));
-    if (h == 0) {
-      smin[wid][li] = kmin;
-      smax[wid][li] = kmax;
+    if (h == 0 && row_ok) {
+      const int64_t col = (int64_t)blockIdx.x * 4 + wid;
+      pmin[col * d + i] = kmin;
+      pmax[col * d + i] = kmax;
     }
-    __syncthreads();
-    if (threadIdx.x < 32) {
-      const int t = threadIdx.x;
-      const int64_t row = i0 + t;
-      if (row < d) {
-        pmin[(int64_t)blockIdx.x * d + row] = min(min(smin[0][t], smin[1][t]), min(smin[2][t], smin[3][t]));
-        pmax[(int64_t)blockIdx.x * d + row] = max(max(smax[0][t], smax[1][t]), max(smax[2][t], smax[3][t]));
-      }
-    }
-    __syncthreads();  // smin / smax are reused by the next row tile
   }
 }
 
@@ -563,16 +568,17 @@ __device__ __forceinline__ int mul_code(float u, float sbar, int zbar, int qmax)
 // U_round from q = U * RN(1/s_bar) instead of RN(U / s_bar).  With RN(1/s_bar) a
 // normal number, q lies within (2^-23 + 2^-48) |U/s_bar| of U/s_bar and RN(U/s_bar)
 // within 2^-24 |U/s_bar|, so for |q| < 512 the two are less than 2^-13 apart; when q
-// is farther than 2^-11 from every half-integer they round to the same integer.
-// `exact` is false otherwise (also for a non-finite q or a subnormal RN(1/s_bar)),
-// and the caller then recomputes the code with the IEEE division.
+// is farther than 2^-11 from every half-integer (|q - rint(q)| < 1/2 - 2^-11; the
+// difference is exact) they round to the same integer.  `exact` is false otherwise
+// (also for a non-finite q or a subnormal RN(1/s_bar): rs_ok false), and the caller
+// then recomputes the code with the IEEE division.
 // (Every valid U lies in [lo, hi], so |U / s_bar| <= 2^bU - 1 < 512 whenever s_bar
 // is the row's own scale.)
-__device__ __forceinline__ int mul_code_fast(float u, const MulParams& P, int qmax, bool& exact) {
+__device__ __forceinline__ int mul_code_fast(float u, const MulParams& P, bool rs_ok, int qmax, bool& exact) {
   const float qt = u * P.rsbar;
-  const float fr = qt - floorf(qt);
-  exact = fabsf(qt) < 512.0f && fabsf(fr - 0.5f) > 0x1p-11f && P.rsbar >= 0x1p-126f;
-  const float q = fminf(fmaxf(rintf(qt), -65536.0f), 65536.0f);
+  const float r = rintf(qt);
+  exact = rs_ok && fabsf(qt) < 512.0f && fabsf(qt - r) < 0.5f - 0x1p-11f;
+  const float q = fminf(fmaxf(r, -65536.0f), 65536.0f);
   const int v = (int)q + P.zbar;
   return v < 0 ? 0 : (v > qmax ? qmax : v);
 }
@@ -610,16 +616,67 @@ __device__ __forceinline__ int code_at(const uint8_t* __restrict__ wround, int64
   return wround[i * n + j];
 }
 
-// CODES: instead of m (and the split codes), store U_round itself as packed nibbles
-// (u_bits <= 4, n even; low nibble = even column), for a linear layer that forms m on
-// load.
-template <bool W4, bool CODES>
+// Per-row parameters of the MUL quantizer, once per row before the element pass: the
+// row range (the reduction of the adaptation kernel's partials into umin_out / umax_out,
+// or the caller's umin_in / umax_in), s_bar and z_bar (written to the outputs), RN(1 /
+// s_bar), and whether every merged integer of the row is certainly small:
+// max |U_round - z_bar| max |W_round - z| <= 32639 (codes W_round in [0, wmax]), so that
+// no element saturates or needs the bias byte split.  split (nullable) is cleared; the
+// quantize kernel raises it for rows holding some m >= 32640.  With `planes` it is
+// the row's byte-plane code instead: 0 for a small row (balanced split; the quantize
+// kernel raises bit 0 when some high byte is not zero), 3 otherwise (bias split).
+__global__ __launch_bounds__(256) void k_mul_params(int64_t d, int ntiles, const int* __restrict__ pmin,
+                                                   const int* __restrict__ pmax, const float* __restrict__ umin_in,
+                                                   const float* __restrict__ umax_in, float* __restrict__ umin_out,
+                                                   float* __restrict__ umax_out, int qmax, int wmax,
+                                                   const int32_t* __restrict__ z, float* __restrict__ sbar,
+                                                   int32_t* __restrict__ zbar, float* __restrict__ rs,
+                                                   int* __restrict__ small, uint8_t* __restrict__ split,
+                                                   bool planes) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < d; i += (int64_t)gridDim.x * blockDim.x) {
+    float a, b;
+    if (umin_in) {
+      a = umin_in[i];
+      b = umax_in[i];
+    } else {
+      row_range(pmin, pmax, d, i, ntiles, a, b);
+      umin_out[i] = a;
+      umax_out[i] = b;
+    }
+    const MulParams P = mul_params(a, b, qmax);
+    sbar[i] = P.sbar;
+    zbar[i] = P.zbar;
+    rs[i] = P.rsbar;
+    const int64_t zi = z[i];
+    const int64_t mw = max(zi < 0 ? -zi : zi, (int64_t)wmax - zi < 0 ? zi - wmax : (int64_t)wmax - zi);
+    const int64_t mu = max(P.zbar, qmax - P.zbar);
+    const bool sm = mw * mu <= (int64_t)(kSplitBiasMin - 1);
+    small[i] = sm;
+    if (split) split[i] = planes ? (sm ? 0 : 3) : 0;
+  }
+}
+
+// Output forms of the MUL quantizer.
+//  kOutInt16:  m as int16 d x n (and the split codes);
+//  kOutCodes:  U_round itself as packed nibbles (u_bits <= 4, n even; low nibble = even
+//              column), for a linear layer that forms m on load;
+//  kOutPlanes: m already split into its two int8 planes, the layout the linear layer
+//              reads without conversion: per row, for each group of 16 columns, the 16
+//              high bytes then the 16 low bytes (d x 2n bytes; n % 16 == 0).  A small
+//              row (plane code 0 on entry) takes the balanced split hi = (m + 128) >> 8,
+//              lo = m - 256 hi, and its code becomes 1 when some hi is not zero; any other
+//              row (code 3) takes the bias split hi = m >> 8, lo = (m & 0xFF) - 128.
+// Per-row s_bar, z_bar, RN(1 / s_bar) and the small-row flag come from k_mul_params.
+enum { kOutInt16 = 0, kOutCodes = 1, kOutPlanes = 2 };
+
+template <bool W4, int OUT>
 __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, int u_bits,
                                                         const uint8_t* __restrict__ wround,
                                                         const int32_t* __restrict__ z, const float* __restrict__ U,
-                                                        const float* __restrict__ umin_r,
-                                                        const float* __restrict__ umax_r, int16_t* __restrict__ m,
-                                                        float* __restrict__ sbar_out, int32_t* __restrict__ zbar_out,
+                                                        const float* __restrict__ sbar_r,
+                                                        const int32_t* __restrict__ zbar_r,
+                                                        const float* __restrict__ rs_r,
+                                                        const int* __restrict__ small_r, int16_t* __restrict__ m,
                                                         uint8_t* __restrict__ split, uint8_t* __restrict__ uround_dbg,
                                                         unsigned long long* __restrict__ sat,
                                                         uint8_t* __restrict__ ucode) {
@@ -644,14 +701,10 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
 #pragma unroll
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
-        if (i >= d) break;
-        const float umin = umin_r[i], umax = umax_r[i];
-        const MulParams P = mul_params(umin, umax, qmax);
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-          sbar_out[i] = P.sbar;
-          zbar_out[i] = P.zbar;
-        }
-        if (j0 >= n) continue;
+        if (i >= d || j0 >= n) break;
+        const MulParams P{sbar_r[i], rs_r[i], zbar_r[i]};
+        const bool rs_ok = P.rsbar >= 0x1p-126f;  // a normal reciprocal
+        const bool small = small_r[i] != 0;
         const int zi = z[i];
         const float uu[8] = {ua[rr].x, ua[rr].y, ua[rr].z, ua[rr].w, ub[rr].x, ub[rr].y, ub[rr].z, ub[rr].w};
         int mm[8], ur[8], w[8];
@@ -660,7 +713,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         for (int e = 0; e < 8; ++e) {
           w[e] = code_of<W4>(cw[rr], e) - zi;
           bool exact = true;
-          ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, qmax, exact) : P.zbar;
+          ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, rs_ok, qmax, exact) : P.zbar;
           redo[e] = !exact;
           any = any || redo[e];
         }
@@ -671,31 +724,63 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           for (int e = 0; e < 8; ++e)
             if (redo[e]) ur[e] = mul_code(uu[e], P.sbar, P.zbar, qmax);
         }
-        if (CODES) {
+        if (OUT == kOutCodes) {
           uint32_t pk = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk |= (uint32_t)ur[e] << (4 * e);
           store_once4(ucode + ((i * n + j0) >> 1), pk);
           continue;
         }
+        if (small) {  // |m| <= 32639 for the whole row: no saturation, no bias split
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          int mv = w[e] != 0 ? (ur[e] - P.zbar) * w[e] : 0;
-          if (mv > 32767) { mv = 32767; ++nsat; }
-          if (mv < -32768) { mv = -32768; ++nsat; }
-          mm[e] = mv;
+          for (int e = 0; e < 8; ++e) mm[e] = (ur[e] - P.zbar) * w[e];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            int mv = w[e] != 0 ? (ur[e] - P.zbar) * w[e] : 0;
+            if (mv > 32767) { mv = 32767; ++nsat; }
+            if (mv < -32768) { mv = -32768; ++nsat; }
+            mm[e] = mv;
+          }
+          if (OUT == kOutInt16 && split) {  // the balanced byte split of the int16 GEMM needs m <= 32639
+            int mx = mm[0];
+#pragma unroll
+            for (int e = 1; e < 8; ++e) mx = max(mx, mm[e]);
+            if (mx >= kSplitBiasMin) split[i] = 1;
+          }
         }
-        int4 pk;
-        pk.x = (mm[0] & 0xFFFF) | (mm[1] << 16);
-        pk.y = (mm[2] & 0xFFFF) | (mm[3] << 16);
-        pk.z = (mm[4] & 0xFFFF) | (mm[5] << 16);
-        pk.w = (mm[6] & 0xFFFF) | (mm[7] << 16);
-        store_once16(m + i * n + j0, pk);
-        if (split) {  // the balanced byte split of the int16 GEMM needs m <= 32639
-          int mx = mm[0];
+        if (OUT == kOutPlanes) {
+          // hi / lo bytes of the 8 values, packed 4 per dword (byte e of the pair = value e)
+          uint32_t h[8], l[8], any_hi = 0;
+          if (small) {  // balanced
 #pragma unroll
-          for (int e = 1; e < 8; ++e) mx = max(mx, mm[e]);
-          if (mx >= kSplitBiasMin) split[i] = 1;
+            for (int e = 0; e < 8; ++e) {
+              const int hv = (mm[e] + 128) >> 8;
+              h[e] = (uint32_t)hv & 0xFFu;
+              l[e] = (uint32_t)(mm[e] - 256 * hv) & 0xFFu;
+              any_hi |= h[e];
+            }
+          } else {  // bias
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              h[e] = (uint32_t)(mm[e] >> 8) & 0xFFu;
+              l[e] = ((uint32_t)mm[e] & 0xFFu) ^ 0x80u;
+            }
+          }
+          uint8_t* row = reinterpret_cast<uint8_t*>(m) + i * 2 * n;
+          const int64_t off = 2 * (j0 & ~(int64_t)15) + (j0 & 15);  // hi bytes; lo bytes 16 further
+          store_once8(row + off, make_uint2(h[0] | h[1] << 8 | h[2] << 16 | h[3] << 24,
+                                            h[4] | h[5] << 8 | h[6] << 16 | h[7] << 24));
+          store_once8(row + off + 16, make_uint2(l[0] | l[1] << 8 | l[2] << 16 | l[3] << 24,
+                                                 l[4] | l[5] << 8 | l[6] << 16 | l[7] << 24));
+          if (small && any_hi) split[i] = 1;
+        } else {
+        int4 pk;
+        pk.x = (int)__builtin_amdgcn_perm((uint32_t)mm[1], (uint32_t)mm[0], 0x05040100u);
+        pk.y = (int)__builtin_amdgcn_perm((uint32_t)mm[3], (uint32_t)mm[2], 0x05040100u);
+        pk.z = (int)__builtin_amdgcn_perm((uint32_t)mm[5], (uint32_t)mm[4], 0x05040100u);
+        pk.w = (int)__builtin_amdgcn_perm((uint32_t)mm[7], (uint32_t)mm[6], 0x05040100u);
+        store_once16(m + i * n + j0, pk);
         }
         if (uround_dbg) {
           uint2 pu;
@@ -708,12 +793,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
         if (i >= d) break;
-        const float umin = umin_r[i], umax = umax_r[i];
-        const MulParams P = mul_params(umin, umax, qmax);
-        if (blockIdx.x == 0 && threadIdx.x == 0) {
-          sbar_out[i] = P.sbar;
-          zbar_out[i] = P.zbar;
-        }
+        const MulParams P{sbar_r[i], rs_r[i], zbar_r[i]};
         const int zi = z[i];
         int lo_code = 0;
         for (int e = 0; e < kQElems; ++e) {
@@ -721,7 +801,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           if (j >= n) break;
           int uv;
           const int mv = mul_merge(code_at<W4>(wround, i, n, j) - zi, U[i * n + j], P, qmax, uv, nsat);
-          if (CODES) {  // n is even: the odd column of every pair exists
+          if (OUT == kOutCodes) {  // n is even: the odd column of every pair exists
             if ((j & 1) == 0)
               lo_code = uv;
             else
@@ -779,7 +859,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_ptq(int64_t d, int64_t n, i
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           bool exact = true;
-          cd[e] = mul_code_fast(xx[e], P, qmax, exact);
+          cd[e] = mul_code_fast(xx[e], P, P.rsbar >= 0x1p-126f, qmax, exact);
           redo[e] = !exact;
           any = any || redo[e];
         }
@@ -994,6 +1074,53 @@ hipError_t launch_aux_debug(int64_t blocks, const uint32_t* words, int dist, flo
   return hipGetLastError();
 }
 
+// Diagnostic: the rank-r product acc[i][j] = sum_k A[i][k] B[k][j] formed on the
+// matrix cores as the merge kernels form it, one instruction per k in increasing k,
+// starting from +0 (d x r and r x n fp32 inputs; d x n output).  One wave per tile of
+// 32 (FORM 0) or 4 (FORM 1) rows x 64 columns; d and n are multiples of the tile.
+//  FORM 0, v_mfma_f32_32x32x1f32 taken transposed as in the adaptation kernel: lane l
+//   supplies B[k][j0 + l] (A operand) and A[i0 + l % 32][k] (B operand); register
+//   4 g + e of lane l ends with row i0 + l % 32, column j0 + 32 (g >> 2) + 8 (g & 3) +
+//   4 (l >> 5) + e.
+//  FORM 1, v_mfma_f32_4x4x1f32 as in the fused merge: lane l supplies B[k][j0 + l] and
+//   A[i0 + l % 4][k]; register e of lane 4 b + q ends with row i0 + q, column j0 + 4 b + e.
+template <int FORM>
+__global__ __launch_bounds__(64) void k_debug_mfma_chain(int64_t d, int64_t n, int r, const float* __restrict__ A,
+                                                        const float* __restrict__ B, float* __restrict__ out) {
+  const int lane = threadIdx.x;
+  const int64_t j0 = (int64_t)blockIdx.x * 64, i0 = (int64_t)blockIdx.y * (FORM == 0 ? 32 : 4);
+  if (FORM == 0) {
+    v32f acc;
+#pragma unroll
+    for (int x = 0; x < 32; ++x) acc[x] = 0.0f;
+    for (int k = 0; k < r; ++k)
+      acc = __builtin_amdgcn_mfma_f32_32x32x1f32(B[(int64_t)k * n + j0 + lane], A[(i0 + (lane & 31)) * r + k], acc,
+                                                 0, 0, 0);
+#pragma unroll
+    for (int g = 0; g < 8; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        out[(i0 + (lane & 31)) * n + j0 + 32 * (g >> 2) + 8 * (g & 3) + 4 * (lane >> 5) + e] = acc[4 * g + e];
+  } else {
+    v4f acc = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int k = 0; k < r; ++k)
+      acc = __builtin_amdgcn_mfma_f32_4x4x1f32(B[(int64_t)k * n + j0 + lane], A[(i0 + (lane & 3)) * r + k], acc, 0, 0,
+                                               0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[(i0 + (lane & 3)) * n + j0 + 4 * (lane >> 2) + e] = acc[e];
+  }
+}
+
+hipError_t launch_debug_mfma_chain(int form, int64_t d, int64_t n, int r, const float* A, const float* B, float* out,
+                                   hipStream_t st) {
+  const dim3 grid((unsigned)(n / 64), (unsigned)(d / (form == 0 ? 32 : 4)));
+  if (form == 0)
+    hipLaunchKernelGGL(k_debug_mfma_chain<0>, grid, dim3(64), 0, st, d, n, r, A, B, out);
+  else
+    hipLaunchKernelGGL(k_debug_mfma_chain<1>, grid, dim3(64), 0, st, d, n, r, A, B, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_ln_odd(int64_t count, const uint32_t* G, float* out, hipStream_t st) {
   hipLaunchKernelGGL(k_ln_odd, dim3(grid1((uint64_t)count, 256)), dim3(256), 0, st, count, G, out);
   return hipGetLastError();
@@ -1031,7 +1158,9 @@ hipError_t launch_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, fl
   return hipGetLastError();
 }
 
-int adapt_max_ntiles(int64_t n) { return (int)((n + kMfmaCols - 1) / kMfmaCols); }
+// Row partials per row: one per wave (4 per 256-column block) on the matrix-core path,
+// one per 1024-column tile on the general path.
+int adapt_max_ntiles(int64_t n) { return 4 * (int)((n + kMfmaCols - 1) / kMfmaCols); }
 
 template <int R, bool W4, bool PTQ, int DIST>
 static int64_t mfma_slots() {
@@ -1052,7 +1181,7 @@ static int64_t mfma_slots() {
 template <int R, bool W4, bool PTQ, int DIST>
 static hipError_t launch_adapt_mfma(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
   const int ntiles = (int)((a.n + kMfmaCols - 1) / kMfmaCols);
-  *ntiles_out = ntiles;
+  *ntiles_out = 4 * ntiles;  // a partial per wave
   const int64_t row_tiles = (a.d + 31) / 32;
   const int64_t slots = mfma_slots<R, W4, PTQ, DIST>();
   // row tiles per block (1..8): the count whose grid best fills the resident slots
@@ -1455,6 +1584,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
       const int a = min(min(smin[0][rr], smin[1][rr]), min(smin[2][rr], smin[3][rr]));
       const int b = max(max(smax[0][rr], smax[1][rr]), max(smax[2][rr], smax[3][rr]));
       const MulParams P = mul_params(key_f32(a), key_f32(b), qmax);
+      const bool rs_ok = P.rsbar >= 0x1p-126f;
       if (tid == 0) {
         sbar_out[i] = P.sbar;
         zbar_out[i] = P.zbar;
@@ -1479,7 +1609,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
         for (int e = 0; e < 4; ++e) {
           uu[e] = sU[rr * pitch + j0 + e];
           bool exact = true;
-          ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, qmax, exact) : P.zbar;
+          ur[e] = w[e] != 0 ? mul_code_fast(uu[e], P, rs_ok, qmax, exact) : P.zbar;
           redo[e] = !exact;
           any = any || redo[e];
         }
@@ -1524,40 +1654,45 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
 
 __global__ void k_zero_u64(unsigned long long* p) { *p = 0ull; }
 
-__global__ __launch_bounds__(256) void k_fill_u8(int64_t count, uint8_t* __restrict__ p, uint8_t v) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = v;
-}
-
-hipError_t launch_fill_u8(int64_t count, uint8_t* p, uint8_t v, hipStream_t st) {
-  if (count <= 0) return hipSuccess;
-  hipLaunchKernelGGL(k_fill_u8, dim3(grid1((uint64_t)count, 256)), dim3(256), 0, st, count, p, v);
-  return hipGetLastError();
-}
-
 static dim3 quant_grid(int64_t d, int64_t n) {
   const int64_t groups = (d + kQRows - 1) / kQRows;
   return dim3((unsigned)((n + kQCols - 1) / kQCols), (unsigned)(groups < 65535 ? (groups ? groups : 1) : 65535));
 }
 
+hipError_t launch_mul_params(int64_t d, int ntiles, const int* pmin, const int* pmax, const float* umin_in,
+                             const float* umax_in, float* umin_out, float* umax_out, int u_bits, int w_bits,
+                             const int32_t* z, float* sbar, int32_t* zbar, float* rs, int* small, uint8_t* split,
+                             bool planes, hipStream_t st) {
+  hipLaunchKernelGGL(k_mul_params, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin_in,
+                     umax_in, umin_out, umax_out, (1 << u_bits) - 1, (1 << w_bits) - 1, z, sbar, zbar, rs, small,
+                     split, planes);
+  return hipGetLastError();
+}
+
 hipError_t launch_quant_mul(int64_t d, int64_t n, int w_bits, int u_bits, const uint8_t* wround, const int32_t* z,
-                            const float* U, const float* umin, const float* umax, int16_t* m, float* sbar,
-                            int32_t* zbar, uint8_t* split, uint8_t* uround_dbg, unsigned long long* sat,
-                            uint8_t* ucode, hipStream_t st) {
+                            const float* U, const float* sbar, const int32_t* zbar, const float* rs,
+                            const int* small, void* m, uint8_t* split, uint8_t* uround_dbg,
+                            unsigned long long* sat, uint8_t* ucode, bool planes, hipStream_t st) {
   const dim3 grid = quant_grid(d, n);
-#define INTLORA_QMUL(W4, CODES)                                                                                  \
-  hipLaunchKernelGGL((k_quant_mul<W4, CODES>), grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, umin, \
-                     umax, m, sbar, zbar, split, uround_dbg, sat, ucode)
+  int16_t* m16 = static_cast<int16_t*>(m);
+#define INTLORA_QMUL(W4, OUT)                                                                                   \
+  hipLaunchKernelGGL((k_quant_mul<W4, OUT>), grid, dim3(kQThreads), 0, st, d, n, u_bits, wround, z, U, sbar, \
+                     zbar, rs, small, m16, split, uround_dbg, sat, ucode)
   if (ucode) {
     if (w_bits == 4)
-      INTLORA_QMUL(true, true);
+      INTLORA_QMUL(true, kOutCodes);
     else
-      INTLORA_QMUL(false, true);
+      INTLORA_QMUL(false, kOutCodes);
+  } else if (planes) {
+    if (w_bits == 4)
+      INTLORA_QMUL(true, kOutPlanes);
+    else
+      INTLORA_QMUL(false, kOutPlanes);
   } else {
     if (w_bits == 4)
-      INTLORA_QMUL(true, false);
+      INTLORA_QMUL(true, kOutInt16);
     else
-      INTLORA_QMUL(false, false);
+      INTLORA_QMUL(false, kOutInt16);
   }
 #undef INTLORA_QMUL
   return hipGetLastError();

@@ -94,6 +94,28 @@ def merge_mul(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out
     return o
 
 
+def merge_mul_planes(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, ws=None, out=None, u_range=None):
+    """MUL merge writing the merged integers as their two int8 byte planes (d x 2n
+    bytes) with per-row plane codes, for the linear layer's INT16_PLANES format."""
+    d, r = A.shape
+    n = Bm.shape[1]
+    dev = A.device
+    dsc = B.desc(d, n, r, w_bits, seed, layer_id, st.get("aux_dist", 0))
+    ws = workspace(B.INTLORA_OP_MERGE_MUL, d, n, r, w_bits, dev) if ws is None else ws
+    o = out or dict(planes=torch.empty((d, 2 * n), dtype=torch.uint8, device=dev),
+                    sbar=torch.empty(d, dtype=torch.float32, device=dev),
+                    zbar=torch.empty(d, dtype=torch.int32, device=dev),
+                    code=torch.empty(d, dtype=torch.uint8, device=dev),
+                    sat=torch.zeros(2, dtype=torch.int64, device=dev))
+    if dbg and "uround" not in o:
+        o["uround"] = torch.empty((d, n), dtype=torch.uint8, device=dev)
+    B.intlora_merge_mul_planes(dsc, B.base(st["wround"], st["z"], st["s"], st["c"]), B.lora(A, Bm), u_bits,
+                               o["planes"], o["sbar"], o["zbar"], o["code"],
+                               u_round_dbg=o.get("uround") if dbg else None, sat_count=o["sat"], ws=ws,
+                               u_min=u_range[0] if u_range else None, u_max=u_range[1] if u_range else None)
+    return o
+
+
 def merge_mul_noalloc(st, A, Bm, w_bits, u_bits, seed, layer_id, dbg=False, out=None, u_range=None):
     """MUL merge with the library's own per-device scratch (no workspace); same outputs
     as merge_mul."""
@@ -212,7 +234,7 @@ def linear(xq, sx, rowsum, wfmt, m, sbar, d, acc_dbg=False, out=None, split=None
     every row."""
     M, n = xq.shape
     Y = torch.empty((M, d), dtype=torch.int16, device=xq.device) if out is None else out
-    planes = 2 if wfmt == B.INTLORA_W_INT16 else 1
+    planes = 2 if wfmt in (B.INTLORA_W_INT16, B.INTLORA_W_INT16_PLANES) else 1
     acc = torch.empty((planes, M, d), dtype=torch.int32, device=xq.device) if acc_dbg else None
     B.intlora_linear_fwd(M, d, n, xq, sx, rowsum, wfmt, m, split, sbar, Y, acc)
     return Y, acc

@@ -397,6 +397,42 @@ def plane_split(m):
     return (m >= 32640).any(axis=1).astype(np.uint8)
 
 
+def plane_store(m, z, zbar, w_bits, u_bits):
+    """Byte-plane storage of MUL merged integers (rows x n, n a multiple of 16), as the
+    linear layer's int8 matrix cores take them ([IntLoRA notes] "two implementation
+    variants", MUL; the int16 values as two int8 byte planes).  Reading of the storage:
+    per row, the split is fixed before any element is known, from the bound
+    |m| <= max(|z|, |2^w_bits - 1 - z|) * max(z_bar, 2^u_bits - 1 - z_bar):
+      bound <= 32639: balanced split (hi = (m + 128) >> 8, lo = m - 256 hi);
+      otherwise:      bias split (hi = m >> 8, lo = (m & 0xFF) - 128).
+    Layout: per row, for each group of 16 columns, the 16 high bytes then the 16 low
+    bytes.  Code: 3 for a bias row; for a balanced row 1 if some high byte is not zero,
+    else 0.  Returns (layout uint8 rows x 2n, codes uint8)."""
+    m = np.asarray(m).astype(np.int64)
+    rows, n = m.shape
+    assert n % 16 == 0
+    z = np.asarray(z, np.int64).reshape(-1)
+    zbar = np.asarray(zbar, np.int64).reshape(-1)
+    wmax, umax = (1 << w_bits) - 1, (1 << u_bits) - 1
+    bound = np.maximum(np.abs(z), np.abs(wmax - z)) * np.maximum(zbar, umax - zbar)
+    bias = bound > 32639
+    hi, lo = byte_planes(m, split=bias.astype(np.uint8))
+    code = np.where(bias, 3, np.where((hi != 0).any(axis=1), 1, 0)).astype(np.uint8)
+    layout = np.concatenate([hi.reshape(rows, n // 16, 16), lo.reshape(rows, n // 16, 16)], axis=2)
+    return np.ascontiguousarray(layout.reshape(rows, 2 * n)).view(np.uint8), code
+
+
+def merged_from_planes(layout, code):
+    """The merged integers a byte-plane layout stores: 256 hi + lo (+ 128 on bias rows)."""
+    layout = np.asarray(layout, np.uint8)
+    rows, n2 = layout.shape
+    g = layout.view(np.int8).astype(np.int64).reshape(rows, n2 // 32, 32)
+    hi = g[:, :, :16].reshape(rows, n2 // 2)
+    lo = g[:, :, 16:].reshape(rows, n2 // 2)
+    bias = ((np.asarray(code, np.uint8) >> 1) & 1).astype(np.int64)[:, None]
+    return 256 * hi + lo + 128 * bias
+
+
 def merged_from_codes(ucode, wround, z, zbar):
     """The merged integers re-formed from stored codes ([IntLoRA notes] "两种实现版本",
     MUL: W' = s_bar (U_round - z_bar) (.) (W_round - z)): m = (U_round - z_bar) *

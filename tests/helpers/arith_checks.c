@@ -15,7 +15,7 @@
  * (2) The MUL quantizer's code (IntLoRA notes, "two implementation variants", MUL):
  *     with rs = RN(1/s) a normal number, qt = RN(u rs) is claimed to round (rint, half
  *     to even) to the same integer as RN(u / s) whenever |qt| < 512 and qt lies more
- *     than 2^-11 from every half-integer.
+ *     than 2^-11 from every half-integer, tested as |qt - rint(qt)| < 1/2 - 2^-11.
  */
 #include <math.h>
 #include <stdint.h>
@@ -98,8 +98,7 @@ int64_t count_code_mismatches(int64_t ns, const float* s, int span, int64_t* fas
                 const float u = from_bits((uint32_t)((int64_t)cb + dlt));
                 if (!isfinite(u)) continue;
                 const float qt = u * rs;
-                const float fr = qt - floorf(qt);
-                const int ok = fabsf(qt) < 512.0f && fabsf(fr - 0.5f) > 0x1p-11f;
+                const int ok = fabsf(qt) < 512.0f && fabsf(qt - rintf(qt)) < 0.5f - 0x1p-11f;
                 ++nt;
                 if (!ok) continue;
                 ++nf;
@@ -137,8 +136,7 @@ int64_t count_code_mismatches_random(int64_t ns, const float* s, int bits, int64
             const float x = ((float)(h >> 8) * 0x1p-24f * 2.0f - 1.0f) * qmax;  /* in [-qmax, qmax) */
             const float u = x * sb;
             const float qt = u * rs;
-            const float fr = qt - floorf(qt);
-            if (!(fabsf(qt) < 512.0f && fabsf(fr - 0.5f) > 0x1p-11f)) continue;
+            if (!(fabsf(qt) < 512.0f && fabsf(qt - rintf(qt)) < 0.5f - 0x1p-11f)) continue;
             ++nf;
             bad += rintf(qt) != rintf(u / sb);
         }

@@ -831,3 +831,188 @@ def test_merges_laws(ops, dist, d, n, r, w_bits):
     ref_p = oracle.ptq_merge(wr, z, s, R, A, Bm, 8)
     assert np.array_equal(host(g["code"]), ref_p["code"])
     assert np.array_equal(bits(host(g["s"])), bits(ref_p["s"]))
+
+
+# ----------------------------------------------------------------------------- matrix-core chains
+def _adversarial_operands(kind, d, n, r, seed):
+    """A (d x r) and B (r x n) whose fmaf chains exercise the roundings the matrix-core
+    instructions must reproduce one by one."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+
+    def mant(shape, bits):  # values 1.m with `bits` random significand bits, random sign
+        m = rng.integers(0, 1 << bits, size=shape)
+        sgn = rng.choice([-1.0, 1.0], size=shape)
+        return (sgn * (1.0 + m / float(1 << bits))).astype(np.float32)
+
+    if kind == "random":
+        A = (rng.standard_normal((d, r)) * np.exp2(rng.integers(-8, 9, (d, r)))).astype(np.float32)
+        B = (rng.standard_normal((r, n)) * np.exp2(rng.integers(-8, 9, (r, n)))).astype(np.float32)
+    elif kind == "ties":  # 12-bit significands: 25-bit products, halfway cases everywhere
+        A = mant((d, r), 12) * np.exp2(rng.integers(-3, 4, (d, r))).astype(np.float32)
+        B = mant((r, n), 12) * np.exp2(rng.integers(-3, 4, (r, n))).astype(np.float32)
+    elif kind == "subnormal":  # products and partial sums below 2^-126
+        A = mant((d, r), 23) * np.float32(2.0 ** -70)
+        B = mant((r, n), 23) * np.exp2(rng.integers(-72, -55, (r, n))).astype(np.float32)
+    elif kind == "cancel":  # pairs of terms that cancel up to a few units of the last place
+        A = mant((d, r), 23)
+        B = mant((r, n), 23)
+        B[1::2] = -B[0::2] * (1.0 + rng.integers(-3, 4, B[1::2].shape) * 2.0 ** -22).astype(np.float32)
+        A[:, 1::2] = A[:, 0::2]
+    elif kind == "zeros":  # signed zeros mixed in, whole zero rows and columns
+        A = mant((d, r), 23)
+        B = mant((r, n), 23)
+        A[rng.random((d, r)) < 0.3] = 0.0
+        B[rng.random((r, n)) < 0.3] = -0.0
+        A[:4] = -0.0
+        B[:, :8] = 0.0
+    else:  # "huge": sums near the top of the binary32 range
+        A = mant((d, r), 23) * np.float32(2.0 ** 60)
+        B = mant((r, n), 23) * np.float32(2.0 ** 60) / np.float32(r)
+    return np.ascontiguousarray(A, np.float32), np.ascontiguousarray(B, np.float32)
+
+
+@pytest.mark.parametrize("form", [0, 1])
+@pytest.mark.parametrize("kind", ["random", "ties", "subnormal", "cancel", "zeros", "huge"])
+def test_mfma_chain_equals_fmaf_chain(ops, form, kind):
+    """One v_mfma_f32_32x32x1f32 / 4x4x1f32 step per k is one fused multiply-add: the
+    chains the merges use for the MLA term's AB (IntLoRA notes, "2. MLA") equal a plain
+    fmaf chain over k from +0, bit for bit (signed zeros included), on operands built to
+    separate a fused from an unfused multiply-add."""
+    from tests.test_arith_substitutions import helper
+
+    d, n, r = 64, 256, 32
+    A, Bm = _adversarial_operands(kind, d, n, r, 31 + form)
+    ref = np.empty((d, n), np.float32)
+    helper().fmaf_chain(d, n, r, A.ctypes.data, Bm.ctypes.data, ref.ctypes.data)
+    out = torch.empty((d, n), dtype=torch.float32, device="cuda")
+    ops.B.intlora_debug_mfma_chain(form, d, n, r, cuda(A), cuda(Bm), out)
+    got = host(out)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (kind, form, int(np.sum(got.view(np.uint32) != ref.view(np.uint32))))
+    # the operands do separate the two: an unfused chain differs somewhere (except the
+    # cases built from exact products)
+    if kind in ("random", "ties", "cancel"):
+        unf = np.zeros((d, n), np.float32)
+        for k in range(r):
+            unf = (unf + (A[:, k:k + 1] * Bm[k:k + 1, :]).astype(np.float32)).astype(np.float32)
+        assert np.any(unf.view(np.uint32) != ref.view(np.uint32))
+
+
+def test_adaptation_kernel_rank_term_in_workspace(ops):
+    """The adaptation kernel's own matrix-core product, read back from the merge's
+    workspace: with c = 0 (R* = 0), s = 0 and W_round - z = 1, U = AB exactly, so the
+    workspace's U equals the fmaf chain of every element (ties and cancellations)."""
+    from tests.test_arith_substitutions import helper
+
+    d, n, r, w_bits = 64, 512, 32, 8
+    for kind in ("ties", "cancel", "random"):
+        A, Bm = _adversarial_operands(kind, d, n, r, 77)
+        ref = np.empty((d, n), np.float32)
+        helper().fmaf_chain(d, n, r, A.ctypes.data, Bm.ctypes.data, ref.ctypes.data)
+        st = dict(wround=cuda(np.full((d, n), 6, np.uint8)), z=cuda(np.full(d, 5, np.int32)),
+                  s=cuda(np.zeros(d, np.float32)), c=cuda(np.zeros(d, np.float32)))
+        ws = ops.workspace(ops.B.INTLORA_OP_STATS_UMINMAX, d, n, r, w_bits, torch.device("cuda"))
+        ops.u_minmax(st, cuda(A), cuda(Bm), w_bits, 0, 0, ws=ws)
+        U = host(ws[: d * n * 4].view(torch.float32).view(d, n))
+        # U = 0 + (0 + acc) / 1: equal to acc up to the sign of a zero
+        nz = ref != 0
+        assert np.array_equal(U[nz].view(np.uint32), ref[nz].view(np.uint32)), kind
+        assert np.all(U[~nz] == 0)
+
+
+# ----------------------------------------------------------------------------- byte-plane storage
+def _planes_linear_check(ops, M, m, z, zbar, w_bits, u_bits, seed, expect_narrow):
+    """The linear layer on the byte-plane storage of m (built by the oracle's storage
+    rule) against the oracle's integer product: every bf16 output and both accumulator
+    planes."""
+    d, n = m.shape
+    rng = np.random.Generator(np.random.PCG64(seed))
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(seed + 1, M, 1e-3, 0.1)
+    sbar = synth.random_positive(seed + 2, d, 1e-5, 1e-2)
+    rs = xq.astype(np.int32).sum(axis=1).astype(np.int32)
+    lay, code = oracle.plane_store(m, z, zbar, w_bits, u_bits)
+    assert (not code.any()) == expect_narrow
+    _, _, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
+    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), ops.B.INTLORA_W_INT16_PLANES, cuda(lay), cuda(sbar), d,
+                        acc_dbg=True, split=cuda(code))
+    g = lay.view(np.int8).astype(np.int64).reshape(d, n // 16, 32)
+    hi, lo = g[:, :, :16].reshape(d, n), g[:, :, 16:].reshape(d, n)
+    acc = host(acc)
+    assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T)
+    assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T)
+    assert np.array_equal(host(Y).view(np.uint16), yref)
+
+
+@pytest.mark.parametrize("M,d,n", [(1, 7, 32), (16, 300, 4128), (32, 1000, 1024), (37, 100, 96), (300, 260, 512),
+                                   (2600, 4000, 224), (1100, 700, 3104)])
+def test_linear_planes_bitexact(ops, M, d, n):
+    """The INT16_PLANES format: narrow calls (every plane code 0: the low planes alone, as
+    int8 weights with 256 outputs per tile), balanced two-plane calls, and calls with
+    bias-split rows; few tokens, ragged tiles, partial last K stages, several tiles per
+    block."""
+    rng = np.random.Generator(np.random.PCG64(M + d + n))
+    # narrow: |m| <= 127 with 4-bit codes and mid-range zero points (bound 8 * 8 = 64)
+    mn = rng.integers(-64, 65, size=(d, n))
+    _planes_linear_check(ops, M, mn, np.full(d, 7), np.full(d, 8), 4, 4, seed=n + 1, expect_narrow=True)
+    # balanced, some rows with values beyond int8
+    mb = rng.integers(-225, 226, size=(d, n))
+    _planes_linear_check(ops, M, mb, np.full(d, 7), np.full(d, 7), 4, 4, seed=n + 2, expect_narrow=False)
+    # 8-bit codes, every third row in the bias split by the bound (z = 0, z_bar = 128)
+    m8 = rng.integers(-32768, 32768, size=(d, n))
+    z = np.where(np.arange(d) % 3 == 0, 0, 128)
+    m8[z == 128] = np.clip(m8[z == 128], -16384, 16384)
+    _planes_linear_check(ops, M, m8, z, np.full(d, 128), 8, 8, seed=n + 3, expect_narrow=False)
+
+
+PLANE_MERGE_CASES = [(37, 1024, 8, 8, 8), (64, 768, 4, 4, 4), (96, 3072, 32, 4, 4), (33, 1600, 4, 8, 8),
+                     (6, 1536, 64, 4, 2)]
+
+
+@pytest.mark.parametrize("d,n,r,w_bits,u_bits", PLANE_MERGE_CASES)
+def test_merge_mul_planes_bitexact(ops, d, n, r, w_bits, u_bits):
+    """intlora_merge_mul_planes against the oracle's MUL merge and its byte-plane
+    storage rule: the layout bytes, plane codes, s_bar, z_bar, U codes and saturations
+    bit for bit; rows whose bound forces the bias split (8-bit zero points at the edge)."""
+    seed = 320 + d + n + r
+    wr, z, s, c, A, Bm = random_state(seed, d, n, r, w_bits)
+    if w_bits == 8:
+        z = z.copy()
+        z[::4] = 0
+    st = gpu_state(wr, z, s, c, w_bits)
+    g = ops.merge_mul_planes(st, cuda(A), cuda(Bm), w_bits, u_bits, 77, 5, dbg=True)
+    R = oracle.gen_r_rows(0, d, n, 77, 5, c)
+    ref = oracle.merge_mul(wr, z, s, R, A, Bm, u_bits)
+    lay, code = oracle.plane_store(ref["m"], z, ref["zbar"], w_bits, u_bits)
+    assert np.array_equal(host(g["code"]), code)
+    assert np.array_equal(host(g["planes"]), lay)
+    assert np.array_equal(host(g["uround"]), ref["uround"])
+    assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
+    assert np.array_equal(host(g["zbar"]), ref["zbar"])
+    assert int(host(g["sat"])[0]) == ref["sat"]
+    # the same integers as the int16 merge
+    g16 = ops.merge_mul(st, cuda(A), cuda(Bm), w_bits, u_bits, 77, 5)
+    assert np.array_equal(oracle.merged_from_planes(host(g["planes"]), host(g["code"])), host(g16["m"]))
+
+
+def test_flux_like_layer_planes_end_to_end(ops):
+    """A reduced FLUX-like layer (W4A8, U 4-bit, r = 32) through the byte-plane merge and
+    the linear layer: every row's plane code 0 here (|m| <= 127), so the layer runs the
+    low planes alone; Y bit for bit against the oracle and equal to the int16 path's."""
+    wl = synth.WORKLOADS[3]
+    d, n, M = 512, 1536, 600
+    W = synth.weight(wl, 0, d=d, n=n)
+    A, Bm = synth.lora(wl, 0, d=d, n=n)
+    X = synth.activations(wl, n, M, 0)
+    st = ops.setup_layer(cuda(W), 4, 0, 0, synth.ALPHA)
+    g = ops.merge_mul_planes(st, cuda(A), cuda(Bm), 4, 4, 0, 0)
+    g16 = ops.merge_mul(st, cuda(A), cuda(Bm), 4, 4, 0, 0)
+    xq, sx, rs = ops.quant_act(cuda(X))
+    Yp, _ = ops.linear(xq, sx, rs, ops.B.INTLORA_W_INT16_PLANES, g["planes"], g["sbar"], d, split=g["code"])
+    Y16, _ = ops.linear(xq, sx, rs, 16, g16["m"], g16["sbar"], d, split=g16["split"])
+    assert not bool(g["code"].any())
+    assert torch.equal(Yp, Y16)
+    ost = oracle.setup_layer(W, 0, 0, 4, synth.ALPHA)
+    ref = oracle.merge_mul(ost["wround"], ost["z"], ost["s"], ost["rstar"], A, Bm, 4)
+    oxq, osx, _ = oracle.quant_act(X)
+    _, _, oy = oracle.linear(oxq, osx, ref["m"].astype(np.int32), ref["sbar"])
+    assert np.array_equal(host(Yp).view(np.uint16), oy)
