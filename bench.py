@@ -13,7 +13,9 @@ term, rank 32, 4608 tokens.
 
 Printed (rank 0, one JSON line): value = 100 * T_roof / T_step, where T_roof is the
 step's time at MI355X peak (merge algorithmic bytes at 8 TB/s HBM plus the GEMM's
-executed int8 MFMA operations at 5.0 POP/s) and T_step the measured time of one step.
+products, each merged integer times each activation counted once as an int8
+multiply-add, at 5.0 POP/s) and T_step the measured time of one step.  T_roof is a
+constant of the workload, so value is inversely proportional to the step time.
 Per-layer merge GB/s and GEMM TOP/s are listed alongside.
 """
 from __future__ import annotations
@@ -64,6 +66,9 @@ def parse():
                    help="skip the step captured in a HIP graph and replayed (reported beside the eager step)")
     p.add_argument("--no-aux-laws", action="store_true",
                    help="skip the merge timed under the other auxiliary laws (Gaussian, Cauchy, Student-t(2))")
+    p.add_argument("--int16-layout", action="store_true",
+                   help="MUL: keep the merged integers as int16 (converted to byte planes inside the linear "
+                        "layer) instead of the byte-plane storage")
     p.add_argument("--kernel-runs", type=int, default=100,
                    help="runs per kernel for the per-kernel medians (merge warm, merge cold, linear layer)")
     p.add_argument("--flush-mib", type=int, default=1024,
@@ -102,9 +107,23 @@ def merge_alg_bytes(d, n, r, w_bits, mode):
     return code_in + out + 4.0 * d * r + 4.0 * r * n + 20.0 * d
 
 
-def gemm_exec_ops(M, d, n, mode):
-    passes = 2 if mode == "mul" else 1
+def gemm_exec_ops(M, d, n, mode, planes=None):
+    """int8 MFMA operations the linear layer executes: one pass per byte plane it
+    multiplies (MUL: two, or one when the byte-plane storage has every high plane zero)."""
+    passes = (2 if mode == "mul" else 1) if planes is None else planes
     return 2.0 * M * d * n * passes
+
+
+def merged_m(lay, torch):
+    """The merged integers of a layer's MUL output as int32 (from either storage)."""
+    o = lay["out"]
+    if "planes" not in o:
+        return o["m"].to(torch.int32)
+    d, n2 = o["planes"].shape
+    g = o["planes"].view(torch.int8).to(torch.int32).view(d, n2 // 32, 32)
+    hi = g[:, :, :16].reshape(d, n2 // 2)
+    lo = g[:, :, 16:].reshape(d, n2 // 2)
+    return 256 * hi + lo + 128 * ((o["code"].to(torch.int32) >> 1) & 1)[:, None]
 
 
 def traffic_from_profile(workload_name):
@@ -164,7 +183,7 @@ def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows
         w = unpack(lay["st"]["wround"][rows], L.n) - lay["st"]["z"][rows].to(torch.int64)[:, None]
         target = (lay["st"]["s"][rows].double()[:, None] * w.double() + R[rows].double()
                   + lay["Ag"][rows].double() @ lay["Bg"].double())
-        m = lay["out"]["m"][rows].double()
+        m = merged_m(lay, torch)[rows].double()
         intlora = lay["out"]["sbar"][rows].double()[:, None] * m
         code = unpack(outs[k]["code"][rows], L.n)
         ptqw = outs[k]["s"][rows].double()[:, None] * (code - outs[k]["z"][rows].to(torch.int64)[:, None]).double()
@@ -256,7 +275,8 @@ def fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits):
         us = sum(ev[s_][k][0].elapsed_time(ev[s_][k][1]) for s_ in range(args.steps)) / args.steps * 1e3
         tot += us
         per.append(dict(layer=lay["L"].name, fused_merge_us=round(us, 2),
-                        same_m_as_three_kernel_merge=bool(torch.equal(outs[k]["m"], lay["out"]["m"]))))
+                        same_m_as_three_kernel_merge=bool(torch.equal(outs[k]["m"].to(torch.int32),
+                                                                      merged_m(lay, torch)))))
     code_b = 0.5 if wl.w_bits == 4 else 1.0
     alg = sum(lay["L"].d * lay["L"].n * (code_b + 2.0) for lay in layers)  # base codes in, int16 m out
     return dict(us_per_step=round(tot, 1), alg_GBps=round(alg / (tot * 1e-6) / 1e9, 1),
@@ -406,6 +426,34 @@ def kernel_medians(args, layers, merge_fn, gemm_fn, torch, dev, stream):
     return out
 
 
+def int16_layout_medians(args, layers, ops, synth, wl, mbits, ws, torch, dev, stream):
+    """The linear layer on the same merged integers stored as int16 (the layer converts
+    them to byte planes after its LDS reads): median of `args.kernel_runs` runs per layer,
+    the outputs checked equal to the byte-plane path's."""
+    out = []
+    for lay in layers:
+        L = lay["L"]
+        g = ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws)
+        Y = torch.empty_like(lay["Y"])
+
+        def fn():
+            ops.linear(lay["xq"], lay["sx"], lay["rs"], 16, g["m"], g["sbar"], L.d, out=Y, split=g["split"])
+
+        for _ in range(10):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(max(1, args.kernel_runs))]
+        for e0, e1 in ev:
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, lay["Y"]), "int16 layout and byte planes disagree"
+        out.append(round(float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3, 2))
+        del g, Y
+    return out
+
+
 def profile_counters(workload_name):
     """Per-kernel counter figures from the committed rocprofv3 summary of this workload
     (profiles/<workload>_counters.json), if it was taken on the current kernel sources;
@@ -548,9 +596,17 @@ def main():
         layers.append(dict(L=L, li=li, lid=lid, W=W, A=A, B=Bm, X=X, st=st, Ag=torch.from_numpy(A).to(dev),
                            Bg=torch.from_numpy(Bm).to(dev), xq=xq, sx=sx, rs=rs))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    planes = mode == "mul" and not args.int16_layout and all(L.n % 16 == 0 for L in wl.layers)
     for lay in layers:
         L = lay["L"]
-        if mode == "mul":
+        if planes:
+            lay["out"] = dict(planes=torch.empty((L.d, 2 * L.n), dtype=torch.uint8, device=dev),
+                              sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
+                              zbar=torch.empty(L.d, dtype=torch.int32, device=dev),
+                              code=torch.empty(L.d, dtype=torch.uint8, device=dev),
+                              sat=torch.zeros(2, dtype=torch.int64, device=dev))
+            lay["wfmt"] = B.INTLORA_W_INT16_PLANES
+        elif mode == "mul":
             lay["out"] = dict(m=torch.empty((L.d, L.n), dtype=torch.int16, device=dev),
                               sbar=torch.empty(L.d, dtype=torch.float32, device=dev),
                               zbar=torch.empty(L.d, dtype=torch.int32, device=dev),
@@ -568,36 +624,38 @@ def main():
 
     stream = torch.cuda.current_stream()
 
-    def step(events=None):
-        for k, lay in enumerate(layers):
-            if events is not None:
-                events[k][0].record(stream)
-            if mode == "mul":
-                ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
-                              ws=ws, out=lay["out"])
-            else:
-                ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
-                                ws=ws, out=lay["out"])
-            if events is not None:
-                events[k][1].record(stream)
-            ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"], lay["L"].d,
-                       out=lay["Y"], split=lay["out"].get("split"))
-            if events is not None:
-                events[k][2].record(stream)
-
-    def merge_fn(k):
-        lay = layers[k]
-        if mode == "mul":
+    def run_merge(lay):
+        if planes:
+            ops.merge_mul_planes(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
+                                 ws=ws, out=lay["out"])
+        elif mode == "mul":
             ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws,
                           out=lay["out"])
         else:
             ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"], ws=ws,
                             out=lay["out"])
 
+    def run_gemm(lay):
+        o = lay["out"]
+        ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], o["planes"] if planes else o["m"], o["sbar"],
+                   lay["L"].d, out=lay["Y"], split=o.get("code") if planes else o.get("split"))
+
+    def step(events=None):
+        for k, lay in enumerate(layers):
+            if events is not None:
+                events[k][0].record(stream)
+            run_merge(lay)
+            if events is not None:
+                events[k][1].record(stream)
+            run_gemm(lay)
+            if events is not None:
+                events[k][2].record(stream)
+
+    def merge_fn(k):
+        run_merge(layers[k])
+
     def gemm_fn(k):
-        lay = layers[k]
-        ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"], lay["L"].d,
-                   out=lay["Y"], split=lay["out"].get("split"))
+        run_gemm(layers[k])
 
     for _ in range(args.warmup):
         step()
@@ -616,6 +674,9 @@ def main():
 
     # ---------------------------------------------------------------- per-kernel medians (untimed region)
     medians = kernel_medians(args, layers, merge_fn, gemm_fn, torch, dev, stream) if args.kernel_runs > 0 else None
+    int16_cmp = None
+    if planes and args.kernel_runs > 0:
+        int16_cmp = int16_layout_medians(args, layers, ops, synth, wl, mbits, ws, torch, dev, stream)
 
     # ---------------------------------------------------------------- pipelined step (optional)
     # The merges run on a side stream, each layer's linear layer waiting only for its own
@@ -630,16 +691,10 @@ def main():
         ms_stream.wait_stream(cur)
         for k, lay in enumerate(layers):
             with torch.cuda.stream(ms_stream):
-                if mode == "mul":
-                    ops.merge_mul(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, lay["lid"],
-                                  ws=ws, out=lay["out"])
-                else:
-                    ops.merge_shift(lay["st"], lay["Ag"], lay["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED,
-                                    lay["lid"], ws=ws, out=lay["out"])
+                run_merge(lay)
                 done_merge[k].record(ms_stream)
             cur.wait_event(done_merge[k])
-            ops.linear(lay["xq"], lay["sx"], lay["rs"], lay["wfmt"], lay["out"]["m"], lay["out"]["sbar"],
-                       lay["L"].d, out=lay["Y"], split=lay["out"].get("split"))
+            run_gemm(lay)
         cur.wait_stream(ms_stream)
 
     overlap_ms = None
@@ -700,18 +755,20 @@ def main():
     counters = profile_counters(wl.name)
     per_layer = []
     roof_ms = 0.0
-    merge_bytes_tot = merge_ms_tot = gemm_ops_tot = gemm_ms_tot = 0.0
+    merge_bytes_tot = merge_ms_tot = gemm_ops_tot = gemm_ms_tot = gemm_eops_tot = 0.0
     for k, lay in enumerate(layers):
         L = lay["L"]
         mms = float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)]))
         gms = float(np.mean([ev[s][k][1].elapsed_time(ev[s][k][2]) for s in range(args.steps)]))
         mb = merge_alg_bytes(L.d, L.n, wl.r, wl.w_bits, mode)
-        gops = gemm_exec_ops(M, L.d, L.n, mode)
+        nplanes = (1 if not bool(lay["out"]["code"].any()) else 2) if planes else None
+        gops = gemm_exec_ops(M, L.d, L.n, mode, nplanes)
         eops = 2.0 * M * L.d * L.n  # the method's int16 x int8 (or int8 x int8) products, once
-        roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + gops / (INT8_PEAK_TOPS * 1e12) * 1e3
+        roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + eops / (INT8_PEAK_TOPS * 1e12) * 1e3
         merge_bytes_tot += mb
         merge_ms_tot += mms
         gemm_ops_tot += gops
+        gemm_eops_tot += eops
         gemm_ms_tot += gms
         row = dict(layer=L.name, d=L.d, n=L.n, merge_us=round(mms * 1e3, 2),
                    merge_alg_GBps=round(mb / (mms * 1e-3) / 1e9, 1),
@@ -723,6 +780,15 @@ def main():
                    sat=int(lay["out"]["sat"][0].item()),
                    int16_split=("balanced" if not bool(lay["out"]["split"].any()) else "bias")
                    if "split" in lay["out"] else None)
+        if planes:
+            c = lay["out"]["code"]
+            row.update(storage="byte planes", gemm_planes_multiplied=nplanes,
+                       plane_code_rows={"0_high_plane_zero": int((c == 0).sum()), "1_balanced": int((c == 1).sum()),
+                                        "3_bias": int((c == 3).sum())})
+            if int16_cmp is not None:
+                row.update(gemm_int16_layout_us_median=int16_cmp[k],
+                           gemm_int16_layout_exec_TOPS=round(gemm_exec_ops(M, L.d, L.n, mode) /
+                                                             (int16_cmp[k] * 1e-6) / 1e12, 1))
         if medians is not None:
             md = medians[k]
             row.update(merge_warm_us_median=md["merge_warm_us"], merge_cold_us_median=md["merge_cold_us"],
@@ -739,8 +805,8 @@ def main():
     result = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": "% of MI355X peak (step time at 8 TB/s HBM for merge bytes + 5.0 POP/s int8 for GEMM ops, "
-                "over measured step time)",
+        "unit": "% of MI355X peak (step time at 8 TB/s HBM for the merge's algorithmic bytes + 5.0 POP/s int8 "
+                "for the GEMM's products counted once, over measured step time)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -752,8 +818,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": [f"{L.name} {L.d}x{L.n}" for L in wl.layers], "tokens": M,
                    "rank": wl.r, "w_bits": wl.w_bits, "mode": mode, "adapt_bits": mbits},
-        "roofline": {"bound": "mfma", "kernel": "k_linear (int8 MFMA, %s)" % ("int16 two-plane" if mode == "mul"
-                                                                            else "int%d" % wl.w_bits),
+        "roofline": {"bound": "mfma", "kernel": ("k_linear_planes (int8 MFMA on the byte-plane storage; planes "
+                                                 "multiplied per layer: %s)" % [r.get("gemm_planes_multiplied")
+                                                                                for r in per_layer]) if planes else
+                     "k_linear (int8 MFMA, %s)" % ("int16 two-plane" if mode == "mul" else "int%d" % wl.w_bits),
                      "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
                      "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profile(wl.name)},
         "merge": {"alg_GBps": round(merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9, 1),
@@ -761,11 +829,11 @@ def main():
                   "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (Philox, the Laplace ln and the division per element in the adaptation kernel)"},
         "gemm": {"exec_TOPS": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
                  "exec_frac_int8_peak": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-                 "effective_TOPS": round(gemm_ops_tot / (2 if mode == "mul" else 1) / (gemm_ms_tot * 1e-3) / 1e12, 1),
-                 "effective_frac_int8_peak": round(gemm_ops_tot / (2 if mode == "mul" else 1) /
-                                                   (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
-                 "exec_vs_effective": "exec counts the int8 MFMA operations run (two byte planes per int16 "
-                                      "merged integer for MUL); effective counts each int16 x int8 product once",
+                 "effective_TOPS": round(gemm_eops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
+                 "effective_frac_int8_peak": round(gemm_eops_tot / (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
+                 "exec_vs_effective": "exec counts the int8 MFMA operations run (MUL: two byte planes per merged "
+                                      "integer, or only the low plane when the merge certified every high byte "
+                                      "zero); effective counts each merged-integer x activation product once",
                  "us_per_step": round(gemm_ms_tot * 1e3, 1)},
         "kernel_timing": {"runs": args.kernel_runs, "statistic": "median",
                           "cold": "a %d MiB buffer written through HBM before each cold merge run" % args.flush_mib}

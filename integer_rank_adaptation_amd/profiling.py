@@ -151,9 +151,11 @@ def traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, workload, kernel):
 # The kernels of one step of the benchmark, in launch order per layer (the merge's three
 # kernels, then the linear layer).  Their launches cycle through the layers in order, so
 # launch k of a kernel belongs to layer k mod L.
-STEP_KERNELS = ("k_adapt_mfma", "k_adapt_generic", "k_row_range", "k_quant_mul", "k_quant_shift", "k_linear")
+STEP_KERNELS = ("k_adapt_mfma", "k_adapt_generic", "k_row_range", "k_mul_params", "k_quant_mul", "k_quant_shift",
+                "k_linear", "k_linear_planes")
 CLOCK_HZ = 2.4e9
 SIMDS = 256 * 4
+XCDS = 8
 
 
 def _by_layer(rows, layers, value):
@@ -222,14 +224,17 @@ def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, 
             for c, v in cv.items():
                 if c not in ("FETCH_SIZE", "WRITE_SIZE"):
                     rec[c] = v
-            if rec["us"] and cv.get("GRBM_GUI_ACTIVE"):
-                rec["clock_GHz"] = round(cv["GRBM_GUI_ACTIVE"] / (rec["us"] * 1e-6) / 1e9, 3)
+            # GRBM_GUI_ACTIVE comes summed over the XCDs: cycles of the kernel = value / XCDS.
+            # Below about 20 us the dispatch's own overhead dominates it, so no clock is derived.
+            cycles = cv["GRBM_GUI_ACTIVE"] / XCDS if cv.get("GRBM_GUI_ACTIVE") else None
+            if rec["us"] and cycles and rec["us"] >= 20:
+                rec["clock_GHz"] = round(cycles / (rec["us"] * 1e-6) / 1e9, 3)
             if rec["us"] and cv.get("SQ_INSTS_VALU"):
                 rec["valu_frac_of_peak"] = round(cv["SQ_INSTS_VALU"] * 4 / (rec["us"] * 1e-6 * CLOCK_HZ * SIMDS), 4)
-                if cv.get("GRBM_GUI_ACTIVE"):
-                    rec["valu_frac_at_clock"] = round(cv["SQ_INSTS_VALU"] * 4 / (cv["GRBM_GUI_ACTIVE"] * SIMDS), 4)
-            if cv.get("SQ_VALU_MFMA_BUSY_CYCLES") and cv.get("GRBM_GUI_ACTIVE"):
-                rec["mfma_busy_frac"] = round(cv["SQ_VALU_MFMA_BUSY_CYCLES"] / (cv["GRBM_GUI_ACTIVE"] * SIMDS), 4)
+                if cycles:
+                    rec["valu_frac_at_clock"] = round(cv["SQ_INSTS_VALU"] * 4 / (cycles * SIMDS), 4)
+            if cv.get("SQ_VALU_MFMA_BUSY_CYCLES") and cycles:
+                rec["mfma_busy_frac"] = round(cv["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * SIMDS), 4)
             per_layer[L][kname] = rec
     out = dict(workload=workload, library_source_sha=library_source_sha(), command=commands,
                calibration=dict(copy_bytes=copy_bytes, copy_fetch_kib=fk, copy_write_kib=wk,
@@ -259,6 +264,42 @@ def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, 
                             source="rocprofv3 SQ_INSTS_VALU (wave64 instructions) x 64 lanes over kernel-trace "
                                    "time; peak 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz")
     return out
+
+
+def counters_md(rec):
+    """Markdown summary of a per-kernel counter record (the output of `counters`)."""
+    cal = rec["calibration"]
+    lines = ["Commands (from the repository root, on one MI355X):", ""]
+    lines += ["    " + c for c in rec.get("command", [])]
+    lines += ["", f"Workload `{rec['workload']}`; library source hash `{rec['library_source_sha']}`.",
+              f"HBM bytes = FETCH_SIZE x {cal['fetch_scale']} + WRITE_SIZE x {cal['write_scale']} (KiB x 1024), "
+              f"calibrated on a {cal['copy_bytes']} byte device copy.",
+              "GRBM_GUI_ACTIVE is summed over the 8 XCDs (clock = value / 8 / duration, not derived under 20 us); VALU fraction of peak = "
+              "SQ_INSTS_VALU x 64 lanes / duration / 39.32 T lane-instructions/s; MfmaUtil and VALUBusy are "
+              "rocprofv3's derived percentages.", "",
+              "| layer | kernel | us (trace) | HBM MB | counter GB/s | % of 8 TB/s | VALU insts / elem | "
+              "VALU % of peak | VALUBusy % | MfmaUtil % | clock GHz |",
+              "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for L, ks in rec["per_layer"].items():
+        for k, r in ks.items():
+            hb = r.get("hbm_bytes")
+            clk = r.get("clock_GHz")
+            epe = r.get("valu_per_elem")
+            lines.append("| %s | `%s` | %s | %s | %s | %s | %s | %s | %s | %s | %s |" % (
+                L, k, f"{r['us']:.1f}" if r.get("us") else "-", f"{hb / 1e6:.1f}" if hb else "-",
+                f"{r['counter_GBps']:.0f}" if r.get("counter_GBps") else "-",
+                f"{r['counter_pct_hbm_peak']:.1f}" if r.get("counter_pct_hbm_peak") else "-",
+                f"{epe:.1f}" if epe else "-",
+                f"{100 * r['valu_frac_of_peak']:.1f}" if r.get("valu_frac_of_peak") else "-",
+                f"{r['VALUBusy']:.1f}" if r.get("VALUBusy") is not None else "-",
+                f"{r['MfmaUtil']:.1f}" if r.get("MfmaUtil") is not None else "-",
+                f"{clk:.2f}" if clk else "-"))
+    for key in ("roofline_merge", "roofline_adapt"):
+        if key in rec:
+            r = rec[key]
+            lines += ["", f"`{key}`: {r['kernel']} -- {r['achieved']} {r['unit']} of {r['peak']} "
+                      f"(frac {r['frac']}); {r['source']}."]
+    return "\n".join(lines) + "\n"
 
 
 def traffic_md(rec, commands):
@@ -300,16 +341,26 @@ def main(argv=None):
     c.add_argument("--copy-bytes", type=int, required=True)
     c.add_argument("--workload", required=True)
     c.add_argument("--layers", required=True, help="comma-separated layer names in step order")
+    c.add_argument("--elems", default="", help="comma-separated weights per layer (VALU instructions per weight)")
     c.add_argument("--json-out", default="")
+    c.add_argument("--md-out", default="")
     c.add_argument("--commands", nargs="*", default=[])
     a = p.parse_args(argv)
     if a.cmd == "counters":
-        rec = counters(a.trace, a.pmc, a.copy_fetch, a.copy_write, a.copy_bytes, a.workload, a.layers.split(","),
-                       a.commands)
+        layers = a.layers.split(",")
+        rec = counters(a.trace, a.pmc, a.copy_fetch, a.copy_write, a.copy_bytes, a.workload, layers, a.commands)
+        if a.elems:
+            for L, e in zip(layers, [float(x) for x in a.elems.split(",")]):
+                for r in rec["per_layer"][L].values():
+                    if r.get("SQ_INSTS_VALU"):
+                        r["valu_per_elem"] = round(r["SQ_INSTS_VALU"] * 64 / e, 2)
         text = json.dumps(rec, indent=1)
         if a.json_out:
             with open(a.json_out, "w") as fh:
                 fh.write(text + "\n")
+        if a.md_out:
+            with open(a.md_out, "w") as fh:
+                fh.write(counters_md(rec))
         print(text)
         return
     if a.cmd == "stats":
