@@ -126,21 +126,23 @@ def merged_m(lay, torch):
     return 256 * hi + lo + 128 * ((o["code"].to(torch.int32) >> 1) & 1)[:, None]
 
 
-def traffic_from_profile(workload_name):
-    """HBM bytes per GEMM launch from the committed counter summary, if it was taken
-    on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", workload_name + "_traffic.json")
+def traffic_from_profile(workload_name, kernel_prefix):
+    """HBM bytes per launch of the dominant kernel (mean over the step's layers) from the
+    committed counter summary, if it was taken on the current library source; else None."""
+    path = os.path.join(ROOT, "profiles", workload_name + "_counters.json")
     if not os.path.exists(path):
         return None
     try:
         rec = json.load(open(path))
     except Exception:
         return None
-    from integer_rank_adaptation_amd.profiling import kernel_source_sha
+    from integer_rank_adaptation_amd.profiling import library_source_sha
 
-    if rec.get("kernel_source_sha") != kernel_source_sha() or rec.get("workload") != workload_name:
+    if rec.get("library_source_sha") != library_source_sha() or rec.get("workload") != workload_name:
         return None
-    return rec.get("hbm_bytes_per_launch")
+    vals = [r["hbm_bytes"] for ks in rec["per_layer"].values() for k, r in ks.items()
+            if k.startswith(kernel_prefix) and r.get("hbm_bytes")]
+    return round(sum(vals) / len(vals)) if vals else None
 
 
 def ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream, rows_per_layer=64):
@@ -823,7 +825,7 @@ def main():
                                                                                 for r in per_layer]) if planes else
                      "k_linear (int8 MFMA, %s)" % ("int16 two-plane" if mode == "mul" else "int%d" % wl.w_bits),
                      "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profile(wl.name)},
+                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profile(wl.name, "k_linear_planes" if planes else "k_linear")},
         "merge": {"alg_GBps": round(merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9, 1),
                   "pct_hbm_peak": round(100 * merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                   "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (Philox, the Laplace ln and the division per element in the adaptation kernel)"},
