@@ -77,6 +77,12 @@ def parse():
                    help="skip the merge-only sweep over the 32 transformer blocks x 7 matrices of the "
                         "Llama-3-8B-shaped workload")
     p.add_argument("--sweep-blocks", type=int, default=32, help="transformer blocks in the merge-only sweep")
+    p.add_argument("--no-library-gemm", action="store_true",
+                   help="skip the context timing of the vendor library's int8 GEMM (torch._int_mm) on the same "
+                        "int8 operands")
+    p.add_argument("--mode-index", type=int, default=0,
+                   help="which of the workload's merge modes to time (the SD-v1.5 640-channel set has MUL "
+                        "then SHIFT)")
     p.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB (counter calibration) and exit")
     return p.parse_args()
@@ -456,6 +462,44 @@ def int16_layout_medians(args, layers, ops, synth, wl, mbits, ws, torch, dev, st
     return out
 
 
+def library_gemm_medians(args, layers, mode, w_bits, planes, torch, stream):
+    """For context: the vendor library's int8 GEMM (torch._int_mm: int32 accumulators, no
+    epilogue, no bf16 output) on the same activations and merged integers, where those
+    are int8 (MUL with every high byte zero, or SHIFT at 8 bits).  Median of
+    `args.kernel_runs` runs per layer; None for layers it cannot take."""
+    out = []
+    for lay in layers:
+        L = lay["L"]
+        o = lay["out"]
+        w8 = None
+        if mode == "mul" and planes and not bool(o["code"].any()):
+            w8 = o["planes"].view(L.d, L.n // 16, 2, 16)[:, :, 1, :].reshape(L.d, L.n).view(torch.int8)
+        elif mode == "shift" and w_bits == 8:
+            w8 = o["m"].view(torch.int8).view(L.d, L.n)
+        if w8 is None or lay["xq"].shape[0] <= 16:
+            out.append(None)
+            continue
+        wt = w8.t()
+
+        def fn():
+            return torch._int_mm(lay["xq"], wt)
+
+        try:
+            for _ in range(10):
+                fn()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(max(1, args.kernel_runs))]
+            for e0, e1 in ev:  # torch's current stream, as every other timing here
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(round(float(np.median([e0.elapsed_time(e1) for e0, e1 in ev])) * 1e3, 2))
+        except RuntimeError:
+            out.append(None)
+    return out
+
+
 def profile_counters(workload_name):
     """Per-kernel counter figures from the committed rocprofv3 summary of this workload
     (profiles/<workload>_counters.json), if it was taken on the current kernel sources;
@@ -578,7 +622,9 @@ def main():
     torch.cuda.set_device(dev)
     wl = synth.WORKLOADS[args.workload]
     M = args.tokens or wl.tokens[0]
-    mode, mbits = wl.modes[0]
+    if not 0 <= args.mode_index < len(wl.modes):
+        sys.exit("workload %d has %d merge mode(s)" % (args.workload, len(wl.modes)))
+    mode, mbits = wl.modes[args.mode_index]
 
     # ---------------------------------------------------------------- inputs (untimed)
     t_setup = time.time()
@@ -679,6 +725,9 @@ def main():
     int16_cmp = None
     if planes and args.kernel_runs > 0:
         int16_cmp = int16_layout_medians(args, layers, ops, synth, wl, mbits, ws, torch, dev, stream)
+    lib_cmp = None
+    if args.kernel_runs > 0 and not args.no_library_gemm:
+        lib_cmp = library_gemm_medians(args, layers, mode, wl.w_bits, planes, torch, stream)
 
     # ---------------------------------------------------------------- pipelined step (optional)
     # The merges run on a side stream, each layer's linear layer waiting only for its own
@@ -791,6 +840,9 @@ def main():
                 row.update(gemm_int16_layout_us_median=int16_cmp[k],
                            gemm_int16_layout_exec_TOPS=round(gemm_exec_ops(M, L.d, L.n, mode) /
                                                              (int16_cmp[k] * 1e-6) / 1e12, 1))
+        if lib_cmp is not None and lib_cmp[k] is not None:
+            row.update(library_int8_gemm_us_median=lib_cmp[k],
+                       library_int8_gemm_TOPS=round(2.0 * M * L.d * L.n / (lib_cmp[k] * 1e-6) / 1e12, 1))
         if medians is not None:
             md = medians[k]
             row.update(merge_warm_us_median=md["merge_warm_us"], merge_cold_us_median=md["merge_cold_us"],
@@ -836,7 +888,13 @@ def main():
                  "exec_vs_effective": "exec counts the int8 MFMA operations run (MUL: two byte planes per merged "
                                       "integer, or only the low plane when the merge certified every high byte "
                                       "zero); effective counts each merged-integer x activation product once",
-                 "us_per_step": round(gemm_ms_tot * 1e3, 1)},
+                 "us_per_step": round(gemm_ms_tot * 1e3, 1),
+                 "library_int8_gemm_us_sum": round(sum(lib_cmp), 1)
+                 if lib_cmp is not None and all(v is not None for v in lib_cmp) else None,
+                 "library_int8_gemm_note": "context only: torch._int_mm (the vendor library's int8 GEMM, int32 "
+                                           "accumulators, no dequant epilogue or bf16 output) on the same int8 "
+                                           "operands, sum of per-layer medians; compare with the sum of "
+                                           "per_layer[].gemm_us_median"},
         "kernel_timing": {"runs": args.kernel_runs, "statistic": "median",
                           "cold": "a %d MiB buffer written through HBM before each cold merge run" % args.flush_mib}
         if medians is not None else None,

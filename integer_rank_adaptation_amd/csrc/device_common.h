@@ -75,12 +75,13 @@ struct LnEntry {  // as stored (generated table)
   float r;
 };
 
-struct LnLds {  // as used, in LDS: every field binary64, r pre-scaled by 2^-24 (exact)
-  double hi, lo, r24;
+struct __attribute__((aligned(16))) LnLds {  // as used, in LDS: 16 bytes, one ds_read_b128;
+  double hi;                                 // r pre-scaled by 2^-24 (exact in binary32)
+  float lo, r24;
 };
 
 __device__ __forceinline__ LnLds ln_lds_entry(const LnEntry& e) {
-  return LnLds{e.neg_ln_r_hi, (double)e.neg_ln_r_lo, (double)e.r * 0x1p-24};
+  return LnLds{e.neg_ln_r_hi, e.neg_ln_r_lo, e.r * 0x1p-24f};
 }
 
 // The integer part of the logarithm below: g = (F 2^-24) 2^e with F 2^-24 in
@@ -113,7 +114,7 @@ __device__ __forceinline__ LnPrep ln_prep(uint32_t G, int bias) {
 __device__ __forceinline__ double ln_finish(const LnPrep& P, const LnLds& t) {
   const uint32_t F = P.F;
   const int e = P.e;
-  const double f = fma((double)F, t.r24, -1.0);  // m r_k - 1, exact
+  const double f = fma((double)F, (double)t.r24, -1.0);  // m r_k - 1, exact
   // log1p(f) = f - f^2/2 + ... - f^8/8 truncated after f^7: |f| <= 2^-7 leaves a
   // relative error below 2^-52, far under the 2^-47.6 the rounding needs.
   double p7 = 1.0 / 7.0;
@@ -128,7 +129,7 @@ __device__ __forceinline__ double ln_finish(const LnPrep& P, const LnLds& t) {
   const double LN2_LO = 0x1.ef35793c76730p-45;
   const double ed = (double)e;
   const double head = fma(ed, LN2_HI, t.hi);
-  const double tail = fma(ed, LN2_LO, t.lo);
+  const double tail = fma(ed, LN2_LO, (double)t.lo);
   return head + (lp + tail);
 }
 

@@ -794,10 +794,14 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear(int64_t M, int64_t 
                         zw_p);
 }
 
-// Byte-plane merged integers: when every row's plane code is 0 (all high bytes zero) the
-// launch multiplies the low planes alone as int8 weights (256 outputs per tile, the
-// high planes never loaded); otherwise both planes, with the bias correction on the rows
-// whose code says so.  Every block reads the codes and votes before its first load.
+// Byte-plane merged integers: when every row's plane code is 0 (all high bytes zero) and
+// the host allows it, the launch multiplies the low planes alone as int8 weights (256
+// outputs per tile, the high planes never loaded); otherwise both planes, with the bias
+// correction on the rows whose code says so.  Every block reads the codes and votes
+// before its first load.  Both bodies give the same integers and outputs; the host
+// allows the low-plane body only where its fewer, wider tiles take fewer rounds of the
+// persistent grid (with equal rounds the two-plane tiles are as fast or faster: half of
+// their products multiply the zero high plane).
 template <bool KTAIL>
 __global__ __launch_bounds__(lin::kThreads, 1) void k_linear_planes(int64_t M, int64_t d, int64_t n,
                                                                    const int8_t* __restrict__ xq,
@@ -807,7 +811,8 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear_planes(int64_t M, i
                                                                    const uint8_t* __restrict__ code,
                                                                    const float* __restrict__ sbar,
                                                                    uint16_t* __restrict__ Y,
-                                                                   int32_t* __restrict__ acc_dbg, int tiles_m) {
+                                                                   int32_t* __restrict__ acc_dbg, int tiles_m,
+                                                                   int allow_narrow) {
   using namespace lin;
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   __shared__ int vote[4];
@@ -825,7 +830,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear_planes(int64_t M, i
   __syncthreads();
   if (__builtin_amdgcn_ballot_w64(fl != 0) != 0 && (tid & 63) == 0) vote[tid >> 6] = 1;
   __syncthreads();
-  const bool narrow = (vote[0] | vote[1] | vote[2] | vote[3]) == 0;
+  const bool narrow = allow_narrow && (vote[0] | vote[1] | vote[2] | vote[3]) == 0;
   if (narrow)
     linear_body<F_P16N, KTAIL>(lds, M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, tiles_m,
                                (int)((d + Cfg<F_P16N>::OUT - 1) / Cfg<F_P16N>::OUT), 0, nullptr, nullptr);
@@ -1179,15 +1184,18 @@ static hipError_t launch_planes(int64_t M, int64_t d, int64_t n, const int8_t* x
   }
   const int tiles_m = (int)((M + BM - 1) / BM);
   const int ntile = tiles_m * (int)((d + Cfg<F_P16T>::OUT - 1) / Cfg<F_P16T>::OUT);
+  const int ntile_n = tiles_m * (int)((d + Cfg<F_P16N>::OUT - 1) / Cfg<F_P16N>::OUT);
   const int KT = (int)((n + BK - 1) / BK);
   const int cus = device_cus();
   const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
+  const int g = (int)grid.x;
+  const int allow_narrow = (ntile_n + g - 1) / g < (ntile + g - 1) / g ? 1 : 0;  // rounds of each body
   if ((n % BK) != 0)
     hipLaunchKernelGGL((k_linear_planes<true>), grid, dim3(kThreads), Cfg<F_P16T>::LDS, st, M, d, n, xq, sx, rowsum,
-                       mb, code, sbar, Y, acc_dbg, tiles_m);
+                       mb, code, sbar, Y, acc_dbg, tiles_m, allow_narrow);
   else
     hipLaunchKernelGGL((k_linear_planes<false>), grid, dim3(kThreads), Cfg<F_P16T>::LDS, st, M, d, n, xq, sx, rowsum,
-                       mb, code, sbar, Y, acc_dbg, tiles_m);
+                       mb, code, sbar, Y, acc_dbg, tiles_m, allow_narrow);
   return hipGetLastError();
 }
 

@@ -56,8 +56,14 @@ def check_layer(ops, wl, li, L, Ms, mode, mbits, block=0, n_rows=6, n_tok=6):
     assert np.array_equal(gwr[rows], wr)
     assert np.array_equal(host(st["z"])[rows], z)
     assert np.array_equal(bits(host(st["s"])[rows]), bits(s))
+    gp = None
     if mode == "mul":
         ref = oracle.merge_mul(wr, z, s, R, A[rows], Bm, mbits)
+        if L.n % 16 == 0:  # the byte-plane storage the benchmark's step uses
+            gp = ops.merge_mul_planes(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid)
+            lay, code = oracle.plane_store(ref["m"], z, ref["zbar"], wl.w_bits, mbits)
+            assert np.array_equal(host(gp["code"])[rows], code)
+            assert np.array_equal(host(gp["planes"])[rows], lay)
         m_all = host(g["m"])
         assert np.array_equal(host(g["uround"])[rows], ref["uround"])
         assert np.array_equal(host(g["zbar"])[rows], ref["zbar"])
@@ -81,6 +87,10 @@ def check_layer(ops, wl, li, L, Ms, mode, mbits, block=0, n_rows=6, n_tok=6):
         if mode == "mul":  # the bias split on every row gives the same outputs
             Yb, _ = ops.linear(xq, sx, rs, wfmt, g["m"], g["sbar"], L.d)
             assert torch.equal(Y, Yb), (wl.name, L.name, M)
+        if gp is not None:  # and so do the byte planes
+            Yp, _ = ops.linear(xq, sx, rs, ops.B.INTLORA_W_INT16_PLANES, gp["planes"], gp["sbar"], L.d,
+                               split=gp["code"])
+            assert torch.equal(Y, Yp), (wl.name, L.name, M)
         toks = sample_rows(M, n_tok, 11 * li + M)
         oxq, osx, _ = oracle.quant_act(X[toks])
         assert np.array_equal(host(xq)[toks], oxq)
@@ -231,7 +241,8 @@ def test_merge_fused_full_size(ops, wl_index, li):
 def check_layer_full(ops, wl, li, M):
     """Every output of one layer at its full size against the oracle run on the whole
     layer: set-up (c, W_round, z, s), the MUL merge (m, U_round, s_bar, z_bar, split
-    codes, saturations) and the linear layer's bf16 outputs for all M tokens."""
+    codes, saturations; and the byte-plane storage with its plane codes) and the linear
+    layer's bf16 outputs for all M tokens, from the int16 and the byte-plane storage."""
     L = wl.layers[li]
     lid = synth.layer_id(wl.index, li)
     W = synth.weight(wl, li)
@@ -243,8 +254,10 @@ def check_layer_full(ops, wl, li, M):
     print(f"full-output check: {wl.name} {L.name} {L.d}x{L.n} M={M}", flush=True)
     st = ops.setup_layer(cuda(W), wl.w_bits, seed, lid, synth.ALPHA)
     g = ops.merge_mul(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid, dbg=True)
+    gp = ops.merge_mul_planes(st, cuda(A), cuda(Bm), wl.w_bits, mbits, seed, lid)
     xq, sx, rs = ops.quant_act(cuda(X))
     Y, _ = ops.linear(xq, sx, rs, 16, g["m"], g["sbar"], L.d, split=g["split"])
+    Yp, _ = ops.linear(xq, sx, rs, ops.B.INTLORA_W_INT16_PLANES, gp["planes"], gp["sbar"], L.d, split=gp["code"])
     ost = oracle.setup_layer(W, seed, lid, wl.w_bits, synth.ALPHA)
     gwr = host(st["wround"])
     gwr = unpack4(gwr) if wl.w_bits == 4 else gwr
@@ -253,7 +266,11 @@ def check_layer_full(ops, wl, li, M):
     assert np.array_equal(host(st["z"]), ost["z"])
     assert np.array_equal(bits(host(st["s"])), bits(ost["s"]))
     ref = oracle.merge_mul(ost["wround"], ost["z"], ost["s"], ost["rstar"], A, Bm, mbits)
+    lay, code = oracle.plane_store(ref["m"], ost["z"], ref["zbar"], wl.w_bits, mbits)
     del ost
+    assert np.array_equal(host(gp["planes"]), lay)
+    assert np.array_equal(host(gp["code"]), code)
+    del lay
     assert np.array_equal(host(g["m"]), ref["m"])
     assert np.array_equal(host(g["uround"]), ref["uround"])
     assert np.array_equal(bits(host(g["sbar"])), bits(ref["sbar"]))
@@ -265,7 +282,8 @@ def check_layer_full(ops, wl, li, M):
     assert np.array_equal(bits(host(sx)), bits(osx))
     _, _, oy = oracle.linear(oxq, osx, ref["m"].astype(np.int32), ref["sbar"], want_exact=False)
     assert np.array_equal(host(Y).view(np.uint16), oy), (wl.name, L.name, M)
-    del g, st, Y, xq
+    assert np.array_equal(host(Yp).view(np.uint16), oy), (wl.name, L.name, M, "planes")
+    del g, gp, st, Y, Yp, xq
     torch.cuda.empty_cache()
 
 

@@ -938,18 +938,20 @@ def _planes_linear_check(ops, M, m, z, zbar, w_bits, u_bits, seed, expect_narrow
     g = lay.view(np.int8).astype(np.int64).reshape(d, n // 16, 32)
     hi, lo = g[:, :, :16].reshape(d, n), g[:, :, 16:].reshape(d, n)
     acc = host(acc)
-    assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T)
-    assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T)
+    # every partial sum is an integer below 127 * 255 * n < 2^53: exact in binary64
+    assert np.array_equal(acc[0], (xq.astype(np.float64) @ hi.T.astype(np.float64)).astype(np.int64))
+    assert np.array_equal(acc[1], (xq.astype(np.float64) @ lo.T.astype(np.float64)).astype(np.int64))
     assert np.array_equal(host(Y).view(np.uint16), yref)
 
 
 @pytest.mark.parametrize("M,d,n", [(1, 7, 32), (16, 300, 4128), (32, 1000, 1024), (37, 100, 96), (300, 260, 512),
-                                   (2600, 4000, 224), (1100, 700, 3104)])
+                                   (2600, 4000, 224), (1100, 700, 3104), (4352, 4096, 160)])
 def test_linear_planes_bitexact(ops, M, d, n):
-    """The INT16_PLANES format: narrow calls (every plane code 0: the low planes alone, as
-    int8 weights with 256 outputs per tile), balanced two-plane calls, and calls with
-    bias-split rows; few tokens, ragged tiles, partial last K stages, several tiles per
-    block."""
+    """The INT16_PLANES format: narrow calls (every plane code 0), balanced two-plane calls,
+    and calls with bias-split rows; few tokens, ragged tiles, partial last K stages,
+    several tiles per block.  A narrow call runs the low planes alone (int8 weights, 256
+    outputs per tile) where that takes fewer rounds of the persistent grid: (2600, 4000)
+    and (4352, 4096, two tiles per block) do, the smaller shapes run both planes."""
     rng = np.random.Generator(np.random.PCG64(M + d + n))
     # narrow: |m| <= 127 with 4-bit codes and mid-range zero points (bound 8 * 8 = 64)
     mn = rng.integers(-64, 65, size=(d, n))
