@@ -77,6 +77,9 @@ def parse():
                    help="skip the merge-only sweep over the 32 transformer blocks x 7 matrices of the "
                         "Llama-3-8B-shaped workload")
     p.add_argument("--sweep-blocks", type=int, default=32, help="transformer blocks in the merge-only sweep")
+    p.add_argument("--no-grouped", action="store_true",
+                   help="Llama-3-8B-shaped block: skip the step with q/k/v and gate/up each run as one linear-layer "
+                        "call over their concatenated rows")
     p.add_argument("--no-library-gemm", action="store_true",
                    help="skip the context timing of the vendor library's int8 GEMM (torch._int_mm) on the same "
                         "int8 operands")
@@ -518,6 +521,89 @@ def profile_counters(workload_name):
     return rec
 
 
+# Llama-3-8B-shaped block: the projections that read the same activations
+SHARED_INPUT_GROUPS = {4: (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))}
+
+
+def grouped_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits, ws):
+    """The projections of a block that read the same activations (q, k, v; gate, up) as
+    one linear-layer call each: every matrix is merged on its own (MUL, byte planes) into
+    its row slice of the group's buffers, and the group's linear layer runs once over the
+    concatenated rows with the first member's activations.  Timed like the step (events
+    around every merge and every group call); each group's outputs are checked equal to
+    the per-matrix calls on the same activations."""
+    by_name = {lay["L"].name: lay for lay in layers}
+    groups = []
+    for names in SHARED_INPUT_GROUPS[wl.index]:
+        mem = [by_name[nm] for nm in names]
+        n = mem[0]["L"].n
+        D = sum(l["L"].d for l in mem)
+        buf = dict(planes=torch.empty((D, 2 * n), dtype=torch.uint8, device=dev),
+                   sbar=torch.empty(D, dtype=torch.float32, device=dev),
+                   zbar=torch.empty(D, dtype=torch.int32, device=dev),
+                   code=torch.empty(D, dtype=torch.uint8, device=dev))
+        outs, r0 = [], 0
+        for l in mem:
+            d = l["L"].d
+            outs.append(dict(planes=buf["planes"][r0:r0 + d], sbar=buf["sbar"][r0:r0 + d],
+                             zbar=buf["zbar"][r0:r0 + d], code=buf["code"][r0:r0 + d],
+                             sat=torch.zeros(2, dtype=torch.int64, device=dev)))
+            r0 += d
+        Y = torch.empty((mem[0]["xq"].shape[0], D), dtype=torch.int16, device=dev)
+        groups.append(dict(mem=mem, buf=buf, outs=outs, D=D, Y=Y, lay0=mem[0]))
+
+    def run(events=None):
+        for gi, g in enumerate(groups):
+            if events is not None:
+                events[gi][0].record(stream)
+            for l, o in zip(g["mem"], g["outs"]):
+                ops.merge_mul_planes(l["st"], l["Ag"], l["Bg"], wl.w_bits, mbits, synth.PHILOX_SEED, l["lid"],
+                                     ws=ws, out=o)
+            if events is not None:
+                events[gi][1].record(stream)
+            x = g["lay0"]
+            ops.linear(x["xq"], x["sx"], x["rs"], ops.B.INTLORA_W_INT16_PLANES, g["buf"]["planes"], g["buf"]["sbar"],
+                       g["D"], out=g["Y"], split=g["buf"]["code"])
+            if events is not None:
+                events[gi][2].record(stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    same = True
+    for g in groups:  # per-matrix calls on the group's activations give the same outputs
+        x = g["lay0"]
+        r0 = 0
+        for l, o in zip(g["mem"], g["outs"]):
+            d = l["L"].d
+            Yk = torch.empty((x["xq"].shape[0], d), dtype=torch.int16, device=dev)
+            ops.linear(x["xq"], x["sx"], x["rs"], ops.B.INTLORA_W_INT16_PLANES, o["planes"], o["sbar"], d, out=Yk,
+                       split=o["code"])
+            same = same and bool(torch.equal(Yk, g["Y"][:, r0:r0 + d]))
+            r0 += d
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in groups] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for s in range(args.steps):
+        run(ev[s])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    per_group = []
+    for gi, g in enumerate(groups):
+        mus = float(np.mean([ev[s][gi][0].elapsed_time(ev[s][gi][1]) for s in range(args.steps)])) * 1e3
+        gus = float(np.mean([ev[s][gi][1].elapsed_time(ev[s][gi][2]) for s in range(args.steps)])) * 1e3
+        nbytes = sum(l["L"].d * l["L"].n * (2 if bool(o["code"].any()) else 1) for l, o in zip(g["mem"], g["outs"]))
+        per_group.append(dict(matrices=[l["L"].name for l in g["mem"]], rows=g["D"], merge_us=round(mus, 2),
+                              gemm_us=round(gus, 2), gemm_weight_bytes=nbytes,
+                              gemm_weight_GBps=round(nbytes / (gus * 1e-6) / 1e9, 1)))
+    return dict(ms_per_step=round(t0.elapsed_time(t1) / args.steps, 4), outputs_equal_per_matrix_calls=same,
+                gemm_us_per_step=round(sum(p["gemm_us"] for p in per_group), 1), per_group=per_group,
+                note="projections reading the same activations merged into row slices of one buffer and run as "
+                     "one linear-layer call; activations of the group's first matrix")
+
+
 def sweep_measure(args, ops, B, synth, torch, dev, stream):
     """The merge-only sweep of the Llama-3-8B-shaped workload: the MUL merge (U 8-bit,
     r = 64) of every matrix of `args.sweep_blocks` transformer blocks (7 matrices each,
@@ -802,6 +888,10 @@ def main():
     if not args.no_sweep and M > 32:
         sweep = sweep_measure(args, ops, B, synth, torch, dev, stream)
 
+    grouped = None
+    if planes and wl.index in SHARED_INPUT_GROUPS and not args.no_grouped:
+        grouped = grouped_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits, ws)
+
     # ---------------------------------------------------------------- per-layer figures
     counters = profile_counters(wl.name)
     per_layer = []
@@ -910,6 +1000,7 @@ def main():
         "ste_backward": ste,
         "aux_laws": aux_laws,
         "sweep": sweep,
+        "grouped_shared_inputs": grouped,
         "setup_s": round(setup_s, 1),
     }
     if counters is not None:

@@ -245,20 +245,51 @@ ORA_API void ora_gen_r_rows(int64_t row0, int64_t rows, int64_t n, uint64_t seed
 /* original weight (per output channel), in binary64, rounded to binary32.     */
 /* c_i = RN32((sigma_W,i / sigma_R)^alpha) with sigma_R = sqrt(2), the         */
 /* standard deviation of the unit Laplace distribution.                        */
+/*                                                                             */
+/* Reading: the pages fix no summation order, and binary64 sums of a row's     */
+/* binary32 values are not exact in general, so the order is part of the      */
+/* definition here.  Each of the two row sums (the values, for the mean; the   */
+/* squared deviations e*e, e = x - mean, for the variance) is formed as        */
+/*   (1) 256 partial sums: partial t adds x_j for j = t, t + 256, t + 512, ... */
+/*       in increasing j, starting from 0;                                      */
+/*   (2) in each group of 64 consecutive partials, a halving tree: entry k     */
+/*       becomes entry k plus entry k + h, for h = 32, 16, 8, 4, 2, 1;          */
+/*   (3) the four group results added in order: ((g0 + g1) + g2) + g3.         */
+/* mean = sum / n; sigma = RN32(sqrt(sum of squares / n)).                     */
 /* ------------------------------------------------------------------------- */
+static double ordered_row_sum(const double* v, int64_t n) {
+    double part[256];
+    for (int t = 0; t < 256; ++t) {
+        double a = 0.0;
+        for (int64_t j = t; j < n; j += 256) a += v[j];
+        part[t] = a;
+    }
+    double g[4];
+    for (int w = 0; w < 4; ++w) {
+        double* p = part + 64 * w;
+        for (int h = 32; h >= 1; h >>= 1)
+            for (int k = 0; k < h; ++k) p[k] = p[k] + p[k + h];
+        g[w] = p[0];
+    }
+    return ((g[0] + g[1]) + g[2]) + g[3];
+}
+
 ORA_API void ora_sigma_w(int64_t d, int64_t n, const float* W, float* sigma_out) {
-#pragma omp parallel for schedule(static)
-    for (int64_t i = 0; i < d; ++i) {
-        const float* row = W + i * n;
-        double sum = 0.0;
-        for (int64_t j = 0; j < n; ++j) sum += (double)row[j];
-        double mean = sum / (double)n;
-        double ss = 0.0;
-        for (int64_t j = 0; j < n; ++j) {
-            double e = (double)row[j] - mean;
-            ss += e * e;
+#pragma omp parallel
+    {
+        double* v = (double*)malloc(sizeof(double) * (size_t)(n > 0 ? n : 1));
+#pragma omp for schedule(static)
+        for (int64_t i = 0; i < d; ++i) {
+            const float* row = W + i * n;
+            for (int64_t j = 0; j < n; ++j) v[j] = (double)row[j];
+            const double mean = ordered_row_sum(v, n) / (double)n;
+            for (int64_t j = 0; j < n; ++j) {
+                const double e = (double)row[j] - mean;
+                v[j] = e * e;
+            }
+            sigma_out[i] = (float)sqrt(ordered_row_sum(v, n) / (double)n);
         }
-        sigma_out[i] = (float)sqrt(ss / (double)n);
+        free(v);
     }
 }
 

@@ -99,8 +99,10 @@ def test_sigma_and_vmc(ops):
     W = synth.weight(synth.WORKLOADS[3], 0, d=67, n=777)
     got = host(ops.sigma_w(cuda(W)))
     ref = oracle.sigma_w(W)
-    ulps = np.abs(bits(got).astype(np.int64) - bits(ref).astype(np.int64))
-    assert ulps.max() <= 1 and (ulps == 0).mean() >= 0.95
+    assert np.array_equal(bits(got), bits(ref))  # the summation order is part of the definition
+    for n in (1, 100, 256, 3072, 12288):  # fewer columns than partial sums, ragged and exact multiples
+        Wn = synth.weight(synth.WORKLOADS[3], 1, d=9, n=n)
+        assert np.array_equal(bits(host(ops.sigma_w(cuda(Wn)))), bits(oracle.sigma_w(Wn))), n
     sig = synth.random_positive(5, 1000, 1e-4, 1.0)
     for alpha in (0.0, 0.5, 1.0, 1.5, 2.0):
         c = host(ops.vmc_scale(cuda(sig), alpha))
@@ -675,8 +677,7 @@ def test_workload_end_to_end_reduced(ops, wl_index):
         for mode, bits_ in wl.modes:
             P = _gpu_pipeline(ops, wl, li, d, L.n, M, mode, bits_)
             st = oracle.setup_layer(P["W"], synth.PHILOX_SEED, synth.layer_id(wl.index, li), wl.w_bits, synth.ALPHA)
-            sig_ulps = np.abs(bits(host(P["st"]["sigma"])).astype(np.int64) - bits(st["sigma"]).astype(np.int64))
-            assert sig_ulps.max() <= 1
+            assert np.array_equal(bits(host(P["st"]["sigma"])), bits(st["sigma"]))
             assert np.array_equal(bits(host(P["st"]["c"])), bits(st["c"])), "VMC scale"
             wr = host(P["st"]["wround"])
             assert np.array_equal(unpack4(wr) if wl.w_bits == 4 else wr, st["wround"])
