@@ -1092,6 +1092,20 @@ __global__ __launch_bounds__(256) void k_linear_skinny_planes(int64_t M, int64_t
     skinny_body<F_P16T, TT>(M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, 0, nullptr, nullptr);
 }
 
+// Blocks of the persistent grid for `tiles` tiles of K depth KT: one per compute unit,
+// except that when the tiles take more than one round and some block count between
+// 3/4 of the units and all of them divides the tiles into the same number of whole
+// rounds, that count is used (every block then owns the same number of tiles, and the
+// idle units draw no power while the others run).  A short K (fewer than 3 stages) runs
+// one block per tile.
+static unsigned persistent_grid(int tiles, int KT, int cus) {
+  if (KT < 3 || tiles <= cus) return (unsigned)tiles;
+  const int rounds = (tiles + cus - 1) / cus;
+  for (int c = cus; c >= cus * 3 / 4; --c)
+    if (tiles % c == 0 && tiles / c == rounds) return (unsigned)c;
+  return (unsigned)cus;
+}
+
 static int device_cus() {
   static int cus = 0;
   if (cus == 0) {
@@ -1154,7 +1168,7 @@ static hipError_t launch_fmt(int64_t M, int64_t d, int64_t n, const int8_t* xq, 
   const int ntile = tiles_m * tiles_n;
   const int KT = (int)((n + BK - 1) / BK);
   const int cus = device_cus();
-  const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
+  const dim3 grid(persistent_grid(ntile, KT, cus));
   if ((n % BK) != 0)
     hipLaunchKernelGGL((k_linear<FMT, true>), grid, dim3(kThreads), Cfg<FMT>::LDS, st, M, d, n, xq, sx, rowsum, mb,
                        split, sbar, Y, acc_dbg, tiles_m, tiles_n, wdelta, zbar, zw);
@@ -1187,9 +1201,10 @@ static hipError_t launch_planes(int64_t M, int64_t d, int64_t n, const int8_t* x
   const int ntile_n = tiles_m * (int)((d + Cfg<F_P16N>::OUT - 1) / Cfg<F_P16N>::OUT);
   const int KT = (int)((n + BK - 1) / BK);
   const int cus = device_cus();
-  const dim3 grid((unsigned)(KT >= 3 && ntile > cus ? cus : ntile));
-  const int g = (int)grid.x;
-  const int allow_narrow = (ntile_n + g - 1) / g < (ntile + g - 1) / g ? 1 : 0;  // rounds of each body
+  // the low-plane body only where its wider tiles take fewer rounds of a full grid
+  const int gf = KT >= 3 && ntile > cus ? cus : ntile;
+  const int allow_narrow = (ntile_n + gf - 1) / gf < (ntile + gf - 1) / gf ? 1 : 0;
+  const dim3 grid(persistent_grid(allow_narrow ? ntile_n : ntile, KT, cus));
   if ((n % BK) != 0)
     hipLaunchKernelGGL((k_linear_planes<true>), grid, dim3(kThreads), Cfg<F_P16T>::LDS, st, M, d, n, xq, sx, rowsum,
                        mb, code, sbar, Y, acc_dbg, tiles_m, allow_narrow);

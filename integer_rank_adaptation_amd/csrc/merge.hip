@@ -596,6 +596,14 @@ __device__ __forceinline__ int mul_merge(int w, float u, const MulParams& P, int
   return mv;
 }
 
+// Byte k (0 or 1) of four 32-bit values, packed into one dword with value e in byte e.
+// __builtin_amdgcn_perm(a, b, sel): selector bytes 0-3 take b's bytes, 4-7 a's, 0x0C a zero.
+__device__ __forceinline__ uint32_t gather_byte(uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3, uint32_t k) {
+  const uint32_t lo = __builtin_amdgcn_perm(v1, v0, 0x0C0C0000u | ((4u + k) << 8) | k);
+  const uint32_t hi = __builtin_amdgcn_perm(v3, v2, ((4u + k) << 24) | (k << 16) | 0x0C0Cu);
+  return lo | hi;
+}
+
 // Eight W_round codes of row i starting at column j0 (j0 % 8 == 0, n % 8 == 0).
 template <bool W4>
 __device__ __forceinline__ uint2 load_codes8(const uint8_t* __restrict__ wround, int64_t i, int64_t n, int64_t j0) {
@@ -750,30 +758,21 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           }
         }
         if (OUT == kOutPlanes) {
-          // hi / lo bytes of the 8 values, packed 4 per dword (byte e of the pair = value e)
-          uint32_t h[8], l[8], any_hi = 0;
-          if (small) {  // balanced
+          // In both splits the low plane is the low byte of m (m - 256 hi keeps it; the bias
+          // split then flips bit 7), and the high plane is byte 1 of m + 128 (balanced) or of
+          // m (bias).  The bytes of four values at a time are gathered with v_perm.
+          uint32_t t[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const int hv = (mm[e] + 128) >> 8;
-              h[e] = (uint32_t)hv & 0xFFu;
-              l[e] = (uint32_t)(mm[e] - 256 * hv) & 0xFFu;
-              any_hi |= h[e];
-            }
-          } else {  // bias
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              h[e] = (uint32_t)(mm[e] >> 8) & 0xFFu;
-              l[e] = ((uint32_t)mm[e] & 0xFFu) ^ 0x80u;
-            }
-          }
+          for (int e = 0; e < 8; ++e) t[e] = (uint32_t)(small ? mm[e] + 128 : mm[e]);
+          const uint32_t flip = small ? 0u : 0x80808080u;
+          const uint2 hi = make_uint2(gather_byte(t[0], t[1], t[2], t[3], 1), gather_byte(t[4], t[5], t[6], t[7], 1));
+          const uint2 lo = make_uint2(gather_byte((uint32_t)mm[0], (uint32_t)mm[1], (uint32_t)mm[2], (uint32_t)mm[3], 0) ^ flip,
+                                      gather_byte((uint32_t)mm[4], (uint32_t)mm[5], (uint32_t)mm[6], (uint32_t)mm[7], 0) ^ flip);
           uint8_t* row = reinterpret_cast<uint8_t*>(m) + i * 2 * n;
           const int64_t off = 2 * (j0 & ~(int64_t)15) + (j0 & 15);  // hi bytes; lo bytes 16 further
-          store_once8(row + off, make_uint2(h[0] | h[1] << 8 | h[2] << 16 | h[3] << 24,
-                                            h[4] | h[5] << 8 | h[6] << 16 | h[7] << 24));
-          store_once8(row + off + 16, make_uint2(l[0] | l[1] << 8 | l[2] << 16 | l[3] << 24,
-                                                 l[4] | l[5] << 8 | l[6] << 16 | l[7] << 24));
-          if (small && any_hi) split[i] = 1;
+          store_once8(row + off, hi);
+          store_once8(row + off + 16, lo);
+          if (small && (hi.x | hi.y) != 0u) split[i] = 1;
         } else {
         int4 pk;
         pk.x = (int)__builtin_amdgcn_perm((uint32_t)mm[1], (uint32_t)mm[0], 0x05040100u);
