@@ -120,8 +120,8 @@ def copy_factor(d, counter, nbytes):
 
 
 def traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, workload, kernel):
-    ff, fk = copy_factor(cf_dir, "FETCH_SIZE", copy_bytes)
-    wf, wk = copy_factor(cw_dir, "WRITE_SIZE", copy_bytes)
+    ff, fk = copy_factor(cf_dir, "FETCH_SIZE", copy_bytes) if cf_dir else (None, None)
+    wf, wk = copy_factor(cw_dir, "WRITE_SIZE", copy_bytes) if cw_dir else (None, None)
     fe = read_counter(fetch_dir, "FETCH_SIZE")
     wr = read_counter(write_dir, "WRITE_SIZE")
     per = collections.OrderedDict()
@@ -152,7 +152,7 @@ def traffic(fetch_dir, write_dir, cf_dir, cw_dir, copy_bytes, workload, kernel):
 # kernels, then the linear layer).  Their launches cycle through the layers in order, so
 # launch k of a kernel belongs to layer k mod L.
 STEP_KERNELS = ("k_adapt_mfma", "k_adapt_generic", "k_row_range", "k_mul_params", "k_quant_mul", "k_quant_shift",
-                "k_linear", "k_linear_planes")
+                "k_linear", "k_linear_planes", "k_linear_skinny", "k_linear_skinny_planes")
 CLOCK_HZ = 2.4e9
 SIMDS = 256 * 4
 XCDS = 8
@@ -197,8 +197,8 @@ def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, 
     2.4 GHz peak) and the matrix-core busy fraction."""
     import statistics
 
-    ff, fk = copy_factor(cf_dir, "FETCH_SIZE", copy_bytes)
-    wf, wk = copy_factor(cw_dir, "WRITE_SIZE", copy_bytes)
+    ff, fk = copy_factor(cf_dir, "FETCH_SIZE", copy_bytes) if cf_dir else (None, None)
+    wf, wk = copy_factor(cw_dir, "WRITE_SIZE", copy_bytes) if cw_dir else (None, None)
     dur = _by_layer(read_trace_rows(trace_dir), layers, lambda r: r["us"])
     vals = collections.defaultdict(dict)  # kernel -> counter -> per-layer lists
     for d in pmc_dirs:
@@ -213,9 +213,9 @@ def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, 
         for li, L in enumerate(layers):
             rec = dict(us=round(med(per[li]), 3) if per[li] else None, launches=len(per[li]))
             cv = {c: med(v[li]) for c, v in vals.get(kname, {}).items() if v[li]}
-            if "FETCH_SIZE" in cv:
+            if "FETCH_SIZE" in cv and ff:
                 rec["fetch_bytes"] = round(cv["FETCH_SIZE"] * 1024 * ff)
-            if "WRITE_SIZE" in cv:
+            if "WRITE_SIZE" in cv and wf:
                 rec["write_bytes"] = round(cv["WRITE_SIZE"] * 1024 * wf)
             if rec["us"] and "fetch_bytes" in rec and "write_bytes" in rec:
                 rec["hbm_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
@@ -238,7 +238,7 @@ def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, 
             per_layer[L][kname] = rec
     out = dict(workload=workload, library_source_sha=library_source_sha(), command=commands,
                calibration=dict(copy_bytes=copy_bytes, copy_fetch_kib=fk, copy_write_kib=wk,
-                                fetch_scale=round(ff, 6), write_scale=round(wf, 6)),
+                                fetch_scale=round(ff, 6) if ff else None, write_scale=round(wf, 6) if wf else None),
                per_layer=per_layer)
     # rooflines of the merge's quantize kernel (HBM) and adaptation kernel (vector ALU),
     # aggregated over the step's layers
@@ -272,8 +272,9 @@ def counters_md(rec):
     lines = ["Commands (from the repository root, on one MI355X):", ""]
     lines += ["    " + c for c in rec.get("command", [])]
     lines += ["", f"Workload `{rec['workload']}`; library source hash `{rec['library_source_sha']}`.",
-              f"HBM bytes = FETCH_SIZE x {cal['fetch_scale']} + WRITE_SIZE x {cal['write_scale']} (KiB x 1024), "
-              f"calibrated on a {cal['copy_bytes']} byte device copy.",
+              (f"HBM bytes = FETCH_SIZE x {cal['fetch_scale']} + WRITE_SIZE x {cal['write_scale']} (KiB x 1024), "
+               f"calibrated on a {cal['copy_bytes']} byte device copy." if cal.get("fetch_scale") else
+               "Kernel trace only (no counter passes)."),
               "GRBM_GUI_ACTIVE is summed over the 8 XCDs (clock = value / 8 / duration, not derived under 20 us); VALU fraction of peak = "
               "SQ_INSTS_VALU x 64 lanes / duration / 39.32 T lane-instructions/s; MfmaUtil and VALUBusy are "
               "rocprofv3's derived percentages.", "",
@@ -335,10 +336,10 @@ def main(argv=None):
     t.add_argument("--commands", nargs="*", default=[])
     c = sub.add_parser("counters")
     c.add_argument("--trace", required=True)
-    c.add_argument("--pmc", nargs="+", required=True)
-    c.add_argument("--copy-fetch", required=True)
-    c.add_argument("--copy-write", required=True)
-    c.add_argument("--copy-bytes", type=int, required=True)
+    c.add_argument("--pmc", nargs="*", default=[])
+    c.add_argument("--copy-fetch", default="")
+    c.add_argument("--copy-write", default="")
+    c.add_argument("--copy-bytes", type=int, default=0)
     c.add_argument("--workload", required=True)
     c.add_argument("--layers", required=True, help="comma-separated layer names in step order")
     c.add_argument("--elems", default="", help="comma-separated weights per layer (VALU instructions per weight)")
