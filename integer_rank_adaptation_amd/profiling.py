@@ -225,9 +225,11 @@ def counters(trace_dir, pmc_dirs, cf_dir, cw_dir, copy_bytes, workload, layers, 
                 if c not in ("FETCH_SIZE", "WRITE_SIZE"):
                     rec[c] = v
             # GRBM_GUI_ACTIVE comes summed over the XCDs: cycles of the kernel = value / XCDS.
-            # Below about 20 us the dispatch's own overhead dominates it, so no clock is derived.
+            # It also counts a few microseconds of dispatch around each launch (short kernels
+            # read above 2.4 GHz), so the clock is derived only for launches of 100 us or
+            # more, and is an upper bound there.
             cycles = cv["GRBM_GUI_ACTIVE"] / XCDS if cv.get("GRBM_GUI_ACTIVE") else None
-            if rec["us"] and cycles and rec["us"] >= 20:
+            if rec["us"] and cycles and rec["us"] >= 100:
                 rec["clock_GHz"] = round(cycles / (rec["us"] * 1e-6) / 1e9, 3)
             if rec["us"] and cv.get("SQ_INSTS_VALU"):
                 rec["valu_frac_of_peak"] = round(cv["SQ_INSTS_VALU"] * 4 / (rec["us"] * 1e-6 * CLOCK_HZ * SIMDS), 4)
@@ -275,7 +277,7 @@ def counters_md(rec):
               (f"HBM bytes = FETCH_SIZE x {cal['fetch_scale']} + WRITE_SIZE x {cal['write_scale']} (KiB x 1024), "
                f"calibrated on a {cal['copy_bytes']} byte device copy." if cal.get("fetch_scale") else
                "Kernel trace only (no counter passes)."),
-              "GRBM_GUI_ACTIVE is summed over the 8 XCDs (clock = value / 8 / duration, not derived under 20 us); VALU fraction of peak = "
+              "GRBM_GUI_ACTIVE is summed over the 8 XCDs and includes a few us of dispatch per launch (clock = value / 8 / duration, an upper bound, given for launches of 100 us or more); VALU fraction of peak = "
               "SQ_INSTS_VALU x 64 lanes / duration / 39.32 T lane-instructions/s; MfmaUtil and VALUBusy are "
               "rocprofv3's derived percentages.", "",
               "| layer | kernel | us (trace) | HBM MB | counter GB/s | % of 8 TB/s | VALU insts / elem | "
