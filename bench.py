@@ -123,6 +123,21 @@ def gemm_exec_ops(M, d, n, mode, planes=None):
     return 2.0 * M * d * n * passes
 
 
+def planes_multiplied(M, d, n, any_code, torch):
+    """Byte planes the linear layer multiplies on the byte-plane storage: one when every
+    plane code is 0 and (above 32 tokens) its 256-output tiles take fewer rounds of the
+    persistent grid than the two-plane tiles -- the library's launch rule -- else two."""
+    if any_code:
+        return 2
+    if M <= 32:
+        return 1
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    tm = -(-M // 256)
+    t2, tn, kt = tm * -(-d // 128), tm * -(-d // 256), -(-n // 64)
+    g = cus if kt >= 3 and t2 > cus else t2
+    return 1 if -(-tn // g) < -(-t2 // g) else 2
+
+
 def merged_m(lay, torch):
     """The merged integers of a layer's MUL output as int32 (from either storage)."""
     o = lay["out"]
@@ -902,7 +917,7 @@ def main():
         mms = float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)]))
         gms = float(np.mean([ev[s][k][1].elapsed_time(ev[s][k][2]) for s in range(args.steps)]))
         mb = merge_alg_bytes(L.d, L.n, wl.r, wl.w_bits, mode)
-        nplanes = (1 if not bool(lay["out"]["code"].any()) else 2) if planes else None
+        nplanes = planes_multiplied(M, L.d, L.n, bool(lay["out"]["code"].any()), torch) if planes else None
         gops = gemm_exec_ops(M, L.d, L.n, mode, nplanes)
         eops = 2.0 * M * L.d * L.n  # the method's int16 x int8 (or int8 x int8) products, once
         roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + eops / (INT8_PEAK_TOPS * 1e12) * 1e3
