@@ -470,16 +470,34 @@ __global__ __launch_bounds__(256) void k_adapt_generic(int64_t d, int64_t n, int
   }
 }
 
-// Row range from the tile partials (order keys; uniform per block).  U_min / U_max
-// are the least / greatest valid U of the row in the IEEE total order (+inf / -inf
-// for a row without valid elements).
-__device__ __forceinline__ void row_range(const int* __restrict__ pmin, const int* __restrict__ pmax, int64_t d,
-                                          int64_t i, int ntiles, float& umin, float& umax) {
+// Row range from the wave partials (order keys): U_min / U_max are the least /
+// greatest valid U of the row in the IEEE total order (+inf / -inf for a row without
+// valid elements).  64 consecutive rows per block of kRangeWaves waves: lane l of every wave
+// takes row i0 + l (coalesced reads of each partial column), wave w the partial columns
+// w, w + kRangeWaves, ...; the waves' order keys are combined through LDS (min / max of
+// integers: the same result in any order).  The result is valid in wave 0 only.
+constexpr int kRangeWaves = 16;
+__device__ __forceinline__ void row_range_block(const int* __restrict__ pmin, const int* __restrict__ pmax, int64_t d,
+                                                int64_t i, int ntiles, float& umin, float& umax) {
+  __shared__ int smin[kRangeWaves][64], smax[kRangeWaves][64];
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   int kmin = kKeyPosInf, kmax = kKeyNegInf;
-#pragma unroll 8
-  for (int t = 0; t < ntiles; ++t) {
-    kmin = min(kmin, pmin[(int64_t)t * d + i]);
-    kmax = max(kmax, pmax[(int64_t)t * d + i]);
+  if (i < d) {
+#pragma unroll 4
+    for (int t = wid; t < ntiles; t += kRangeWaves) {
+      kmin = min(kmin, pmin[(int64_t)t * d + i]);
+      kmax = max(kmax, pmax[(int64_t)t * d + i]);
+    }
+  }
+  smin[wid][lane] = kmin;
+  smax[wid][lane] = kmax;
+  __syncthreads();
+  if (wid == 0) {
+#pragma unroll
+    for (int w = 1; w < kRangeWaves; ++w) {
+      kmin = min(kmin, smin[w][lane]);
+      kmax = max(kmax, smax[w][lane]);
+    }
   }
   umin = key_f32(kmin);
   umax = key_f32(kmax);
@@ -487,14 +505,14 @@ __device__ __forceinline__ void row_range(const int* __restrict__ pmin, const in
 
 // Exposes U_min / U_max (the statistics entry point).  `split` (nullable) is the
 // per-row plane-split code of the MUL merge, cleared here and raised by the quantize
-// kernel for rows holding some m >= 32640.
-__global__ __launch_bounds__(256) void k_row_range(int64_t d, int ntiles, const int* __restrict__ pmin,
-                                                  const int* __restrict__ pmax, float* __restrict__ umin,
-                                                  float* __restrict__ umax, uint8_t* __restrict__ split) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < d) {
-    float a, b;
-    row_range(pmin, pmax, d, i, ntiles, a, b);
+// kernel for rows holding some m >= 32640.  64 rows per block of kRangeWaves waves.
+__global__ __launch_bounds__(64 * kRangeWaves) void k_row_range(int64_t d, int ntiles, const int* __restrict__ pmin,
+                                                               const int* __restrict__ pmax, float* __restrict__ umin,
+                                                               float* __restrict__ umax, uint8_t* __restrict__ split) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  float a, b;
+  row_range_block(pmin, pmax, d, i, ntiles, a, b);
+  if ((threadIdx.x >> 6) == 0 && i < d) {
     umin[i] = a;
     umax[i] = b;
     if (split) split[i] = 0;
@@ -633,21 +651,27 @@ __device__ __forceinline__ int code_at(const uint8_t* __restrict__ wround, int64
 // quantize kernel raises it for rows holding some m >= 32640.  With `planes` it is
 // the row's byte-plane code instead: 0 for a small row (balanced split; the quantize
 // kernel raises bit 0 when some high byte is not zero), 3 otherwise (bias split).
-__global__ __launch_bounds__(256) void k_mul_params(int64_t d, int ntiles, const int* __restrict__ pmin,
-                                                   const int* __restrict__ pmax, const float* __restrict__ umin_in,
-                                                   const float* __restrict__ umax_in, float* __restrict__ umin_out,
-                                                   float* __restrict__ umax_out, int qmax, int wmax,
-                                                   const int32_t* __restrict__ z, float* __restrict__ sbar,
-                                                   int32_t* __restrict__ zbar, float* __restrict__ rs,
-                                                   int* __restrict__ small, uint8_t* __restrict__ split,
-                                                   bool planes) {
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < d; i += (int64_t)gridDim.x * blockDim.x) {
-    float a, b;
+// 64 rows per block of kRangeWaves waves (the row range as in k_row_range); wave 0 then
+// derives each row's parameters.
+__global__ __launch_bounds__(64 * kRangeWaves) void k_mul_params(int64_t d, int ntiles, const int* __restrict__ pmin,
+                                                                const int* __restrict__ pmax,
+                                                                const float* __restrict__ umin_in,
+                                                                const float* __restrict__ umax_in,
+                                                                float* __restrict__ umin_out,
+                                                                float* __restrict__ umax_out, int qmax, int wmax,
+                                                                const int32_t* __restrict__ z, float* __restrict__ sbar,
+                                                                int32_t* __restrict__ zbar, float* __restrict__ rs,
+                                                                int* __restrict__ small, uint8_t* __restrict__ split,
+                                                                bool planes) {
+  const int64_t i = (int64_t)blockIdx.x * 64 + (threadIdx.x & 63);
+  float a = 0.0f, b = 0.0f;
+  if (!umin_in) row_range_block(pmin, pmax, d, i, ntiles, a, b);  // uniform: every wave reaches the barrier
+  if ((threadIdx.x >> 6) != 0 || i >= d) return;
+  {
     if (umin_in) {
       a = umin_in[i];
       b = umax_in[i];
     } else {
-      row_range(pmin, pmax, d, i, ntiles, a, b);
       umin_out[i] = a;
       umax_out[i] = b;
     }
@@ -1041,6 +1065,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
 // =================================================================================
 // Host launchers (called by the C ABI layer after validation).
 // =================================================================================
+// Blocks of the row-range kernels: one per 64 rows, every row covered (d < 2^31).
+static inline unsigned range_blocks(int64_t d) { return (unsigned)(d > 0 ? (d + 63) / 64 : 1); }
+
 static inline unsigned grid1(uint64_t work, unsigned block) {
   uint64_t g = (work + block - 1) / block;
   if (g > (1u << 20)) g = 1u << 20;
@@ -1249,7 +1276,7 @@ hipError_t launch_adapt(const AdaptArgs& a, int* ntiles_out, hipStream_t st) {
 
 hipError_t launch_row_range(int64_t d, int ntiles, const int* pmin, const int* pmax, float* umin, float* umax,
                             uint8_t* split, hipStream_t st) {
-  hipLaunchKernelGGL(k_row_range, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin, umax,
+  hipLaunchKernelGGL(k_row_range, dim3(range_blocks(d)), dim3(64 * kRangeWaves), 0, st, d, ntiles, pmin, pmax, umin, umax,
                      split);
   return hipGetLastError();
 }
@@ -1662,7 +1689,7 @@ hipError_t launch_mul_params(int64_t d, int ntiles, const int* pmin, const int* 
                              const float* umax_in, float* umin_out, float* umax_out, int u_bits, int w_bits,
                              const int32_t* z, float* sbar, int32_t* zbar, float* rs, int* small, uint8_t* split,
                              bool planes, hipStream_t st) {
-  hipLaunchKernelGGL(k_mul_params, dim3(grid1((uint64_t)d, 256)), dim3(256), 0, st, d, ntiles, pmin, pmax, umin_in,
+  hipLaunchKernelGGL(k_mul_params, dim3(range_blocks(d)), dim3(64 * kRangeWaves), 0, st, d, ntiles, pmin, pmax, umin_in,
                      umax_in, umin_out, umax_out, (1 << u_bits) - 1, (1 << w_bits) - 1, z, sbar, zbar, rs, small,
                      split, planes);
   return hipGetLastError();
