@@ -792,10 +792,18 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           const uint2 hi = make_uint2(gather_byte(t[0], t[1], t[2], t[3], 1), gather_byte(t[4], t[5], t[6], t[7], 1));
           const uint2 lo = make_uint2(gather_byte((uint32_t)mm[0], (uint32_t)mm[1], (uint32_t)mm[2], (uint32_t)mm[3], 0) ^ flip,
                                       gather_byte((uint32_t)mm[4], (uint32_t)mm[5], (uint32_t)mm[6], (uint32_t)mm[7], 0) ^ flip);
-          uint8_t* row = reinterpret_cast<uint8_t*>(m) + i * 2 * n;
-          const int64_t off = 2 * (j0 & ~(int64_t)15) + (j0 & 15);  // hi bytes; lo bytes 16 further
-          store_once8(row + off, hi);
-          store_once8(row + off + 16, lo);
+          // Lanes 2k and 2k + 1 hold columns 0-7 and 8-15 of one group of 16 (n % 16 == 0,
+          // so both are active for every row): they swap halves so that the even lane
+          // stores the group's 16 high bytes and the odd lane its 16 low bytes, one
+          // 16-byte store each, together one whole 32-byte group.
+          const bool odd = (threadIdx.x & 1) != 0;
+          const uint2 give = odd ? hi : lo;
+          const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 1, kWave), (uint32_t)__shfl_xor((int)give.y, 1, kWave));
+          uint8_t* grp = reinterpret_cast<uint8_t*>(m) + i * 2 * n + 2 * (j0 & ~(int64_t)15);
+          if (odd)
+            store_once16(grp + 16, make_int4((int)got.x, (int)got.y, (int)lo.x, (int)lo.y));
+          else
+            store_once16(grp, make_int4((int)hi.x, (int)hi.y, (int)got.x, (int)got.y));
           if (small && (hi.x | hi.y) != 0u) split[i] = 1;
         } else {
         int4 pk;
