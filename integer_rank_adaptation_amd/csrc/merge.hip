@@ -268,8 +268,11 @@ constexpr int kMfmaMaxRowTiles = 8;
 
 // PTQ (the QLoRA-style comparison path): x = (s w + R*) + AB for every element instead
 // of U, with no division and no excluded elements.
+// Three waves per SIMD up to r = 32; at r = 64 the 64 B values per lane need the
+// registers of two waves per SIMD (with three, every instantiation spilled, and the
+// Laplace one ran 1-6 % slower on the Llama-shaped layers).
 template <int R, bool W4, bool PTQ, int DIST>
-__global__ __launch_bounds__(256, 3) void k_adapt_mfma(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
+__global__ __launch_bounds__(256, (R > 32 ? 2 : 3)) void k_adapt_mfma(int64_t d, int64_t n, uint64_t seed, uint32_t layer_id,
                                                     const uint8_t* __restrict__ wround, const int32_t* __restrict__ z,
                                                     const float* __restrict__ s, const float* __restrict__ c,
                                                     const float* __restrict__ A, const float* __restrict__ B,
