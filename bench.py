@@ -491,7 +491,7 @@ def library_gemm_medians(args, layers, mode, w_bits, planes, torch, stream):
         o = lay["out"]
         w8 = None
         if mode == "mul" and planes and not bool(o["code"].any()):
-            w8 = o["planes"].view(L.d, L.n // 16, 2, 16)[:, :, 1, :].reshape(L.d, L.n).view(torch.int8)
+            w8 = o["planes"].view(L.d, 2, L.n)[:, 1, :].contiguous().view(torch.int8)  # the low planes
         elif mode == "shift" and w_bits == 8:
             w8 = o["m"].view(torch.int8).view(L.d, L.n)
         if w8 is None or lay["xq"].shape[0] <= 16:

@@ -214,8 +214,9 @@ int intlora_merge_mul(const intlora_desc* desc, const intlora_base* base, const 
  *   bound_i = max(|z_i|, |2^w_bits - 1 - z_i|) * max(z_bar_i, 2^u_bits - 1 - z_bar_i);
  *   bound_i <= 32639: balanced split hi = (m + 128) >> 8, lo = m - 256 hi (m = 256 hi + lo);
  *   otherwise:        bias split hi = m >> 8, lo = (m & 0xFF) - 128 (m = 256 hi + lo + 128).
- * Layout m_planes (uint8, d x 2n): per row, for each group of 16 consecutive columns,
- * the 16 high bytes then the 16 low bytes (two's complement).  plane_code[d] (uint8):
+ * Layout m_planes (uint8, d x 2n): per row, the row's n high bytes in column order,
+ * then its n low bytes (two's complement), so that a call whose high planes are all
+ * zero streams whole runs of low bytes.  plane_code[d] (uint8):
  * 0 = balanced and every high byte of the row is zero (-128 <= m <= 127: the high plane adds
  * nothing), 1 = balanced, 3 = bias split.  n must be a multiple of 16 (INTLORA_ESHAPE).
  * Other arguments, outputs and workspace as intlora_merge_mul (whose split codes

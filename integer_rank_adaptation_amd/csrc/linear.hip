@@ -67,8 +67,9 @@ typedef __bf16 bf2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 // F_P16T / F_P16N: the int16 merged integers stored as their two byte planes (per row,
-// each group of 16 columns holds 16 high bytes then 16 low bytes); F_P16T multiplies
-// both planes, F_P16N only the low plane (every high byte of the call is zero).
+// the n high bytes, then the n low bytes); F_P16T multiplies both planes, F_P16N only
+// the low plane (every high byte of the call is zero), whose rows it reads as whole
+// contiguous runs.
 enum { F_INT4 = 4, F_INT8 = 8, F_INT16 = 16, F_P16T = 17, F_P16N = 18, F_UW4 = 44 };
 // B-tile layout families in LDS: 128-byte rows (64 int16, or 64 high + 64 low bytes)
 // for 128 outputs; 64-byte rows (64 int8) for 256 outputs.
@@ -151,10 +152,14 @@ __device__ __forceinline__ void make_plan(int n, Plan<F>& p) {
     if (F == F_INT8) {           // 64-byte rows
       const int row = 16 * g + (lane >> 2);
       p.b[q] = (uint32_t)(row * n + 16 * ((lane & 3) ^ swz64(row)));
-    } else if (F == F_P16N) {    // the low bytes of each 16-column group: 16 bytes at stride 32
+    } else if (F == F_P16N) {    // 64-byte rows of the low plane (n bytes into the row)
       const int row = 16 * g + (lane >> 2);
-      p.b[q] = (uint32_t)(row * 2 * n + 32 * ((lane & 3) ^ swz64(row)) + 16);
-    } else if (is_l16(F)) {      // 128-byte rows (64 int16, or 4 groups of 16 high + 16 low bytes)
+      p.b[q] = (uint32_t)(row * 2 * n + n + 16 * ((lane & 3) ^ swz64(row)));
+    } else if (F == F_P16T) {    // 128-byte LDS rows: chunk c holds 16 high (c even) or low
+      const int row = 8 * g + (lane >> 3);  // (c odd) bytes of columns 16 (c / 2) + 0..15
+      const int c = (lane & 7) ^ swz128(row);
+      p.b[q] = (uint32_t)(row * 2 * n + (c & 1) * n + 16 * (c >> 1));
+    } else if (is_l16(F)) {      // 128-byte rows (64 int16)
       const int row = 8 * g + (lane >> 3);
       p.b[q] = (uint32_t)(2 * (row * n + 8 * ((lane & 7) ^ swz128(row))));
     } else if (F == F_UW4) {     // 32-byte rows: loads 0..3 U's 128 rows, 4..7 W's (same offsets)
@@ -175,7 +180,9 @@ __device__ __forceinline__ void stage_rsrc(int kt, const int8_t* a_tile, int64_t
                                            int64_t b_bytes, __amdgpu_buffer_rsrc_t& ra, __amdgpu_buffer_rsrc_t& rb) {
   using namespace lin;
   const int k0 = kt * BK;
-  const int64_t kb = (F == F_INT16 || planar(F)) ? 2 * (int64_t)k0 : (F == F_INT8 ? (int64_t)k0 : (int64_t)(k0 >> 1));
+  // bytes of the stage's first K element from the row start: INT16 2 per element, the
+  // planes and INT8 1 (a plane's offset within the row is in the plan), INT4 / UW4 1/2
+  const int64_t kb = F == F_INT16 ? 2 * (int64_t)k0 : ((F == F_INT8 || planar(F)) ? (int64_t)k0 : (int64_t)(k0 >> 1));
   ra = make_rsrc(a_tile + k0, a_bytes - k0);
   rb = make_rsrc(b_tile + kb, b_bytes - kb);
 }
@@ -895,12 +902,15 @@ __device__ __forceinline__ void skinny_body(int64_t M, int64_t d, int64_t n, con
     st = st < KT ? st : KT - 1;
     int64_t k = st * 64 + 16 * kg;
     k = k < n ? k : n - 16;  // n is a multiple of 32: chunks are whole
-    if (F == F_INT16 || F == F_P16T) {  // 16 int16, or 16 high then 16 low bytes
+    if (F == F_INT16) {  // 16 int16
       const v4i* pw = reinterpret_cast<const v4i*>(m + wr * wrow + 2 * k);
       S.w[0] = pw[0];
       S.w[1] = pw[1];
+    } else if (F == F_P16T) {  // 16 high bytes, and the same columns' 16 low bytes
+      S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + k);
+      S.w[1] = *reinterpret_cast<const v4i*>(m + wr * wrow + n + k);
     } else if (F == F_P16N) {  // the 16 low bytes
-      S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + 2 * k + 16);
+      S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + n + k);
       S.w[1] = v4i{0, 0, 0, 0};
     } else if (F == F_INT8) {
       S.w[0] = *reinterpret_cast<const v4i*>(m + wr * wrow + k);

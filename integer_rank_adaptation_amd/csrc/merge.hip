@@ -696,8 +696,8 @@ __global__ __launch_bounds__(64 * kRangeWaves) void k_mul_params(int64_t d, int 
 //  kOutCodes:  U_round itself as packed nibbles (u_bits <= 4, n even; low nibble = even
 //              column), for a linear layer that forms m on load;
 //  kOutPlanes: m already split into its two int8 planes, the layout the linear layer
-//              reads without conversion: per row, for each group of 16 columns, the 16
-//              high bytes then the 16 low bytes (d x 2n bytes; n % 16 == 0).  A small
+//              reads without conversion: per row, the n high bytes, then the n low
+//              bytes (d x 2n bytes; n % 16 == 0).  A small
 //              row (plane code 0 on entry) takes the balanced split hi = (m + 128) >> 8,
 //              lo = m - 256 hi, and its code becomes 1 when some hi is not zero; any other
 //              row (code 3) takes the bias split hi = m >> 8, lo = (m & 0xFF) - 128.
@@ -797,14 +797,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
                                       gather_byte((uint32_t)mm[4], (uint32_t)mm[5], (uint32_t)mm[6], (uint32_t)mm[7], 0) ^ flip);
           // Lanes 2k and 2k + 1 hold columns 0-7 and 8-15 of one group of 16 (n % 16 == 0,
           // so both are active for every row): they swap halves so that the even lane
-          // stores the group's 16 high bytes and the odd lane its 16 low bytes, one
-          // 16-byte store each, together one whole 32-byte group.
+          // stores the group's 16 high bytes (in the row's high plane) and the odd lane its
+          // 16 low bytes (in the low plane, n bytes further on), one 16-byte store each.
           const bool odd = (threadIdx.x & 1) != 0;
           const uint2 give = odd ? hi : lo;
           const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 1, kWave), (uint32_t)__shfl_xor((int)give.y, 1, kWave));
-          uint8_t* grp = reinterpret_cast<uint8_t*>(m) + i * 2 * n + 2 * (j0 & ~(int64_t)15);
+          uint8_t* grp = reinterpret_cast<uint8_t*>(m) + i * 2 * n + (j0 & ~(int64_t)15);
           if (odd)
-            store_once16(grp + 16, make_int4((int)got.x, (int)got.y, (int)lo.x, (int)lo.y));
+            store_once16(grp + n, make_int4((int)got.x, (int)got.y, (int)lo.x, (int)lo.y));
           else
             store_once16(grp, make_int4((int)hi.x, (int)hi.y, (int)got.x, (int)got.y));
           if (small && (hi.x | hi.y) != 0u) split[i] = 1;

@@ -405,9 +405,9 @@ def plane_store(m, z, zbar, w_bits, u_bits):
     |m| <= max(|z|, |2^w_bits - 1 - z|) * max(z_bar, 2^u_bits - 1 - z_bar):
       bound <= 32639: balanced split (hi = (m + 128) >> 8, lo = m - 256 hi);
       otherwise:      bias split (hi = m >> 8, lo = (m & 0xFF) - 128).
-    Layout: per row, for each group of 16 columns, the 16 high bytes then the 16 low
-    bytes.  Code: 3 for a bias row; for a balanced row 1 if some high byte is not zero,
-    else 0.  Returns (layout uint8 rows x 2n, codes uint8)."""
+    Layout: per row, the n high bytes (column order), then the n low bytes.  Code: 3
+    for a bias row; for a balanced row 1 if some high byte is not zero, else 0.
+    Returns (layout uint8 rows x 2n, codes uint8)."""
     m = np.asarray(m).astype(np.int64)
     rows, n = m.shape
     assert n % 16 == 0
@@ -418,17 +418,16 @@ def plane_store(m, z, zbar, w_bits, u_bits):
     bias = bound > 32639
     hi, lo = byte_planes(m, split=bias.astype(np.uint8))
     code = np.where(bias, 3, np.where((hi != 0).any(axis=1), 1, 0)).astype(np.uint8)
-    layout = np.concatenate([hi.reshape(rows, n // 16, 16), lo.reshape(rows, n // 16, 16)], axis=2)
-    return np.ascontiguousarray(layout.reshape(rows, 2 * n)).view(np.uint8), code
+    layout = np.concatenate([hi, lo], axis=1).astype(np.int8)
+    return np.ascontiguousarray(layout).view(np.uint8), code
 
 
 def merged_from_planes(layout, code):
     """The merged integers a byte-plane layout stores: 256 hi + lo (+ 128 on bias rows)."""
-    layout = np.asarray(layout, np.uint8)
-    rows, n2 = layout.shape
-    g = layout.view(np.int8).astype(np.int64).reshape(rows, n2 // 32, 32)
-    hi = g[:, :, :16].reshape(rows, n2 // 2)
-    lo = g[:, :, 16:].reshape(rows, n2 // 2)
+    layout = np.ascontiguousarray(layout, np.uint8)
+    n = layout.shape[1] // 2
+    planes = layout.view(np.int8).astype(np.int64)
+    hi, lo = planes[:, :n], planes[:, n:]
     bias = ((np.asarray(code, np.uint8) >> 1) & 1).astype(np.int64)[:, None]
     return 256 * hi + lo + 128 * bias
 

@@ -936,8 +936,8 @@ def _planes_linear_check(ops, M, m, z, zbar, w_bits, u_bits, seed, expect_narrow
     _, _, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
     Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), ops.B.INTLORA_W_INT16_PLANES, cuda(lay), cuda(sbar), d,
                         acc_dbg=True, split=cuda(code))
-    g = lay.view(np.int8).astype(np.int64).reshape(d, n // 16, 32)
-    hi, lo = g[:, :, :16].reshape(d, n), g[:, :, 16:].reshape(d, n)
+    g = lay.view(np.int8).astype(np.int64)
+    hi, lo = g[:, :n], g[:, n:]  # per row: the n high bytes, then the n low bytes
     acc = host(acc)
     # every partial sum is an integer below 127 * 255 * n < 2^53: exact in binary64
     assert np.array_equal(acc[0], (xq.astype(np.float64) @ hi.T.astype(np.float64)).astype(np.int64))

@@ -50,19 +50,23 @@ def test_code_zero_means_zero_high_plane():
     m[6, 7] = -129
     lay, code = oracle.plane_store(m, np.full(8, 7), np.full(8, 8), 4, 4)
     assert list(code) == [0, 0, 0, 1, 0, 0, 1, 0]
-    hi = lay.view(np.int8).reshape(8, 4, 32)[:, :, :16]
+    hi = lay.view(np.int8)[:, :64]
     assert np.all(hi[code == 0] == 0)
     assert np.any(hi[3] != 0) and np.any(hi[6] != 0)
 
 
-def test_layout_groups_of_sixteen():
-    m = np.arange(32, dtype=np.int64).reshape(1, 32) * 300 - 4000
+def test_layout_whole_row_planes():
+    """Row i of the layout: its n high bytes in column order, then its n low bytes; the
+    bytes are written out here by hand for one small row (balanced split, 4-bit codes)."""
+    m = np.array([[-4000, -129, -128, -1, 0, 1, 127, 128, 255, 256, 300, 1000, 4000, 6000, 7000, 7400]])
     lay, code = oracle.plane_store(m, [7], [7], 4, 4)
-    hi, lo = oracle.byte_planes(m, split=np.zeros(1, np.uint8))
-    assert np.array_equal(lay[0, :16].view(np.int8), hi[0, :16])
-    assert np.array_equal(lay[0, 16:32].view(np.int8), lo[0, :16])
-    assert np.array_equal(lay[0, 32:48].view(np.int8), hi[0, 16:])
-    assert np.array_equal(lay[0, 48:].view(np.int8), lo[0, 16:])
+    # balanced split: hi = floor((m + 128) / 256), lo = m - 256 hi
+    hi = [-16, -1, 0, 0, 0, 0, 0, 1, 1, 1, 1, 4, 16, 23, 27, 29]
+    lo = [96, 127, -128, -1, 0, 1, 127, -128, -1, 0, 44, -24, -96, 112, 88, -24]
+    assert code[0] == 1
+    assert lay.shape == (1, 32)
+    assert list(lay[0, :16].view(np.int8)) == hi
+    assert list(lay[0, 16:].view(np.int8)) == lo
 
 
 @pytest.mark.parametrize("bias_rows", [False, True])
@@ -74,8 +78,8 @@ def test_linear_on_planes_equals_integer_product(bias_rows):
     z = np.where(np.arange(d) % 3 == 0, 0, 100) if bias_rows else np.full(d, 100)
     lay, code = oracle.plane_store(m, z, np.full(d, 128), 8, 8)
     assert (code == 3).any() == bias_rows
-    g = lay.view(np.int8).astype(np.int64).reshape(d, n // 16, 32)
-    hi, lo = g[:, :, :16].reshape(d, n), g[:, :, 16:].reshape(d, n)
+    g = lay.view(np.int8).astype(np.int64)
+    hi, lo = g[:, :n], g[:, n:]
     x = xq.astype(np.int64)
     exact = 256 * (x @ hi.T) + x @ lo.T + 128 * x.sum(axis=1)[:, None] * ((code >> 1) & 1)[None, :]
     assert np.array_equal(exact, x @ m.T)
