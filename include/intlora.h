@@ -330,8 +330,9 @@ int intlora_quant_act(int64_t M, int64_t n, const float* X, int8_t* xq, float* s
  *   y = RN32(RN32(float(exact) * s_x[t]) * s_bar[i]),  Y = bf16 round-to-nearest-even.
  * wfmt INTLORA_W_INT8 / INTLORA_W_INT4 (SHIFT merged integers): one int8 MFMA pass.
  * wfmt INTLORA_W_INT16 (MUL merged integers): two int8 MFMA passes over a byte split
- * of m (x_rowsum required), one split for the whole call, chosen from the split codes
- * m_split[i] (uint8 per row, 0 or 1; NULL = all 1):
+ * of m (x_rowsum required), one split for the whole call (for M <= 32: for each block
+ * of 16 consecutive rows), chosen from the split codes m_split[i] (uint8 per row, 0 or
+ * 1; NULL = all 1):
  *   some row coded 1 (any int16): bias split hi = m >> 8, lo = (m & 0xFF) - 128,
  *      exact = 256 acc_hi + acc_lo + 128 x_rowsum[t];
  *   every row coded 0 (the caller guarantees each m[i, j] <= 32639, as the codes

@@ -461,6 +461,29 @@ __device__ __forceinline__ void tile_coords(int tile, int tiles_m, int tiles_n, 
   tn = in_group / gsize;
 }
 
+// Whether any of the d codes (16-byte aligned) is not zero, for this thread's share:
+// the block's threads together cover all d and the caller combines their flags.  A
+// thread's loads carry no branch between them, so for d <= 64 blockDim.x the whole scan
+// costs one memory round trip.
+__device__ __forceinline__ int any_code(const uint8_t* __restrict__ code, int64_t d) {
+  const int64_t d16 = d & ~(int64_t)15;
+  const int64_t stride = 16 * (int64_t)blockDim.x;
+  int fl = 0;
+  for (int64_t x0 = 16 * (int64_t)threadIdx.x; x0 < d16; x0 += 4 * stride) {
+    uint4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t x = x0 + u * stride;
+      v[u] = x < d16 ? *reinterpret_cast<const uint4*>(code + x) : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) fl |= (int)((v[u].x | v[u].y | v[u].z | v[u].w) != 0u);
+  }
+  const int64_t k = d16 + threadIdx.x;
+  if (k < d) fl |= (int)(code[k] != 0);
+  return fl;
+}
+
 // Persistent kernel: each block owns the tiles r * G + slot (r = 0, 1, ...), where G is
 // the grid size and slot renumbers the block so that each of the 8 XCDs (blocks are
 // dealt to them round-robin) receives a contiguous range of slots, i.e. a compact
@@ -551,20 +574,7 @@ __device__ __forceinline__ void linear_body(uint8_t* __restrict__ lds, int64_t M
   // else balanced.  The codes are read before the first stages are issued and voted
   // on at the prologue's barrier.
   int fl = 0;
-  if (F == F_INT16) {
-    if (split == nullptr) {
-      fl = 1;
-    } else {
-      for (int64_t i = 16 * (int64_t)tid; i < d; i += 16 * kThreads) {
-        if (i + 16 <= d) {
-          const uint4 v = *reinterpret_cast<const uint4*>(split + i);
-          fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
-        } else {
-          for (int64_t k = i; k < d; ++k) fl |= (int)(split[k] != 0);
-        }
-      }
-    }
-  }
+  if (F == F_INT16) fl = split == nullptr ? 1 : any_code(split, d);
 
   // stages 0..2 of the stream (KT >= 3 whenever a block owns more than one tile)
 #pragma unroll
@@ -824,15 +834,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear_planes(int64_t M, i
   extern __shared__ __attribute__((aligned(1024))) uint8_t lds[];
   __shared__ int vote[4];
   const int tid = threadIdx.x;
-  int fl = 0;
-  for (int64_t i = 16 * (int64_t)tid; i < d; i += 16 * kThreads) {
-    if (i + 16 <= d) {
-      const uint4 v = *reinterpret_cast<const uint4*>(code + i);
-      fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
-    } else {
-      for (int64_t k = i; k < d; ++k) fl |= (int)(code[k] != 0);
-    }
-  }
+  const int fl = any_code(code, d);
   if ((tid & 63) == 0) vote[tid >> 6] = 0;
   __syncthreads();
   if (__builtin_amdgcn_ballot_w64(fl != 0) != 0 && (tid & 63) == 0) vote[tid >> 6] = 1;
@@ -853,7 +855,7 @@ __global__ __launch_bounds__(lin::kThreads, 1) void k_linear_planes(int64_t M, i
 // A operand (lane l: row l % 16, K 16 (l / 16) .. + 15 of the step) and 16 tokens as B
 // (lane l: token l % 16, same K); lane l, register v of the result hold output row
 // 4 (l / 16) + v and token l % 16.  Formats as in the tiled kernel: INT16 through the
-// same byte split (one split per launch, voted from the split codes), INT4 through the
+// same byte split (one split per block of 16 rows, from their split codes), INT4 through the
 // same 16 w unpack.  Loads run four steps ahead from clamped (always valid) addresses;
 // K chunks past n, and the steps that pad a wave's quarter to a multiple of four, are
 // zeroed on the token side.  The four waves' int32 sums are added
@@ -874,7 +876,6 @@ __device__ __forceinline__ void skinny_body(int64_t M, int64_t d, int64_t n, con
                                             const int32_t* __restrict__ zbar_p, const int32_t* __restrict__ zw_p) {
   constexpr int PL = (F == F_INT16 || F == F_UW4 || F == F_P16T) ? 2 : 1;  // byte planes
   __shared__ int red[4][PL * TT][4][64];
-  __shared__ int vote;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int64_t i0 = (int64_t)blockIdx.x * 16;
   const int rl = lane & 15, kg = lane >> 4;
@@ -933,24 +934,13 @@ __device__ __forceinline__ void skinny_body(int64_t M, int64_t d, int64_t n, con
     }
   };
 
+  // INT16: the split of the block's own 16 rows (their outputs depend on nothing else):
+  // bias when some row's code is 1, or when there are no codes.  Every wave reads the
+  // same 16 codes, so the choice is uniform over the block.
   bool bias = false;
   if (F == F_INT16) {
-    if (tid == 0) vote = split == nullptr ? 1 : 0;
-    __syncthreads();
-    int fl = 0;
-    if (split) {
-      for (int64_t x = 16 * (int64_t)tid; x < d; x += 16 * 256) {
-        if (x + 16 <= d) {
-          const uint4 v = *reinterpret_cast<const uint4*>(split + x);
-          fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
-        } else {
-          for (int64_t k = x; k < d; ++k) fl |= (int)(split[k] != 0);
-        }
-      }
-    }
-    if (fl) vote = 1;  // every writer stores 1
-    __syncthreads();
-    bias = vote != 0;
+    const int c = split == nullptr ? 1 : (i0 + rl < d ? (int)split[i0 + rl] : 0);
+    bias = __builtin_amdgcn_ballot_w64(c != 0) != 0;
   }
   v4i acc[PL][TT];
 #pragma unroll
@@ -1071,7 +1061,8 @@ __global__ __launch_bounds__(256) void k_linear_skinny(int64_t M, int64_t d, int
   skinny_body<F, TT>(M, d, n, xq, sx, rowsum, m, split, sbar, Y, acc_dbg, wdelta, zbar_p, zw_p);
 }
 
-// Byte planes at few tokens: the low planes alone when every plane code is 0.
+// Byte planes at few tokens: a block multiplies the low planes alone when the plane codes
+// of its 16 rows are all 0.
 template <int TT>
 __global__ __launch_bounds__(256) void k_linear_skinny_planes(int64_t M, int64_t d, int64_t n,
                                                              const int8_t* __restrict__ xq,
@@ -1081,22 +1072,10 @@ __global__ __launch_bounds__(256) void k_linear_skinny_planes(int64_t M, int64_t
                                                              const uint8_t* __restrict__ code,
                                                              const float* __restrict__ sbar, uint16_t* __restrict__ Y,
                                                              int32_t* __restrict__ acc_dbg) {
-  __shared__ int nz;
-  const int tid = threadIdx.x;
-  if (tid == 0) nz = 0;
-  __syncthreads();
-  int fl = 0;
-  for (int64_t x = 16 * (int64_t)tid; x < d; x += 16 * 256) {
-    if (x + 16 <= d) {
-      const uint4 v = *reinterpret_cast<const uint4*>(code + x);
-      fl |= (int)((v.x | v.y | v.z | v.w) != 0u);
-    } else {
-      for (int64_t k = x; k < d; ++k) fl |= (int)(code[k] != 0);
-    }
-  }
-  if (fl) nz = 1;  // every writer stores 1
-  __syncthreads();
-  if (nz == 0)
+  // the plane codes of the block's own 16 rows (read by every wave: a uniform choice)
+  const int64_t r = (int64_t)blockIdx.x * 16 + (threadIdx.x & 15);
+  const int c = r < d ? (int)code[r] : 0;
+  if (__builtin_amdgcn_ballot_w64(c != 0) == 0)
     skinny_body<F_P16N, TT>(M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, 0, nullptr, nullptr);
   else
     skinny_body<F_P16T, TT>(M, d, n, xq, sx, rowsum, m, code, sbar, Y, acc_dbg, 0, nullptr, nullptr);

@@ -455,8 +455,18 @@ def _int16_weights(rng, d, n, capped):
 
 
 def launch_split(sp):
-    """The split the GEMM applies to every row: bias (1) when some row's code is 1."""
+    """The split the tiled GEMM applies to every row: bias (1) when some row's code is 1."""
     return np.full(np.asarray(sp).size, int(np.asarray(sp).any()), np.uint8)
+
+
+def block_split(sp, rows=16):
+    """The split the few-token kernel (M <= 32) applies: per block of 16 consecutive rows,
+    bias (1) when some row of the block has code 1 (no other row's output depends on it)."""
+    sp = np.asarray(sp).reshape(-1)
+    out = np.zeros(sp.size, np.uint8)
+    for b0 in range(0, sp.size, rows):
+        out[b0:b0 + rows] = int(sp[b0:b0 + rows].any())
+    return out
 
 
 def _linear_case(ops, M, d, n, wfmt, seed):
@@ -483,7 +493,8 @@ def _linear_case(ops, M, d, n, wfmt, seed):
         Yh = host(Y).view(np.uint16)
         acc = host(acc)
         if wfmt == 16:
-            hi, lo = oracle.byte_planes(m, split=None if sp is None else launch_split(sp))
+            rule = block_split if M <= 32 else launch_split
+            hi, lo = oracle.byte_planes(m, split=None if sp is None else rule(sp))
             assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
             assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
         else:
