@@ -536,21 +536,17 @@ __device__ __forceinline__ void add_saturations(unsigned long long* sat, int loc
 typedef float vf4 __attribute__((ext_vector_type(4)));
 typedef int vi4 __attribute__((ext_vector_type(4)));
 typedef unsigned int vu2 __attribute__((ext_vector_type(2)));
-// 16-byte load that does not keep the line in the caches (U is read once).
-__device__ __forceinline__ float4 load_once4(const float* p) {
-  const vf4 v = __builtin_nontemporal_load(reinterpret_cast<const vf4*>(p));
+// Plain (cached) vector loads and stores.  The U scratch the adaptation kernel has just
+// written is read back largely from the Infinity Cache, and the merged integers stay
+// there for the linear layer that reads them next; with non-temporal hints both round
+// trips went to HBM (the FLUX block's step was 4 % slower).
+__device__ __forceinline__ float4 load4f(const float* p) {
+  const vf4 v = *reinterpret_cast<const vf4*>(p);
   return make_float4(v.x, v.y, v.z, v.w);
 }
-// Streaming stores of the merged integers (written once, read by a later kernel).
-__device__ __forceinline__ void store_once16(void* p, int4 v) {
-  __builtin_nontemporal_store(vi4{v.x, v.y, v.z, v.w}, reinterpret_cast<vi4*>(p));
-}
-__device__ __forceinline__ void store_once8(void* p, uint2 v) {
-  __builtin_nontemporal_store(vu2{v.x, v.y}, reinterpret_cast<vu2*>(p));
-}
-__device__ __forceinline__ void store_once4(void* p, uint32_t v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<uint32_t*>(p));
-}
+__device__ __forceinline__ void store16(void* p, int4 v) { *reinterpret_cast<vi4*>(p) = vi4{v.x, v.y, v.z, v.w}; }
+__device__ __forceinline__ void store8(void* p, uint2 v) { *reinterpret_cast<vu2*>(p) = vu2{v.x, v.y}; }
+__device__ __forceinline__ void store4(void* p, uint32_t v) { *reinterpret_cast<uint32_t*>(p) = v; }
 
 constexpr int kQThreads = 128;
 constexpr int kQElems = 8;
@@ -729,8 +725,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         const int64_t i = i0 + rr;
         if (i < d && j0 < n) {
           cw[rr] = load_codes8<W4>(wround, i, n, j0);
-          ua[rr] = load_once4(U + i * n + j0);
-          ub[rr] = load_once4(U + i * n + j0 + 4);
+          ua[rr] = load4f(U + i * n + j0);
+          ub[rr] = load4f(U + i * n + j0 + 4);
         }
       }
 #pragma unroll
@@ -763,7 +759,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           uint32_t pk = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk |= (uint32_t)ur[e] << (4 * e);
-          store_once4(ucode + ((i * n + j0) >> 1), pk);
+          store4(ucode + ((i * n + j0) >> 1), pk);
           continue;
         }
         if (small) {  // |m| <= 32639 for the whole row: no saturation, no bias split
@@ -804,9 +800,9 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
           const uint2 got = make_uint2((uint32_t)__shfl_xor((int)give.x, 1, kWave), (uint32_t)__shfl_xor((int)give.y, 1, kWave));
           uint8_t* grp = reinterpret_cast<uint8_t*>(m) + i * 2 * n + (j0 & ~(int64_t)15);
           if (odd)
-            store_once16(grp + n, make_int4((int)got.x, (int)got.y, (int)lo.x, (int)lo.y));
+            store16(grp + n, make_int4((int)got.x, (int)got.y, (int)lo.x, (int)lo.y));
           else
-            store_once16(grp, make_int4((int)hi.x, (int)hi.y, (int)got.x, (int)got.y));
+            store16(grp, make_int4((int)hi.x, (int)hi.y, (int)got.x, (int)got.y));
           if (small && (hi.x | hi.y) != 0u) split[i] = 1;
         } else {
         int4 pk;
@@ -814,7 +810,7 @@ __global__ __launch_bounds__(kQThreads) void k_quant_mul(int64_t d, int64_t n, i
         pk.y = (int)__builtin_amdgcn_perm((uint32_t)mm[3], (uint32_t)mm[2], 0x05040100u);
         pk.z = (int)__builtin_amdgcn_perm((uint32_t)mm[5], (uint32_t)mm[4], 0x05040100u);
         pk.w = (int)__builtin_amdgcn_perm((uint32_t)mm[7], (uint32_t)mm[6], 0x05040100u);
-        store_once16(m + i * n + j0, pk);
+        store16(m + i * n + j0, pk);
         }
         if (uround_dbg) {
           uint2 pu;
@@ -873,8 +869,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_ptq(int64_t d, int64_t n, i
       for (int rr = 0; rr < kQRows; ++rr) {
         const int64_t i = i0 + rr;
         if (i < d && j0 < n) {
-          xa[rr] = load_once4(X + i * n + j0);
-          xb[rr] = load_once4(X + i * n + j0 + 4);
+          xa[rr] = load4f(X + i * n + j0);
+          xb[rr] = load4f(X + i * n + j0 + 4);
         }
       }
 #pragma unroll
@@ -907,12 +903,12 @@ __global__ __launch_bounds__(kQThreads) void k_quant_ptq(int64_t d, int64_t n, i
           uint32_t pk = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk |= (uint32_t)cd[e] << (4 * e);
-          store_once4(code + i * (n >> 1) + (j0 >> 1), pk);
+          store4(code + i * (n >> 1) + (j0 >> 1), pk);
         } else {
           uint2 pk;
           pk.x = (uint32_t)cd[0] | ((uint32_t)cd[1] << 8) | ((uint32_t)cd[2] << 16) | ((uint32_t)cd[3] << 24);
           pk.y = (uint32_t)cd[4] | ((uint32_t)cd[5] << 8) | ((uint32_t)cd[6] << 16) | ((uint32_t)cd[7] << 24);
-          store_once8(code + i * n + j0, pk);
+          store8(code + i * n + j0, pk);
         }
       }
     } else {
@@ -999,8 +995,8 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
         const int64_t i = i0 + rr;
         if (i < d && j0 < n) {
           cw[rr] = load_codes8<W4>(wround, i, n, j0);
-          ua[rr] = load_once4(U + i * n + j0);
-          ub[rr] = load_once4(U + i * n + j0 + 4);
+          ua[rr] = load4f(U + i * n + j0);
+          ub[rr] = load4f(U + i * n + j0 + 4);
         }
       }
 #pragma unroll
@@ -1021,14 +1017,14 @@ __global__ __launch_bounds__(kQThreads) void k_quant_shift(int64_t d, int64_t n,
           uint32_t pk = 0;
 #pragma unroll
           for (int e = 0; e < 8; ++e) pk |= ((uint32_t)mm[e] & 15u) << (4 * e);
-          store_once4(m + i * (n >> 1) + (j0 >> 1), pk);
+          store4(m + i * (n >> 1) + (j0 >> 1), pk);
         } else {
           uint2 pk;
           pk.x = ((uint32_t)mm[0] & 255u) | (((uint32_t)mm[1] & 255u) << 8) | (((uint32_t)mm[2] & 255u) << 16) |
                  ((uint32_t)mm[3] << 24);
           pk.y = ((uint32_t)mm[4] & 255u) | (((uint32_t)mm[5] & 255u) << 8) | (((uint32_t)mm[6] & 255u) << 16) |
                  ((uint32_t)mm[7] << 24);
-          store_once8(m + i * n + j0, pk);
+          store8(m + i * n + j0, pk);
         }
         if (shift_dbg) {
           uint2 ps;
@@ -1668,7 +1664,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
           mm[e] = mv;
         }
         if (quad) {
-          store_once8(m + i * n + j0, make_uint2((uint32_t)(mm[0] & 0xFFFF) | ((uint32_t)mm[1] << 16),
+          store8(m + i * n + j0, make_uint2((uint32_t)(mm[0] & 0xFFFF) | ((uint32_t)mm[1] << 16),
                                                  (uint32_t)(mm[2] & 0xFFFF) | ((uint32_t)mm[3] << 16)));
         } else {
 #pragma unroll
