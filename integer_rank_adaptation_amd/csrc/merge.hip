@@ -342,67 +342,172 @@ __global__ __launch_bounds__(256, (R > 32 ? 2 : 3)) void k_adapt_mfma(int64_t d,
       // reciprocal-table entry of w = code - zi is code + (255 - zc): exact when zi is in
       // [0, 255]; other rows take the IEEE division and only need an index in range
       const int rbase = 255 - min(max(zi, 0), 255);
-      // accumulator group g = 4 blk + q: columns jw + 32 blk + 8 q + 4 h + 0..3
+      // The Gaussian and Cauchy samplers' longer chains do not fit the registers of
+      // interleaved groups (they spilled): those laws keep one group at a time, with the
+      // IEEE division behind a branch in each group.
+      if constexpr (DIST == kAuxGauss || DIST == kAuxCauchy) {
+        // accumulator group g = 4 blk + q: columns jw + 32 blk + 8 q + 4 h + 0..3
 #pragma unroll
-      for (int g = 0; g < 8; ++g) {
-        const int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
-        if (jg >= n) continue;  // n % 4 == 0: a group is entirely inside or outside
-        int code[4], w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          code[e] = W4 ? (int)((wcode[g] >> (4 * e)) & 15u) : (int)((wcode[g] >> (8 * e)) & 255u);
-          w[e] = code[e] - zi;
-        }
-        float y[4];  // reciprocals of w, read first: the Philox rounds cover the LDS latency
-        if (!PTQ) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) y[e] = rcp[code[e] + rbase];
-        }
-        const U4 rnd = philox_block((qrow + (uint64_t)jg) >> 2, layer_id, seed);
-        float rs[4];
-        if (DIST == kAuxLaplace) {
-          float L[4];
-          laplace4(rnd, tab, L);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rs[e] = ci * L[e];
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) rs[e] = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
-        }
-        float u[4], t[4], q[4];
-        if (PTQ) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) q[e] = (si * (float)w[e] + rs[e]) + acc[4 * g + e];  // binary32, in this order
-        } else {
-          // the steps of div_small_int are exact for 2^-100 <= |t| < 2^100, i.e. biased
-          // exponents 27 .. 226 (NaN and inf have 255); the group's extremes decide
-          int emin = 255, emax = 0;
+        for (int g = 0; g < 8; ++g) {
+          const int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
+          if (jg >= n) continue;  // n % 4 == 0: a group is entirely inside or outside
+          int code[4], w[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            t[e] = rs[e] + acc[4 * g + e];
-            q[e] = div_small_int(t[e], (float)w[e], y[e]);
-            const int ex = (int)((__float_as_uint(t[e]) >> 23) & 0xFFu);
-            emin = min(emin, ex);
-            emax = max(emax, ex);
+            code[e] = W4 ? (int)((wcode[g] >> (4 * e)) & 15u) : (int)((wcode[g] >> (8 * e)) & 255u);
+            w[e] = code[e] - zi;
           }
-          const bool slow = !zok || emin < 27 || emax > 226;
-          // the IEEE division runs only in waves where some lane needs it
-          if (__builtin_amdgcn_ballot_w64(slow) != 0) {
-            __asm__ volatile("");  // keeps the branch: the division is not speculated
+          float y[4];  // reciprocals of w, read first: the Philox rounds cover the LDS latency
+          if (!PTQ) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (w[e] != 0 && (!zok || !div_small_int_ok(t[e]))) q[e] = t[e] / (float)w[e];
+            for (int e = 0; e < 4; ++e) y[e] = rcp[code[e] + rbase];
+          }
+          const U4 rnd = philox_block((qrow + (uint64_t)jg) >> 2, layer_id, seed);
+          float rs[4];
+          if (DIST == kAuxLaplace) {
+            float L[4];
+            laplace4(rnd, tab, L);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs[e] = ci * L[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs[e] = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
+          }
+          float u[4], t[4], q[4];
+          if (PTQ) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[e] = (si * (float)w[e] + rs[e]) + acc[4 * g + e];  // binary32, in this order
+          } else {
+            // the steps of div_small_int are exact for 2^-100 <= |t| < 2^100, i.e. biased
+            // exponents 27 .. 226 (NaN and inf have 255); the group's extremes decide
+            int emin = 255, emax = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              t[e] = rs[e] + acc[4 * g + e];
+              q[e] = div_small_int(t[e], (float)w[e], y[e]);
+              const int ex = (int)((__float_as_uint(t[e]) >> 23) & 0xFFu);
+              emin = min(emin, ex);
+              emax = max(emax, ex);
+            }
+            const bool slow = !zok || emin < 27 || emax > 226;
+            // the IEEE division runs only in waves where some lane needs it
+            if (__builtin_amdgcn_ballot_w64(slow) != 0) {
+              __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (w[e] != 0 && (!zok || !div_small_int_ok(t[e]))) q[e] = t[e] / (float)w[e];
+            }
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const bool valid = PTQ || w[e] != 0;
+            u[e] = PTQ ? q[e] : si + q[e];  // U of a w == 0 element is written but never read
+            const int key = f32_key(u[e]);
+            kmin = valid ? min(kmin, key) : kmin;
+            kmax = valid ? max(kmax, key) : kmax;
+          }
+          *reinterpret_cast<float4*>(U + i * n + jg) = make_float4(u[0], u[1], u[2], u[3]);
+        }
+      } else {
+        // The values u[e] of accumulator group g (g = 4 blk + q: columns jw + 32 blk + 8 q +
+        // 4 h + 0..3, starting at jg) and whether each enters the row range.  The fast form
+        // divides with div_small_int and returns true when the group is not certainly exact
+        // (some t outside the window, or a zero point outside the code range): its values
+        // are then excluded here and recomputed by the IEEE form after all groups.  With no
+        // branch inside a group, the eight groups form one straight run that the compiler
+        // interleaves (one group's Philox rounds and table reads beside another's ln).
+        auto group = [&](int g, int64_t jg, auto ieee_tag, float (&u)[4], bool (&valid)[4]) -> bool {
+          constexpr bool IEEE = decltype(ieee_tag)::value;
+          int code[4], w[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            code[e] = W4 ? (int)((wcode[g] >> (4 * e)) & 15u) : (int)((wcode[g] >> (8 * e)) & 255u);
+            w[e] = code[e] - zi;
+          }
+          float y[4];  // reciprocals of w, read first: the Philox rounds cover the LDS latency
+          if (!PTQ) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) y[e] = rcp[code[e] + rbase];
+          }
+          const U4 rnd = philox_block((qrow + (uint64_t)jg) >> 2, layer_id, seed);
+          float rs[4];
+          if (DIST == kAuxLaplace) {
+            float L[4];
+            laplace4(rnd, tab, L);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs[e] = ci * L[e];
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rs[e] = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
+          }
+          float q[4];
+          bool slow = false;
+          if (PTQ) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) q[e] = (si * (float)w[e] + rs[e]) + acc[4 * g + e];  // binary32, in this order
+          } else {
+            // the steps of div_small_int are exact for 2^-100 <= |t| < 2^100, i.e. biased
+            // exponents 27 .. 226 (NaN and inf have 255); the group's extremes decide
+            int emin = 255, emax = 0;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float t = rs[e] + acc[4 * g + e];
+              q[e] = div_small_int(t, (float)w[e], y[e]);
+              if (IEEE && w[e] != 0 && (!zok || !div_small_int_ok(t))) q[e] = t / (float)w[e];
+              const int ex = (int)((__float_as_uint(t) >> 23) & 0xFFu);
+              emin = min(emin, ex);
+              emax = max(emax, ex);
+            }
+            slow = !IEEE && (!zok || emin < 27 || emax > 226);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            valid[e] = PTQ || (w[e] != 0 && !slow);
+            u[e] = PTQ ? q[e] : si + q[e];  // U of a w == 0 element is written but never read
+          }
+          return slow;
+        };
+        auto emit = [&](int64_t jg, const float (&u)[4], const bool (&valid)[4]) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int key = f32_key(u[e]);
+            kmin = valid[e] ? min(kmin, key) : kmin;
+            kmax = valid[e] ? max(kmax, key) : kmax;
+          }
+          *reinterpret_cast<float4*>(U + i * n + jg) = make_float4(u[0], u[1], u[2], u[3]);
+        };
+        uint32_t slow_groups = 0;
+        auto fast = [&](auto whole_tag) {
+          constexpr bool WHOLE = decltype(whole_tag)::value;  // the wave's 64 columns lie inside n
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            const int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
+            if (!WHOLE && jg >= n) continue;  // n % 4 == 0: a group is entirely inside or outside
+            float u[4];
+            bool valid[4];
+            const bool slow = group(g, jg, std::false_type{}, u, valid);
+            slow_groups |= (uint32_t)slow << g;
+            emit(jg, u, valid);
+          }
+        };
+        if (jw + 64 <= n)
+          fast(std::true_type{});
+        else
+          fast(std::false_type{});
+        // the IEEE division runs only in waves where some lane needs it; its stores replace
+        // the fast ones (same thread, later in program order)
+        if (!PTQ && __builtin_amdgcn_ballot_w64(slow_groups != 0) != 0) {
+          __asm__ volatile("");  // keeps the branch: the division is not speculated
+#pragma unroll
+          for (int g = 0; g < 8; ++g) {
+            if (((slow_groups >> g) & 1u) == 0) continue;
+            const int64_t jg = jw + 32 * (g >> 2) + 8 * (g & 3) + 4 * h;
+            float u[4];
+            bool valid[4];
+            group(g, jg, std::true_type{}, u, valid);
+            emit(jg, u, valid);
           }
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool valid = PTQ || w[e] != 0;
-          u[e] = PTQ ? q[e] : si + q[e];  // U of a w == 0 element is written but never read
-          const int key = f32_key(u[e]);
-          kmin = valid ? min(kmin, key) : kmin;
-          kmax = valid ? max(kmax, key) : kmax;
-        }
-        *reinterpret_cast<float4*>(U + i * n + jg) = make_float4(u[0], u[1], u[2], u[3]);
       }
     }
     // lanes l and l ^ 32 hold the same row; each wave writes the partial of its own 64
@@ -1473,7 +1578,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
     }
     if (!done) {
       int kmin[RB], kmax[RB];
-  #pragma unroll
+#pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
         kmin[rr] = kKeyPosInf;
         kmax[rr] = kKeyNegInf;
@@ -1482,9 +1587,9 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
         const int64_t j0 = 4 * ((int64_t)tid + 256 * g);
         if (j0 >= n) break;
         float acc[RB][4];
-  #pragma unroll
+#pragma unroll
         for (int rr = 0; rr < RB; ++rr)
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) acc[rr][e] = 0.0f;
         if (quad) {
           // B is read in chunks of KU rows, all loads of a chunk issued together and the
@@ -1493,11 +1598,11 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
           // loads need no branch; a clamped k is never used.
           constexpr int KU = RB >= 8 ? 2 : RB >= 4 ? 4 : 8;  // shorter chunks where more rows share a load
           float4 bc[KU], bn[KU];
-  #pragma unroll
+#pragma unroll
           for (int kk = 0; kk < KU; ++kk)
             bc[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(kk < r ? kk : r - 1) * n + j0);
           for (int k0 = 0; k0 < r; k0 += KU) {
-  #pragma unroll
+#pragma unroll
             for (int kk = 0; kk < KU; ++kk) {
               const int k = k0 + KU + kk;
               bn[kk] = *reinterpret_cast<const float4*>(B + (int64_t)(k < r ? k : r - 1) * n + j0);
@@ -1505,9 +1610,9 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
             // A[rows][k0 .. k0 + KU) with vector LDS reads (k0 is a multiple of KU, the
             // pitch a multiple of 4; entries past r are read but never used)
             float av[RB][KU];
-  #pragma unroll
+#pragma unroll
             for (int rr = 0; rr < RB; ++rr) {
-  #pragma unroll
+#pragma unroll
               for (int c = 0; c < KU; c += (KU >= 4 ? 4 : 2)) {
                 if (KU >= 4) {
                   const float4 v = *reinterpret_cast<const float4*>(sA + rr * RP + k0 + c);
@@ -1522,33 +1627,33 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
                 }
               }
             }
-  #pragma unroll
+#pragma unroll
             for (int kk = 0; kk < KU; ++kk) {
               if (k0 + kk < r) {  // uniform over the block
                 const float b[4] = {bc[kk].x, bc[kk].y, bc[kk].z, bc[kk].w};
-  #pragma unroll
+#pragma unroll
                 for (int rr = 0; rr < RB; ++rr)
-  #pragma unroll
+#pragma unroll
                   for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(av[rr][kk], b[e], acc[rr][e]);
               }
             }
-  #pragma unroll
+#pragma unroll
             for (int kk = 0; kk < KU; ++kk) bc[kk] = bn[kk];
           }
         } else {
           for (int k = 0; k < r; ++k) {
             float b[4];
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) b[e] = j0 + e < n ? B[(int64_t)k * n + j0 + e] : 0.0f;
-  #pragma unroll
+#pragma unroll
             for (int rr = 0; rr < RB; ++rr) {
               const float a = sA[rr * RP + k];
-  #pragma unroll
+#pragma unroll
               for (int e = 0; e < 4; ++e) acc[rr][e] = fmaf(a, b[e], acc[rr][e]);
             }
           }
         }
-  #pragma unroll
+#pragma unroll
         for (int rr = 0; rr < RB; ++rr) {
           const bool row_ok = i0 + rr < d;
           const int64_t i = row_ok ? i0 + rr : d - 1;  // a row past d is computed, never stored
@@ -1560,13 +1665,13 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
             const uint32_t cv = W4 ? (uint32_t)*reinterpret_cast<const uint16_t*>(wround + ((i * n + j0) >> 1))
                                    : *reinterpret_cast<const uint32_t*>(wround + i * n + j0);
             const U4 rnd = philox_block(((uint64_t)i * (uint64_t)n + (uint64_t)j0) >> 2, layer_id, seed);
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) {
               w[e] = (W4 ? (int)((cv >> (4 * e)) & 15u) : (int)((cv >> (8 * e)) & 255u)) - zi;
               rs[e] = ci * aux_sample<DIST>(rnd, (unsigned)e, tab);
             }
           } else {
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int64_t j = j0 + e < n ? j0 + e : n - 1;
               w[e] = code_at<W4>(wround, i, n, j) - zi;
@@ -1576,7 +1681,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
           float t[4], q[4];
           const bool zok = zero_point_ok(zi);
           bool slow = !zok;
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             t[e] = rs[e] + acc[rr][e];
             q[e] = div_small_int(t[e], (float)w[e], rcp[rcp_index(w[e])]);
@@ -1584,11 +1689,11 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
           }
           if (__builtin_amdgcn_ballot_w64(slow) != 0) {
             __asm__ volatile("");  // keeps the branch: the division is not speculated
-  #pragma unroll
+#pragma unroll
             for (int e = 0; e < 4; ++e)
               if (w[e] != 0 && (!zok || !div_small_int_ok(t[e]))) q[e] = t[e] / (float)w[e];
           }
-  #pragma unroll
+#pragma unroll
           for (int e = 0; e < 4; ++e) {
             const float uu = si + q[e];
             sU[rr * pitch + j0 + e] = uu;
@@ -1601,7 +1706,7 @@ __global__ __launch_bounds__(256) void k_merge_fused(int64_t d, int64_t n, int r
         }
       }
       // each row's range over the block (order keys)
-  #pragma unroll
+#pragma unroll
       for (int rr = 0; rr < RB; ++rr) {
         const int a = wave_min_i32(kmin[rr]), b = wave_max_i32(kmax[rr]);
         if (lane == 0) {
