@@ -111,19 +111,34 @@ __device__ __forceinline__ LnPrep ln_prep(uint32_t G, int bias) {
 // ln(G 2^-bias) for odd G < 2^bias, bias 23 or 24, as the binary64 value before the
 // final rounding (the Gaussian sampler takes its logarithm at bias 24), from its
 // integer part and table entry t = tab[P.k].
+template <bool ESTRIN = true>
 __device__ __forceinline__ double ln_finish(const LnPrep& P, const LnLds& t) {
   const uint32_t F = P.F;
   const int e = P.e;
   const double f = fma((double)F, (double)t.r24, -1.0);  // m r_k - 1, exact
   // log1p(f) = f - f^2/2 + ... - f^8/8 truncated after f^7: |f| <= 2^-7 leaves a
-  // relative error below 2^-52, far under the 2^-47.6 the rounding needs.
-  double p7 = 1.0 / 7.0;
-  p7 = fma(p7, f, -1.0 / 6.0);
-  p7 = fma(p7, f, 1.0 / 5.0);
-  p7 = fma(p7, f, -0.25);
-  p7 = fma(p7, f, 1.0 / 3.0);
-  p7 = fma(p7, f, -0.5);
-  const double lp = fma(f * f, p7, f);
+  // relative error below 2^-52, far under the 2^-47.6 the rounding needs.  The
+  // polynomial p(f) = -1/2 + f/3 - f^2/4 + ... + f^5/7 in log1p(f) = f + f^2 p(f) is
+  // evaluated in Estrin's pairs (three dependent steps instead of Horner's five: in
+  // the adaptation kernel the chain, not the operation count, sets the pace), or by
+  // Horner's rule where registers are short (the Gaussian sampler); either way its
+  // rounding errors are scaled by f^2 <= 2^-14 in the result.
+  const double f2 = f * f;
+  double p7;
+  if (ESTRIN) {
+    const double p01 = fma(1.0 / 3.0, f, -0.5);
+    const double p23 = fma(1.0 / 5.0, f, -0.25);
+    const double p45 = fma(1.0 / 7.0, f, -1.0 / 6.0);
+    p7 = fma(f2, fma(f2, p45, p23), p01);
+  } else {
+    p7 = 1.0 / 7.0;
+    p7 = fma(p7, f, -1.0 / 6.0);
+    p7 = fma(p7, f, 1.0 / 5.0);
+    p7 = fma(p7, f, -0.25);
+    p7 = fma(p7, f, 1.0 / 3.0);
+    p7 = fma(p7, f, -0.5);
+  }
+  const double lp = fma(f2, p7, f);
   // e*ln2 as a head with trailing zeros (exact product) plus a tail
   const double LN2_HI = 0x1.62e42fefa3800p-1;
   const double LN2_LO = 0x1.ef35793c76730p-45;
@@ -133,9 +148,10 @@ __device__ __forceinline__ double ln_finish(const LnPrep& P, const LnLds& t) {
   return head + (lp + tail);
 }
 
+template <bool ESTRIN = true>
 __device__ __forceinline__ double ln_odd_d(uint32_t G, int bias, const LnLds* __restrict__ tab) {
   const LnPrep P = ln_prep(G, bias);
-  return ln_finish(P, tab[P.k]);
+  return ln_finish<ESTRIN>(P, tab[P.k]);
 }
 
 __device__ __forceinline__ float ln_odd_g(uint32_t G, const LnLds* __restrict__ tab) {
@@ -245,7 +261,7 @@ __device__ __forceinline__ float aux_sample(const U4& rnd, unsigned e, const LnL
   if (DIST == kAuxLaplace) return laplace_from_word(pick_word(rnd, e), tab);
   if (DIST == kAuxGauss) {
     const uint32_t w1 = pick_word(rnd, e & 2u), w2 = pick_word(rnd, (e & 2u) | 1u);
-    const float L = (float)ln_odd_d(2u * (w1 >> 9) + 1u, 24, tab);
+    const float L = (float)ln_odd_d<false>(2u * (w1 >> 9) + 1u, 24, tab);
     const float S = sqrtf(-2.0f * L);
     const double v = (double)(2u * (w2 >> 9) + 1u) * 0x1p-23;  // 2 u2, exact
     const float C = (float)((e & 1u) ? sinpi_v(v) : cospi_v(v));
