@@ -978,6 +978,51 @@ def test_linear_planes_bitexact(ops, M, d, n):
     _planes_linear_check(ops, M, m8, z, np.full(d, 128), 8, 8, seed=n + 3, expect_narrow=False)
 
 
+@pytest.mark.parametrize("M", [1, 16, 32])
+def test_few_tokens_blocks_choose_their_own_split(ops, M):
+    """At few tokens (M <= 32) each block of 16 rows picks its byte split (INT16) or its
+    plane form (byte planes) from its own rows' codes: blocks of small rows beside blocks
+    that need the bias split or the high plane, blocks mixing both, and a ragged last
+    block.  Every output and both accumulator planes against the oracle."""
+    d, n = 16 * 7 + 5, 1024
+    rng = np.random.Generator(np.random.PCG64(700 + M))
+    blk = np.arange(d) // 16
+    # INT16: blocks 1, 3 and 6 hold one row with m >= 32640 (code 1); every other row is
+    # capped at 32639 (code 0), so those blocks take the balanced split
+    m = rng.integers(-32768, 32640, size=(d, n))
+    for b in (1, 3, 6):
+        m[16 * b + 5, 7] = 32700
+    sp = oracle.plane_split(m)
+    assert set(blk[sp == 1].tolist()) == {1, 3, 6}
+    xq = rng.integers(-127, 128, size=(M, n)).astype(np.int8)
+    sx = synth.random_positive(701 + M, M, 1e-3, 0.1)
+    sbar = synth.random_positive(702 + M, d, 1e-5, 1e-2)
+    rs = xq.astype(np.int32).sum(axis=1).astype(np.int32)
+    _, _, yref = oracle.linear(xq, sx, m.astype(np.int32), sbar)
+    Y, acc = ops.linear(cuda(xq), cuda(sx), cuda(rs), 16, cuda(m.astype(np.int16)), cuda(sbar), d, acc_dbg=True,
+                        split=cuda(sp))
+    hi, lo = oracle.byte_planes(m, split=block_split(sp))
+    acc = host(acc)
+    assert np.array_equal(acc[0], xq.astype(np.int64) @ hi.T.astype(np.int64))
+    assert np.array_equal(acc[1], xq.astype(np.int64) @ lo.T.astype(np.int64))
+    assert np.array_equal(host(Y).view(np.uint16), yref)
+    # byte planes (8-bit codes): z = z_bar = 128 gives the balanced split, z = 0 the bias
+    # split.  Blocks 0, 2, 4, 6 and the ragged one: small rows (code 0); block 1: values
+    # beyond int8 (code 1); blocks 3 and 5: eight bias rows (code 3) beside small rows.
+    z = np.full(d, 128)
+    zbar = np.full(d, 128)
+    mp = rng.integers(-127, 128, size=(d, n))
+    mp[blk == 1] = rng.integers(-16384, 16385, size=(16, n))
+    for b in (3, 5):
+        rows = np.arange(16 * b, 16 * b + 8)
+        z[rows] = 0
+        mp[rows] = rng.integers(-32768, 32768, size=(8, n))
+    _, code = oracle.plane_store(mp, z, zbar, 8, 8)
+    assert set(blk[code == 1].tolist()) == {1} and set(blk[code == 3].tolist()) == {3, 5}
+    assert not code[blk == 7].any()
+    _planes_linear_check(ops, M, mp, z, zbar, 8, 8, seed=703 + M, expect_narrow=False)
+
+
 PLANE_MERGE_CASES = [(37, 1024, 8, 8, 8), (64, 768, 4, 4, 4), (96, 3072, 32, 4, 4), (33, 1600, 4, 8, 8),
                      (6, 1536, 64, 4, 2)]
 
