@@ -16,7 +16,12 @@ step's time at MI355X peak (merge algorithmic bytes at 8 TB/s HBM plus the GEMM'
 products, each merged integer times each activation counted once as an int8
 multiply-add, at 5.0 POP/s) and T_step the measured time of one step.  T_roof is a
 constant of the workload, so value is inversely proportional to the step time.
-Per-layer merge GB/s and GEMM TOP/s are listed alongside.
+T_step is that of the fastest of the measured schedules of the same kernels whose
+outputs equal the sequential step's (sequential; pipelined, the merges on a second
+stream; each also replayed from a HIP graph), named in `schedule`; every schedule's
+time is listed, and the roofline of the dominant kernel comes from the per-launch
+events of the sequential step.  Per-layer merge GB/s and GEMM TOP/s are listed
+alongside.
 """
 from __future__ import annotations
 
@@ -957,6 +962,18 @@ def main():
         if counters is not None:
             row["counters"] = counters["per_layer"].get(L.name)
         per_layer.append(row)
+    # The step's time is that of the fastest measured schedule of the same kernels whose
+    # outputs were checked equal to the sequential step's: sequential, pipelined (merges
+    # on a second stream), and each replayed from a HIP graph.
+    schedules = {"sequential": ms_per_step}
+    if overlap_ms is not None and overlap_same:
+        schedules["pipelined"] = overlap_ms
+    if graph is not None and graph["replay_equals_eager"]:
+        schedules["sequential_graph"] = graph["ms_per_step"]
+        schedules["pipelined_graph"] = graph["overlap_ms_per_step"]
+    schedule = min(schedules, key=schedules.get)
+    seq_ms_per_step = ms_per_step
+    ms_per_step = schedules[schedule]
     value = 100.0 * roof_ms / ms_per_step
     gemm_avg_ms = gemm_ms_tot / len(layers)
     achieved = gemm_ops_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e12
@@ -970,6 +987,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "schedule": schedule,
+        "schedules_ms_per_step": {k: round(v, 4) for k, v in schedules.items()},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
