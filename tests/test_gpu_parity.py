@@ -763,6 +763,68 @@ def test_graph_replay_matches_eager(ops):
             assert torch.equal(a, b), rep
 
 
+def test_pipelined_step_matches_sequential(ops):
+    """The pipelined schedule the benchmark may time: each layer's byte-plane merge on a
+    second stream, its linear layer on the first waiting only for that merge, the second
+    stream forked at the start of a step and joined at its end (so no merge rewrites a
+    layer's planes while the previous step's linear layer reads them).  Three layers,
+    four pipelined steps back to back, then three more with eager work and zeroed outputs
+    in between; every output equals the sequential step's."""
+    shapes = [(512, 1536), (256, 1536), (768, 512)]
+    M = 600
+    layers = []
+    for k, (d, n) in enumerate(shapes):
+        wr, z, s, c, A, Bm = random_state(900 + k, d, n, 8, 4)
+        st = gpu_state(wr, z, s, c, 4)
+        rng = np.random.Generator(np.random.PCG64(910 + k))
+        xq, sx, rs = ops.quant_act(cuda(rng.normal(0.0, 1.0, (M, n)).astype(np.float32)))
+        ws = ops.workspace(ops.B.INTLORA_OP_MERGE_MUL, d, n, 8, 4, xq.device)
+        Ag, Bg = cuda(A), cuda(Bm)
+        o = ops.merge_mul_planes(st, Ag, Bg, 4, 4, 3, k, ws=ws)
+        Y = torch.empty((M, d), dtype=torch.int16, device=xq.device)
+        layers.append(dict(st=st, Ag=Ag, Bg=Bg, xq=xq, sx=sx, rs=rs, ws=ws, o=o, Y=Y, d=d, k=k))
+
+    def merge(ly):
+        ops.merge_mul_planes(ly["st"], ly["Ag"], ly["Bg"], 4, 4, 3, ly["k"], ws=ly["ws"], out=ly["o"])
+
+    def gemm(ly):
+        ops.linear(ly["xq"], ly["sx"], ly["rs"], ops.B.INTLORA_W_INT16_PLANES, ly["o"]["planes"], ly["o"]["sbar"],
+                   ly["d"], out=ly["Y"], split=ly["o"]["code"])
+
+    for ly in layers:
+        merge(ly)
+        gemm(ly)
+    torch.cuda.synchronize()
+    ref = [(ly["o"]["planes"].clone(), ly["o"]["code"].clone(), ly["Y"].clone()) for ly in layers]
+    side = torch.cuda.Stream()
+    done = [torch.cuda.Event() for _ in layers]
+
+    def pipelined():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        for j, ly in enumerate(layers):
+            with torch.cuda.stream(side):
+                merge(ly)
+                done[j].record(side)
+            cur.wait_event(done[j])
+            gemm(ly)
+        cur.wait_stream(side)
+
+    for rep in range(7):
+        if rep >= 4:
+            for ly in layers:
+                ly["Y"].zero_()
+                ly["o"]["planes"].zero_()
+            ops.quant_act(cuda(np.ones((4, 64), np.float32)))  # unrelated eager work
+        pipelined()
+        if rep >= 3:
+            torch.cuda.synchronize()
+            for ly, (p_ref, c_ref, y_ref) in zip(layers, ref):
+                assert torch.equal(ly["o"]["planes"], p_ref), rep
+                assert torch.equal(ly["o"]["code"], c_ref), rep
+                assert torch.equal(ly["Y"], y_ref), rep
+
+
 # ----------------------------------------------------------------------------- auxiliary laws
 # The distribution ablation of the auxiliary matrix ([IntLoRA summary], "Measured
 # effects": Laplace against Gaussian, Cauchy and Student-t samples).
