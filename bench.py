@@ -12,9 +12,10 @@ out 3072x3072, mlp 12288x3072 and 3072x12288), W4A8, MUL with a 4-bit adaptation
 term, rank 32, 4608 tokens.
 
 Printed (rank 0, one JSON line): value = 100 * T_roof / T_step, where T_roof is the
-step's time at MI355X peak (merge algorithmic bytes at 8 TB/s HBM plus the GEMM's
-products, each merged integer times each activation counted once as an int8
-multiply-add, at 5.0 POP/s) and T_step the measured time of one step.  T_roof is a
+step's time at MI355X peak (merge algorithmic bytes at 8 TB/s HBM plus, per linear
+layer, the longer of its products -- each merged integer times each activation counted
+once as an int8 multiply-add -- at 5.0 POP/s and its bytes at 8 TB/s) and T_step the
+measured time of one step.  T_roof is a
 constant of the workload, so value is inversely proportional to the step time.
 T_step is that of the fastest of the measured schedules of the same kernels whose
 outputs equal the sequential step's (sequential; pipelined, the merges on a second
@@ -128,10 +129,23 @@ def gemm_exec_ops(M, d, n, mode, planes=None):
     return 2.0 * M * d * n * passes
 
 
+def gemm_alg_bytes(M, d, n, mode, w_bits, nplanes):
+    """HBM bytes the linear layer needs: the int8 activations, the stored weights (MUL:
+    one byte per multiplied plane, or the int16 integers; SHIFT: the w_bits codes) and
+    the bf16 outputs."""
+    if mode == "mul":
+        wb = 2.0 if nplanes is None else float(nplanes)
+    else:
+        wb = w_bits / 8.0
+    return float(M) * n + d * n * wb + 2.0 * M * d
+
+
 def planes_multiplied(M, d, n, any_code, torch):
     """Byte planes the linear layer multiplies on the byte-plane storage: one when every
     plane code is 0 and (above 32 tokens) its 256-output tiles take fewer rounds of the
-    persistent grid than the two-plane tiles -- the library's launch rule -- else two."""
+    persistent grid than the two-plane tiles -- the library's launch rule -- else two.
+    (At most 32 tokens the kernel decides per block of 16 rows; the workloads' codes are
+    uniform over a layer, so the layer-wide answer is the same.)"""
     if any_code:
         return 2
     if M <= 32:
@@ -917,6 +931,7 @@ def main():
     per_layer = []
     roof_ms = 0.0
     merge_bytes_tot = merge_ms_tot = gemm_ops_tot = gemm_ms_tot = gemm_eops_tot = 0.0
+    gemm_bytes_tot = gemm_ops_roof_ms = gemm_bytes_roof_ms = 0.0
     for k, lay in enumerate(layers):
         L = lay["L"]
         mms = float(np.mean([ev[s][k][0].elapsed_time(ev[s][k][1]) for s in range(args.steps)]))
@@ -925,7 +940,14 @@ def main():
         nplanes = planes_multiplied(M, L.d, L.n, bool(lay["out"]["code"].any()), torch) if planes else None
         gops = gemm_exec_ops(M, L.d, L.n, mode, nplanes)
         eops = 2.0 * M * L.d * L.n  # the method's int16 x int8 (or int8 x int8) products, once
-        roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + eops / (INT8_PEAK_TOPS * 1e12) * 1e3
+        gb = gemm_alg_bytes(M, L.d, L.n, mode, wl.w_bits, nplanes)
+        # the linear layer at peak: its products at the int8 rate or its bytes at the HBM
+        # rate, whichever takes longer (the bytes, at few tokens or on small layers)
+        roof_ms += mb / (HBM_PEAK_GBPS * 1e9) * 1e3 + max(eops / (INT8_PEAK_TOPS * 1e12),
+                                                          gb / (HBM_PEAK_GBPS * 1e9)) * 1e3
+        gemm_bytes_tot += gb
+        gemm_ops_roof_ms += eops / (INT8_PEAK_TOPS * 1e12) * 1e3
+        gemm_bytes_roof_ms += gb / (HBM_PEAK_GBPS * 1e9) * 1e3
         merge_bytes_tot += mb
         merge_ms_tot += mms
         gemm_ops_tot += gops
@@ -938,6 +960,7 @@ def main():
                    gemm_exec_pct_int8_peak=round(100 * gops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
                    gemm_effective_TOPS=round(eops / (gms * 1e-3) / 1e12, 1),
                    gemm_effective_pct_int8_peak=round(100 * eops / (gms * 1e-3) / 1e12 / INT8_PEAK_TOPS, 2),
+                   gemm_alg_GBps=round(gb / (gms * 1e-3) / 1e9, 1),
                    sat=int(lay["out"]["sat"][0].item()),
                    int16_split=("balanced" if not bool(lay["out"]["split"].any()) else "bias")
                    if "split" in lay["out"] else None)
@@ -976,13 +999,32 @@ def main():
     ms_per_step = schedules[schedule]
     value = 100.0 * roof_ms / ms_per_step
     gemm_avg_ms = gemm_ms_tot / len(layers)
-    achieved = gemm_ops_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e12
+    skinny = M <= 32
+    # The dominant kernel's bound: its products (MFMA) or, at few tokens or on layers too
+    # small to keep the matrix cores busy, its bytes (HBM).
+    gemm_hbm = gemm_bytes_roof_ms > gemm_ops_roof_ms
+    if gemm_hbm:
+        achieved, peak, runit = gemm_bytes_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e9, HBM_PEAK_GBPS, "GB/s"
+    else:
+        achieved, peak, runit = gemm_ops_tot / len(layers) / (gemm_avg_ms * 1e-3) / 1e12, INT8_PEAK_TOPS, "TOP/s"
+    if planes:
+        kname = ("k_linear_skinny_planes (weight streaming" if skinny else
+                 "k_linear_planes (int8 MFMA") + " on the byte-plane storage; planes multiplied per layer: %s)" % [
+                     r.get("gemm_planes_multiplied") for r in per_layer]
+        kprefix = "k_linear_skinny_planes" if skinny else "k_linear_planes"
+    else:
+        kname = ("k_linear_skinny (weight streaming, %s)" if skinny else "k_linear (int8 MFMA, %s)") % (
+            "int16 two-plane" if mode == "mul" else "int%d" % wl.w_bits)
+        kprefix = "k_linear_skinny" if skinny else "k_linear"
+    # counter bytes exist for the token count the profiles were taken at (the workload's own)
+    traffic = traffic_from_profile(wl.name, kprefix) if M == wl.tokens[0] else None
 
     result = {
         "metric": METRIC,
         "value": round(value, 3),
-        "unit": "% of MI355X peak (step time at 8 TB/s HBM for the merge's algorithmic bytes + 5.0 POP/s int8 "
-                "for the GEMM's products counted once, over measured step time)",
+        "unit": "% of MI355X peak (step time at 8 TB/s HBM for the merge's algorithmic bytes + the GEMM at "
+                "5.0 POP/s int8 for its products counted once or at 8 TB/s for its bytes, whichever is longer, "
+                "over measured step time)",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -996,16 +1038,14 @@ def main():
         "data": "synthetic",
         "config": {"workload": wl.name, "layers": [f"{L.name} {L.d}x{L.n}" for L in wl.layers], "tokens": M,
                    "rank": wl.r, "w_bits": wl.w_bits, "mode": mode, "adapt_bits": mbits},
-        "roofline": {"bound": "mfma", "kernel": ("k_linear_planes (int8 MFMA on the byte-plane storage; planes "
-                                                 "multiplied per layer: %s)" % [r.get("gemm_planes_multiplied")
-                                                                                for r in per_layer]) if planes else
-                     "k_linear (int8 MFMA, %s)" % ("int16 two-plane" if mode == "mul" else "int%d" % wl.w_bits),
-                     "achieved": round(achieved, 1), "peak": INT8_PEAK_TOPS, "unit": "TOP/s",
-                     "frac": round(achieved / INT8_PEAK_TOPS, 4), "traffic": traffic_from_profile(wl.name, "k_linear_planes" if planes else "k_linear")},
+        "roofline": {"bound": "hbm" if gemm_hbm else "mfma", "kernel": kname,
+                     "achieved": round(achieved, 1), "peak": peak, "unit": runit,
+                     "frac": round(achieved / peak, 4), "traffic": traffic},
         "merge": {"alg_GBps": round(merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9, 1),
                   "pct_hbm_peak": round(100 * merge_bytes_tot / (merge_ms_tot * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
                   "us_per_step": round(merge_ms_tot * 1e3, 1), "bound": "alu (Philox, the Laplace ln and the division per element in the adaptation kernel)"},
-        "gemm": {"exec_TOPS": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
+        "gemm": {"alg_GBps": round(gemm_bytes_tot / (gemm_ms_tot * 1e-3) / 1e9, 1),
+                 "exec_TOPS": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
                  "exec_frac_int8_peak": round(gemm_ops_tot / (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
                  "effective_TOPS": round(gemm_eops_tot / (gemm_ms_tot * 1e-3) / 1e12, 1),
                  "effective_frac_int8_peak": round(gemm_eops_tot / (gemm_ms_tot * 1e-3) / 1e12 / INT8_PEAK_TOPS, 4),
