@@ -718,8 +718,18 @@ def sweep_measure(args, ops, B, synth, torch, dev, stream):
                        "set up on the GPU; layer id 7 * block + matrix")
 
 
+def stage(name):
+    """Names the part of the run that starts next (stderr, flushed), so that a run that
+    ends abnormally shows where."""
+    sys.stderr.write("[bench] %s\n" % name)
+    sys.stderr.flush()
+
+
 def main():
     args = parse()
+    import faulthandler
+
+    faulthandler.enable()  # a fatal signal prints the Python stack of every thread to stderr
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
@@ -747,6 +757,7 @@ def main():
     mode, mbits = wl.modes[args.mode_index]
 
     # ---------------------------------------------------------------- inputs (untimed)
+    stage("setup (inputs, set-up kernels)")
     t_setup = time.time()
     layers = []
     ws_bytes = 0
@@ -825,6 +836,7 @@ def main():
     def gemm_fn(k):
         run_gemm(layers[k])
 
+    stage("timed step (%d warm-up, %d timed)" % (args.warmup, args.steps))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -841,6 +853,7 @@ def main():
     ms_per_step = total_ms / args.steps
 
     # ---------------------------------------------------------------- per-kernel medians (untimed region)
+    stage("per-kernel medians")
     medians = kernel_medians(args, layers, merge_fn, gemm_fn, torch, dev, stream) if args.kernel_runs > 0 else None
     int16_cmp = None
     if planes and args.kernel_runs > 0:
@@ -850,6 +863,7 @@ def main():
         lib_cmp = library_gemm_medians(args, layers, mode, wl.w_bits, planes, torch, stream)
 
     # ---------------------------------------------------------------- pipelined step (optional)
+    stage("pipelined step")
     # The merges run on a side stream, each layer's linear layer waiting only for its own
     # merge; the side stream forks from the step's stream at the start of the step (so a
     # merge never overwrites m while the previous step's linear layer still reads it) and
@@ -890,6 +904,7 @@ def main():
         overlap_ms = t0_.elapsed_time(t1_) / args.steps
 
     # ---------------------------------------------------------------- the step as a HIP graph (optional)
+    stage("graph replay")
     graph = None
     if not args.no_graph:
         graph = graph_measure(args, layers, step, torch, stream)
@@ -900,33 +915,41 @@ def main():
     # ---------------------------------------------------------------- QLoRA-style comparison
     ptq = None
     if mode == "mul" and not args.no_ptq:
+        stage("QLoRA-style comparison merge")
         ptq = ptq_comparison(args, wl, layers, ws, ops, B, synth, torch, dev, stream)
 
     fused = None
     if mode == "mul" and max(lay["L"].n for lay in layers) <= 16384 and not args.no_fused:
+        stage("fused merge")
         fused = fused_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits)
 
     codes = None
     if mode == "mul" and wl.w_bits == 4 and mbits <= 4 and not args.no_codes:
+        stage("merge keeping the codes + merge-on-load linear layer")
         codes = codes_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mbits)
 
     aux_laws = None
     if not args.no_aux_laws:
+        stage("auxiliary-matrix laws")
         aux_laws = aux_laws_measure(args, wl, layers, ops, synth, torch, dev, ws, stream, mode, mbits)
 
     ste = None
     if not args.no_ste:
+        stage("straight-through backward")
         ste = ste_measure(args, wl, layers, ops, torch, dev, stream)
 
     sweep = None
     if not args.no_sweep and M > 32:
+        stage("merge sweep over every block")
         sweep = sweep_measure(args, ops, B, synth, torch, dev, stream)
 
     grouped = None
     if planes and wl.index in SHARED_INPUT_GROUPS and not args.no_grouped:
+        stage("shared-input groups")
         grouped = grouped_measure(args, wl, layers, ops, synth, torch, dev, stream, mbits, ws)
 
     # ---------------------------------------------------------------- per-layer figures
+    stage("figures")
     counters = profile_counters(wl.name)
     per_layer = []
     roof_ms = 0.0
@@ -1083,6 +1106,7 @@ def main():
                 result[key] = counters[key]
 
     # ---------------------------------------------------------------- CPU baseline (oracle)
+    stage("CPU baseline (oracle)")
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, layers, M, mode, mbits, roof_ms, args.cpu_sample)
     line = json.dumps(result)
