@@ -19,6 +19,7 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+__attribute__((format(printf, 2, 3))) int fail(int status, const char* fmt, ...);
 int fail(int status, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);

@@ -20,7 +20,7 @@ shift 2
 ROOT=$(cd "$(dirname "$0")/.." && pwd)
 mkdir -p "$OUT"
 OUT=$(cd "$OUT" && pwd)
-BENCH=(python3 "$ROOT/bench.py" --workload "$WL" --steps 3 --warmup 1 --no-cpu-baseline --no-ptq --no-fused
+BENCH=(python3 "$ROOT/bench.py" --workload "$WL" --steps 10 --warmup 3 --no-cpu-baseline --no-ptq --no-fused
        --no-codes --no-ste --no-graph --no-overlap --no-aux-laws --no-sweep --no-grouped --no-library-gemm
        --kernel-runs 0 "$@")
 cd /tmp
