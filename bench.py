@@ -162,10 +162,9 @@ def merged_m(lay, torch):
     o = lay["out"]
     if "planes" not in o:
         return o["m"].to(torch.int32)
-    d, n2 = o["planes"].shape
-    g = o["planes"].view(torch.int8).to(torch.int32).view(d, n2 // 32, 32)
-    hi = g[:, :, :16].reshape(d, n2 // 2)
-    lo = g[:, :, 16:].reshape(d, n2 // 2)
+    n = o["planes"].shape[1] // 2
+    g = o["planes"].view(torch.int8).to(torch.int32)
+    hi, lo = g[:, :n], g[:, n:]  # per row: the high plane, then the low plane
     return 256 * hi + lo + 128 * ((o["code"].to(torch.int32) >> 1) & 1)[:, None]
 
 
