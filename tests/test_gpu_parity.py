@@ -1086,7 +1086,7 @@ def test_few_tokens_blocks_choose_their_own_split(ops, M):
 
 
 PLANE_MERGE_CASES = [(37, 1024, 8, 8, 8), (64, 768, 4, 4, 4), (96, 3072, 32, 4, 4), (33, 1600, 4, 8, 8),
-                     (6, 1536, 64, 4, 2)]
+                     (6, 1536, 64, 4, 2), (5, 48, 4, 4, 4), (19, 80, 8, 8, 8), (3, 16, 4, 4, 4)]
 
 
 @pytest.mark.parametrize("d,n,r,w_bits,u_bits", PLANE_MERGE_CASES)
